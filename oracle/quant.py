@@ -1,0 +1,54 @@
+"""INT8 quantisation of the non-RoPE part of K (test infrastructure only).
+
+Sources: MindIE LLM page "FA3 quantization", overview paragraph (only the
+non-RoPE slice of K is quantised to 8 bits, per head; the RoPE slice of K is
+left unquantised); msModelSlim page "FA3量化", section 适用要求 (only symmetric
+INT8) and section 算法流程 (``scale = abs_max / 127``).
+
+The pages print no quantisation formula.  Readings (also in the design doc):
+
+* Q1 symmetric INT8 means no offset: ``code = clamp(round(x / scale), -127, 127)``;
+  -128 is never produced and values beyond the calibrated range saturate.
+* Q2 ``x / scale`` is one correctly rounded float32 division of the float32
+  value of the bf16 input, and ``round`` is round-half-to-even applied to that
+  float32 quotient.
+* Q3 a head whose scale is 0 gets code 0 everywhere.
+* Q4 the first ``Dn`` features of a K row are the non-RoPE part and the last
+  ``Dr`` the RoPE part; the RoPE part is copied bit for bit, per head.
+"""
+from __future__ import annotations
+
+from typing import Tuple
+
+import numpy as np
+
+from .floats import bf16_bits_to_f32
+
+
+def quantize_k(k_bits, scale, Dn: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Split a bf16 K tensor ``(B, H, S, Dn + Dr)`` into INT8 K-nope codes and bf16 K-rope.
+
+    ``k_bits`` holds raw bf16 patterns; ``scale`` is float32 ``[H]``.  Returns
+    ``(codes (B,H,S,Dn) int8, rope (B,H,S,Dr) uint16 patterns)``.
+    """
+    k_bits = np.asarray(k_bits).view(np.uint16) if np.asarray(k_bits).dtype == np.int16 else np.asarray(k_bits, dtype=np.uint16)
+    if k_bits.ndim != 4:
+        raise ValueError("k must be (B, H, S, Dn + Dr)")
+    H = k_bits.shape[1]
+    scale = np.asarray(scale, dtype=np.float32).reshape(H)
+    x = bf16_bits_to_f32(k_bits[..., :Dn])
+    s = scale.reshape(1, H, 1, 1)
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        quotient = (x / s).astype(np.float32)          # Q2: float32 division
+        code = np.clip(np.rint(quotient), -127.0, 127.0)  # Q2: half-to-even, Q1: clamp
+    code = np.where(s == np.float32(0.0), 0.0, code)       # Q3
+    rope = k_bits[..., Dn:].copy()                          # Q4: bitwise copy
+    return code.astype(np.int8), rope
+
+
+def dequantize_k_nope(codes, scale) -> np.ndarray:
+    """float64 value represented by the INT8 K-nope cache: ``scale[h] * code``."""
+    codes = np.asarray(codes, dtype=np.int8)
+    H = codes.shape[1]
+    s = np.asarray(scale, dtype=np.float32).astype(np.float64).reshape(1, H, 1, 1)
+    return s * codes.astype(np.float64)

@@ -1,0 +1,98 @@
+"""Pins for the oracle's float64 decode attention.
+
+The pages show no attention operator (MindIE page "FA3 quantization" only says
+the INT8 K cache serves decode-phase attention), so the oracle is the textbook
+definition; it is pinned against torch's float64 scaled_dot_product_attention
+on the CPU and against special cases with closed-form answers.
+"""
+import math
+
+import numpy as np
+import torch
+
+import oracle
+
+
+def _rand_bits(rng, shape, std=1.0):
+    return oracle.f32_to_bf16_bits_rne(rng.normal(size=shape).astype(np.float32) * np.float32(std))
+
+
+def test_attention_matches_torch_sdpa_fp64():
+    rng = np.random.default_rng(31)
+    B, H, T, Dk, Dv = 2, 3, 37, 24, 16
+    q = rng.normal(size=(B, H, Dk)); k = rng.normal(size=(B, H, T, Dk)); v = rng.normal(size=(B, H, T, Dv))
+    sm = 1 / math.sqrt(Dk)
+    ours = oracle.attention_fp64(q, k, v, sm)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q).unsqueeze(2), torch.from_numpy(k), torch.from_numpy(v), scale=sm
+    ).squeeze(2).numpy()
+    np.testing.assert_allclose(ours, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_single_token_returns_its_value():
+    rng = np.random.default_rng(32)
+    q = rng.normal(size=(1, 2, 8)); k = rng.normal(size=(1, 2, 1, 8)); v = rng.normal(size=(1, 2, 1, 5))
+    np.testing.assert_allclose(oracle.attention_fp64(q, k, v, 0.3), v[:, :, 0], rtol=0, atol=1e-15)
+
+
+def test_zero_query_is_mean_of_values():
+    rng = np.random.default_rng(33)
+    k = rng.normal(size=(1, 1, 50, 8)); v = rng.normal(size=(1, 1, 50, 4))
+    out = oracle.attention_fp64(np.zeros((1, 1, 8)), k, v, 1.0)
+    np.testing.assert_allclose(out[0, 0], v[0, 0].mean(axis=0), rtol=1e-13, atol=1e-15)
+
+
+def test_known_two_token_weights():
+    # scores 0 and ln 3 -> weights 1/4 and 3/4
+    q = np.array([[[1.0]]]); k = np.array([[[[0.0], [math.log(3.0)]]]])
+    v = np.array([[[[4.0, 0.0], [0.0, 8.0]]]])
+    out = oracle.attention_fp64(q, k, v, 1.0)
+    np.testing.assert_allclose(out[0, 0], [1.0, 6.0], rtol=1e-14)
+
+
+def test_dominant_token():
+    rng = np.random.default_rng(34)
+    k = rng.normal(size=(1, 1, 20, 4)) * 0.01
+    k[0, 0, 13] = [50.0, 0, 0, 0]
+    v = rng.normal(size=(1, 1, 20, 3))
+    out = oracle.attention_fp64(np.array([[[1.0, 0, 0, 0]]]), k, v, 1.0)
+    np.testing.assert_allclose(out[0, 0], v[0, 0, 13], rtol=1e-15, atol=1e-15)
+
+
+def test_decode_attn_is_attention_over_dequantised_cache():
+    rng = np.random.default_rng(35)
+    B, H, T, Dn, Dr, Dv = 2, 4, 64, 32, 16, 32
+    qb = _rand_bits(rng, (B, H, Dn + Dr))
+    codes = rng.integers(-127, 128, size=(B, H, T, Dn)).astype(np.int8)
+    scale = np.exp(rng.uniform(-6, -2, size=H)).astype(np.float32)
+    rope = _rand_bits(rng, (B, H, T, Dr))
+    vb = _rand_bits(rng, (B, H, T, Dv))
+    sm = np.float32(1 / math.sqrt(Dn + Dr))
+    out = oracle.decode_attn(qb, codes, scale, rope, vb, sm)
+    # independent assembly through torch fp64 SDPA on the dequantised K
+    kd = torch.from_numpy(codes.astype(np.float64)) * torch.from_numpy(scale.astype(np.float64)).view(1, H, 1, 1)
+    kr = torch.from_numpy(oracle.bf16_bits_to_f64(rope))
+    k = torch.cat([kd, kr], dim=-1)
+    q = torch.from_numpy(oracle.bf16_bits_to_f64(qb)).unsqueeze(2)
+    v = torch.from_numpy(oracle.bf16_bits_to_f64(vb))
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=float(sm)).squeeze(2).numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-13)
+    # factoring the per-head scale out of the nope dot product is the same attention
+    qn = oracle.bf16_bits_to_f64(qb)[..., :Dn]
+    s_factored = scale.astype(np.float64).reshape(1, H, 1) * np.einsum("bhd,bhtd->bht", qn, codes.astype(np.float64))
+    s_elem = np.einsum("bhd,bhtd->bht", qn, kd.numpy())
+    np.testing.assert_allclose(s_factored, s_elem, rtol=1e-13, atol=1e-13)
+
+
+def test_bf16_helpers_roundtrip():
+    x = np.array([1.0, -2.5, 3.140625, 0.0, -0.0, 1e-30, 65504.0], np.float32)
+    bits = oracle.f32_to_bf16_bits_rne(x)
+    back = oracle.bf16_bits_to_f32(bits)
+    # values already representable in bf16 come back unchanged
+    for a, b in zip(x[[0, 1, 2, 3, 4]], back[[0, 1, 2, 3, 4]]):
+        assert a.view(np.uint32) == b.view(np.uint32)
+    # rounding matches torch's float32 -> bfloat16 cast (round to nearest even)
+    rng = np.random.default_rng(36)
+    y = (rng.normal(size=10000) * np.exp(rng.uniform(-20, 20, size=10000))).astype(np.float32)
+    tb = torch.from_numpy(y).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(oracle.f32_to_bf16_bits_rne(y), tb)

@@ -1,0 +1,265 @@
+#!/usr/bin/env python3
+"""Benchmark of the FA3 per-head INT8 hot path on one MI355X.
+
+One step runs every stage once, on inputs already resident in HBM:
+  1. calibrate   4 batches of bf16 activations (8,128,2048,128), Student-t(3) tails,
+                 ratio 0.9999 (N = 2,097,152 values and K = 211 windows per head)
+  2. accumulate  running per-head min/max over the 4 batches (after an init)
+  3. qparams     scale[h] = abs_max / 127
+  4. quantize    K of 64 sequences x 4096 tokens, H=128, 128 nope + 64 rope dims, bf16
+                 -> int8 K-nope cache + bf16 K-rope (scales from step 3)
+  5. decode      batch 64, 128 heads, one query each over the 4096 cached tokens of
+                 step 4 plus bf16 V (128 dims), softmax scale 1/sqrt(192)
+
+Prints one JSON line.  ``value`` is the step's algorithmic HBM bytes divided by its
+wall time (GB/s); per-stage figures (calib Gelem/s, quantize GB/s, decode KV GB/s, each
+as a fraction of the 8 TB/s HBM peak) are under ``breakdown``; ``roofline`` is for the
+kernel that takes the most time, timed with HIP events on the stream it runs on;
+``cpu_baseline`` is the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+METRIC = "calib Gelem/s; quantize GB/s; decode-attn KV GB/s (fraction of HBM peak)"
+
+# workload shapes
+H = 128
+CAL_SHAPE = (8, H, 2048, 128)
+CAL_BATCHES = 4
+RATIO = 0.9999
+QB, QS, DN, DR = 64, 4096, 128, 64
+DV = 128
+
+CAL_BYTES = 2 * math.prod(CAL_SHAPE)                            # per batch, bf16 read once
+QUANT_BYTES = QB * H * QS * (2 * (DN + DR) + DN + 2 * DR)       # 640 B per (token, head)
+DEC_BYTES = QB * H * QS * (DN + 2 * DR + 2 * DV) + QB * H * (2 * (DN + DR) + 4 * DV)  # 512 B per (b,h,t) + q + out
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of CPU oracle work for the baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def cpu_baseline(inputs, budget_s: float):
+    """Time the oracle (as is, single process) on bounded slices of the same workload."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    def bits16(t):
+        return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+    per_stage = budget_s / 3.0
+    # calibrate: whole heads of batch 0 (one Recall Window per head)
+    x0 = inputs["calib"][0]
+    n_head = CAL_SHAPE[0] * CAL_SHAPE[2] * CAL_SHAPE[3]
+    done, t_cal, h = 0, 0.0, 0
+    while t_cal < per_stage and h < H:
+        head = x0[:, h].to(torch.float32).cpu().numpy().reshape(-1)
+        t0 = time.perf_counter()
+        oracle.recall_window(head, RATIO)
+        t_cal += time.perf_counter() - t0
+        done += n_head
+        h += 1
+    cal_rate = done / t_cal  # elements / s
+    heads_cal = h
+    # quantize: 8 heads x 4096 tokens of one sequence per round
+    k = inputs["k"]
+    scale = inputs["scale"].cpu().numpy()
+    done_b, t_q, rounds = 0, 0.0, 0
+    while t_q < per_stage and rounds < QB:
+        kb = bits16(k[rounds:rounds + 1, :8])
+        t0 = time.perf_counter()
+        oracle.quantize_k(kb, scale[:8], DN)
+        t_q += time.perf_counter() - t0
+        done_b += kb.size // (DN + DR) * (2 * (DN + DR) + DN + 2 * DR)
+        rounds += 1
+    q_rate = done_b / t_q
+    # decode: 4 (b,h) pairs per round
+    kq, kr, v, q = inputs["kq"], inputs["kr"], inputs["v"], inputs["q"]
+    done_d, t_d, r = 0, 0.0, 0
+    while t_d < per_stage and r < QB:
+        args = (bits16(q[r:r + 1, :4]), kq[r:r + 1, :4].cpu().numpy(), scale[:4], bits16(kr[r:r + 1, :4]),
+                bits16(v[r:r + 1, :4]), 1.0 / math.sqrt(DN + DR))
+        t0 = time.perf_counter()
+        oracle.decode_attn(*args)
+        t_d += time.perf_counter() - t0
+        done_d += 4 * QS * (DN + 2 * DR + 2 * DV)
+        r += 1
+    d_rate = done_d / t_d
+    step_s = CAL_BATCHES * CAL_BYTES / (2 * cal_rate) + QUANT_BYTES / q_rate + DEC_BYTES / d_rate
+    total = CAL_BATCHES * CAL_BYTES + QUANT_BYTES + DEC_BYTES
+    return {
+        "value": total / step_s / 1e9,
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"{heads_cal} whole heads of one calibration batch (2,097,152 values each), {rounds} x "
+                   f"(8 heads x 4096 tokens) of K quantisation, {r} x 4 (b,h) decode pairs over 4096 tokens; "
+                   "rates scaled to one full step by the step's bytes per stage"),
+        "stages": {"calib_gelem_s": cal_rate / 1e9, "quantize_gbs": q_rate / 1e9, "decode_kv_gbs": d_rate / 1e9},
+        "cpu": platform.processor() or platform.machine(),
+        "host_threads_available": len(os.sched_getaffinity(0)),
+    }
+
+
+def main() -> int:
+    args = parse()
+    if args.gpus != 1:
+        log("bench.py measures one GPU: this build has no multi-GPU path (each GPU would run its own "
+            "heads or sequences with no exchange); run with --gpus 1")
+        return 2
+    import torch
+
+    import kv_cache_quantization_fa3q_amd as fa
+    import synth
+
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+    log(f"device: {props.name} CUs={props.multi_processor_count} mem={props.total_memory / 2**30:.0f} GiB "
+        f"lib={fa.library_path()}")
+
+    t_setup = time.perf_counter()
+    sigma = synth.head_sigmas(H, seed=2024)
+    calib = [synth.activations(CAL_SHAPE, sigma, law="t3", dtype=torch.bfloat16, seed=100 + i, device=dev)
+             for i in range(CAL_BATCHES)]
+    k = synth.activations((QB, H, QS, DN + DR), sigma, law="normal", outlier_frac=0.0005, outlier_mult=40.0,
+                          dtype=torch.bfloat16, seed=200, device=dev)
+    v = synth.activations((QB, H, QS, DV), sigma, law="normal", dtype=torch.bfloat16, seed=300, device=dev)
+    q = synth.normal_tensor((QB, H, DN + DR), dtype=torch.bfloat16, seed=400, device=dev)
+    kq = torch.empty((QB, H, QS, DN), dtype=torch.int8, device=dev)
+    kr = torch.empty((QB, H, QS, DR), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((QB, H, DV), dtype=torch.float32, device=dev)
+    win_min = torch.empty(H, dtype=torch.float32, device=dev)
+    win_max = torch.empty(H, dtype=torch.float32, device=dev)
+    run_min = torch.empty(H, dtype=torch.float32, device=dev)
+    run_max = torch.empty(H, dtype=torch.float32, device=dev)
+    scale = torch.empty(H, dtype=torch.float32, device=dev)
+    ws_cal = torch.empty(max(1, fa.fa3q_calibrate_workspace_bytes(torch.bfloat16, *CAL_SHAPE, RATIO)),
+                         dtype=torch.uint8, device=dev)
+    dec_ws_bytes = fa.fa3q_decode_attn_workspace_bytes(QB, H, QS, DV)
+    ws_dec = torch.empty(dec_ws_bytes, dtype=torch.uint8, device=dev) if dec_ws_bytes else None
+    sm = 1.0 / math.sqrt(DN + DR)
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.perf_counter() - t_setup:.1f} s")
+
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        fa.fa3q_init_minmax(run_min, run_max, stream=stream)
+        for xb in calib:
+            fa.fa3q_calibrate_perhead(xb, RATIO, win_min, win_max, ws_cal, stream=stream)
+            fa.fa3q_accumulate_minmax(run_min, run_max, win_min, win_max, stream=stream)
+        if ev:
+            ev[1].record(stream)
+        fa.fa3q_qparams(run_min, run_max, scale, stream=stream)
+        if ev:
+            ev[2].record(stream)
+        fa.fa3q_quantize_k(k, scale, DN, kq, kr, stream=stream)
+        if ev:
+            ev[3].record(stream)
+        fa.fa3q_decode_attn(q, kq, scale, kr, v, sm, out, ws_dec, stream=stream)
+        if ev:
+            ev[4].record(stream)
+
+    for i in range(args.warmup):
+        step()
+        log(f"warmup step {i + 1}/{args.warmup} enqueued")
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log(f"timed {args.steps} steps in {wall:.3f} s")
+
+    def avg(a, b):
+        return sum(events[i][a].elapsed_time(events[i][b]) for i in range(args.steps)) / args.steps  # ms
+
+    cal_ms, qp_ms, quant_ms, dec_ms = avg(0, 1), avg(1, 2), avg(2, 3), avg(3, 4)
+    ms_per_step = wall * 1e3 / args.steps
+    total_bytes = CAL_BATCHES * CAL_BYTES + QUANT_BYTES + DEC_BYTES
+    value = total_bytes / (ms_per_step * 1e-3) / 1e9
+
+    cal_gbs = CAL_BATCHES * CAL_BYTES / (cal_ms * 1e-3) / 1e9
+    quant_gbs = QUANT_BYTES / (quant_ms * 1e-3) / 1e9
+    dec_gbs = DEC_BYTES / (dec_ms * 1e-3) / 1e9
+    breakdown = {
+        "calibrate": {"ms": cal_ms, "gelem_s": CAL_BATCHES * CAL_BYTES / 2 / (cal_ms * 1e-3) / 1e9,
+                      "gbs": cal_gbs, "frac_hbm": cal_gbs / HBM_PEAK_GBS,
+                      "note": "4 batches: chunk+merge kernels per batch, plus init/accumulate"},
+        "qparams": {"ms": qp_ms},
+        "quantize": {"ms": quant_ms, "gbs": quant_gbs, "frac_hbm": quant_gbs / HBM_PEAK_GBS},
+        "decode": {"ms": dec_ms, "kv_gbs": dec_gbs, "frac_hbm": dec_gbs / HBM_PEAK_GBS},
+    }
+    stages = {"quantize_k_kernel": (quant_ms, QUANT_BYTES), "decode_split_kernel": (dec_ms, DEC_BYTES),
+              "calibrate (per batch)": (cal_ms / CAL_BATCHES, CAL_BYTES)}
+    dom = max(stages, key=lambda s: stages[s][0] * (CAL_BATCHES if s.startswith("calib") else 1))
+    d_ms, d_bytes = stages[dom]
+    achieved = d_bytes / (d_ms * 1e-3) / 1e9
+    roofline = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                "algorithmic_bytes_per_launch": d_bytes, "avg_launch_ms": d_ms}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        cpu = cpu_baseline({"calib": calib, "k": k, "scale": scale, "kq": kq, "kr": kr, "v": v, "q": q},
+                           args.cpu_budget)
+
+    rec = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": ("fa3q hot path: calibrate 4 x bf16 (8,128,2048,128) ratio 0.9999 -> accumulate -> qparams "
+                         "-> quantize K (64,128,4096,128+64) -> decode attention B=64 H=128 T=4096 Dv=128"),
+            "storage": "bf16 activations/K-rope/V, int8 K-nope cache, float32 stats and scales",
+            "algorithmic_bytes_per_step": total_bytes,
+        },
+        "breakdown": breakdown,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

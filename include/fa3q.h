@@ -1,0 +1,210 @@
+/*
+ * fa3q.h -- C ABI of libfa3q, the FA3 per-head INT8 path for AMD Instinct MI355X (gfx950).
+ *
+ * The library computes the data-parallel hot path of "FA3" per-head INT8
+ * quantisation of MLA attention activations and the decode-phase attention
+ * that reads the quantised K cache:
+ *
+ *   1. fa3q_calibrate_perhead  -- per-head Recall Window of one calibration batch
+ *   2. fa3q_accumulate_minmax  -- running min/max across calibration batches
+ *      (fa3q_init_minmax sets the running state to its identity first)
+ *   3. fa3q_qparams            -- symmetric per-head scale = abs_max / 127
+ *   4. fa3q_quantize_k         -- non-RoPE part of K -> INT8 codes, RoPE part kept in bf16
+ *   5. fa3q_decode_attn        -- single-query attention over INT8 K-nope + bf16 K-rope + bf16 V
+ *
+ * Sources, cited by page title and section:
+ *   [MS] msModelSlim documentation, "FA3量化：Flash Attention 3激活量化算法说明"
+ *        (FA3 quantization: Flash Attention 3 activation quantization algorithm),
+ *        sections 原理 -> 算法流程 (algorithm flow) and 适用要求 (requirements).
+ *   [MI] MindIE LLM user guide, "FA3 quantization", overview paragraph.
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer is a DEVICE pointer owned by the caller; the library never
+ *     allocates, frees or retains memory and keeps no state between calls.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the default stream.
+ *     Calls only enqueue work on `stream`; they never synchronise.
+ *   - Arguments are validated on the host BEFORE anything is enqueued: a
+ *     non-zero status means nothing was launched and no output was touched.
+ *     Validation makes no HIP call, so it works on a host without a GPU.
+ *   - FA3Q_ERR_HIP means a launch was rejected by the HIP runtime; earlier
+ *     kernels of the same call may already be enqueued.
+ *   - bf16 tensors are passed as their raw 16-bit patterns (uint16_t).
+ *   - Inputs must be finite; for NaN/Inf inputs the outputs are unspecified
+ *     (the kernels stay inside their buffers for any input bits).
+ *   - Outputs must not overlap inputs, except the in/out running statistics.
+ *   - Concurrent calls on different streams are safe if they use distinct
+ *     output and workspace buffers.
+ */
+#ifndef FA3Q_H_
+#define FA3Q_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa3q_status {
+  FA3Q_OK = 0,
+  FA3Q_ERR_NULL = 1,        /* a required pointer is NULL */
+  FA3Q_ERR_DTYPE = 2,       /* unknown dtype code */
+  FA3Q_ERR_SHAPE = 3,       /* a size is <= 0, too large, or not a multiple the kernels need */
+  FA3Q_ERR_RATIO = 4,       /* ratio not in (0, 1], or int(ratio*N) < 1 */
+  FA3Q_ERR_ALIGN = 5,       /* a pointer is not aligned as documented */
+  FA3Q_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than the *_workspace_bytes query */
+  FA3Q_ERR_HIP = 7,         /* the HIP runtime rejected a launch */
+  FA3Q_ERR_UNSUPPORTED = 8  /* valid arguments outside what this build handles (see each call) */
+} fa3q_status;
+
+typedef enum fa3q_dtype {
+  FA3Q_F32 = 0,  /* IEEE binary32 */
+  FA3Q_BF16 = 1  /* bfloat16, raw 16-bit patterns */
+} fa3q_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* fa3q_status_string(int status);
+
+/* ABI version: (major << 16) | minor. */
+int fa3q_version(void);
+
+/* ------------------------------------------------------------------------ */
+/* 1. Recall Window calibration                                              */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Largest number of windows K = N - int(ratio*N) + 1 that fa3q_calibrate_perhead
+ * handles for `dtype`; a larger K returns FA3Q_ERR_UNSUPPORTED.  0 for an
+ * unknown dtype.
+ */
+int64_t fa3q_calibrate_max_windows(int dtype);
+
+/*
+ * Device workspace fa3q_calibrate_perhead needs for these arguments, in bytes
+ * (0 when the arguments are invalid).  Depends only on the arguments.
+ */
+size_t fa3q_calibrate_workspace_bytes(int dtype, int64_t B, int64_t H, int64_t S, int64_t D,
+                                      double ratio);
+
+/*
+ * [MS] 算法流程, per-head statistics and Recall Window.  For one calibration
+ * batch x of shape (B, H, S, D), row-major, every head h gathers its
+ * N = B*S*D values x[:, h, :, :] (grouped per head, not a raw reshape),
+ * sorts them (float32 total order, -0.0 before +0.0), sets
+ * t = int(ratio*N) (ratio*N rounded as an IEEE double, then truncated toward
+ * zero) and among the windows [s[i], s[i+t-1]], i = 0 .. N-t inclusive, picks
+ * the one whose float32 length s[i+t-1] - s[i] is smallest, the smallest i on
+ * ties.  Writes win_min[h] = s[i*] and win_max[h] = s[i*+t-1] (float32 values
+ * of the input; exact, no rounding).
+ *
+ *   x          device, dtype FA3Q_F32 or FA3Q_BF16, (B,H,S,D) contiguous, 16-byte aligned.
+ *   B,H,S,D    > 0; S*D must be a multiple of 8 (bf16) or 4 (f32).
+ *   ratio      in (0, 1]; t = int(ratio*N) must be >= 1.
+ *   win_min,
+ *   win_max    device float32 [H], 4-byte aligned.
+ *   workspace  device, 256-byte aligned, >= fa3q_calibrate_workspace_bytes(...).
+ *
+ * Only the K = N-t+1 smallest and K largest values of a head can bound a
+ * window, so the kernels select those two tails in one pass over x instead of
+ * sorting.  K above fa3q_calibrate_max_windows(dtype) -> FA3Q_ERR_UNSUPPORTED.
+ */
+int fa3q_calibrate_perhead(const void* x, int dtype, int64_t B, int64_t H, int64_t S, int64_t D,
+                           double ratio, float* win_min, float* win_max, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* 2. Cross-batch accumulation                                               */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Sets run_min[h] = +inf and run_max[h] = -inf, the identities of the running
+ * min/max of [MS] 算法流程 (cross-batch accumulation).  float32 [H] device
+ * arrays, 4-byte aligned, H > 0.
+ */
+int fa3q_init_minmax(float* run_min, float* run_max, int64_t H, void* stream);
+
+/*
+ * [MS] 算法流程, cross-batch accumulation: in place,
+ *   run_min[h] = min(run_min[h], cur_min[h]),  run_max[h] = max(run_max[h], cur_max[h])
+ * under the float32 total order (-0.0 < +0.0).  All float32 [H] device arrays,
+ * 4-byte aligned; cur_* may be the win_min/win_max of fa3q_calibrate_perhead.
+ */
+int fa3q_accumulate_minmax(float* run_min, float* run_max, const float* cur_min,
+                           const float* cur_max, int64_t H, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* 3. Symmetric per-head scale                                               */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * [MS] 算法流程, quantisation parameters, and 适用要求 (INT8 symmetric only):
+ *   scale[h] = max(|run_min[h]|, |run_max[h]|) / 127
+ * as one correctly rounded float32 division.  float32 [H] device arrays,
+ * 4-byte aligned.  A head whose range is {0} gets scale 0.
+ */
+int fa3q_qparams(const float* run_min, const float* run_max, float* scale, int64_t H,
+                 void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* 4. K-cache quantisation                                                   */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * [MI] overview: only the non-RoPE part of K is quantised to 8 bits, per
+ * head; the RoPE part of K is not quantised.  For every row (b, h, s) of the
+ * bf16 tensor k (B, H, S, Dn+Dr):
+ *   k_nope_q[b,h,s,d] = clamp(round_half_even(fl32(x / scale[h])), -127, 127),  d < Dn
+ *                       with x the float32 value of k[b,h,s,d]; 0 when scale[h] == 0
+ *   k_rope[b,h,s,j]   = k[b,h,s,Dn+j] bit for bit,  j < Dr
+ *
+ *   k         device bf16 (B,H,S,Dn+Dr) contiguous, 16-byte aligned.
+ *   scale     device float32 [H] (from fa3q_qparams), 4-byte aligned.
+ *   k_nope_q  device int8 (B,H,S,Dn) contiguous, 16-byte aligned.
+ *   k_rope    device bf16 (B,H,S,Dr) contiguous, 16-byte aligned; may be NULL iff Dr == 0.
+ *   B,H,S > 0; Dn > 0 multiple of 16, Dn <= 4096; Dr >= 0 multiple of 8, Dr <= 2048.
+ */
+int fa3q_quantize_k(const uint16_t* k, const float* scale, int8_t* k_nope_q, uint16_t* k_rope,
+                    int64_t B, int64_t H, int64_t S, int64_t Dn, int64_t Dr, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* 5. Decode attention over the quantised cache                             */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Device workspace fa3q_decode_attn needs, in bytes (0 when none is needed or
+ * the arguments are invalid); the call splits long caches over several
+ * workgroups per (b, h) and merges their partial softmax states here.
+ */
+size_t fa3q_decode_attn_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t Dv);
+
+/*
+ * [MI] overview: the INT8 K-nope cache serves the decode-phase attention
+ * operator.  One query token per (b, h) attends to all T cached tokens:
+ *   s_t   = sm_scale * ( scale[h] * sum_{d<Dn} q[b,h,d] * k_nope_q[b,h,t,d]
+ *                        + sum_{j<Dr} q[b,h,Dn+j] * k_rope[b,h,t,j] )
+ *   out[b,h,:] = sum_t softmax(s)_t * v[b,h,t,:]
+ * i.e. attention over the cache dequantised per head (scale[h] * code).
+ * Arithmetic is float32 (exact int8/bf16 widening, float32 accumulation).
+ *
+ *   q          device bf16 (B,H,Dn+Dr) contiguous, 16-byte aligned.
+ *   k_nope_q   device int8 (B,H,T,Dn), 16-byte aligned.
+ *   scale      device float32 [H].
+ *   k_rope     device bf16 (B,H,T,Dr), 16-byte aligned; may be NULL iff Dr == 0.
+ *   v          device bf16 (B,H,T,Dv), 16-byte aligned.
+ *   out        device float32 (B,H,Dv), 16-byte aligned.
+ *   B,H,T > 0; Dn in {16,32,...,1024} with Dn/16 a power of two or Dn/16 <= 64;
+ *   Dr a multiple of 8 with Dr/8 <= 64; at least one of Dn, Dr > 0 with
+ *   Dn % 16 == 0; Dv a power of two in [8, 512].
+ *   workspace  device, 256-byte aligned, >= fa3q_decode_attn_workspace_bytes(B,H,T,Dv);
+ *              may be NULL when that query returns 0.
+ */
+int fa3q_decode_attn(const uint16_t* q, const int8_t* k_nope_q, const float* scale,
+                     const uint16_t* k_rope, const uint16_t* v, int64_t B, int64_t H,
+                     int64_t T, int64_t Dn, int64_t Dr, int64_t Dv, float sm_scale, float* out,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA3Q_H_ */

@@ -1,0 +1,402 @@
+// Decode-phase attention over the quantised cache: INT8 K-nope (per-head scale),
+// bf16 K-rope and bf16 V, one query token per (b, h).
+//
+// MindIE LLM page "FA3 quantization", overview: the INT8 K-nope / float K-rope cache is
+// there to cut KV-cache memory and speed up decode-phase attention.  The pages show no
+// operator; this is softmax attention over the cache dequantised per head:
+//   s_t = sm * (scale[h] * <q_nope, code_t> + <q_rope, k_rope_t>),  out = sum_t softmax(s)_t v_t
+// with scale[h] factored out of the nope dot product (equal to dequantising each code).
+//
+// Shape of the work: a single query per (b, h) makes QK^T a matrix-vector product over
+// T rows of 2*Dn + 2*Dr + 2*Dv bytes (512 B for the MLA shape), at about 1.25 flop per
+// byte; it is bound by HBM, so it runs on the vector ALUs (a 16x16 MFMA tile would be
+// 15/16 empty).  Each workgroup owns (b, h, split) and a run of up to kMaxSplitLen tokens:
+//   phase 1  LK lanes per token, 16 int8 nope codes + 8 rope values per lane (two
+//            16-byte loads), eight tokens in flight per lane, DPP row reductions;
+//            scores (log2 domain) go to LDS;
+//   phase 2  block max and exp2 -> probabilities in LDS, block sum;
+//   phase 3  LV = Dv/8 lanes per token, one 16-byte V load per lane, probability-weighted
+//            sums, eight tokens in flight per lane.
+// Splits of one (b, h) leave (max, sum, unnormalised output) in the workspace and a
+// combine kernel merges them; with one split the output is written directly.
+#include <cmath>
+
+#include "fa3q_internal.hpp"
+
+namespace fa3q {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kMaxSplitLen = 4096;  // scores of one split are kept in LDS (16 KiB)
+constexpr int kMinSplitLen = 256;
+constexpr int64_t kTargetGroups = 2048;  // enough workgroups to fill 256 CUs several times
+constexpr int kUk = 8;  // tokens per lane in flight, phase 1
+constexpr int kUv = 8;  // tokens per lane in flight, phase 3
+
+struct DecodeArgs {
+  const uint16_t* q;
+  const int8_t* kq;
+  const float* scale;
+  const uint16_t* kr;
+  const uint16_t* v;
+  float* out;
+  float* ws_ml;  // [B*H*nsplit][2] (max, sum)
+  float* ws_o;   // [B*H*nsplit][Dv]
+  int64_t T;
+  int32_t H;
+  int32_t Dn;
+  int32_t Dr;
+  int32_t Dv;
+  int32_t nsplit;
+  int32_t split_len;
+  float sm_log2;  // sm_scale * log2(e)
+};
+
+// Sum over lanes of one wave that share (lane % LV): lane bits at and above log2(LV).
+template <int LV>
+__device__ __forceinline__ float slot_sum(float v) {
+#pragma unroll
+  for (int o = LV; o < kWave; o <<= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// <q, code> over 16 int8 codes held in a uint4, using unsigned bytes code+128 and the
+// precomputed sum of q (v_cvt_f32_ubyte* reads the offset codes directly).
+__device__ __forceinline__ float dot16_i8(const float (&qn)[16], float qsum, uint4 w) {
+  const uint32_t d[4] = {w.x ^ 0x80808080u, w.y ^ 0x80808080u, w.z ^ 0x80808080u, w.w ^ 0x80808080u};
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc = fmaf(qn[4 * i + 0], static_cast<float>(d[i] & 0xffu), acc);
+    acc = fmaf(qn[4 * i + 1], static_cast<float>((d[i] >> 8) & 0xffu), acc);
+    acc = fmaf(qn[4 * i + 2], static_cast<float>((d[i] >> 16) & 0xffu), acc);
+    acc = fmaf(qn[4 * i + 3], static_cast<float>(d[i] >> 24), acc);
+  }
+  return fmaf(-128.0f, qsum, acc);
+}
+
+__device__ __forceinline__ float dot8_bf16(const float (&qr)[8], uint4 w) {
+  float acc = 0.0f;
+  acc = fmaf(qr[0], bf16_lo(w.x), acc);
+  acc = fmaf(qr[1], bf16_hi(w.x), acc);
+  acc = fmaf(qr[2], bf16_lo(w.y), acc);
+  acc = fmaf(qr[3], bf16_hi(w.y), acc);
+  acc = fmaf(qr[4], bf16_lo(w.z), acc);
+  acc = fmaf(qr[5], bf16_hi(w.z), acc);
+  acc = fmaf(qr[6], bf16_lo(w.w), acc);
+  acc = fmaf(qr[7], bf16_hi(w.w), acc);
+  return acc;
+}
+
+template <int LK, int LV>
+__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
+  extern __shared__ float smem[];
+  float* sc = smem;                       // [split_len] scores, then probabilities
+  float* red = smem + a.split_len;        // [kWaves] block reduction scratch
+  float* part = red + kWaves;             // [kWaves][Dv] per-wave output partials
+
+  const int bh = static_cast<int>(blockIdx.x) / a.nsplit;
+  const int sp = static_cast<int>(blockIdx.x) - bh * a.nsplit;
+  const int h = bh % a.H;
+  const int64_t t0 = static_cast<int64_t>(sp) * a.split_len;
+  const int n = static_cast<int>(min(a.T - t0, static_cast<int64_t>(a.split_len)));
+  const int tid = static_cast<int>(threadIdx.x);
+  const int lane = lane_id();
+  const int wave = tid / kWave;
+
+  // ---------------------------------------------------------------- phase 1: scores
+  {
+    constexpr int kSlots = kWave / LK;
+    const int j = lane % LK;
+    const int slot = lane / LK;
+    const bool has_n = j < (a.Dn >> 4);
+    const bool has_r = j < (a.Dr >> 3);
+    const int Dk = a.Dn + a.Dr;
+    const uint16_t* qrow = a.q + static_cast<int64_t>(bh) * Dk;
+    float qn[16], qr[8];
+    float qsum = 0.0f;
+    if (has_n) {
+      const uint4* p = reinterpret_cast<const uint4*>(qrow + 16 * j);
+      const uint4 u0 = p[0], u1 = p[1];
+      const uint32_t w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        qn[2 * i] = bf16_lo(w[i]);
+        qn[2 * i + 1] = bf16_hi(w[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) qsum += qn[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) qn[i] = 0.0f;
+    }
+    if (has_r) {
+      const uint4 u = *reinterpret_cast<const uint4*>(qrow + a.Dn + 8 * j);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        qr[2 * i] = bf16_lo(w[i]);
+        qr[2 * i + 1] = bf16_hi(w[i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qr[i] = 0.0f;
+    }
+    const float head_scale = a.scale[h];
+    const int8_t* kq = a.kq + (static_cast<int64_t>(bh) * a.T + t0) * a.Dn + 16 * j;
+    const uint16_t* kr = a.kr + (static_cast<int64_t>(bh) * a.T + t0) * a.Dr + 8 * j;
+    const int step = kWaves * kSlots;
+    for (int base = wave * kSlots + slot; base < n; base += step * kUk) {
+      uint4 wn[kUk], wr[kUk];
+#pragma unroll
+      for (int u = 0; u < kUk; ++u) {
+        const int tt = base + u * step;
+        wn[u] = make_uint4(0, 0, 0, 0);
+        wr[u] = make_uint4(0, 0, 0, 0);
+        if (tt < n) {
+          if (has_n) wn[u] = *reinterpret_cast<const uint4*>(kq + static_cast<int64_t>(tt) * a.Dn);
+          if (has_r) wr[u] = *reinterpret_cast<const uint4*>(kr + static_cast<int64_t>(tt) * a.Dr);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kUk; ++u) {
+        const int tt = base + u * step;
+        float s = 0.0f;
+        if (has_n) s = head_scale * dot16_i8(qn, qsum, wn[u]);
+        if (has_r) s += dot8_bf16(qr, wr[u]);
+        s = group_sum<LK>(s);
+        if (j == 0 && tt < n) sc[tt] = s * a.sm_log2;
+      }
+    }
+  }
+  lds_barrier();
+
+  // ---------------------------------------------------------------- phase 2: softmax
+  float m = -INFINITY;
+  for (int i = tid; i < n; i += kThreads) m = fmaxf(m, sc[i]);
+  m = wave_max(m);
+  if (lane == 0) red[wave] = m;
+  lds_barrier();
+  m = red[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) m = fmaxf(m, red[w]);
+  float l = 0.0f;
+  for (int i = tid; i < n; i += kThreads) {
+    const float p = exp2f(sc[i] - m);
+    sc[i] = p;
+    l += p;
+  }
+  l = wave_sum(l);
+  lds_barrier();  // every wave has read red[] (max) before it is reused for the sum
+  if (lane == 0) red[wave] = l;
+  lds_barrier();
+  l = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) l += red[w];
+
+  // ---------------------------------------------------------------- phase 3: P . V
+  constexpr int kVSlots = kWave / LV;
+  const int jv = lane % LV;
+  const int vslot = lane / LV;
+  float acc[8];
+#pragma unroll
+  for (int d = 0; d < 8; ++d) acc[d] = 0.0f;
+  {
+    const uint16_t* vp = a.v + (static_cast<int64_t>(bh) * a.T + t0) * a.Dv + 8 * jv;
+    const int step = kWaves * kVSlots;
+    for (int base = wave * kVSlots + vslot; base < n; base += step * kUv) {
+      uint4 wv[kUv];
+      float p[kUv];
+#pragma unroll
+      for (int u = 0; u < kUv; ++u) {
+        const int tt = base + u * step;
+        wv[u] = make_uint4(0, 0, 0, 0);
+        p[u] = 0.0f;
+        if (tt < n) {
+          wv[u] = *reinterpret_cast<const uint4*>(vp + static_cast<int64_t>(tt) * a.Dv);
+          p[u] = sc[tt];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kUv; ++u) {
+        acc[0] = fmaf(p[u], bf16_lo(wv[u].x), acc[0]);
+        acc[1] = fmaf(p[u], bf16_hi(wv[u].x), acc[1]);
+        acc[2] = fmaf(p[u], bf16_lo(wv[u].y), acc[2]);
+        acc[3] = fmaf(p[u], bf16_hi(wv[u].y), acc[3]);
+        acc[4] = fmaf(p[u], bf16_lo(wv[u].z), acc[4]);
+        acc[5] = fmaf(p[u], bf16_hi(wv[u].z), acc[5]);
+        acc[6] = fmaf(p[u], bf16_lo(wv[u].w), acc[6]);
+        acc[7] = fmaf(p[u], bf16_hi(wv[u].w), acc[7]);
+      }
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < 8; ++d) acc[d] = slot_sum<LV>(acc[d]);
+  if (vslot == 0) {
+#pragma unroll
+    for (int d = 0; d < 8; ++d) part[wave * a.Dv + 8 * jv + d] = acc[d];
+  }
+  lds_barrier();
+  const int64_t row = static_cast<int64_t>(bh) * a.nsplit + sp;
+  for (int dim = tid; dim < a.Dv; dim += kThreads) {
+    float o = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) o += part[w * a.Dv + dim];
+    if (a.nsplit == 1) {
+      a.out[static_cast<int64_t>(bh) * a.Dv + dim] = o / l;
+    } else {
+      a.ws_o[row * a.Dv + dim] = o;
+    }
+  }
+  if (a.nsplit > 1 && tid == 0) {
+    a.ws_ml[2 * row] = m;
+    a.ws_ml[2 * row + 1] = l;
+  }
+}
+
+// Merge the per-split softmax states of one (b, h): out = sum_s w_s o_s / sum_s w_s l_s,
+// w_s = 2^(m_s - max_s m_s).
+__global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
+  const int64_t bh = blockIdx.x;
+  const float* ml = a.ws_ml + 2 * bh * a.nsplit;
+  float mmax = -INFINITY;
+  for (int s = 0; s < a.nsplit; ++s) mmax = fmaxf(mmax, ml[2 * s]);
+  float den = 0.0f;
+  for (int s = 0; s < a.nsplit; ++s) den += exp2f(ml[2 * s] - mmax) * ml[2 * s + 1];
+  for (int dim = threadIdx.x; dim < a.Dv; dim += blockDim.x) {
+    float num = 0.0f;
+    for (int s = 0; s < a.nsplit; ++s)
+      num += exp2f(ml[2 * s] - mmax) * a.ws_o[(bh * a.nsplit + s) * a.Dv + dim];
+    a.out[bh * a.Dv + dim] = num / den;
+  }
+}
+
+struct SplitPlan {
+  int32_t nsplit;
+  int32_t split_len;
+};
+
+SplitPlan plan_splits(int64_t B, int64_t H, int64_t T) {
+  const int64_t pairs = B * H;
+  int64_t ns = (T + kMaxSplitLen - 1) / kMaxSplitLen;
+  const int64_t want = (kTargetGroups + pairs - 1) / pairs;
+  const int64_t cap = std::max<int64_t>(1, T / kMinSplitLen);
+  ns = std::max(ns, std::min(want, cap));
+  const int64_t len = (T + ns - 1) / ns;
+  ns = (T + len - 1) / len;  // no empty split
+  return {static_cast<int32_t>(ns), static_cast<int32_t>(len)};
+}
+
+bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+int64_t next_pow2(int64_t v) {
+  int64_t p = 1;
+  while (p < v) p <<= 1;
+  return p;
+}
+
+using KernelFn = void (*)(DecodeArgs);
+
+template <int LK>
+KernelFn pick_lv(int lv) {
+  switch (lv) {
+    case 1: return decode_split_kernel<LK, 1>;
+    case 2: return decode_split_kernel<LK, 2>;
+    case 4: return decode_split_kernel<LK, 4>;
+    case 8: return decode_split_kernel<LK, 8>;
+    case 16: return decode_split_kernel<LK, 16>;
+    case 32: return decode_split_kernel<LK, 32>;
+    case 64: return decode_split_kernel<LK, 64>;
+    default: return nullptr;
+  }
+}
+
+KernelFn pick_kernel(int lk, int lv) {
+  switch (lk) {
+    case 1: return pick_lv<1>(lv);
+    case 2: return pick_lv<2>(lv);
+    case 4: return pick_lv<4>(lv);
+    case 8: return pick_lv<8>(lv);
+    case 16: return pick_lv<16>(lv);
+    case 32: return pick_lv<32>(lv);
+    case 64: return pick_lv<64>(lv);
+    default: return nullptr;
+  }
+}
+
+bool valid_dims(int64_t Dn, int64_t Dr, int64_t Dv) {
+  if (Dn <= 0 || Dn % 16 != 0 || Dn > 1024) return false;
+  if (Dr < 0 || Dr % 8 != 0 || Dr > 512) return false;
+  if (!pow2(Dv) || Dv < 8 || Dv > 512) return false;
+  return true;
+}
+
+}  // namespace
+}  // namespace fa3q
+
+using namespace fa3q;
+
+extern "C" size_t fa3q_decode_attn_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t Dv) {
+  if (B <= 0 || H <= 0 || T <= 0 || !pow2(Dv) || Dv < 8 || Dv > 512) return 0;
+  if (B > (int64_t{1} << 31) / H || T > (int64_t{1} << 40)) return 0;
+  const SplitPlan p = plan_splits(B, H, T);
+  if (p.nsplit <= 1) return 0;
+  return round_up(static_cast<size_t>(B * H * p.nsplit) * 2 * sizeof(float), 256) +
+         static_cast<size_t>(B * H * p.nsplit) * static_cast<size_t>(Dv) * sizeof(float);
+}
+
+extern "C" int fa3q_decode_attn(const uint16_t* q, const int8_t* k_nope_q, const float* scale,
+                                const uint16_t* k_rope, const uint16_t* v, int64_t B, int64_t H,
+                                int64_t T, int64_t Dn, int64_t Dr, int64_t Dv, float sm_scale,
+                                float* out, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  if (!q || !k_nope_q || !scale || !v || !out || (Dr > 0 && !k_rope)) return FA3Q_ERR_NULL;
+  if (B <= 0 || H <= 0 || T <= 0) return FA3Q_ERR_SHAPE;
+  if (!valid_dims(Dn, Dr, Dv)) return FA3Q_ERR_SHAPE;
+  if (B > (int64_t{1} << 31) / H || T > (int64_t{1} << 40)) return FA3Q_ERR_SHAPE;
+  if (B * H * T > (int64_t{1} << 62) / (Dn + Dr + Dv)) return FA3Q_ERR_SHAPE;
+  if (!std::isfinite(sm_scale)) return FA3Q_ERR_SHAPE;
+  if (!is_aligned(q, 16) || !is_aligned(k_nope_q, 16) || (Dr > 0 && !is_aligned(k_rope, 16)) ||
+      !is_aligned(v, 16) || !is_aligned(out, 16) || !is_aligned(scale, 4))
+    return FA3Q_ERR_ALIGN;
+  const SplitPlan p = plan_splits(B, H, T);
+  if (B * H * p.nsplit > (int64_t{1} << 31) - 1) return FA3Q_ERR_SHAPE;
+  const size_t need = fa3q_decode_attn_workspace_bytes(B, H, T, Dv);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return FA3Q_ERR_WORKSPACE;
+    if (!is_aligned(workspace, 256)) return FA3Q_ERR_ALIGN;
+  }
+  const int lk = static_cast<int>(next_pow2(std::max<int64_t>(Dn / 16, Dr / 8)));
+  const int lv = static_cast<int>(Dv / 8);
+  KernelFn fn = pick_kernel(lk, lv);
+  if (!fn) return FA3Q_ERR_UNSUPPORTED;
+
+  DecodeArgs a;
+  a.q = q;
+  a.kq = k_nope_q;
+  a.scale = scale;
+  a.kr = k_rope;
+  a.v = v;
+  a.out = out;
+  a.ws_ml = need ? static_cast<float*>(workspace) : nullptr;
+  a.ws_o = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                           round_up(static_cast<size_t>(B * H * p.nsplit) * 2 * sizeof(float), 256))
+                : nullptr;
+  a.T = T;
+  a.H = static_cast<int32_t>(H);
+  a.Dn = static_cast<int32_t>(Dn);
+  a.Dr = static_cast<int32_t>(Dr);
+  a.Dv = static_cast<int32_t>(Dv);
+  a.nsplit = p.nsplit;
+  a.split_len = p.split_len;
+  a.sm_log2 = static_cast<float>(static_cast<double>(sm_scale) * 1.4426950408889634);
+  const size_t lds = (static_cast<size_t>(p.split_len) + kWaves + kWaves * static_cast<size_t>(Dv)) * sizeof(float);
+  hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(B * H * p.nsplit)), dim3(kThreads), lds,
+                     as_stream(stream), a);
+  if (p.nsplit > 1) {
+    hipLaunchKernelGGL(decode_combine_kernel, dim3(static_cast<unsigned>(B * H)), dim3(128), 0,
+                       as_stream(stream), a);
+  }
+  return launch_status();
+}

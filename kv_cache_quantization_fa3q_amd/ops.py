@@ -1,0 +1,187 @@
+"""torch-facing binding of libfa3q: same names as the C ABI, argument marshalling only.
+
+Every function checks dtypes/devices/contiguity, allocates outputs and workspaces
+with torch when the caller passes none, passes raw device pointers and the current
+HIP stream to the library, and raises ``Fa3qError`` on a non-zero status.  All of
+the path's arithmetic runs in the library's HIP kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple
+
+import torch
+
+from ._lib import FA3Q_BF16, FA3Q_F32, Fa3qError, lib
+
+__all__ = [
+    "fa3q_calibrate_max_windows",
+    "fa3q_calibrate_workspace_bytes",
+    "fa3q_calibrate_perhead",
+    "fa3q_init_minmax",
+    "fa3q_accumulate_minmax",
+    "fa3q_qparams",
+    "fa3q_quantize_k",
+    "fa3q_decode_attn_workspace_bytes",
+    "fa3q_decode_attn",
+    "dtype_code",
+]
+
+
+def dtype_code(dtype: torch.dtype) -> int:
+    if dtype == torch.float32:
+        return FA3Q_F32
+    if dtype == torch.bfloat16:
+        return FA3Q_BF16
+    raise TypeError(f"unsupported dtype {dtype}; float32 or bfloat16")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _need_gpu(name: str, *tensors: Optional[torch.Tensor]) -> None:
+    for t in tensors:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name}: tensors must be on a GPU device")
+        if not t.is_contiguous():
+            raise ValueError(f"{name}: tensors must be contiguous")
+
+
+def _check(status: int, name: str) -> None:
+    if status != 0:
+        raise Fa3qError(status, name)
+
+
+def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return workspace
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes, needs {nbytes}")
+    return workspace
+
+
+# --------------------------------------------------------------------------- calibration
+
+
+def fa3q_calibrate_max_windows(dtype: torch.dtype) -> int:
+    return int(lib().fa3q_calibrate_max_windows(dtype_code(dtype)))
+
+
+def fa3q_calibrate_workspace_bytes(dtype: torch.dtype, B: int, H: int, S: int, D: int, ratio: float) -> int:
+    return int(lib().fa3q_calibrate_workspace_bytes(dtype_code(dtype), B, H, S, D, float(ratio)))
+
+
+def fa3q_calibrate_perhead(x: torch.Tensor, ratio: float, win_min: Optional[torch.Tensor] = None,
+                           win_max: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                           stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Recall Window of every head of one batch ``x (B,H,S,D)`` -> ``(win_min[H], win_max[H])``."""
+    if x.dim() != 4:
+        raise ValueError("x must be (B, H, S, D)")
+    B, H, S, D = (int(v) for v in x.shape)
+    code = dtype_code(x.dtype)
+    if win_min is None:
+        win_min = torch.empty(H, dtype=torch.float32, device=x.device)
+    if win_max is None:
+        win_max = torch.empty(H, dtype=torch.float32, device=x.device)
+    _need_gpu("fa3q_calibrate_perhead", x, win_min, win_max)
+    nbytes = int(lib().fa3q_calibrate_workspace_bytes(code, B, H, S, D, float(ratio)))
+    workspace = _workspace(nbytes, x.device, workspace)
+    st = lib().fa3q_calibrate_perhead(_ptr(x), code, B, H, S, D, float(ratio), _ptr(win_min), _ptr(win_max),
+                                      _ptr(workspace), nbytes if workspace is None else
+                                      workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "fa3q_calibrate_perhead")
+    return win_min, win_max
+
+
+def fa3q_init_minmax(run_min: torch.Tensor, run_max: torch.Tensor, stream=None) -> None:
+    _need_gpu("fa3q_init_minmax", run_min, run_max)
+    _check(lib().fa3q_init_minmax(_ptr(run_min), _ptr(run_max), run_min.numel(), _stream(stream)),
+           "fa3q_init_minmax")
+
+
+def fa3q_accumulate_minmax(run_min: torch.Tensor, run_max: torch.Tensor, cur_min: torch.Tensor,
+                           cur_max: torch.Tensor, stream=None) -> None:
+    _need_gpu("fa3q_accumulate_minmax", run_min, run_max, cur_min, cur_max)
+    H = run_min.numel()
+    if not (run_max.numel() == cur_min.numel() == cur_max.numel() == H):
+        raise ValueError("all four statistics must have H elements")
+    _check(lib().fa3q_accumulate_minmax(_ptr(run_min), _ptr(run_max), _ptr(cur_min), _ptr(cur_max), H,
+                                        _stream(stream)), "fa3q_accumulate_minmax")
+
+
+def fa3q_qparams(run_min: torch.Tensor, run_max: torch.Tensor, scale: Optional[torch.Tensor] = None,
+                 stream=None) -> torch.Tensor:
+    H = run_min.numel()
+    if scale is None:
+        scale = torch.empty(H, dtype=torch.float32, device=run_min.device)
+    _need_gpu("fa3q_qparams", run_min, run_max, scale)
+    _check(lib().fa3q_qparams(_ptr(run_min), _ptr(run_max), _ptr(scale), H, _stream(stream)), "fa3q_qparams")
+    return scale
+
+
+# --------------------------------------------------------------------------- quantize
+
+
+def fa3q_quantize_k(k: torch.Tensor, scale: torch.Tensor, Dn: int, k_nope_q: Optional[torch.Tensor] = None,
+                    k_rope: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """bf16 ``k (B,H,S,Dn+Dr)`` -> ``(int8 k_nope_q (B,H,S,Dn), bf16 k_rope (B,H,S,Dr))``."""
+    if k.dim() != 4 or k.dtype != torch.bfloat16:
+        raise ValueError("k must be bfloat16 (B, H, S, Dn + Dr)")
+    B, H, S, Dk = (int(v) for v in k.shape)
+    Dr = Dk - int(Dn)
+    if k_nope_q is None:
+        k_nope_q = torch.empty((B, H, S, int(Dn)), dtype=torch.int8, device=k.device)
+    if k_rope is None:
+        k_rope = torch.empty((B, H, S, Dr), dtype=torch.bfloat16, device=k.device)
+    _need_gpu("fa3q_quantize_k", k, scale, k_nope_q, k_rope)
+    _check(lib().fa3q_quantize_k(_ptr(k), _ptr(scale), _ptr(k_nope_q), _ptr(k_rope) if Dr > 0 else None,
+                                 B, H, S, int(Dn), Dr, _stream(stream)), "fa3q_quantize_k")
+    return k_nope_q, k_rope
+
+
+# --------------------------------------------------------------------------- decode
+
+
+def fa3q_decode_attn_workspace_bytes(B: int, H: int, T: int, Dv: int) -> int:
+    return int(lib().fa3q_decode_attn_workspace_bytes(B, H, T, Dv))
+
+
+def fa3q_decode_attn(q: torch.Tensor, k_nope_q: torch.Tensor, scale: torch.Tensor, k_rope: torch.Tensor,
+                     v: torch.Tensor, sm_scale: float, out: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Single-query attention over the INT8 K-nope + bf16 K-rope + bf16 V cache -> float32 ``(B,H,Dv)``."""
+    if k_nope_q.dim() != 4 or k_nope_q.dtype != torch.int8:
+        raise ValueError("k_nope_q must be int8 (B, H, T, Dn)")
+    B, H, T, Dn = (int(s) for s in k_nope_q.shape)
+    Dr = int(k_rope.shape[-1]) if k_rope is not None else 0
+    Dv = int(v.shape[-1])
+    if q.shape != (B, H, Dn + Dr) or q.dtype != torch.bfloat16:
+        raise ValueError("q must be bfloat16 (B, H, Dn + Dr)")
+    if v.shape != (B, H, T, Dv) or v.dtype != torch.bfloat16:
+        raise ValueError("v must be bfloat16 (B, H, T, Dv)")
+    if k_rope is not None and (k_rope.shape != (B, H, T, Dr) or k_rope.dtype != torch.bfloat16):
+        raise ValueError("k_rope must be bfloat16 (B, H, T, Dr)")
+    if out is None:
+        out = torch.empty((B, H, Dv), dtype=torch.float32, device=q.device)
+    _need_gpu("fa3q_decode_attn", q, k_nope_q, scale, k_rope, v, out)
+    nbytes = int(lib().fa3q_decode_attn_workspace_bytes(B, H, T, Dv))
+    workspace = _workspace(nbytes, q.device, workspace)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().fa3q_decode_attn(_ptr(q), _ptr(k_nope_q), _ptr(scale), _ptr(k_rope) if Dr > 0 else None, _ptr(v),
+                                B, H, T, Dn, Dr, Dv, ctypes.c_float(float(sm_scale)), _ptr(out), _ptr(workspace),
+                                wbytes, _stream(stream))
+    _check(st, "fa3q_decode_attn")
+    return out

@@ -1,0 +1,46 @@
+"""Helpers shared by the GPU parity tests (conversion of device tensors to the
+oracle's NumPy representations and the comparison metrics)."""
+import sys
+
+import numpy as np
+import torch
+
+DECODE_TOL = 2e-2        # contract: max row-normalised relative error vs the float64 oracle
+DECODE_DESIGN_TOL = 1e-4  # what float32 accumulation should reach (derived in the design notes)
+
+
+def log(msg: str) -> None:
+    """Name the case before a GPU step so a failing run says what it was doing."""
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def bits16(t: torch.Tensor) -> np.ndarray:
+    """bf16 tensor -> uint16 patterns on the host."""
+    assert t.dtype == torch.bfloat16
+    return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def f32(t: torch.Tensor) -> np.ndarray:
+    return t.detach().contiguous().cpu().numpy().astype(np.float32, copy=False)
+
+
+def assert_bits_equal(a, b, what: str) -> None:
+    """Bitwise equality of two float32 (or int) arrays, with the first mismatches named."""
+    a = np.ascontiguousarray(a)
+    b = np.ascontiguousarray(b)
+    assert a.shape == b.shape, f"{what}: shapes {a.shape} vs {b.shape}"
+    if a.dtype == np.float32:
+        a, b = a.view(np.uint32), b.view(np.uint32)
+    diff = np.flatnonzero(a.reshape(-1) != b.reshape(-1))
+    if len(diff):
+        first = [(int(i), a.reshape(-1)[i].item(), b.reshape(-1)[i].item()) for i in diff[:5]]
+        raise AssertionError(f"{what}: {len(diff)} of {a.size} differ; (flat index, gpu, oracle): {first}")
+
+
+def row_rel_err(out: np.ndarray, ref: np.ndarray) -> float:
+    """max over rows (b, h) of max_j |out - ref| / max_j |ref|."""
+    out = np.asarray(out, dtype=np.float64).reshape(-1, out.shape[-1])
+    ref = np.asarray(ref, dtype=np.float64).reshape(-1, ref.shape[-1])
+    denom = np.maximum(np.abs(ref).max(axis=1), 1e-300)
+    return float((np.abs(out - ref).max(axis=1) / denom).max())

@@ -1,0 +1,156 @@
+"""Calibration parity on the GPU: every head's window bit-for-bit against the oracle.
+
+Covers float32 and bf16 inputs, several chunks per slab and ragged chunk tails,
+K from 1 to 4196 windows, heavy ties (coarse values), signed zeros, constant heads,
+monotone heads in ascending and descending memory order (the latter makes every
+streamed value a new extreme), and the accumulate/qparams stages over batches.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import assert_bits_equal, f32, log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import kv_cache_quantization_fa3q_amd as m
+    return m
+
+
+def _host_f32(x: torch.Tensor) -> np.ndarray:
+    return x.detach().cpu().to(torch.float32).numpy()
+
+
+def _check(fa, x: torch.Tensor, ratios, name):
+    dev = torch.device("cuda:0")
+    xg = x.to(dev)
+    xf = _host_f32(x)
+    for ratio in ratios:
+        N = x.shape[0] * x.shape[2] * x.shape[3]
+        K = N - int(ratio * N) + 1
+        log(f"calibrate {name}: {x.dtype} {tuple(x.shape)} ratio={ratio} K={K}")
+        wmin, wmax = fa.fa3q_calibrate_perhead(xg, ratio)
+        torch.cuda.synchronize()
+        omin, omax = oracle.calibrate(xf, ratio)
+        assert_bits_equal(f32(wmin), omin, f"{name} win_min ratio={ratio}")
+        assert_bits_equal(f32(wmax), omax, f"{name} win_max ratio={ratio}")
+
+
+RANDOM_CASES = [
+    # name, dtype, (B, H, S, D), law, ratios
+    ("f32_ragged", torch.float32, (2, 3, 37, 12), "normal", (0.5, 0.9, 0.99, 1.0)),
+    ("f32_one_vector", torch.float32, (1, 1, 1, 4), "normal", (0.25, 0.5, 1.0)),
+    ("bf16_small", torch.bfloat16, (1, 2, 1, 8), "normal", (0.125, 0.5, 0.875)),
+    ("bf16_t3", torch.bfloat16, (3, 5, 1000, 24), "t3", (0.999, 0.9999)),
+    ("f32_multichunk", torch.float32, (1, 2, 8192, 64), "t3", (0.9999, 0.999)),
+    ("bf16_multichunk", torch.bfloat16, (4, 3, 4096, 40), "normal", (0.9999, 0.99)),
+]
+
+
+@pytest.mark.parametrize("name,dtype,shape,law,ratios", RANDOM_CASES, ids=[c[0] for c in RANDOM_CASES])
+def test_random(fa, name, dtype, shape, law, ratios):
+    sigma = synth.head_sigmas(shape[1], seed=sum(name.encode()) % 1000)
+    x = synth.activations(shape, sigma, law=law, outlier_frac=0.0005, outlier_mult=40.0, dtype=dtype,
+                          seed=7 + len(name))
+    _check(fa, x, ratios, name)
+
+
+def test_coarse_values_heavy_ties(fa):
+    rng = np.random.default_rng(5)
+    B, H, S, D = 2, 4, 700, 32
+    vals = (rng.integers(-24, 25, size=(B, H, S, D)) * 0.25).astype(np.float32)
+    vals[:, 1] = np.round(vals[:, 1] / 4)  # even coarser head
+    x = torch.from_numpy(vals).to(torch.bfloat16)
+    _check(fa, x, (0.9, 0.99, 0.999, 0.9999, 1.0), "coarse")
+    _check(fa, x.to(torch.float32), (0.99, 0.999), "coarse_f32")
+
+
+def test_special_heads(fa):
+    B, H, S, D = 2, 6, 256, 16
+    n_per_b = S * D
+    x = np.zeros((B, H, S, D), np.float32)
+    x[:, 0] = -1.5                                                  # constant head
+    zeros = np.where(np.arange(B * n_per_b) % 3 == 0, -0.0, 0.0).astype(np.float32)
+    zeros[::7] = 1e-3
+    x[:, 1] = zeros.reshape(B, S, D)                                # signed zeros
+    ramp = np.arange(B * n_per_b, dtype=np.float32) * np.float32(0.5)
+    x[:, 2] = ramp.reshape(B, S, D)                                 # ascending in memory order
+    x[:, 3] = ramp[::-1].reshape(B, S, D)                           # descending in memory order
+    x[:, 4] = 0.0                                                   # all +0 (scale 0 later)
+    x[:, 5] = -ramp[::-1].reshape(B, S, D)                          # negative descending
+    xt = torch.from_numpy(x)
+    _check(fa, xt, (0.9, 0.999, 1.0), "special_f32")
+    _check(fa, xt.to(torch.bfloat16), (0.5, 0.99, 0.9999), "special_bf16")
+
+
+def test_k4196_long_context_shape(fa):
+    # bf16 (2,2,16384,128) with t3 tails and 1e-4 outliers at +-60 sigma; ratio 0.999 -> K = 4196
+    sigma = synth.head_sigmas(2, seed=55)
+    x = synth.activations((2, 2, 16384, 128), sigma, law="t3", outlier_frac=1e-4, outlier_mult=60.0,
+                          dtype=torch.bfloat16, seed=56)
+    _check(fa, x, (0.999, 0.99999), "k4196")
+
+
+def test_batches_accumulate_and_scale(fa):
+    dev = torch.device("cuda:0")
+    H = 6
+    sigma = synth.head_sigmas(H, seed=61)
+    run_min = torch.empty(H, dtype=torch.float32, device=dev)
+    run_max = torch.empty(H, dtype=torch.float32, device=dev)
+    fa.fa3q_init_minmax(run_min, run_max)
+    omin, omax = oracle.init_running(H)
+    for bidx in range(4):
+        x = synth.activations((2, H, 512, 32), sigma, law="t3", dtype=torch.bfloat16, seed=70 + bidx)
+        log(f"accumulate batch {bidx}")
+        wmin, wmax = fa.fa3q_calibrate_perhead(x.to(dev), 0.999)
+        fa.fa3q_accumulate_minmax(run_min, run_max, wmin, wmax)
+        cmin, cmax = oracle.calibrate(_host_f32(x), 0.999)
+        omin, omax = oracle.accumulate(omin, omax, cmin, cmax)
+    scale = fa.fa3q_qparams(run_min, run_max)
+    torch.cuda.synchronize()
+    assert_bits_equal(f32(run_min), omin, "run_min")
+    assert_bits_equal(f32(run_max), omax, "run_max")
+    assert_bits_equal(f32(scale), oracle.qparams(omin, omax), "scale")
+
+
+def test_accumulate_signed_zero_and_identity(fa):
+    dev = torch.device("cuda:0")
+    a = torch.tensor([0.0, -0.0, 1.0, -2.0], device=dev)
+    b = torch.tensor([-0.0, 0.0, -1.0, 5.0], device=dev)
+    run_min = a.clone()
+    run_max = b.clone()
+    fa.fa3q_accumulate_minmax(run_min, run_max, b, a)
+    torch.cuda.synchronize()
+    omin, omax = oracle.accumulate(a.cpu().numpy(), b.cpu().numpy(), b.cpu().numpy(), a.cpu().numpy())
+    assert_bits_equal(f32(run_min), omin, "min")
+    assert_bits_equal(f32(run_max), omax, "max")
+    fa.fa3q_init_minmax(run_min, run_max)
+    torch.cuda.synchronize()
+    assert torch.isinf(run_min).all() and (run_min > 0).all()
+    assert torch.isinf(run_max).all() and (run_max < 0).all()
+
+
+def test_qparams_closed_form(fa):
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(91)
+    mn = (-np.abs(rng.standard_t(3, size=5000)) * np.exp(rng.uniform(-40, 40, size=5000))).astype(np.float32)
+    mx = (np.abs(rng.standard_t(3, size=5000)) * np.exp(rng.uniform(-40, 40, size=5000))).astype(np.float32)
+    mn[:4] = [0.0, -0.0, -127.0, -12.7]
+    mx[:4] = [0.0, -0.0, 3.0, 1.0]
+    s = fa.fa3q_qparams(torch.from_numpy(mn).to(dev), torch.from_numpy(mx).to(dev))
+    torch.cuda.synchronize()
+    assert_bits_equal(f32(s), oracle.qparams(mn, mx), "scale")
+
+
+def test_large_k_uses_more_than_64k_lds(fa):
+    # K ~ 1e4 (bf16) and K = 4097 (float32) need 100-150 KiB of LDS per workgroup
+    rng = np.random.default_rng(17)
+    x = torch.from_numpy((rng.standard_t(3, size=(2, 2, 4096, 64)) * 0.7).astype(np.float32))
+    log(f"device LDS per block: {torch.cuda.get_device_properties(0)}")
+    _check(fa, x.to(torch.bfloat16), (0.98,), "large_k_bf16")   # K = 10486
+    _check(fa, x[:, :, :64], (0.5,), "large_k_f32")               # N = 8192, K = 4097

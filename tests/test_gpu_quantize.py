@@ -77,7 +77,7 @@ def test_every_bf16_value_against_many_scales(fa):
 
 def test_exact_half_integer_quotients(fa):
     s = np.float32(0.25)
-    halves = (np.arange(-130, 130, dtype=np.float32) + np.float32(0.5)) * s  # exact in bf16
+    halves = (np.arange(-128, 128, dtype=np.float32) + np.float32(0.5)) * s  # 2n+1 <= 255: exact in bf16
     n = len(halves)
     S = (n + 15) // 16
     x = np.zeros(S * 16, np.float32)

@@ -32,11 +32,11 @@ namespace {
 
 constexpr int kChunkThreads = 256;
 constexpr int kMergeThreads = 1024;
-constexpr int kVecPerThread = 2;       // 16-byte vectors per thread per tile (chunk kernel)
+constexpr int kVecPerThread = 4;       // 16-byte vectors per thread per tile (chunk kernel)
 constexpr int kMergePerThread = 4;     // keys per thread per tile (merge kernel)
 constexpr int kMergeTile = kMergeThreads * kMergePerThread;
-constexpr int64_t kTargetChunkGroups = 2048;
-constexpr int kMinTilesPerChunk = 16;
+constexpr int64_t kTargetCUs = 256;    // MI355X compute units (sizes the chunk grid)
+constexpr int kMinTilesPerChunk = 8;
 
 // Control words at the start of dynamic LDS.
 enum Ctl : int {
@@ -69,13 +69,55 @@ struct KeyInfo<uint32_t> {
   static constexpr int kBits = 32;
 };
 
-// Order-preserving key of a bf16 pattern (low 16 bits of w).
+// Order-preserving key of a bf16 pattern (low 16 bits) and of a float32 pattern.
 __device__ __forceinline__ uint32_t key_bf16(uint32_t b) {
   return b ^ ((b & 0x8000u) ? 0xffffu : 0x8000u);
 }
 __device__ __forceinline__ uint32_t key_f32(uint32_t b) {
   return b ^ ((b & 0x80000000u) ? 0xffffffffu : 0x80000000u);
 }
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+// Keys held in dwords as they come from memory: two 16-bit keys per dword for bf16
+// input (transformed in place with packed 16-bit ops), one 32-bit key for float32.
+template <typename InT>
+struct Pack;
+template <>
+struct Pack<uint16_t> {
+  static constexpr int kPerDword = 2;
+  static constexpr uint32_t kMinInit = 0xffffffffu;
+  static constexpr uint32_t kMaxInit = 0u;
+  __device__ static uint32_t keys(uint32_t w) {  // key_bf16 on both halves
+    const s16x2 sg = __builtin_bit_cast(s16x2, w) >> (s16x2){15, 15};
+    return w ^ ((__builtin_bit_cast(uint32_t, sg) & 0x7fff7fffu) | 0x80008000u);
+  }
+  __device__ static uint32_t at(uint32_t w, int i) { return i ? (w >> 16) : (w & 0xffffu); }
+  __device__ static uint32_t pmin(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, a),
+                                                                 __builtin_bit_cast(u16x2, b)));
+  }
+  __device__ static uint32_t pmax(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                 __builtin_bit_cast(u16x2, b)));
+  }
+  __device__ static uint32_t hmin(uint32_t p) { return min(p & 0xffffu, p >> 16); }
+  __device__ static uint32_t hmax(uint32_t p) { return max(p & 0xffffu, p >> 16); }
+};
+template <>
+struct Pack<uint32_t> {
+  static constexpr int kPerDword = 1;
+  static constexpr uint32_t kMinInit = 0xffffffffu;
+  static constexpr uint32_t kMaxInit = 0u;
+  __device__ static uint32_t keys(uint32_t w) { return key_f32(w); }
+  __device__ static uint32_t at(uint32_t w, int) { return w; }
+  __device__ static uint32_t pmin(uint32_t a, uint32_t b) { return min(a, b); }
+  __device__ static uint32_t pmax(uint32_t a, uint32_t b) { return max(a, b); }
+  __device__ static uint32_t hmin(uint32_t p) { return p; }
+  __device__ static uint32_t hmax(uint32_t p) { return p; }
+};
+
 __device__ __forceinline__ float value_of_key(uint32_t k, uint16_t) {
   const uint32_t b = (k & 0x8000u) ? (k ^ 0x8000u) : (k ^ 0xffffu);
   return __uint_as_float(b << 16);
@@ -201,8 +243,8 @@ struct TailState {
   uint32_t tile;      // most entries one tile can append per side
   uint32_t base_lo;   // entries held before the current tile
   uint32_t base_hi;
-  uint32_t thr_lo;
-  uint32_t thr_hi;
+  uint32_t thr_lo;    // lo candidates: key < thr_lo
+  uint32_t thr_hi;    // hi candidates: key > thr_hi
   int parity;         // tile counter mod 3 (append-counter slot)
 
   __device__ void init() {
@@ -255,6 +297,91 @@ struct TailState {
     }
   }
 
+  // Filter one tile into both buffers.  kw holds W dwords of packed keys per thread, in
+  // groups of 4 dwords (one 16-byte vector each); vv[] marks vectors inside the chunk.
+  template <typename InT, int W>
+  __device__ __forceinline__ void filter_tile(const uint32_t (&kw)[W], const bool (&vv)[W / 4]) {
+    using P = Pack<InT>;
+    uint32_t pmn = P::kMinInit, pmx = P::kMaxInit;
+#pragma unroll
+    for (int j = 0; j < W; ++j) {
+      if (vv[j / 4]) {
+        pmn = P::pmin(pmn, kw[j]);
+        pmx = P::pmax(pmx, kw[j]);
+      }
+    }
+    const uint32_t kmin = P::hmin(pmn), kmax = P::hmax(pmx);
+    if (__ballot(kmin < thr_lo) != 0) {
+#pragma unroll
+      for (int j = 0; j < W; ++j)
+#pragma unroll
+        for (int i = 0; i < P::kPerDword; ++i) {
+          const uint32_t k = P::at(kw[j], i);
+          append_lo(vv[j / 4] && k < thr_lo, k);
+        }
+    }
+    if (__ballot(kmax > thr_hi) != 0) {
+#pragma unroll
+      for (int j = 0; j < W; ++j)
+#pragma unroll
+        for (int i = 0; i < P::kPerDword; ++i) {
+          const uint32_t k = P::at(kw[j], i);
+          append_hi(vv[j / 4] && k > thr_hi, k);
+        }
+    }
+    end_tile();
+  }
+
+  // First tile of a chunk, all of it real data: split every thread's keys into `groups`
+  // groups of consecutive keys.  The K-th smallest group minimum has at least K keys at
+  // or below it (one per group), so it is a valid lo threshold from the start and only
+  // keys at or below it enter the buffer; symmetrically for the K-th largest group
+  // maximum.  Needs NT * groups >= K and groups dividing the keys per thread.
+  template <typename InT, int W>
+  __device__ void bootstrap(const uint32_t (&kw)[W], int groups) {
+    using P = Pack<InT>;
+    constexpr int E = W * P::kPerDword;
+    const int tid = static_cast<int>(threadIdx.x);
+    const int gs = E / groups;
+    uint32_t mn = KeyInfo<KeyT>::kMax, mx = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const uint32_t k = P::at(kw[e / P::kPerDword], e % P::kPerDword);
+      mn = min(mn, k);
+      mx = max(mx, k);
+      if (((e + 1) % gs) == 0) {
+        const int g = tid * groups + (e + 1) / gs - 1;
+        lo[g] = static_cast<KeyT>(mn);
+        hi[g] = static_cast<KeyT>(mx);
+        mn = KeyInfo<KeyT>::kMax;
+        mx = 0;
+      }
+    }
+    const uint32_t n = static_cast<uint32_t>(NT * groups);
+    lds_barrier();
+    uint32_t t_lo, t_hi, less, eq;
+    block_select<KeyT, NT>(lo, n, K, ctl, t_lo, less, eq);
+    block_select<KeyT, NT>(hi, n, n - K + 1, ctl, t_hi, less, eq);
+    // block_select returns after its last barrier: nobody reads lo[]/hi[] any more
+#pragma unroll
+    for (int j = 0; j < W; ++j)
+#pragma unroll
+      for (int i = 0; i < P::kPerDword; ++i) {
+        const uint32_t k = P::at(kw[j], i);
+        append_lo(k <= t_lo, k);
+      }
+#pragma unroll
+    for (int j = 0; j < W; ++j)
+#pragma unroll
+      for (int i = 0; i < P::kPerDword; ++i) {
+        const uint32_t k = P::at(kw[j], i);
+        append_hi(k >= t_hi, k);
+      }
+    thr_lo = t_lo;
+    thr_hi = t_hi;
+    end_tile();
+  }
+
   // Leave exactly min(K, held) entries per side.
   __device__ void finish() {
     if (base_lo > K) {
@@ -270,49 +397,29 @@ struct TailState {
 
 struct ChunkArgs {
   const void* x;
-  uint32_t* counts;   // [2][H][nch]
-  void* lists;        // [2][H][nch][K] keys
+  void* lists;        // [2][H][nch][K] keys; unused slots hold keys no filter lets through
   int64_t L;          // S*D, elements per (b,h) slab
   int64_t CL;         // elements per chunk (multiple of the vector width)
   int32_t H;
   int32_t cps;        // chunks per slab
   int32_t nch;        // chunks per head = B*cps
+  int32_t boot_groups;  // groups per thread for the first-tile bootstrap (0: none)
   uint32_t K;
   uint32_t cap;
 };
 
-// One 16-byte vector of input -> up to 8 keys (8 for bf16, 4 for float32).
 template <typename InT>
-struct VecKeys;
-template <>
-struct VecKeys<uint16_t> {
-  static constexpr int kPerVec = 8;
-  __device__ static void get(const uint4& v, uint32_t (&k)[8]) {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      k[2 * i] = key_bf16(w[i] & 0xffffu);
-      k[2 * i + 1] = key_bf16(w[i] >> 16);
-    }
-  }
-};
-template <>
-struct VecKeys<uint32_t> {
-  static constexpr int kPerVec = 4;
-  __device__ static void get(const uint4& v, uint32_t (&k)[8]) {
-    k[0] = key_f32(v.x);
-    k[1] = key_f32(v.y);
-    k[2] = key_f32(v.z);
-    k[3] = key_f32(v.w);
-  }
-};
+constexpr int chunk_tile() {
+  return kChunkThreads * kVecPerThread * 4 * Pack<InT>::kPerDword;
+}
 
 template <typename InT>
-__global__ __launch_bounds__(kChunkThreads) void calib_chunk_kernel(ChunkArgs a) {
+__global__ __launch_bounds__(kChunkThreads, 4) void calib_chunk_kernel(ChunkArgs a) {
   using KeyT = InT;  // 16-bit keys for bf16 input, 32-bit keys for float32 input
   constexpr int NT = kChunkThreads;
-  constexpr int kPerVec = VecKeys<InT>::kPerVec;
-  constexpr int kTile = NT * kVecPerThread * kPerVec;
+  constexpr int kPerVec = 16 / sizeof(InT);  // elements per 16-byte vector
+  constexpr int W = kVecPerThread * 4;        // dwords per thread per tile
+  constexpr int kTile = chunk_tile<InT>();
   extern __shared__ __align__(16) unsigned char smem[];
   uint32_t* ctl = reinterpret_cast<uint32_t*>(smem);
   KeyT* lo = reinterpret_cast<KeyT*>(smem + kCtlBytes);
@@ -337,6 +444,11 @@ __global__ __launch_bounds__(kChunkThreads) void calib_chunk_kernel(ChunkArgs a)
   const int tid = static_cast<int>(threadIdx.x);
 
   uint4 cur[kVecPerThread], nxt[kVecPerThread];
+#pragma unroll
+  for (int v = 0; v < kVecPerThread; ++v) {
+    cur[v] = make_uint4(0, 0, 0, 0);
+    nxt[v] = make_uint4(0, 0, 0, 0);
+  }
   auto load_tile = [&](int64_t t0, uint4 (&dst)[kVecPerThread]) {
 #pragma unroll
     for (int v = 0; v < kVecPerThread; ++v) {
@@ -345,55 +457,42 @@ __global__ __launch_bounds__(kChunkThreads) void calib_chunk_kernel(ChunkArgs a)
     }
   };
   if (begin < end) load_tile(begin, cur);
+  bool first = true;
   for (int64_t t0 = begin; t0 < end; t0 += kTile) {
     if (t0 + kTile < end) load_tile(t0 + kTile, nxt);
-    uint32_t keys[kVecPerThread][8];
-    bool valid[kVecPerThread];
-    uint32_t kmin = KeyInfo<KeyT>::kMax, kmax = 0;
+    uint32_t kw[W];
+    bool vv[kVecPerThread];
 #pragma unroll
     for (int v = 0; v < kVecPerThread; ++v) {
-      valid[v] = t0 + static_cast<int64_t>(v * NT + tid) * kPerVec < end;
-      VecKeys<InT>::get(cur[v], keys[v]);
-      if (valid[v]) {
-#pragma unroll
-        for (int i = 0; i < kPerVec; ++i) {
-          kmin = min(kmin, keys[v][i]);
-          kmax = max(kmax, keys[v][i]);
-        }
-      }
+      kw[4 * v + 0] = Pack<InT>::keys(cur[v].x);
+      kw[4 * v + 1] = Pack<InT>::keys(cur[v].y);
+      kw[4 * v + 2] = Pack<InT>::keys(cur[v].z);
+      kw[4 * v + 3] = Pack<InT>::keys(cur[v].w);
+      vv[v] = t0 + static_cast<int64_t>(v * NT + tid) * kPerVec < end;
     }
-    if (__ballot(kmin < st.thr_lo) != 0) {
-#pragma unroll
-      for (int v = 0; v < kVecPerThread; ++v)
-#pragma unroll
-        for (int i = 0; i < kPerVec; ++i) st.append_lo(valid[v] && keys[v][i] < st.thr_lo, keys[v][i]);
+    if (first && a.boot_groups > 0 && t0 + kTile <= end) {
+      st.template bootstrap<InT, W>(kw, a.boot_groups);
+    } else {
+      st.template filter_tile<InT, W>(kw, vv);
     }
-    if (__ballot(kmax > st.thr_hi) != 0) {
-#pragma unroll
-      for (int v = 0; v < kVecPerThread; ++v)
-#pragma unroll
-        for (int i = 0; i < kPerVec; ++i) st.append_hi(valid[v] && keys[v][i] > st.thr_hi, keys[v][i]);
-    }
-    st.end_tile();
+    first = false;
 #pragma unroll
     for (int v = 0; v < kVecPerThread; ++v) cur[v] = nxt[v];
   }
   st.finish();
 
+  // Fixed-size list per chunk; slots past the held count get keys that fail both filters.
   const int64_t list = static_cast<int64_t>(h) * a.nch + c;
   const int64_t heads_lists = static_cast<int64_t>(a.H) * a.nch;
   KeyT* out_lo = static_cast<KeyT*>(a.lists) + list * a.K;
   KeyT* out_hi = static_cast<KeyT*>(a.lists) + (heads_lists + list) * a.K;
-  for (uint32_t i = tid; i < st.base_lo; i += NT) out_lo[i] = st.lo[i];
-  for (uint32_t i = tid; i < st.base_hi; i += NT) out_hi[i] = st.hi[i];
-  if (tid == 0) {
-    a.counts[list] = st.base_lo;
-    a.counts[heads_lists + list] = st.base_hi;
+  for (uint32_t i = tid; i < a.K; i += NT) {
+    out_lo[i] = i < st.base_lo ? st.lo[i] : static_cast<KeyT>(KeyInfo<KeyT>::kMax);
+    out_hi[i] = i < st.base_hi ? st.hi[i] : static_cast<KeyT>(0);
   }
 }
 
 struct MergeArgs {
-  const uint32_t* counts;
   const void* lists;
   float* win_min;
   float* win_max;
@@ -423,34 +522,26 @@ __global__ __launch_bounds__(kMergeThreads) void calib_merge_kernel(MergeArgs a)
 
   const int h = static_cast<int>(blockIdx.x);
   const int tid = static_cast<int>(threadIdx.x);
-  const int64_t heads_lists = static_cast<int64_t>(a.H) * a.nch;
-  const KeyT* lists = static_cast<const KeyT*>(a.lists);
+  const int64_t per_head = static_cast<int64_t>(a.nch) * a.K;
+  const KeyT* src_lo = static_cast<const KeyT*>(a.lists) + h * per_head;
+  const KeyT* src_hi = static_cast<const KeyT*>(a.lists) + (static_cast<int64_t>(a.H) + h) * per_head;
 
-  // Stream the chunk tails of head h through the same two-sided filter.
-  for (int c = 0; c < a.nch; ++c) {
-    const int64_t list = static_cast<int64_t>(h) * a.nch + c;
-    const uint32_t n_lo = a.counts[list];
-    const uint32_t n_hi = a.counts[heads_lists + list];
-    const KeyT* src_lo = lists + list * a.K;
-    const KeyT* src_hi = lists + (heads_lists + list) * a.K;
-    const uint32_t n = max(n_lo, n_hi);
-    for (uint32_t t0 = 0; t0 < n; t0 += kMergeTile) {
-      uint32_t klo[kMergePerThread], khi[kMergePerThread];
-      bool vlo[kMergePerThread], vhi[kMergePerThread];
+  // Stream the head's chunk tails (one flat array per side) through the same filter.
+  for (int64_t t0 = 0; t0 < per_head; t0 += kMergeTile) {
+    uint32_t klo[kMergePerThread], khi[kMergePerThread];
+    bool ev[kMergePerThread];
 #pragma unroll
-      for (int e = 0; e < kMergePerThread; ++e) {
-        const uint32_t i = t0 + e * NT + tid;
-        vlo[e] = i < n_lo;
-        vhi[e] = i < n_hi;
-        klo[e] = vlo[e] ? static_cast<uint32_t>(src_lo[i]) : 0u;
-        khi[e] = vhi[e] ? static_cast<uint32_t>(src_hi[i]) : 0u;
-      }
-#pragma unroll
-      for (int e = 0; e < kMergePerThread; ++e) st.append_lo(vlo[e] && klo[e] < st.thr_lo, klo[e]);
-#pragma unroll
-      for (int e = 0; e < kMergePerThread; ++e) st.append_hi(vhi[e] && khi[e] > st.thr_hi, khi[e]);
-      st.end_tile();
+    for (int e = 0; e < kMergePerThread; ++e) {
+      const int64_t i = t0 + e * NT + tid;
+      ev[e] = i < per_head;
+      klo[e] = ev[e] ? static_cast<uint32_t>(src_lo[i]) : KeyInfo<KeyT>::kMax;
+      khi[e] = ev[e] ? static_cast<uint32_t>(src_hi[i]) : 0u;
     }
+#pragma unroll
+    for (int e = 0; e < kMergePerThread; ++e) st.append_lo(klo[e] < st.thr_lo, klo[e]);
+#pragma unroll
+    for (int e = 0; e < kMergePerThread; ++e) st.append_hi(khi[e] > st.thr_hi, khi[e]);
+    st.end_tile();
   }
   st.finish();  // now exactly K per side (every head holds at least K values)
 
@@ -522,11 +613,11 @@ __global__ __launch_bounds__(kMergeThreads) void calib_merge_kernel(MergeArgs a)
 struct CalibPlan {
   int64_t N = 0, t = 0, K = 0;
   int64_t L = 0, CL = 0;
-  int32_t cps = 0, nch = 0;
+  int32_t cps = 0, nch = 0, boot_groups = 0;
   uint32_t cap_chunk = 0, cap_merge = 0, P = 0;
   size_t lds_chunk = 0, lds_merge = 0;
   size_t key_bytes = 0;
-  size_t counts_bytes = 0, lists_bytes = 0, total_bytes = 0;
+  size_t lists_bytes = 0, total_bytes = 0;
 };
 
 int64_t next_pow2(int64_t v) {
@@ -535,7 +626,8 @@ int64_t next_pow2(int64_t v) {
   return p;
 }
 
-// Validates everything except pointers and computes the launch plan.
+// Validates everything except pointers and computes the launch plan.  The plan depends
+// only on the arguments (not on the device), so the workspace query is reproducible.
 int make_plan(int dtype, int64_t B, int64_t H, int64_t S, int64_t D, double ratio, CalibPlan& p) {
   if (dtype != FA3Q_F32 && dtype != FA3Q_BF16) return FA3Q_ERR_DTYPE;
   if (B <= 0 || H <= 0 || S <= 0 || D <= 0) return FA3Q_ERR_SHAPE;
@@ -552,9 +644,20 @@ int make_plan(int dtype, int64_t B, int64_t H, int64_t S, int64_t D, double rati
   p.K = p.N - p.t + 1;
   if (p.K > fa3q_calibrate_max_windows(dtype)) return FA3Q_ERR_UNSUPPORTED;
 
-  const int64_t tile = static_cast<int64_t>(kChunkThreads) * kVecPerThread * vec;
-  const int64_t pairs = B * H;
-  const int64_t want = (kTargetChunkGroups + pairs - 1) / pairs;
+  p.key_bytes = dtype == FA3Q_BF16 ? 2 : 4;
+  const int64_t tile = dtype == FA3Q_BF16 ? chunk_tile<uint16_t>() : chunk_tile<uint32_t>();
+  const int E = static_cast<int>(tile / kChunkThreads);
+  p.cap_chunk = static_cast<uint32_t>(2 * p.K + tile);
+  p.cap_merge = static_cast<uint32_t>(2 * p.K + kMergeTile);
+  p.P = static_cast<uint32_t>(next_pow2(p.K));
+  p.lds_chunk = kCtlBytes + (2 * static_cast<size_t>(p.cap_chunk) + p.K) * p.key_bytes;
+  p.lds_merge = kCtlBytes + (2 * static_cast<size_t>(p.cap_merge) + p.K) * p.key_bytes;
+  if (p.lds_chunk > kLdsLimit || p.lds_merge > kLdsLimit) return FA3Q_ERR_UNSUPPORTED;
+
+  // Workgroups resident per CU (LDS-bound, at most 8) times 256 CUs: one round of chunks,
+  // each as long as possible, never shorter than kMinTilesPerChunk tiles.
+  const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(8, static_cast<int64_t>(kLdsLimit / p.lds_chunk)));
+  const int64_t want = (kTargetCUs * per_cu + B * H - 1) / (B * H);
   const int64_t most = std::max<int64_t>(1, p.L / (kMinTilesPerChunk * tile));
   p.cps = static_cast<int32_t>(std::max<int64_t>(1, std::min(want, most)));
   p.CL = (p.L + p.cps - 1) / p.cps;
@@ -563,18 +666,16 @@ int make_plan(int dtype, int64_t B, int64_t H, int64_t S, int64_t D, double rati
   if (B * p.cps > (int64_t{1} << 30) || H * B * p.cps > (int64_t{1} << 31) - 1) return FA3Q_ERR_SHAPE;
   p.nch = static_cast<int32_t>(B * p.cps);
 
-  p.key_bytes = dtype == FA3Q_BF16 ? 2 : 4;
-  p.cap_chunk = static_cast<uint32_t>(2 * p.K + tile);
-  p.cap_merge = static_cast<uint32_t>(2 * p.K + kMergeTile);
-  p.P = static_cast<uint32_t>(next_pow2(p.K));
-  p.lds_chunk = kCtlBytes + (2 * static_cast<size_t>(p.cap_chunk) + p.K) * p.key_bytes;
-  p.lds_merge = kCtlBytes + (2 * static_cast<size_t>(p.cap_merge) + p.K) * p.key_bytes;
-  if (p.lds_chunk > kLdsLimit || p.lds_merge > kLdsLimit) return FA3Q_ERR_UNSUPPORTED;
+  // First-tile bootstrap: groups per thread so that NT * groups >= K (only for K <= tile).
+  p.boot_groups = 0;
+  if (p.K <= tile) {
+    int64_t g = next_pow2((p.K + kChunkThreads - 1) / kChunkThreads);
+    if (g <= E) p.boot_groups = static_cast<int32_t>(g);
+  }
 
   const size_t lists = static_cast<size_t>(H) * p.nch;
-  p.counts_bytes = round_up(2 * lists * sizeof(uint32_t), 256);
   p.lists_bytes = round_up(2 * lists * static_cast<size_t>(p.K) * p.key_bytes, 256);
-  p.total_bytes = p.counts_bytes + p.lists_bytes;
+  p.total_bytes = p.lists_bytes;
   return FA3Q_OK;
 }
 
@@ -587,24 +688,21 @@ int launch(const void* x, int64_t H, const CalibPlan& p, float* win_min, float* 
   st = allow_dynamic_lds(reinterpret_cast<const void*>(calib_merge_kernel<KeyT>), p.lds_merge);
   if (st != FA3Q_OK) return st;
 
-  uint32_t* counts = static_cast<uint32_t*>(workspace);
-  void* lists = static_cast<char*>(workspace) + p.counts_bytes;
   ChunkArgs ca;
   ca.x = x;
-  ca.counts = counts;
-  ca.lists = lists;
+  ca.lists = workspace;
   ca.L = p.L;
   ca.CL = p.CL;
   ca.H = static_cast<int32_t>(H);
   ca.cps = p.cps;
   ca.nch = p.nch;
+  ca.boot_groups = p.boot_groups;
   ca.K = static_cast<uint32_t>(p.K);
   ca.cap = p.cap_chunk;
   hipLaunchKernelGGL(calib_chunk_kernel<InT>, dim3(static_cast<unsigned>(H * p.nch)), dim3(kChunkThreads),
                      p.lds_chunk, stream, ca);
   MergeArgs ma;
-  ma.counts = counts;
-  ma.lists = lists;
+  ma.lists = workspace;
   ma.win_min = win_min;
   ma.win_max = win_max;
   ma.H = static_cast<int32_t>(H);
@@ -623,12 +721,14 @@ int launch(const void* x, int64_t H, const CalibPlan& p, float* win_min, float* 
 using namespace fa3q;
 
 extern "C" int64_t fa3q_calibrate_max_windows(int dtype) {
-  // Both kernels keep 2*cap + K keys in LDS with cap = 2K + tile; the merge tile (4096
-  // keys) is the larger one.  Largest K whose LDS fits the 160 KiB of a gfx950 workgroup.
+  // Each kernel keeps 2*cap + K keys in LDS with cap = 2K + tile.  Largest K for which
+  // both fit the 160 KiB a gfx950 workgroup may use.
   if (dtype != FA3Q_F32 && dtype != FA3Q_BF16) return 0;
   const int64_t kb = dtype == FA3Q_BF16 ? 2 : 4;
+  const int64_t tile = std::max<int64_t>(dtype == FA3Q_BF16 ? chunk_tile<uint16_t>() : chunk_tile<uint32_t>(),
+                                         kMergeTile);
   const int64_t room = (static_cast<int64_t>(kLdsLimit) - static_cast<int64_t>(kCtlBytes)) / kb;
-  return (room - 2 * static_cast<int64_t>(kMergeTile)) / 5;
+  return (room - 2 * tile) / 5;
 }
 
 extern "C" size_t fa3q_calibrate_workspace_bytes(int dtype, int64_t B, int64_t H, int64_t S,

@@ -12,10 +12,10 @@
 //   calib_chunk_kernel   one HBM pass.  Each workgroup streams a contiguous chunk of one
 //                        head (inside one (b,h) slab) and keeps, in LDS, a candidate
 //                        buffer per side holding a superset of the chunk's K smallest
-//                        (K largest) values.  A value enters only if it beats the side's
-//                        threshold; when a buffer passes 2K entries an exact LDS radix
-//                        select cuts it back to the K extreme values and tightens the
-//                        threshold.  The chunk's exact tails go to the workspace.
+//                        (K largest) values.  A value is a candidate only if it beats the
+//                        side's threshold; when a buffer passes 2K entries an exact LDS
+//                        radix select cuts it back to the K extreme values and tightens
+//                        the threshold.  The chunk's exact tails go to the workspace.
 //   calib_merge_kernel   one workgroup per head: the same select over the chunks' tails
 //                        gives the head's exact K smallest and K largest values, a
 //                        bitonic sort orders them, and a block reduction finds the
@@ -25,36 +25,51 @@
 // 32-bit for float32), which realise the float total order with -0.0 below +0.0.
 // Ties need no special care: a tail is a multiset of key values, and dropping a value
 // equal to the K-th smallest once K values <= it are held never changes that multiset.
+//
+// Streaming filter of the chunk kernel.  Once the lo threshold is a negative value and
+// the hi threshold a non-negative one (the usual case after the first tile), the test
+// needs no key transform: among sign-magnitude patterns, "below a negative threshold"
+// is an unsigned compare of the raw bits and "above a non-negative threshold" a signed
+// one, so each dword of input costs one packed unsigned and one packed signed max.
+// Only 16-byte vectors holding a candidate are copied to a per-wave LDS stage, from
+// which the wave appends the qualifying keys; a round appends at most 64 vectors per
+// wave, so the buffers need room for one round, not for a whole tile.
 #include "fa3q_internal.hpp"
 
 namespace fa3q {
 namespace {
 
 constexpr int kChunkThreads = 256;
+constexpr int kChunkWaves = kChunkThreads / kWave;
+constexpr int kVec = 8;                // 16-byte vectors per thread per tile (chunk kernel)
+constexpr int kStageVecs = 64;         // vectors one wave stages and appends per round
 constexpr int kMergeThreads = 1024;
-constexpr int kVecPerThread = 4;       // 16-byte vectors per thread per tile (chunk kernel)
 constexpr int kMergePerThread = 4;     // keys per thread per tile (merge kernel)
 constexpr int kMergeTile = kMergeThreads * kMergePerThread;
 constexpr int64_t kTargetCUs = 256;    // MI355X compute units (sizes the chunk grid)
-constexpr int kMinTilesPerChunk = 8;
+constexpr int64_t kChunkGroupsPerCU = 4;  // chunk workgroups resident per CU (VGPR-bound)
+constexpr int kMinTilesPerChunk = 4;
 
 // Control words at the start of dynamic LDS.
 enum Ctl : int {
-  kSlotLo = 0,   // [3] per-tile append counters, lo side
+  kSlotLo = 0,   // [3] per-round append counters, lo side
   kSlotHi = 3,   // [3] hi side
-  kThrLo = 6,    // current lo threshold key: candidates are keys < thrLo
-  kThrHi = 7,    // current hi threshold key: candidates are keys > thrHi
+  kThrLo = 6,    // threshold key after the latest compaction, lo side
+  kThrHi = 7,    // hi side
   kTmpCnt = 8,
   kSelDigit = 9,
   kSelBefore = 10,
   kSelCount = 11,
   kBestLen = 12,
+  kWaveTot = 16,  // [3][kChunkWaves] staged-vector totals per wave, one set per round slot
   kHist = 64,    // [256] radix histogram
   kWaveScratch = 64 + 256,  // [2 * 16] per-wave (length, index) pairs
   kCtlWords = 64 + 256 + 32
 };
 constexpr size_t kCtlBytes = 2048;
 static_assert(kCtlWords * 4 <= kCtlBytes, "control block too small");
+static_assert(kWaveTot + 3 * kChunkWaves <= kHist, "wave totals overlap the histogram");
+constexpr size_t kStageBytes = static_cast<size_t>(kChunkWaves) * kStageVecs * 16;
 
 template <typename KeyT>
 struct KeyInfo;
@@ -69,53 +84,65 @@ struct KeyInfo<uint32_t> {
   static constexpr int kBits = 32;
 };
 
-// Order-preserving key of a bf16 pattern (low 16 bits) and of a float32 pattern.
-__device__ __forceinline__ uint32_t key_bf16(uint32_t b) {
-  return b ^ ((b & 0x8000u) ? 0xffffu : 0x8000u);
-}
-__device__ __forceinline__ uint32_t key_f32(uint32_t b) {
-  return b ^ ((b & 0x80000000u) ? 0xffffffffu : 0x80000000u);
-}
-
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// Keys held in dwords as they come from memory: two 16-bit keys per dword for bf16
-// input (transformed in place with packed 16-bit ops), one 32-bit key for float32.
+// Per input type: keys packed in dwords as they come from memory, the raw-bit maxima of
+// the sign-split filter, and the limits that make that filter exact.
+//   key(v)  = bits ^ (sign ? all-ones : sign-bit)       (order-preserving, unsigned)
+//   Lim     signed type wide enough for key - 1 and key + 1
 template <typename InT>
-struct Pack;
+struct In;
+
 template <>
-struct Pack<uint16_t> {
+struct In<uint16_t> {  // bf16 patterns, two per dword
+  using KeyT = uint16_t;
+  using Lim = int32_t;
   static constexpr int kPerDword = 2;
-  static constexpr uint32_t kMinInit = 0xffffffffu;
-  static constexpr uint32_t kMaxInit = 0u;
-  __device__ static uint32_t keys(uint32_t w) {  // key_bf16 on both halves
+  static constexpr Lim kKeyZero = 0x8000;  // key of +0.0: smaller keys are negative values or -0.0
+  __device__ static uint32_t keys(uint32_t w) {
     const s16x2 sg = __builtin_bit_cast(s16x2, w) >> (s16x2){15, 15};
     return w ^ ((__builtin_bit_cast(uint32_t, sg) & 0x7fff7fffu) | 0x80008000u);
   }
   __device__ static uint32_t at(uint32_t w, int i) { return i ? (w >> 16) : (w & 0xffffu); }
-  __device__ static uint32_t pmin(uint32_t a, uint32_t b) {
+  __device__ static uint32_t umin(uint32_t a, uint32_t b) {
     return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, a),
                                                                  __builtin_bit_cast(u16x2, b)));
   }
-  __device__ static uint32_t pmax(uint32_t a, uint32_t b) {
+  __device__ static uint32_t umax(uint32_t a, uint32_t b) {
     return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
                                                                  __builtin_bit_cast(u16x2, b)));
   }
-  __device__ static uint32_t hmin(uint32_t p) { return min(p & 0xffffu, p >> 16); }
-  __device__ static uint32_t hmax(uint32_t p) { return max(p & 0xffffu, p >> 16); }
+  __device__ static uint32_t smax(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(s16x2, a),
+                                                                 __builtin_bit_cast(s16x2, b)));
+  }
+  __device__ static Lim ulane_min(uint32_t p) { return static_cast<Lim>(min(p & 0xffffu, p >> 16)); }
+  __device__ static Lim ulane_max(uint32_t p) { return static_cast<Lim>(max(p & 0xffffu, p >> 16)); }
+  __device__ static Lim slane_max(uint32_t p) {
+    return max(static_cast<Lim>(static_cast<int16_t>(p & 0xffffu)), static_cast<Lim>(static_cast<int32_t>(p) >> 16));
+  }
 };
+
 template <>
-struct Pack<uint32_t> {
+struct In<uint32_t> {  // float32 patterns, one per dword
+  using KeyT = uint32_t;
+  using Lim = int64_t;
   static constexpr int kPerDword = 1;
-  static constexpr uint32_t kMinInit = 0xffffffffu;
-  static constexpr uint32_t kMaxInit = 0u;
-  __device__ static uint32_t keys(uint32_t w) { return key_f32(w); }
+  static constexpr Lim kKeyZero = 0x80000000ll;
+  __device__ static uint32_t keys(uint32_t w) {
+    return w ^ ((w & 0x80000000u) ? 0xffffffffu : 0x80000000u);
+  }
   __device__ static uint32_t at(uint32_t w, int) { return w; }
-  __device__ static uint32_t pmin(uint32_t a, uint32_t b) { return min(a, b); }
-  __device__ static uint32_t pmax(uint32_t a, uint32_t b) { return max(a, b); }
-  __device__ static uint32_t hmin(uint32_t p) { return p; }
-  __device__ static uint32_t hmax(uint32_t p) { return p; }
+  __device__ static uint32_t umin(uint32_t a, uint32_t b) { return min(a, b); }
+  __device__ static uint32_t umax(uint32_t a, uint32_t b) { return max(a, b); }
+  __device__ static uint32_t smax(uint32_t a, uint32_t b) {
+    return static_cast<uint32_t>(max(static_cast<int32_t>(a), static_cast<int32_t>(b)));
+  }
+  __device__ static Lim ulane_min(uint32_t p) { return static_cast<Lim>(p); }
+  __device__ static Lim ulane_max(uint32_t p) { return static_cast<Lim>(p); }
+  __device__ static Lim slane_max(uint32_t p) { return static_cast<Lim>(static_cast<int32_t>(p)); }
 };
 
 __device__ __forceinline__ float value_of_key(uint32_t k, uint16_t) {
@@ -125,6 +152,11 @@ __device__ __forceinline__ float value_of_key(uint32_t k, uint16_t) {
 __device__ __forceinline__ float value_of_key(uint32_t k, uint32_t) {
   const uint32_t b = (k & 0x80000000u) ? (k ^ 0x80000000u) : ~k;
   return __uint_as_float(b);
+}
+
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
 }
 
 // Wave-aggregated append of `key` (where pred holds) at buf[*cnt ...]; all lanes of the
@@ -137,9 +169,21 @@ __device__ __forceinline__ void wave_append(bool pred, uint32_t key, KeyT* buf, 
   uint32_t base = 0;
   if (lane_id() == leader) base = atomicAdd(cnt, static_cast<uint32_t>(__popcll(m)));
   base = __shfl(base, leader);
-  const uint32_t below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
-                                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
-  if (pred) buf[base + below] = static_cast<KeyT>(key);
+  if (pred) buf[base + lanes_below(m)] = static_cast<KeyT>(key);
+}
+
+// Same for two keys per lane with one counter update; every lane of the wave is active.
+template <typename KeyT>
+__device__ __forceinline__ void wave_append2(bool p0, uint32_t k0, bool p1, uint32_t k1, KeyT* buf,
+                                             uint32_t* cnt) {
+  const uint64_t m0 = __ballot(p0), m1 = __ballot(p1);
+  if ((m0 | m1) == 0) return;
+  const uint32_t c0 = static_cast<uint32_t>(__popcll(m0));
+  uint32_t base = 0;
+  if (lane_id() == 0) base = atomicAdd(cnt, c0 + static_cast<uint32_t>(__popcll(m1)));
+  base = __builtin_amdgcn_readfirstlane(base);
+  if (p0) buf[base + lanes_below(m0)] = static_cast<KeyT>(k0);
+  if (p1) buf[base + c0 + lanes_below(m1)] = static_cast<KeyT>(k1);
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave.
@@ -240,12 +284,12 @@ struct TailState {
   uint32_t* ctl;
   uint32_t K;
   uint32_t cap;       // entries per side buffer
-  uint32_t tile;      // most entries one tile can append per side
-  uint32_t base_lo;   // entries held before the current tile
+  uint32_t room;      // most entries one round can append per side
+  uint32_t base_lo;   // entries held before the current round
   uint32_t base_hi;
   uint32_t thr_lo;    // lo candidates: key < thr_lo
   uint32_t thr_hi;    // hi candidates: key > thr_hi
-  int parity;         // tile counter mod 3 (append-counter slot)
+  int parity;         // round counter mod 3 (append-counter slot)
 
   __device__ void init() {
     const int tid = static_cast<int>(threadIdx.x);
@@ -271,115 +315,33 @@ struct TailState {
     wave_append<KeyT>(pred, key, hi + base_hi, &ctl[kSlotHi + parity]);
   }
 
-  // After every thread appended its share of one tile.  Three rotating counter slots let
-  // a single barrier per tile separate "read this tile's count" from the next tile's
-  // appends: slot p is filled in tile i, read after barrier i, and cleared after
-  // barrier i+1 (when every thread has read it), before tile i+3 uses it again.
-  __device__ void end_tile() {
+  // After every thread appended its share of one round.  Three rotating counter slots let
+  // a single barrier per round separate "read this round's count" from the next round's
+  // appends: slot p is filled in round i, read after barrier i, and cleared after
+  // barrier i+1 (when every thread has read it), before round i+3 uses it again.
+  // Returns the slot that was current before the barrier.
+  __device__ int end_round() {
     lds_barrier();
-    base_lo += ctl[kSlotLo + parity];
-    base_hi += ctl[kSlotHi + parity];
-    const int clear = parity == 0 ? 2 : parity - 1;
+    const int cur = parity;
+    base_lo += ctl[kSlotLo + cur];
+    base_hi += ctl[kSlotHi + cur];
+    const int clear = cur == 0 ? 2 : cur - 1;
     if (threadIdx.x == 0) {
       ctl[kSlotLo + clear] = 0;
       ctl[kSlotHi + clear] = 0;
     }
-    parity = parity == 2 ? 0 : parity + 1;
-    if (base_lo > cap - tile) {
+    parity = cur == 2 ? 0 : cur + 1;
+    if (base_lo > cap - room) {
       compact<KeyT, NT, true>(lo, base_lo, K, tmp, ctl);
       base_lo = K;
       thr_lo = ctl[kThrLo];
     }
-    if (base_hi > cap - tile) {
+    if (base_hi > cap - room) {
       compact<KeyT, NT, false>(hi, base_hi, K, tmp, ctl);
       base_hi = K;
       thr_hi = ctl[kThrHi];
     }
-  }
-
-  // Filter one tile into both buffers.  kw holds W dwords of packed keys per thread, in
-  // groups of 4 dwords (one 16-byte vector each); vv[] marks vectors inside the chunk.
-  template <typename InT, int W>
-  __device__ __forceinline__ void filter_tile(const uint32_t (&kw)[W], const bool (&vv)[W / 4]) {
-    using P = Pack<InT>;
-    uint32_t pmn = P::kMinInit, pmx = P::kMaxInit;
-#pragma unroll
-    for (int j = 0; j < W; ++j) {
-      if (vv[j / 4]) {
-        pmn = P::pmin(pmn, kw[j]);
-        pmx = P::pmax(pmx, kw[j]);
-      }
-    }
-    const uint32_t kmin = P::hmin(pmn), kmax = P::hmax(pmx);
-    if (__ballot(kmin < thr_lo) != 0) {
-#pragma unroll
-      for (int j = 0; j < W; ++j)
-#pragma unroll
-        for (int i = 0; i < P::kPerDword; ++i) {
-          const uint32_t k = P::at(kw[j], i);
-          append_lo(vv[j / 4] && k < thr_lo, k);
-        }
-    }
-    if (__ballot(kmax > thr_hi) != 0) {
-#pragma unroll
-      for (int j = 0; j < W; ++j)
-#pragma unroll
-        for (int i = 0; i < P::kPerDword; ++i) {
-          const uint32_t k = P::at(kw[j], i);
-          append_hi(vv[j / 4] && k > thr_hi, k);
-        }
-    }
-    end_tile();
-  }
-
-  // First tile of a chunk, all of it real data: split every thread's keys into `groups`
-  // groups of consecutive keys.  The K-th smallest group minimum has at least K keys at
-  // or below it (one per group), so it is a valid lo threshold from the start and only
-  // keys at or below it enter the buffer; symmetrically for the K-th largest group
-  // maximum.  Needs NT * groups >= K and groups dividing the keys per thread.
-  template <typename InT, int W>
-  __device__ void bootstrap(const uint32_t (&kw)[W], int groups) {
-    using P = Pack<InT>;
-    constexpr int E = W * P::kPerDword;
-    const int tid = static_cast<int>(threadIdx.x);
-    const int gs = E / groups;
-    uint32_t mn = KeyInfo<KeyT>::kMax, mx = 0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const uint32_t k = P::at(kw[e / P::kPerDword], e % P::kPerDword);
-      mn = min(mn, k);
-      mx = max(mx, k);
-      if (((e + 1) % gs) == 0) {
-        const int g = tid * groups + (e + 1) / gs - 1;
-        lo[g] = static_cast<KeyT>(mn);
-        hi[g] = static_cast<KeyT>(mx);
-        mn = KeyInfo<KeyT>::kMax;
-        mx = 0;
-      }
-    }
-    const uint32_t n = static_cast<uint32_t>(NT * groups);
-    lds_barrier();
-    uint32_t t_lo, t_hi, less, eq;
-    block_select<KeyT, NT>(lo, n, K, ctl, t_lo, less, eq);
-    block_select<KeyT, NT>(hi, n, n - K + 1, ctl, t_hi, less, eq);
-    // block_select returns after its last barrier: nobody reads lo[]/hi[] any more
-#pragma unroll
-    for (int j = 0; j < W; ++j)
-#pragma unroll
-      for (int i = 0; i < P::kPerDword; ++i) {
-        const uint32_t k = P::at(kw[j], i);
-        append_lo(k <= t_lo, k);
-      }
-#pragma unroll
-    for (int j = 0; j < W; ++j)
-#pragma unroll
-      for (int i = 0; i < P::kPerDword; ++i) {
-        const uint32_t k = P::at(kw[j], i);
-        append_hi(k >= t_hi, k);
-      }
-    thr_lo = t_lo;
-    thr_hi = t_hi;
-    end_tile();
+    return cur;
   }
 
   // Leave exactly min(K, held) entries per side.
@@ -403,26 +365,58 @@ struct ChunkArgs {
   int32_t H;
   int32_t cps;        // chunks per slab
   int32_t nch;        // chunks per head = B*cps
-  int32_t boot_groups;  // groups per thread for the first-tile bootstrap (0: none)
+  int32_t boot;       // 1: seed the thresholds from the first tile's per-thread extremes
   uint32_t K;
   uint32_t cap;
 };
 
 template <typename InT>
 constexpr int chunk_tile() {
-  return kChunkThreads * kVecPerThread * 4 * Pack<InT>::kPerDword;
+  return kChunkThreads * kVec * (16 / static_cast<int>(sizeof(InT)));
+}
+template <typename InT>
+constexpr uint32_t chunk_room() {  // keys one round appends per side at most
+  return static_cast<uint32_t>(kChunkWaves * kStageVecs * (16 / static_cast<int>(sizeof(InT))));
+}
+
+// One thread's 16-byte vector holds a candidate: some key < lo_lim or > hi_lim.
+template <typename InT>
+__device__ __forceinline__ bool vec_flag_keys(const u32x4& x, typename In<InT>::Lim lo_lim,
+                                              typename In<InT>::Lim hi_lim) {
+  using T = In<InT>;
+  const uint32_t k0 = T::keys(x.x), k1 = T::keys(x.y), k2 = T::keys(x.z), k3 = T::keys(x.w);
+  const uint32_t mn = T::umin(T::umin(k0, k1), T::umin(k2, k3));
+  const uint32_t mx = T::umax(T::umax(k0, k1), T::umax(k2, k3));
+  return T::ulane_min(mn) < lo_lim || T::ulane_max(mx) > hi_lim;
+}
+// Same test on raw bits; valid when lo_lim <= key(+0) and hi_lim >= key(+0) - 1, with
+// rlo = key_max - lo_lim and rhi = hi_lim - key(+0) (see the file header).
+template <typename InT>
+__device__ __forceinline__ bool vec_flag_raw(const u32x4& x, typename In<InT>::Lim rlo,
+                                             typename In<InT>::Lim rhi) {
+  using T = In<InT>;
+  const uint32_t mu = T::umax(T::umax(x.x, x.y), T::umax(x.z, x.w));
+  const uint32_t ms = T::smax(T::smax(x.x, x.y), T::smax(x.z, x.w));
+  return T::ulane_max(mu) > rlo || T::slane_max(ms) > rhi;
 }
 
 template <typename InT>
-__global__ __launch_bounds__(kChunkThreads, 4) void calib_chunk_kernel(ChunkArgs a) {
-  using KeyT = InT;  // 16-bit keys for bf16 input, 32-bit keys for float32 input
+__global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void calib_chunk_kernel(ChunkArgs a) {
+  using T = In<InT>;
+  using KeyT = typename T::KeyT;
+  using Lim = typename T::Lim;
   constexpr int NT = kChunkThreads;
   constexpr int kPerVec = 16 / sizeof(InT);  // elements per 16-byte vector
-  constexpr int W = kVecPerThread * 4;        // dwords per thread per tile
   constexpr int kTile = chunk_tile<InT>();
+  constexpr Lim kKeyMax = static_cast<Lim>(KeyInfo<KeyT>::kMax);
   extern __shared__ __align__(16) unsigned char smem[];
   uint32_t* ctl = reinterpret_cast<uint32_t*>(smem);
-  KeyT* lo = reinterpret_cast<KeyT*>(smem + kCtlBytes);
+  const int tid = static_cast<int>(threadIdx.x);
+  const int wave = tid / kWave;
+  const int lane = lane_id();
+  u32x4* stage = reinterpret_cast<u32x4*>(smem + kCtlBytes) + wave * kStageVecs;
+  const uint32_t* stage_dw = reinterpret_cast<const uint32_t*>(stage);
+  KeyT* lo = reinterpret_cast<KeyT*>(smem + kCtlBytes + kStageBytes);
 
   TailState<KeyT, NT> st;
   st.lo = lo;
@@ -431,7 +425,7 @@ __global__ __launch_bounds__(kChunkThreads, 4) void calib_chunk_kernel(ChunkArgs
   st.ctl = ctl;
   st.K = a.K;
   st.cap = a.cap;
-  st.tile = kTile;
+  st.room = chunk_room<InT>();
   st.init();
 
   const int h = static_cast<int>(blockIdx.x) / a.nch;
@@ -441,43 +435,123 @@ __global__ __launch_bounds__(kChunkThreads, 4) void calib_chunk_kernel(ChunkArgs
   const InT* slab = static_cast<const InT*>(a.x) + (static_cast<int64_t>(b) * a.H + h) * a.L;
   const int64_t begin = static_cast<int64_t>(part) * a.CL;
   const int64_t end = min(a.L, begin + a.CL);
-  const int tid = static_cast<int>(threadIdx.x);
 
-  uint4 cur[kVecPerThread], nxt[kVecPerThread];
+  u32x4 x[kVec];
+  // Unconditional loads (a vector past the chunk end re-reads the chunk's last vector and
+  // is masked out), so no load has to merge with the register's previous contents.
+  const int64_t last = end - kPerVec;
+  auto load_tile = [&](int64_t t0) {
 #pragma unroll
-  for (int v = 0; v < kVecPerThread; ++v) {
-    cur[v] = make_uint4(0, 0, 0, 0);
-    nxt[v] = make_uint4(0, 0, 0, 0);
-  }
-  auto load_tile = [&](int64_t t0, uint4 (&dst)[kVecPerThread]) {
-#pragma unroll
-    for (int v = 0; v < kVecPerThread; ++v) {
-      const int64_t e = t0 + static_cast<int64_t>(v * NT + tid) * kPerVec;
-      if (e < end) dst[v] = *reinterpret_cast<const uint4*>(slab + e);
+    for (int v = 0; v < kVec; ++v) {
+      const int64_t e = min(t0 + static_cast<int64_t>(v * NT + tid) * kPerVec, last);
+      x[v] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(slab + e));
     }
   };
-  if (begin < end) load_tile(begin, cur);
+
+  // Candidate limits: key < lo_lim or key > hi_lim (nothing held yet: every key).
+  Lim lo_lim = kKeyMax + 1, hi_lim = -1;
+  if (begin < end) load_tile(begin);
   bool first = true;
   for (int64_t t0 = begin; t0 < end; t0 += kTile) {
-    if (t0 + kTile < end) load_tile(t0 + kTile, nxt);
-    uint32_t kw[W];
-    bool vv[kVecPerThread];
+    bool vv[kVec];
 #pragma unroll
-    for (int v = 0; v < kVecPerThread; ++v) {
-      kw[4 * v + 0] = Pack<InT>::keys(cur[v].x);
-      kw[4 * v + 1] = Pack<InT>::keys(cur[v].y);
-      kw[4 * v + 2] = Pack<InT>::keys(cur[v].z);
-      kw[4 * v + 3] = Pack<InT>::keys(cur[v].w);
-      vv[v] = t0 + static_cast<int64_t>(v * NT + tid) * kPerVec < end;
-    }
-    if (first && a.boot_groups > 0 && t0 + kTile <= end) {
-      st.template bootstrap<InT, W>(kw, a.boot_groups);
-    } else {
-      st.template filter_tile<InT, W>(kw, vv);
+    for (int v = 0; v < kVec; ++v) vv[v] = t0 + static_cast<int64_t>(v * NT + tid) * kPerVec < end;
+    Lim boot_lo = kKeyMax + 1, boot_hi = -1;
+    if (first && a.boot && t0 + kTile <= end) {
+      // The K-th smallest of the NT per-thread minima has at least K keys at or below it
+      // (one per thread), so it bounds the chunk's K-th smallest key; symmetrically for
+      // the maxima.  Keys at the bound itself are candidates in this tile only.
+      uint32_t mn = KeyInfo<KeyT>::kMax, mx = 0;
+#pragma unroll
+      for (int v = 0; v < kVec; ++v) {
+        const uint32_t k0 = T::keys(x[v].x), k1 = T::keys(x[v].y), k2 = T::keys(x[v].z), k3 = T::keys(x[v].w);
+        mn = min(mn, static_cast<uint32_t>(T::ulane_min(T::umin(T::umin(k0, k1), T::umin(k2, k3)))));
+        mx = max(mx, static_cast<uint32_t>(T::ulane_max(T::umax(T::umax(k0, k1), T::umax(k2, k3)))));
+      }
+      st.tmp[tid] = static_cast<KeyT>(mn);
+      st.tmp[NT + tid] = static_cast<KeyT>(mx);
+      lds_barrier();
+      uint32_t t_lo, t_hi, less, eq;
+      block_select<KeyT, NT>(st.tmp, NT, a.K, ctl, t_lo, less, eq);
+      block_select<KeyT, NT>(st.tmp + NT, NT, NT - a.K + 1, ctl, t_hi, less, eq);
+      boot_lo = static_cast<Lim>(t_lo);
+      boot_hi = static_cast<Lim>(t_hi);
+      lo_lim = boot_lo + 1;
+      hi_lim = boot_hi - 1;
     }
     first = false;
+
+    bool f[kVec];
+    if (lo_lim <= T::kKeyZero && hi_lim >= T::kKeyZero - 1) {
+      const Lim rlo = kKeyMax - lo_lim, rhi = hi_lim - T::kKeyZero;
 #pragma unroll
-    for (int v = 0; v < kVecPerThread; ++v) cur[v] = nxt[v];
+      for (int v = 0; v < kVec; ++v) f[v] = vv[v] && vec_flag_raw<InT>(x[v], rlo, rhi);
+    } else {
+#pragma unroll
+      for (int v = 0; v < kVec; ++v) f[v] = vv[v] && vec_flag_keys<InT>(x[v], lo_lim, hi_lim);
+    }
+    uint64_t m[kVec];
+    uint32_t off[kVec];
+    uint32_t tot = 0;
+#pragma unroll
+    for (int v = 0; v < kVec; ++v) {
+      m[v] = __ballot(f[v]);
+      off[v] = tot;
+      tot += static_cast<uint32_t>(__popcll(m[v]));
+    }
+    if (lane == 0) ctl[kWaveTot + st.parity * kChunkWaves + wave] = tot;
+
+    const int64_t tn = t0 + kTile;
+    uint32_t rounds = 1;
+    for (uint32_t r = 0; r < rounds; ++r) {
+      const uint32_t r0 = r * kStageVecs;
+      if (tot > r0) {
+        // stage this round's vectors: the wave's flagged vectors ranked r0 .. r0+63
+#pragma unroll
+        for (int v = 0; v < kVec; ++v) {
+          if (m[v] != 0) {
+            const uint32_t rank = off[v] + lanes_below(m[v]);
+            if (f[v] && rank >= r0 && rank < r0 + kStageVecs) stage[rank - r0] = x[v];
+          }
+        }
+        // the registers are free once the last round of this wave is staged
+        if (tot <= r0 + kStageVecs && tn < end) load_tile(tn);
+        __asm__ volatile("" ::: "memory");  // stage writes before the reads below (same wave)
+        const uint32_t dwords = min(tot - r0, static_cast<uint32_t>(kStageVecs)) * 4;
+        for (uint32_t j0 = 0; j0 < dwords; j0 += kWave) {
+          const uint32_t j = j0 + lane;
+          const bool ok = j < dwords;
+          const uint32_t w = T::keys(ok ? stage_dw[j] : 0u);
+          if constexpr (T::kPerDword == 2) {
+            const Lim k0 = static_cast<Lim>(w & 0xffffu), k1 = static_cast<Lim>(w >> 16);
+            wave_append2<KeyT>(ok && k0 < lo_lim, w & 0xffffu, ok && k1 < lo_lim, w >> 16,
+                               st.lo + st.base_lo, &ctl[kSlotLo + st.parity]);
+            wave_append2<KeyT>(ok && k0 > hi_lim, w & 0xffffu, ok && k1 > hi_lim, w >> 16,
+                               st.hi + st.base_hi, &ctl[kSlotHi + st.parity]);
+          } else {
+            const Lim k = static_cast<Lim>(w);
+            wave_append2<KeyT>(ok && k < lo_lim, w, false, 0u, st.lo + st.base_lo, &ctl[kSlotLo + st.parity]);
+            wave_append2<KeyT>(ok && k > hi_lim, w, false, 0u, st.hi + st.base_hi, &ctl[kSlotHi + st.parity]);
+          }
+        }
+        __asm__ volatile("" ::: "memory");
+      } else if (r == 0 && tn < end) {
+        load_tile(tn);
+      }
+      const uint32_t thr_lo0 = st.thr_lo, thr_hi0 = st.thr_hi;
+      const int slot = st.end_round();
+      if (r == 0) {
+        uint32_t most = 0;
+#pragma unroll
+        for (int w = 0; w < kChunkWaves; ++w) most = max(most, ctl[kWaveTot + slot * kChunkWaves + w]);
+        rounds = (most + kStageVecs - 1) / kStageVecs;
+      }
+      if (st.thr_lo != thr_lo0) lo_lim = min(lo_lim, static_cast<Lim>(st.thr_lo));
+      if (st.thr_hi != thr_hi0) hi_lim = max(hi_lim, static_cast<Lim>(st.thr_hi));
+    }
+    // after the bootstrap tile the buffers hold at least K keys at or beyond the bounds
+    lo_lim = min(lo_lim, boot_lo);
+    hi_lim = max(hi_lim, boot_hi);
   }
   st.finish();
 
@@ -517,7 +591,7 @@ __global__ __launch_bounds__(kMergeThreads) void calib_merge_kernel(MergeArgs a)
   st.ctl = ctl;
   st.K = a.K;
   st.cap = a.cap;
-  st.tile = kMergeTile;
+  st.room = kMergeTile;
   st.init();
 
   const int h = static_cast<int>(blockIdx.x);
@@ -541,7 +615,7 @@ __global__ __launch_bounds__(kMergeThreads) void calib_merge_kernel(MergeArgs a)
     for (int e = 0; e < kMergePerThread; ++e) st.append_lo(klo[e] < st.thr_lo, klo[e]);
 #pragma unroll
     for (int e = 0; e < kMergePerThread; ++e) st.append_hi(khi[e] > st.thr_hi, khi[e]);
-    st.end_tile();
+    st.end_round();
   }
   st.finish();  // now exactly K per side (every head holds at least K values)
 
@@ -613,7 +687,7 @@ __global__ __launch_bounds__(kMergeThreads) void calib_merge_kernel(MergeArgs a)
 struct CalibPlan {
   int64_t N = 0, t = 0, K = 0;
   int64_t L = 0, CL = 0;
-  int32_t cps = 0, nch = 0, boot_groups = 0;
+  int32_t cps = 0, nch = 0, boot = 0;
   uint32_t cap_chunk = 0, cap_merge = 0, P = 0;
   size_t lds_chunk = 0, lds_merge = 0;
   size_t key_bytes = 0;
@@ -646,17 +720,21 @@ int make_plan(int dtype, int64_t B, int64_t H, int64_t S, int64_t D, double rati
 
   p.key_bytes = dtype == FA3Q_BF16 ? 2 : 4;
   const int64_t tile = dtype == FA3Q_BF16 ? chunk_tile<uint16_t>() : chunk_tile<uint32_t>();
-  const int E = static_cast<int>(tile / kChunkThreads);
-  p.cap_chunk = static_cast<uint32_t>(2 * p.K + tile);
+  const int64_t room = dtype == FA3Q_BF16 ? chunk_room<uint16_t>() : chunk_room<uint32_t>();
+  // First-tile bootstrap selects the K-th of kChunkThreads per-thread extremes: K <= threads.
+  p.boot = p.K <= kChunkThreads ? 1 : 0;
+  const size_t tmp_keys = std::max<size_t>(static_cast<size_t>(p.K), p.boot ? 2 * kChunkThreads : 0);
+  p.cap_chunk = static_cast<uint32_t>(2 * p.K + room);
   p.cap_merge = static_cast<uint32_t>(2 * p.K + kMergeTile);
   p.P = static_cast<uint32_t>(next_pow2(p.K));
-  p.lds_chunk = kCtlBytes + (2 * static_cast<size_t>(p.cap_chunk) + p.K) * p.key_bytes;
+  p.lds_chunk = kCtlBytes + kStageBytes + (2 * static_cast<size_t>(p.cap_chunk) + tmp_keys) * p.key_bytes;
   p.lds_merge = kCtlBytes + (2 * static_cast<size_t>(p.cap_merge) + p.K) * p.key_bytes;
   if (p.lds_chunk > kLdsLimit || p.lds_merge > kLdsLimit) return FA3Q_ERR_UNSUPPORTED;
 
-  // Workgroups resident per CU (LDS-bound, at most 8) times 256 CUs: one round of chunks,
-  // each as long as possible, never shorter than kMinTilesPerChunk tiles.
-  const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(8, static_cast<int64_t>(kLdsLimit / p.lds_chunk)));
+  // Workgroups resident per CU (bound by LDS and by registers) times 256 CUs: one round of
+  // chunks, each as long as possible, never shorter than kMinTilesPerChunk tiles.
+  const int64_t per_cu = std::max<int64_t>(
+      1, std::min<int64_t>(kChunkGroupsPerCU, static_cast<int64_t>(kLdsLimit / p.lds_chunk)));
   const int64_t want = (kTargetCUs * per_cu + B * H - 1) / (B * H);
   const int64_t most = std::max<int64_t>(1, p.L / (kMinTilesPerChunk * tile));
   p.cps = static_cast<int32_t>(std::max<int64_t>(1, std::min(want, most)));
@@ -665,13 +743,6 @@ int make_plan(int dtype, int64_t B, int64_t H, int64_t S, int64_t D, double rati
   p.cps = static_cast<int32_t>((p.L + p.CL - 1) / p.CL);
   if (B * p.cps > (int64_t{1} << 30) || H * B * p.cps > (int64_t{1} << 31) - 1) return FA3Q_ERR_SHAPE;
   p.nch = static_cast<int32_t>(B * p.cps);
-
-  // First-tile bootstrap: groups per thread so that NT * groups >= K (only for K <= tile).
-  p.boot_groups = 0;
-  if (p.K <= tile) {
-    int64_t g = next_pow2((p.K + kChunkThreads - 1) / kChunkThreads);
-    if (g <= E) p.boot_groups = static_cast<int32_t>(g);
-  }
 
   const size_t lists = static_cast<size_t>(H) * p.nch;
   p.lists_bytes = round_up(2 * lists * static_cast<size_t>(p.K) * p.key_bytes, 256);
@@ -696,7 +767,7 @@ int launch(const void* x, int64_t H, const CalibPlan& p, float* win_min, float* 
   ca.H = static_cast<int32_t>(H);
   ca.cps = p.cps;
   ca.nch = p.nch;
-  ca.boot_groups = p.boot_groups;
+  ca.boot = p.boot;
   ca.K = static_cast<uint32_t>(p.K);
   ca.cap = p.cap_chunk;
   hipLaunchKernelGGL(calib_chunk_kernel<InT>, dim3(static_cast<unsigned>(H * p.nch)), dim3(kChunkThreads),
@@ -721,14 +792,17 @@ int launch(const void* x, int64_t H, const CalibPlan& p, float* win_min, float* 
 using namespace fa3q;
 
 extern "C" int64_t fa3q_calibrate_max_windows(int dtype) {
-  // Each kernel keeps 2*cap + K keys in LDS with cap = 2K + tile.  Largest K for which
-  // both fit the 160 KiB a gfx950 workgroup may use.
+  // The chunk kernel keeps 2*cap + K keys (cap = 2K + one round of appends) after its
+  // control block and stage; the merge kernel 2*cap + K keys (cap = 2K + one merge tile)
+  // after its control block.  Largest K for which both fit the 160 KiB a gfx950
+  // workgroup may use.
   if (dtype != FA3Q_F32 && dtype != FA3Q_BF16) return 0;
   const int64_t kb = dtype == FA3Q_BF16 ? 2 : 4;
-  const int64_t tile = std::max<int64_t>(dtype == FA3Q_BF16 ? chunk_tile<uint16_t>() : chunk_tile<uint32_t>(),
-                                         kMergeTile);
-  const int64_t room = (static_cast<int64_t>(kLdsLimit) - static_cast<int64_t>(kCtlBytes)) / kb;
-  return (room - 2 * tile) / 5;
+  const int64_t round = dtype == FA3Q_BF16 ? chunk_room<uint16_t>() : chunk_room<uint32_t>();
+  const int64_t lds = static_cast<int64_t>(kLdsLimit);
+  const int64_t chunk = (lds - static_cast<int64_t>(kCtlBytes + kStageBytes) - 2 * round * kb) / (5 * kb);
+  const int64_t merge = (lds - static_cast<int64_t>(kCtlBytes) - 2 * kMergeTile * kb) / (5 * kb);
+  return std::min(chunk, merge);
 }
 
 extern "C" size_t fa3q_calibrate_workspace_bytes(int dtype, int64_t B, int64_t H, int64_t S,

@@ -211,9 +211,27 @@ __device__ void block_select(const KeyT* buf, uint32_t n, uint32_t rank, uint32_
   for (int shift = KeyInfo<KeyT>::kBits - 8; shift >= 0; shift -= 8) {
     for (int i = tid; i < 256; i += NT) hist[i] = 0;
     lds_barrier();
-    for (uint32_t i = tid; i < n; i += NT) {
-      const uint32_t k = buf[i];
-      if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 0xffu], 1u);
+    if (shift == KeyInfo<KeyT>::kBits - 8) {
+      // top digit: tail keys share few values, so equal digits of a wave are counted with
+      // one atomic per distinct digit instead of one per lane
+      const uint32_t n_round = (n + NT - 1) / NT * NT;
+      for (uint32_t i = tid; i < n_round; i += NT) {
+        const bool act = i < n;
+        const uint32_t d = act ? (static_cast<uint32_t>(buf[i]) >> shift) & 0xffu : 0u;
+        uint64_t pending = __ballot(act);
+        while (pending != 0) {
+          const int leader = __ffsll(static_cast<unsigned long long>(pending)) - 1;
+          const uint32_t dl = __builtin_amdgcn_readlane(d, leader);
+          const uint64_t same = __ballot(act && d == dl);
+          if (lane_id() == leader) atomicAdd(&hist[dl], static_cast<uint32_t>(__popcll(same)));
+          pending &= ~same;
+        }
+      }
+    } else {
+      for (uint32_t i = tid; i < n; i += NT) {
+        const uint32_t k = buf[i];
+        if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 0xffu], 1u);
+      }
     }
     lds_barrier();
     if (tid < kWave) {
@@ -365,7 +383,7 @@ struct ChunkArgs {
   int32_t H;
   int32_t cps;        // chunks per slab
   int32_t nch;        // chunks per head = B*cps
-  int32_t boot;       // 1: seed the thresholds from the first tile's per-thread extremes
+  int32_t boot;       // 1: seed the thresholds from the first tile's per-vector extremes
   uint32_t K;
   uint32_t cap;
 };
@@ -458,22 +476,22 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
     for (int v = 0; v < kVec; ++v) vv[v] = t0 + static_cast<int64_t>(v * NT + tid) * kPerVec < end;
     Lim boot_lo = kKeyMax + 1, boot_hi = -1;
     if (first && a.boot && t0 + kTile <= end) {
-      // The K-th smallest of the NT per-thread minima has at least K keys at or below it
-      // (one per thread), so it bounds the chunk's K-th smallest key; symmetrically for
-      // the maxima.  Keys at the bound itself are candidates in this tile only.
-      uint32_t mn = KeyInfo<KeyT>::kMax, mx = 0;
+      // Each 16-byte vector of the first tile is a group of keys.  The K-th smallest of the
+      // M = NT*kVec group minima has at least K keys at or below it (one per group), so it
+      // bounds the chunk's K-th smallest key; symmetrically for the maxima.  With groups of
+      // a few keys it lands close to the tile's own K-th smallest key.  Keys at the bound
+      // itself are candidates in this tile only.
+      constexpr uint32_t M = static_cast<uint32_t>(NT * kVec);
 #pragma unroll
       for (int v = 0; v < kVec; ++v) {
         const uint32_t k0 = T::keys(x[v].x), k1 = T::keys(x[v].y), k2 = T::keys(x[v].z), k3 = T::keys(x[v].w);
-        mn = min(mn, static_cast<uint32_t>(T::ulane_min(T::umin(T::umin(k0, k1), T::umin(k2, k3)))));
-        mx = max(mx, static_cast<uint32_t>(T::ulane_max(T::umax(T::umax(k0, k1), T::umax(k2, k3)))));
+        st.tmp[v * NT + tid] = static_cast<KeyT>(T::ulane_min(T::umin(T::umin(k0, k1), T::umin(k2, k3))));
+        st.tmp[M + v * NT + tid] = static_cast<KeyT>(T::ulane_max(T::umax(T::umax(k0, k1), T::umax(k2, k3))));
       }
-      st.tmp[tid] = static_cast<KeyT>(mn);
-      st.tmp[NT + tid] = static_cast<KeyT>(mx);
       lds_barrier();
       uint32_t t_lo, t_hi, less, eq;
-      block_select<KeyT, NT>(st.tmp, NT, a.K, ctl, t_lo, less, eq);
-      block_select<KeyT, NT>(st.tmp + NT, NT, NT - a.K + 1, ctl, t_hi, less, eq);
+      block_select<KeyT, NT>(st.tmp, M, a.K, ctl, t_lo, less, eq);
+      block_select<KeyT, NT>(st.tmp + M, M, M - a.K + 1, ctl, t_hi, less, eq);
       boot_lo = static_cast<Lim>(t_lo);
       boot_hi = static_cast<Lim>(t_hi);
       lo_lim = boot_lo + 1;
@@ -721,9 +739,10 @@ int make_plan(int dtype, int64_t B, int64_t H, int64_t S, int64_t D, double rati
   p.key_bytes = dtype == FA3Q_BF16 ? 2 : 4;
   const int64_t tile = dtype == FA3Q_BF16 ? chunk_tile<uint16_t>() : chunk_tile<uint32_t>();
   const int64_t room = dtype == FA3Q_BF16 ? chunk_room<uint16_t>() : chunk_room<uint32_t>();
-  // First-tile bootstrap selects the K-th of kChunkThreads per-thread extremes: K <= threads.
-  p.boot = p.K <= kChunkThreads ? 1 : 0;
-  const size_t tmp_keys = std::max<size_t>(static_cast<size_t>(p.K), p.boot ? 2 * kChunkThreads : 0);
+  // First-tile bootstrap selects the K-th of the tile's per-vector extremes: K <= vectors.
+  const int64_t boot_groups = static_cast<int64_t>(kChunkThreads) * kVec;
+  p.boot = p.K <= boot_groups ? 1 : 0;
+  const size_t tmp_keys = std::max<size_t>(static_cast<size_t>(p.K), p.boot ? 2 * boot_groups : 0);
   p.cap_chunk = static_cast<uint32_t>(2 * p.K + room);
   p.cap_merge = static_cast<uint32_t>(2 * p.K + kMergeTile);
   p.P = static_cast<uint32_t>(next_pow2(p.K));

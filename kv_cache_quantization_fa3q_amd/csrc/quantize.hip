@@ -8,18 +8,28 @@
 //
 // Pure streaming: per (token, head) row the kernel reads (Dn + Dr) bf16 and writes Dn int8
 // plus Dr bf16.  Layout in HBM: k (B,H,S,Dn+Dr), k_nope_q (B,H,S,Dn), k_rope (B,H,S,Dr),
-// all row-major.  A workgroup takes one (b,h) and a block of up to kRowsPerItem rows, so
-// scale[h] is one scalar load; threads own fixed 16-element (nope) or 8-element (rope)
-// column units, so every load and store is a 16-byte vector and a wave covers whole
-// 128-byte lines.
+// all row-major.  A work item is one (b,h) and a block of up to kRowsPerItem rows, so
+// scale[h] is one scalar load.  Every thread moves whole 16-byte vectors of 8 elements;
+// consecutive lanes take consecutive vectors of a row part, so each load instruction of a
+// wave covers whole 128-byte lines (16 lanes per 256-byte nope row, 8 per 128-byte rope
+// row) and the 8-byte code stores of a row are contiguous.  Loads and stores carry the
+// nontemporal hint: every byte is touched once.
+//
+// The quotient: with r = fl32(1/s) and y = fl32(x*r), |y - x/s| <= |x/s| * 2^-23 (1 + 2^-25),
+// at most 1.53e-5 below 128, and the IEEE quotient fl32(x/s) is within half an ulp (7.6e-6)
+// of x/s.  So rint(y) equals rint(fl32(x/s)) unless y lies within 2.3e-5 of a half-integer;
+// such elements (and every element of a head whose scale is not a moderate normal number)
+// take the correctly rounded division.  Above 127.5 both clamp to 127.
 #include "fa3q_internal.hpp"
 
 namespace fa3q {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRowsPerItem = 128;
-constexpr int kUnroll = 4;
+constexpr int kRowsPerItem = 64;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 struct QuantArgs {
   const uint16_t* k;
@@ -34,80 +44,94 @@ struct QuantArgs {
   int32_t Dr;
 };
 
-__device__ __forceinline__ uint32_t code_byte(float x, float s, bool zero) {
-  float y = x / s;  // correctly rounded float32 division
-  y = rintf(y);     // round half to even
-  y = fminf(fmaxf(y, -127.0f), 127.0f);
-  const int c = zero ? 0 : static_cast<int>(y);
-  return static_cast<uint32_t>(c) & 0xffu;
+__device__ __forceinline__ int code_exact(float x, float s) {
+  const float y = __builtin_amdgcn_fmed3f(rintf(x / s), -127.0f, 127.0f);  // IEEE division
+  return static_cast<int>(y);
 }
 
-// 4 bf16 (two dwords) -> 4 int8 codes in one dword (little-endian element order).
-__device__ __forceinline__ uint32_t quant4(uint32_t w0, uint32_t w1, float s, bool zero) {
-  return code_byte(bf16_lo(w0), s, zero) | (code_byte(bf16_hi(w0), s, zero) << 8) |
-         (code_byte(bf16_lo(w1), s, zero) << 16) | (code_byte(bf16_hi(w1), s, zero) << 24);
+// 8 bf16 (one 16-byte vector) -> 8 codes in two dwords (little-endian element order).
+__device__ __forceinline__ u32x2 quant8(const u32x4& w, float s, float r, bool fast) {
+  float xv[8];
+  xv[0] = bf16_lo(w.x); xv[1] = bf16_hi(w.x); xv[2] = bf16_lo(w.y); xv[3] = bf16_hi(w.y);
+  xv[4] = bf16_lo(w.z); xv[5] = bf16_hi(w.z); xv[6] = bf16_lo(w.w); xv[7] = bf16_hi(w.w);
+  int c[8];
+  bool amb = !fast;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float y = xv[i] * r;
+    const float n = rintf(y);
+    amb |= fabsf(y - n) > 0.5f - 0x1p-14f;
+    c[i] = static_cast<int>(__builtin_amdgcn_fmed3f(n, -127.0f, 127.0f));
+  }
+  if (__ballot(amb) != 0) {
+    if (amb) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) c[i] = code_exact(xv[i], s);
+    }
+  }
+  u32x2 o;
+  o.x = (c[0] & 0xff) | ((c[1] & 0xff) << 8) | ((c[2] & 0xff) << 16) | (static_cast<uint32_t>(c[3]) << 24);
+  o.y = (c[4] & 0xff) | ((c[5] & 0xff) << 8) | ((c[6] & 0xff) << 16) | (static_cast<uint32_t>(c[7]) << 24);
+  return o;
 }
 
+// UN / UR: 8-element units per nope / rope row when known at compile time (0: runtime).
+template <int UN, int UR>
 __global__ __launch_bounds__(kThreads) void quantize_k_kernel(QuantArgs a) {
   const int tid = static_cast<int>(threadIdx.x);
   const int Dk = a.Dn + a.Dr;
-  const int Un = a.Dn >> 4;  // 16-wide nope units per row
-  const int Ur = a.Dr >> 3;  // 8-wide rope units per row
-  const int un = tid % Un, rn0 = tid / Un, rstep_n = kThreads / Un;
-  const int ur = Ur ? tid % Ur : 0, rr0 = Ur ? tid / Ur : kThreads, rstep_r = Ur ? kThreads / Ur : 1;
+  const int Un = UN ? UN : a.Dn >> 3;
+  const int Ur = UR ? UR : a.Dr >> 3;
+  constexpr int kNope = UN ? kRowsPerItem * UN / kThreads : 4;  // nope vectors per thread per pass
+  constexpr int kRope = UR ? (kRowsPerItem * UR + kThreads - 1) / kThreads : 2;
 
   for (int64_t item = blockIdx.x; item < a.items; item += gridDim.x) {
     const int64_t bh = item / a.chunks_per_bh;
     const int64_t chunk = item - bh * a.chunks_per_bh;
     const float s = a.scale[bh % a.H];
     const bool zero = (s == 0.0f);
+    // fast quotient only for a moderate normal scale (1/s normal, x*(1/s) free of overflow)
+    const bool fast = fabsf(s) >= 0x1p-100f && fabsf(s) <= 0x1p100f;
+    const float r = 1.0f / s;
     const int64_t r_begin = chunk * kRowsPerItem;
     const int nr = static_cast<int>(min(static_cast<int64_t>(kRowsPerItem), a.S - r_begin));
     const int64_t row0 = bh * a.S + r_begin;
     const uint16_t* __restrict__ kin = a.k + row0 * Dk;
     int8_t* __restrict__ qout = a.kq + row0 * a.Dn;
     uint16_t* __restrict__ rout = a.kr + row0 * a.Dr;
+    const int nn = nr * Un, nrp = nr * Ur;
 
-    if (rn0 < rstep_n) {
-      for (int rb = rn0; rb < nr; rb += rstep_n * kUnroll) {
-        uint4 x0[kUnroll], x1[kUnroll];
+    for (int pass = 0; pass * kThreads * kNope < nn || pass * kThreads * kRope < nrp; ++pass) {
+      u32x4 xn[kNope], xr[kRope];
+      int on[kNope], orr[kRope];
 #pragma unroll
-        for (int j = 0; j < kUnroll; ++j) {
-          const int r = rb + j * rstep_n;
-          if (r < nr) {
-            const uint4* src = reinterpret_cast<const uint4*>(kin + static_cast<int64_t>(r) * Dk + un * 16);
-            x0[j] = src[0];
-            x1[j] = src[1];
-          }
-        }
+      for (int j = 0; j < kNope; ++j) {
+        const int q = (pass * kNope + j) * kThreads + tid;
+        const int row = q / Un, unit = q - row * Un;
+        on[j] = q < nn ? row * a.Dn + unit * 8 : -1;
+        if (q < nn) xn[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kin + static_cast<int64_t>(row) * Dk + unit * 8));
+      }
+      if (Ur > 0) {
 #pragma unroll
-        for (int j = 0; j < kUnroll; ++j) {
-          const int r = rb + j * rstep_n;
-          if (r < nr) {
-            uint4 o;
-            o.x = quant4(x0[j].x, x0[j].y, s, zero);
-            o.y = quant4(x0[j].z, x0[j].w, s, zero);
-            o.z = quant4(x1[j].x, x1[j].y, s, zero);
-            o.w = quant4(x1[j].z, x1[j].w, s, zero);
-            *reinterpret_cast<uint4*>(qout + static_cast<int64_t>(r) * a.Dn + un * 16) = o;
-          }
+        for (int j = 0; j < kRope; ++j) {
+          const int q = (pass * kRope + j) * kThreads + tid;
+          const int row = q / Ur, unit = q - row * Ur;
+          orr[j] = q < nrp ? row * a.Dr + unit * 8 : -1;
+          if (q < nrp)
+            xr[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kin + static_cast<int64_t>(row) * Dk + a.Dn + unit * 8));
         }
       }
-    }
-    if (rr0 < rstep_r) {
-      for (int rb = rr0; rb < nr; rb += rstep_r * kUnroll) {
-        uint4 x[kUnroll];
 #pragma unroll
-        for (int j = 0; j < kUnroll; ++j) {
-          const int r = rb + j * rstep_r;
-          if (r < nr)
-            x[j] = *reinterpret_cast<const uint4*>(kin + static_cast<int64_t>(r) * Dk + a.Dn + ur * 8);
+      for (int j = 0; j < kNope; ++j) {
+        if (on[j] >= 0) {
+          const u32x2 o = zero ? u32x2{0u, 0u} : quant8(xn[j], s, r, fast);
+          __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(qout + on[j]));
         }
+      }
+      if (Ur > 0) {
 #pragma unroll
-        for (int j = 0; j < kUnroll; ++j) {
-          const int r = rb + j * rstep_r;
-          if (r < nr) *reinterpret_cast<uint4*>(rout + static_cast<int64_t>(r) * a.Dr + ur * 8) = x[j];
-        }
+        for (int j = 0; j < kRope; ++j)
+          if (orr[j] >= 0) __builtin_nontemporal_store(xr[j], reinterpret_cast<u32x4*>(rout + orr[j]));
       }
     }
   }
@@ -145,7 +169,10 @@ extern "C" int fa3q_quantize_k(const uint16_t* k, const float* scale, int8_t* k_
   a.Dn = static_cast<int32_t>(Dn);
   a.Dr = static_cast<int32_t>(Dr);
   const int64_t grid = std::min<int64_t>(a.items, static_cast<int64_t>(device_cu_count()) * 8);
-  hipLaunchKernelGGL(quantize_k_kernel, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0,
-                     as_stream(stream), a);
+  const dim3 g(static_cast<unsigned>(grid)), blk(kThreads);
+  if (Dn == 128 && Dr == 64)
+    hipLaunchKernelGGL((quantize_k_kernel<16, 8>), g, blk, 0, as_stream(stream), a);
+  else
+    hipLaunchKernelGGL((quantize_k_kernel<0, 0>), g, blk, 0, as_stream(stream), a);
   return launch_status();
 }

@@ -1,6 +1,6 @@
 """K quantisation parity on the GPU: INT8 codes and RoPE bytes bit-for-bit vs the oracle.
 
-Includes every finite bf16 value against a range of scales (the division, the
+Includes every finite bf16 value against fixed and random scales (the division, the
 half-to-even rounding and the clamp are exercised on all inputs a bf16 K can hold),
 exact half-integer quotients, zero-scale heads, Dr = 0 and ragged row counts.
 """
@@ -73,6 +73,22 @@ def test_every_bf16_value_against_many_scales(fa):
     k = torch.from_numpy(k_bits.view(np.int16)).view(torch.bfloat16)
     codes = _run(fa, k, scales, 16, "all_bf16")
     assert codes.min() >= -127 and codes.max() <= 127
+
+
+def test_every_bf16_value_against_random_scales(fa):
+    # 64 log-uniform scales over [1e-6, 1e6]: every bf16 value lands near many half-integer
+    # quotients, where a multiply by the reciprocal can round differently from the division
+    vals = _all_finite_bf16()
+    n = len(vals)
+    S = (n + 15) // 16
+    pad = np.zeros(S * 16, np.uint16)
+    pad[:n] = vals
+    rng = np.random.default_rng(7)
+    scales = np.exp(rng.uniform(np.log(1e-6), np.log(1e6), 64)).astype(np.float32)
+    H = len(scales)
+    k_bits = np.broadcast_to(pad.reshape(1, 1, S, 16), (1, H, S, 16)).copy()
+    k = torch.from_numpy(k_bits.view(np.int16)).view(torch.bfloat16)
+    _run(fa, k, scales, 16, "all_bf16_random_scales")
 
 
 def test_exact_half_integer_quotients(fa):

@@ -45,6 +45,15 @@ DV = 128
 CAL_BYTES = 2 * math.prod(CAL_SHAPE)                            # per batch, bf16 read once
 QUANT_BYTES = QB * H * QS * (2 * (DN + DR) + DN + 2 * DR)       # 640 B per (token, head)
 DEC_BYTES = QB * H * QS * (DN + 2 * DR + 2 * DV) + QB * H * (2 * (DN + DR) + 4 * DV)  # 512 B per (b,h,t) + q + out
+COPY_BYTES = 1 << 30  # device-to-device copy reference (read + write of 1 GiB each)
+
+# kernel -> the sources its code comes from (the committed counter summary names their hash)
+KERNEL_SOURCES = {
+    "quantize_k_kernel": ("quantize.hip", "fa3q_internal.hpp"),
+    "decode_split_kernel": ("decode.hip", "fa3q_internal.hpp"),
+    "calib_chunk_kernel": ("calibrate.hip", "fa3q_internal.hpp"),
+}
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fa3q_step_hbm_traffic.md")
 
 
 def log(msg: str) -> None:
@@ -61,8 +70,49 @@ def parse():
     return ap.parse_args()
 
 
+def source_hash(kernel: str) -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "kv_cache_quantization_fa3q_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_summary(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None when the
+    summary is missing or was taken on different kernel sources."""
+    try:
+        with open(TRAFFIC_SUMMARY) as f:
+            text = f.read()
+    except OSError:
+        return None, "no counter summary"
+    start = text.find("```json")
+    if start < 0:
+        return None, "counter summary has no json block"
+    end = text.find("```", start + 7)
+    try:
+        entries = json.loads(text[start + 7:end])
+    except ValueError:
+        return None, "counter summary json unreadable"
+    e = entries.get(kernel)
+    if not e:
+        return None, f"no counters for {kernel}"
+    if e.get("source_sha256_16") != source_hash(kernel):
+        return None, f"{kernel} changed since its counters were taken"
+    return float(e["hbm_bytes_per_launch"]), f"{os.path.relpath(TRAFFIC_SUMMARY, ROOT)} (sources {e['source_sha256_16']})"
+
+
 def cpu_baseline(inputs, budget_s: float):
-    """Time the oracle (as is, single process) on bounded slices of the same workload."""
+    """Time the oracle (as is, single process, one BLAS thread) on bounded slices of the same workload."""
+    from threadpoolctl import threadpool_limits
+
+    with threadpool_limits(limits=1):
+        return _cpu_baseline(inputs, budget_s)
+
+
+def _cpu_baseline(inputs, budget_s: float):
     import numpy as np
     import torch
 
@@ -219,14 +269,36 @@ def main() -> int:
         "quantize": {"ms": quant_ms, "gbs": quant_gbs, "frac_hbm": quant_gbs / HBM_PEAK_GBS},
         "decode": {"ms": dec_ms, "kv_gbs": dec_gbs, "frac_hbm": dec_gbs / HBM_PEAK_GBS},
     }
-    stages = {"quantize_k_kernel": (quant_ms, QUANT_BYTES), "decode_split_kernel": (dec_ms, DEC_BYTES),
-              "calibrate (per batch)": (cal_ms / CAL_BATCHES, CAL_BYTES)}
-    dom = max(stages, key=lambda s: stages[s][0] * (CAL_BATCHES if s.startswith("calib") else 1))
-    d_ms, d_bytes = stages[dom]
+    # the kernel with the largest share of the step; its events bracket exactly one launch
+    stages = {"quantize_k_kernel": (quant_ms, QUANT_BYTES, 1), "decode_split_kernel": (dec_ms, DEC_BYTES, 1),
+              "calib_chunk_kernel": (cal_ms / CAL_BATCHES, CAL_BYTES, CAL_BATCHES)}
+    dom = max(stages, key=lambda s: stages[s][0] * stages[s][2])
+    d_ms, d_bytes, _ = stages[dom]
     achieved = d_bytes / (d_ms * 1e-3) / 1e9
+    traffic, traffic_src = traffic_from_summary(dom)
     roofline = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "traffic_source": traffic_src,
                 "algorithmic_bytes_per_launch": d_bytes, "avg_launch_ms": d_ms}
+    if dom == "calib_chunk_kernel":
+        roofline["note"] = "calibration: chunk + merge kernels per batch, events around both"
+
+    # device-to-device copy of COPY_BYTES: a reference ceiling for read+write streaming, and the
+    # known-size kernel the HBM byte counters are scaled by
+    src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1.0)
+    for _ in range(2):
+        dst.copy_(src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_ms = c0.elapsed_time(c1) / 5
+    copy_ref = {"bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES, "ms": copy_ms,
+                "gbs_read_plus_write": 2 * COPY_BYTES / (copy_ms * 1e-3) / 1e9}
+    del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -255,6 +327,7 @@ def main() -> int:
         },
         "breakdown": breakdown,
         "roofline": roofline,
+        "copy_reference": copy_ref,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

@@ -9,17 +9,29 @@
 // starting at i is [L[i], U[i]] with L the K smallest values and U the K largest, both
 // ascending.  So instead of sorting N values the library selects the two tails:
 //
+//   calib_sample_kernel  one workgroup per head reads a small evenly spaced sample of the
+//                        head (8 runs of 1024 16-byte vectors, about 3% of a 2M-value
+//                        head) and sets per-head bounds: the K-th smallest per-vector
+//                        minimum (K-th largest maximum), which has at least K of the
+//                        head's values at or beyond it.
 //   calib_chunk_kernel   one HBM pass.  Each workgroup streams a contiguous chunk of one
 //                        head (inside one (b,h) slab) and keeps, in LDS, a candidate
-//                        buffer per side holding a superset of the chunk's K smallest
-//                        (K largest) values.  A value is a candidate only if it beats the
-//                        side's threshold; when a buffer passes 2K entries an exact LDS
-//                        radix select cuts it back to the K extreme values and tightens
-//                        the threshold.  The chunk's exact tails go to the workspace.
-//   calib_merge_kernel   one workgroup per head: the same select over the chunks' tails
+//                        buffer per side holding a superset of the chunk's part of the
+//                        head's K smallest (K largest) values.  A value is a candidate
+//                        only if it is within the head bound and beats the chunk's own
+//                        threshold; when a buffer passes 2K entries an exact LDS radix
+//                        select cuts it back to the K extreme values and tightens the
+//                        threshold.  At most K values per side go to the workspace.
+//   calib_merge_kernel   one workgroup per head: the same select over the chunks' lists
 //                        gives the head's exact K smallest and K largest values, a
 //                        bitonic sort orders them, and a block reduction finds the
 //                        shortest float32 window U[i]-L[i], smallest i on ties.
+//
+// Why the union of the chunk lists holds the head's K smallest values: a value v at or
+// below the head's K-th smallest value is never dropped.  The head bound has at least K
+// head values at or below it, so v is within it; a chunk's own K-th smallest value is at
+// least the head's, so v is within that too (values equal to a threshold are kept until
+// K values at or below it are held, as below).
 //
 // Values are compared through order-preserving unsigned keys (16-bit for bf16 input,
 // 32-bit for float32), which realise the float total order with -0.0 below +0.0.
@@ -27,7 +39,7 @@
 // equal to the K-th smallest once K values <= it are held never changes that multiset.
 //
 // Streaming filter of the chunk kernel.  Once the lo threshold is a negative value and
-// the hi threshold a non-negative one (the usual case after the first tile), the test
+// the hi threshold a non-negative one (the usual case from the start), the test
 // needs no key transform: among sign-magnitude patterns, "below a negative threshold"
 // is an unsigned compare of the raw bits and "above a non-negative threshold" a signed
 // one, so each dword of input costs one packed unsigned and one packed signed max.
@@ -44,6 +56,8 @@ constexpr int kChunkWaves = kChunkThreads / kWave;
 constexpr int kVec = 8;                // 16-byte vectors per thread per tile (chunk kernel)
 constexpr int kStageVecs = 64;         // vectors one wave stages and appends per round
 constexpr int kMergeThreads = 1024;
+constexpr int kSampleThreads = 1024;
+constexpr int kSampleRuns = 8;        // runs of kSampleThreads vectors sampled per head
 constexpr int kMergePerThread = 4;     // keys per thread per tile (merge kernel)
 constexpr int kMergeTile = kMergeThreads * kMergePerThread;
 constexpr int64_t kTargetCUs = 256;    // MI355X compute units (sizes the chunk grid)
@@ -383,7 +397,7 @@ struct ChunkArgs {
   int32_t H;
   int32_t cps;        // chunks per slab
   int32_t nch;        // chunks per head = B*cps
-  int32_t boot;       // 1: seed the thresholds from the first tile's per-vector extremes
+  const uint32_t* bounds;  // [2][H] sampled bound keys per head (lo side, then hi side)
   uint32_t K;
   uint32_t cap;
 };
@@ -418,6 +432,118 @@ __device__ __forceinline__ bool vec_flag_raw(const u32x4& x, typename In<InT>::L
   return T::ulane_max(mu) > rlo || T::slane_max(ms) > rhi;
 }
 
+// Sum over the 64 lanes of a wave (uniform result): an inclusive scan with DPP row shifts
+// and row broadcasts leaves the total in lane 63.
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+struct SampleArgs {
+  const void* x;
+  uint32_t* bounds;  // [2][H] out: lo bound keys, then hi bound keys
+  int64_t Lv;        // 16-byte vectors per (b,h) slab
+  int64_t run_off[kSampleRuns];  // element offset of each run's first vector in head 0
+  uint32_t run_w[kSampleRuns];   // that vector's index inside its slab
+  uint32_t run_n[kSampleRuns];   // vectors in the run (0 .. kSampleThreads)
+  int32_t H;
+  uint32_t M;        // sampled vectors per head
+  uint32_t K;
+};
+
+// Head bounds from a sample: kSampleRuns evenly spaced runs of kSampleThreads consecutive
+// vectors of the head (all of it when it is small).  Each 16-byte vector is a group of
+// keys; the K-th smallest of the M sampled group minima has at least K of the head's keys
+// at or below it (one per group), so the head's K smallest keys all lie at or below it;
+// symmetrically the K-th largest group maximum.  With M >> K it sits near the head's
+// K/(M * keys per vector) quantile.  Both ranks are found by one bisection over the key
+// bits, counting with ballots and one barrier per bit.  M < K gives no bound (every key
+// passes the chunk filter until the chunk itself holds K).
+// kSmallSlab: slabs shorter than a run, so a run may cross several slab boundaries.
+template <typename InT, bool kSmallSlab>
+__global__ __launch_bounds__(kSampleThreads) void calib_sample_kernel(SampleArgs a) {
+  using T = In<InT>;
+  using KeyT = typename T::KeyT;
+  constexpr int kPerVec = 16 / sizeof(InT);
+  constexpr int kWaves = kSampleThreads / kWave;
+  __shared__ uint32_t cnt[2][kWaves];  // [bit parity][wave]: lo count | hi count << 16
+  const int h = static_cast<int>(blockIdx.x);
+  const int tid = static_cast<int>(threadIdx.x);
+  const int wave = tid / kWave;
+  const int lane = lane_id();
+  const InT* x = static_cast<const InT*>(a.x);
+
+  // every load of the sample is issued before the first is used
+  u32x4 xs[kSampleRuns];
+  uint32_t valid = 0;  // bit j: this thread's vector of run j lies inside the head
+  const int64_t head_off = static_cast<int64_t>(h) * a.Lv * kPerVec;
+  const int64_t jump = static_cast<int64_t>(a.H - 1) * a.Lv * kPerVec;  // slab end -> next slab of the head
+#pragma unroll
+  for (int j = 0; j < kSampleRuns; ++j) {
+    const uint32_t w = a.run_w[j] + static_cast<uint32_t>(tid);
+    // slab boundaries crossed inside the run: at most one unless slabs are short
+    const uint32_t d = kSmallSlab ? w / static_cast<uint32_t>(a.Lv) : static_cast<uint32_t>(w >= a.Lv);
+    const bool ok = static_cast<uint32_t>(tid) < a.run_n[j];
+    valid |= static_cast<uint32_t>(ok) << j;
+    const int64_t e = a.run_off[j] + head_off + static_cast<int64_t>(tid) * kPerVec + d * jump;
+    xs[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + (ok ? e : 0)));
+  }
+  uint32_t gmin[kSampleRuns], gmax[kSampleRuns];
+#pragma unroll
+  for (int j = 0; j < kSampleRuns; ++j) {
+    const uint32_t k0 = T::keys(xs[j].x), k1 = T::keys(xs[j].y), k2 = T::keys(xs[j].z), k3 = T::keys(xs[j].w);
+    gmin[j] = T::ulane_min(T::umin(T::umin(k0, k1), T::umin(k2, k3)));
+    gmax[j] = T::ulane_max(T::umax(T::umax(k0, k1), T::umax(k2, k3)));
+  }
+
+  // least t_lo with #{gmin <= t_lo} >= K, least t_hi with #{gmax <= t_hi} >= M-K+1, bit by
+  // bit from the top: bit b is 0 exactly when the largest value agreeing with the bits
+  // fixed so far and having bit b clear already reaches the rank.  Vectors outside the
+  // head count as the largest key, and are taken off again when a probe reaches it.
+  const bool have = a.M >= a.K;
+  const uint32_t rank_lo = a.K, rank_hi = a.M - a.K + 1;
+  const uint32_t n_out = static_cast<uint32_t>(kSampleRuns * kSampleThreads) - a.M;
+#pragma unroll
+  for (int j = 0; j < kSampleRuns; ++j) {
+    if (!((valid >> j) & 1u)) {
+      gmin[j] = KeyInfo<KeyT>::kMax;
+      gmax[j] = KeyInfo<KeyT>::kMax;
+    }
+  }
+  uint32_t t_lo = 0, t_hi = 0;
+#pragma unroll 1
+  for (int bit = KeyInfo<KeyT>::kBits - 1; bit >= 0 && have; --bit) {
+    const uint32_t p_lo = t_lo | ((1u << bit) - 1u), p_hi = t_hi | ((1u << bit) - 1u);
+    uint32_t c = 0;  // lo count in the low half, hi count in the high half
+#pragma unroll
+    for (int j = 0; j < kSampleRuns; ++j) c += (gmin[j] <= p_lo ? 1u : 0u) + (gmax[j] <= p_hi ? 0x10000u : 0u);
+    c = wave_sum(c);
+    const int par = bit & 1;  // a slot is rewritten two bits later, after every wave read it
+    if (lane == 0) cnt[par][wave] = c;
+    __syncthreads();
+    uint32_t s_lo = 0, s_hi = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const uint32_t v = cnt[par][w];
+      s_lo += v & 0xffffu;
+      s_hi += v >> 16;
+    }
+    if (p_lo == KeyInfo<KeyT>::kMax) s_lo -= n_out;
+    if (p_hi == KeyInfo<KeyT>::kMax) s_hi -= n_out;
+    if (s_lo < rank_lo) t_lo |= 1u << bit;
+    if (s_hi < rank_hi) t_hi |= 1u << bit;
+  }
+  if (tid == 0) {
+    a.bounds[h] = have ? t_lo : KeyInfo<KeyT>::kMax;
+    a.bounds[a.H + h] = have ? t_hi : 0u;
+  }
+}
+
 template <typename InT>
 __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void calib_chunk_kernel(ChunkArgs a) {
   using T = In<InT>;
@@ -446,10 +572,15 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
   st.room = chunk_room<InT>();
   st.init();
 
-  const int h = static_cast<int>(blockIdx.x) / a.nch;
-  const int c = static_cast<int>(blockIdx.x) - h * a.nch;
-  const int b = c / a.cps;
-  const int part = c - b * a.cps;
+  // Blocks take chunks in address order (block i: slab i / cps, slab = b*H + h), so the
+  // blocks the dispatcher deals round-robin to the XCDs read neighbouring chunks and every
+  // XCD streams from all of memory at once; a block per (h, b) in head order would hand
+  // each XCD one batch's contiguous range instead, which runs far below the HBM rate.
+  const int slab_i = static_cast<int>(blockIdx.x) / a.cps;
+  const int part = static_cast<int>(blockIdx.x) - slab_i * a.cps;
+  const int b = slab_i / a.H;
+  const int h = slab_i - b * a.H;
+  const int c = b * a.cps + part;
   const InT* slab = static_cast<const InT*>(a.x) + (static_cast<int64_t>(b) * a.H + h) * a.L;
   const int64_t begin = static_cast<int64_t>(part) * a.CL;
   const int64_t end = min(a.L, begin + a.CL);
@@ -466,38 +597,16 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
     }
   };
 
-  // Candidate limits: key < lo_lim or key > hi_lim (nothing held yet: every key).
-  Lim lo_lim = kKeyMax + 1, hi_lim = -1;
+  // Candidate limits: key < lo_lim or key > hi_lim.  The head's sampled bounds have at
+  // least K of the head's keys at or beyond them, so the head's K extreme keys all lie
+  // within them: the chunk keeps every key up to and including the bounds (it may hold
+  // fewer than K such keys), then its own K-th extreme key once it holds K.
+  Lim lo_lim = static_cast<Lim>(a.bounds[h]) + 1, hi_lim = static_cast<Lim>(a.bounds[a.H + h]) - 1;
   if (begin < end) load_tile(begin);
-  bool first = true;
   for (int64_t t0 = begin; t0 < end; t0 += kTile) {
     bool vv[kVec];
 #pragma unroll
     for (int v = 0; v < kVec; ++v) vv[v] = t0 + static_cast<int64_t>(v * NT + tid) * kPerVec < end;
-    Lim boot_lo = kKeyMax + 1, boot_hi = -1;
-    if (first && a.boot && t0 + kTile <= end) {
-      // Each 16-byte vector of the first tile is a group of keys.  The K-th smallest of the
-      // M = NT*kVec group minima has at least K keys at or below it (one per group), so it
-      // bounds the chunk's K-th smallest key; symmetrically for the maxima.  With groups of
-      // a few keys it lands close to the tile's own K-th smallest key.  Keys at the bound
-      // itself are candidates in this tile only.
-      constexpr uint32_t M = static_cast<uint32_t>(NT * kVec);
-#pragma unroll
-      for (int v = 0; v < kVec; ++v) {
-        const uint32_t k0 = T::keys(x[v].x), k1 = T::keys(x[v].y), k2 = T::keys(x[v].z), k3 = T::keys(x[v].w);
-        st.tmp[v * NT + tid] = static_cast<KeyT>(T::ulane_min(T::umin(T::umin(k0, k1), T::umin(k2, k3))));
-        st.tmp[M + v * NT + tid] = static_cast<KeyT>(T::ulane_max(T::umax(T::umax(k0, k1), T::umax(k2, k3))));
-      }
-      lds_barrier();
-      uint32_t t_lo, t_hi, less, eq;
-      block_select<KeyT, NT>(st.tmp, M, a.K, ctl, t_lo, less, eq);
-      block_select<KeyT, NT>(st.tmp + M, M, M - a.K + 1, ctl, t_hi, less, eq);
-      boot_lo = static_cast<Lim>(t_lo);
-      boot_hi = static_cast<Lim>(t_hi);
-      lo_lim = boot_lo + 1;
-      hi_lim = boot_hi - 1;
-    }
-    first = false;
 
     bool f[kVec];
     if (lo_lim <= T::kKeyZero && hi_lim >= T::kKeyZero - 1) {
@@ -567,9 +676,6 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
       if (st.thr_lo != thr_lo0) lo_lim = min(lo_lim, static_cast<Lim>(st.thr_lo));
       if (st.thr_hi != thr_hi0) hi_lim = max(hi_lim, static_cast<Lim>(st.thr_hi));
     }
-    // after the bootstrap tile the buffers hold at least K keys at or beyond the bounds
-    lo_lim = min(lo_lim, boot_lo);
-    hi_lim = max(hi_lim, boot_hi);
   }
   st.finish();
 
@@ -705,11 +811,13 @@ __global__ __launch_bounds__(kMergeThreads) void calib_merge_kernel(MergeArgs a)
 struct CalibPlan {
   int64_t N = 0, t = 0, K = 0;
   int64_t L = 0, CL = 0;
-  int32_t cps = 0, nch = 0, boot = 0;
+  int32_t cps = 0, nch = 0;
+  int64_t sample_off[kSampleRuns] = {};
+  uint32_t sample_w[kSampleRuns] = {}, sample_n[kSampleRuns] = {}, sample_m = 0;
   uint32_t cap_chunk = 0, cap_merge = 0, P = 0;
   size_t lds_chunk = 0, lds_merge = 0;
   size_t key_bytes = 0;
-  size_t lists_bytes = 0, total_bytes = 0;
+  size_t lists_bytes = 0, bounds_bytes = 0, total_bytes = 0;
 };
 
 int64_t next_pow2(int64_t v) {
@@ -739,10 +847,7 @@ int make_plan(int dtype, int64_t B, int64_t H, int64_t S, int64_t D, double rati
   p.key_bytes = dtype == FA3Q_BF16 ? 2 : 4;
   const int64_t tile = dtype == FA3Q_BF16 ? chunk_tile<uint16_t>() : chunk_tile<uint32_t>();
   const int64_t room = dtype == FA3Q_BF16 ? chunk_room<uint16_t>() : chunk_room<uint32_t>();
-  // First-tile bootstrap selects the K-th of the tile's per-vector extremes: K <= vectors.
-  const int64_t boot_groups = static_cast<int64_t>(kChunkThreads) * kVec;
-  p.boot = p.K <= boot_groups ? 1 : 0;
-  const size_t tmp_keys = std::max<size_t>(static_cast<size_t>(p.K), p.boot ? 2 * boot_groups : 0);
+  const size_t tmp_keys = static_cast<size_t>(p.K);
   p.cap_chunk = static_cast<uint32_t>(2 * p.K + room);
   p.cap_merge = static_cast<uint32_t>(2 * p.K + kMergeTile);
   p.P = static_cast<uint32_t>(next_pow2(p.K));
@@ -765,7 +870,23 @@ int make_plan(int dtype, int64_t B, int64_t H, int64_t S, int64_t D, double rati
 
   const size_t lists = static_cast<size_t>(H) * p.nch;
   p.lists_bytes = round_up(2 * lists * static_cast<size_t>(p.K) * p.key_bytes, 256);
-  p.total_bytes = p.lists_bytes;
+  p.bounds_bytes = round_up(2 * static_cast<size_t>(H) * sizeof(uint32_t), 256);
+  p.total_bytes = p.lists_bytes + p.bounds_bytes;
+
+  // Sample runs: evenly spaced over the head's B*L/vec vectors, or back to back (covering
+  // the whole head) when it has fewer than kSampleRuns runs' worth.
+  const int64_t Lv = p.L / vec, Q = B * Lv;
+  const int64_t stride = std::max<int64_t>(kSampleThreads, Q / kSampleRuns);
+  int64_t m = 0;
+  for (int j = 0; j < kSampleRuns; ++j) {
+    const int64_t q0 = j * stride;
+    p.sample_n[j] = static_cast<uint32_t>(std::min<int64_t>(kSampleThreads, std::max<int64_t>(0, Q - q0)));
+    const int64_t b = p.sample_n[j] ? q0 / Lv : 0, w = p.sample_n[j] ? q0 - b * Lv : 0;
+    p.sample_off[j] = (b * H * Lv + w) * vec;
+    p.sample_w[j] = static_cast<uint32_t>(w);
+    m += p.sample_n[j];
+  }
+  p.sample_m = static_cast<uint32_t>(m);
   return FA3Q_OK;
 }
 
@@ -778,15 +899,33 @@ int launch(const void* x, int64_t H, const CalibPlan& p, float* win_min, float* 
   st = allow_dynamic_lds(reinterpret_cast<const void*>(calib_merge_kernel<KeyT>), p.lds_merge);
   if (st != FA3Q_OK) return st;
 
+  uint32_t* bounds = reinterpret_cast<uint32_t*>(static_cast<unsigned char*>(workspace) + p.lists_bytes);
+  SampleArgs sa;
+  sa.x = x;
+  sa.bounds = bounds;
+  sa.Lv = p.L / (16 / static_cast<int64_t>(p.key_bytes));
+  for (int j = 0; j < kSampleRuns; ++j) {
+    sa.run_off[j] = p.sample_off[j];
+    sa.run_w[j] = p.sample_w[j];
+    sa.run_n[j] = p.sample_n[j];
+  }
+  sa.H = static_cast<int32_t>(H);
+  sa.M = p.sample_m;
+  sa.K = static_cast<uint32_t>(p.K);
+  if (sa.Lv >= kSampleThreads)
+    hipLaunchKernelGGL((calib_sample_kernel<InT, false>), dim3(static_cast<unsigned>(H)), dim3(kSampleThreads), 0, stream, sa);
+  else
+    hipLaunchKernelGGL((calib_sample_kernel<InT, true>), dim3(static_cast<unsigned>(H)), dim3(kSampleThreads), 0, stream, sa);
+
   ChunkArgs ca;
   ca.x = x;
   ca.lists = workspace;
+  ca.bounds = bounds;
   ca.L = p.L;
   ca.CL = p.CL;
   ca.H = static_cast<int32_t>(H);
   ca.cps = p.cps;
   ca.nch = p.nch;
-  ca.boot = p.boot;
   ca.K = static_cast<uint32_t>(p.K);
   ca.cap = p.cap_chunk;
   hipLaunchKernelGGL(calib_chunk_kernel<InT>, dim3(static_cast<unsigned>(H * p.nch)), dim3(kChunkThreads),

@@ -612,10 +612,10 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
     if (lo_lim <= T::kKeyZero && hi_lim >= T::kKeyZero - 1) {
       const Lim rlo = kKeyMax - lo_lim, rhi = hi_lim - T::kKeyZero;
 #pragma unroll
-      for (int v = 0; v < kVec; ++v) f[v] = vv[v] && vec_flag_raw<InT>(x[v], rlo, rhi);
+      for (int v = 0; v < kVec; ++v) f[v] = vv[v] & vec_flag_raw<InT>(x[v], rlo, rhi);  // no short-circuit branch
     } else {
 #pragma unroll
-      for (int v = 0; v < kVec; ++v) f[v] = vv[v] && vec_flag_keys<InT>(x[v], lo_lim, hi_lim);
+      for (int v = 0; v < kVec; ++v) f[v] = vv[v] & vec_flag_keys<InT>(x[v], lo_lim, hi_lim);
     }
     uint64_t m[kVec];
     uint32_t off[kVec];

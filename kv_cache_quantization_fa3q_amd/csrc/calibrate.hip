@@ -806,6 +806,137 @@ __global__ __launch_bounds__(kMergeThreads) void calib_merge_kernel(MergeArgs a)
   }
 }
 
+// Merge for heads whose lists fit in registers (nch*K <= 64*R, K <= 64*E):
+// wave 0 takes the lo side, wave 1 the hi side with its keys complemented (kMax - key), so
+// that both look for their side's K smallest keys in ascending order.  Each wave alone,
+// with no barrier: the K-th smallest key by a search over the key bits (counts in
+// registers, summed with DPP), the K keys below it (ballot appends, then copies of the
+// K-th key up to K), and a bitonic sort of them, E keys per lane (element lane*E + e),
+// exchanging registers across lanes for the wide steps.  One barrier, then the window.
+constexpr int kWaveMergeRegs = 64;  // most union keys per lane
+constexpr int kWaveMergeThreads = 2 * kWave;
+
+template <typename KeyT, int R, int E>
+__global__ __launch_bounds__(kWaveMergeThreads) void calib_merge_wave_kernel(MergeArgs a) {
+  constexpr uint32_t kMax = KeyInfo<KeyT>::kMax;
+  constexpr int P = kWave * E;
+  __shared__ uint32_t sorted[2][P];
+  __shared__ float best_l[2];
+  __shared__ uint32_t best_at[2];
+  const int h = static_cast<int>(blockIdx.x);
+  const int tid = static_cast<int>(threadIdx.x);
+  const int side = tid / kWave;
+  const uint32_t lane = static_cast<uint32_t>(lane_id());
+  const uint32_t K = a.K;
+  const uint32_t n = static_cast<uint32_t>(a.nch) * K;
+  const KeyT* src = static_cast<const KeyT*>(a.lists) +
+                    (static_cast<int64_t>(side) * a.H + h) * static_cast<int64_t>(n);
+  const uint32_t flip = side == 0 ? 0u : kMax;  // hi side: complemented keys
+
+  uint32_t k[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint32_t i = static_cast<uint32_t>(r) * kWave + lane;
+    k[r] = i < n ? (static_cast<uint32_t>(src[i]) ^ flip) : kMax;
+  }
+  // least t with #{k <= t} >= K (entries past n hold kMax and never change that answer,
+  // since the n list entries already reach K at kMax)
+  uint32_t t = 0;
+#pragma unroll 1
+  for (int bit = KeyInfo<KeyT>::kBits - 1; bit >= 0; --bit) {
+    const uint32_t probe = t | ((1u << bit) - 1u);
+    uint32_t c = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) c += k[r] <= probe ? 1u : 0u;
+    if (wave_sum(c) < K) t |= 1u << bit;
+  }
+  // the keys below t, then copies of t up to K
+  uint32_t* out = sorted[side];
+  uint32_t less = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const bool take = k[r] < t;
+    const uint64_t m = __ballot(take);
+    if (take) out[less + lanes_below(m)] = k[r];
+    less += static_cast<uint32_t>(__popcll(m));
+  }
+  for (uint32_t i = less + lane; i < static_cast<uint32_t>(P); i += kWave) out[i] = i < K ? t : kMax;
+  __asm__ volatile("" ::: "memory");  // the wave reads back what it wrote (in order)
+  uint32_t v[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) v[e] = out[lane * E + e];
+  // bitonic network over P = 64*E elements, element lane*E + e
+#pragma unroll
+  for (int kk = 2; kk <= P; kk <<= 1) {
+#pragma unroll
+    for (int j = kk >> 1; j > 0; j >>= 1) {
+      if (j < E) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          if ((e & j) == 0) {
+            const bool up = ((lane * E + e) & kk) == 0;
+            const uint32_t x0 = v[e], x1 = v[e ^ j];
+            const bool sw = (x0 > x1) == up;
+            v[e] = sw ? x1 : x0;
+            v[e ^ j] = sw ? x0 : x1;
+          }
+        }
+      } else {
+        const int lm = j / E;  // partner lane = lane ^ lm
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const uint32_t o = static_cast<uint32_t>(__shfl_xor(static_cast<int>(v[e]), lm));
+          const uint32_t i = lane * E + e;
+          const bool up = (i & kk) == 0;
+          const bool low = (i & j) == 0;
+          v[e] = (low == up) ? min(v[e], o) : max(v[e], o);
+        }
+      }
+    }
+  }
+  __asm__ volatile("" ::: "memory");
+#pragma unroll
+  for (int e = 0; e < E; ++e) out[lane * E + e] = v[e];
+  __syncthreads();
+
+  // Shortest window U[i] - L[i] (float32), smallest i on ties; U[i] is the (K-1-i)-th
+  // complemented hi key.
+  float bl = __uint_as_float(0x7f800000u);
+  uint32_t bi = 0xffffffffu;
+  for (uint32_t i = static_cast<uint32_t>(tid); i < K; i += kWaveMergeThreads) {
+    const float len = value_of_key(sorted[1][K - 1 - i] ^ kMax, KeyT{}) - value_of_key(sorted[0][i], KeyT{});
+    if (len < bl || bi == 0xffffffffu) {
+      bl = len;
+      bi = i;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float ol = __shfl_xor(bl, o);
+    const uint32_t oi = static_cast<uint32_t>(__shfl_xor(static_cast<int>(bi), o));
+    if (ol < bl || (ol == bl && oi < bi)) {
+      bl = ol;
+      bi = oi;
+    }
+  }
+  if (lane == 0) {
+    best_l[side] = bl;
+    best_at[side] = bi;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    if (best_l[1] < best_l[0] || (best_l[1] == best_l[0] && best_at[1] < best_at[0])) {
+      bl = best_l[1];
+      bi = best_at[1];
+    } else {
+      bl = best_l[0];
+      bi = best_at[0];
+    }
+    a.win_min[h] = value_of_key(sorted[0][bi], KeyT{});
+    a.win_max[h] = value_of_key(sorted[1][K - 1 - bi] ^ kMax, KeyT{});
+  }
+}
+
 // ----------------------------------------------------------------------------- host side
 
 struct CalibPlan {
@@ -817,6 +948,8 @@ struct CalibPlan {
   uint32_t cap_chunk = 0, cap_merge = 0, P = 0;
   size_t lds_chunk = 0, lds_merge = 0;
   size_t key_bytes = 0;
+  int wave_merge_e = 0;  // > 0: the two-wave merge with this many sorted keys per lane
+  int wave_merge_r = 0;  // and this many union keys per lane
   size_t lists_bytes = 0, bounds_bytes = 0, total_bytes = 0;
 };
 
@@ -867,6 +1000,15 @@ int make_plan(int dtype, int64_t B, int64_t H, int64_t S, int64_t D, double rati
   p.cps = static_cast<int32_t>((p.L + p.CL - 1) / p.CL);
   if (B * p.cps > (int64_t{1} << 30) || H * B * p.cps > (int64_t{1} << 31) - 1) return FA3Q_ERR_SHAPE;
   p.nch = static_cast<int32_t>(B * p.cps);
+  if (static_cast<int64_t>(p.nch) * p.K <= static_cast<int64_t>(kWave) * kWaveMergeRegs) {
+    p.wave_merge_r = static_cast<int64_t>(p.nch) * p.K <= static_cast<int64_t>(kWave) * 32 ? 32 : 64;
+    for (int e = 1; e <= 16; e <<= 1) {
+      if (p.K <= static_cast<int64_t>(kWave) * e) {
+        p.wave_merge_e = e;
+        break;
+      }
+    }
+  }
 
   const size_t lists = static_cast<size_t>(H) * p.nch;
   p.lists_bytes = round_up(2 * lists * static_cast<size_t>(p.K) * p.key_bytes, 256);
@@ -888,6 +1030,18 @@ int make_plan(int dtype, int64_t B, int64_t H, int64_t S, int64_t D, double rati
   }
   p.sample_m = static_cast<uint32_t>(m);
   return FA3Q_OK;
+}
+
+template <typename KeyT, int R>
+void launch_wave_merge(int e, int64_t H, const MergeArgs& ma, hipStream_t stream) {
+  const dim3 g(static_cast<unsigned>(H)), blk(kWaveMergeThreads);
+  switch (e) {
+    case 1: hipLaunchKernelGGL((calib_merge_wave_kernel<KeyT, R, 1>), g, blk, 0, stream, ma); break;
+    case 2: hipLaunchKernelGGL((calib_merge_wave_kernel<KeyT, R, 2>), g, blk, 0, stream, ma); break;
+    case 4: hipLaunchKernelGGL((calib_merge_wave_kernel<KeyT, R, 4>), g, blk, 0, stream, ma); break;
+    case 8: hipLaunchKernelGGL((calib_merge_wave_kernel<KeyT, R, 8>), g, blk, 0, stream, ma); break;
+    default: hipLaunchKernelGGL((calib_merge_wave_kernel<KeyT, R, 16>), g, blk, 0, stream, ma); break;
+  }
 }
 
 template <typename InT>
@@ -939,8 +1093,13 @@ int launch(const void* x, int64_t H, const CalibPlan& p, float* win_min, float* 
   ma.K = static_cast<uint32_t>(p.K);
   ma.cap = p.cap_merge;
   ma.P = p.P;
-  hipLaunchKernelGGL(calib_merge_kernel<KeyT>, dim3(static_cast<unsigned>(H)), dim3(kMergeThreads),
-                     p.lds_merge, stream, ma);
+  if (p.wave_merge_e > 0 && p.wave_merge_r == 32)
+    launch_wave_merge<KeyT, 32>(p.wave_merge_e, H, ma, stream);
+  else if (p.wave_merge_e > 0)
+    launch_wave_merge<KeyT, 64>(p.wave_merge_e, H, ma, stream);
+  else
+    hipLaunchKernelGGL(calib_merge_kernel<KeyT>, dim3(static_cast<unsigned>(H)), dim3(kMergeThreads),
+                       p.lds_merge, stream, ma);
   return launch_status();
 }
 

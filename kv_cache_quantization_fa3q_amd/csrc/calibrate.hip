@@ -56,8 +56,10 @@ constexpr int kChunkWaves = kChunkThreads / kWave;
 constexpr int kVec = 8;                // 16-byte vectors per thread per tile (chunk kernel)
 constexpr int kStageVecs = 64;         // vectors one wave stages and appends per round
 constexpr int kMergeThreads = 1024;
-constexpr int kSampleThreads = 1024;
-constexpr int kSampleRuns = 8;        // runs of kSampleThreads vectors sampled per head
+constexpr int kSampleThreads = 256;
+constexpr int kSampleRuns = 32;       // runs of kSampleThreads vectors sampled per head
+constexpr int kSampleGroupRuns = 4;   // a thread's vectors of this many runs form one group
+constexpr int kSampleGroups = kSampleRuns / kSampleGroupRuns;  // groups per thread
 constexpr int kMergePerThread = 4;     // keys per thread per tile (merge kernel)
 constexpr int kMergeTile = kMergeThreads * kMergePerThread;
 constexpr int64_t kTargetCUs = 256;    // MI355X compute units (sizes the chunk grid)
@@ -452,18 +454,19 @@ struct SampleArgs {
   uint32_t run_w[kSampleRuns];   // that vector's index inside its slab
   uint32_t run_n[kSampleRuns];   // vectors in the run (0 .. kSampleThreads)
   int32_t H;
-  uint32_t M;        // sampled vectors per head
+  uint32_t M;        // sampled groups per head
   uint32_t K;
 };
 
 // Head bounds from a sample: kSampleRuns evenly spaced runs of kSampleThreads consecutive
-// vectors of the head (all of it when it is small).  Each 16-byte vector is a group of
-// keys; the K-th smallest of the M sampled group minima has at least K of the head's keys
-// at or below it (one per group), so the head's K smallest keys all lie at or below it;
-// symmetrically the K-th largest group maximum.  With M >> K it sits near the head's
-// K/(M * keys per vector) quantile.  Both ranks are found by one bisection over the key
-// bits, counting with ballots and one barrier per bit.  M < K gives no bound (every key
-// passes the chunk filter until the chunk itself holds K).
+// 16-byte vectors of the head (all of it when it is small).  A thread's vectors of
+// kSampleGroupRuns runs form a group of keys; the K-th smallest of the M sampled group
+// minima has at least K of the head's keys at or below it (one per group), so the head's
+// K smallest keys all lie at or below it; symmetrically the K-th largest group maximum.
+// With K a small fraction of M it sits near the head's K/(sampled keys) quantile.  Both
+// ranks are found by one bisection over the key bits, counting with ballots and one
+// barrier per bit.  M < K gives no bound (every key passes the chunk filter until the
+// chunk itself holds K).
 // kSmallSlab: slabs shorter than a run, so a run may cross several slab boundaries.
 template <typename InT, bool kSmallSlab>
 __global__ __launch_bounds__(kSampleThreads) void calib_sample_kernel(SampleArgs a) {
@@ -493,36 +496,44 @@ __global__ __launch_bounds__(kSampleThreads) void calib_sample_kernel(SampleArgs
     const int64_t e = a.run_off[j] + head_off + static_cast<int64_t>(tid) * kPerVec + d * jump;
     xs[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + (ok ? e : 0)));
   }
-  uint32_t gmin[kSampleRuns], gmax[kSampleRuns];
+  // A group is a thread's vectors of kSampleGroupRuns runs (any distinct keys make a
+  // group); its extremes are taken over the vectors inside the head.  Groups with no such
+  // vector count as the largest key, and are taken off again when a probe reaches it.
+  uint32_t gmin[kSampleGroups], gmax[kSampleGroups];
 #pragma unroll
-  for (int j = 0; j < kSampleRuns; ++j) {
-    const uint32_t k0 = T::keys(xs[j].x), k1 = T::keys(xs[j].y), k2 = T::keys(xs[j].z), k3 = T::keys(xs[j].w);
-    gmin[j] = T::ulane_min(T::umin(T::umin(k0, k1), T::umin(k2, k3)));
-    gmax[j] = T::ulane_max(T::umax(T::umax(k0, k1), T::umax(k2, k3)));
+  for (int g = 0; g < kSampleGroups; ++g) {
+    uint32_t mn = KeyInfo<KeyT>::kMax, mx = 0;
+    bool any = false;
+#pragma unroll
+    for (int q = 0; q < kSampleGroupRuns; ++q) {
+      const int j = g * kSampleGroupRuns + q;
+      const uint32_t k0 = T::keys(xs[j].x), k1 = T::keys(xs[j].y), k2 = T::keys(xs[j].z), k3 = T::keys(xs[j].w);
+      const bool ok = (valid >> j) & 1u;
+      any |= ok;
+      mn = ok ? min(mn, T::ulane_min(T::umin(T::umin(k0, k1), T::umin(k2, k3)))) : mn;
+      mx = ok ? max(mx, T::ulane_max(T::umax(T::umax(k0, k1), T::umax(k2, k3)))) : mx;
+    }
+    gmin[g] = any ? mn : KeyInfo<KeyT>::kMax;
+    gmax[g] = any ? mx : KeyInfo<KeyT>::kMax;
   }
 
   // least t_lo with #{gmin <= t_lo} >= K, least t_hi with #{gmax <= t_hi} >= M-K+1, bit by
   // bit from the top: bit b is 0 exactly when the largest value agreeing with the bits
-  // fixed so far and having bit b clear already reaches the rank.  Vectors outside the
-  // head count as the largest key, and are taken off again when a probe reaches it.
+  // fixed so far and having bit b clear already reaches the rank.
   const bool have = a.M >= a.K;
   const uint32_t rank_lo = a.K, rank_hi = a.M - a.K + 1;
-  const uint32_t n_out = static_cast<uint32_t>(kSampleRuns * kSampleThreads) - a.M;
-#pragma unroll
-  for (int j = 0; j < kSampleRuns; ++j) {
-    if (!((valid >> j) & 1u)) {
-      gmin[j] = KeyInfo<KeyT>::kMax;
-      gmax[j] = KeyInfo<KeyT>::kMax;
-    }
-  }
+  const uint32_t n_out = static_cast<uint32_t>(kSampleGroups * kSampleThreads) - a.M;
   uint32_t t_lo = 0, t_hi = 0;
 #pragma unroll 1
   for (int bit = KeyInfo<KeyT>::kBits - 1; bit >= 0 && have; --bit) {
     const uint32_t p_lo = t_lo | ((1u << bit) - 1u), p_hi = t_hi | ((1u << bit) - 1u);
-    uint32_t c = 0;  // lo count in the low half, hi count in the high half
+    uint32_t c_lo = 0, c_hi = 0;  // wave counts: a ballot per register, popcounts on the scalar unit
 #pragma unroll
-    for (int j = 0; j < kSampleRuns; ++j) c += (gmin[j] <= p_lo ? 1u : 0u) + (gmax[j] <= p_hi ? 0x10000u : 0u);
-    c = wave_sum(c);
+    for (int g = 0; g < kSampleGroups; ++g) {
+      c_lo += static_cast<uint32_t>(__popcll(__ballot(gmin[g] <= p_lo)));
+      c_hi += static_cast<uint32_t>(__popcll(__ballot(gmax[g] <= p_hi)));
+    }
+    const uint32_t c = c_lo | (c_hi << 16);  // each at most kSampleGroups * 64
     const int par = bit & 1;  // a slot is rewritten two bits later, after every wave read it
     if (lane == 0) cnt[par][wave] = c;
     __syncthreads();
@@ -1026,7 +1037,13 @@ int make_plan(int dtype, int64_t B, int64_t H, int64_t S, int64_t D, double rati
     const int64_t b = p.sample_n[j] ? q0 / Lv : 0, w = p.sample_n[j] ? q0 - b * Lv : 0;
     p.sample_off[j] = (b * H * Lv + w) * vec;
     p.sample_w[j] = static_cast<uint32_t>(w);
-    m += p.sample_n[j];
+  }
+  // a thread's group holds a vector inside the head when its lane is below the largest
+  // run length among the group's runs
+  for (int g = 0; g < kSampleGroups; ++g) {
+    uint32_t most = 0;
+    for (int q = 0; q < kSampleGroupRuns; ++q) most = std::max(most, p.sample_n[g * kSampleGroupRuns + q]);
+    m += most;
   }
   p.sample_m = static_cast<uint32_t>(m);
   return FA3Q_OK;

@@ -282,6 +282,26 @@ def main() -> int:
     if dom == "calib_chunk_kernel":
         roofline["note"] = "calibration: chunk + merge kernels per batch, events around both"
 
+    # Decode step with append (one new token per (b,h) written into the cache at position
+    # T-1, then attention over all T tokens): the same cache reads as decode plus one row
+    # written per (b,h); measured after the timed steps, outside the step.
+    k_new = synth.normal_tensor((QB, H, DN + DR), dtype=torch.bfloat16, seed=410, device=dev)
+    v_new = synth.normal_tensor((QB, H, DV), dtype=torch.bfloat16, seed=420, device=dev)
+    kv_len = torch.full((QB,), QS - 1, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        fa.fa3q_decode_append_attn(q, k_new, v_new, scale, kq, kr, v, kv_len, sm, out, ws_dec, stream=stream)
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record(stream)
+    for _ in range(5):
+        fa.fa3q_decode_append_attn(q, k_new, v_new, scale, kq, kr, v, kv_len, sm, out, ws_dec, stream=stream)
+    a1.record(stream)
+    torch.cuda.synchronize()
+    app_ms = a0.elapsed_time(a1) / 5
+    breakdown["decode_append"] = {"ms": app_ms, "kv_gbs": DEC_BYTES / (app_ms * 1e-3) / 1e9,
+                                  "frac_hbm": DEC_BYTES / (app_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                  "note": "append one token per (b,h) at position T-1, then attention over T "
+                                          "(outside the step)"}
+
     # device-to-device copy of COPY_BYTES: a reference ceiling for read+write streaming, and the
     # known-size kernel the HBM byte counters are scaled by
     src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)

@@ -11,6 +11,8 @@
  *   3. fa3q_qparams            -- symmetric per-head scale = abs_max / 127
  *   4. fa3q_quantize_k         -- non-RoPE part of K -> INT8 codes, RoPE part kept in bf16
  *   5. fa3q_decode_attn        -- single-query attention over INT8 K-nope + bf16 K-rope + bf16 V
+ *   6. fa3q_decode_append_attn -- one decode step: append the new token to the cache in place
+ *      (K-nope quantised as in 4), then attention over ragged per-sequence lengths
  *
  * Sources, cited by page title and section:
  *   [MS] msModelSlim documentation, "FA3量化：Flash Attention 3激活量化算法说明"
@@ -202,6 +204,43 @@ int fa3q_decode_attn(const uint16_t* q, const int8_t* k_nope_q, const float* sca
                      const uint16_t* k_rope, const uint16_t* v, int64_t B, int64_t H,
                      int64_t T, int64_t Dn, int64_t Dr, int64_t Dv, float sm_scale, float* out,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* 6. Decode step: append the new token, attend over ragged lengths         */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * [MI] overview: the INT8 K-nope cache is written during decode as each new
+ * token's K is produced, and read by the same step's attention.  The cache has
+ * room for T tokens per (b, h); sequence b holds kv_len[b] of them.
+ *
+ * With k_new != NULL (append): for every (b, h), with p = kv_len[b],
+ *   k_nope_q[b,h,p,:] = clamp(round_half_even(fl32(k_new[b,h,d] / scale[h])), -127, 127)
+ *                       for d < Dn (0 for a head with scale 0), exactly as fa3q_quantize_k,
+ *   k_rope[b,h,p,:]   = k_new[b,h,Dn:Dn+Dr]   (bit copy),
+ *   v[b,h,p,:]        = v_new[b,h,:]          (bit copy),
+ * then out[b,h,:] is the attention of fa3q_decode_attn over tokens 0..p
+ * (p + 1 tokens).  Requires 0 <= kv_len[b] <= T-1.
+ * With k_new == NULL (and v_new == NULL): attention over tokens
+ * 0..kv_len[b]-1, nothing is written to the cache.  Requires 1 <= kv_len[b] <= T.
+ *
+ *   q, scale, out, T, Dn, Dr, Dv, sm_scale, workspace: as fa3q_decode_attn
+ *              (the workspace query takes the capacity T).
+ *   k_new      device bf16 (B,H,Dn+Dr), 16-byte aligned, or NULL.
+ *   v_new      device bf16 (B,H,Dv), 16-byte aligned; NULL exactly when k_new is.
+ *   k_nope_q, k_rope, v  the cache as in fa3q_decode_attn with capacity T; written
+ *              in place at position kv_len[b] when appending.
+ *   kv_len     device int32 [B], 4-byte aligned; read on the device, not changed.
+ *              Lengths outside the required range are clamped into it (the kernels
+ *              never leave the cache); the caller advances kv_len after the step.
+ * Ownership and errors as for every call; the cache rows written are only
+ * those at position kv_len[b].
+ */
+int fa3q_decode_append_attn(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                            const float* scale, int8_t* k_nope_q, uint16_t* k_rope, uint16_t* v,
+                            const int32_t* kv_len, int64_t B, int64_t H, int64_t T, int64_t Dn,
+                            int64_t Dr, int64_t Dv, float sm_scale, float* out, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

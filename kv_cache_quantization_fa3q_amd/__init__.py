@@ -20,6 +20,7 @@ from .ops import (  # noqa: F401
     fa3q_calibrate_max_windows,
     fa3q_calibrate_perhead,
     fa3q_calibrate_workspace_bytes,
+    fa3q_decode_append_attn,
     fa3q_decode_attn,
     fa3q_decode_attn_workspace_bytes,
     fa3q_init_minmax,

@@ -48,6 +48,8 @@ SIGNATURES = {
     "fa3q_decode_attn_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
     "fa3q_decode_attn": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_float,
                                 _vp, _vp, _sz, _vp]),
+    "fa3q_decode_append_attn": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
+                                       ctypes.c_float, _vp, _vp, _sz, _vp]),
 }
 
 _lock = threading.Lock()

@@ -21,6 +21,14 @@
 // combine kernel merges them; with one split the output is written directly.
 // Cache loads carry the nontemporal hint: each byte is read once (about 10% more bandwidth
 // than plain loads on MI355X at the MLA shape).
+//
+// Decode step with append and ragged lengths (fa3q_decode_append_attn): sequence b holds
+// kv_len[b] cached tokens out of a capacity of T.  With a new token, the split that owns
+// position kv_len[b] quantises the new K-nope row exactly as fa3q_quantize_k does (same
+// per-head scale, correctly rounded quotient, round half to even, clamp to +-127), stores
+// it with the new K-rope and V rows at that position, and scores and weights the token
+// from registers; attention then covers kv_len[b] + 1 tokens.  Without one it covers
+// kv_len[b].  Splits past a sequence's end leave an empty softmax state.
 #include <cmath>
 
 #include "fa3q_internal.hpp"
@@ -43,6 +51,9 @@ struct DecodeArgs {
   const uint16_t* kr;
   const uint16_t* v;
   float* out;
+  const int32_t* kv_len;   // [B] cached tokens per sequence (ragged kernels only)
+  const uint16_t* k_new;   // (B,H,Dn+Dr) token to append, or null
+  const uint16_t* v_new;   // (B,H,Dv)
   float* ws_ml;  // [B*H*nsplit][2] (max, sum)
   float* ws_o;   // [B*H*nsplit][Dv]
   int64_t T;
@@ -98,7 +109,21 @@ __device__ __forceinline__ uint4 load_nt(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-template <int LK, int LV>
+// 4 bf16 values (two dwords) -> 4 INT8 codes in one dword, little-endian element order:
+// clamp(round_half_even(fl32(x / s)), -127, 127) with the IEEE quotient; 0 when s == 0.
+__device__ __forceinline__ uint32_t quant4_exact(uint32_t w0, uint32_t w1, float s) {
+  const float xv[4] = {bf16_lo(w0), bf16_hi(w0), bf16_lo(w1), bf16_hi(w1)};
+  uint32_t o = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = s == 0.0f ? 0 : static_cast<int>(__builtin_amdgcn_fmed3f(rintf(xv[i] / s), -127.0f, 127.0f));
+    o |= (static_cast<uint32_t>(c) & 0xffu) << (8 * i);
+  }
+  return o;
+}
+
+// kVar: ragged lengths from kv_len[] and, when k_new is set, the appended token.
+template <int LK, int LV, bool kVar>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
   extern __shared__ float smem[];
   float* sc = smem;                       // [split_len] scores, then probabilities
@@ -109,10 +134,36 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
   const int sp = static_cast<int>(blockIdx.x) - bh * a.nsplit;
   const int h = bh % a.H;
   const int64_t t0 = static_cast<int64_t>(sp) * a.split_len;
-  const int n = static_cast<int>(min(a.T - t0, static_cast<int64_t>(a.split_len)));
   const int tid = static_cast<int>(threadIdx.x);
   const int lane = lane_id();
   const int wave = tid / kWave;
+  // tokens this split attends to: n from the cache, plus the new one when it owns it
+  int n = static_cast<int>(min(a.T - t0, static_cast<int64_t>(a.split_len)));
+  bool own_new = false;
+  int64_t pos_new = 0;
+  if constexpr (kVar) {
+    // lengths out of range are clamped, so no access leaves the cache
+    int64_t len = a.kv_len[bh / a.H];
+    if (a.k_new) {
+      pos_new = min(max(len, int64_t{0}), a.T - 1);
+      len = pos_new;
+      own_new = pos_new >= t0 && pos_new < t0 + a.split_len;
+    } else {
+      len = min(max(len, int64_t{1}), a.T);
+    }
+    n = static_cast<int>(max(int64_t{0}, min(len - t0, static_cast<int64_t>(a.split_len))));
+    if (n == 0 && !own_new) {
+      // past the sequence's end: an empty softmax state for the combine
+      const int64_t row = static_cast<int64_t>(bh) * a.nsplit + sp;
+      for (int dim = tid; dim < a.Dv; dim += kThreads) a.ws_o[row * a.Dv + dim] = 0.0f;
+      if (tid == 0) {
+        a.ws_ml[2 * row] = -INFINITY;
+        a.ws_ml[2 * row + 1] = 0.0f;
+      }
+      return;
+    }
+  }
+  const int n_all = n + (own_new ? 1 : 0);  // scores in LDS: the cached tokens, then the new one
 
   // ---------------------------------------------------------------- phase 1: scores
   {
@@ -178,12 +229,36 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
         if (j == 0 && tt < n) sc[tt] = s * a.sm_log2;
       }
     }
+    if constexpr (kVar) {
+      if (own_new && wave == 0) {
+        // every slot of wave 0 quantises the same new row; slot 0 stores it and its score
+        const uint16_t* knew = a.k_new + static_cast<int64_t>(bh) * Dk;
+        const int64_t at = static_cast<int64_t>(bh) * a.T + pos_new;
+        uint4 cn = make_uint4(0, 0, 0, 0), rn = make_uint4(0, 0, 0, 0);
+        if (has_n) {
+          const uint4* p = reinterpret_cast<const uint4*>(knew + 16 * j);
+          const uint4 u0 = p[0], u1 = p[1];
+          cn = make_uint4(quant4_exact(u0.x, u0.y, head_scale), quant4_exact(u0.z, u0.w, head_scale),
+                          quant4_exact(u1.x, u1.y, head_scale), quant4_exact(u1.z, u1.w, head_scale));
+          if (slot == 0) *reinterpret_cast<uint4*>(const_cast<int8_t*>(a.kq) + at * a.Dn + 16 * j) = cn;
+        }
+        if (has_r) {
+          rn = *reinterpret_cast<const uint4*>(knew + a.Dn + 8 * j);
+          if (slot == 0) *reinterpret_cast<uint4*>(const_cast<uint16_t*>(a.kr) + at * a.Dr + 8 * j) = rn;
+        }
+        float s = 0.0f;
+        if (has_n) s = head_scale * dot16_i8(qn, qsum, cn);
+        if (has_r) s += dot8_bf16(qr, rn);
+        s = group_sum<LK>(s);
+        if (j == 0 && slot == 0) sc[n] = s * a.sm_log2;
+      }
+    }
   }
   lds_barrier();
 
   // ---------------------------------------------------------------- phase 2: softmax
   float m = -INFINITY;
-  for (int i = tid; i < n; i += kThreads) m = fmaxf(m, sc[i]);
+  for (int i = tid; i < n_all; i += kThreads) m = fmaxf(m, sc[i]);
   m = wave_max(m);
   if (lane == 0) red[wave] = m;
   lds_barrier();
@@ -191,7 +266,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
   for (int w = 1; w < kWaves; ++w) m = fmaxf(m, red[w]);
   float l = 0.0f;
-  for (int i = tid; i < n; i += kThreads) {
+  for (int i = tid; i < n_all; i += kThreads) {
     const float p = exp2f(sc[i] - m);
     sc[i] = p;
     l += p;
@@ -238,6 +313,21 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
         acc[6] = fmaf(p[u], bf16_lo(wv[u].w), acc[6]);
         acc[7] = fmaf(p[u], bf16_hi(wv[u].w), acc[7]);
       }
+    }
+  }
+  if constexpr (kVar) {
+    if (own_new && wave == 0 && vslot == 0) {
+      const uint4 wv = *reinterpret_cast<const uint4*>(a.v_new + static_cast<int64_t>(bh) * a.Dv + 8 * jv);
+      *reinterpret_cast<uint4*>(const_cast<uint16_t*>(a.v) + (static_cast<int64_t>(bh) * a.T + pos_new) * a.Dv + 8 * jv) = wv;
+      const float p = sc[n];
+      acc[0] = fmaf(p, bf16_lo(wv.x), acc[0]);
+      acc[1] = fmaf(p, bf16_hi(wv.x), acc[1]);
+      acc[2] = fmaf(p, bf16_lo(wv.y), acc[2]);
+      acc[3] = fmaf(p, bf16_hi(wv.y), acc[3]);
+      acc[4] = fmaf(p, bf16_lo(wv.z), acc[4]);
+      acc[5] = fmaf(p, bf16_hi(wv.z), acc[5]);
+      acc[6] = fmaf(p, bf16_lo(wv.w), acc[6]);
+      acc[7] = fmaf(p, bf16_hi(wv.w), acc[7]);
     }
   }
 #pragma unroll
@@ -307,29 +397,30 @@ int64_t next_pow2(int64_t v) {
 
 using KernelFn = void (*)(DecodeArgs);
 
-template <int LK>
+template <int LK, bool kVar>
 KernelFn pick_lv(int lv) {
   switch (lv) {
-    case 1: return decode_split_kernel<LK, 1>;
-    case 2: return decode_split_kernel<LK, 2>;
-    case 4: return decode_split_kernel<LK, 4>;
-    case 8: return decode_split_kernel<LK, 8>;
-    case 16: return decode_split_kernel<LK, 16>;
-    case 32: return decode_split_kernel<LK, 32>;
-    case 64: return decode_split_kernel<LK, 64>;
+    case 1: return decode_split_kernel<LK, 1, kVar>;
+    case 2: return decode_split_kernel<LK, 2, kVar>;
+    case 4: return decode_split_kernel<LK, 4, kVar>;
+    case 8: return decode_split_kernel<LK, 8, kVar>;
+    case 16: return decode_split_kernel<LK, 16, kVar>;
+    case 32: return decode_split_kernel<LK, 32, kVar>;
+    case 64: return decode_split_kernel<LK, 64, kVar>;
     default: return nullptr;
   }
 }
 
+template <bool kVar>
 KernelFn pick_kernel(int lk, int lv) {
   switch (lk) {
-    case 1: return pick_lv<1>(lv);
-    case 2: return pick_lv<2>(lv);
-    case 4: return pick_lv<4>(lv);
-    case 8: return pick_lv<8>(lv);
-    case 16: return pick_lv<16>(lv);
-    case 32: return pick_lv<32>(lv);
-    case 64: return pick_lv<64>(lv);
+    case 1: return pick_lv<1, kVar>(lv);
+    case 2: return pick_lv<2, kVar>(lv);
+    case 4: return pick_lv<4, kVar>(lv);
+    case 8: return pick_lv<8, kVar>(lv);
+    case 16: return pick_lv<16, kVar>(lv);
+    case 32: return pick_lv<32, kVar>(lv);
+    case 64: return pick_lv<64, kVar>(lv);
     default: return nullptr;
   }
 }
@@ -355,12 +446,17 @@ extern "C" size_t fa3q_decode_attn_workspace_bytes(int64_t B, int64_t H, int64_t
          static_cast<size_t>(B * H * p.nsplit) * static_cast<size_t>(Dv) * sizeof(float);
 }
 
-extern "C" int fa3q_decode_attn(const uint16_t* q, const int8_t* k_nope_q, const float* scale,
-                                const uint16_t* k_rope, const uint16_t* v, int64_t B, int64_t H,
-                                int64_t T, int64_t Dn, int64_t Dr, int64_t Dv, float sm_scale,
-                                float* out, void* workspace, size_t workspace_bytes,
-                                void* stream) {
+namespace fa3q {
+namespace {
+
+// Shared validation and launch of both decode entry points (kVar: ragged / append).
+template <bool kVar>
+int decode_launch(const uint16_t* q, const int8_t* k_nope_q, const float* scale, const uint16_t* k_rope,
+                  const uint16_t* v, const int32_t* kv_len, const uint16_t* k_new, const uint16_t* v_new,
+                  int64_t B, int64_t H, int64_t T, int64_t Dn, int64_t Dr, int64_t Dv, float sm_scale,
+                  float* out, void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k_nope_q || !scale || !v || !out || (Dr > 0 && !k_rope)) return FA3Q_ERR_NULL;
+  if (kVar && (!kv_len || (k_new != nullptr) != (v_new != nullptr))) return FA3Q_ERR_NULL;
   if (B <= 0 || H <= 0 || T <= 0) return FA3Q_ERR_SHAPE;
   if (!valid_dims(Dn, Dr, Dv)) return FA3Q_ERR_SHAPE;
   if (B > (int64_t{1} << 31) / H || T > (int64_t{1} << 40)) return FA3Q_ERR_SHAPE;
@@ -368,6 +464,8 @@ extern "C" int fa3q_decode_attn(const uint16_t* q, const int8_t* k_nope_q, const
   if (!std::isfinite(sm_scale)) return FA3Q_ERR_SHAPE;
   if (!is_aligned(q, 16) || !is_aligned(k_nope_q, 16) || (Dr > 0 && !is_aligned(k_rope, 16)) ||
       !is_aligned(v, 16) || !is_aligned(out, 16) || !is_aligned(scale, 4))
+    return FA3Q_ERR_ALIGN;
+  if (kVar && (!is_aligned(kv_len, 4) || (k_new && (!is_aligned(k_new, 16) || !is_aligned(v_new, 16)))))
     return FA3Q_ERR_ALIGN;
   const SplitPlan p = plan_splits(B, H, T);
   if (B * H * p.nsplit > (int64_t{1} << 31) - 1) return FA3Q_ERR_SHAPE;
@@ -378,7 +476,7 @@ extern "C" int fa3q_decode_attn(const uint16_t* q, const int8_t* k_nope_q, const
   }
   const int lk = static_cast<int>(next_pow2(std::max<int64_t>(Dn / 16, Dr / 8)));
   const int lv = static_cast<int>(Dv / 8);
-  KernelFn fn = pick_kernel(lk, lv);
+  KernelFn fn = pick_kernel<kVar>(lk, lv);
   if (!fn) return FA3Q_ERR_UNSUPPORTED;
 
   DecodeArgs a;
@@ -388,6 +486,9 @@ extern "C" int fa3q_decode_attn(const uint16_t* q, const int8_t* k_nope_q, const
   a.kr = k_rope;
   a.v = v;
   a.out = out;
+  a.kv_len = kv_len;
+  a.k_new = k_new;
+  a.v_new = v_new;
   a.ws_ml = need ? static_cast<float*>(workspace) : nullptr;
   a.ws_o = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                            round_up(static_cast<size_t>(B * H * p.nsplit) * 2 * sizeof(float), 256))
@@ -408,4 +509,26 @@ extern "C" int fa3q_decode_attn(const uint16_t* q, const int8_t* k_nope_q, const
                        as_stream(stream), a);
   }
   return launch_status();
+}
+
+}  // namespace
+}  // namespace fa3q
+
+extern "C" int fa3q_decode_attn(const uint16_t* q, const int8_t* k_nope_q, const float* scale,
+                                const uint16_t* k_rope, const uint16_t* v, int64_t B, int64_t H,
+                                int64_t T, int64_t Dn, int64_t Dr, int64_t Dv, float sm_scale,
+                                float* out, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  return decode_launch<false>(q, k_nope_q, scale, k_rope, v, nullptr, nullptr, nullptr, B, H, T, Dn, Dr,
+                              Dv, sm_scale, out, workspace, workspace_bytes, stream);
+}
+
+extern "C" int fa3q_decode_append_attn(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                                       const float* scale, int8_t* k_nope_q, uint16_t* k_rope,
+                                       uint16_t* v, const int32_t* kv_len, int64_t B, int64_t H,
+                                       int64_t T, int64_t Dn, int64_t Dr, int64_t Dv, float sm_scale,
+                                       float* out, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  return decode_launch<true>(q, k_nope_q, scale, k_rope, v, kv_len, k_new, v_new, B, H, T, Dn, Dr, Dv,
+                             sm_scale, out, workspace, workspace_bytes, stream);
 }

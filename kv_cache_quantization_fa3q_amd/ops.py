@@ -24,6 +24,7 @@ __all__ = [
     "fa3q_quantize_k",
     "fa3q_decode_attn_workspace_bytes",
     "fa3q_decode_attn",
+    "fa3q_decode_append_attn",
     "dtype_code",
 ]
 
@@ -184,4 +185,45 @@ def fa3q_decode_attn(q: torch.Tensor, k_nope_q: torch.Tensor, scale: torch.Tenso
                                 B, H, T, Dn, Dr, Dv, ctypes.c_float(float(sm_scale)), _ptr(out), _ptr(workspace),
                                 wbytes, _stream(stream))
     _check(st, "fa3q_decode_attn")
+    return out
+
+
+def fa3q_decode_append_attn(q: torch.Tensor, k_new: Optional[torch.Tensor], v_new: Optional[torch.Tensor],
+                            scale: torch.Tensor, k_nope_q: torch.Tensor, k_rope: torch.Tensor, v: torch.Tensor,
+                            kv_len: torch.Tensor, sm_scale: float, out: Optional[torch.Tensor] = None,
+                            workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One decode step over a cache of capacity ``T``: with ``k_new``/``v_new`` the token is appended
+    in place at position ``kv_len[b]`` and attention covers ``kv_len[b] + 1`` tokens; without them it
+    covers ``kv_len[b]`` tokens.  Returns float32 ``(B,H,Dv)``; ``kv_len`` (int32 ``[B]``) is not changed."""
+    if k_nope_q.dim() != 4 or k_nope_q.dtype != torch.int8:
+        raise ValueError("k_nope_q must be int8 (B, H, T, Dn)")
+    B, H, T, Dn = (int(s) for s in k_nope_q.shape)
+    Dr = int(k_rope.shape[-1]) if k_rope is not None else 0
+    Dv = int(v.shape[-1])
+    if q.shape != (B, H, Dn + Dr) or q.dtype != torch.bfloat16:
+        raise ValueError("q must be bfloat16 (B, H, Dn + Dr)")
+    if v.shape != (B, H, T, Dv) or v.dtype != torch.bfloat16:
+        raise ValueError("v must be bfloat16 (B, H, T, Dv)")
+    if k_rope is not None and (k_rope.shape != (B, H, T, Dr) or k_rope.dtype != torch.bfloat16):
+        raise ValueError("k_rope must be bfloat16 (B, H, T, Dr)")
+    if (k_new is None) != (v_new is None):
+        raise ValueError("k_new and v_new are given together or not at all")
+    if k_new is not None:
+        if k_new.shape != (B, H, Dn + Dr) or k_new.dtype != torch.bfloat16:
+            raise ValueError("k_new must be bfloat16 (B, H, Dn + Dr)")
+        if v_new.shape != (B, H, Dv) or v_new.dtype != torch.bfloat16:
+            raise ValueError("v_new must be bfloat16 (B, H, Dv)")
+    if kv_len.shape != (B,) or kv_len.dtype != torch.int32:
+        raise ValueError("kv_len must be int32 (B,)")
+    if out is None:
+        out = torch.empty((B, H, Dv), dtype=torch.float32, device=q.device)
+    _need_gpu("fa3q_decode_append_attn", q, k_new, v_new, scale, k_nope_q, k_rope, v, kv_len, out)
+    nbytes = int(lib().fa3q_decode_attn_workspace_bytes(B, H, T, Dv))
+    workspace = _workspace(nbytes, q.device, workspace)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().fa3q_decode_append_attn(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(scale), _ptr(k_nope_q),
+                                       _ptr(k_rope) if Dr > 0 else None, _ptr(v), _ptr(kv_len), B, H, T, Dn, Dr,
+                                       Dv, ctypes.c_float(float(sm_scale)), _ptr(out), _ptr(workspace), wbytes,
+                                       _stream(stream))
+    _check(st, "fa3q_decode_append_attn")
     return out

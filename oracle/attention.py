@@ -19,7 +19,7 @@ from __future__ import annotations
 import numpy as np
 
 from .floats import bf16_bits_to_f64
-from .quant import dequantize_k_nope
+from .quant import dequantize_k_nope, quantize_k
 
 
 def attention_fp64(q, k, v, sm_scale: float) -> np.ndarray:
@@ -47,3 +47,45 @@ def decode_attn(q_bits, codes, scale, rope_bits, v_bits, sm_scale: float) -> np.
     k_rope = bf16_bits_to_f64(rope_bits)
     k = np.concatenate([k_nope, k_rope], axis=-1)
     return attention_fp64(bf16_bits_to_f64(q_bits), k, bf16_bits_to_f64(v_bits), float(np.float32(sm_scale)))
+
+
+def decode_append_attn(q_bits, k_new_bits, v_new_bits, scale, codes, rope_bits, v_bits, kv_len,
+                       sm_scale: float, Dn: int):
+    """One decode step on a cache of capacity ``T`` with ragged lengths.
+
+    Readings (also in the design doc): A5 sequence ``b`` holds ``kv_len[b]`` cached
+    tokens at positions ``0 .. kv_len[b]-1``; the rest of its capacity is not
+    part of the attention.  A6 a new token (``k_new (B,H,Dn+Dr)``,
+    ``v_new (B,H,Dv)`` bf16 patterns) goes to the next free position
+    ``p = kv_len[b]``: its K-nope is quantised with the head's scale exactly as
+    :func:`quantize_k` does, its K-rope and V are copied, and the step's query
+    attends to positions ``0 .. p`` (the new token included).  Without a new
+    token the query attends to ``0 .. kv_len[b]-1``.
+
+    Returns ``(out (B,H,Dv) float64, codes, rope_bits, v_bits)`` with the
+    cache arrays after the step (copies; the inputs are not modified).
+    """
+    codes = np.array(codes, dtype=np.int8, copy=True)
+    rope_bits = np.array(rope_bits, dtype=np.uint16, copy=True)
+    v_bits = np.array(v_bits, dtype=np.uint16, copy=True)
+    B, H, T, _ = codes.shape
+    Dv = v_bits.shape[-1]
+    kv_len = np.asarray(kv_len, dtype=np.int64).reshape(B)
+    out = np.zeros((B, H, Dv), dtype=np.float64)
+    for b in range(B):
+        p = int(kv_len[b])
+        if k_new_bits is not None:
+            if not 0 <= p < T:
+                raise ValueError("appending needs 0 <= kv_len[b] < T")
+            new_codes, new_rope = quantize_k(np.asarray(k_new_bits, dtype=np.uint16)[b][None, :, None, :], scale, Dn)
+            codes[b, :, p, :] = new_codes[0, :, 0, :]
+            rope_bits[b, :, p, :] = new_rope[0, :, 0, :]
+            v_bits[b, :, p, :] = np.asarray(v_new_bits, dtype=np.uint16)[b]
+            n = p + 1
+        else:
+            if not 1 <= p <= T:
+                raise ValueError("attention needs 1 <= kv_len[b] <= T")
+            n = p
+        out[b] = decode_attn(np.asarray(q_bits)[b:b + 1], codes[b:b + 1, :, :n], scale, rope_bits[b:b + 1, :, :n],
+                             v_bits[b:b + 1, :, :n], sm_scale)[0]
+    return out, codes, rope_bits, v_bits

@@ -174,6 +174,33 @@ def test_decode_rejections():
     assert call(ws=_p(128)) == L.FA3Q_ERR_ALIGN
 
 
+
+@no_gpu_only
+def test_decode_append_rejections():
+    f = fa.lib().fa3q_decode_append_attn
+    ok = dict(q=_p(), kn=_p(), vn=_p(), s=_p(), kq=_p(), kr=_p(), v=_p(), kl=_p(), B=8, H=128, T=32768, Dn=128,
+              Dr=64, Dv=128, sm=0.07, o=_p(), ws=_p(), wsb=1 << 30)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["q"], a["kn"], a["vn"], a["s"], a["kq"], a["kr"], a["v"], a["kl"], a["B"], a["H"], a["T"],
+                 a["Dn"], a["Dr"], a["Dv"], ctypes.c_float(a["sm"]), a["o"], a["ws"], a["wsb"], None)
+
+    for name in ("q", "s", "kq", "kr", "v", "kl", "o"):
+        assert call(**{name: None}) == L.FA3Q_ERR_NULL, name
+    # the new token comes whole or not at all
+    assert call(vn=None) == L.FA3Q_ERR_NULL
+    assert call(kn=None) == L.FA3Q_ERR_NULL
+    assert call(T=0) == L.FA3Q_ERR_SHAPE
+    assert call(Dn=120) == L.FA3Q_ERR_SHAPE
+    assert call(Dv=96) == L.FA3Q_ERR_SHAPE
+    assert call(sm=float("nan")) == L.FA3Q_ERR_SHAPE
+    assert call(kn=_p(8)) == L.FA3Q_ERR_ALIGN
+    assert call(vn=_p(8)) == L.FA3Q_ERR_ALIGN
+    assert call(kl=_p(2)) == L.FA3Q_ERR_ALIGN
+    assert call(ws=None) == L.FA3Q_ERR_WORKSPACE
+    assert call(ws=_p(128)) == L.FA3Q_ERR_ALIGN
+
 def test_binding_refuses_host_tensors():
     import torch
     x = torch.zeros((1, 4, 64, 32), dtype=torch.float32)

@@ -96,3 +96,101 @@ def test_bf16_helpers_roundtrip():
     y = (rng.normal(size=10000) * np.exp(rng.uniform(-20, 20, size=10000))).astype(np.float32)
     tb = torch.from_numpy(y).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     np.testing.assert_array_equal(oracle.f32_to_bf16_bits_rne(y), tb)
+
+
+# ----------------------------------------------------------------------------- decode step
+
+
+def _step_inputs(rng, B=3, H=4, T=40, Dn=32, Dr=16, Dv=32):
+    k_full = _rand_bits(rng, (B, H, T, Dn + Dr), std=0.7)
+    v_full = _rand_bits(rng, (B, H, T, Dv))
+    qb = _rand_bits(rng, (B, H, Dn + Dr))
+    scale = np.exp(rng.uniform(-6, -3, size=H)).astype(np.float32)
+    return k_full, v_full, qb, scale
+
+
+def test_append_at_last_position_reproduces_full_quantisation_and_attention():
+    # The step writes the new token at position kv_len[b] = T-1: the cache must then equal
+    # quantize_k of the whole K (a different call of the pinned quantiser, on the full
+    # tensor), and the output the attention over all T tokens.
+    rng = np.random.default_rng(41)
+    B, H, T, Dn, Dr, Dv = 3, 4, 40, 32, 16, 32
+    k_full, v_full, qb, scale = _step_inputs(rng, B, H, T, Dn, Dr, Dv)
+    codes_full, rope_full = oracle.quantize_k(k_full, scale, Dn)
+    # cache holding the first T-1 tokens and junk in the last slot
+    codes = codes_full.copy()
+    junk = rng.integers(-127, 128, size=(B, H, Dn)).astype(np.int8)
+    codes[:, :, T - 1] = junk
+    rope = rope_full.copy()
+    rope[:, :, T - 1] = 0x7F00
+    vb = v_full.copy()
+    vb[:, :, T - 1] = 0x4000
+    kv_len = np.full(B, T - 1, np.int32)
+    out, c2, r2, v2 = oracle.decode_append_attn(qb, k_full[:, :, T - 1], v_full[:, :, T - 1], scale, codes, rope,
+                                                vb, kv_len, np.float32(1 / math.sqrt(Dn + Dr)), Dn)
+    np.testing.assert_array_equal(c2, codes_full)
+    np.testing.assert_array_equal(r2, rope_full)
+    np.testing.assert_array_equal(v2, v_full)
+    ref = oracle.decode_attn(qb, codes_full, scale, rope_full, v_full, np.float32(1 / math.sqrt(Dn + Dr)))
+    np.testing.assert_allclose(out, ref, rtol=1e-13, atol=1e-14)
+    # the input arrays are not modified
+    np.testing.assert_array_equal(codes[:, :, T - 1], junk)
+    assert (rope[:, :, T - 1] == 0x7F00).all() and (vb[:, :, T - 1] == 0x4000).all()
+
+
+def test_append_to_empty_cache_returns_the_new_value():
+    rng = np.random.default_rng(42)
+    B, H, T, Dn, Dr, Dv = 2, 3, 8, 16, 8, 16
+    k_full, v_full, qb, scale = _step_inputs(rng, B, H, T, Dn, Dr, Dv)
+    codes = rng.integers(-127, 128, size=(B, H, T, Dn)).astype(np.int8)
+    rope = _rand_bits(rng, (B, H, T, Dr))
+    vb = _rand_bits(rng, (B, H, T, Dv))
+    out, c2, _, _ = oracle.decode_append_attn(qb, k_full[:, :, 0], v_full[:, :, 0], scale, codes, rope, vb,
+                                              np.zeros(B, np.int32), 0.3, Dn)
+    # one token: its softmax weight is exactly 1
+    np.testing.assert_array_equal(out, oracle.bf16_bits_to_f64(v_full[:, :, 0]))
+    # rows other than position 0 are untouched
+    np.testing.assert_array_equal(c2[:, :, 1:], codes[:, :, 1:])
+
+
+def test_ragged_lengths_ignore_everything_past_the_length():
+    rng = np.random.default_rng(43)
+    B, H, T, Dn, Dr, Dv = 4, 2, 24, 16, 8, 16
+    _, _, qb, scale = _step_inputs(rng, B, H, T, Dn, Dr, Dv)
+    codes = rng.integers(-127, 128, size=(B, H, T, Dn)).astype(np.int8)
+    rope = _rand_bits(rng, (B, H, T, Dr))
+    vb = _rand_bits(rng, (B, H, T, Dv))
+    kv_len = np.array([1, 7, 23, 24], np.int32)
+    out, c2, r2, v2 = oracle.decode_append_attn(qb, None, None, scale, codes, rope, vb, kv_len, 0.25, Dn)
+    # nothing is written without a new token
+    np.testing.assert_array_equal(c2, codes)
+    np.testing.assert_array_equal(r2, rope)
+    np.testing.assert_array_equal(v2, vb)
+    # scrambling the capacity past each length changes nothing
+    codes_x, rope_x, vb_x = codes.copy(), rope.copy(), vb.copy()
+    for b, n in enumerate(kv_len):
+        codes_x[b, :, n:] = 127
+        rope_x[b, :, n:] = 0x4700  # 32768.0
+        vb_x[b, :, n:] = 0xC700
+    out_x, _, _, _ = oracle.decode_append_attn(qb, None, None, scale, codes_x, rope_x, vb_x, kv_len, 0.25, Dn)
+    np.testing.assert_array_equal(out, out_x)
+    # length 1: the first cached value
+    np.testing.assert_array_equal(out[0], oracle.bf16_bits_to_f64(vb[0, :, 0]))
+    # full length: the plain decode over the whole cache
+    np.testing.assert_allclose(out[3], oracle.decode_attn(qb[3:], codes[3:], scale, rope[3:], vb[3:], 0.25)[0],
+                               rtol=1e-14, atol=0)
+
+
+def test_append_validates_lengths():
+    rng = np.random.default_rng(44)
+    B, H, T, Dn, Dr, Dv = 1, 1, 4, 16, 8, 16
+    k_full, v_full, qb, scale = _step_inputs(rng, B, H, T, Dn, Dr, Dv)
+    codes = np.zeros((B, H, T, Dn), np.int8)
+    rope = np.zeros((B, H, T, Dr), np.uint16)
+    vb = np.zeros((B, H, T, Dv), np.uint16)
+    import pytest
+    with pytest.raises(ValueError):
+        oracle.decode_append_attn(qb, k_full[:, :, 0], v_full[:, :, 0], scale, codes, rope, vb,
+                                  np.array([T], np.int32), 1.0, Dn)
+    with pytest.raises(ValueError):
+        oracle.decode_append_attn(qb, None, None, scale, codes, rope, vb, np.array([0], np.int32), 1.0, Dn)

@@ -302,6 +302,41 @@ def main() -> int:
                                   "note": "append one token per (b,h) at position T-1, then attention over T "
                                           "(outside the step)"}
 
+    # Decode with Q (non-RoPE part), K-nope and V all INT8: V and Q get per-head scales from
+    # the library's own calibration (V: sequence 0 of the cache; Q: its non-RoPE part), are
+    # quantised by fa3q_quantize_k, then fa3q_decode_attn_qkv8 runs over the same K cache;
+    # measured outside the step.  384 B per cached token instead of 512.
+    def per_head_scale(x4):
+        mn = torch.empty(H, dtype=torch.float32, device=dev)
+        mx = torch.empty(H, dtype=torch.float32, device=dev)
+        rmin = torch.empty(H, dtype=torch.float32, device=dev)
+        rmax = torch.empty(H, dtype=torch.float32, device=dev)
+        fa.fa3q_init_minmax(rmin, rmax, stream=stream)
+        fa.fa3q_calibrate_perhead(x4, RATIO, mn, mx, stream=stream)
+        fa.fa3q_accumulate_minmax(rmin, rmax, mn, mx, stream=stream)
+        return fa.fa3q_qparams(rmin, rmax, stream=stream)
+
+    scale_v = per_head_scale(v[:1].contiguous())
+    scale_q = per_head_scale(q[:, :, :DN].contiguous().view(QB, H, 1, DN))
+    vq, _ = fa.fa3q_quantize_k(v, scale_v, DV, stream=stream)
+    qc, qrope = fa.fa3q_quantize_k(q.view(QB, H, 1, DN + DR), scale_q, DN, stream=stream)
+    qc, qrope = qc.view(QB, H, DN), qrope.view(QB, H, DR)
+    for _ in range(2):
+        fa.fa3q_decode_attn_qkv8(qc, qrope, scale_q, kq, scale, kr, vq, scale_v, sm, out, ws_dec, stream=stream)
+    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    b0.record(stream)
+    for _ in range(5):
+        fa.fa3q_decode_attn_qkv8(qc, qrope, scale_q, kq, scale, kr, vq, scale_v, sm, out, ws_dec, stream=stream)
+    b1.record(stream)
+    torch.cuda.synchronize()
+    q8_ms = b0.elapsed_time(b1) / 5
+    q8_bytes = QB * H * (QS * (DN + 2 * DR + DV) + DN + 2 * DR + 4 * DV)
+    breakdown["decode_qkv8"] = {"ms": q8_ms, "bytes": q8_bytes, "kv_gbs": q8_bytes / (q8_ms * 1e-3) / 1e9,
+                                "frac_hbm": q8_bytes / (q8_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                "note": "Q (non-RoPE), K-nope and V INT8 with per-head scales; 384 B per cached "
+                                        "token (outside the step)"}
+    del vq
+
     # device-to-device copy of COPY_BYTES: a reference ceiling for read+write streaming, and the
     # known-size kernel the HBM byte counters are scaled by
     src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)

@@ -13,6 +13,7 @@
  *   5. fa3q_decode_attn        -- single-query attention over INT8 K-nope + bf16 K-rope + bf16 V
  *   6. fa3q_decode_append_attn -- one decode step: append the new token to the cache in place
  *      (K-nope quantised as in 4), then attention over ragged per-sequence lengths
+ *   7. fa3q_decode_attn_qkv8   -- attention with Q (non-RoPE part), K-nope and V all INT8
  *
  * Sources, cited by page title and section:
  *   [MS] msModelSlim documentation, "FA3量化：Flash Attention 3激活量化算法说明"
@@ -241,6 +242,36 @@ int fa3q_decode_append_attn(const uint16_t* q, const uint16_t* k_new, const uint
                             const int32_t* kv_len, int64_t B, int64_t H, int64_t T, int64_t Dn,
                             int64_t Dr, int64_t Dv, float sm_scale, float* out, void* workspace,
                             size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* 7. Decode attention with Q, K and V per-head INT8                        */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * [MS] 简介 (overview): FA3 quantises the Q, K and V activations of attention
+ * to INT8, one scale per head.  Q's non-RoPE part and all of V get per-head
+ * codes from fa3q_quantize_k (V as a (B,H,T,Dv) tensor with Dr = 0, Q as a
+ * (B,H,1,Dn+Dr) tensor whose RoPE part comes back as bf16), each with its own
+ * calibrated scale; K-nope is the cache of fa3q_quantize_k.  For every (b, h):
+ *   s_t   = sm_scale * ( scale_q[h] * scale_k[h] * sum_{d<Dn} qc[b,h,d] * kc[b,h,t,d]
+ *                        + sum_{j<Dr} q_rope[b,h,j] * k_rope[b,h,t,j] )
+ *   out[b,h,:] = scale_v[h] * sum_t softmax(s)_t * vc[b,h,t,:]
+ * i.e. fa3q_decode_attn's attention over the dequantised Q, K and V.  The
+ * integer dot product is exact (int32); the rest is float32.
+ *
+ *   q_nope_q   device int8 (B,H,Dn), 16-byte aligned.
+ *   q_rope     device bf16 (B,H,Dr), 16-byte aligned; may be NULL iff Dr == 0.
+ *   scale_q, scale_k, scale_v  device float32 [H], 4-byte aligned.
+ *   k_nope_q, k_rope  the cache as in fa3q_decode_attn.
+ *   v_q        device int8 (B,H,T,Dv), 16-byte aligned.
+ *   out, T, Dn, Dr, sm_scale, workspace  as fa3q_decode_attn (same workspace query).
+ *   Dv a power of two in [16, 512].
+ */
+int fa3q_decode_attn_qkv8(const int8_t* q_nope_q, const uint16_t* q_rope, const float* scale_q,
+                          const int8_t* k_nope_q, const float* scale_k, const uint16_t* k_rope,
+                          const int8_t* v_q, const float* scale_v, int64_t B, int64_t H, int64_t T,
+                          int64_t Dn, int64_t Dr, int64_t Dv, float sm_scale, float* out, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -22,6 +22,7 @@ from .ops import (  # noqa: F401
     fa3q_calibrate_workspace_bytes,
     fa3q_decode_append_attn,
     fa3q_decode_attn,
+    fa3q_decode_attn_qkv8,
     fa3q_decode_attn_workspace_bytes,
     fa3q_init_minmax,
     fa3q_qparams,

@@ -50,6 +50,8 @@ SIGNATURES = {
                                 _vp, _vp, _sz, _vp]),
     "fa3q_decode_append_attn": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
                                        ctypes.c_float, _vp, _vp, _sz, _vp]),
+    "fa3q_decode_attn_qkv8": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
+                                     ctypes.c_float, _vp, _vp, _sz, _vp]),
 }
 
 _lock = threading.Lock()

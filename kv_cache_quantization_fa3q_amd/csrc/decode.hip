@@ -29,6 +29,12 @@
 // it with the new K-rope and V rows at that position, and scores and weights the token
 // from registers; attention then covers kv_len[b] + 1 tokens.  Without one it covers
 // kv_len[b].  Splits past a sequence's end leave an empty softmax state.
+//
+// Q, K and V all INT8 (fa3q_decode_attn_qkv8): Q's non-RoPE part and V carry per-head
+// codes too (from fa3q_quantize_k).  The non-RoPE score is scale_q[h]*scale_k[h] times an
+// exact integer dot product (v_dot4 over four code pairs per instruction), the RoPE part
+// stays bf16, and V is weighted as codes with scale_v[h] applied once at the end: 384
+// bytes per cached token instead of 512 at the MLA shape.
 #include <cmath>
 
 #include "fa3q_internal.hpp"
@@ -54,6 +60,10 @@ struct DecodeArgs {
   const int32_t* kv_len;   // [B] cached tokens per sequence (ragged kernels only)
   const uint16_t* k_new;   // (B,H,Dn+Dr) token to append, or null
   const uint16_t* v_new;   // (B,H,Dv)
+  const int8_t* qq;        // (B,H,Dn) query codes (INT8 kernels; q is then the (B,H,Dr) RoPE part)
+  const int8_t* vq;        // (B,H,T,Dv) value codes (INT8 kernels)
+  const float* scale_q;    // [H]
+  const float* scale_v;    // [H]
   float* ws_ml;  // [B*H*nsplit][2] (max, sum)
   float* ws_o;   // [B*H*nsplit][Dv]
   int64_t T;
@@ -123,8 +133,10 @@ __device__ __forceinline__ uint32_t quant4_exact(uint32_t w0, uint32_t w1, float
 }
 
 // kVar: ragged lengths from kv_len[] and, when k_new is set, the appended token.
-template <int LK, int LV, bool kVar>
+// kQ8: INT8 query (non-RoPE part) and INT8 values; LV is then Dv/16 lanes per token.
+template <int LK, int LV, bool kVar, bool kQ8>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
+  static_assert(!(kVar && kQ8), "the append step takes a bf16 cache");
   extern __shared__ float smem[];
   float* sc = smem;                       // [split_len] scores, then probabilities
   float* red = smem + a.split_len;        // [kWaves] block reduction scratch
@@ -173,10 +185,15 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     const bool has_n = j < (a.Dn >> 4);
     const bool has_r = j < (a.Dr >> 3);
     const int Dk = a.Dn + a.Dr;
-    const uint16_t* qrow = a.q + static_cast<int64_t>(bh) * Dk;
+    const uint16_t* qrow = a.q + static_cast<int64_t>(bh) * Dk;  // bf16 query row (bf16 kernels)
+    // RoPE part of the query: inside that row, or its own (B,H,Dr) tensor (INT8 kernels)
+    const uint16_t* qrope = kQ8 ? a.q + static_cast<int64_t>(bh) * a.Dr : qrow + a.Dn;
     float qn[16], qr[8];
     float qsum = 0.0f;
-    if (has_n) {
+    uint4 qc = make_uint4(0, 0, 0, 0);  // query codes (INT8 kernels)
+    if (kQ8) {
+      if (has_n) qc = *reinterpret_cast<const uint4*>(a.qq + static_cast<int64_t>(bh) * a.Dn + 16 * j);
+    } else if (has_n) {
       const uint4* p = reinterpret_cast<const uint4*>(qrow + 16 * j);
       const uint4 u0 = p[0], u1 = p[1];
       const uint32_t w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
@@ -192,7 +209,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
       for (int i = 0; i < 16; ++i) qn[i] = 0.0f;
     }
     if (has_r) {
-      const uint4 u = *reinterpret_cast<const uint4*>(qrow + a.Dn + 8 * j);
+      const uint4 u = *reinterpret_cast<const uint4*>(qrope + 8 * j);
       const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -203,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) qr[i] = 0.0f;
     }
-    const float head_scale = a.scale[h];
+    const float head_scale = kQ8 ? a.scale_q[h] * a.scale[h] : a.scale[h];
     const int8_t* kq = a.kq + (static_cast<int64_t>(bh) * a.T + t0) * a.Dn + 16 * j;
     const uint16_t* kr = a.kr + (static_cast<int64_t>(bh) * a.T + t0) * a.Dr + 8 * j;
     const int step = kWaves * kSlots;
@@ -223,7 +240,17 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
       for (int u = 0; u < kUk; ++u) {
         const int tt = base + u * step;
         float s = 0.0f;
-        if (has_n) s = head_scale * dot16_i8(qn, qsum, wn[u]);
+        if (has_n) {
+          if constexpr (kQ8) {
+            int d = __builtin_amdgcn_sdot4(static_cast<int>(qc.x), static_cast<int>(wn[u].x), 0, false);
+            d = __builtin_amdgcn_sdot4(static_cast<int>(qc.y), static_cast<int>(wn[u].y), d, false);
+            d = __builtin_amdgcn_sdot4(static_cast<int>(qc.z), static_cast<int>(wn[u].z), d, false);
+            d = __builtin_amdgcn_sdot4(static_cast<int>(qc.w), static_cast<int>(wn[u].w), d, false);
+            s = head_scale * static_cast<float>(d);  // |d| <= 16*127*127: exact in float32
+          } else {
+            s = head_scale * dot16_i8(qn, qsum, wn[u]);
+          }
+        }
         if (has_r) s += dot8_bf16(qr, wr[u]);
         s = group_sum<LK>(s);
         if (j == 0 && tt < n) sc[tt] = s * a.sm_log2;
@@ -281,13 +308,17 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
 
   // ---------------------------------------------------------------- phase 3: P . V
   constexpr int kVSlots = kWave / LV;
+  constexpr int kVD = kQ8 ? 16 : 8;  // value dims per lane: one 16-byte load per token
   const int jv = lane % LV;
   const int vslot = lane / LV;
-  float acc[8];
+  float acc[kVD];
 #pragma unroll
-  for (int d = 0; d < 8; ++d) acc[d] = 0.0f;
+  for (int d = 0; d < kVD; ++d) acc[d] = 0.0f;
+  float psum = 0.0f;  // INT8 values: sum of the weights, for the +128 offset of the byte reads
   {
-    const uint16_t* vp = a.v + (static_cast<int64_t>(bh) * a.T + t0) * a.Dv + 8 * jv;
+    const char* vp = kQ8 ? reinterpret_cast<const char*>(a.vq + (static_cast<int64_t>(bh) * a.T + t0) * a.Dv + 16 * jv)
+                         : reinterpret_cast<const char*>(a.v + (static_cast<int64_t>(bh) * a.T + t0) * a.Dv + 8 * jv);
+    const int64_t vrow = kQ8 ? a.Dv : 2 * static_cast<int64_t>(a.Dv);  // bytes per token
     const int step = kWaves * kVSlots;
     for (int base = wave * kVSlots + vslot; base < n; base += step * kUv) {
       uint4 wv[kUv];
@@ -298,22 +329,41 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
         wv[u] = make_uint4(0, 0, 0, 0);
         p[u] = 0.0f;
         if (tt < n) {
-          wv[u] = load_nt(vp + static_cast<int64_t>(tt) * a.Dv);
+          wv[u] = load_nt(vp + static_cast<int64_t>(tt) * vrow);
           p[u] = sc[tt];
         }
       }
 #pragma unroll
       for (int u = 0; u < kUv; ++u) {
-        acc[0] = fmaf(p[u], bf16_lo(wv[u].x), acc[0]);
-        acc[1] = fmaf(p[u], bf16_hi(wv[u].x), acc[1]);
-        acc[2] = fmaf(p[u], bf16_lo(wv[u].y), acc[2]);
-        acc[3] = fmaf(p[u], bf16_hi(wv[u].y), acc[3]);
-        acc[4] = fmaf(p[u], bf16_lo(wv[u].z), acc[4]);
-        acc[5] = fmaf(p[u], bf16_hi(wv[u].z), acc[5]);
-        acc[6] = fmaf(p[u], bf16_lo(wv[u].w), acc[6]);
-        acc[7] = fmaf(p[u], bf16_hi(wv[u].w), acc[7]);
+        if constexpr (kQ8) {
+          const uint32_t d[4] = {wv[u].x ^ 0x80808080u, wv[u].y ^ 0x80808080u, wv[u].z ^ 0x80808080u,
+                                 wv[u].w ^ 0x80808080u};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[4 * i + 0] = fmaf(p[u], static_cast<float>(d[i] & 0xffu), acc[4 * i + 0]);
+            acc[4 * i + 1] = fmaf(p[u], static_cast<float>((d[i] >> 8) & 0xffu), acc[4 * i + 1]);
+            acc[4 * i + 2] = fmaf(p[u], static_cast<float>((d[i] >> 16) & 0xffu), acc[4 * i + 2]);
+            acc[4 * i + 3] = fmaf(p[u], static_cast<float>(d[i] >> 24), acc[4 * i + 3]);
+          }
+          psum += p[u];
+        } else {
+          acc[0] = fmaf(p[u], bf16_lo(wv[u].x), acc[0]);
+          acc[1] = fmaf(p[u], bf16_hi(wv[u].x), acc[1]);
+          acc[2] = fmaf(p[u], bf16_lo(wv[u].y), acc[2]);
+          acc[3] = fmaf(p[u], bf16_hi(wv[u].y), acc[3]);
+          acc[4] = fmaf(p[u], bf16_lo(wv[u].z), acc[4]);
+          acc[5] = fmaf(p[u], bf16_hi(wv[u].z), acc[5]);
+          acc[6] = fmaf(p[u], bf16_lo(wv[u].w), acc[6]);
+          acc[7] = fmaf(p[u], bf16_hi(wv[u].w), acc[7]);
+        }
       }
     }
+  }
+  if constexpr (kQ8) {
+    // codes were read as unsigned bytes code + 128; the head scale comes in once
+    const float sv = a.scale_v[h];
+#pragma unroll
+    for (int d = 0; d < kVD; ++d) acc[d] = fmaf(-128.0f, psum, acc[d]) * sv;
   }
   if constexpr (kVar) {
     if (own_new && wave == 0 && vslot == 0) {
@@ -331,10 +381,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     }
   }
 #pragma unroll
-  for (int d = 0; d < 8; ++d) acc[d] = slot_sum<LV>(acc[d]);
+  for (int d = 0; d < kVD; ++d) acc[d] = slot_sum<LV>(acc[d]);
   if (vslot == 0) {
 #pragma unroll
-    for (int d = 0; d < 8; ++d) part[wave * a.Dv + 8 * jv + d] = acc[d];
+    for (int d = 0; d < kVD; ++d) part[wave * a.Dv + kVD * jv + d] = acc[d];
   }
   lds_barrier();
   const int64_t row = static_cast<int64_t>(bh) * a.nsplit + sp;
@@ -397,30 +447,32 @@ int64_t next_pow2(int64_t v) {
 
 using KernelFn = void (*)(DecodeArgs);
 
-template <int LK, bool kVar>
+template <int LK, bool kVar, bool kQ8>
 KernelFn pick_lv(int lv) {
   switch (lv) {
-    case 1: return decode_split_kernel<LK, 1, kVar>;
-    case 2: return decode_split_kernel<LK, 2, kVar>;
-    case 4: return decode_split_kernel<LK, 4, kVar>;
-    case 8: return decode_split_kernel<LK, 8, kVar>;
-    case 16: return decode_split_kernel<LK, 16, kVar>;
-    case 32: return decode_split_kernel<LK, 32, kVar>;
-    case 64: return decode_split_kernel<LK, 64, kVar>;
+    case 1: return decode_split_kernel<LK, 1, kVar, kQ8>;
+    case 2: return decode_split_kernel<LK, 2, kVar, kQ8>;
+    case 4: return decode_split_kernel<LK, 4, kVar, kQ8>;
+    case 8: return decode_split_kernel<LK, 8, kVar, kQ8>;
+    case 16: return decode_split_kernel<LK, 16, kVar, kQ8>;
+    case 32: return decode_split_kernel<LK, 32, kVar, kQ8>;
+    case 64:
+      if constexpr (kQ8) return nullptr;  // Dv = 1024 is past the supported range
+      else return decode_split_kernel<LK, 64, kVar, kQ8>;
     default: return nullptr;
   }
 }
 
-template <bool kVar>
+template <bool kVar, bool kQ8>
 KernelFn pick_kernel(int lk, int lv) {
   switch (lk) {
-    case 1: return pick_lv<1, kVar>(lv);
-    case 2: return pick_lv<2, kVar>(lv);
-    case 4: return pick_lv<4, kVar>(lv);
-    case 8: return pick_lv<8, kVar>(lv);
-    case 16: return pick_lv<16, kVar>(lv);
-    case 32: return pick_lv<32, kVar>(lv);
-    case 64: return pick_lv<64, kVar>(lv);
+    case 1: return pick_lv<1, kVar, kQ8>(lv);
+    case 2: return pick_lv<2, kVar, kQ8>(lv);
+    case 4: return pick_lv<4, kVar, kQ8>(lv);
+    case 8: return pick_lv<8, kVar, kQ8>(lv);
+    case 16: return pick_lv<16, kVar, kQ8>(lv);
+    case 32: return pick_lv<32, kVar, kQ8>(lv);
+    case 64: return pick_lv<64, kVar, kQ8>(lv);
     default: return nullptr;
   }
 }
@@ -449,21 +501,39 @@ extern "C" size_t fa3q_decode_attn_workspace_bytes(int64_t B, int64_t H, int64_t
 namespace fa3q {
 namespace {
 
-// Shared validation and launch of both decode entry points (kVar: ragged / append).
-template <bool kVar>
+// INT8 query and values of fa3q_decode_attn_qkv8 (unused by the bf16 entry points).
+struct Int8QV {
+  const int8_t* qq = nullptr;
+  const int8_t* vq = nullptr;
+  const float* scale_q = nullptr;
+  const float* scale_v = nullptr;
+};
+
+// Shared validation and launch of the decode entry points (kVar: ragged / append;
+// kQ8: INT8 query and values, with q the (B,H,Dr) RoPE part and v unused).
+template <bool kVar, bool kQ8>
 int decode_launch(const uint16_t* q, const int8_t* k_nope_q, const float* scale, const uint16_t* k_rope,
                   const uint16_t* v, const int32_t* kv_len, const uint16_t* k_new, const uint16_t* v_new,
-                  int64_t B, int64_t H, int64_t T, int64_t Dn, int64_t Dr, int64_t Dv, float sm_scale,
-                  float* out, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!q || !k_nope_q || !scale || !v || !out || (Dr > 0 && !k_rope)) return FA3Q_ERR_NULL;
+                  const Int8QV& i8, int64_t B, int64_t H, int64_t T, int64_t Dn, int64_t Dr, int64_t Dv,
+                  float sm_scale, float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (kQ8) {
+    if (!i8.qq || !i8.vq || !i8.scale_q || !i8.scale_v || !k_nope_q || !scale || !out || (Dr > 0 && (!q || !k_rope)))
+      return FA3Q_ERR_NULL;
+  } else if (!q || !k_nope_q || !scale || !v || !out || (Dr > 0 && !k_rope)) {
+    return FA3Q_ERR_NULL;
+  }
   if (kVar && (!kv_len || (k_new != nullptr) != (v_new != nullptr))) return FA3Q_ERR_NULL;
   if (B <= 0 || H <= 0 || T <= 0) return FA3Q_ERR_SHAPE;
-  if (!valid_dims(Dn, Dr, Dv)) return FA3Q_ERR_SHAPE;
+  if (!valid_dims(Dn, Dr, Dv) || (kQ8 && Dv < 16)) return FA3Q_ERR_SHAPE;
   if (B > (int64_t{1} << 31) / H || T > (int64_t{1} << 40)) return FA3Q_ERR_SHAPE;
   if (B * H * T > (int64_t{1} << 62) / (Dn + Dr + Dv)) return FA3Q_ERR_SHAPE;
   if (!std::isfinite(sm_scale)) return FA3Q_ERR_SHAPE;
-  if (!is_aligned(q, 16) || !is_aligned(k_nope_q, 16) || (Dr > 0 && !is_aligned(k_rope, 16)) ||
-      !is_aligned(v, 16) || !is_aligned(out, 16) || !is_aligned(scale, 4))
+  if ((Dr > 0 && !is_aligned(q, 16)) || !is_aligned(k_nope_q, 16) || (Dr > 0 && !is_aligned(k_rope, 16)) ||
+      !is_aligned(out, 16) || !is_aligned(scale, 4))
+    return FA3Q_ERR_ALIGN;
+  if (kQ8 ? (!is_aligned(i8.qq, 16) || !is_aligned(i8.vq, 16) || !is_aligned(i8.scale_q, 4) ||
+             !is_aligned(i8.scale_v, 4))
+          : (!is_aligned(q, 16) || !is_aligned(v, 16)))
     return FA3Q_ERR_ALIGN;
   if (kVar && (!is_aligned(kv_len, 4) || (k_new && (!is_aligned(k_new, 16) || !is_aligned(v_new, 16)))))
     return FA3Q_ERR_ALIGN;
@@ -475,8 +545,8 @@ int decode_launch(const uint16_t* q, const int8_t* k_nope_q, const float* scale,
     if (!is_aligned(workspace, 256)) return FA3Q_ERR_ALIGN;
   }
   const int lk = static_cast<int>(next_pow2(std::max<int64_t>(Dn / 16, Dr / 8)));
-  const int lv = static_cast<int>(Dv / 8);
-  KernelFn fn = pick_kernel<kVar>(lk, lv);
+  const int lv = static_cast<int>(Dv / (kQ8 ? 16 : 8));
+  KernelFn fn = pick_kernel<kVar, kQ8>(lk, lv);
   if (!fn) return FA3Q_ERR_UNSUPPORTED;
 
   DecodeArgs a;
@@ -489,6 +559,10 @@ int decode_launch(const uint16_t* q, const int8_t* k_nope_q, const float* scale,
   a.kv_len = kv_len;
   a.k_new = k_new;
   a.v_new = v_new;
+  a.qq = i8.qq;
+  a.vq = i8.vq;
+  a.scale_q = i8.scale_q;
+  a.scale_v = i8.scale_v;
   a.ws_ml = need ? static_cast<float*>(workspace) : nullptr;
   a.ws_o = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                            round_up(static_cast<size_t>(B * H * p.nsplit) * 2 * sizeof(float), 256))
@@ -519,8 +593,8 @@ extern "C" int fa3q_decode_attn(const uint16_t* q, const int8_t* k_nope_q, const
                                 int64_t T, int64_t Dn, int64_t Dr, int64_t Dv, float sm_scale,
                                 float* out, void* workspace, size_t workspace_bytes,
                                 void* stream) {
-  return decode_launch<false>(q, k_nope_q, scale, k_rope, v, nullptr, nullptr, nullptr, B, H, T, Dn, Dr,
-                              Dv, sm_scale, out, workspace, workspace_bytes, stream);
+  return decode_launch<false, false>(q, k_nope_q, scale, k_rope, v, nullptr, nullptr, nullptr, Int8QV{}, B, H, T,
+                                     Dn, Dr, Dv, sm_scale, out, workspace, workspace_bytes, stream);
 }
 
 extern "C" int fa3q_decode_append_attn(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
@@ -529,6 +603,20 @@ extern "C" int fa3q_decode_append_attn(const uint16_t* q, const uint16_t* k_new,
                                        int64_t T, int64_t Dn, int64_t Dr, int64_t Dv, float sm_scale,
                                        float* out, void* workspace, size_t workspace_bytes,
                                        void* stream) {
-  return decode_launch<true>(q, k_nope_q, scale, k_rope, v, kv_len, k_new, v_new, B, H, T, Dn, Dr, Dv,
-                             sm_scale, out, workspace, workspace_bytes, stream);
+  return decode_launch<true, false>(q, k_nope_q, scale, k_rope, v, kv_len, k_new, v_new, Int8QV{}, B, H, T, Dn,
+                                    Dr, Dv, sm_scale, out, workspace, workspace_bytes, stream);
+}
+
+extern "C" int fa3q_decode_attn_qkv8(const int8_t* q_nope_q, const uint16_t* q_rope, const float* scale_q,
+                                     const int8_t* k_nope_q, const float* scale_k, const uint16_t* k_rope,
+                                     const int8_t* v_q, const float* scale_v, int64_t B, int64_t H, int64_t T,
+                                     int64_t Dn, int64_t Dr, int64_t Dv, float sm_scale, float* out,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  Int8QV i8;
+  i8.qq = q_nope_q;
+  i8.vq = v_q;
+  i8.scale_q = scale_q;
+  i8.scale_v = scale_v;
+  return decode_launch<false, true>(q_rope, k_nope_q, scale_k, k_rope, nullptr, nullptr, nullptr, nullptr, i8, B, H,
+                                    T, Dn, Dr, Dv, sm_scale, out, workspace, workspace_bytes, stream);
 }

@@ -25,6 +25,7 @@ __all__ = [
     "fa3q_decode_attn_workspace_bytes",
     "fa3q_decode_attn",
     "fa3q_decode_append_attn",
+    "fa3q_decode_attn_qkv8",
     "dtype_code",
 ]
 
@@ -226,4 +227,38 @@ def fa3q_decode_append_attn(q: torch.Tensor, k_new: Optional[torch.Tensor], v_ne
                                        Dv, ctypes.c_float(float(sm_scale)), _ptr(out), _ptr(workspace), wbytes,
                                        _stream(stream))
     _check(st, "fa3q_decode_append_attn")
+    return out
+
+
+def fa3q_decode_attn_qkv8(q_nope_q: torch.Tensor, q_rope: Optional[torch.Tensor], scale_q: torch.Tensor,
+                          k_nope_q: torch.Tensor, scale_k: torch.Tensor, k_rope: Optional[torch.Tensor],
+                          v_q: torch.Tensor, scale_v: torch.Tensor, sm_scale: float,
+                          out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                          stream=None) -> torch.Tensor:
+    """Attention with INT8 query (non-RoPE part), K-nope and V, per-head scales -> float32 ``(B,H,Dv)``."""
+    if k_nope_q.dim() != 4 or k_nope_q.dtype != torch.int8:
+        raise ValueError("k_nope_q must be int8 (B, H, T, Dn)")
+    B, H, T, Dn = (int(s) for s in k_nope_q.shape)
+    Dr = int(k_rope.shape[-1]) if k_rope is not None else 0
+    if v_q.dim() != 4 or v_q.dtype != torch.int8 or tuple(v_q.shape[:3]) != (B, H, T):
+        raise ValueError("v_q must be int8 (B, H, T, Dv)")
+    Dv = int(v_q.shape[-1])
+    if q_nope_q.shape != (B, H, Dn) or q_nope_q.dtype != torch.int8:
+        raise ValueError("q_nope_q must be int8 (B, H, Dn)")
+    if Dr > 0 and (q_rope is None or q_rope.shape != (B, H, Dr) or q_rope.dtype != torch.bfloat16):
+        raise ValueError("q_rope must be bfloat16 (B, H, Dr)")
+    if k_rope is not None and (k_rope.shape != (B, H, T, Dr) or k_rope.dtype != torch.bfloat16):
+        raise ValueError("k_rope must be bfloat16 (B, H, T, Dr)")
+    if out is None:
+        out = torch.empty((B, H, Dv), dtype=torch.float32, device=k_nope_q.device)
+    _need_gpu("fa3q_decode_attn_qkv8", q_nope_q, q_rope if Dr > 0 else None, scale_q, k_nope_q, scale_k, k_rope,
+              v_q, scale_v, out)
+    nbytes = int(lib().fa3q_decode_attn_workspace_bytes(B, H, T, Dv))
+    workspace = _workspace(nbytes, k_nope_q.device, workspace)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().fa3q_decode_attn_qkv8(_ptr(q_nope_q), _ptr(q_rope) if Dr > 0 else None, _ptr(scale_q),
+                                     _ptr(k_nope_q), _ptr(scale_k), _ptr(k_rope) if Dr > 0 else None, _ptr(v_q),
+                                     _ptr(scale_v), B, H, T, Dn, Dr, Dv, ctypes.c_float(float(sm_scale)), _ptr(out),
+                                     _ptr(workspace), wbytes, _stream(stream))
+    _check(st, "fa3q_decode_attn_qkv8")
     return out

@@ -35,7 +35,7 @@ from .recall_window import (
     qparams,
 )
 from .quant import quantize_k, dequantize_k_nope
-from .attention import attention_fp64, decode_attn, decode_append_attn
+from .attention import attention_fp64, decode_attn, decode_append_attn, decode_attn_qkv8
 
 __all__ = [
     "bf16_bits_to_f32",
@@ -55,4 +55,5 @@ __all__ = [
     "attention_fp64",
     "decode_attn",
     "decode_append_attn",
+    "decode_attn_qkv8",
 ]

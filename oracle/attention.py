@@ -89,3 +89,26 @@ def decode_append_attn(q_bits, k_new_bits, v_new_bits, scale, codes, rope_bits, 
         out[b] = decode_attn(np.asarray(q_bits)[b:b + 1], codes[b:b + 1, :, :n], scale, rope_bits[b:b + 1, :, :n],
                              v_bits[b:b + 1, :, :n], sm_scale)[0]
     return out, codes, rope_bits, v_bits
+
+
+def decode_attn_qkv8(q_codes, q_rope_bits, scale_q, k_codes, scale_k, k_rope_bits, v_codes, scale_v,
+                     sm_scale: float) -> np.ndarray:
+    """Attention with Q, K and V all per-head INT8 (the RoPE parts of Q and K in bf16).
+
+    Readings (also in the design doc): A8 Q's non-RoPE part and all of V are quantised
+    per head with the same symmetric formula as K (``quantize_k``); their
+    dequantised values are ``scale_q[h] * code`` and ``scale_v[h] * code``; the
+    RoPE parts of Q and K stay bf16.  The attention is the textbook one over the
+    dequantised tensors, in float64.
+
+    ``q_codes (B,H,Dn) int8``, ``q_rope_bits (B,H,Dr)``, ``k_codes (B,H,T,Dn) int8``,
+    ``k_rope_bits (B,H,T,Dr)``, ``v_codes (B,H,T,Dv) int8``; scales float32 ``[H]``.
+    Returns float64 ``(B,H,Dv)``.
+    """
+    q_codes = np.asarray(q_codes, dtype=np.int8)
+    B, H, Dn = q_codes.shape
+    q_nope = dequantize_k_nope(q_codes.reshape(B, H, 1, Dn), scale_q).reshape(B, H, Dn)
+    q = np.concatenate([q_nope, bf16_bits_to_f64(q_rope_bits)], axis=-1)
+    k = np.concatenate([dequantize_k_nope(k_codes, scale_k), bf16_bits_to_f64(k_rope_bits)], axis=-1)
+    v = dequantize_k_nope(v_codes, scale_v)
+    return attention_fp64(q, k, v, float(np.float32(sm_scale)))

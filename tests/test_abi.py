@@ -201,6 +201,28 @@ def test_decode_append_rejections():
     assert call(ws=None) == L.FA3Q_ERR_WORKSPACE
     assert call(ws=_p(128)) == L.FA3Q_ERR_ALIGN
 
+
+@no_gpu_only
+def test_decode_qkv8_rejections():
+    f = fa.lib().fa3q_decode_attn_qkv8
+    ok = dict(qq=_p(), qr=_p(), sq=_p(), kq=_p(), sk=_p(), kr=_p(), vq=_p(), sv=_p(), B=8, H=128, T=32768, Dn=128,
+              Dr=64, Dv=128, sm=0.07, o=_p(), ws=_p(), wsb=1 << 30)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["qq"], a["qr"], a["sq"], a["kq"], a["sk"], a["kr"], a["vq"], a["sv"], a["B"], a["H"], a["T"],
+                 a["Dn"], a["Dr"], a["Dv"], ctypes.c_float(a["sm"]), a["o"], a["ws"], a["wsb"], None)
+
+    for name in ("qq", "qr", "sq", "kq", "sk", "kr", "vq", "sv", "o"):
+        assert call(**{name: None}) == L.FA3Q_ERR_NULL, name
+    assert call(Dv=8) == L.FA3Q_ERR_SHAPE      # INT8 values need 16 per lane
+    assert call(Dv=96) == L.FA3Q_ERR_SHAPE
+    assert call(Dn=120) == L.FA3Q_ERR_SHAPE
+    assert call(qq=_p(8)) == L.FA3Q_ERR_ALIGN
+    assert call(vq=_p(8)) == L.FA3Q_ERR_ALIGN
+    assert call(sv=_p(2)) == L.FA3Q_ERR_ALIGN
+    assert call(ws=None) == L.FA3Q_ERR_WORKSPACE
+
 def test_binding_refuses_host_tensors():
     import torch
     x = torch.zeros((1, 4, 64, 32), dtype=torch.float32)

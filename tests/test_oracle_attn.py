@@ -194,3 +194,49 @@ def test_append_validates_lengths():
                                   np.array([T], np.int32), 1.0, Dn)
     with pytest.raises(ValueError):
         oracle.decode_append_attn(qb, None, None, scale, codes, rope, vb, np.array([0], np.int32), 1.0, Dn)
+
+
+# ----------------------------------------------------------------------------- Q, K, V all INT8
+
+
+def test_qkv8_attention_matches_sdpa_over_dequantised_tensors():
+    rng = np.random.default_rng(45)
+    B, H, T, Dn, Dr, Dv = 2, 3, 50, 32, 16, 32
+    qc = rng.integers(-127, 128, size=(B, H, Dn)).astype(np.int8)
+    qr = _rand_bits(rng, (B, H, Dr))
+    kc = rng.integers(-127, 128, size=(B, H, T, Dn)).astype(np.int8)
+    kr = _rand_bits(rng, (B, H, T, Dr))
+    vc = rng.integers(-127, 128, size=(B, H, T, Dv)).astype(np.int8)
+    sq, sk, sv = (np.exp(rng.uniform(-6, -2, size=H)).astype(np.float32) for _ in range(3))
+    sm = np.float32(1 / math.sqrt(Dn + Dr))
+    out = oracle.decode_attn_qkv8(qc, qr, sq, kc, sk, kr, vc, sv, sm)
+    # independent assembly: torch float64 SDPA over tensors dequantised here
+    s_ = lambda a: torch.from_numpy(a.astype(np.float64))
+    q = torch.cat([s_(qc) * s_(sq).view(1, H, 1), torch.from_numpy(oracle.bf16_bits_to_f64(qr))], -1).unsqueeze(2)
+    k = torch.cat([s_(kc) * s_(sk).view(1, H, 1, 1), torch.from_numpy(oracle.bf16_bits_to_f64(kr))], -1)
+    v = s_(vc) * s_(sv).view(1, H, 1, 1)
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=float(sm)).squeeze(2).numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-15)
+    # the integer form: q_nope . k_nope = sq*sk * sum(qc*kc), exact in integers
+    ints = np.einsum("bhd,bhtd->bht", qc.astype(np.int64), kc.astype(np.int64))
+    s_int = sq.astype(np.float64).reshape(1, H, 1) * sk.astype(np.float64).reshape(1, H, 1) * ints
+    s_deq = np.einsum("bhd,bhtd->bht", q[..., 0, :Dn].numpy(), k[..., :Dn].numpy())
+    np.testing.assert_allclose(s_int, s_deq, rtol=1e-13, atol=0)
+
+
+def test_qkv8_with_unit_scales_is_plain_attention_over_codes():
+    rng = np.random.default_rng(46)
+    B, H, T, Dn, Dr, Dv = 1, 2, 9, 16, 8, 16
+    qc = rng.integers(-3, 4, size=(B, H, Dn)).astype(np.int8)
+    kc = rng.integers(-3, 4, size=(B, H, T, Dn)).astype(np.int8)
+    vc = rng.integers(-127, 128, size=(B, H, T, Dv)).astype(np.int8)
+    zero_r = np.zeros((B, H, Dr), np.uint16)
+    zero_kr = np.zeros((B, H, T, Dr), np.uint16)
+    one = np.ones(H, np.float32)
+    out = oracle.decode_attn_qkv8(qc, zero_r, one, kc, one, zero_kr, vc, one, 0.5)
+    ref = oracle.attention_fp64(qc.astype(np.float64), kc.astype(np.float64), vc.astype(np.float64), 0.5)
+    np.testing.assert_allclose(out, ref, rtol=1e-14, atol=0)
+    # and a single token returns its dequantised value exactly
+    out1 = oracle.decode_attn_qkv8(qc, zero_r, one, kc[:, :, :1], one, zero_kr[:, :, :1], vc[:, :, :1],
+                                   np.full(H, 0.25, np.float32), 0.5)
+    np.testing.assert_array_equal(out1, 0.25 * vc[:, :, 0].astype(np.float64))

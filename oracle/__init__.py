@@ -35,7 +35,8 @@ from .recall_window import (
     qparams,
 )
 from .quant import quantize_k, dequantize_k_nope
-from .attention import attention_fp64, decode_attn, decode_append_attn, decode_attn_qkv8
+from .attention import attention_fp64, decode_attn, decode_append_attn, decode_attn_qkv8, decode_attn_asym
+from .asym import params_to_f32, quantize_asym, dequantize_asym
 
 __all__ = [
     "bf16_bits_to_f32",
@@ -56,4 +57,8 @@ __all__ = [
     "decode_attn",
     "decode_append_attn",
     "decode_attn_qkv8",
+    "decode_attn_asym",
+    "params_to_f32",
+    "quantize_asym",
+    "dequantize_asym",
 ]

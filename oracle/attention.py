@@ -112,3 +112,15 @@ def decode_attn_qkv8(q_codes, q_rope_bits, scale_q, k_codes, scale_k, k_rope_bit
     k = np.concatenate([dequantize_k_nope(k_codes, scale_k), bf16_bits_to_f64(k_rope_bits)], axis=-1)
     v = dequantize_k_nope(v_codes, scale_v)
     return attention_fp64(q, k, v, float(np.float32(sm_scale)))
+
+
+def decode_attn_asym(q_bits, codes, scale_bits, offset_bits, rope_bits, v_bits, sm_scale: float,
+                     dtype: str = "bfloat16") -> np.ndarray:
+    """Attention of bf16 ``q (B,H,Dn+Dr)`` over an asymmetric per-(head, dim) INT8 K-nope cache.
+
+    Same as :func:`decode_attn` with the K-nope value ``(code - offset[h,d]) * scale[h,d]``
+    (readings S1-S2 of ``oracle.asym``); K-rope and V bf16.  Returns float64 ``(B,H,Dv)``.
+    """
+    from .asym import dequantize_asym
+    k = np.concatenate([dequantize_asym(codes, scale_bits, offset_bits, dtype), bf16_bits_to_f64(rope_bits)], axis=-1)
+    return attention_fp64(bf16_bits_to_f64(q_bits), k, bf16_bits_to_f64(v_bits), float(np.float32(sm_scale)))

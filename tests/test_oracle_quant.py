@@ -118,3 +118,121 @@ def test_quantize_roundtrip_with_calibrated_scale():
 def test_shape_validation(bad):
     with pytest.raises(ValueError):
         oracle.quantize_k(bad.astype(np.uint16), np.ones(3, np.float32), 2)
+
+
+# ----------------------------------------------------------------------------- asymmetric per-(head, dim)
+# MindIE Turbo page "Attention量化", tables 1 and 2: scale and offset tables [heads, head_dim] in
+# float16 or bfloat16.  The quantiser is checked against exact rational arithmetic (float32
+# division, then float32 addition, then half-to-even), closed forms and the symmetric quantiser.
+
+
+def _f32(q: Fraction) -> Fraction:
+    return Fraction(_round_f32(q))
+
+
+def _code_asym(x: float, s: float, o: float) -> int:
+    if s == 0.0:
+        return 0
+    y = _f32(Fraction(x) / Fraction(s))
+    z = _f32(y + Fraction(o))
+    return max(-128, min(127, round(z)))
+
+
+def _bf16_params(rng, H, Dn, lo, hi):
+    return oracle.f32_to_bf16_bits_rne(rng.uniform(lo, hi, size=(H, Dn)).astype(np.float32))
+
+
+def test_asym_codes_match_exact_rational_arithmetic():
+    rng = np.random.default_rng(51)
+    B, H, S, Dn, Dr = 2, 3, 20, 16, 8
+    sigma = np.exp(rng.uniform(-1, 1, size=H)).astype(np.float32)
+    k = _random_k(rng, B, H, S, Dn, Dr, sigma)
+    scale = _bf16_params(rng, H, Dn, 0.005, 0.05)
+    offset = _bf16_params(rng, H, Dn, -20.0, 20.0)
+    codes, rope = oracle.quantize_asym(k, scale, offset, Dn)
+    xs = oracle.bf16_bits_to_f32(k[..., :Dn])
+    sf, of = oracle.bf16_bits_to_f32(scale), oracle.bf16_bits_to_f32(offset)
+    for idx in np.ndindex(codes.shape):
+        b, h, s_, d = idx
+        assert codes[idx] == _code_asym(float(xs[idx]), float(sf[h, d]), float(of[h, d])), idx
+    np.testing.assert_array_equal(rope, k[..., Dn:])
+
+
+def test_asym_hand_values_and_saturation():
+    # s = 1, o = 0.5: z = x + 0.5 -> 0.5 + 0.5 = 1, -1.0 + 0.5 = -0.5 -> -0 (half to even), 2.0 + 0.5 = 2.5 -> 2
+    # -129 + 0.5 = -128.5 rounds half to even to -128 (inside the range); -1000 saturates
+    x = np.array([0.5, -1.0, 2.0, 1000.0, -1000.0, 126.5, -129.0], np.float32)
+    k = _bits16(x).reshape(1, 1, 1, -1)
+    Dn = x.size
+    one = _bits16(np.ones((1, Dn), np.float32))
+    half = _bits16(np.full((1, Dn), 0.5, np.float32))
+    codes, _ = oracle.quantize_asym(k, one, half, Dn)
+    assert codes.reshape(-1).tolist() == [1, 0, 2, 127, -128, 127, -128]
+
+
+def test_asym_without_offset_is_the_symmetric_quantiser_inside_its_range():
+    # offset 0 and a per-head scale copied to every dim: the same codes as quantize_k wherever
+    # |x / s| rounds inside +-127 (the symmetric range); only the asymmetric -128 differs
+    rng = np.random.default_rng(52)
+    B, H, S, Dn, Dr = 2, 4, 30, 32, 16
+    sigma = np.exp(rng.uniform(-1, 1, size=H)).astype(np.float32)
+    k = _random_k(rng, B, H, S, Dn, Dr, sigma)
+    s_head = oracle.bf16_bits_to_f32(oracle.f32_to_bf16_bits_rne((sigma * np.float32(3.0) / np.float32(127))))
+    sym, _ = oracle.quantize_k(k, s_head, Dn)
+    scale_tab = np.repeat(oracle.f32_to_bf16_bits_rne(s_head).reshape(H, 1), Dn, axis=1)
+    asym, _ = oracle.quantize_asym(k, scale_tab, np.zeros((H, Dn), np.uint16), Dn)
+    inside = np.abs(asym.astype(np.int32)) <= 127
+    np.testing.assert_array_equal(asym[inside], sym[inside])
+    assert np.all(sym[~inside] == -127) and np.all(asym[~inside] == -128)
+
+
+def test_asym_roundtrip_error_bound_and_float16_tables():
+    rng = np.random.default_rng(53)
+    B, H, S, Dn, Dr = 1, 2, 64, 16, 0
+    x = rng.uniform(-3, 5, size=(B, H, S, Dn)).astype(np.float32)
+    k = oracle.f32_to_bf16_bits_rne(x).reshape(B, H, S, Dn)
+    xf = oracle.bf16_bits_to_f32(k).astype(np.float64)
+    lo, hi = -3.0, 5.0
+    s = np.float32((hi - lo) / 255.0)
+    o = np.float32(-128.0 - np.rint(lo / s))
+    for dtype, conv in (("float16", lambda a: np.asarray(a, np.float16).view(np.uint16)),
+                        ("bfloat16", lambda a: oracle.f32_to_bf16_bits_rne(np.asarray(a, np.float32)))):
+        sb = conv(np.full((H, Dn), s, np.float32))
+        ob = conv(np.full((H, Dn), o, np.float32))
+        codes, _ = oracle.quantize_asym(k, sb, ob, Dn, dtype)
+        deq = oracle.dequantize_asym(codes, sb, ob, dtype)
+        s_used = float(oracle.params_to_f32(sb, dtype)[0, 0])
+        # every value inside the representable range comes back within half a step (plus
+        # the float32 rounding of the quotient and of the addition)
+        assert np.max(np.abs(deq - xf)) <= s_used * (0.5 + 1e-3)
+    # float16 patterns are read as float16 values
+    np.testing.assert_array_equal(oracle.params_to_f32(np.array([0x3C00, 0xC000], np.uint16), "float16"),
+                                  np.array([1.0, -2.0], np.float32))
+
+
+def test_asym_decode_is_attention_over_dequantised_cache():
+    import math
+    import torch
+    rng = np.random.default_rng(54)
+    B, H, T, Dn, Dr, Dv = 2, 3, 40, 32, 16, 32
+    q = oracle.f32_to_bf16_bits_rne(rng.normal(size=(B, H, Dn + Dr)).astype(np.float32))
+    codes = rng.integers(-128, 128, size=(B, H, T, Dn)).astype(np.int8)
+    scale = _bf16_params(rng, H, Dn, 0.001, 0.02)
+    offset = _bf16_params(rng, H, Dn, -30.0, 30.0)
+    rope = oracle.f32_to_bf16_bits_rne(rng.normal(size=(B, H, T, Dr)).astype(np.float32))
+    v = oracle.f32_to_bf16_bits_rne(rng.normal(size=(B, H, T, Dv)).astype(np.float32))
+    sm = np.float32(1 / math.sqrt(Dn + Dr))
+    out = oracle.decode_attn_asym(q, codes, scale, offset, rope, v, sm)
+    sf = torch.from_numpy(oracle.bf16_bits_to_f32(scale).astype(np.float64)).view(1, H, 1, Dn)
+    of = torch.from_numpy(oracle.bf16_bits_to_f32(offset).astype(np.float64)).view(1, H, 1, Dn)
+    kd = (torch.from_numpy(codes.astype(np.float64)) - of) * sf
+    k = torch.cat([kd, torch.from_numpy(oracle.bf16_bits_to_f64(rope))], -1)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(oracle.bf16_bits_to_f64(q)).unsqueeze(2), k, torch.from_numpy(oracle.bf16_bits_to_f64(v)),
+        scale=float(sm)).squeeze(2).numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-14)
+    # zero offsets and one scale per head: the symmetric decode
+    s_head = oracle.bf16_bits_to_f32(scale)[:, 0]
+    tab = np.repeat(scale[:, :1], Dn, axis=1)
+    np.testing.assert_allclose(oracle.decode_attn_asym(q, codes, tab, np.zeros((H, Dn), np.uint16), rope, v, sm),
+                               oracle.decode_attn(q, codes, s_head, rope, v, sm), rtol=1e-14, atol=0)

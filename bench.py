@@ -337,6 +337,41 @@ def main() -> int:
                                         "token (outside the step)"}
     del vq
 
+    # Asymmetric K cache with a scale and an offset per (head, dim) (float16 tables): the tables
+    # are inputs (per-channel min/max of sequence 0 of K mapped onto [-128, 127], set up with
+    # torch), then fa3q_quantize_asym over the whole K and fa3q_decode_attn_asym over the
+    # resulting cache; measured outside the step.
+    kn0 = k[0, :, :, :DN].float()
+    lo, hi = kn0.amin(dim=1), kn0.amax(dim=1)
+    a_scale = ((hi - lo) / 255.0).clamp_min(1e-6)
+    a_offset = -128.0 - lo / a_scale
+    a_scale, a_offset = a_scale.to(torch.float16).contiguous(), a_offset.to(torch.float16).contiguous()
+    del kn0, lo, hi
+    akq = torch.empty_like(kq)
+    akr = torch.empty_like(kr)
+
+    def timed(fn, reps=5):
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    aq_ms = timed(lambda: fa.fa3q_quantize_asym(k, a_scale, a_offset, DN, akq, akr, stream=stream))
+    ad_ms = timed(lambda: fa.fa3q_decode_attn_asym(q, akq, a_scale, a_offset, akr, v, sm, out, ws_dec,
+                                                   stream=stream))
+    breakdown["quantize_asym"] = {"ms": aq_ms, "gbs": QUANT_BYTES / (aq_ms * 1e-3) / 1e9,
+                                  "frac_hbm": QUANT_BYTES / (aq_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                  "note": "scale and offset per (head, dim), float16 tables (outside the step)"}
+    breakdown["decode_asym"] = {"ms": ad_ms, "kv_gbs": DEC_BYTES / (ad_ms * 1e-3) / 1e9,
+                                "frac_hbm": DEC_BYTES / (ad_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                "note": "attention over the asymmetric K-nope cache (outside the step)"}
+    del akq, akr
+
     # device-to-device copy of COPY_BYTES: a reference ceiling for read+write streaming, and the
     # known-size kernel the HBM byte counters are scaled by
     src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)

@@ -14,12 +14,17 @@
  *   6. fa3q_decode_append_attn -- one decode step: append the new token to the cache in place
  *      (K-nope quantised as in 4), then attention over ragged per-sequence lengths
  *   7. fa3q_decode_attn_qkv8   -- attention with Q (non-RoPE part), K-nope and V all INT8
+ *   8. fa3q_quantize_asym      -- non-RoPE part of K -> asymmetric INT8 codes with a scale and
+ *      an offset per (head, dim); RoPE part kept in bf16
+ *   9. fa3q_decode_attn_asym   -- attention as in 5 over the asymmetric K-nope cache of 8
  *
  * Sources, cited by page title and section:
  *   [MS] msModelSlim documentation, "FA3量化：Flash Attention 3激活量化算法说明"
  *        (FA3 quantization: Flash Attention 3 activation quantization algorithm),
  *        sections 原理 -> 算法流程 (algorithm flow) and 适用要求 (requirements).
  *   [MI] MindIE LLM user guide, "FA3 quantization", overview paragraph.
+ *   [MT] MindIE Turbo documentation, "Attention量化" (attention quantization),
+ *        tables 1 and 2 (q/k/v scale and offset of shape [head_num, head_dim]).
  *
  * Conventions shared by every entry point:
  *   - Every pointer is a DEVICE pointer owned by the caller; the library never
@@ -62,7 +67,8 @@ typedef enum fa3q_status {
 
 typedef enum fa3q_dtype {
   FA3Q_F32 = 0,  /* IEEE binary32 */
-  FA3Q_BF16 = 1  /* bfloat16, raw 16-bit patterns */
+  FA3Q_BF16 = 1, /* bfloat16, raw 16-bit patterns */
+  FA3Q_F16 = 2   /* IEEE binary16, raw 16-bit patterns (asymmetric parameter tables only) */
 } fa3q_dtype;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -271,6 +277,58 @@ int fa3q_decode_attn_qkv8(const int8_t* q_nope_q, const uint16_t* q_rope, const 
                           const int8_t* k_nope_q, const float* scale_k, const uint16_t* k_rope,
                           const int8_t* v_q, const float* scale_v, int64_t B, int64_t H, int64_t T,
                           int64_t Dn, int64_t Dr, int64_t Dv, float sm_scale, float* out, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* 8. Asymmetric K-cache quantisation with per-(head, dim) tables            */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * [MT] tables 1 and 2: the K activation carries a scale and an offset per
+ * (head, dim), as float16 (table 1) or bfloat16 (table 2).  The page gives no
+ * formula or calibration for them; they are caller inputs, and the code is the
+ * plain asymmetric INT8 one.  For every row (b, h, s) of k (B, H, S, Dn+Dr):
+ *   k_nope_q[b,h,s,d] = clamp(round_half_even(fl32(fl32(x / sc) + of)), -128, 127),  d < Dn
+ *                       with x the float32 value of k[b,h,s,d], sc = scale[h,d] and
+ *                       of = offset[h,d] widened exactly to float32, the division
+ *                       correctly rounded; 0 when sc == 0
+ *   k_rope[b,h,s,j]   = k[b,h,s,Dn+j] bit for bit,  j < Dr
+ * A code stands for the value (code - of) * sc.
+ *
+ *   k             device bf16 (B,H,S,Dn+Dr) contiguous, 16-byte aligned.
+ *   scale, offset device [H][Dn] row-major, dtype params_dtype (FA3Q_BF16 or
+ *                 FA3Q_F16), 16-byte aligned; finite.
+ *   k_nope_q      device int8 (B,H,S,Dn) contiguous, 16-byte aligned.
+ *   k_rope        device bf16 (B,H,S,Dr) contiguous, 16-byte aligned; may be NULL iff Dr == 0.
+ *   B,H,S > 0; Dn > 0 multiple of 16, Dn <= 4096; Dr >= 0 multiple of 8, Dr <= 2048.
+ *   FA3Q_ERR_DTYPE for any other params_dtype.
+ */
+int fa3q_quantize_asym(const uint16_t* k, const uint16_t* scale, const uint16_t* offset,
+                       int params_dtype, int8_t* k_nope_q, uint16_t* k_rope, int64_t B, int64_t H,
+                       int64_t S, int64_t Dn, int64_t Dr, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* 9. Decode attention over the asymmetric K cache                           */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * [MI] overview and [MT] tables 1 and 2: fa3q_decode_attn's attention with the
+ * K-nope cache of fa3q_quantize_asym dequantised per (head, dim):
+ *   s_t   = sm_scale * ( sum_{d<Dn} q[b,h,d] * (k_nope_q[b,h,t,d] - offset[h,d]) * scale[h,d]
+ *                        + sum_{j<Dr} q[b,h,Dn+j] * k_rope[b,h,t,j] )
+ *   out[b,h,:] = sum_t softmax(s)_t * v[b,h,t,:]
+ * Arithmetic is float32: q[b,h,d] * scale[h,d] is formed once per (b, h) and
+ * the offset term sum_d q[b,h,d] * scale[h,d] * offset[h,d] is one constant
+ * per (b, h) subtracted from every score.
+ *
+ *   scale, offset, params_dtype  as fa3q_quantize_asym.
+ *   q, k_nope_q, k_rope, v, out, B, H, T, Dn, Dr, Dv, sm_scale, workspace
+ *                 as fa3q_decode_attn (same workspace query).
+ */
+int fa3q_decode_attn_asym(const uint16_t* q, const int8_t* k_nope_q, const uint16_t* scale,
+                          const uint16_t* offset, int params_dtype, const uint16_t* k_rope,
+                          const uint16_t* v, int64_t B, int64_t H, int64_t T, int64_t Dn, int64_t Dr,
+                          int64_t Dv, float sm_scale, float* out, void* workspace,
                           size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus

@@ -6,6 +6,7 @@ its calls.  Build the library with ``python -m kv_cache_quantization_fa3q_amd.bu
 """
 from ._lib import (  # noqa: F401
     FA3Q_BF16,
+    FA3Q_F16,
     FA3Q_F32,
     FA3Q_OK,
     Fa3qError,
@@ -22,9 +23,11 @@ from .ops import (  # noqa: F401
     fa3q_calibrate_workspace_bytes,
     fa3q_decode_append_attn,
     fa3q_decode_attn,
+    fa3q_decode_attn_asym,
     fa3q_decode_attn_qkv8,
     fa3q_decode_attn_workspace_bytes,
     fa3q_init_minmax,
     fa3q_qparams,
+    fa3q_quantize_asym,
     fa3q_quantize_k,
 )

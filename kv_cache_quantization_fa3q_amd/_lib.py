@@ -28,6 +28,7 @@ FA3Q_ERR_UNSUPPORTED = 8
 
 FA3Q_F32 = 0
 FA3Q_BF16 = 1
+FA3Q_F16 = 2
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -51,6 +52,9 @@ SIGNATURES = {
     "fa3q_decode_append_attn": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
                                        ctypes.c_float, _vp, _vp, _sz, _vp]),
     "fa3q_decode_attn_qkv8": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
+                                     ctypes.c_float, _vp, _vp, _sz, _vp]),
+    "fa3q_quantize_asym": (_int, [_vp, _vp, _vp, _int, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp]),
+    "fa3q_decode_attn_asym": (_int, [_vp, _vp, _vp, _vp, _int, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
                                      ctypes.c_float, _vp, _vp, _sz, _vp]),
 }
 

@@ -10,10 +10,10 @@
 // ascending.  So instead of sorting N values the library selects the two tails:
 //
 //   calib_sample_kernel  one workgroup per head reads a small evenly spaced sample of the
-//                        head (8 runs of 1024 16-byte vectors, about 3% of a 2M-value
-//                        head) and sets per-head bounds: the K-th smallest per-vector
-//                        minimum (K-th largest maximum), which has at least K of the
-//                        head's values at or beyond it.
+//                        head (32 runs of 256 16-byte vectors, about 3% of a 2M-value
+//                        head) and sets per-head bounds: the K-th smallest minimum of a
+//                        group of sampled vectors (K-th largest maximum), which has at
+//                        least K of the head's values at or beyond it.
 //   calib_chunk_kernel   one HBM pass.  Each workgroup streams a contiguous chunk of one
 //                        head (inside one (b,h) slab) and keeps, in LDS, a candidate
 //                        buffer per side holding a superset of the chunk's part of the
@@ -25,7 +25,9 @@
 //   calib_merge_kernel   one workgroup per head: the same select over the chunks' lists
 //                        gives the head's exact K smallest and K largest values, a
 //                        bitonic sort orders them, and a block reduction finds the
-//                        shortest float32 window U[i]-L[i], smallest i on ties.
+//                        shortest float32 window U[i]-L[i], smallest i on ties.  Heads
+//                        whose lists fit in registers take calib_merge_wave_kernel
+//                        instead: one wave per side, no LDS select.
 //
 // Why the union of the chunk lists holds the head's K smallest values: a value v at or
 // below the head's K-th smallest value is never dropped.  The head bound has at least K

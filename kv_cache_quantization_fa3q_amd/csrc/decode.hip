@@ -35,6 +35,11 @@
 // exact integer dot product (v_dot4 over four code pairs per instruction), the RoPE part
 // stays bf16, and V is weighted as codes with scale_v[h] applied once at the end: 384
 // bytes per cached token instead of 512 at the MLA shape.
+//
+// Asymmetric K cache (fa3q_decode_attn_asym): K-nope codes with a scale and an offset per
+// (head, dim) (fa3q_quantize_asym), the value of a code being (code - o[h,d]) * s[h,d].
+// The per-dim scale folds into the query (q'_d = q_d * s[h,d]) and the offsets into one
+// constant per (b, h) (sum_d q'_d * o[h,d]), so the score is the same code dot product.
 #include <cmath>
 
 #include "fa3q_internal.hpp"
@@ -64,6 +69,9 @@ struct DecodeArgs {
   const int8_t* vq;        // (B,H,T,Dv) value codes (INT8 kernels)
   const float* scale_q;    // [H]
   const float* scale_v;    // [H]
+  const uint16_t* k_scale_hd;   // [H][Dn] bf16 or float16 (asymmetric kernels)
+  const uint16_t* k_offset_hd;  // [H][Dn]
+  int32_t params_f16;           // 1: the tables are float16, 0: bfloat16
   float* ws_ml;  // [B*H*nsplit][2] (max, sum)
   float* ws_o;   // [B*H*nsplit][Dv]
   int64_t T;
@@ -132,11 +140,21 @@ __device__ __forceinline__ uint32_t quant4_exact(uint32_t w0, uint32_t w1, float
   return o;
 }
 
+// float32 value of a bf16 or float16 parameter pattern.
+__device__ __forceinline__ float param_f32(uint16_t bits, bool f16) {
+  return f16 ? static_cast<float>(__builtin_bit_cast(_Float16, bits)) : __uint_as_float(static_cast<uint32_t>(bits) << 16);
+}
+
+constexpr int kFmtBf16 = 0;  // bf16 query and values, per-head symmetric K-nope codes
+constexpr int kFmtQkv8 = 1;  // INT8 query (non-RoPE part) and values; LV is then Dv/16
+constexpr int kFmtAsym = 2;  // bf16 query and values, per-(head, dim) asymmetric K-nope codes
+
 // kVar: ragged lengths from kv_len[] and, when k_new is set, the appended token.
-// kQ8: INT8 query (non-RoPE part) and INT8 values; LV is then Dv/16 lanes per token.
-template <int LK, int LV, bool kVar, bool kQ8>
+template <int LK, int LV, bool kVar, int kFmt>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
-  static_assert(!(kVar && kQ8), "the append step takes a bf16 cache");
+  constexpr bool kQ8 = kFmt == kFmtQkv8;
+  constexpr bool kAsym = kFmt == kFmtAsym;
+  static_assert(!kVar || kFmt == kFmtBf16, "the append step takes the per-head bf16-query cache");
   extern __shared__ float smem[];
   float* sc = smem;                       // [split_len] scores, then probabilities
   float* red = smem + a.split_len;        // [kWaves] block reduction scratch
@@ -220,7 +238,27 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) qr[i] = 0.0f;
     }
-    const float head_scale = kQ8 ? a.scale_q[h] * a.scale[h] : a.scale[h];
+    const float head_scale = kQ8 ? a.scale_q[h] * a.scale[h] : (kAsym ? 1.0f : a.scale[h]);
+    float c0 = 0.0f;  // asymmetric cache: this lane's share of sum_d q'_d * o[h,d]
+    if constexpr (kAsym) {
+      if (has_n) {
+        const bool f16 = a.params_f16 != 0;
+        const uint4* sp = reinterpret_cast<const uint4*>(a.k_scale_hd + static_cast<int64_t>(h) * a.Dn + 16 * j);
+        const uint4* op = reinterpret_cast<const uint4*>(a.k_offset_hd + static_cast<int64_t>(h) * a.Dn + 16 * j);
+        const uint4 s0 = sp[0], s1 = sp[1], o0 = op[0], o1 = op[1];
+        const uint32_t sw[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+        const uint32_t ow[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+        qsum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          qn[2 * i] *= param_f32(static_cast<uint16_t>(sw[i] & 0xffffu), f16);
+          qn[2 * i + 1] *= param_f32(static_cast<uint16_t>(sw[i] >> 16), f16);
+          c0 = fmaf(qn[2 * i], param_f32(static_cast<uint16_t>(ow[i] & 0xffffu), f16), c0);
+          c0 = fmaf(qn[2 * i + 1], param_f32(static_cast<uint16_t>(ow[i] >> 16), f16), c0);
+          qsum += qn[2 * i] + qn[2 * i + 1];
+        }
+      }
+    }
     const int8_t* kq = a.kq + (static_cast<int64_t>(bh) * a.T + t0) * a.Dn + 16 * j;
     const uint16_t* kr = a.kr + (static_cast<int64_t>(bh) * a.T + t0) * a.Dr + 8 * j;
     const int step = kWaves * kSlots;
@@ -247,6 +285,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
             d = __builtin_amdgcn_sdot4(static_cast<int>(qc.z), static_cast<int>(wn[u].z), d, false);
             d = __builtin_amdgcn_sdot4(static_cast<int>(qc.w), static_cast<int>(wn[u].w), d, false);
             s = head_scale * static_cast<float>(d);  // |d| <= 16*127*127: exact in float32
+          } else if constexpr (kAsym) {
+            s = dot16_i8(qn, qsum, wn[u]) - c0;
           } else {
             s = head_scale * dot16_i8(qn, qsum, wn[u]);
           }
@@ -447,32 +487,32 @@ int64_t next_pow2(int64_t v) {
 
 using KernelFn = void (*)(DecodeArgs);
 
-template <int LK, bool kVar, bool kQ8>
+template <int LK, bool kVar, int kFmt>
 KernelFn pick_lv(int lv) {
   switch (lv) {
-    case 1: return decode_split_kernel<LK, 1, kVar, kQ8>;
-    case 2: return decode_split_kernel<LK, 2, kVar, kQ8>;
-    case 4: return decode_split_kernel<LK, 4, kVar, kQ8>;
-    case 8: return decode_split_kernel<LK, 8, kVar, kQ8>;
-    case 16: return decode_split_kernel<LK, 16, kVar, kQ8>;
-    case 32: return decode_split_kernel<LK, 32, kVar, kQ8>;
+    case 1: return decode_split_kernel<LK, 1, kVar, kFmt>;
+    case 2: return decode_split_kernel<LK, 2, kVar, kFmt>;
+    case 4: return decode_split_kernel<LK, 4, kVar, kFmt>;
+    case 8: return decode_split_kernel<LK, 8, kVar, kFmt>;
+    case 16: return decode_split_kernel<LK, 16, kVar, kFmt>;
+    case 32: return decode_split_kernel<LK, 32, kVar, kFmt>;
     case 64:
-      if constexpr (kQ8) return nullptr;  // Dv = 1024 is past the supported range
-      else return decode_split_kernel<LK, 64, kVar, kQ8>;
+      if constexpr (kFmt == kFmtQkv8) return nullptr;  // Dv = 1024 is past the supported range
+      else return decode_split_kernel<LK, 64, kVar, kFmt>;
     default: return nullptr;
   }
 }
 
-template <bool kVar, bool kQ8>
+template <bool kVar, int kFmt>
 KernelFn pick_kernel(int lk, int lv) {
   switch (lk) {
-    case 1: return pick_lv<1, kVar, kQ8>(lv);
-    case 2: return pick_lv<2, kVar, kQ8>(lv);
-    case 4: return pick_lv<4, kVar, kQ8>(lv);
-    case 8: return pick_lv<8, kVar, kQ8>(lv);
-    case 16: return pick_lv<16, kVar, kQ8>(lv);
-    case 32: return pick_lv<32, kVar, kQ8>(lv);
-    case 64: return pick_lv<64, kVar, kQ8>(lv);
+    case 1: return pick_lv<1, kVar, kFmt>(lv);
+    case 2: return pick_lv<2, kVar, kFmt>(lv);
+    case 4: return pick_lv<4, kVar, kFmt>(lv);
+    case 8: return pick_lv<8, kVar, kFmt>(lv);
+    case 16: return pick_lv<16, kVar, kFmt>(lv);
+    case 32: return pick_lv<32, kVar, kFmt>(lv);
+    case 64: return pick_lv<64, kVar, kFmt>(lv);
     default: return nullptr;
   }
 }
@@ -501,27 +541,36 @@ extern "C" size_t fa3q_decode_attn_workspace_bytes(int64_t B, int64_t H, int64_t
 namespace fa3q {
 namespace {
 
-// INT8 query and values of fa3q_decode_attn_qkv8 (unused by the bf16 entry points).
+// INT8 query and values of fa3q_decode_attn_qkv8, and the asymmetric K tables of
+// fa3q_decode_attn_asym (unused by the other entry points).
 struct Int8QV {
   const int8_t* qq = nullptr;
   const int8_t* vq = nullptr;
   const float* scale_q = nullptr;
   const float* scale_v = nullptr;
+  const uint16_t* k_scale_hd = nullptr;
+  const uint16_t* k_offset_hd = nullptr;
+  int params_f16 = 0;
 };
 
 // Shared validation and launch of the decode entry points (kVar: ragged / append;
-// kQ8: INT8 query and values, with q the (B,H,Dr) RoPE part and v unused).
-template <bool kVar, bool kQ8>
+// kFmt: kFmtQkv8 takes INT8 query and values, with q the (B,H,Dr) RoPE part and v unused;
+// kFmtAsym takes the per-(head, dim) K tables instead of the per-head scale).
+template <bool kVar, int kFmt>
 int decode_launch(const uint16_t* q, const int8_t* k_nope_q, const float* scale, const uint16_t* k_rope,
                   const uint16_t* v, const int32_t* kv_len, const uint16_t* k_new, const uint16_t* v_new,
                   const Int8QV& i8, int64_t B, int64_t H, int64_t T, int64_t Dn, int64_t Dr, int64_t Dv,
                   float sm_scale, float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  constexpr bool kQ8 = kFmt == kFmtQkv8;
+  constexpr bool kAsym = kFmt == kFmtAsym;
   if (kQ8) {
     if (!i8.qq || !i8.vq || !i8.scale_q || !i8.scale_v || !k_nope_q || !scale || !out || (Dr > 0 && (!q || !k_rope)))
       return FA3Q_ERR_NULL;
-  } else if (!q || !k_nope_q || !scale || !v || !out || (Dr > 0 && !k_rope)) {
+  } else if (!q || !k_nope_q || (!kAsym && !scale) || !v || !out || (Dr > 0 && !k_rope)) {
     return FA3Q_ERR_NULL;
   }
+  if (kAsym && (!i8.k_scale_hd || !i8.k_offset_hd)) return FA3Q_ERR_NULL;
+  if (kAsym && i8.params_f16 != 0 && i8.params_f16 != 1) return FA3Q_ERR_DTYPE;
   if (kVar && (!kv_len || (k_new != nullptr) != (v_new != nullptr))) return FA3Q_ERR_NULL;
   if (B <= 0 || H <= 0 || T <= 0) return FA3Q_ERR_SHAPE;
   if (!valid_dims(Dn, Dr, Dv) || (kQ8 && Dv < 16)) return FA3Q_ERR_SHAPE;
@@ -529,8 +578,9 @@ int decode_launch(const uint16_t* q, const int8_t* k_nope_q, const float* scale,
   if (B * H * T > (int64_t{1} << 62) / (Dn + Dr + Dv)) return FA3Q_ERR_SHAPE;
   if (!std::isfinite(sm_scale)) return FA3Q_ERR_SHAPE;
   if ((Dr > 0 && !is_aligned(q, 16)) || !is_aligned(k_nope_q, 16) || (Dr > 0 && !is_aligned(k_rope, 16)) ||
-      !is_aligned(out, 16) || !is_aligned(scale, 4))
+      !is_aligned(out, 16) || (!kAsym && !is_aligned(scale, 4)))
     return FA3Q_ERR_ALIGN;
+  if (kAsym && (!is_aligned(i8.k_scale_hd, 16) || !is_aligned(i8.k_offset_hd, 16))) return FA3Q_ERR_ALIGN;
   if (kQ8 ? (!is_aligned(i8.qq, 16) || !is_aligned(i8.vq, 16) || !is_aligned(i8.scale_q, 4) ||
              !is_aligned(i8.scale_v, 4))
           : (!is_aligned(q, 16) || !is_aligned(v, 16)))
@@ -546,7 +596,7 @@ int decode_launch(const uint16_t* q, const int8_t* k_nope_q, const float* scale,
   }
   const int lk = static_cast<int>(next_pow2(std::max<int64_t>(Dn / 16, Dr / 8)));
   const int lv = static_cast<int>(Dv / (kQ8 ? 16 : 8));
-  KernelFn fn = pick_kernel<kVar, kQ8>(lk, lv);
+  KernelFn fn = pick_kernel<kVar, kFmt>(lk, lv);
   if (!fn) return FA3Q_ERR_UNSUPPORTED;
 
   DecodeArgs a;
@@ -563,6 +613,9 @@ int decode_launch(const uint16_t* q, const int8_t* k_nope_q, const float* scale,
   a.vq = i8.vq;
   a.scale_q = i8.scale_q;
   a.scale_v = i8.scale_v;
+  a.k_scale_hd = i8.k_scale_hd;
+  a.k_offset_hd = i8.k_offset_hd;
+  a.params_f16 = i8.params_f16;
   a.ws_ml = need ? static_cast<float*>(workspace) : nullptr;
   a.ws_o = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                            round_up(static_cast<size_t>(B * H * p.nsplit) * 2 * sizeof(float), 256))
@@ -593,7 +646,7 @@ extern "C" int fa3q_decode_attn(const uint16_t* q, const int8_t* k_nope_q, const
                                 int64_t T, int64_t Dn, int64_t Dr, int64_t Dv, float sm_scale,
                                 float* out, void* workspace, size_t workspace_bytes,
                                 void* stream) {
-  return decode_launch<false, false>(q, k_nope_q, scale, k_rope, v, nullptr, nullptr, nullptr, Int8QV{}, B, H, T,
+  return decode_launch<false, kFmtBf16>(q, k_nope_q, scale, k_rope, v, nullptr, nullptr, nullptr, Int8QV{}, B, H, T,
                                      Dn, Dr, Dv, sm_scale, out, workspace, workspace_bytes, stream);
 }
 
@@ -603,7 +656,7 @@ extern "C" int fa3q_decode_append_attn(const uint16_t* q, const uint16_t* k_new,
                                        int64_t T, int64_t Dn, int64_t Dr, int64_t Dv, float sm_scale,
                                        float* out, void* workspace, size_t workspace_bytes,
                                        void* stream) {
-  return decode_launch<true, false>(q, k_nope_q, scale, k_rope, v, kv_len, k_new, v_new, Int8QV{}, B, H, T, Dn,
+  return decode_launch<true, kFmtBf16>(q, k_nope_q, scale, k_rope, v, kv_len, k_new, v_new, Int8QV{}, B, H, T, Dn,
                                     Dr, Dv, sm_scale, out, workspace, workspace_bytes, stream);
 }
 
@@ -617,6 +670,19 @@ extern "C" int fa3q_decode_attn_qkv8(const int8_t* q_nope_q, const uint16_t* q_r
   i8.vq = v_q;
   i8.scale_q = scale_q;
   i8.scale_v = scale_v;
-  return decode_launch<false, true>(q_rope, k_nope_q, scale_k, k_rope, nullptr, nullptr, nullptr, nullptr, i8, B, H,
-                                    T, Dn, Dr, Dv, sm_scale, out, workspace, workspace_bytes, stream);
+  return decode_launch<false, kFmtQkv8>(q_rope, k_nope_q, scale_k, k_rope, nullptr, nullptr, nullptr, nullptr, i8, B,
+                                        H, T, Dn, Dr, Dv, sm_scale, out, workspace, workspace_bytes, stream);
+}
+
+extern "C" int fa3q_decode_attn_asym(const uint16_t* q, const int8_t* k_nope_q, const uint16_t* k_scale,
+                                     const uint16_t* k_offset, int params_dtype, const uint16_t* k_rope,
+                                     const uint16_t* v, int64_t B, int64_t H, int64_t T, int64_t Dn, int64_t Dr,
+                                     int64_t Dv, float sm_scale, float* out, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  Int8QV i8;
+  i8.k_scale_hd = k_scale;
+  i8.k_offset_hd = k_offset;
+  i8.params_f16 = params_dtype == FA3Q_BF16 ? 0 : (params_dtype == FA3Q_F16 ? 1 : -1);
+  return decode_launch<false, kFmtAsym>(q, k_nope_q, nullptr, k_rope, v, nullptr, nullptr, nullptr, i8, B, H, T, Dn,
+                                        Dr, Dv, sm_scale, out, workspace, workspace_bytes, stream);
 }

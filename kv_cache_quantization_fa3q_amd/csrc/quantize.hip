@@ -20,13 +20,33 @@
 // of x/s.  So rint(y) equals rint(fl32(x/s)) unless y lies within 2.3e-5 of a half-integer;
 // such elements (and every element of a head whose scale is not a moderate normal number)
 // take the correctly rounded division.  Above 127.5 both clamp to 127.
+//
+// Asymmetric variant (fa3q_quantize_asym).  MindIE Turbo page "Attention量化", tables 1
+// and 2: the K activation carries a scale and an offset per (head, dim), stored as float16
+// or bfloat16; the pages give no formula, so the plain asymmetric INT8 code is used:
+//   code = clamp(round_half_even(fl32(fl32(x / s[h,d]) + o[h,d])), -128, 127),
+// 0 for a channel whose scale is 0, the value of a code being (code - o) * s.  Same
+// streaming layout and item shape; each lane also holds the 8 scales, reciprocals and
+// offsets of the dims it covers.  The quotient: with r = v_rcp(s) (at most 1 ulp off 1/s)
+// and y' = x*r, |y' - fl32(x/s)| <= |y'| * 2^-22 (1 + 2^-20); both sums are rounded to
+// float32 below 256 with an ulp of at most 2^-16, so the two codes agree unless z' = y' + o
+// lies within |y'| * 2^-20 + 2^-15 of a half-integer (checked; the correctly rounded
+// division then decides), and for |z'| >= 200 both saturate the same way while |y'| <= 2^24
+// (the margin check sends larger |y'| to the division).  A scale outside [2^-100, 2^100]
+// sends its channel to the division too.
 #include "fa3q_internal.hpp"
 
 namespace fa3q {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kRowsPerItem = 64;
+// One single-wave workgroup per item of 16 rows, a grid of all items.  On MI355X that
+// streams this read+write mix about 15% faster than a grid-stride loop over a few
+// workgroups per CU (3.6 ms against 4.1-4.4 ms for the (64,128,4096,128+64) K); 64 to
+// 512 threads with 16 to 128 rows per item all measured within 6% of each other.  The
+// item loop remains for grids past the cap.
+constexpr int kThreads = 64;
+constexpr int kRowsPerItem = 16;
+constexpr int64_t kMaxGrid = int64_t{1} << 30;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -88,11 +108,7 @@ __global__ __launch_bounds__(kThreads) void quantize_k_kernel(QuantArgs a) {
   for (int64_t item = blockIdx.x; item < a.items; item += gridDim.x) {
     const int64_t bh = item / a.chunks_per_bh;
     const int64_t chunk = item - bh * a.chunks_per_bh;
-    const float s = a.scale[bh % a.H];
-    const bool zero = (s == 0.0f);
-    // fast quotient only for a moderate normal scale (1/s normal, x*(1/s) free of overflow)
-    const bool fast = fabsf(s) >= 0x1p-100f && fabsf(s) <= 0x1p100f;
-    const float r = 1.0f / s;
+    const int hh = __builtin_amdgcn_readfirstlane(static_cast<int>(bh % a.H));  // uniform: scalar read
     const int64_t r_begin = chunk * kRowsPerItem;
     const int nr = static_cast<int>(min(static_cast<int64_t>(kRowsPerItem), a.S - r_begin));
     const int64_t row0 = bh * a.S + r_begin;
@@ -104,27 +120,192 @@ __global__ __launch_bounds__(kThreads) void quantize_k_kernel(QuantArgs a) {
     for (int pass = 0; pass * kThreads * kNope < nn || pass * kThreads * kRope < nrp; ++pass) {
       u32x4 xn[kNope], xr[kRope];
       int on[kNope], orr[kRope];
+      // Loads are unconditional (a vector past the item's end re-reads its last vector and is
+      // not stored), so they issue back to back instead of one exec-masked block at a time.
 #pragma unroll
       for (int j = 0; j < kNope; ++j) {
         const int q = (pass * kNope + j) * kThreads + tid;
-        const int row = q / Un, unit = q - row * Un;
+        const int qc = min(q, nn - 1);
+        const int row = qc / Un, unit = qc - row * Un;
         on[j] = q < nn ? row * a.Dn + unit * 8 : -1;
-        if (q < nn) xn[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kin + static_cast<int64_t>(row) * Dk + unit * 8));
+        xn[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kin + static_cast<int64_t>(row) * Dk + unit * 8));
       }
       if (Ur > 0) {
 #pragma unroll
         for (int j = 0; j < kRope; ++j) {
           const int q = (pass * kRope + j) * kThreads + tid;
-          const int row = q / Ur, unit = q - row * Ur;
+          const int qc = min(q, nrp - 1);
+          const int row = qc / Ur, unit = qc - row * Ur;
           orr[j] = q < nrp ? row * a.Dr + unit * 8 : -1;
-          if (q < nrp)
-            xr[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kin + static_cast<int64_t>(row) * Dk + a.Dn + unit * 8));
+          xr[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kin + static_cast<int64_t>(row) * Dk + a.Dn + unit * 8));
         }
       }
+      // the scale is read after the data loads are issued, so its latency hides behind theirs
+      const float s = a.scale[hh];
+      const bool zero = (s == 0.0f);
+      // fast quotient only for a moderate normal scale (1/s normal, x*(1/s) free of overflow)
+      const bool fast = fabsf(s) >= 0x1p-100f && fabsf(s) <= 0x1p100f;
+      const float r = 1.0f / s;
 #pragma unroll
       for (int j = 0; j < kNope; ++j) {
         if (on[j] >= 0) {
           const u32x2 o = zero ? u32x2{0u, 0u} : quant8(xn[j], s, r, fast);
+          __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(qout + on[j]));
+        }
+      }
+      if (Ur > 0) {
+#pragma unroll
+        for (int j = 0; j < kRope; ++j)
+          if (orr[j] >= 0) __builtin_nontemporal_store(xr[j], reinterpret_cast<u32x4*>(rout + orr[j]));
+      }
+    }
+  }
+}
+
+struct AsymArgs {
+  const uint16_t* k;
+  const uint16_t* scale;   // [H][Dn] bf16 or float16 patterns
+  const uint16_t* offset;  // [H][Dn]
+  int8_t* kq;
+  uint16_t* kr;
+  int64_t S;
+  int64_t items;
+  int32_t chunks_per_bh;
+  int32_t H;
+  int32_t Dn;
+  int32_t Dr;
+  int32_t f16;  // 1: float16 tables, 0: bfloat16
+};
+
+__device__ __forceinline__ float param_value(uint32_t bits16, bool f16) {
+  return f16 ? static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)))
+             : __uint_as_float(bits16 << 16);
+}
+
+// The 8 channels of one 16-byte unit: scale, fast-path reciprocal (NaN for a scale the fast
+// path does not take, which forces the division) and offset.
+struct AsymUnit {
+  float s[8], r[8], o[8];
+};
+
+__device__ __forceinline__ AsymUnit load_asym_unit(const uint16_t* scale, const uint16_t* offset, bool f16) {
+  const u32x4 sw = *reinterpret_cast<const u32x4*>(scale);
+  const u32x4 ow = *reinterpret_cast<const u32x4*>(offset);
+  const uint32_t sv[4] = {sw.x, sw.y, sw.z, sw.w}, ov[4] = {ow.x, ow.y, ow.z, ow.w};
+  AsymUnit u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    u.s[2 * i] = param_value(sv[i] & 0xffffu, f16);
+    u.s[2 * i + 1] = param_value(sv[i] >> 16, f16);
+    u.o[2 * i] = param_value(ov[i] & 0xffffu, f16);
+    u.o[2 * i + 1] = param_value(ov[i] >> 16, f16);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float m = fabsf(u.s[i]);
+    u.r[i] = (m >= 0x1p-100f && m <= 0x1p100f) ? __builtin_amdgcn_rcpf(u.s[i]) : __builtin_nanf("");
+  }
+  return u;
+}
+
+__device__ __forceinline__ int asym_code_exact(float x, float s, float o) {
+  if (s == 0.0f) return 0;
+  const float z = x / s + o;  // IEEE division, then one float32 addition
+  return static_cast<int>(__builtin_amdgcn_fmed3f(rintf(z), -128.0f, 127.0f));
+}
+
+__device__ __forceinline__ u32x2 quant8_asym(const u32x4& w, const AsymUnit& p) {
+  float xv[8];
+  xv[0] = bf16_lo(w.x); xv[1] = bf16_hi(w.x); xv[2] = bf16_lo(w.y); xv[3] = bf16_hi(w.y);
+  xv[4] = bf16_lo(w.z); xv[5] = bf16_hi(w.z); xv[6] = bf16_lo(w.w); xv[7] = bf16_hi(w.w);
+  int c[8];
+  bool amb = false;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float y = __fmul_rn(xv[i], p.r[i]);
+    const float z = __fadd_rn(y, p.o[i]);
+    const float n = rintf(z);
+    const float thr = fmaf(-fabsf(y), 0x1p-20f, 0.5f - 0x1p-15f);
+    amb |= !(fabsf(z - n) <= thr);  // NaN anywhere (skipped scale, non-finite input) -> division
+    c[i] = static_cast<int>(__builtin_amdgcn_fmed3f(n, -128.0f, 127.0f));
+  }
+  if (__ballot(amb) != 0) {
+    if (amb) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) c[i] = asym_code_exact(xv[i], p.s[i], p.o[i]);
+    }
+  }
+  u32x2 o;
+  o.x = (c[0] & 0xff) | ((c[1] & 0xff) << 8) | ((c[2] & 0xff) << 16) | (static_cast<uint32_t>(c[3]) << 24);
+  o.y = (c[4] & 0xff) | ((c[5] & 0xff) << 8) | ((c[6] & 0xff) << 16) | (static_cast<uint32_t>(c[7]) << 24);
+  return o;
+}
+
+// UN / UR as in quantize_k_kernel.  When UN divides the block size every nope vector of a
+// lane lies in the same unit (q % UN == tid % UN), so the lane loads its 8 channels' tables
+// once per item; otherwise per vector.
+template <int UN, int UR>
+__global__ __launch_bounds__(kThreads) void quantize_asym_kernel(AsymArgs a) {
+  const int tid = static_cast<int>(threadIdx.x);
+  const int Dk = a.Dn + a.Dr;
+  const int Un = UN ? UN : a.Dn >> 3;
+  const int Ur = UR ? UR : a.Dr >> 3;
+  constexpr bool kFixedUnit = UN != 0 && kThreads % UN == 0;
+  constexpr int kNope = UN ? kRowsPerItem * UN / kThreads : 4;
+  constexpr int kRope = UR ? (kRowsPerItem * UR + kThreads - 1) / kThreads : 2;
+  const bool f16 = a.f16 != 0;
+
+  for (int64_t item = blockIdx.x; item < a.items; item += gridDim.x) {
+    const int64_t bh = item / a.chunks_per_bh;
+    const int64_t chunk = item - bh * a.chunks_per_bh;
+    const int64_t h = bh % a.H;
+    const uint16_t* stab = a.scale + h * a.Dn;
+    const uint16_t* otab = a.offset + h * a.Dn;
+    const int64_t r_begin = chunk * kRowsPerItem;
+    const int nr = static_cast<int>(min(static_cast<int64_t>(kRowsPerItem), a.S - r_begin));
+    const int64_t row0 = bh * a.S + r_begin;
+    const uint16_t* __restrict__ kin = a.k + row0 * Dk;
+    int8_t* __restrict__ qout = a.kq + row0 * a.Dn;
+    uint16_t* __restrict__ rout = a.kr + row0 * a.Dr;
+    const int nn = nr * Un, nrp = nr * Ur;
+
+    for (int pass = 0; pass * kThreads * kNope < nn || pass * kThreads * kRope < nrp; ++pass) {
+      u32x4 xn[kNope], xr[kRope];
+      int on[kNope], un[kNope], orr[kRope];
+      // Loads are unconditional (a vector past the item's end re-reads its last vector and is
+      // not stored), so they issue back to back instead of one exec-masked block at a time.
+#pragma unroll
+      for (int j = 0; j < kNope; ++j) {
+        const int q = (pass * kNope + j) * kThreads + tid;
+        const int qc = min(q, nn - 1);
+        const int row = qc / Un, unit = qc - row * Un;
+        on[j] = q < nn ? row * a.Dn + unit * 8 : -1;
+        un[j] = unit;
+        xn[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kin + static_cast<int64_t>(row) * Dk + unit * 8));
+      }
+      if (Ur > 0) {
+#pragma unroll
+        for (int j = 0; j < kRope; ++j) {
+          const int q = (pass * kRope + j) * kThreads + tid;
+          const int qc = min(q, nrp - 1);
+          const int row = qc / Ur, unit = qc - row * Ur;
+          orr[j] = q < nrp ? row * a.Dr + unit * 8 : -1;
+          xr[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kin + static_cast<int64_t>(row) * Dk + a.Dn + unit * 8));
+        }
+      }
+      // tables after the data loads (their latency hides behind the data's)
+      AsymUnit fixed;
+      if constexpr (kFixedUnit) fixed = load_asym_unit(stab + (tid % UN) * 8, otab + (tid % UN) * 8, f16);
+#pragma unroll
+      for (int j = 0; j < kNope; ++j) {
+        if (on[j] >= 0) {
+          u32x2 o;
+          if constexpr (kFixedUnit) {
+            o = quant8_asym(xn[j], fixed);
+          } else {
+            const AsymUnit p = load_asym_unit(stab + un[j] * 8, otab + un[j] * 8, f16);
+            o = quant8_asym(xn[j], p);
+          }
           __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(qout + on[j]));
         }
       }
@@ -168,11 +349,49 @@ extern "C" int fa3q_quantize_k(const uint16_t* k, const float* scale, int8_t* k_
   a.H = static_cast<int32_t>(H);
   a.Dn = static_cast<int32_t>(Dn);
   a.Dr = static_cast<int32_t>(Dr);
-  const int64_t grid = std::min<int64_t>(a.items, static_cast<int64_t>(device_cu_count()) * 8);
+  const int64_t grid = std::min<int64_t>(a.items, kMaxGrid);
   const dim3 g(static_cast<unsigned>(grid)), blk(kThreads);
   if (Dn == 128 && Dr == 64)
     hipLaunchKernelGGL((quantize_k_kernel<16, 8>), g, blk, 0, as_stream(stream), a);
   else
     hipLaunchKernelGGL((quantize_k_kernel<0, 0>), g, blk, 0, as_stream(stream), a);
+  return launch_status();
+}
+
+extern "C" int fa3q_quantize_asym(const uint16_t* k, const uint16_t* scale, const uint16_t* offset,
+                                  int params_dtype, int8_t* k_nope_q, uint16_t* k_rope, int64_t B,
+                                  int64_t H, int64_t S, int64_t Dn, int64_t Dr, void* stream) {
+  if (!k || !scale || !offset || !k_nope_q || (Dr > 0 && !k_rope)) return FA3Q_ERR_NULL;
+  if (params_dtype != FA3Q_BF16 && params_dtype != FA3Q_F16) return FA3Q_ERR_DTYPE;
+  if (B <= 0 || H <= 0 || S <= 0) return FA3Q_ERR_SHAPE;
+  if (Dn <= 0 || Dn % 16 != 0 || Dn > 4096) return FA3Q_ERR_SHAPE;
+  if (Dr < 0 || Dr % 8 != 0 || Dr > 2048) return FA3Q_ERR_SHAPE;
+  if (B > (int64_t{1} << 31) / H) return FA3Q_ERR_SHAPE;
+  const int64_t chunks = (S + kRowsPerItem - 1) / kRowsPerItem;
+  if (chunks > (int64_t{1} << 30) || B * H > (int64_t{1} << 62) / (chunks * kRowsPerItem * (Dn + Dr)))
+    return FA3Q_ERR_SHAPE;
+  if (!is_aligned(k, 16) || !is_aligned(k_nope_q, 16) || (Dr > 0 && !is_aligned(k_rope, 16)) ||
+      !is_aligned(scale, 16) || !is_aligned(offset, 16))
+    return FA3Q_ERR_ALIGN;
+
+  AsymArgs a;
+  a.k = k;
+  a.scale = scale;
+  a.offset = offset;
+  a.kq = k_nope_q;
+  a.kr = k_rope;
+  a.S = S;
+  a.chunks_per_bh = static_cast<int32_t>(chunks);
+  a.items = B * H * chunks;
+  a.H = static_cast<int32_t>(H);
+  a.Dn = static_cast<int32_t>(Dn);
+  a.Dr = static_cast<int32_t>(Dr);
+  a.f16 = params_dtype == FA3Q_F16 ? 1 : 0;
+  const int64_t grid = std::min<int64_t>(a.items, kMaxGrid);
+  const dim3 g(static_cast<unsigned>(grid)), blk(kThreads);
+  if (Dn == 128 && Dr == 64)
+    hipLaunchKernelGGL((quantize_asym_kernel<16, 8>), g, blk, 0, as_stream(stream), a);
+  else
+    hipLaunchKernelGGL((quantize_asym_kernel<0, 0>), g, blk, 0, as_stream(stream), a);
   return launch_status();
 }

@@ -12,7 +12,7 @@ from typing import Optional, Tuple
 
 import torch
 
-from ._lib import FA3Q_BF16, FA3Q_F32, Fa3qError, lib
+from ._lib import FA3Q_BF16, FA3Q_F16, FA3Q_F32, Fa3qError, lib
 
 __all__ = [
     "fa3q_calibrate_max_windows",
@@ -26,6 +26,8 @@ __all__ = [
     "fa3q_decode_attn",
     "fa3q_decode_append_attn",
     "fa3q_decode_attn_qkv8",
+    "fa3q_quantize_asym",
+    "fa3q_decode_attn_asym",
     "dtype_code",
 ]
 
@@ -261,4 +263,66 @@ def fa3q_decode_attn_qkv8(q_nope_q: torch.Tensor, q_rope: Optional[torch.Tensor]
                                      _ptr(scale_v), B, H, T, Dn, Dr, Dv, ctypes.c_float(float(sm_scale)), _ptr(out),
                                      _ptr(workspace), wbytes, _stream(stream))
     _check(st, "fa3q_decode_attn_qkv8")
+    return out
+
+
+# --------------------------------------------------------------------------- asymmetric K cache
+
+
+def _param_code(name: str, scale: torch.Tensor, offset: torch.Tensor, H: int, Dn: int) -> int:
+    if scale.dtype != offset.dtype or scale.dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError(f"{name}: scale and offset must both be bfloat16 or both float16")
+    if tuple(scale.shape) != (H, Dn) or tuple(offset.shape) != (H, Dn):
+        raise ValueError(f"{name}: scale and offset must be (H, Dn) = ({H}, {Dn})")
+    return FA3Q_BF16 if scale.dtype == torch.bfloat16 else FA3Q_F16
+
+
+def fa3q_quantize_asym(k: torch.Tensor, scale: torch.Tensor, offset: torch.Tensor, Dn: int,
+                       k_nope_q: Optional[torch.Tensor] = None, k_rope: Optional[torch.Tensor] = None,
+                       stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """bf16 ``k (B,H,S,Dn+Dr)`` and ``(H,Dn)`` scale / offset tables -> asymmetric int8 codes and bf16 RoPE part."""
+    if k.dim() != 4 or k.dtype != torch.bfloat16:
+        raise ValueError("k must be bfloat16 (B, H, S, Dn + Dr)")
+    B, H, S, Dk = (int(v) for v in k.shape)
+    Dr = Dk - int(Dn)
+    code = _param_code("fa3q_quantize_asym", scale, offset, H, int(Dn))
+    if k_nope_q is None:
+        k_nope_q = torch.empty((B, H, S, int(Dn)), dtype=torch.int8, device=k.device)
+    if k_rope is None:
+        k_rope = torch.empty((B, H, S, Dr), dtype=torch.bfloat16, device=k.device)
+    _need_gpu("fa3q_quantize_asym", k, scale, offset, k_nope_q, k_rope)
+    _check(lib().fa3q_quantize_asym(_ptr(k), _ptr(scale), _ptr(offset), code, _ptr(k_nope_q),
+                                    _ptr(k_rope) if Dr > 0 else None, B, H, S, int(Dn), Dr, _stream(stream)),
+           "fa3q_quantize_asym")
+    return k_nope_q, k_rope
+
+
+def fa3q_decode_attn_asym(q: torch.Tensor, k_nope_q: torch.Tensor, scale: torch.Tensor, offset: torch.Tensor,
+                          k_rope: Optional[torch.Tensor], v: torch.Tensor, sm_scale: float,
+                          out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                          stream=None) -> torch.Tensor:
+    """Single-query attention over the asymmetric INT8 K-nope cache -> float32 ``(B,H,Dv)``."""
+    if k_nope_q.dim() != 4 or k_nope_q.dtype != torch.int8:
+        raise ValueError("k_nope_q must be int8 (B, H, T, Dn)")
+    B, H, T, Dn = (int(s) for s in k_nope_q.shape)
+    Dr = int(k_rope.shape[-1]) if k_rope is not None else 0
+    Dv = int(v.shape[-1])
+    code = _param_code("fa3q_decode_attn_asym", scale, offset, H, Dn)
+    if q.shape != (B, H, Dn + Dr) or q.dtype != torch.bfloat16:
+        raise ValueError("q must be bfloat16 (B, H, Dn + Dr)")
+    if v.shape != (B, H, T, Dv) or v.dtype != torch.bfloat16:
+        raise ValueError("v must be bfloat16 (B, H, T, Dv)")
+    if k_rope is not None and (k_rope.shape != (B, H, T, Dr) or k_rope.dtype != torch.bfloat16):
+        raise ValueError("k_rope must be bfloat16 (B, H, T, Dr)")
+    if out is None:
+        out = torch.empty((B, H, Dv), dtype=torch.float32, device=q.device)
+    _need_gpu("fa3q_decode_attn_asym", q, k_nope_q, scale, offset, k_rope, v, out)
+    nbytes = int(lib().fa3q_decode_attn_workspace_bytes(B, H, T, Dv))
+    workspace = _workspace(nbytes, q.device, workspace)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().fa3q_decode_attn_asym(_ptr(q), _ptr(k_nope_q), _ptr(scale), _ptr(offset), code,
+                                     _ptr(k_rope) if Dr > 0 else None, _ptr(v), B, H, T, Dn, Dr, Dv,
+                                     ctypes.c_float(float(sm_scale)), _ptr(out), _ptr(workspace), wbytes,
+                                     _stream(stream))
+    _check(st, "fa3q_decode_attn_asym")
     return out

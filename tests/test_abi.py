@@ -223,6 +223,66 @@ def test_decode_qkv8_rejections():
     assert call(sv=_p(2)) == L.FA3Q_ERR_ALIGN
     assert call(ws=None) == L.FA3Q_ERR_WORKSPACE
 
+@no_gpu_only
+def test_quantize_asym_rejections():
+    f = fa.lib().fa3q_quantize_asym
+    ok = dict(k=_p(), s=_p(), o=_p(), dt=L.FA3Q_BF16, q=_p(), r=_p(), B=1, H=4, S=64, Dn=32, Dr=16)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["k"], a["s"], a["o"], a["dt"], a["q"], a["r"], a["B"], a["H"], a["S"], a["Dn"], a["Dr"], None)
+
+    for name in ("k", "s", "o", "q", "r"):
+        assert call(**{name: None}) == L.FA3Q_ERR_NULL, name
+    assert call(dt=L.FA3Q_F32) == L.FA3Q_ERR_DTYPE
+    assert call(dt=7) == L.FA3Q_ERR_DTYPE
+    assert call(S=0) == L.FA3Q_ERR_SHAPE
+    assert call(Dn=24) == L.FA3Q_ERR_SHAPE
+    assert call(Dr=12) == L.FA3Q_ERR_SHAPE
+    assert call(k=_p(8)) == L.FA3Q_ERR_ALIGN
+    assert call(s=_p(8)) == L.FA3Q_ERR_ALIGN   # tables are read 16 bytes at a time
+    assert call(o=_p(4)) == L.FA3Q_ERR_ALIGN
+    assert call(q=_p(4)) == L.FA3Q_ERR_ALIGN
+
+
+@no_gpu_only
+def test_decode_asym_rejections():
+    f = fa.lib().fa3q_decode_attn_asym
+    ok = dict(q=_p(), kq=_p(), s=_p(), of=_p(), dt=L.FA3Q_F16, kr=_p(), v=_p(), B=8, H=128, T=32768, Dn=128,
+              Dr=64, Dv=128, sm=0.07, o=_p(), ws=_p(), wsb=1 << 30)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["q"], a["kq"], a["s"], a["of"], a["dt"], a["kr"], a["v"], a["B"], a["H"], a["T"], a["Dn"],
+                 a["Dr"], a["Dv"], ctypes.c_float(a["sm"]), a["o"], a["ws"], a["wsb"], None)
+
+    for name in ("q", "kq", "s", "of", "kr", "v", "o"):
+        assert call(**{name: None}) == L.FA3Q_ERR_NULL, name
+    assert call(dt=L.FA3Q_F32) == L.FA3Q_ERR_DTYPE
+    assert call(dt=3) == L.FA3Q_ERR_DTYPE
+    assert call(T=0) == L.FA3Q_ERR_SHAPE
+    assert call(Dn=120) == L.FA3Q_ERR_SHAPE
+    assert call(Dv=96) == L.FA3Q_ERR_SHAPE
+    assert call(s=_p(8)) == L.FA3Q_ERR_ALIGN
+    assert call(of=_p(2)) == L.FA3Q_ERR_ALIGN
+    assert call(v=_p(8)) == L.FA3Q_ERR_ALIGN
+    assert call(ws=None) == L.FA3Q_ERR_WORKSPACE
+
+
+def test_binding_refuses_mismatched_asym_tables():
+    import torch
+    k = torch.zeros((1, 2, 16, 48), dtype=torch.bfloat16)
+    s = torch.ones((2, 32), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.fa3q_quantize_asym(k, s, s.to(torch.float16), 32)     # mixed table dtypes
+    with pytest.raises(ValueError):
+        fa.fa3q_quantize_asym(k, s[:, :16], s[:, :16], 32)       # wrong table shape
+    with pytest.raises(ValueError):
+        fa.fa3q_quantize_asym(k, s.float(), s.float(), 32)       # float32 tables
+    with pytest.raises(ValueError):
+        fa.fa3q_quantize_asym(k, s, s, 32)                       # host tensors
+
+
 def test_binding_refuses_host_tensors():
     import torch
     x = torch.zeros((1, 4, 64, 32), dtype=torch.float32)

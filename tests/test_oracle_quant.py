@@ -168,6 +168,11 @@ def test_asym_hand_values_and_saturation():
     half = _bits16(np.full((1, Dn), 0.5, np.float32))
     codes, _ = oracle.quantize_asym(k, one, half, Dn)
     assert codes.reshape(-1).tolist() == [1, 0, 2, 127, -128, 127, -128]
+    # a channel whose scale is 0 gets code 0 whatever its input and offset
+    zero_first = one.copy()
+    zero_first[0, 0] = 0
+    codes, _ = oracle.quantize_asym(k, zero_first, half, Dn)
+    assert codes.reshape(-1).tolist() == [0, 0, 2, 127, -128, 127, -128]
 
 
 def test_asym_without_offset_is_the_symmetric_quantiser_inside_its_range():

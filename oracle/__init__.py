@@ -35,7 +35,8 @@ from .recall_window import (
     qparams,
 )
 from .quant import quantize_k, dequantize_k_nope
-from .attention import attention_fp64, decode_attn, decode_append_attn, decode_attn_qkv8, decode_attn_asym
+from .attention import (attention_fp64, decode_attn, decode_append_attn, decode_attn_qkv8, decode_attn_asym,
+                        decode_attn_latent)
 from .asym import params_to_f32, quantize_asym, dequantize_asym
 
 __all__ = [
@@ -57,6 +58,7 @@ __all__ = [
     "decode_attn",
     "decode_append_attn",
     "decode_attn_qkv8",
+    "decode_attn_latent",
     "decode_attn_asym",
     "params_to_f32",
     "quantize_asym",

@@ -124,3 +124,36 @@ def decode_attn_asym(q_bits, codes, scale_bits, offset_bits, rope_bits, v_bits, 
     from .asym import dequantize_asym
     k = np.concatenate([dequantize_asym(codes, scale_bits, offset_bits, dtype), bf16_bits_to_f64(rope_bits)], axis=-1)
     return attention_fp64(bf16_bits_to_f64(q_bits), k, bf16_bits_to_f64(v_bits), float(np.float32(sm_scale)))
+
+
+def decode_attn_latent(q_bits, codes, scale, rope_bits, sm_scale: float, Dl: int) -> np.ndarray:
+    """Decode over a shared-latent (absorbed MLA) cache: every head of a sequence reads the same rows.
+
+    MindIE LLM page "FA3 quantization", overview (MLA attention; only the non-RoPE part of
+    K goes to INT8, the RoPE part stays floating point).  The pages give no layout for the
+    shared latent; the readings (also in the design doc) are:
+
+    * L1 the latent rows ``[c | k_rope]`` of a sequence form one head shared by all query
+      heads, so the per-head method runs with one head: ``c`` holds INT8 codes with one
+      scale ``s`` (from the same calibration and quantiser), ``k_rope`` stays bf16;
+    * L2 the query is already absorbed: ``q (B,H,Dl+Dr)`` bf16 is ``[q_abs | q_rope]``; the
+      score of token t is ``sm * (s * <q_abs, c_t> + <q_rope, r_t>)`` and the value is the
+      dequantised latent ``s * c_t``;
+    * L3 the output is the latent-space attention ``(B,H,Dl)``, float64 here (the
+      up-projection to the head's value space is outside the path).
+
+    ``codes (B,T,Dl)`` int8, ``rope_bits (B,T,Dr)`` bf16 patterns, ``scale`` a scalar.
+    """
+    q = bf16_bits_to_f64(np.asarray(q_bits, dtype=np.uint16))
+    codes = np.asarray(codes, dtype=np.int8)
+    B, H, _ = q.shape
+    T = codes.shape[1]
+    if codes.shape != (B, T, Dl):
+        raise ValueError("codes must be (B, T, Dl)")
+    s = float(np.float32(scale))
+    c = codes.astype(np.float64) * s                                   # L1: dequantised latent
+    r = bf16_bits_to_f64(np.asarray(rope_bits, dtype=np.uint16)).reshape(B, T, -1)
+    k = np.concatenate([c, r], axis=-1)                                # (B,T,Dl+Dr)
+    k = np.broadcast_to(k[:, None], (B, H, T, k.shape[-1]))            # shared by every head
+    v = np.broadcast_to(c[:, None], (B, H, T, Dl))                     # L2: value = latent
+    return attention_fp64(q, k, v, float(np.float32(sm_scale)))       # sm as the float32 callers pass

@@ -8,6 +8,7 @@ on the CPU and against special cases with closed-form answers.
 import math
 
 import numpy as np
+import pytest
 import torch
 
 import oracle
@@ -240,3 +241,65 @@ def test_qkv8_with_unit_scales_is_plain_attention_over_codes():
     out1 = oracle.decode_attn_qkv8(qc, zero_r, one, kc[:, :, :1], one, zero_kr[:, :, :1], vc[:, :, :1],
                                    np.full(H, 0.25, np.float32), 0.5)
     np.testing.assert_array_equal(out1, 0.25 * vc[:, :, 0].astype(np.float64))
+
+
+# ----------------------------------------------------------------------------- shared-latent (absorbed MLA) cache
+
+
+def test_latent_decode_matches_sdpa_over_an_independently_assembled_cache():
+    rng = np.random.default_rng(61)
+    B, H, T, Dl, Dr = 2, 5, 40, 32, 16
+    qb = _rand_bits(rng, (B, H, Dl + Dr))
+    codes = rng.integers(-127, 128, size=(B, T, Dl)).astype(np.int8)
+    rope = _rand_bits(rng, (B, T, Dr))
+    s = np.float32(0.0173)
+    sm = float(np.float32(1.0 / math.sqrt(192)))
+    out = oracle.decode_attn_latent(qb, codes, s, rope, sm, Dl)
+    q = torch.from_numpy(oracle.bf16_bits_to_f64(qb)).unsqueeze(2)                       # (B,H,1,D)
+    lat = torch.from_numpy(codes.astype(np.float64)) * float(s)                          # (B,T,Dl)
+    k = torch.cat([lat, torch.from_numpy(oracle.bf16_bits_to_f64(rope))], -1)           # (B,T,D)
+    k = k.unsqueeze(1).expand(B, H, T, Dl + Dr)
+    v = lat.unsqueeze(1).expand(B, H, T, Dl)
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=sm).squeeze(2).numpy()
+    assert out.shape == (B, H, Dl)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-15)
+
+
+def test_latent_decode_is_per_head_decode_of_the_latent_copied_to_every_head():
+    # with a power-of-two scale the dequantised latent is exact in bf16, so the per-head
+    # decode (K-nope codes + per-head scale, bf16 V) over the latent copied to every head
+    # must give the same numbers
+    rng = np.random.default_rng(62)
+    B, H, T, Dl, Dr = 2, 4, 33, 16, 8
+    qb = _rand_bits(rng, (B, H, Dl + Dr))
+    codes = rng.integers(-127, 128, size=(B, T, Dl)).astype(np.int8)
+    rope = _rand_bits(rng, (B, T, Dr))
+    s = np.float32(2.0 ** -6)
+    v_bits = oracle.f32_to_bf16_bits_rne(codes.astype(np.float32) * s)
+    assert np.array_equal(oracle.bf16_bits_to_f64(v_bits), codes.astype(np.float64) * float(s))
+    per_head = oracle.decode_attn(qb, np.repeat(codes[:, None], H, 1), np.full(H, s, np.float32),
+                                  np.repeat(rope[:, None], H, 1), np.repeat(v_bits[:, None], H, 1), 0.3)
+    np.testing.assert_allclose(oracle.decode_attn_latent(qb, codes, s, rope, 0.3, Dl), per_head, rtol=1e-13, atol=0)
+
+
+def test_latent_decode_special_cases():
+    rng = np.random.default_rng(63)
+    B, H, T, Dl, Dr = 1, 3, 12, 16, 8
+    codes = rng.integers(-127, 128, size=(B, T, Dl)).astype(np.int8)
+    rope = _rand_bits(rng, (B, T, Dr))
+    s = np.float32(0.05)
+    # one token: every head returns its dequantised latent
+    qb = _rand_bits(rng, (B, H, Dl + Dr))
+    out1 = oracle.decode_attn_latent(qb, codes[:, :1], s, rope[:, :1], 0.2, Dl)
+    np.testing.assert_array_equal(out1, np.broadcast_to(codes[:, None, 0].astype(np.float64) * float(s), (B, H, Dl)))
+    # zero query: uniform weights, the mean of the dequantised latent
+    q0 = np.zeros((B, H, Dl + Dr), np.uint16)
+    out0 = oracle.decode_attn_latent(q0, codes, s, rope, 0.2, Dl)
+    mean = codes.astype(np.float64).mean(axis=1) * float(s)
+    np.testing.assert_allclose(out0, np.broadcast_to(mean[:, None], (B, H, Dl)), rtol=1e-13, atol=1e-16)
+    # heads with equal query rows see the same weights
+    qb[:, 2] = qb[:, 0]
+    out = oracle.decode_attn_latent(qb, codes, s, rope, 0.2, Dl)
+    np.testing.assert_array_equal(out[:, 2], out[:, 0])
+    with pytest.raises(ValueError):
+        oracle.decode_attn_latent(qb, codes[..., :8], s, rope, 0.2, Dl)

@@ -17,6 +17,8 @@
  *   8. fa3q_quantize_asym      -- non-RoPE part of K -> asymmetric INT8 codes with a scale and
  *      an offset per (head, dim); RoPE part kept in bf16
  *   9. fa3q_decode_attn_asym   -- attention as in 5 over the asymmetric K-nope cache of 8
+ *  10. fa3q_decode_latent      -- attention of every head of a sequence over one shared-latent
+ *      (absorbed MLA) cache: INT8 latent (one scale) + bf16 RoPE part, on the matrix cores
  *
  * Sources, cited by page title and section:
  *   [MS] msModelSlim documentation, "FA3量化：Flash Attention 3激活量化算法说明"
@@ -330,6 +332,42 @@ int fa3q_decode_attn_asym(const uint16_t* q, const int8_t* k_nope_q, const uint1
                           const uint16_t* v, int64_t B, int64_t H, int64_t T, int64_t Dn, int64_t Dr,
                           int64_t Dv, float sm_scale, float* out, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* 10. Decode attention over a shared-latent (absorbed MLA) cache            */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Device workspace fa3q_decode_latent needs, in bytes (0 when none is needed or
+ * the arguments are invalid).
+ */
+size_t fa3q_decode_latent_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t Dl);
+
+/*
+ * [MI] overview: in MLA attention only the non-RoPE part of K goes to 8 bits,
+ * the RoPE part stays floating point.  With the up-projections absorbed into the
+ * query, all H query heads of sequence b read the same cache rows: a latent
+ * c[b,t,:] of Dl INT8 codes with ONE scale s (the per-head method of 1-4 run
+ * with one head, e.g. fa3q_quantize_k on a (B,1,T,Dl+Dr) tensor) and Dr bf16
+ * RoPE features k_rope[b,t,:].  For q[b,h,:] = [q_abs (Dl) | q_rope (Dr)]:
+ *   s_t        = sm_scale * ( s * sum_{d<Dl} q_abs[d] * c[b,t,d] + sum_{j<Dr} q_rope[j] * k_rope[b,t,j] )
+ *   out[b,h,:] = s * sum_t softmax(s)_t * c[b,t,:]        (latent-space output)
+ * Both products run on the matrix cores with float32 accumulation; the softmax
+ * weights enter the second product as two bf16 terms (hi + lo), so each weight
+ * carries a relative error below 2^-17.
+ *
+ *   q          device bf16 (B,H,Dl+Dr) contiguous, 16-byte aligned.
+ *   c_q        device int8 (B,T,Dl) contiguous, 16-byte aligned.
+ *   scale      device float32 [1], 4-byte aligned.
+ *   k_rope     device bf16 (B,T,Dr), 16-byte aligned; may be NULL iff Dr == 0.
+ *   out        device float32 (B,H,Dl), 16-byte aligned.
+ *   B,H,T > 0; Dl in {128, 256, 512}; Dr in {0, 32, 64}.
+ *   workspace  device, 256-byte aligned, >= fa3q_decode_latent_workspace_bytes(B,H,T,Dl);
+ *              may be NULL when that query returns 0.
+ */
+int fa3q_decode_latent(const uint16_t* q, const int8_t* c_q, const float* scale, const uint16_t* k_rope,
+                       int64_t B, int64_t H, int64_t T, int64_t Dl, int64_t Dr, float sm_scale, float* out,
+                       void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

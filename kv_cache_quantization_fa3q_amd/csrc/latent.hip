@@ -1,0 +1,375 @@
+// Decode attention over a shared-latent (absorbed MLA) cache on the matrix cores.
+//
+// MindIE LLM page "FA3 quantization", overview: in MLA attention only the non-RoPE part of
+// K goes to 8 bits and the RoPE part stays floating point, to shrink the KV cache of the
+// decode phase.  With the up-projections absorbed into the query, every query head of a
+// sequence reads the same cache rows [c | k_rope]: a latent c of Dl features (INT8 codes
+// with one scale s, the per-head method applied with one head) and Dr bf16 RoPE features.
+// For query q = [q_abs | q_rope] of head h:
+//   score_t = sm * (s * <q_abs, c_t> + <q_rope, r_t>),  out = s * sum_t softmax(score)_t c_t
+// (the latent-space output; the value up-projection is outside this path).
+//
+// Sharing the rows across heads makes both products dense [heads x tokens] contractions,
+// so they run on MFMA (v_mfma_f32_16x16x32_bf16, float32 accumulation):
+//   S^T (16 tokens x 16 heads) = K (tokens x dims) . Q^T (dims x heads)
+//   O^T (16 dims x 16 heads)  += V^T (dims x tokens) . P^T (tokens x heads)
+// The transposed forms put one head in each lane's accumulator column (lane % 16), so the
+// running max, sum and rescale of the online softmax are per lane, and the probabilities
+// a lane holds after the softmax are exactly the B operand of the second product: over a
+// 32-token tile, lane group g = lane / 16 holds tokens {4g + 0..3} and {16 + 4g + 0..3},
+// which become k-slots 8g .. 8g+7; V^T is stored in LDS with its tokens in that order, so
+// one 8-byte read gives the matching A operand.
+//
+// A workgroup is four waves (64 heads, 16 per wave) of one sequence over one run of tokens
+// (a split).  Per tile of 32 tokens the workgroup stages the INT8 latent rows twice in LDS,
+// row-major for the first product and transposed for the second (a 4x4 byte transpose in
+// registers), plus the bf16 RoPE rows; codes are widened to bf16 (exact) as operands are
+// read.  The wave's query stays in registers for the whole split, with the Dl/16 output
+// tiles.  Splits leave (max, sum, s * unnormalised output) in the workspace; a combine
+// kernel merges them.
+//
+// Probabilities enter the second product as two bf16 terms, p = hi + lo with hi = bf16(p)
+// and lo = bf16(p - hi), through two MFMAs that share the V operand: the weight error is
+// below 2^-17 relative instead of the 2^-9 of a single bf16 term, whose error bound
+// 2^-9 * max|v| would exceed 1e-4 of the output when the weights are spread out.
+#include <cmath>
+
+#include "fa3q_internal.hpp"
+
+namespace fa3q {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kLatThreads = 256;  // four waves, 16 heads each
+constexpr int kLatHeads = 64;     // heads per workgroup
+constexpr int kTT = 32;           // tokens per tile
+constexpr int kVRow = 40;         // bytes per transposed latent row (32 tokens + pad)
+constexpr int64_t kLatTargetGroups = 512;
+constexpr int64_t kLatMinSplit = 64;
+
+struct LatentArgs {
+  const uint16_t* q;      // (B,H,Dl+Dr) bf16
+  const int8_t* cq;       // (B,T,Dl) latent codes
+  const float* scale;     // [1]
+  const uint16_t* kr;     // (B,T,Dr) bf16
+  float* out;             // (B,H,Dl)
+  float* ws_ml;           // [B*H*nsplit][2]
+  float* ws_o;            // [B*H*nsplit][Dl]
+  int64_t T;
+  int32_t H;
+  int32_t groups;         // ceil(H / 64)
+  int32_t nsplit;
+  int32_t split_len;      // multiple of kTT
+  float sm_log2;          // sm_scale * log2(e)
+};
+
+// 8 INT8 codes (two dwords) -> 8 bf16 (exact: |code| <= 128 has at most 8 significant bits).
+__device__ __forceinline__ bf16x8 widen8(uint32_t lo, uint32_t hi) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r[i] = static_cast<__bf16>(static_cast<float>(static_cast<int8_t>(lo >> (8 * i))));
+    r[4 + i] = static_cast<__bf16>(static_cast<float>(static_cast<int8_t>(hi >> (8 * i))));
+  }
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+// 4x4 byte transpose: y[e] byte r = x[r] byte e.
+__device__ __forceinline__ void transpose4x4(const uint32_t (&x)[4], uint32_t (&y)[4]) {
+  const uint32_t a = __builtin_amdgcn_perm(x[1], x[0], 0x05010400u);  // x0.b0 x1.b0 x0.b1 x1.b1
+  const uint32_t b = __builtin_amdgcn_perm(x[1], x[0], 0x07030602u);  // x0.b2 x1.b2 x0.b3 x1.b3
+  const uint32_t c = __builtin_amdgcn_perm(x[3], x[2], 0x05010400u);
+  const uint32_t d = __builtin_amdgcn_perm(x[3], x[2], 0x07030602u);
+  y[0] = __builtin_amdgcn_perm(c, a, 0x05040100u);  // a.lo16 c.lo16
+  y[1] = __builtin_amdgcn_perm(c, a, 0x07060302u);  // a.hi16 c.hi16
+  y[2] = __builtin_amdgcn_perm(d, b, 0x05040100u);
+  y[3] = __builtin_amdgcn_perm(d, b, 0x07060302u);
+}
+
+template <int DL, int DR>
+__global__ __launch_bounds__(kLatThreads) void latent_split_kernel(LatentArgs a) {
+  constexpr int KL = DL / 32;          // k-steps of the latent part of S
+  constexpr int KR = DR / 32;          // k-steps of the RoPE part
+  constexpr int MT = DL / 16;          // 16-dim tiles of the output
+  constexpr int KROW = DL + 16;        // bytes per row-major latent row in LDS
+  constexpr int RROW = DR + 8;         // bf16 per RoPE row in LDS
+  constexpr int DC = DL / 16;          // 16-byte chunks per latent row
+  constexpr int UNITS = (kTT / 4) * DC;  // (4 tokens x 16 dims) staging units per tile
+  constexpr int RCH = kTT * DR / 8;    // 16-byte RoPE chunks per tile
+  __shared__ __align__(16) int8_t klat[kTT * KROW];
+  __shared__ __align__(16) int8_t vt[DL * kVRow];
+  __shared__ __align__(16) uint16_t krope[DR > 0 ? kTT * RROW : 8];
+
+  const int tid = static_cast<int>(threadIdx.x);
+  const int wave = tid / kWave;
+  const int lane = tid % kWave;
+  const int hl = lane & 15, lg = lane >> 4;
+
+  const int split = static_cast<int>(blockIdx.x % a.nsplit);
+  const int rest = static_cast<int>(blockIdx.x / a.nsplit);
+  const int grp = rest % a.groups;
+  const int b = rest / a.groups;
+  const int head = grp * kLatHeads + wave * 16 + hl;
+  const bool hv = head < a.H;
+  const int64_t t_begin = static_cast<int64_t>(split) * a.split_len;
+  const int64_t t_end = min(a.T, t_begin + a.split_len);
+
+  // the wave's query as B operands (Q^T: dims x heads): lane holds dims 32kk + 8lg .. +7
+  bf16x8 ql[KL];
+  bf16x8 qr[KR > 0 ? KR : 1];
+  {
+    const uint16_t* qrow = a.q + (static_cast<int64_t>(b) * a.H + (hv ? head : 0)) * (DL + DR);
+#pragma unroll
+    for (int kk = 0; kk < KL; ++kk) {
+      const uint4 u = hv ? *reinterpret_cast<const uint4*>(qrow + 32 * kk + 8 * lg) : make_uint4(0, 0, 0, 0);
+      ql[kk] = as_bf16x8(u);
+    }
+#pragma unroll
+    for (int kk = 0; kk < KR; ++kk) {
+      const uint4 u = hv ? *reinterpret_cast<const uint4*>(qrow + DL + 32 * kk + 8 * lg) : make_uint4(0, 0, 0, 0);
+      qr[kk] = as_bf16x8(u);
+    }
+  }
+  const float s = a.scale[0];
+
+  f32x4 o[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) o[mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  float m = -INFINITY, l = 0.0f;
+
+  const int8_t* cbase = a.cq + static_cast<int64_t>(b) * a.T * DL;
+  const uint16_t* rbase = a.kr + static_cast<int64_t>(b) * a.T * DR;
+
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += kTT) {
+    // ---- stage the tile: latent rows (row-major and transposed) and RoPE rows
+    __syncthreads();  // the previous tile's reads are done
+    for (int u = tid; u < UNITS; u += kLatThreads) {
+      const int tg = u / DC, dc = u - tg * DC;  // tokens 4tg..4tg+3, dims 16dc..16dc+15
+      uint4 x[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t tok = min(t0 + 4 * tg + r, t_end - 1);  // past the end: a valid row, masked later
+        x[r] = *reinterpret_cast<const uint4*>(cbase + tok * DL + 16 * dc);
+        *reinterpret_cast<uint4*>(klat + (4 * tg + r) * KROW + 16 * dc) = x[r];
+      }
+      // token offset t = 4tg + r (tg = 4*b4 + (b3 b2))  ->  position 8*(b3 b2) + 4*b4 + r
+      const int pos = 8 * (tg & 3) + 4 * (tg >> 2);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t xs[4] = {(&x[0].x)[w], (&x[1].x)[w], (&x[2].x)[w], (&x[3].x)[w]};
+        uint32_t y[4];
+        transpose4x4(xs, y);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          *reinterpret_cast<uint32_t*>(vt + (16 * dc + 4 * w + e) * kVRow + pos) = y[e];
+      }
+    }
+    if constexpr (DR > 0) {
+      for (int c = tid; c < RCH; c += kLatThreads) {
+        const int r = c / (DR / 8), k8 = c - r * (DR / 8);
+        const int64_t tok = min(t0 + r, t_end - 1);
+        *reinterpret_cast<uint4*>(krope + r * RROW + 8 * k8) =
+            *reinterpret_cast<const uint4*>(rbase + tok * DR + 8 * k8);
+      }
+    }
+    __syncthreads();
+
+    // ---- S^T = K . Q^T for tokens 16tt .. 16tt+15 (latent and RoPE parts apart)
+    f32x4 sl[2], sr[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      sl[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      sr[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kk = 0; kk < KL; ++kk) {
+        const uint2 w = *reinterpret_cast<const uint2*>(klat + (16 * tt + hl) * KROW + 32 * kk + 8 * lg);
+        sl[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen8(w.x, w.y), ql[kk], sl[tt], 0, 0, 0);
+      }
+#pragma unroll
+      for (int kk = 0; kk < KR; ++kk) {
+        const uint4 w = *reinterpret_cast<const uint4*>(krope + (16 * tt + hl) * RROW + 32 * kk + 8 * lg);
+        sr[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w), qr[kk], sr[tt], 0, 0, 0);
+      }
+    }
+
+    // ---- online softmax of the lane's head over its 8 tokens (16tt + 4lg + j)
+    float p[8];
+    float rmax = -INFINITY;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t tok = t0 + 16 * tt + 4 * lg + j;
+        const float sc = fmaf(s, sl[tt][j], sr[tt][j]) * a.sm_log2;
+        p[4 * tt + j] = tok < t_end ? sc : -INFINITY;
+        rmax = fmaxf(rmax, p[4 * tt + j]);
+      }
+    rmax = fmaxf(rmax, __shfl_xor(rmax, 16));
+    rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
+    const float m_new = fmaxf(m, rmax);  // finite: every tile holds a valid token
+    const float alpha = exp2f(m - m_new);
+    float rsum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      p[i] = exp2f(p[i] - m_new);
+      rsum += p[i];
+    }
+    rsum += __shfl_xor(rsum, 16);
+    rsum += __shfl_xor(rsum, 32);
+    l = fmaf(l, alpha, rsum);
+    m = m_new;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) o[mt] *= alpha;
+
+    // ---- O^T += V^T . P^T: k-slot 8lg + i holds token 4lg + i (i < 4) or 16 + 4lg + i - 4
+    bf16x8 phi, plo;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      phi[i] = static_cast<__bf16>(p[i]);
+      plo[i] = static_cast<__bf16>(p[i] - static_cast<float>(phi[i]));  // the difference is exact in float32
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const uint2 w = *reinterpret_cast<const uint2*>(vt + (16 * mt + hl) * kVRow + 8 * lg);
+      const bf16x8 v8 = widen8(w.x, w.y);
+      o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v8, phi, o[mt], 0, 0, 0);
+      o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v8, plo, o[mt], 0, 0, 0);
+    }
+  }
+
+  // ---- lane holds O^T[dims 16mt + 4lg + j][head]
+  if (!hv) return;
+  const int64_t row = static_cast<int64_t>(b) * a.H + head;
+  const float f = a.nsplit == 1 ? s / l : s;
+  float* dst = a.nsplit == 1 ? a.out + row * DL : a.ws_o + (row * a.nsplit + split) * DL;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+    *reinterpret_cast<float4*>(dst + 16 * mt + 4 * lg) =
+        make_float4(o[mt][0] * f, o[mt][1] * f, o[mt][2] * f, o[mt][3] * f);
+  if (a.nsplit > 1 && lg == 0) {
+    const int64_t slot = row * a.nsplit + split;
+    a.ws_ml[2 * slot] = m;
+    a.ws_ml[2 * slot + 1] = l;
+  }
+}
+
+// out = sum_s w_s o_s / sum_s w_s l_s with w_s = 2^(m_s - max m), per (b, h).
+__global__ __launch_bounds__(128) void latent_combine_kernel(LatentArgs a, int dl) {
+  const int64_t row = blockIdx.x;
+  const float* ml = a.ws_ml + 2 * row * a.nsplit;
+  float mmax = -INFINITY;
+  for (int s = 0; s < a.nsplit; ++s) mmax = fmaxf(mmax, ml[2 * s]);
+  float den = 0.0f;
+  for (int s = 0; s < a.nsplit; ++s) den += exp2f(ml[2 * s] - mmax) * ml[2 * s + 1];
+  for (int d = threadIdx.x; d < dl; d += blockDim.x) {
+    float num = 0.0f;
+    for (int s = 0; s < a.nsplit; ++s) num += exp2f(ml[2 * s] - mmax) * a.ws_o[(row * a.nsplit + s) * dl + d];
+    a.out[row * dl + d] = num / den;
+  }
+}
+
+struct LatentPlan {
+  int32_t groups, nsplit, split_len;
+};
+
+LatentPlan plan_latent(int64_t B, int64_t H, int64_t T) {
+  LatentPlan p;
+  p.groups = static_cast<int32_t>((H + kLatHeads - 1) / kLatHeads);
+  const int64_t base = B * p.groups;
+  int64_t ns = (kLatTargetGroups + base - 1) / base;
+  ns = std::max<int64_t>(1, std::min(ns, (T + kLatMinSplit - 1) / kLatMinSplit));
+  int64_t len = (T + ns - 1) / ns;
+  len = (len + kTT - 1) / kTT * kTT;
+  ns = (T + len - 1) / len;  // no empty split
+  p.nsplit = static_cast<int32_t>(ns);
+  p.split_len = static_cast<int32_t>(len);
+  return p;
+}
+
+bool latent_dims_ok(int64_t Dl, int64_t Dr) {
+  return (Dl == 128 || Dl == 256 || Dl == 512) && (Dr == 0 || Dr == 32 || Dr == 64);
+}
+
+bool latent_shape_ok(int64_t B, int64_t H, int64_t T, int64_t Dl) {
+  if (B <= 0 || H <= 0 || T <= 0) return false;
+  if (H > 65536 || B > (int64_t{1} << 24) || T > (int64_t{1} << 31)) return false;
+  if (B * ((H + kLatHeads - 1) / kLatHeads) > (int64_t{1} << 24)) return false;
+  return B <= (int64_t{1} << 62) / (T * (Dl + 128));
+}
+
+using LatentFn = void (*)(LatentArgs);
+
+template <int DL>
+LatentFn pick_dr(int64_t dr) {
+  switch (dr) {
+    case 0: return latent_split_kernel<DL, 0>;
+    case 32: return latent_split_kernel<DL, 32>;
+    default: return latent_split_kernel<DL, 64>;
+  }
+}
+
+LatentFn pick_latent(int64_t dl, int64_t dr) {
+  switch (dl) {
+    case 128: return pick_dr<128>(dr);
+    case 256: return pick_dr<256>(dr);
+    default: return pick_dr<512>(dr);
+  }
+}
+
+}  // namespace
+}  // namespace fa3q
+
+using namespace fa3q;
+
+extern "C" size_t fa3q_decode_latent_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t Dl) {
+  if (!latent_shape_ok(B, H, T, Dl) || !(Dl == 128 || Dl == 256 || Dl == 512)) return 0;
+  const LatentPlan p = plan_latent(B, H, T);
+  if (p.nsplit <= 1) return 0;
+  const size_t slots = static_cast<size_t>(B * H) * p.nsplit;
+  return round_up(slots * 2 * sizeof(float), 256) + slots * static_cast<size_t>(Dl) * sizeof(float);
+}
+
+extern "C" int fa3q_decode_latent(const uint16_t* q, const int8_t* c_q, const float* scale, const uint16_t* k_rope,
+                                  int64_t B, int64_t H, int64_t T, int64_t Dl, int64_t Dr, float sm_scale,
+                                  float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !c_q || !scale || !out || (Dr > 0 && !k_rope)) return FA3Q_ERR_NULL;
+  if (!latent_dims_ok(Dl, Dr) || !latent_shape_ok(B, H, T, Dl)) return FA3Q_ERR_SHAPE;
+  if (!std::isfinite(sm_scale)) return FA3Q_ERR_SHAPE;
+  if (!is_aligned(q, 16) || !is_aligned(c_q, 16) || !is_aligned(scale, 4) || !is_aligned(out, 16) ||
+      (Dr > 0 && !is_aligned(k_rope, 16)))
+    return FA3Q_ERR_ALIGN;
+  const LatentPlan p = plan_latent(B, H, T);
+  const size_t need = fa3q_decode_latent_workspace_bytes(B, H, T, Dl);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return FA3Q_ERR_WORKSPACE;
+    if (!is_aligned(workspace, 256)) return FA3Q_ERR_ALIGN;
+  }
+  LatentArgs a;
+  a.q = q;
+  a.cq = c_q;
+  a.scale = scale;
+  a.kr = k_rope;
+  a.out = out;
+  const size_t slots = static_cast<size_t>(B * H) * p.nsplit;
+  a.ws_ml = need ? static_cast<float*>(workspace) : nullptr;
+  a.ws_o = need ? reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) +
+                                           round_up(slots * 2 * sizeof(float), 256))
+                : nullptr;
+  a.T = T;
+  a.H = static_cast<int32_t>(H);
+  a.groups = p.groups;
+  a.nsplit = p.nsplit;
+  a.split_len = p.split_len;
+  a.sm_log2 = sm_scale * 1.4426950408889634f;
+  const int64_t grid = B * p.groups * p.nsplit;
+  hipLaunchKernelGGL(pick_latent(Dl, Dr), dim3(static_cast<unsigned>(grid)), dim3(kLatThreads), 0,
+                     as_stream(stream), a);
+  if (p.nsplit > 1)
+    hipLaunchKernelGGL(latent_combine_kernel, dim3(static_cast<unsigned>(B * H)), dim3(128), 0, as_stream(stream), a,
+                       static_cast<int>(Dl));
+  return launch_status();
+}

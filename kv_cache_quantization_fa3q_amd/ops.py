@@ -28,6 +28,8 @@ __all__ = [
     "fa3q_decode_attn_qkv8",
     "fa3q_quantize_asym",
     "fa3q_decode_attn_asym",
+    "fa3q_decode_latent_workspace_bytes",
+    "fa3q_decode_latent",
     "dtype_code",
 ]
 
@@ -325,4 +327,47 @@ def fa3q_decode_attn_asym(q: torch.Tensor, k_nope_q: torch.Tensor, scale: torch.
                                      ctypes.c_float(float(sm_scale)), _ptr(out), _ptr(workspace), wbytes,
                                      _stream(stream))
     _check(st, "fa3q_decode_attn_asym")
+    return out
+
+
+# --------------------------------------------------------------------------- shared-latent (absorbed MLA) cache
+
+
+def fa3q_decode_latent_workspace_bytes(B: int, H: int, T: int, Dl: int) -> int:
+    return int(lib().fa3q_decode_latent_workspace_bytes(B, H, T, Dl))
+
+
+def fa3q_decode_latent(q: torch.Tensor, c_q: torch.Tensor, scale: torch.Tensor, k_rope: Optional[torch.Tensor],
+                       sm_scale: float, out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                       stream=None) -> torch.Tensor:
+    """Attention of every head over one shared latent cache -> float32 ``(B,H,Dl)`` (latent space).
+
+    ``q (B,H,Dl+Dr)`` bf16 absorbed query, ``c_q (B,T,Dl)`` int8 latent codes (or ``(B,1,T,Dl)``),
+    ``scale`` float32 with one element, ``k_rope (B,T,Dr)`` bf16 (or ``(B,1,T,Dr)``) or None.
+    """
+    if c_q.dim() == 4 and c_q.shape[1] == 1:
+        c_q = c_q.view(c_q.shape[0], c_q.shape[2], c_q.shape[3])
+    if k_rope is not None and k_rope.dim() == 4 and k_rope.shape[1] == 1:
+        k_rope = k_rope.view(k_rope.shape[0], k_rope.shape[2], k_rope.shape[3])
+    if c_q.dim() != 3 or c_q.dtype != torch.int8:
+        raise ValueError("c_q must be int8 (B, T, Dl)")
+    B, T, Dl = (int(v) for v in c_q.shape)
+    Dr = int(k_rope.shape[-1]) if k_rope is not None else 0
+    if q.dim() != 3 or q.shape[0] != B or q.shape[2] != Dl + Dr or q.dtype != torch.bfloat16:
+        raise ValueError("q must be bfloat16 (B, H, Dl + Dr)")
+    H = int(q.shape[1])
+    if k_rope is not None and (tuple(k_rope.shape) != (B, T, Dr) or k_rope.dtype != torch.bfloat16):
+        raise ValueError("k_rope must be bfloat16 (B, T, Dr)")
+    if scale.numel() != 1 or scale.dtype != torch.float32:
+        raise ValueError("scale must be one float32 value")
+    if out is None:
+        out = torch.empty((B, H, Dl), dtype=torch.float32, device=q.device)
+    _need_gpu("fa3q_decode_latent", q, c_q, scale, k_rope, out)
+    nbytes = fa3q_decode_latent_workspace_bytes(B, H, T, Dl)
+    workspace = _workspace(nbytes, q.device, workspace)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().fa3q_decode_latent(_ptr(q), _ptr(c_q), _ptr(scale), _ptr(k_rope) if Dr > 0 else None, B, H, T, Dl,
+                                  Dr, ctypes.c_float(float(sm_scale)), _ptr(out), _ptr(workspace), wbytes,
+                                  _stream(stream))
+    _check(st, "fa3q_decode_latent")
     return out

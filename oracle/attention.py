@@ -153,7 +153,10 @@ def decode_attn_latent(q_bits, codes, scale, rope_bits, sm_scale: float, Dl: int
     s = float(np.float32(scale))
     c = codes.astype(np.float64) * s                                   # L1: dequantised latent
     r = bf16_bits_to_f64(np.asarray(rope_bits, dtype=np.uint16)).reshape(B, T, -1)
-    k = np.concatenate([c, r], axis=-1)                                # (B,T,Dl+Dr)
-    k = np.broadcast_to(k[:, None], (B, H, T, k.shape[-1]))            # shared by every head
-    v = np.broadcast_to(c[:, None], (B, H, T, Dl))                     # L2: value = latent
-    return attention_fp64(q, k, v, float(np.float32(sm_scale)))       # sm as the float32 callers pass
+    k = np.concatenate([c, r], axis=-1)                                # (B,T,Dl+Dr), one K for every head
+    # textbook softmax attention with that K and V = c (L2) shared by all heads of a sequence
+    scores = float(np.float32(sm_scale)) * np.einsum("bhd,btd->bht", q, k)   # sm as the float32 callers pass
+    scores = scores - scores.max(axis=-1, keepdims=True)
+    weights = np.exp(scores)
+    weights = weights / weights.sum(axis=-1, keepdims=True)
+    return np.einsum("bht,btd->bhd", weights, c)

@@ -269,6 +269,37 @@ def test_decode_asym_rejections():
     assert call(ws=None) == L.FA3Q_ERR_WORKSPACE
 
 
+@no_gpu_only
+def test_decode_latent_rejections():
+    lib = fa.lib()
+    f = lib.fa3q_decode_latent
+    ok = dict(q=_p(), c=_p(), s=_p(), kr=_p(), B=64, H=128, T=4096, Dl=512, Dr=64, sm=0.07, o=_p(), ws=_p(),
+              wsb=1 << 30)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["q"], a["c"], a["s"], a["kr"], a["B"], a["H"], a["T"], a["Dl"], a["Dr"], ctypes.c_float(a["sm"]),
+                 a["o"], a["ws"], a["wsb"], None)
+
+    for name in ("q", "c", "s", "kr", "o"):
+        assert call(**{name: None}) == L.FA3Q_ERR_NULL, name
+    assert call(kr=None, Dr=0, o=_p(4)) == L.FA3Q_ERR_ALIGN   # no RoPE part: NULL accepted, stops at `out`
+    assert call(Dl=192) == L.FA3Q_ERR_SHAPE
+    assert call(Dr=16) == L.FA3Q_ERR_SHAPE      # RoPE width a multiple of 32 (MFMA k-step)
+    assert call(T=0) == L.FA3Q_ERR_SHAPE
+    assert call(H=0) == L.FA3Q_ERR_SHAPE
+    assert call(sm=float("inf")) == L.FA3Q_ERR_SHAPE
+    assert call(q=_p(8)) == L.FA3Q_ERR_ALIGN
+    assert call(o=_p(4)) == L.FA3Q_ERR_ALIGN
+    assert call(s=_p(2)) == L.FA3Q_ERR_ALIGN
+    assert call(ws=None) == L.FA3Q_ERR_WORKSPACE
+    assert call(wsb=64) == L.FA3Q_ERR_WORKSPACE
+    assert call(ws=_p(128)) == L.FA3Q_ERR_ALIGN
+    assert lib.fa3q_decode_latent_workspace_bytes(64, 128, 4096, 512) > 0
+    assert lib.fa3q_decode_latent_workspace_bytes(64, 128, 4096, 192) == 0
+    assert lib.fa3q_decode_latent_workspace_bytes(1024, 128, 64, 512) == 0   # one split: no workspace
+
+
 def test_binding_refuses_mismatched_asym_tables():
     import torch
     k = torch.zeros((1, 2, 16, 48), dtype=torch.bfloat16)

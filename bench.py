@@ -32,6 +32,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
 METRIC = "calib Gelem/s; quantize GB/s; decode-attn KV GB/s (fraction of HBM peak)"
 
 # workload shapes
@@ -307,10 +308,11 @@ def main() -> int:
     # quantised by fa3q_quantize_k, then fa3q_decode_attn_qkv8 runs over the same K cache;
     # measured outside the step.  384 B per cached token instead of 512.
     def per_head_scale(x4):
-        mn = torch.empty(H, dtype=torch.float32, device=dev)
-        mx = torch.empty(H, dtype=torch.float32, device=dev)
-        rmin = torch.empty(H, dtype=torch.float32, device=dev)
-        rmax = torch.empty(H, dtype=torch.float32, device=dev)
+        nh = int(x4.shape[1])
+        mn = torch.empty(nh, dtype=torch.float32, device=dev)
+        mx = torch.empty(nh, dtype=torch.float32, device=dev)
+        rmin = torch.empty(nh, dtype=torch.float32, device=dev)
+        rmax = torch.empty(nh, dtype=torch.float32, device=dev)
         fa.fa3q_init_minmax(rmin, rmax, stream=stream)
         fa.fa3q_calibrate_perhead(x4, RATIO, mn, mx, stream=stream)
         fa.fa3q_accumulate_minmax(rmin, rmax, mn, mx, stream=stream)
@@ -371,6 +373,30 @@ def main() -> int:
                                 "frac_hbm": DEC_BYTES / (ad_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                                 "note": "attention over the asymmetric K-nope cache (outside the step)"}
     del akq, akr
+
+    # Shared-latent (absorbed MLA) cache, the same sequences: per token one latent row of
+    # 512 features (+ 64 RoPE) shared by all 128 heads, built by the library's own path with
+    # one head (calibration, scale, quantisation), then fa3q_decode_latent; outside the step.
+    # Both products run on MFMA: 2 * H * (Dl + Dr + Dl) flop per (b, t).
+    LAT_DL = 512
+    lat_rows = synth.activations((QB, 1, QS, LAT_DL + DR), sigma[:1], law="normal", outlier_frac=0.0005,
+                                 outlier_mult=40.0, dtype=torch.bfloat16, seed=500, device=dev)
+    lat_scale = per_head_scale(lat_rows[:, :, :, :LAT_DL].contiguous())
+    lat_c, lat_r = fa.fa3q_quantize_k(lat_rows, lat_scale, LAT_DL, stream=stream)
+    del lat_rows
+    lat_q = synth.normal_tensor((QB, H, LAT_DL + DR), dtype=torch.bfloat16, seed=510, device=dev)
+    lat_out = torch.empty((QB, H, LAT_DL), dtype=torch.float32, device=dev)
+    lat_ws_bytes = fa.fa3q_decode_latent_workspace_bytes(QB, H, QS, LAT_DL)
+    lat_ws = torch.empty(max(1, lat_ws_bytes), dtype=torch.uint8, device=dev)
+    lt_ms = timed(lambda: fa.fa3q_decode_latent(lat_q, lat_c, lat_scale, lat_r, sm, lat_out, lat_ws, stream=stream))
+    lat_flop = QB * H * QS * 2 * (2 * LAT_DL + DR)
+    lat_bytes = QB * QS * (LAT_DL + 2 * DR) + QB * H * (2 * (LAT_DL + DR) + 4 * LAT_DL)
+    breakdown["decode_latent"] = {
+        "ms": lt_ms, "tflops": lat_flop / (lt_ms * 1e-3) / 1e12,
+        "frac_mfma_bf16": lat_flop / (lt_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        "cache_gbs": lat_bytes / (lt_ms * 1e-3) / 1e9,
+        "note": "shared-latent MLA cache, B=64 H=128 T=4096 Dl=512 Dr=64, MFMA bf16 (outside the step)"}
+    del lat_c, lat_r, lat_q, lat_out, lat_ws
 
     # device-to-device copy of COPY_BYTES: a reference ceiling for read+write streaming, and the
     # known-size kernel the HBM byte counters are scaled by

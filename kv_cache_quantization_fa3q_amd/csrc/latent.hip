@@ -21,12 +21,14 @@
 // one 8-byte read gives the matching A operand.
 //
 // A workgroup is four waves (64 heads, 16 per wave) of one sequence over one run of tokens
-// (a split).  Per tile of 32 tokens the workgroup stages the INT8 latent rows twice in LDS,
-// row-major for the first product and transposed for the second (a 4x4 byte transpose in
-// registers), plus the bf16 RoPE rows; codes are widened to bf16 (exact) as operands are
-// read.  The wave's query stays in registers for the whole split, with the Dl/16 output
-// tiles.  Splits leave (max, sum, s * unnormalised output) in the workspace; a combine
-// kernel merges them.
+// (a split).  Per tile of 32 tokens the workgroup widens the INT8 latent rows to bf16
+// (exact) once and stages them twice in LDS, row-major for the first product and
+// transposed for the second (a 4x4 byte transpose in registers), plus the bf16 RoPE rows;
+// the next tile's global loads are issued before the current tile is computed.  The
+// wave's query stays in registers for the whole split, with the Dl/16 output tiles.  The
+// output is rescaled only when a head's running max grows by more than 2^8.  Splits leave
+// (max reference, sum, s * unnormalised output) in the workspace; a combine kernel merges
+// them.
 //
 // Probabilities enter the second product as two bf16 terms, p = hi + lo with hi = bf16(p)
 // and lo = bf16(p - hi), through two MFMAs that share the V operand: the weight error is
@@ -41,6 +43,8 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kLatThreads = 256;  // four waves, 16 heads each
 constexpr int kLatHeads = 64;     // heads per workgroup
@@ -65,17 +69,6 @@ struct LatentArgs {
   float sm_log2;          // sm_scale * log2(e)
 };
 
-// 8 INT8 codes (two dwords) -> 8 bf16 (exact: |code| <= 128 has at most 8 significant bits).
-__device__ __forceinline__ bf16x8 widen8(uint32_t lo, uint32_t hi) {
-  bf16x8 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    r[i] = static_cast<__bf16>(static_cast<float>(static_cast<int8_t>(lo >> (8 * i))));
-    r[4 + i] = static_cast<__bf16>(static_cast<float>(static_cast<int8_t>(hi >> (8 * i))));
-  }
-  return r;
-}
-
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
 // 4x4 byte transpose: y[e] byte r = x[r] byte e.
@@ -90,19 +83,45 @@ __device__ __forceinline__ void transpose4x4(const uint32_t (&x)[4], uint32_t (&
   y[3] = __builtin_amdgcn_perm(d, b, 0x07060302u);
 }
 
+// Staged operands of one tile: 4 tokens x 16 latent dims and one 16-byte RoPE chunk.
+struct LatentStage {
+  u32x4v x[4];
+  u32x4v r;
+};
+
+// Two bf16 (packed) from two float32 (exact here: small integers).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// 4 INT8 codes of one dword -> 4 bf16 in two dwords, element order kept.
+__device__ __forceinline__ uint2 widen4(uint32_t w) {
+  const float f0 = static_cast<float>(static_cast<int8_t>(w));
+  const float f1 = static_cast<float>(static_cast<int8_t>(w >> 8));
+  const float f2 = static_cast<float>(static_cast<int8_t>(w >> 16));
+  const float f3 = static_cast<float>(static_cast<int8_t>(w >> 24));
+  return make_uint2(pack_bf16(f0, f1), pack_bf16(f2, f3));
+}
+
 template <int DL, int DR>
 __global__ __launch_bounds__(kLatThreads) void latent_split_kernel(LatentArgs a) {
   constexpr int KL = DL / 32;          // k-steps of the latent part of S
   constexpr int KR = DR / 32;          // k-steps of the RoPE part
   constexpr int MT = DL / 16;          // 16-dim tiles of the output
-  constexpr int KROW = DL + 16;        // bytes per row-major latent row in LDS
+  constexpr int KROW = DL + 8;         // bf16 per row-major latent row in LDS
   constexpr int RROW = DR + 8;         // bf16 per RoPE row in LDS
+  constexpr int VROW = kTT + 8;        // bf16 per transposed latent row in LDS
   constexpr int DC = DL / 16;          // 16-byte chunks per latent row
   constexpr int UNITS = (kTT / 4) * DC;  // (4 tokens x 16 dims) staging units per tile
+  constexpr int UPT = (UNITS + kLatThreads - 1) / kLatThreads;  // units per thread
   constexpr int RCH = kTT * DR / 8;    // 16-byte RoPE chunks per tile
-  __shared__ __align__(16) int8_t klat[kTT * KROW];
-  __shared__ __align__(16) int8_t vt[DL * kVRow];
-  __shared__ __align__(16) uint16_t krope[DR > 0 ? kTT * RROW : 8];
+  static_assert(RCH <= kLatThreads, "one RoPE chunk per thread");
+  constexpr float kLazy = 8.0f;        // log2 headroom before the output is rescaled
+  // two buffers: the next tile is staged while this one is read
+  __shared__ __align__(16) uint16_t klat_buf[2][kTT * KROW];
+  __shared__ __align__(16) uint16_t vt_buf[2][DL * VROW];
+  __shared__ __align__(16) uint16_t krope_buf[2][DR > 0 ? kTT * RROW : 8];
 
   const int tid = static_cast<int>(threadIdx.x);
   const int wave = tid / kWave;
@@ -117,6 +136,72 @@ __global__ __launch_bounds__(kLatThreads) void latent_split_kernel(LatentArgs a)
   const bool hv = head < a.H;
   const int64_t t_begin = static_cast<int64_t>(split) * a.split_len;
   const int64_t t_end = min(a.T, t_begin + a.split_len);
+
+  const int8_t* cbase = a.cq + static_cast<int64_t>(b) * a.T * DL;
+  const uint16_t* rbase = a.kr + static_cast<int64_t>(b) * a.T * DR;
+
+  // global -> registers for tile t0 (rows past the end re-read the last row; masked later)
+  auto fetch = [&](int64_t t0, LatentStage (&st)[UPT]) {
+#pragma unroll
+    for (int k = 0; k < UPT; ++k) {
+      const int u = tid + k * kLatThreads;
+      if (u < UNITS) {
+        const int tg = u % (kTT / 4), dc = u / (kTT / 4);  // token group fastest: spreads LDS banks
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t tok = min(t0 + 4 * tg + r, t_end - 1);
+          st[k].x[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(cbase + tok * DL + 16 * dc));
+        }
+      }
+    }
+    if constexpr (DR > 0) {
+      if (tid < RCH) {
+        const int r = tid / (DR / 8), k8 = tid - r * (DR / 8);
+        const int64_t tok = min(t0 + r, t_end - 1);
+        st[0].r = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(rbase + tok * DR + 8 * k8));
+      }
+    }
+  };
+  // registers -> LDS buffer `buf`: latent rows widened to bf16, row-major and transposed; RoPE rows
+  auto stage = [&](const LatentStage (&st)[UPT], int buf) {
+    uint16_t* klat = klat_buf[buf];
+    uint16_t* vt = vt_buf[buf];
+    uint16_t* krope = krope_buf[buf];
+#pragma unroll
+    for (int k = 0; k < UPT; ++k) {
+      const int u = tid + k * kLatThreads;
+      if (u < UNITS) {
+        const int tg = u % (kTT / 4), dc = u / (kTT / 4);  // token group fastest: spreads LDS banks
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t w[4] = {st[k].x[r][0], st[k].x[r][1], st[k].x[r][2], st[k].x[r][3]};
+          uint2 h[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) h[e] = widen4(w[e]);
+          uint16_t* row = klat + (4 * tg + r) * KROW + 16 * dc;
+          *reinterpret_cast<uint4*>(row) = make_uint4(h[0].x, h[0].y, h[1].x, h[1].y);
+          *reinterpret_cast<uint4*>(row + 8) = make_uint4(h[2].x, h[2].y, h[3].x, h[3].y);
+        }
+        // token offset t = 4tg + r (tg = 4*b4 + (b3 b2))  ->  position 8*(b3 b2) + 4*b4 + r
+        const int pos = 8 * (tg & 3) + 4 * (tg >> 2);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t xs[4] = {st[k].x[0][w], st[k].x[1][w], st[k].x[2][w], st[k].x[3][w]};
+          uint32_t y[4];
+          transpose4x4(xs, y);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            *reinterpret_cast<uint2*>(vt + (16 * dc + 4 * w + e) * VROW + pos) = widen4(y[e]);
+        }
+      }
+    }
+    if constexpr (DR > 0) {
+      if (tid < RCH) {
+        const int r = tid / (DR / 8), k8 = tid - r * (DR / 8);
+        *reinterpret_cast<u32x4v*>(krope + r * RROW + 8 * k8) = st[0].r;
+      }
+    }
+  };
 
   // the wave's query as B operands (Q^T: dims x heads): lane holds dims 32kk + 8lg .. +7
   bf16x8 ql[KL];
@@ -139,93 +224,23 @@ __global__ __launch_bounds__(kLatThreads) void latent_split_kernel(LatentArgs a)
   f32x4 o[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) o[mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  float m = -INFINITY, l = 0.0f;
+  // mu: the reference the weights are taken against (p = 2^(score - mu)); it lags the
+  // running max by at most kLazy, so the output is rescaled only when the max has grown
+  // by more than that (weights stay <= 2^kLazy, far inside float32 and bf16 range)
+  float mu = -INFINITY, l = 0.0f;
 
-  const int8_t* cbase = a.cq + static_cast<int64_t>(b) * a.T * DL;
-  const uint16_t* rbase = a.kr + static_cast<int64_t>(b) * a.T * DR;
-
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += kTT) {
-    // ---- stage the tile: latent rows (row-major and transposed) and RoPE rows
-    __syncthreads();  // the previous tile's reads are done
-    for (int u = tid; u < UNITS; u += kLatThreads) {
-      const int tg = u / DC, dc = u - tg * DC;  // tokens 4tg..4tg+3, dims 16dc..16dc+15
-      uint4 x[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t tok = min(t0 + 4 * tg + r, t_end - 1);  // past the end: a valid row, masked later
-        x[r] = *reinterpret_cast<const uint4*>(cbase + tok * DL + 16 * dc);
-        *reinterpret_cast<uint4*>(klat + (4 * tg + r) * KROW + 16 * dc) = x[r];
-      }
-      // token offset t = 4tg + r (tg = 4*b4 + (b3 b2))  ->  position 8*(b3 b2) + 4*b4 + r
-      const int pos = 8 * (tg & 3) + 4 * (tg >> 2);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t xs[4] = {(&x[0].x)[w], (&x[1].x)[w], (&x[2].x)[w], (&x[3].x)[w]};
-        uint32_t y[4];
-        transpose4x4(xs, y);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          *reinterpret_cast<uint32_t*>(vt + (16 * dc + 4 * w + e) * kVRow + pos) = y[e];
-      }
-    }
-    if constexpr (DR > 0) {
-      for (int c = tid; c < RCH; c += kLatThreads) {
-        const int r = c / (DR / 8), k8 = c - r * (DR / 8);
-        const int64_t tok = min(t0 + r, t_end - 1);
-        *reinterpret_cast<uint4*>(krope + r * RROW + 8 * k8) =
-            *reinterpret_cast<const uint4*>(rbase + tok * DR + 8 * k8);
-      }
-    }
-    __syncthreads();
-
-    // ---- S^T = K . Q^T for tokens 16tt .. 16tt+15 (latent and RoPE parts apart)
-    f32x4 sl[2], sr[2];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      sl[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      sr[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int kk = 0; kk < KL; ++kk) {
-        const uint2 w = *reinterpret_cast<const uint2*>(klat + (16 * tt + hl) * KROW + 32 * kk + 8 * lg);
-        sl[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen8(w.x, w.y), ql[kk], sl[tt], 0, 0, 0);
-      }
-#pragma unroll
-      for (int kk = 0; kk < KR; ++kk) {
-        const uint4 w = *reinterpret_cast<const uint4*>(krope + (16 * tt + hl) * RROW + 32 * kk + 8 * lg);
-        sr[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w), qr[kk], sr[tt], 0, 0, 0);
-      }
-    }
-
-    // ---- online softmax of the lane's head over its 8 tokens (16tt + 4lg + j)
-    float p[8];
-    float rmax = -INFINITY;
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t tok = t0 + 16 * tt + 4 * lg + j;
-        const float sc = fmaf(s, sl[tt][j], sr[tt][j]) * a.sm_log2;
-        p[4 * tt + j] = tok < t_end ? sc : -INFINITY;
-        rmax = fmaxf(rmax, p[4 * tt + j]);
-      }
-    rmax = fmaxf(rmax, __shfl_xor(rmax, 16));
-    rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
-    const float m_new = fmaxf(m, rmax);  // finite: every tile holds a valid token
-    const float alpha = exp2f(m - m_new);
+  // ---- softmax weights of one tile against mu, then O^T += V^T . P^T
+  // (k-slot 8lg + i holds token 4lg + i for i < 4, 16 + 4lg + i - 4 otherwise)
+  auto accumulate = [&](float (&p)[8], const uint16_t* vt) {
     float rsum = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      p[i] = exp2f(p[i] - m_new);
+      p[i] = exp2f(p[i] - mu);
       rsum += p[i];
     }
     rsum += __shfl_xor(rsum, 16);
     rsum += __shfl_xor(rsum, 32);
-    l = fmaf(l, alpha, rsum);
-    m = m_new;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) o[mt] *= alpha;
-
-    // ---- O^T += V^T . P^T: k-slot 8lg + i holds token 4lg + i (i < 4) or 16 + 4lg + i - 4
+    l += rsum;
     bf16x8 phi, plo;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -234,11 +249,81 @@ __global__ __launch_bounds__(kLatThreads) void latent_split_kernel(LatentArgs a)
     }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const uint2 w = *reinterpret_cast<const uint2*>(vt + (16 * mt + hl) * kVRow + 8 * lg);
-      const bf16x8 v8 = widen8(w.x, w.y);
-      o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v8, phi, o[mt], 0, 0, 0);
-      o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v8, plo, o[mt], 0, 0, 0);
+      const uint4 w = *reinterpret_cast<const uint4*>(vt + (16 * mt + hl) * VROW + 8 * lg);
+      o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w), phi, o[mt], 0, 0, 0);
+      o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w), plo, o[mt], 0, 0, 0);
     }
+  };
+
+  LatentStage st[UPT];
+  fetch(t_begin, st);
+  stage(st, 0);
+  if (t_begin + kTT < t_end) fetch(t_begin + kTT, st);
+  __syncthreads();
+  int64_t t0 = t_begin;
+  int buf = 0;
+  float p[8];
+  float rmax = -INFINITY;
+  // The tile loop leaves early when a head's max outgrows mu + kLazy (the first tile, then
+  // rarely): the output is rescaled outside it, so the hot loop holds no operation on the
+  // accumulators other than the MFMAs.  Each pass computes tile t0 from buffer `buf` while
+  // tile t0 + 32 (already in registers) is staged into the other buffer and tile t0 + 64 is
+  // fetched; one barrier per tile.
+  for (;;) {
+    for (; t0 < t_end; t0 += kTT, buf ^= 1) {
+      const uint16_t* klat = klat_buf[buf];
+      const uint16_t* krope = krope_buf[buf];
+      // ---- S^T = K . Q^T for tokens 16tt .. 16tt+15 (latent and RoPE parts apart)
+      f32x4 sl[2], sr[2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        sl[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        sr[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kk = 0; kk < KL; ++kk) {
+          const uint4 w = *reinterpret_cast<const uint4*>(klat + (16 * tt + hl) * KROW + 32 * kk + 8 * lg);
+          sl[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w), ql[kk], sl[tt], 0, 0, 0);
+        }
+#pragma unroll
+        for (int kk = 0; kk < KR; ++kk) {
+          const uint4 w = *reinterpret_cast<const uint4*>(krope + (16 * tt + hl) * RROW + 32 * kk + 8 * lg);
+          sr[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w), qr[kk], sr[tt], 0, 0, 0);
+        }
+      }
+      // the other buffer was last read before the previous barrier
+      if (t0 + kTT < t_end) stage(st, buf ^ 1);
+      if (t0 + 2 * kTT < t_end) fetch(t0 + 2 * kTT, st);
+      // ---- scores (log2 domain) of the lane's head over its 8 tokens (16tt + 4lg + j)
+      rmax = -INFINITY;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t tok = t0 + 16 * tt + 4 * lg + j;
+          const float sc = fmaf(s, sl[tt][j], sr[tt][j]) * a.sm_log2;
+          p[4 * tt + j] = tok < t_end ? sc : -INFINITY;
+          rmax = fmaxf(rmax, p[4 * tt + j]);
+        }
+      rmax = fmaxf(rmax, __shfl_xor(rmax, 16));
+      rmax = fmaxf(rmax, __shfl_xor(rmax, 32));  // finite: every tile holds a valid token
+      if (__builtin_amdgcn_ballot_w64(rmax > mu + kLazy) != 0) break;
+      accumulate(p, vt_buf[buf]);
+      __syncthreads();
+    }
+    if (t0 >= t_end) break;
+    // rescale to the new reference, then finish the tile the loop left; a lane moves its
+    // reference only when its own max outgrew it (alpha is then exactly 1 elsewhere), so a
+    // head's arithmetic does not depend on the other heads of its wave
+    const float mu_new = rmax > mu + kLazy ? rmax : mu;
+    const float alpha = exp2f(mu - mu_new);
+    l *= alpha;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) o[mt] *= alpha;
+    mu = mu_new;
+    accumulate(p, vt_buf[buf]);
+    __syncthreads();
+    t0 += kTT;
+    buf ^= 1;
   }
 
   // ---- lane holds O^T[dims 16mt + 4lg + j][head]
@@ -252,7 +337,7 @@ __global__ __launch_bounds__(kLatThreads) void latent_split_kernel(LatentArgs a)
         make_float4(o[mt][0] * f, o[mt][1] * f, o[mt][2] * f, o[mt][3] * f);
   if (a.nsplit > 1 && lg == 0) {
     const int64_t slot = row * a.nsplit + split;
-    a.ws_ml[2 * slot] = m;
+    a.ws_ml[2 * slot] = mu;
     a.ws_ml[2 * slot + 1] = l;
   }
 }

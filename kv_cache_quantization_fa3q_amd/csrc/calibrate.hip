@@ -29,6 +29,17 @@
 //                        whose lists fit in registers take calib_merge_wave_kernel
 //                        instead: one wave per side, no LDS select.
 //
+// Estimated bounds.  A group-minimum bound is certain but loose: with a sampled fraction f
+// of the head it lets about K/f values per side through.  When K is large against the
+// sample (no certain bound at all once K exceeds the number of groups) the sample instead
+// gives the r-th smallest group minimum with r = 2e + 4 sqrt(e) + 8, e = K f the expected
+// number of sampled keys among the head's K smallest: about r/f values pass, a few times K.
+// Such a bound is checked, exactly, by the merge: it holds at least K head values iff the
+// chunk lists together hold at least K keys (a chunk that cut its buffer held K by
+// itself; otherwise every value within the bound was kept).  A head that fails is flagged
+// and redone by a second chunk pass and merge that use no bound (their workgroups exit at
+// once for every head that passed).
+//
 // Why the union of the chunk lists holds the head's K smallest values: a value v at or
 // below the head's K-th smallest value is never dropped.  The head bound has at least K
 // head values at or below it, so v is within it; a chunk's own K-th smallest value is at
@@ -48,6 +59,8 @@
 // Only 16-byte vectors holding a candidate are copied to a per-wave LDS stage, from
 // which the wave appends the qualifying keys; a round appends at most 64 vectors per
 // wave, so the buffers need room for one round, not for a whole tile.
+#include <cmath>
+
 #include "fa3q_internal.hpp"
 
 namespace fa3q {
@@ -402,6 +415,7 @@ struct ChunkArgs {
   int32_t cps;        // chunks per slab
   int32_t nch;        // chunks per head = B*cps
   const uint32_t* bounds;  // [2][H] sampled bound keys per head (lo side, then hi side)
+  const uint32_t* fail;    // fix-up pass: [H] heads to redo with no bound (nullptr: the first pass)
   uint32_t K;
   uint32_t cap;
 };
@@ -615,6 +629,11 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
   // within them: the chunk keeps every key up to and including the bounds (it may hold
   // fewer than K such keys), then its own K-th extreme key once it holds K.
   Lim lo_lim = static_cast<Lim>(a.bounds[h]) + 1, hi_lim = static_cast<Lim>(a.bounds[a.H + h]) - 1;
+  if (a.fail != nullptr) {  // fix-up pass: only flagged heads, and every key is a candidate
+    if (a.fail[h] == 0) return;  // uniform over the workgroup
+    lo_lim = kKeyMax + 1;
+    hi_lim = -1;
+  }
   if (begin < end) load_tile(begin);
   for (int64_t t0 = begin; t0 < end; t0 += kTile) {
     bool vv[kVec];
@@ -707,6 +726,8 @@ struct MergeArgs {
   const void* lists;
   float* win_min;
   float* win_max;
+  uint32_t* fail;  // [H] with an estimated bound: written by the check pass, read by the fix-up
+  int32_t fixup;   // 0: check pass (verifies the bound when fail != nullptr), 1: fix-up pass
   int32_t H;
   int32_t nch;
   uint32_t K;
@@ -733,11 +754,15 @@ __global__ __launch_bounds__(kMergeThreads) void calib_merge_kernel(MergeArgs a)
 
   const int h = static_cast<int>(blockIdx.x);
   const int tid = static_cast<int>(threadIdx.x);
+  if (a.fixup && a.fail[h] == 0) return;  // uniform over the workgroup
+  const bool check = !a.fixup && a.fail != nullptr;
   const int64_t per_head = static_cast<int64_t>(a.nch) * a.K;
   const KeyT* src_lo = static_cast<const KeyT*>(a.lists) + h * per_head;
   const KeyT* src_hi = static_cast<const KeyT*>(a.lists) + (static_cast<int64_t>(a.H) + h) * per_head;
 
-  // Stream the head's chunk tails (one flat array per side) through the same filter.
+  // Stream the head's chunk tails (one flat array per side) through the same filter,
+  // counting the keys the lists hold (their unused slots hold keys no filter passes).
+  uint32_t held_lo = 0, held_hi = 0;
   for (int64_t t0 = 0; t0 < per_head; t0 += kMergeTile) {
     uint32_t klo[kMergePerThread], khi[kMergePerThread];
     bool ev[kMergePerThread];
@@ -747,12 +772,30 @@ __global__ __launch_bounds__(kMergeThreads) void calib_merge_kernel(MergeArgs a)
       ev[e] = i < per_head;
       klo[e] = ev[e] ? static_cast<uint32_t>(src_lo[i]) : KeyInfo<KeyT>::kMax;
       khi[e] = ev[e] ? static_cast<uint32_t>(src_hi[i]) : 0u;
+      held_lo += klo[e] != KeyInfo<KeyT>::kMax ? 1u : 0u;
+      held_hi += khi[e] != 0u ? 1u : 0u;
     }
 #pragma unroll
     for (int e = 0; e < kMergePerThread; ++e) st.append_lo(klo[e] < st.thr_lo, klo[e]);
 #pragma unroll
     for (int e = 0; e < kMergePerThread; ++e) st.append_hi(khi[e] > st.thr_hi, khi[e]);
     st.end_round();
+  }
+  if (check) {
+    // the estimated bound holds iff the lists hold at least K keys per side
+    uint32_t* cnt = ctl + kWaveScratch;
+    if (tid < 2) cnt[tid] = 0;
+    lds_barrier();
+    held_lo = wave_sum(held_lo);
+    held_hi = wave_sum(held_hi);
+    if (lane_id() == 0) {
+      atomicAdd(&cnt[0], held_lo);
+      atomicAdd(&cnt[1], held_hi);
+    }
+    lds_barrier();
+    const bool ok = cnt[0] >= a.K && cnt[1] >= a.K;
+    if (tid == 0) a.fail[h] = ok ? 0u : 1u;
+    if (!ok) return;  // uniform: the fix-up pass redoes this head
   }
   st.finish();  // now exactly K per side (every head holds at least K values)
 
@@ -845,12 +888,27 @@ __global__ __launch_bounds__(kWaveMergeThreads) void calib_merge_wave_kernel(Mer
   const KeyT* src = static_cast<const KeyT*>(a.lists) +
                     (static_cast<int64_t>(side) * a.H + h) * static_cast<int64_t>(n);
   const uint32_t flip = side == 0 ? 0u : kMax;  // hi side: complemented keys
+  if (a.fixup && a.fail[h] == 0) return;  // uniform over the workgroup
 
   uint32_t k[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const uint32_t i = static_cast<uint32_t>(r) * kWave + lane;
     k[r] = i < n ? (static_cast<uint32_t>(src[i]) ^ flip) : kMax;
+  }
+  if (!a.fixup && a.fail != nullptr) {
+    // the estimated bound holds iff the lists hold at least K keys per side (unused
+    // slots hold kMax after the complement)
+    uint32_t c = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) c += k[r] != kMax ? 1u : 0u;
+    c = wave_sum(c);
+    if (lane == 0) best_at[side] = c;
+    __syncthreads();
+    const bool ok = best_at[0] >= K && best_at[1] >= K;
+    __syncthreads();  // both waves have read best_at before it is reused
+    if (tid == 0) a.fail[h] = ok ? 0u : 1u;
+    if (!ok) return;  // uniform: the fix-up pass redoes this head
   }
   // least t with #{k <= t} >= K (entries past n hold kMax and never change that answer,
   // since the n list entries already reach K at kMax)
@@ -963,7 +1021,9 @@ struct CalibPlan {
   size_t key_bytes = 0;
   int wave_merge_e = 0;  // > 0: the two-wave merge with this many sorted keys per lane
   int wave_merge_r = 0;  // and this many union keys per lane
-  size_t lists_bytes = 0, bounds_bytes = 0, total_bytes = 0;
+  uint32_t rank = 0;     // rank of the sampled group minimum used as the bound
+  bool estimate = false; // rank < K: the bound is checked by the merge, failures redone
+  size_t lists_bytes = 0, bounds_bytes = 0, fail_bytes = 0, total_bytes = 0;
 };
 
 int64_t next_pow2(int64_t v) {
@@ -1026,7 +1086,8 @@ int make_plan(int dtype, int64_t B, int64_t H, int64_t S, int64_t D, double rati
   const size_t lists = static_cast<size_t>(H) * p.nch;
   p.lists_bytes = round_up(2 * lists * static_cast<size_t>(p.K) * p.key_bytes, 256);
   p.bounds_bytes = round_up(2 * static_cast<size_t>(H) * sizeof(uint32_t), 256);
-  p.total_bytes = p.lists_bytes + p.bounds_bytes;
+  p.fail_bytes = round_up(static_cast<size_t>(H) * sizeof(uint32_t), 256);
+  p.total_bytes = p.lists_bytes + p.bounds_bytes + p.fail_bytes;
 
   // Sample runs: evenly spaced over the head's B*L/vec vectors, or back to back (covering
   // the whole head) when it has fewer than kSampleRuns runs' worth.
@@ -1048,6 +1109,19 @@ int make_plan(int dtype, int64_t B, int64_t H, int64_t S, int64_t D, double rati
     m += most;
   }
   p.sample_m = static_cast<uint32_t>(m);
+
+  // Rank of the bound: K gives a certain bound (while the sample has K groups); the
+  // estimate r = 2e + 4 sqrt(e) + 8 (e: expected sampled keys among the head's K extremes)
+  // is used, with the merge's check, when it is far tighter or the only bound there is.
+  int64_t sampled = 0;
+  for (int j = 0; j < kSampleRuns; ++j) sampled += p.sample_n[j];
+  sampled *= vec;
+  const double e = static_cast<double>(p.K) * static_cast<double>(sampled) / static_cast<double>(p.N);
+  const double r = std::ceil(2.0 * e + 4.0 * std::sqrt(e) + 8.0);
+  const int64_t r_est = r < static_cast<double>(p.K) ? static_cast<int64_t>(r) : p.K;
+  p.estimate = r_est < p.K && r_est <= static_cast<int64_t>(p.sample_m) &&
+               (8 * r_est <= p.K || static_cast<int64_t>(p.sample_m) < p.K);
+  p.rank = static_cast<uint32_t>(p.estimate ? r_est : p.K);
   return FA3Q_OK;
 }
 
@@ -1084,7 +1158,7 @@ int launch(const void* x, int64_t H, const CalibPlan& p, float* win_min, float* 
   }
   sa.H = static_cast<int32_t>(H);
   sa.M = p.sample_m;
-  sa.K = static_cast<uint32_t>(p.K);
+  sa.K = p.rank;
   if (sa.Lv >= kSampleThreads)
     hipLaunchKernelGGL((calib_sample_kernel<InT, false>), dim3(static_cast<unsigned>(H)), dim3(kSampleThreads), 0, stream, sa);
   else
@@ -1094,6 +1168,7 @@ int launch(const void* x, int64_t H, const CalibPlan& p, float* win_min, float* 
   ca.x = x;
   ca.lists = workspace;
   ca.bounds = bounds;
+  ca.fail = nullptr;
   ca.L = p.L;
   ca.CL = p.CL;
   ca.H = static_cast<int32_t>(H);
@@ -1103,22 +1178,38 @@ int launch(const void* x, int64_t H, const CalibPlan& p, float* win_min, float* 
   ca.cap = p.cap_chunk;
   hipLaunchKernelGGL(calib_chunk_kernel<InT>, dim3(static_cast<unsigned>(H * p.nch)), dim3(kChunkThreads),
                      p.lds_chunk, stream, ca);
+  uint32_t* fail = reinterpret_cast<uint32_t*>(static_cast<unsigned char*>(workspace) + p.lists_bytes + p.bounds_bytes);
   MergeArgs ma;
   ma.lists = workspace;
   ma.win_min = win_min;
   ma.win_max = win_max;
+  ma.fail = p.estimate ? fail : nullptr;
+  ma.fixup = 0;
   ma.H = static_cast<int32_t>(H);
   ma.nch = p.nch;
   ma.K = static_cast<uint32_t>(p.K);
   ma.cap = p.cap_merge;
   ma.P = p.P;
-  if (p.wave_merge_e > 0 && p.wave_merge_r == 32)
-    launch_wave_merge<KeyT, 32>(p.wave_merge_e, H, ma, stream);
-  else if (p.wave_merge_e > 0)
-    launch_wave_merge<KeyT, 64>(p.wave_merge_e, H, ma, stream);
-  else
-    hipLaunchKernelGGL(calib_merge_kernel<KeyT>, dim3(static_cast<unsigned>(H)), dim3(kMergeThreads),
-                       p.lds_merge, stream, ma);
+  auto merge = [&](const MergeArgs& m) {
+    if (p.wave_merge_e > 0 && p.wave_merge_r == 32)
+      launch_wave_merge<KeyT, 32>(p.wave_merge_e, H, m, stream);
+    else if (p.wave_merge_e > 0)
+      launch_wave_merge<KeyT, 64>(p.wave_merge_e, H, m, stream);
+    else
+      hipLaunchKernelGGL(calib_merge_kernel<KeyT>, dim3(static_cast<unsigned>(H)), dim3(kMergeThreads),
+                         p.lds_merge, stream, m);
+  };
+  merge(ma);
+  if (p.estimate) {
+    // heads whose estimated bound held fewer than K values: again with no bound
+    ChunkArgs cf = ca;
+    cf.fail = fail;
+    hipLaunchKernelGGL(calib_chunk_kernel<InT>, dim3(static_cast<unsigned>(H * p.nch)), dim3(kChunkThreads),
+                       p.lds_chunk, stream, cf);
+    MergeArgs mf = ma;
+    mf.fixup = 1;
+    merge(mf);
+  }
   return launch_status();
 }
 

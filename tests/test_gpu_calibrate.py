@@ -154,3 +154,36 @@ def test_large_k_uses_more_than_64k_lds(fa):
     log(f"device LDS per block: {torch.cuda.get_device_properties(0)}")
     _check(fa, x.to(torch.bfloat16), (0.98,), "large_k_bf16")   # K = 10486
     _check(fa, x[:, :, :64], (0.5,), "large_k_f32")               # N = 8192, K = 4097
+
+
+def test_estimated_bound_that_fails_is_redone_exactly(fa):
+    # K = 10487 against 2048 sampled groups: the head bound is an estimate, checked by the
+    # merge.  Values placed where the evenly spaced sample reads (runs of 256 vectors every
+    # Q/32 vectors; a group is a thread's vectors of four consecutive runs) give every group
+    # an extreme, so the sample bounds tightly while the head holds only 2048 values beyond
+    # the bound: the check fails and the head is redone without a bound.
+    B, H, S, D = 1, 2, 8192, 128
+    vec = 8                                   # bf16 values per 16-byte vector
+    q_vecs = B * S * D // vec                 # vectors per head
+    stride = max(256, q_vecs // 32)
+    rng = np.random.default_rng(23)
+    x = np.ones((B, H, S * D), np.float32)
+    x[0, 1] = rng.standard_normal(S * D).astype(np.float32)
+    for g in range(8):
+        lo_run, hi_run = 4 * g, 4 * g + 1
+        for t in range(256):
+            x[0, 0, (lo_run * stride + t) * vec] = -7.0        # head 0: both sides fail
+            x[0, 0, (hi_run * stride + t) * vec] = 9.0
+            x[0, 1, (lo_run * stride + t) * vec + 3] = -50.0   # head 1: the low side fails
+    xt = torch.from_numpy(x.reshape(B, H, S, D)).to(torch.bfloat16)
+    _check(fa, xt, (0.99,), "estimate_fails")
+    _check(fa, xt, (0.999, 0.9999), "estimate_fails_other_ratios")
+    # the per-head check flags (the workspace's last 256-byte block) show that both heads
+    # failed the check and took the second pass
+    dev = torch.device("cuda:0")
+    nbytes = fa.fa3q_calibrate_workspace_bytes(torch.bfloat16, B, H, S, D, 0.99)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+    fa.fa3q_calibrate_perhead(xt.to(dev), 0.99, workspace=ws)
+    torch.cuda.synchronize()
+    flags = ws[nbytes - 256:nbytes - 256 + 4 * H].cpu().view(torch.int32).numpy()
+    assert flags.tolist() == [1, 1], flags

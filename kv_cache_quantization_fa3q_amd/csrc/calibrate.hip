@@ -735,6 +735,90 @@ struct MergeArgs {
   uint32_t P;  // next power of two >= K
 };
 
+// Ascending bitonic sort of lo[0..P) and hi[0..P) together, P = kMergeThreads * E.
+// Thread t holds elements t*E .. t*E+E-1 of each array in registers: compare-exchange
+// distances below E stay in registers, distances below 64*E go through lane shuffles, and
+// only the wider ones through LDS (one barrier each) -- 10 barriers instead of 91 for
+// P = 8192.
+template <typename KeyT, int E>
+__device__ void bitonic_sort2(KeyT* lo, KeyT* hi, int tid) {
+  constexpr int NT = kMergeThreads;
+  constexpr uint32_t P = static_cast<uint32_t>(NT) * E;
+  constexpr uint32_t kWide = static_cast<uint32_t>(kWave) * E;  // distances from here on cross waves
+  uint32_t a[E], b[E];
+  const uint32_t base = static_cast<uint32_t>(tid) * E;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    a[e] = lo[base + e];
+    b[e] = hi[base + e];
+  }
+#pragma unroll
+  for (uint32_t k = 2; k <= P; k <<= 1) {
+    uint32_t j = k >> 1;
+    if (j >= kWide) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        lo[base + e] = static_cast<KeyT>(a[e]);
+        hi[base + e] = static_cast<KeyT>(b[e]);
+      }
+      lds_barrier();
+      for (; j >= kWide; j >>= 1) {
+        for (uint32_t i = static_cast<uint32_t>(tid); i < P / 2; i += NT) {
+          const uint32_t l = ((i & ~(j - 1)) << 1) | (i & (j - 1));
+          const uint32_t r = l + j;
+          const bool up = (l & k) == 0;
+          const KeyT a0 = lo[l], a1 = lo[r];
+          if ((a0 > a1) == up) { lo[l] = a1; lo[r] = a0; }
+          const KeyT b0 = hi[l], b1 = hi[r];
+          if ((b0 > b1) == up) { hi[l] = b1; hi[r] = b0; }
+        }
+        lds_barrier();
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) {  // each thread reads back only its own elements
+        a[e] = lo[base + e];
+        b[e] = hi[base + e];
+      }
+    }
+#pragma unroll
+    for (; j >= static_cast<uint32_t>(E); j >>= 1) {
+      const int lm = static_cast<int>(j / E);  // partner lane = lane ^ lm
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const uint32_t oa = static_cast<uint32_t>(__shfl_xor(static_cast<int>(a[e]), lm));
+        const uint32_t ob = static_cast<uint32_t>(__shfl_xor(static_cast<int>(b[e]), lm));
+        const uint32_t i = base + e;
+        const bool keep_min = ((i & k) == 0) == ((i & j) == 0);
+        a[e] = keep_min ? min(a[e], oa) : max(a[e], oa);
+        b[e] = keep_min ? min(b[e], ob) : max(b[e], ob);
+      }
+    }
+#pragma unroll
+    for (; j > 0; j >>= 1) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        if ((e & j) == 0) {
+          const bool up = ((base + e) & k) == 0;
+          const uint32_t x0 = a[e], x1 = a[e ^ j];
+          const bool sa = (x0 > x1) == up;
+          a[e] = sa ? x1 : x0;
+          a[e ^ j] = sa ? x0 : x1;
+          const uint32_t y0 = b[e], y1 = b[e ^ j];
+          const bool sb = (y0 > y1) == up;
+          b[e] = sb ? y1 : y0;
+          b[e ^ j] = sb ? y0 : y1;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    lo[base + e] = static_cast<KeyT>(a[e]);
+    hi[base + e] = static_cast<KeyT>(b[e]);
+  }
+  lds_barrier();
+}
+
 template <typename KeyT>
 __global__ __launch_bounds__(kMergeThreads) void calib_merge_kernel(MergeArgs a) {
   constexpr int NT = kMergeThreads;
@@ -806,19 +890,27 @@ __global__ __launch_bounds__(kMergeThreads) void calib_merge_kernel(MergeArgs a)
     st.hi[i] = static_cast<KeyT>(KeyInfo<KeyT>::kMax);
   }
   lds_barrier();
-  for (uint32_t k = 2; k <= P; k <<= 1) {
-    for (uint32_t j = k >> 1; j > 0; j >>= 1) {
-      for (uint32_t i = tid; i < P / 2; i += NT) {
-        const uint32_t l = ((i & ~(j - 1)) << 1) | (i & (j - 1));
-        const uint32_t r = l + j;
-        const bool up = (l & k) == 0;
-        const KeyT a0 = st.lo[l], a1 = st.lo[r];
-        if ((a0 > a1) == up) { st.lo[l] = a1; st.lo[r] = a0; }
-        const KeyT b0 = st.hi[l], b1 = st.hi[r];
-        if ((b0 > b1) == up) { st.hi[l] = b1; st.hi[r] = b0; }
+  switch (P / NT) {  // P >= NT: registers, shuffles and LDS; smaller: all in LDS
+    case 1: bitonic_sort2<KeyT, 1>(st.lo, st.hi, tid); break;
+    case 2: bitonic_sort2<KeyT, 2>(st.lo, st.hi, tid); break;
+    case 4: bitonic_sort2<KeyT, 4>(st.lo, st.hi, tid); break;
+    case 8: bitonic_sort2<KeyT, 8>(st.lo, st.hi, tid); break;
+    case 16: bitonic_sort2<KeyT, 16>(st.lo, st.hi, tid); break;
+    default:
+      for (uint32_t k = 2; k <= P; k <<= 1) {
+        for (uint32_t j = k >> 1; j > 0; j >>= 1) {
+          for (uint32_t i = tid; i < P / 2; i += NT) {
+            const uint32_t l = ((i & ~(j - 1)) << 1) | (i & (j - 1));
+            const uint32_t r = l + j;
+            const bool up = (l & k) == 0;
+            const KeyT a0 = st.lo[l], a1 = st.lo[r];
+            if ((a0 > a1) == up) { st.lo[l] = a1; st.lo[r] = a0; }
+            const KeyT b0 = st.hi[l], b1 = st.hi[r];
+            if ((b0 > b1) == up) { st.hi[l] = b1; st.hi[r] = b0; }
+          }
+          lds_barrier();
+        }
       }
-      lds_barrier();
-    }
   }
 
   // Shortest window U[i] - L[i] (float32), smallest i on ties.
@@ -1050,11 +1142,53 @@ int make_plan(int dtype, int64_t B, int64_t H, int64_t S, int64_t D, double rati
   p.K = p.N - p.t + 1;
   if (p.K > fa3q_calibrate_max_windows(dtype)) return FA3Q_ERR_UNSUPPORTED;
 
+  // Sample runs: evenly spaced over the head's B*L/vec vectors, or back to back (covering
+  // the whole head) when it has fewer than kSampleRuns runs' worth.
+  const int64_t Lv = p.L / vec, Q = B * Lv;
+  const int64_t stride = std::max<int64_t>(kSampleThreads, Q / kSampleRuns);
+  int64_t m = 0;
+  for (int j = 0; j < kSampleRuns; ++j) {
+    const int64_t q0 = j * stride;
+    p.sample_n[j] = static_cast<uint32_t>(std::min<int64_t>(kSampleThreads, std::max<int64_t>(0, Q - q0)));
+    const int64_t b = p.sample_n[j] ? q0 / Lv : 0, w = p.sample_n[j] ? q0 - b * Lv : 0;
+    p.sample_off[j] = (b * H * Lv + w) * vec;
+    p.sample_w[j] = static_cast<uint32_t>(w);
+  }
+  // a thread's group holds a vector inside the head when its lane is below the largest
+  // run length among the group's runs
+  for (int g = 0; g < kSampleGroups; ++g) {
+    uint32_t most = 0;
+    for (int q = 0; q < kSampleGroupRuns; ++q) most = std::max(most, p.sample_n[g * kSampleGroupRuns + q]);
+    m += most;
+  }
+  p.sample_m = static_cast<uint32_t>(m);
+
+  // Rank of the bound: K gives a certain bound (while the sample has K groups); the
+  // estimate r = 2e + 4 sqrt(e) + 8 (e: expected sampled keys among the head's K extremes)
+  // is used, with the merge's check, when it is far tighter or the only bound there is.
+  int64_t sampled = 0;
+  for (int j = 0; j < kSampleRuns; ++j) sampled += p.sample_n[j];
+  sampled *= vec;
+  const double e = static_cast<double>(p.K) * static_cast<double>(sampled) / static_cast<double>(p.N);
+  const double r = std::ceil(2.0 * e + 4.0 * std::sqrt(e) + 8.0);
+  const int64_t r_est = r < static_cast<double>(p.K) ? static_cast<int64_t>(r) : p.K;
+  p.estimate = r_est < p.K && r_est <= static_cast<int64_t>(p.sample_m) &&
+               (8 * r_est <= p.K || static_cast<int64_t>(p.sample_m) < p.K);
+  p.rank = static_cast<uint32_t>(p.estimate ? r_est : p.K);
+
   p.key_bytes = dtype == FA3Q_BF16 ? 2 : 4;
   const int64_t tile = dtype == FA3Q_BF16 ? chunk_tile<uint16_t>() : chunk_tile<uint32_t>();
   const int64_t room = dtype == FA3Q_BF16 ? chunk_room<uint16_t>() : chunk_room<uint32_t>();
   const size_t tmp_keys = static_cast<size_t>(p.K);
   p.cap_chunk = static_cast<uint32_t>(2 * p.K + room);
+  if (p.estimate) {
+    // candidates are sparse under an estimated bound: a buffer that still leaves room to
+    // cut (at least K + one round) but lets kChunkGroupsPerCU workgroups share a CU
+    const int64_t fit = (static_cast<int64_t>(kLdsLimit / kChunkGroupsPerCU) - static_cast<int64_t>(kCtlBytes + kStageBytes)) /
+                            static_cast<int64_t>(p.key_bytes) - p.K;
+    const int64_t cap = std::min<int64_t>(2 * p.K + room, fit / 2);
+    if (cap >= p.K + room + 64) p.cap_chunk = static_cast<uint32_t>(cap);
+  }
   p.cap_merge = static_cast<uint32_t>(2 * p.K + kMergeTile);
   p.P = static_cast<uint32_t>(next_pow2(p.K));
   p.lds_chunk = kCtlBytes + kStageBytes + (2 * static_cast<size_t>(p.cap_chunk) + tmp_keys) * p.key_bytes;
@@ -1089,39 +1223,6 @@ int make_plan(int dtype, int64_t B, int64_t H, int64_t S, int64_t D, double rati
   p.fail_bytes = round_up(static_cast<size_t>(H) * sizeof(uint32_t), 256);
   p.total_bytes = p.lists_bytes + p.bounds_bytes + p.fail_bytes;
 
-  // Sample runs: evenly spaced over the head's B*L/vec vectors, or back to back (covering
-  // the whole head) when it has fewer than kSampleRuns runs' worth.
-  const int64_t Lv = p.L / vec, Q = B * Lv;
-  const int64_t stride = std::max<int64_t>(kSampleThreads, Q / kSampleRuns);
-  int64_t m = 0;
-  for (int j = 0; j < kSampleRuns; ++j) {
-    const int64_t q0 = j * stride;
-    p.sample_n[j] = static_cast<uint32_t>(std::min<int64_t>(kSampleThreads, std::max<int64_t>(0, Q - q0)));
-    const int64_t b = p.sample_n[j] ? q0 / Lv : 0, w = p.sample_n[j] ? q0 - b * Lv : 0;
-    p.sample_off[j] = (b * H * Lv + w) * vec;
-    p.sample_w[j] = static_cast<uint32_t>(w);
-  }
-  // a thread's group holds a vector inside the head when its lane is below the largest
-  // run length among the group's runs
-  for (int g = 0; g < kSampleGroups; ++g) {
-    uint32_t most = 0;
-    for (int q = 0; q < kSampleGroupRuns; ++q) most = std::max(most, p.sample_n[g * kSampleGroupRuns + q]);
-    m += most;
-  }
-  p.sample_m = static_cast<uint32_t>(m);
-
-  // Rank of the bound: K gives a certain bound (while the sample has K groups); the
-  // estimate r = 2e + 4 sqrt(e) + 8 (e: expected sampled keys among the head's K extremes)
-  // is used, with the merge's check, when it is far tighter or the only bound there is.
-  int64_t sampled = 0;
-  for (int j = 0; j < kSampleRuns; ++j) sampled += p.sample_n[j];
-  sampled *= vec;
-  const double e = static_cast<double>(p.K) * static_cast<double>(sampled) / static_cast<double>(p.N);
-  const double r = std::ceil(2.0 * e + 4.0 * std::sqrt(e) + 8.0);
-  const int64_t r_est = r < static_cast<double>(p.K) ? static_cast<int64_t>(r) : p.K;
-  p.estimate = r_est < p.K && r_est <= static_cast<int64_t>(p.sample_m) &&
-               (8 * r_est <= p.K || static_cast<int64_t>(p.sample_m) < p.K);
-  p.rank = static_cast<uint32_t>(p.estimate ? r_est : p.K);
   return FA3Q_OK;
 }
 

@@ -203,13 +203,11 @@ def main() -> int:
     kq = torch.empty((QB, H, QS, DN), dtype=torch.int8, device=dev)
     kr = torch.empty((QB, H, QS, DR), dtype=torch.bfloat16, device=dev)
     out = torch.empty((QB, H, DV), dtype=torch.float32, device=dev)
-    win_min = torch.empty(H, dtype=torch.float32, device=dev)
-    win_max = torch.empty(H, dtype=torch.float32, device=dev)
     run_min = torch.empty(H, dtype=torch.float32, device=dev)
     run_max = torch.empty(H, dtype=torch.float32, device=dev)
     scale = torch.empty(H, dtype=torch.float32, device=dev)
-    ws_cal = torch.empty(max(1, fa.fa3q_calibrate_workspace_bytes(torch.bfloat16, *CAL_SHAPE, RATIO)),
-                         dtype=torch.uint8, device=dev)
+    ws_cal = torch.empty(max(1, fa.fa3q_calibrate_batches_workspace_bytes(torch.bfloat16, CAL_BATCHES, *CAL_SHAPE,
+                                                                          RATIO)), dtype=torch.uint8, device=dev)
     dec_ws_bytes = fa.fa3q_decode_attn_workspace_bytes(QB, H, QS, DV)
     ws_dec = torch.empty(dec_ws_bytes, dtype=torch.uint8, device=dev) if dec_ws_bytes else None
     sm = 1.0 / math.sqrt(DN + DR)
@@ -221,10 +219,8 @@ def main() -> int:
     def step(ev=None):
         if ev:
             ev[0].record(stream)
-        fa.fa3q_init_minmax(run_min, run_max, stream=stream)
-        for xb in calib:
-            fa.fa3q_calibrate_perhead(xb, RATIO, win_min, win_max, ws_cal, stream=stream)
-            fa.fa3q_accumulate_minmax(run_min, run_max, win_min, win_max, stream=stream)
+        # every calibration batch's windows folded into the running min/max, in one call
+        fa.fa3q_calibrate_batches(calib, RATIO, run_min, run_max, True, workspace=ws_cal, stream=stream)
         if ev:
             ev[1].record(stream)
         fa.fa3q_qparams(run_min, run_max, scale, stream=stream)
@@ -265,14 +261,14 @@ def main() -> int:
     breakdown = {
         "calibrate": {"ms": cal_ms, "gelem_s": CAL_BATCHES * CAL_BYTES / 2 / (cal_ms * 1e-3) / 1e9,
                       "gbs": cal_gbs, "frac_hbm": cal_gbs / HBM_PEAK_GBS,
-                      "note": "4 batches: chunk+merge kernels per batch, plus init/accumulate"},
+                      "note": "4 batches in one fa3q_calibrate_batches call: sample, chunk, merge, accumulate"},
         "qparams": {"ms": qp_ms},
         "quantize": {"ms": quant_ms, "gbs": quant_gbs, "frac_hbm": quant_gbs / HBM_PEAK_GBS},
         "decode": {"ms": dec_ms, "kv_gbs": dec_gbs, "frac_hbm": dec_gbs / HBM_PEAK_GBS},
     }
     # the kernel with the largest share of the step; its events bracket exactly one launch
     stages = {"quantize_k_kernel": (quant_ms, QUANT_BYTES, 1), "decode_split_kernel": (dec_ms, DEC_BYTES, 1),
-              "calib_chunk_kernel": (cal_ms / CAL_BATCHES, CAL_BYTES, CAL_BATCHES)}
+              "calib_chunk_kernel": (cal_ms, CAL_BATCHES * CAL_BYTES, 1)}
     dom = max(stages, key=lambda s: stages[s][0] * stages[s][2])
     d_ms, d_bytes, _ = stages[dom]
     achieved = d_bytes / (d_ms * 1e-3) / 1e9
@@ -281,7 +277,7 @@ def main() -> int:
                 "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "traffic_source": traffic_src,
                 "algorithmic_bytes_per_launch": d_bytes, "avg_launch_ms": d_ms}
     if dom == "calib_chunk_kernel":
-        roofline["note"] = "calibration: chunk + merge kernels per batch, events around both"
+        roofline["note"] = "calibration: sample, chunk, merge and accumulate kernels, events around all four"
 
     # Decode step with append (one new token per (b,h) written into the cache at position
     # T-1, then attention over all T tokens): the same cache reads as decode plus one row

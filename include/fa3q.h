@@ -19,6 +19,7 @@
  *   9. fa3q_decode_attn_asym   -- attention as in 5 over the asymmetric K-nope cache of 8
  *  10. fa3q_decode_latent      -- attention of every head of a sequence over one shared-latent
  *      (absorbed MLA) cache: INT8 latent (one scale) + bf16 RoPE part, on the matrix cores
+ *  11. fa3q_calibrate_batches  -- 1 and 2 over several calibration batches in one call
  *
  * Sources, cited by page title and section:
  *   [MS] msModelSlim documentation, "FA3量化：Flash Attention 3激活量化算法说明"
@@ -332,6 +333,40 @@ int fa3q_decode_attn_asym(const uint16_t* q, const int8_t* k_nope_q, const uint1
                           const uint16_t* v, int64_t B, int64_t H, int64_t T, int64_t Dn, int64_t Dr,
                           int64_t Dv, float sm_scale, float* out, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* 11. Several calibration batches: windows and running min/max in one call  */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Device workspace fa3q_calibrate_batches needs, in bytes (0 when the arguments are
+ * invalid, nb outside 1..16 included).
+ */
+size_t fa3q_calibrate_batches_workspace_bytes(int dtype, int64_t nb, int64_t B, int64_t H, int64_t S,
+                                              int64_t D, double ratio);
+
+/*
+ * [MS] 算法流程: each calibration batch gives per-head Recall Windows, and the running
+ * statistics keep the smallest window minimum and largest window maximum over batches.
+ * For batches b = 0 .. nb-1 of the same shape, in order:
+ *   (win_min[b], win_max[b]) = fa3q_calibrate_perhead(xs[b], ...)   (bit for bit)
+ *   run_min = min(run_min, win_min[b]), run_max = max(run_max, win_max[b])  (as fa3q_accumulate_minmax)
+ * with run_min/run_max starting at (+inf, -inf) when init != 0 (fa3q_init_minmax), at
+ * their current contents otherwise.  The batches share each launch: one sample, one
+ * streaming pass over all of them, one merge and one accumulation.
+ *
+ *   xs         HOST array of nb device pointers, each as x of fa3q_calibrate_perhead
+ *              (dtype, (B,H,S,D) contiguous, 16-byte aligned); read during the call only.
+ *   nb         1 .. 16.
+ *   run_min, run_max  device float32 [H], 4-byte aligned, in/out.
+ *   win_min, win_max  device float32 [nb][H], 4-byte aligned, or both NULL (the windows
+ *              then live in the workspace only).
+ *   workspace  device, 256-byte aligned, >= fa3q_calibrate_batches_workspace_bytes(...).
+ *   Other arguments and errors as fa3q_calibrate_perhead; FA3Q_ERR_SHAPE for nb out of range.
+ */
+int fa3q_calibrate_batches(const void* const* xs, int64_t nb, int dtype, int64_t B, int64_t H, int64_t S, int64_t D,
+                           double ratio, float* run_min, float* run_max, int init, float* win_min, float* win_max,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* 10. Decode attention over a shared-latent (absorbed MLA) cache            */

@@ -18,6 +18,8 @@ from ._lib import (  # noqa: F401
 from .ops import (  # noqa: F401
     dtype_code,
     fa3q_accumulate_minmax,
+    fa3q_calibrate_batches,
+    fa3q_calibrate_batches_workspace_bytes,
     fa3q_calibrate_max_windows,
     fa3q_calibrate_perhead,
     fa3q_calibrate_workspace_bytes,

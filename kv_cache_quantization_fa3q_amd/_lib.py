@@ -57,6 +57,9 @@ SIGNATURES = {
     "fa3q_decode_attn_asym": (_int, [_vp, _vp, _vp, _vp, _int, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
                                      ctypes.c_float, _vp, _vp, _sz, _vp]),
     "fa3q_decode_latent_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
+    "fa3q_calibrate_batches_workspace_bytes": (_sz, [_int, _i64, _i64, _i64, _i64, _i64, ctypes.c_double]),
+    "fa3q_calibrate_batches": (_int, [ctypes.POINTER(_vp), _i64, _int, _i64, _i64, _i64, _i64, ctypes.c_double, _vp,
+                                      _vp, _int, _vp, _vp, _vp, _sz, _vp]),
     "fa3q_decode_latent": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, ctypes.c_float, _vp, _vp, _sz,
                                   _vp]),
 }

@@ -60,6 +60,7 @@
 // which the wave appends the qualifying keys; a round appends at most 64 vectors per
 // wave, so the buffers need room for one round, not for a whole tile.
 #include <cmath>
+#include <type_traits>
 
 #include "fa3q_internal.hpp"
 
@@ -80,6 +81,20 @@ constexpr int kMergeTile = kMergeThreads * kMergePerThread;
 constexpr int64_t kTargetCUs = 256;    // MI355X compute units (sizes the chunk grid)
 constexpr int64_t kChunkGroupsPerCU = 4;  // chunk workgroups resident per CU (VGPR-bound)
 constexpr int kMinTilesPerChunk = 4;
+constexpr int kMaxBatches = 16;        // calibration batches one call can take
+
+// Several batches of the same shape in one launch: workgroup i serves batch i / per, with
+// that batch's input and its own region of the workspace (lists, bounds, flags).
+struct Batches {
+  const void* x[kMaxBatches];
+  int64_t region;  // workspace bytes per batch
+  int32_t per;     // workgroups per batch
+};
+
+template <typename T>
+__device__ __forceinline__ T* in_region(T* p, int64_t off) {
+  return p ? reinterpret_cast<T*>(reinterpret_cast<unsigned char*>(const_cast<std::remove_const_t<T>*>(p)) + off) : p;
+}
 
 // Control words at the start of dynamic LDS.
 enum Ctl : int {
@@ -485,17 +500,19 @@ struct SampleArgs {
 // chunk itself holds K).
 // kSmallSlab: slabs shorter than a run, so a run may cross several slab boundaries.
 template <typename InT, bool kSmallSlab>
-__global__ __launch_bounds__(kSampleThreads) void calib_sample_kernel(SampleArgs a) {
+__global__ __launch_bounds__(kSampleThreads) void calib_sample_kernel(SampleArgs a, Batches bt) {
   using T = In<InT>;
   using KeyT = typename T::KeyT;
   constexpr int kPerVec = 16 / sizeof(InT);
   constexpr int kWaves = kSampleThreads / kWave;
   __shared__ uint32_t cnt[2][kWaves];  // [bit parity][wave]: lo count | hi count << 16
-  const int h = static_cast<int>(blockIdx.x);
+  const int batch = static_cast<int>(blockIdx.x) / bt.per;
+  const int h = static_cast<int>(blockIdx.x) - batch * bt.per;
+  a.bounds = in_region(a.bounds, batch * bt.region);
   const int tid = static_cast<int>(threadIdx.x);
   const int wave = tid / kWave;
   const int lane = lane_id();
-  const InT* x = static_cast<const InT*>(a.x);
+  const InT* x = static_cast<const InT*>(bt.x[batch]);
 
   // every load of the sample is issued before the first is used
   u32x4 xs[kSampleRuns];
@@ -572,7 +589,7 @@ __global__ __launch_bounds__(kSampleThreads) void calib_sample_kernel(SampleArgs
 }
 
 template <typename InT>
-__global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void calib_chunk_kernel(ChunkArgs a) {
+__global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void calib_chunk_kernel(ChunkArgs a, Batches bt) {
   using T = In<InT>;
   using KeyT = typename T::KeyT;
   using Lim = typename T::Lim;
@@ -603,8 +620,14 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
   // blocks the dispatcher deals round-robin to the XCDs read neighbouring chunks and every
   // XCD streams from all of memory at once; a block per (h, b) in head order would hand
   // each XCD one batch's contiguous range instead, which runs far below the HBM rate.
-  const int slab_i = static_cast<int>(blockIdx.x) / a.cps;
-  const int part = static_cast<int>(blockIdx.x) - slab_i * a.cps;
+  const int batch = static_cast<int>(blockIdx.x) / bt.per;
+  const int bid = static_cast<int>(blockIdx.x) - batch * bt.per;
+  a.x = bt.x[batch];
+  a.lists = in_region(a.lists, batch * bt.region);
+  a.bounds = in_region(a.bounds, batch * bt.region);
+  a.fail = in_region(a.fail, batch * bt.region);
+  const int slab_i = bid / a.cps;
+  const int part = bid - slab_i * a.cps;
   const int b = slab_i / a.H;
   const int h = slab_i - b * a.H;
   const int c = b * a.cps + part;
@@ -820,7 +843,7 @@ __device__ void bitonic_sort2(KeyT* lo, KeyT* hi, int tid) {
 }
 
 template <typename KeyT>
-__global__ __launch_bounds__(kMergeThreads) void calib_merge_kernel(MergeArgs a) {
+__global__ __launch_bounds__(kMergeThreads) void calib_merge_kernel(MergeArgs a, Batches bt) {
   constexpr int NT = kMergeThreads;
   extern __shared__ __align__(16) unsigned char smem[];
   uint32_t* ctl = reinterpret_cast<uint32_t*>(smem);
@@ -836,7 +859,12 @@ __global__ __launch_bounds__(kMergeThreads) void calib_merge_kernel(MergeArgs a)
   st.room = kMergeTile;
   st.init();
 
-  const int h = static_cast<int>(blockIdx.x);
+  const int batch = static_cast<int>(blockIdx.x) / bt.per;
+  const int h = static_cast<int>(blockIdx.x) - batch * bt.per;
+  a.lists = in_region(a.lists, batch * bt.region);
+  a.fail = in_region(a.fail, batch * bt.region);
+  a.win_min += static_cast<int64_t>(batch) * a.H;
+  a.win_max += static_cast<int64_t>(batch) * a.H;
   const int tid = static_cast<int>(threadIdx.x);
   if (a.fixup && a.fail[h] == 0) return;  // uniform over the workgroup
   const bool check = !a.fixup && a.fail != nullptr;
@@ -965,13 +993,18 @@ constexpr int kWaveMergeRegs = 64;  // most union keys per lane
 constexpr int kWaveMergeThreads = 2 * kWave;
 
 template <typename KeyT, int R, int E>
-__global__ __launch_bounds__(kWaveMergeThreads) void calib_merge_wave_kernel(MergeArgs a) {
+__global__ __launch_bounds__(kWaveMergeThreads) void calib_merge_wave_kernel(MergeArgs a, Batches bt) {
   constexpr uint32_t kMax = KeyInfo<KeyT>::kMax;
   constexpr int P = kWave * E;
   __shared__ uint32_t sorted[2][P];
   __shared__ float best_l[2];
   __shared__ uint32_t best_at[2];
-  const int h = static_cast<int>(blockIdx.x);
+  const int batch = static_cast<int>(blockIdx.x) / bt.per;
+  const int h = static_cast<int>(blockIdx.x) - batch * bt.per;
+  a.lists = in_region(a.lists, batch * bt.region);
+  a.fail = in_region(a.fail, batch * bt.region);
+  a.win_min += static_cast<int64_t>(batch) * a.H;
+  a.win_max += static_cast<int64_t>(batch) * a.H;
   const int tid = static_cast<int>(threadIdx.x);
   const int side = tid / kWave;
   const uint32_t lane = static_cast<uint32_t>(lane_id());
@@ -1227,19 +1260,21 @@ int make_plan(int dtype, int64_t B, int64_t H, int64_t S, int64_t D, double rati
 }
 
 template <typename KeyT, int R>
-void launch_wave_merge(int e, int64_t H, const MergeArgs& ma, hipStream_t stream) {
-  const dim3 g(static_cast<unsigned>(H)), blk(kWaveMergeThreads);
+void launch_wave_merge(int e, int64_t groups, const MergeArgs& ma, const Batches& bt, hipStream_t stream) {
+  const dim3 g(static_cast<unsigned>(groups)), blk(kWaveMergeThreads);
   switch (e) {
-    case 1: hipLaunchKernelGGL((calib_merge_wave_kernel<KeyT, R, 1>), g, blk, 0, stream, ma); break;
-    case 2: hipLaunchKernelGGL((calib_merge_wave_kernel<KeyT, R, 2>), g, blk, 0, stream, ma); break;
-    case 4: hipLaunchKernelGGL((calib_merge_wave_kernel<KeyT, R, 4>), g, blk, 0, stream, ma); break;
-    case 8: hipLaunchKernelGGL((calib_merge_wave_kernel<KeyT, R, 8>), g, blk, 0, stream, ma); break;
-    default: hipLaunchKernelGGL((calib_merge_wave_kernel<KeyT, R, 16>), g, blk, 0, stream, ma); break;
+    case 1: hipLaunchKernelGGL((calib_merge_wave_kernel<KeyT, R, 1>), g, blk, 0, stream, ma, bt); break;
+    case 2: hipLaunchKernelGGL((calib_merge_wave_kernel<KeyT, R, 2>), g, blk, 0, stream, ma, bt); break;
+    case 4: hipLaunchKernelGGL((calib_merge_wave_kernel<KeyT, R, 4>), g, blk, 0, stream, ma, bt); break;
+    case 8: hipLaunchKernelGGL((calib_merge_wave_kernel<KeyT, R, 8>), g, blk, 0, stream, ma, bt); break;
+    default: hipLaunchKernelGGL((calib_merge_wave_kernel<KeyT, R, 16>), g, blk, 0, stream, ma, bt); break;
   }
 }
 
+// Windows of nb batches (x[b], each (B,H,S,D)) into win_min/win_max [nb][H]; batch b uses
+// the workspace region b (p.total_bytes each).
 template <typename InT>
-int launch(const void* x, int64_t H, const CalibPlan& p, float* win_min, float* win_max,
+int launch(const void* const* x, int64_t nb, int64_t H, const CalibPlan& p, float* win_min, float* win_max,
            void* workspace, hipStream_t stream) {
   using KeyT = InT;
   int st = allow_dynamic_lds(reinterpret_cast<const void*>(calib_chunk_kernel<InT>), p.lds_chunk);
@@ -1247,9 +1282,13 @@ int launch(const void* x, int64_t H, const CalibPlan& p, float* win_min, float* 
   st = allow_dynamic_lds(reinterpret_cast<const void*>(calib_merge_kernel<KeyT>), p.lds_merge);
   if (st != FA3Q_OK) return st;
 
+  Batches bt;
+  for (int b = 0; b < kMaxBatches; ++b) bt.x[b] = b < nb ? x[b] : nullptr;
+  bt.region = static_cast<int64_t>(p.total_bytes);
   uint32_t* bounds = reinterpret_cast<uint32_t*>(static_cast<unsigned char*>(workspace) + p.lists_bytes);
+  uint32_t* fail = reinterpret_cast<uint32_t*>(static_cast<unsigned char*>(workspace) + p.lists_bytes + p.bounds_bytes);
   SampleArgs sa;
-  sa.x = x;
+  sa.x = nullptr;
   sa.bounds = bounds;
   sa.Lv = p.L / (16 / static_cast<int64_t>(p.key_bytes));
   for (int j = 0; j < kSampleRuns; ++j) {
@@ -1260,13 +1299,15 @@ int launch(const void* x, int64_t H, const CalibPlan& p, float* win_min, float* 
   sa.H = static_cast<int32_t>(H);
   sa.M = p.sample_m;
   sa.K = p.rank;
+  bt.per = static_cast<int32_t>(H);
+  const dim3 g_heads(static_cast<unsigned>(nb * H));
   if (sa.Lv >= kSampleThreads)
-    hipLaunchKernelGGL((calib_sample_kernel<InT, false>), dim3(static_cast<unsigned>(H)), dim3(kSampleThreads), 0, stream, sa);
+    hipLaunchKernelGGL((calib_sample_kernel<InT, false>), g_heads, dim3(kSampleThreads), 0, stream, sa, bt);
   else
-    hipLaunchKernelGGL((calib_sample_kernel<InT, true>), dim3(static_cast<unsigned>(H)), dim3(kSampleThreads), 0, stream, sa);
+    hipLaunchKernelGGL((calib_sample_kernel<InT, true>), g_heads, dim3(kSampleThreads), 0, stream, sa, bt);
 
   ChunkArgs ca;
-  ca.x = x;
+  ca.x = nullptr;
   ca.lists = workspace;
   ca.bounds = bounds;
   ca.fail = nullptr;
@@ -1277,9 +1318,10 @@ int launch(const void* x, int64_t H, const CalibPlan& p, float* win_min, float* 
   ca.nch = p.nch;
   ca.K = static_cast<uint32_t>(p.K);
   ca.cap = p.cap_chunk;
-  hipLaunchKernelGGL(calib_chunk_kernel<InT>, dim3(static_cast<unsigned>(H * p.nch)), dim3(kChunkThreads),
-                     p.lds_chunk, stream, ca);
-  uint32_t* fail = reinterpret_cast<uint32_t*>(static_cast<unsigned char*>(workspace) + p.lists_bytes + p.bounds_bytes);
+  Batches bc = bt;
+  bc.per = static_cast<int32_t>(H * p.nch);
+  const dim3 g_chunks(static_cast<unsigned>(nb * H * p.nch));
+  hipLaunchKernelGGL(calib_chunk_kernel<InT>, g_chunks, dim3(kChunkThreads), p.lds_chunk, stream, ca, bc);
   MergeArgs ma;
   ma.lists = workspace;
   ma.win_min = win_min;
@@ -1293,25 +1335,48 @@ int launch(const void* x, int64_t H, const CalibPlan& p, float* win_min, float* 
   ma.P = p.P;
   auto merge = [&](const MergeArgs& m) {
     if (p.wave_merge_e > 0 && p.wave_merge_r == 32)
-      launch_wave_merge<KeyT, 32>(p.wave_merge_e, H, m, stream);
+      launch_wave_merge<KeyT, 32>(p.wave_merge_e, nb * H, m, bt, stream);
     else if (p.wave_merge_e > 0)
-      launch_wave_merge<KeyT, 64>(p.wave_merge_e, H, m, stream);
+      launch_wave_merge<KeyT, 64>(p.wave_merge_e, nb * H, m, bt, stream);
     else
-      hipLaunchKernelGGL(calib_merge_kernel<KeyT>, dim3(static_cast<unsigned>(H)), dim3(kMergeThreads),
-                         p.lds_merge, stream, m);
+      hipLaunchKernelGGL(calib_merge_kernel<KeyT>, g_heads, dim3(kMergeThreads), p.lds_merge, stream, m, bt);
   };
   merge(ma);
   if (p.estimate) {
     // heads whose estimated bound held fewer than K values: again with no bound
     ChunkArgs cf = ca;
     cf.fail = fail;
-    hipLaunchKernelGGL(calib_chunk_kernel<InT>, dim3(static_cast<unsigned>(H * p.nch)), dim3(kChunkThreads),
-                       p.lds_chunk, stream, cf);
+    hipLaunchKernelGGL(calib_chunk_kernel<InT>, g_chunks, dim3(kChunkThreads), p.lds_chunk, stream, cf, bc);
     MergeArgs mf = ma;
     mf.fixup = 1;
     merge(mf);
   }
   return launch_status();
+}
+
+// Unsigned key whose order is the float32 total order with -0.0 below +0.0.
+__device__ __forceinline__ uint32_t total_order_key(float f) {
+  const uint32_t b = __float_as_uint(f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// Running min/max over nb batches' windows, head by head, in batch order (the same
+// comparisons as nb accumulate calls); init starts from the identity (+inf, -inf).
+__global__ __launch_bounds__(256) void accumulate_batches_kernel(float* __restrict__ run_min, float* __restrict__ run_max,
+                                                                 const float* __restrict__ win_min,
+                                                                 const float* __restrict__ win_max, int64_t nb,
+                                                                 int64_t H, int init) {
+  const int64_t h = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (h >= H) return;
+  float mn = init ? __uint_as_float(0x7f800000u) : run_min[h];
+  float mx = init ? __uint_as_float(0xff800000u) : run_max[h];
+  for (int64_t b = 0; b < nb; ++b) {
+    const float c = win_min[b * H + h], d = win_max[b * H + h];
+    mn = total_order_key(c) < total_order_key(mn) ? c : mn;
+    mx = total_order_key(d) > total_order_key(mx) ? d : mx;
+  }
+  run_min[h] = mn;
+  run_max[h] = mx;
 }
 
 }  // namespace
@@ -1351,7 +1416,47 @@ extern "C" int fa3q_calibrate_perhead(const void* x, int dtype, int64_t B, int64
     return FA3Q_ERR_ALIGN;
   if (!workspace || workspace_bytes < p.total_bytes) return FA3Q_ERR_WORKSPACE;
   if (!is_aligned(workspace, 256)) return FA3Q_ERR_ALIGN;
+  const void* xs[1] = {x};
   if (dtype == FA3Q_BF16)
-    return launch<uint16_t>(x, H, p, win_min, win_max, workspace, as_stream(stream));
-  return launch<uint32_t>(x, H, p, win_min, win_max, workspace, as_stream(stream));
+    return launch<uint16_t>(xs, 1, H, p, win_min, win_max, workspace, as_stream(stream));
+  return launch<uint32_t>(xs, 1, H, p, win_min, win_max, workspace, as_stream(stream));
+}
+
+extern "C" size_t fa3q_calibrate_batches_workspace_bytes(int dtype, int64_t nb, int64_t B, int64_t H, int64_t S,
+                                                         int64_t D, double ratio) {
+  CalibPlan p;
+  if (nb <= 0 || nb > kMaxBatches || make_plan(dtype, B, H, S, D, ratio, p) != FA3Q_OK) return 0;
+  if (nb * B * H * p.nch > (int64_t{1} << 31) - 1) return 0;
+  return static_cast<size_t>(nb) * p.total_bytes + round_up(2 * static_cast<size_t>(nb * H) * sizeof(float), 256);
+}
+
+extern "C" int fa3q_calibrate_batches(const void* const* xs, int64_t nb, int dtype, int64_t B, int64_t H, int64_t S,
+                                      int64_t D, double ratio, float* run_min, float* run_max, int init,
+                                      float* win_min, float* win_max, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  if (!xs || !run_min || !run_max || (!win_min != !win_max)) return FA3Q_ERR_NULL;
+  if (nb <= 0 || nb > kMaxBatches) return FA3Q_ERR_SHAPE;
+  for (int64_t b = 0; b < nb; ++b)
+    if (!xs[b]) return FA3Q_ERR_NULL;
+  CalibPlan p;
+  const int st = make_plan(dtype, B, H, S, D, ratio, p);
+  if (st != FA3Q_OK) return st;
+  if (nb * H * p.nch > (int64_t{1} << 31) - 1) return FA3Q_ERR_SHAPE;
+  for (int64_t b = 0; b < nb; ++b)
+    if (!is_aligned(xs[b], 16)) return FA3Q_ERR_ALIGN;
+  if (!is_aligned(run_min, 4) || !is_aligned(run_max, 4) || (win_min && (!is_aligned(win_min, 4) || !is_aligned(win_max, 4))))
+    return FA3Q_ERR_ALIGN;
+  const size_t need = fa3q_calibrate_batches_workspace_bytes(dtype, nb, B, H, S, D, ratio);
+  if (!workspace || workspace_bytes < need) return FA3Q_ERR_WORKSPACE;
+  if (!is_aligned(workspace, 256)) return FA3Q_ERR_ALIGN;
+  float* wins = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + static_cast<size_t>(nb) * p.total_bytes);
+  float* wmin = win_min ? win_min : wins;
+  float* wmax = win_max ? win_max : wins + nb * H;
+  hipStream_t s = as_stream(stream);
+  const int lst = dtype == FA3Q_BF16 ? launch<uint16_t>(xs, nb, H, p, wmin, wmax, workspace, s)
+                                     : launch<uint32_t>(xs, nb, H, p, wmin, wmax, workspace, s);
+  if (lst != FA3Q_OK) return lst;
+  hipLaunchKernelGGL(accumulate_batches_kernel, dim3(static_cast<unsigned>((H + 255) / 256)), dim3(256), 0, s, run_min,
+                     run_max, wmin, wmax, nb, H, init ? 1 : 0);
+  return launch_status();
 }

@@ -18,6 +18,8 @@ __all__ = [
     "fa3q_calibrate_max_windows",
     "fa3q_calibrate_workspace_bytes",
     "fa3q_calibrate_perhead",
+    "fa3q_calibrate_batches_workspace_bytes",
+    "fa3q_calibrate_batches",
     "fa3q_init_minmax",
     "fa3q_accumulate_minmax",
     "fa3q_qparams",
@@ -110,6 +112,35 @@ def fa3q_calibrate_perhead(x: torch.Tensor, ratio: float, win_min: Optional[torc
                                       workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "fa3q_calibrate_perhead")
     return win_min, win_max
+
+
+def fa3q_calibrate_batches_workspace_bytes(dtype: torch.dtype, nb: int, B: int, H: int, S: int, D: int,
+                                           ratio: float) -> int:
+    return int(lib().fa3q_calibrate_batches_workspace_bytes(dtype_code(dtype), nb, B, H, S, D, float(ratio)))
+
+
+def fa3q_calibrate_batches(xs, ratio: float, run_min: torch.Tensor, run_max: torch.Tensor, init: bool = True,
+                           win_min: Optional[torch.Tensor] = None, win_max: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Recall Windows of every batch in ``xs`` (same shape and dtype) folded into ``run_min``/``run_max``."""
+    xs = list(xs)
+    if not xs:
+        raise ValueError("at least one batch")
+    B, H, S, D = (int(v) for v in xs[0].shape)
+    code = dtype_code(xs[0].dtype)
+    for x in xs:
+        if x.dim() != 4 or tuple(x.shape) != (B, H, S, D) or x.dtype != xs[0].dtype:
+            raise ValueError("every batch must have the same (B, H, S, D) shape and dtype")
+    _need_gpu("fa3q_calibrate_batches", *xs, run_min, run_max, win_min, win_max)
+    nb = len(xs)
+    nbytes = fa3q_calibrate_batches_workspace_bytes(xs[0].dtype, nb, B, H, S, D, ratio)
+    workspace = _workspace(nbytes, xs[0].device, workspace)
+    ptrs = (ctypes.c_void_p * nb)(*[x.data_ptr() for x in xs])
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().fa3q_calibrate_batches(ptrs, nb, code, B, H, S, D, float(ratio), _ptr(run_min), _ptr(run_max),
+                                      1 if init else 0, _ptr(win_min), _ptr(win_max), _ptr(workspace), wbytes,
+                                      _stream(stream))
+    _check(st, "fa3q_calibrate_batches")
 
 
 def fa3q_init_minmax(run_min: torch.Tensor, run_max: torch.Tensor, stream=None) -> None:

@@ -300,6 +300,35 @@ def test_decode_latent_rejections():
     assert lib.fa3q_decode_latent_workspace_bytes(1024, 128, 64, 512) == 0   # one split: no workspace
 
 
+@no_gpu_only
+def test_calibrate_batches_rejections():
+    lib = fa.lib()
+    f = lib.fa3q_calibrate_batches
+    shape = (8, 128, 2048, 128)
+    need = lib.fa3q_calibrate_batches_workspace_bytes(L.FA3Q_BF16, 4, *shape, 0.9999)
+    assert need > 4 * lib.fa3q_calibrate_workspace_bytes(L.FA3Q_BF16, *shape, 0.9999)
+    assert lib.fa3q_calibrate_batches_workspace_bytes(L.FA3Q_BF16, 0, *shape, 0.9999) == 0
+    assert lib.fa3q_calibrate_batches_workspace_bytes(L.FA3Q_BF16, 17, *shape, 0.9999) == 0
+
+    def call(xs=None, nb=4, dt=L.FA3Q_BF16, ratio=0.9999, rmin=_p(), rmax=_p(), wmin=None, wmax=None, ws=_p(),
+             wsb=None):
+        ptrs = (ctypes.c_void_p * 4)(*(xs if xs is not None else [FAKE] * 4))
+        return f(ptrs, nb, dt, *shape, ratio, rmin, rmax, 1, wmin, wmax, ws, need if wsb is None else wsb, None)
+
+    assert call(rmin=None) == L.FA3Q_ERR_NULL
+    assert call(wmin=_p()) == L.FA3Q_ERR_NULL                 # one window array without the other
+    assert call(xs=[FAKE, FAKE, 0, FAKE]) == L.FA3Q_ERR_NULL
+    assert call(nb=0) == L.FA3Q_ERR_SHAPE
+    assert call(nb=17) == L.FA3Q_ERR_SHAPE
+    assert call(dt=9) == L.FA3Q_ERR_DTYPE
+    assert call(ratio=0.0) == L.FA3Q_ERR_RATIO
+    assert call(xs=[FAKE, FAKE + 8, FAKE, FAKE]) == L.FA3Q_ERR_ALIGN
+    assert call(rmax=_p(2)) == L.FA3Q_ERR_ALIGN
+    assert call(ws=None) == L.FA3Q_ERR_WORKSPACE
+    assert call(wsb=64) == L.FA3Q_ERR_WORKSPACE
+    assert call(ws=_p(128)) == L.FA3Q_ERR_ALIGN
+
+
 def test_binding_refuses_mismatched_asym_tables():
     import torch
     k = torch.zeros((1, 2, 16, 48), dtype=torch.bfloat16)

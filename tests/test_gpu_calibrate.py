@@ -187,3 +187,91 @@ def test_estimated_bound_that_fails_is_redone_exactly(fa):
     torch.cuda.synchronize()
     flags = ws[nbytes - 256:nbytes - 256 + 4 * H].cpu().view(torch.int32).numpy()
     assert flags.tolist() == [1, 1], flags
+
+
+def test_batches_in_one_call_match_the_oracle(fa):
+    dev = torch.device("cuda:0")
+    shape, ratio = (2, 4, 2048, 64), 0.999
+    sigma = synth.head_sigmas(shape[1], seed=321)
+    xs = [synth.activations(shape, sigma, law="t3", outlier_frac=0.0005, outlier_mult=40.0, dtype=torch.bfloat16,
+                            seed=330 + i) for i in range(3)]
+    log(f"calibrate_batches: 3 x {shape} ratio={ratio}")
+    H = shape[1]
+    rmin = torch.empty(H, dtype=torch.float32, device=dev)
+    rmax = torch.empty(H, dtype=torch.float32, device=dev)
+    wmin = torch.empty((3, H), dtype=torch.float32, device=dev)
+    wmax = torch.empty((3, H), dtype=torch.float32, device=dev)
+    fa.fa3q_calibrate_batches([x.to(dev) for x in xs], ratio, rmin, rmax, True, wmin, wmax)
+    torch.cuda.synchronize()
+    run_lo, run_hi = oracle.init_running(H)
+    for i, x in enumerate(xs):
+        olo, ohi = oracle.calibrate(_host_f32(x), ratio)
+        assert_bits_equal(f32(wmin[i]), olo, f"batch {i} win_min")
+        assert_bits_equal(f32(wmax[i]), ohi, f"batch {i} win_max")
+        run_lo, run_hi = oracle.accumulate(run_lo, run_hi, olo, ohi)
+    assert_bits_equal(f32(rmin), run_lo, "run_min")
+    assert_bits_equal(f32(rmax), run_hi, "run_max")
+    # init off: the running state carries over (a second call over the same batches changes nothing)
+    fa.fa3q_calibrate_batches([x.to(dev) for x in xs[:2]], ratio, rmin, rmax, False)
+    torch.cuda.synchronize()
+    assert_bits_equal(f32(rmin), run_lo, "run_min carried")
+    assert_bits_equal(f32(rmax), run_hi, "run_max carried")
+
+
+def test_batches_equal_per_batch_calls_at_the_calibration_workload(fa):
+    # 4 bf16 batches (8,128,2048,128), ratio 0.9999: one call against 4 calibrate + accumulate calls
+    dev = torch.device("cuda:0")
+    shape, ratio = (8, 128, 2048, 128), 0.9999
+    sigma = synth.head_sigmas(128, seed=2024)
+    xs = [synth.activations(shape, sigma, law="t3", dtype=torch.bfloat16, seed=100 + i, device=dev) for i in range(4)]
+    log(f"calibrate_batches: 4 x {shape} ratio={ratio}")
+    rmin = torch.empty(128, dtype=torch.float32, device=dev)
+    rmax = torch.empty(128, dtype=torch.float32, device=dev)
+    wmin = torch.empty((4, 128), dtype=torch.float32, device=dev)
+    wmax = torch.empty((4, 128), dtype=torch.float32, device=dev)
+    fa.fa3q_calibrate_batches(xs, ratio, rmin, rmax, True, wmin, wmax)
+    qmin = torch.empty(128, dtype=torch.float32, device=dev)
+    qmax = torch.empty(128, dtype=torch.float32, device=dev)
+    fa.fa3q_init_minmax(qmin, qmax)
+    for i, x in enumerate(xs):
+        lo, hi = fa.fa3q_calibrate_perhead(x, ratio)
+        torch.cuda.synchronize()
+        assert torch.equal(lo.view(torch.int32), wmin[i].view(torch.int32)), i
+        assert torch.equal(hi.view(torch.int32), wmax[i].view(torch.int32)), i
+        fa.fa3q_accumulate_minmax(qmin, qmax, lo, hi)
+    torch.cuda.synchronize()
+    assert torch.equal(qmin.view(torch.int32), rmin.view(torch.int32))
+    assert torch.equal(qmax.view(torch.int32), rmax.view(torch.int32))
+
+
+def test_batches_with_an_estimated_bound_that_fails_in_one_batch(fa):
+    # K = 10487 (estimated bounds): batch 1 plants the sampled-position extremes that make
+    # its check fail; batches 0 and 2 are ordinary.  Each batch has its own flags and lists.
+    dev = torch.device("cuda:0")
+    B, H, S, D = 1, 2, 8192, 128
+    vec, stride = 8, max(256, (B * S * D // 8) // 32)
+    rng = np.random.default_rng(29)
+    xs = []
+    for i in range(3):
+        x = rng.standard_normal((B, H, S * D)).astype(np.float32)
+        if i == 1:
+            for g in range(8):
+                for t in range(256):
+                    x[0, :, (4 * g * stride + t) * vec] = -70.0
+                    x[0, :, ((4 * g + 1) * stride + t) * vec] = 90.0
+        xs.append(torch.from_numpy(x.reshape(B, H, S, D)).to(torch.bfloat16))
+    rmin = torch.empty(H, dtype=torch.float32, device=dev)
+    rmax = torch.empty(H, dtype=torch.float32, device=dev)
+    wmin = torch.empty((3, H), dtype=torch.float32, device=dev)
+    wmax = torch.empty((3, H), dtype=torch.float32, device=dev)
+    log("calibrate_batches: estimated bound failing in batch 1")
+    fa.fa3q_calibrate_batches([x.to(dev) for x in xs], 0.99, rmin, rmax, True, wmin, wmax)
+    torch.cuda.synchronize()
+    run_lo, run_hi = oracle.init_running(H)
+    for i, x in enumerate(xs):
+        olo, ohi = oracle.calibrate(_host_f32(x), 0.99)
+        assert_bits_equal(f32(wmin[i]), olo, f"batch {i} win_min")
+        assert_bits_equal(f32(wmax[i]), ohi, f"batch {i} win_max")
+        run_lo, run_hi = oracle.accumulate(run_lo, run_hi, olo, ohi)
+    assert_bits_equal(f32(rmin), run_lo, "run_min")
+    assert_bits_equal(f32(rmax), run_hi, "run_max")

@@ -47,6 +47,8 @@ CAL_BYTES = 2 * math.prod(CAL_SHAPE)                            # per batch, bf1
 QUANT_BYTES = QB * H * QS * (2 * (DN + DR) + DN + 2 * DR)       # 640 B per (token, head)
 DEC_BYTES = QB * H * QS * (DN + 2 * DR + 2 * DV) + QB * H * (2 * (DN + DR) + 4 * DV)  # 512 B per (b,h,t) + q + out
 COPY_BYTES = 1 << 30  # device-to-device copy reference (read + write of 1 GiB each)
+LONG_SHAPE = (2, H, 16384, 128)  # long-context calibration tensor
+LONG_RATIOS = (0.999, 0.9999, 0.99999)
 
 # kernel -> the sources its code comes from (the committed counter summary names their hash)
 KERNEL_SOURCES = {
@@ -393,6 +395,36 @@ def main() -> int:
         "cache_gbs": lat_bytes / (lt_ms * 1e-3) / 1e9,
         "note": "shared-latent MLA cache, B=64 H=128 T=4096 Dl=512 Dr=64, MFMA bf16 (outside the step)"}
     del lat_c, lat_r, lat_q, lat_out, lat_ws
+
+    # Long context, outside the step.  Calibration of one (2,128,16384,128) bf16 tensor
+    # (Student-t(3) tails, 1e-4 outliers at +-60 sigma) at each of the three ratios, one
+    # fa3q_calibrate_perhead call each; then decode with B=8, T=32768 over the step's cache
+    # bytes read as 8 sequences of 32768 tokens (the same 17.2 GB; the split path).
+    long_x = synth.activations(LONG_SHAPE, synth.head_sigmas(H, seed=77), law="t3", outlier_frac=1e-4,
+                               outlier_mult=60.0, dtype=torch.bfloat16, seed=501, device=dev)
+    long_ws = torch.empty(max(fa.fa3q_calibrate_workspace_bytes(torch.bfloat16, *LONG_SHAPE, r) for r in LONG_RATIOS),
+                          dtype=torch.uint8, device=dev)
+    long_min = torch.empty(H, dtype=torch.float32, device=dev)
+    long_max = torch.empty(H, dtype=torch.float32, device=dev)
+    long_bytes = 2 * math.prod(LONG_SHAPE)
+    for r in LONG_RATIOS:
+        n = LONG_SHAPE[0] * LONG_SHAPE[2] * LONG_SHAPE[3]
+        c_ms = timed(lambda: fa.fa3q_calibrate_perhead(long_x, r, long_min, long_max, long_ws, stream=stream))
+        breakdown[f"calibrate_long_{r}"] = {
+            "ms": c_ms, "gbs": long_bytes / (c_ms * 1e-3) / 1e9,
+            "frac_hbm": long_bytes / (c_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "K": n - int(r * n) + 1,
+            "note": f"one (2,128,16384,128) bf16 tensor at ratio {r} (outside the step)"}
+    del long_x, long_ws
+    LB, LT = 8, QB * QS // 8
+    long_dec_bytes = LB * H * LT * (DN + 2 * DR + 2 * DV) + LB * H * (2 * (DN + DR) + 4 * DV)
+    ld_ws = torch.empty(max(1, fa.fa3q_decode_attn_workspace_bytes(LB, H, LT, DV)), dtype=torch.uint8, device=dev)
+    kq_l, kr_l, v_l = kq.view(LB, H, LT, DN), kr.view(LB, H, LT, DR), v.view(LB, H, LT, DV)
+    q_l, out_l = q[:LB], out[:LB]
+    ld_ms = timed(lambda: fa.fa3q_decode_attn(q_l, kq_l, scale, kr_l, v_l, sm, out_l, ld_ws, stream=stream))
+    breakdown["decode_long"] = {"ms": ld_ms, "kv_gbs": long_dec_bytes / (ld_ms * 1e-3) / 1e9,
+                                "frac_hbm": long_dec_bytes / (ld_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                "note": "B=8 H=128 T=32768 Dv=128, split over the tokens (outside the step)"}
+    del ld_ws
 
     # device-to-device copy of COPY_BYTES: a reference ceiling for read+write streaming, and the
     # known-size kernel the HBM byte counters are scaled by

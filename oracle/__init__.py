@@ -34,7 +34,7 @@ from .recall_window import (
     init_running,
     qparams,
 )
-from .quant import quantize_k, dequantize_k_nope
+from .quant import quantize_k, dequantize_k_nope, fake_quant
 from .attention import (attention_fp64, decode_attn, decode_append_attn, decode_attn_qkv8, decode_attn_asym,
                         decode_attn_latent)
 from .asym import params_to_f32, quantize_asym, dequantize_asym
@@ -54,6 +54,7 @@ __all__ = [
     "qparams",
     "quantize_k",
     "dequantize_k_nope",
+    "fake_quant",
     "attention_fp64",
     "decode_attn",
     "decode_append_attn",

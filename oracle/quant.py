@@ -15,6 +15,14 @@ The pages print no quantisation formula.  Readings (also in the design doc):
 * Q3 a head whose scale is 0 gets code 0 everywhere.
 * Q4 the first ``Dn`` features of a K row are the non-RoPE part and the last
   ``Dr`` the RoPE part; the RoPE part is copied bit for bit, per head.
+
+Fake quantisation (msModelSlim page "FA3量化", section 原理 -> 伪量化部署阶段: the
+observer is replaced by a quantisation node built from the symmetric per-head
+parameters).  The page gives no formula for the node; reading:
+
+* F1 the node quantises as above and returns each code's value in the input's
+  dtype: ``round_to_bf16(fl32(code * scale))``, one correctly rounded float32
+  product, then round-half-to-even to bf16; the RoPE part passes unchanged.
 """
 from __future__ import annotations
 
@@ -22,7 +30,7 @@ from typing import Tuple
 
 import numpy as np
 
-from .floats import bf16_bits_to_f32
+from .floats import bf16_bits_to_f32, f32_to_bf16_bits_rne
 
 
 def quantize_k(k_bits, scale, Dn: int) -> Tuple[np.ndarray, np.ndarray]:
@@ -44,6 +52,17 @@ def quantize_k(k_bits, scale, Dn: int) -> Tuple[np.ndarray, np.ndarray]:
     code = np.where(s == np.float32(0.0), 0.0, code)       # Q3
     rope = k_bits[..., Dn:].copy()                          # Q4: bitwise copy
     return code.astype(np.int8), rope
+
+
+def fake_quant(x_bits, scale, Dn: int) -> np.ndarray:
+    """Quantise then dequantise the first ``Dn`` features of a bf16 ``(B, H, S, Dn + Dr)``
+    tensor per head (F1); returns bf16 patterns of the same shape."""
+    codes, rope = quantize_k(x_bits, scale, Dn)
+    H = codes.shape[1]
+    s = np.asarray(scale, dtype=np.float32).reshape(1, H, 1, 1)
+    with np.errstate(over="ignore"):
+        value = codes.astype(np.float32) * s                 # float32 product, correctly rounded
+    return np.concatenate([f32_to_bf16_bits_rne(value), rope], axis=-1)
 
 
 def dequantize_k_nope(codes, scale) -> np.ndarray:

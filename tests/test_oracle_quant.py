@@ -241,3 +241,102 @@ def test_asym_decode_is_attention_over_dequantised_cache():
     tab = np.repeat(scale[:, :1], Dn, axis=1)
     np.testing.assert_allclose(oracle.decode_attn_asym(q, codes, tab, np.zeros((H, Dn), np.uint16), rope, v, sm),
                                oracle.decode_attn(q, codes, s_head, rope, v, sm), rtol=1e-14, atol=0)
+
+
+# ----------------------------------------------------------------------------- fake quantisation
+# msModelSlim page "FA3量化", 原理 -> 伪量化部署阶段: the observer becomes a quantisation node
+# built from the symmetric per-head parameters; reading F1: each code's value scale * code,
+# one float32 product, rounded to bf16.  Checked against exact rationals rounded by hand,
+# hand values, and the invariants any quantise-dequantise pair must keep.
+
+
+def _round_sig(q: Fraction, p: int) -> Fraction:
+    """q rounded to p significant bits, ties to even (normal range, no overflow)."""
+    if q == 0:
+        return Fraction(0)
+    sign = -1 if q < 0 else 1
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    unit = Fraction(2) ** (e - p + 1)
+    n, rem = divmod(a, unit)
+    n = int(n)
+    if rem > unit / 2 or (rem == unit / 2 and n % 2 == 1):
+        n += 1
+    return sign * n * unit
+
+
+def _fake_value(x: float, s: float) -> float:
+    c = _code(x, s)
+    return float(_round_sig(_round_sig(Fraction(c) * Fraction(s), 24), 8))
+
+
+def test_fake_quant_hand_values():
+    # scale 0.25: quotients 2, 4, -11, 400 (-> 127), 1.5 (-> 2), 2.5 (-> 2), -1.5 (-> -2), -127.5 (-> -127)
+    x = np.array([0.5, 1.0, -2.75, 100.0, 0.375, 0.625, -0.375, -31.875] * 2, np.float32)
+    k = _bits16(x).reshape(1, 1, 1, 16)
+    got = oracle.bf16_bits_to_f32(oracle.fake_quant(k, np.array([0.25], np.float32), 16)).reshape(-1)
+    want = np.array([0.5, 1.0, -2.75, 31.75, 0.5, 0.5, -0.5, -31.75] * 2, np.float32)
+    np.testing.assert_array_equal(got, want)
+    # scale fl32(0.01): 5.0 saturates to 127 * s = 1.26999997..., whose nearest bf16 is 1.2734375
+    y = oracle.bf16_bits_to_f32(oracle.fake_quant(_bits16(np.full(16, 5.0, np.float32)).reshape(1, 1, 1, 16),
+                                                  np.array([0.01], np.float32), 16))
+    assert np.all(y == np.float32(1.2734375))
+
+
+def test_fake_quant_matches_exact_double_rounding():
+    rng = np.random.default_rng(31)
+    B, H, S, Dn, Dr = 1, 4, 24, 16, 8
+    sigma = np.exp(rng.uniform(-3, 3, size=H)).astype(np.float32)
+    k = _random_k(rng, B, H, S, Dn, Dr, sigma)
+    scale = (sigma * np.exp(rng.uniform(0.0, 2.0, size=H)) / 127).astype(np.float32)  # arbitrary float32 scales
+    y = oracle.fake_quant(k, scale, Dn)
+    assert y.shape == k.shape and y.dtype == np.uint16
+    ys = oracle.bf16_bits_to_f32(y[..., :Dn])
+    xs = oracle.bf16_bits_to_f32(k[..., :Dn])
+    for idx in np.ndindex(ys.shape):
+        assert ys[idx] == _fake_value(float(xs[idx]), float(scale[idx[1]])), idx
+    np.testing.assert_array_equal(y[..., Dn:], k[..., Dn:])
+
+
+def test_fake_quant_is_idempotent_and_monotone():
+    # bf16 rounding moves scale * code by at most half an ulp, 2^-8 of itself: under
+    # 127 * 2^-8 < 0.4961 scale for |code| <= 127 (plus float32 rounding far below the
+    # remaining margin), so quantising a fake-quantised value returns the same code and value
+    rng = np.random.default_rng(32)
+    H, S, Dn = 6, 200, 32
+    sigma = np.exp(rng.uniform(-4, 4, size=H)).astype(np.float32)
+    k = _random_k(rng, 1, H, S, Dn, 0, sigma)
+    scale = (sigma * np.exp(rng.uniform(-1.0, 2.0, size=H)) / 127).astype(np.float32)
+    y = oracle.fake_quant(k, scale, Dn)
+    np.testing.assert_array_equal(oracle.fake_quant(y, scale, Dn), y)
+    xs = oracle.bf16_bits_to_f32(k).astype(np.float64)
+    ys = oracle.bf16_bits_to_f32(y).astype(np.float64)
+    for h in range(H):
+        order = np.argsort(xs[0, h].reshape(-1), kind="stable")
+        assert np.all(np.diff(ys[0, h].reshape(-1)[order]) >= 0), h
+
+
+def test_fake_quant_error_bound_saturation_zero_scale():
+    rng = np.random.default_rng(33)
+    H, S, Dn, Dr = 4, 256, 16, 8
+    sigma = np.ones(H, np.float32)
+    k = _random_k(rng, 1, H, S, Dn, Dr, sigma)
+    scale = np.array([0.02, 0.005, 0.0, 1.0 / 127], np.float32)  # head 2 has an empty range
+    y = oracle.fake_quant(k, scale, Dn)
+    xs = oracle.bf16_bits_to_f32(k[..., :Dn]).astype(np.float64)
+    ys = oracle.bf16_bits_to_f32(y[..., :Dn]).astype(np.float64)
+    for h in (0, 1, 3):
+        s = float(scale[h])
+        x, v = xs[0, h], ys[0, h]
+        inside = np.abs(x) <= 127 * s
+        assert np.all(np.abs(v[inside] - x[inside]) <= 0.5 * s * (1 + 1e-6) + np.abs(v[inside]) * 2.0 ** -8)
+        top = float(oracle.bf16_bits_to_f32(oracle.f32_to_bf16_bits_rne(np.float32(127) * np.float32(s))).reshape(-1)[0])
+        out = np.abs(x) >= 127.5 * s * (1 + 1e-6)
+        assert out.any() or h == 3
+        np.testing.assert_array_equal(v[out], np.sign(x[out]) * top)
+    assert np.all(y[0, 2, :, :Dn] == 0)                           # +0 everywhere
+    np.testing.assert_array_equal(y[..., Dn:], k[..., Dn:])       # RoPE part unchanged

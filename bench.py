@@ -372,6 +372,23 @@ def main() -> int:
                                 "note": "attention over the asymmetric K-nope cache (outside the step)"}
     del akq, akr
 
+    # Fake quantisation of the same K (quantise, dequantise back to bf16; the RoPE part copied):
+    # out of place (768 B per (token, head)), then in place on the result (512 B: the RoPE part
+    # is neither read nor written; the operation is idempotent, so every call does the same
+    # work); outside the step.
+    fq_y = torch.empty_like(k)
+    fq_ms = timed(lambda: fa.fa3q_fake_quant(k, scale, DN, fq_y, stream=stream))
+    fqi_ms = timed(lambda: fa.fa3q_fake_quant(fq_y, scale, DN, fq_y, stream=stream))
+    fq_bytes = QB * H * QS * 4 * (DN + DR)
+    fqi_bytes = QB * H * QS * 4 * DN
+    breakdown["fake_quant"] = {"ms": fq_ms, "gbs": fq_bytes / (fq_ms * 1e-3) / 1e9,
+                               "frac_hbm": fq_bytes / (fq_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                               "note": "K (64,128,4096,128+64) bf16 -> bf16, out of place (outside the step)"}
+    breakdown["fake_quant_in_place"] = {"ms": fqi_ms, "gbs": fqi_bytes / (fqi_ms * 1e-3) / 1e9,
+                                        "frac_hbm": fqi_bytes / (fqi_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                        "note": "the same in place: only the non-RoPE part is touched"}
+    del fq_y
+
     # Shared-latent (absorbed MLA) cache, the same sequences: per token one latent row of
     # 512 features (+ 64 RoPE) shared by all 128 heads, built by the library's own path with
     # one head (calibration, scale, quantisation), then fa3q_decode_latent; outside the step.

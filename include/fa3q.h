@@ -20,6 +20,8 @@
  *  10. fa3q_decode_latent      -- attention of every head of a sequence over one shared-latent
  *      (absorbed MLA) cache: INT8 latent (one scale) + bf16 RoPE part, on the matrix cores
  *  11. fa3q_calibrate_batches  -- 1 and 2 over several calibration batches in one call
+ *  12. fa3q_fake_quant         -- quantise and dequantise (the codes of 4 turned back into bf16),
+ *      in place or into a second buffer
  *
  * Sources, cited by page title and section:
  *   [MS] msModelSlim documentation, "FA3量化：Flash Attention 3激活量化算法说明"
@@ -42,7 +44,8 @@
  *   - bf16 tensors are passed as their raw 16-bit patterns (uint16_t).
  *   - Inputs must be finite; for NaN/Inf inputs the outputs are unspecified
  *     (the kernels stay inside their buffers for any input bits).
- *   - Outputs must not overlap inputs, except the in/out running statistics.
+ *   - Outputs must not overlap inputs, except the in/out running statistics and
+ *     fa3q_fake_quant's in-place form.
  *   - Concurrent calls on different streams are safe if they use distinct
  *     output and workspace buffers.
  */
@@ -65,7 +68,8 @@ typedef enum fa3q_status {
   FA3Q_ERR_ALIGN = 5,       /* a pointer is not aligned as documented */
   FA3Q_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than the *_workspace_bytes query */
   FA3Q_ERR_HIP = 7,         /* the HIP runtime rejected a launch */
-  FA3Q_ERR_UNSUPPORTED = 8  /* valid arguments outside what this build handles (see each call) */
+  FA3Q_ERR_UNSUPPORTED = 8, /* valid arguments outside what this build handles (see each call) */
+  FA3Q_ERR_ALIAS = 9        /* an output partly overlaps an input (where exact aliasing is allowed) */
 } fa3q_status;
 
 typedef enum fa3q_dtype {
@@ -403,6 +407,31 @@ size_t fa3q_decode_latent_workspace_bytes(int64_t B, int64_t H, int64_t T, int64
 int fa3q_decode_latent(const uint16_t* q, const int8_t* c_q, const float* scale, const uint16_t* k_rope,
                        int64_t B, int64_t H, int64_t T, int64_t Dl, int64_t Dr, float sm_scale, float* out,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* 12. Fake quantisation (quantise, then dequantise)                         */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * [MS] 原理 -> 伪量化部署阶段 (fake-quantisation deployment stage): after calibration
+ * the per-head min/max give the symmetric parameters and the observer is replaced by
+ * a quantisation node.  The page gives no formula for that node; this is the plain
+ * reading, the code of fa3q_quantize_k turned back into a bf16 value:
+ *   y[b,h,s,d]    = round_half_even_to_bf16( fl32( code * scale[h] ) ),  d < Dn
+ *                   code = clamp(round_half_even(fl32(x / scale[h])), -127, 127) exactly as
+ *                   fa3q_quantize_k (0 when scale[h] == 0, so y = +0)
+ *   y[b,h,s,Dn+j] = x[b,h,s,Dn+j] bit for bit,  j < Dr
+ * The float32 product is correctly rounded, then rounded once more to bf16.
+ *
+ *   x       device bf16 (B,H,S,Dn+Dr) contiguous, 16-byte aligned.
+ *   scale   device float32 [H], 4-byte aligned; finite and >= 0 (as fa3q_qparams gives).
+ *   y       device bf16 (B,H,S,Dn+Dr) contiguous, 16-byte aligned: either x itself (in
+ *           place; the RoPE part is then neither read nor written) or memory that does
+ *           not overlap x (FA3Q_ERR_ALIAS otherwise).
+ *   B,H,S > 0; Dn > 0 multiple of 16, Dn <= 4096; Dr >= 0 multiple of 8, Dr <= 2048.
+ */
+int fa3q_fake_quant(const uint16_t* x, const float* scale, uint16_t* y, int64_t B, int64_t H, int64_t S,
+                    int64_t Dn, int64_t Dr, void* stream);
 
 #ifdef __cplusplus
 }

@@ -25,6 +25,7 @@ FA3Q_ERR_ALIGN = 5
 FA3Q_ERR_WORKSPACE = 6
 FA3Q_ERR_HIP = 7
 FA3Q_ERR_UNSUPPORTED = 8
+FA3Q_ERR_ALIAS = 9
 
 FA3Q_F32 = 0
 FA3Q_BF16 = 1
@@ -54,6 +55,7 @@ SIGNATURES = {
     "fa3q_decode_attn_qkv8": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
                                      ctypes.c_float, _vp, _vp, _sz, _vp]),
     "fa3q_quantize_asym": (_int, [_vp, _vp, _vp, _int, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp]),
+    "fa3q_fake_quant": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp]),
     "fa3q_decode_attn_asym": (_int, [_vp, _vp, _vp, _vp, _int, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
                                      ctypes.c_float, _vp, _vp, _sz, _vp]),
     "fa3q_decode_latent_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),

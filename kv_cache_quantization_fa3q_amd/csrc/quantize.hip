@@ -69,12 +69,11 @@ __device__ __forceinline__ int code_exact(float x, float s) {
   return static_cast<int>(y);
 }
 
-// 8 bf16 (one 16-byte vector) -> 8 codes in two dwords (little-endian element order).
-__device__ __forceinline__ u32x2 quant8(const u32x4& w, float s, float r, bool fast) {
+// 8 bf16 (one 16-byte vector) -> their 8 codes.
+__device__ __forceinline__ void codes8(const u32x4& w, float s, float r, bool fast, int (&c)[8]) {
   float xv[8];
   xv[0] = bf16_lo(w.x); xv[1] = bf16_hi(w.x); xv[2] = bf16_lo(w.y); xv[3] = bf16_hi(w.y);
   xv[4] = bf16_lo(w.z); xv[5] = bf16_hi(w.z); xv[6] = bf16_lo(w.w); xv[7] = bf16_hi(w.w);
-  int c[8];
   bool amb = !fast;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -89,10 +88,26 @@ __device__ __forceinline__ u32x2 quant8(const u32x4& w, float s, float r, bool f
       for (int i = 0; i < 8; ++i) c[i] = code_exact(xv[i], s);
     }
   }
+}
+
+// 8 bf16 -> 8 codes in two dwords (little-endian element order).
+__device__ __forceinline__ u32x2 quant8(const u32x4& w, float s, float r, bool fast) {
+  int c[8];
+  codes8(w, s, r, fast, c);
   u32x2 o;
   o.x = (c[0] & 0xff) | ((c[1] & 0xff) << 8) | ((c[2] & 0xff) << 16) | (static_cast<uint32_t>(c[3]) << 24);
   o.y = (c[4] & 0xff) | ((c[5] & 0xff) << 8) | ((c[6] & 0xff) << 16) | (static_cast<uint32_t>(c[7]) << 24);
   return o;
+}
+
+// 8 bf16 -> the bf16 values of their codes: round_half_even_to_bf16(fl32(code * s)).
+__device__ __forceinline__ u32x4 fake8(const u32x4& w, float s, float r, bool fast) {
+  int c[8];
+  codes8(w, s, r, fast, c);
+  uint32_t h[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) h[i] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(__fmul_rn(static_cast<float>(c[i]), s)));
+  return u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
 }
 
 // UN / UR: 8-element units per nope / rope row when known at compile time (0: runtime).
@@ -157,6 +172,83 @@ __global__ __launch_bounds__(kThreads) void quantize_k_kernel(QuantArgs a) {
 #pragma unroll
         for (int j = 0; j < kRope; ++j)
           if (orr[j] >= 0) __builtin_nontemporal_store(xr[j], reinterpret_cast<u32x4*>(rout + orr[j]));
+      }
+    }
+  }
+}
+
+struct FakeArgs {
+  const uint16_t* x;
+  const float* scale;
+  uint16_t* y;
+  int64_t S;
+  int64_t items;
+  int32_t chunks_per_bh;
+  int32_t H;
+  int32_t Dn;
+  int32_t Dr;
+  int32_t copy_rope;  // 0 when y is x: the RoPE part is already in place
+};
+
+// Fake quantisation: the same items, loads and code decision as quantize_k_kernel; the
+// codes are turned back into bf16 values (scale[h] * code) and written over a copy of the
+// row layout, the RoPE part copied unchanged.
+template <int UN, int UR>
+__global__ __launch_bounds__(kThreads) void fake_quant_kernel(FakeArgs a) {
+  const int tid = static_cast<int>(threadIdx.x);
+  const int Dk = a.Dn + a.Dr;
+  const int Un = UN ? UN : a.Dn >> 3;
+  const int Ur = a.copy_rope ? (UR ? UR : a.Dr >> 3) : 0;
+  constexpr int kNope = UN ? kRowsPerItem * UN / kThreads : 4;
+  constexpr int kRope = UR ? (kRowsPerItem * UR + kThreads - 1) / kThreads : 2;
+
+  for (int64_t item = blockIdx.x; item < a.items; item += gridDim.x) {
+    const int64_t bh = item / a.chunks_per_bh;
+    const int64_t chunk = item - bh * a.chunks_per_bh;
+    const int hh = __builtin_amdgcn_readfirstlane(static_cast<int>(bh % a.H));
+    const int64_t r_begin = chunk * kRowsPerItem;
+    const int nr = static_cast<int>(min(static_cast<int64_t>(kRowsPerItem), a.S - r_begin));
+    const int64_t row0 = bh * a.S + r_begin;
+    const uint16_t* xin = a.x + row0 * Dk;  // may be the same memory as yout (in place)
+    uint16_t* yout = a.y + row0 * Dk;
+    const int nn = nr * Un, nrp = nr * Ur;
+
+    for (int pass = 0; pass * kThreads * kNope < nn || pass * kThreads * kRope < nrp; ++pass) {
+      u32x4 xn[kNope], xr[kRope];
+      int on[kNope], orr[kRope];
+#pragma unroll
+      for (int j = 0; j < kNope; ++j) {
+        const int q = (pass * kNope + j) * kThreads + tid;
+        const int qc = min(q, nn - 1);
+        const int row = qc / Un, unit = qc - row * Un;
+        on[j] = q < nn ? row * Dk + unit * 8 : -1;
+        xn[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xin + static_cast<int64_t>(row) * Dk + unit * 8));
+      }
+      if (Ur > 0) {
+#pragma unroll
+        for (int j = 0; j < kRope; ++j) {
+          const int q = (pass * kRope + j) * kThreads + tid;
+          const int qc = min(q, nrp - 1);
+          const int row = qc / Ur, unit = qc - row * Ur;
+          orr[j] = q < nrp ? row * Dk + a.Dn + unit * 8 : -1;
+          xr[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xin + static_cast<int64_t>(row) * Dk + a.Dn + unit * 8));
+        }
+      }
+      const float s = a.scale[hh];
+      const bool zero = (s == 0.0f);
+      const bool fast = fabsf(s) >= 0x1p-100f && fabsf(s) <= 0x1p100f;
+      const float r = 1.0f / s;
+#pragma unroll
+      for (int j = 0; j < kNope; ++j) {
+        if (on[j] >= 0) {
+          const u32x4 o = zero ? u32x4{0u, 0u, 0u, 0u} : fake8(xn[j], s, r, fast);
+          __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(yout + on[j]));
+        }
+      }
+      if (Ur > 0) {
+#pragma unroll
+        for (int j = 0; j < kRope; ++j)
+          if (orr[j] >= 0) __builtin_nontemporal_store(xr[j], reinterpret_cast<u32x4*>(yout + orr[j]));
       }
     }
   }
@@ -355,6 +447,42 @@ extern "C" int fa3q_quantize_k(const uint16_t* k, const float* scale, int8_t* k_
     hipLaunchKernelGGL((quantize_k_kernel<16, 8>), g, blk, 0, as_stream(stream), a);
   else
     hipLaunchKernelGGL((quantize_k_kernel<0, 0>), g, blk, 0, as_stream(stream), a);
+  return launch_status();
+}
+
+extern "C" int fa3q_fake_quant(const uint16_t* x, const float* scale, uint16_t* y, int64_t B, int64_t H,
+                               int64_t S, int64_t Dn, int64_t Dr, void* stream) {
+  if (!x || !scale || !y) return FA3Q_ERR_NULL;
+  if (B <= 0 || H <= 0 || S <= 0) return FA3Q_ERR_SHAPE;
+  if (Dn <= 0 || Dn % 16 != 0 || Dn > 4096) return FA3Q_ERR_SHAPE;
+  if (Dr < 0 || Dr % 8 != 0 || Dr > 2048) return FA3Q_ERR_SHAPE;
+  if (B > (int64_t{1} << 31) / H) return FA3Q_ERR_SHAPE;
+  const int64_t chunks = (S + kRowsPerItem - 1) / kRowsPerItem;
+  if (chunks > (int64_t{1} << 30) || B * H > (int64_t{1} << 62) / (chunks * kRowsPerItem * (Dn + Dr)))
+    return FA3Q_ERR_SHAPE;
+  if (!is_aligned(x, 16) || !is_aligned(y, 16) || !is_aligned(scale, 4)) return FA3Q_ERR_ALIGN;
+  // y is x (in place) or does not overlap it
+  const size_t bytes = static_cast<size_t>(B * H * S * (Dn + Dr)) * 2;
+  const uintptr_t xb = reinterpret_cast<uintptr_t>(x), yb = reinterpret_cast<uintptr_t>(y);
+  if (xb != yb && xb < yb + bytes && yb < xb + bytes) return FA3Q_ERR_ALIAS;
+
+  FakeArgs a;
+  a.x = x;
+  a.scale = scale;
+  a.y = y;
+  a.S = S;
+  a.chunks_per_bh = static_cast<int32_t>(chunks);
+  a.items = B * H * chunks;
+  a.H = static_cast<int32_t>(H);
+  a.Dn = static_cast<int32_t>(Dn);
+  a.Dr = static_cast<int32_t>(Dr);
+  a.copy_rope = xb != yb ? 1 : 0;
+  const int64_t grid = std::min<int64_t>(a.items, kMaxGrid);
+  const dim3 g(static_cast<unsigned>(grid)), blk(kThreads);
+  if (Dn == 128 && Dr == 64)
+    hipLaunchKernelGGL((fake_quant_kernel<16, 8>), g, blk, 0, as_stream(stream), a);
+  else
+    hipLaunchKernelGGL((fake_quant_kernel<0, 0>), g, blk, 0, as_stream(stream), a);
   return launch_status();
 }
 

@@ -189,6 +189,23 @@ def fa3q_quantize_k(k: torch.Tensor, scale: torch.Tensor, Dn: int, k_nope_q: Opt
     return k_nope_q, k_rope
 
 
+def fa3q_fake_quant(x: torch.Tensor, scale: torch.Tensor, Dn: int, y: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """bf16 ``x (B,H,S,Dn+Dr)`` -> bf16 ``y``: the first Dn features quantised and dequantised
+    per head, the rest copied.  ``y`` may be ``x`` itself (in place)."""
+    if x.dim() != 4 or x.dtype != torch.bfloat16:
+        raise ValueError("x must be bfloat16 (B, H, S, Dn + Dr)")
+    B, H, S, Dk = (int(v) for v in x.shape)
+    if y is None:
+        y = torch.empty_like(x)
+    if y.shape != x.shape or y.dtype != torch.bfloat16:
+        raise ValueError("y must be bfloat16 with x's shape")
+    _need_gpu("fa3q_fake_quant", x, scale, y)
+    _check(lib().fa3q_fake_quant(_ptr(x), _ptr(scale), _ptr(y), B, H, S, int(Dn), Dk - int(Dn), _stream(stream)),
+           "fa3q_fake_quant")
+    return y
+
+
 # --------------------------------------------------------------------------- decode
 
 

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_function():
 def test_version_and_status_strings():
     lib = fa.lib()
     assert lib.fa3q_version() >> 16 == 1
-    for code in range(9):
+    for code in range(10):
         s = fa.status_string(code)
         assert s.startswith("FA3Q_")
     assert fa.status_string(0) == "FA3Q_OK"
@@ -222,6 +222,30 @@ def test_decode_qkv8_rejections():
     assert call(vq=_p(8)) == L.FA3Q_ERR_ALIGN
     assert call(sv=_p(2)) == L.FA3Q_ERR_ALIGN
     assert call(ws=None) == L.FA3Q_ERR_WORKSPACE
+
+@no_gpu_only
+def test_fake_quant_rejections():
+    f = fa.lib().fa3q_fake_quant
+    ok = dict(x=_p(), s=_p(), y=_p(1 << 20), B=1, H=4, S=64, Dn=32, Dr=16)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["x"], a["s"], a["y"], a["B"], a["H"], a["S"], a["Dn"], a["Dr"], None)
+
+    for name in ("x", "s", "y"):
+        assert call(**{name: None}) == L.FA3Q_ERR_NULL, name
+    assert call(B=0) == L.FA3Q_ERR_SHAPE
+    assert call(Dn=24) == L.FA3Q_ERR_SHAPE
+    assert call(Dr=12) == L.FA3Q_ERR_SHAPE
+    assert call(x=_p(8)) == L.FA3Q_ERR_ALIGN
+    assert call(y=_p(8)) == L.FA3Q_ERR_ALIGN
+    assert call(s=_p(2)) == L.FA3Q_ERR_ALIGN
+    # 4 * 64 rows of 48 bf16 = 24 KiB: y starting 16 bytes in (or ending 16 bytes in) overlaps x
+    assert call(y=_p(16)) == L.FA3Q_ERR_ALIAS
+    assert call(x=_p(16), y=_p()) == L.FA3Q_ERR_ALIAS
+    assert call(y=_p(24576 - 16)) == L.FA3Q_ERR_ALIAS
+    assert fa.status_string(L.FA3Q_ERR_ALIAS).startswith("FA3Q_ERR_ALIAS")
+
 
 @no_gpu_only
 def test_quantize_asym_rejections():

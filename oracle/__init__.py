@@ -35,8 +35,8 @@ from .recall_window import (
     qparams,
 )
 from .quant import quantize_k, dequantize_k_nope, fake_quant
-from .attention import (attention_fp64, decode_attn, decode_append_attn, decode_attn_qkv8, decode_attn_asym,
-                        decode_attn_latent)
+from .attention import (attention_fp64, decode_attn, decode_append_attn, decode_paged_attn, decode_attn_qkv8,
+                        decode_attn_asym, decode_attn_latent)
 from .asym import params_to_f32, quantize_asym, dequantize_asym
 
 __all__ = [
@@ -58,6 +58,7 @@ __all__ = [
     "attention_fp64",
     "decode_attn",
     "decode_append_attn",
+    "decode_paged_attn",
     "decode_attn_qkv8",
     "decode_attn_latent",
     "decode_attn_asym",

@@ -91,6 +91,60 @@ def decode_append_attn(q_bits, k_new_bits, v_new_bits, scale, codes, rope_bits, 
     return out, codes, rope_bits, v_bits
 
 
+def decode_paged_attn(q_bits, k_new_bits, v_new_bits, scale, code_pool, rope_pool, v_pool, block_table, kv_len,
+                      sm_scale: float, Dn: int):
+    """:func:`decode_append_attn` over a paged cache.
+
+    Reading P1 (also in the design doc): each cache is a pool of pages of ``P`` tokens laid
+    out ``(num_pages, H, P, .)``; logical token ``t`` of sequence ``b`` is row ``t % P`` of
+    physical page ``block_table[b, t // P]``.  The step reads the rows of tokens
+    ``0 .. n-1`` (``n = kv_len[b] + 1`` with a new token, else ``kv_len[b]``), and the new
+    token's rows are written at position ``kv_len[b]``.  Sequences are taken in order; an
+    append into a page that another sequence reads is outside the reading (the steps of
+    different sequences are independent).
+
+    Returns ``(out (B,H,Dv) float64, code_pool, rope_pool, v_pool)`` after the step
+    (copies; the inputs are not modified).
+    """
+    code_pool = np.array(code_pool, dtype=np.int8, copy=True)
+    rope_pool = np.array(rope_pool, dtype=np.uint16, copy=True)
+    v_pool = np.array(v_pool, dtype=np.uint16, copy=True)
+    NP, H, P, _ = code_pool.shape
+    block_table = np.asarray(block_table, dtype=np.int64)
+    B, MP = block_table.shape
+    T = MP * P
+    kv_len = np.asarray(kv_len, dtype=np.int64).reshape(B)
+    Dv = v_pool.shape[-1]
+    out = np.zeros((B, H, Dv), dtype=np.float64)
+    for b in range(B):
+        p = int(kv_len[b])
+        if k_new_bits is not None:
+            if not 0 <= p < T:
+                raise ValueError("appending needs 0 <= kv_len[b] < T")
+            n = p + 1
+        else:
+            if not 1 <= p <= T:
+                raise ValueError("attention needs 1 <= kv_len[b] <= T")
+            n = p
+        pages = block_table[b, :(n + P - 1) // P]
+        if np.any(pages < 0) or np.any(pages >= NP):
+            raise ValueError("block table entry outside the pool")
+        if k_new_bits is not None:
+            new_codes, new_rope = quantize_k(np.asarray(k_new_bits, dtype=np.uint16)[b][None, :, None, :], scale, Dn)
+            pg, row = block_table[b, p // P], p % P
+            code_pool[pg, :, row, :] = new_codes[0, :, 0, :]
+            rope_pool[pg, :, row, :] = new_rope[0, :, 0, :]
+            v_pool[pg, :, row, :] = np.asarray(v_new_bits, dtype=np.uint16)[b]
+        # the sequence's first n tokens, in logical order: (H, n, .)
+        t = np.arange(n)
+        pg, row = block_table[b, t // P], t % P
+        codes = code_pool[pg, :, row, :].transpose(1, 0, 2)
+        rope = rope_pool[pg, :, row, :].transpose(1, 0, 2)
+        vals = v_pool[pg, :, row, :].transpose(1, 0, 2)
+        out[b] = decode_attn(np.asarray(q_bits)[b:b + 1], codes[None], scale, rope[None], vals[None], sm_scale)[0]
+    return out, code_pool, rope_pool, v_pool
+
+
 def decode_attn_qkv8(q_codes, q_rope_bits, scale_q, k_codes, scale_k, k_rope_bits, v_codes, scale_v,
                      sm_scale: float) -> np.ndarray:
     """Attention with Q, K and V all per-head INT8 (the RoPE parts of Q and K in bf16).

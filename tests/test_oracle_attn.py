@@ -197,6 +197,85 @@ def test_append_validates_lengths():
         oracle.decode_append_attn(qb, None, None, scale, codes, rope, vb, np.array([0], np.int32), 1.0, Dn)
 
 
+# ----------------------------------------------------------------------------- paged cache
+
+
+def _scatter_pages(cache, page_of, NP, P):
+    """(B,H,T,D) contiguous cache -> (NP,H,P,D) pool with logical page j of sequence b at
+    physical page page_of[b][j]; pages nobody owns hold a fixed junk pattern."""
+    B, H, T, D = cache.shape
+    pool = np.full((NP, H, P, D), 0x55 if cache.dtype == np.int8 else 0x7F7F, dtype=cache.dtype)
+    for b in range(B):
+        for j in range(T // P):
+            for h in range(H):
+                for r in range(P):
+                    pool[page_of[b][j], h, r] = cache[b, h, j * P + r]
+    return pool
+
+
+def _paged_case(rng, B=3, H=2, P=16, MP=4, Dn=32, Dr=16, Dv=16, NP=None):
+    T = MP * P
+    NP = NP or B * MP + 3
+    k_full, v_full, qb, scale = _step_inputs(rng, B, H, T, Dn, Dr, Dv)
+    codes, rope = oracle.quantize_k(k_full, scale, Dn)
+    page_of = rng.permutation(NP)[:B * MP].reshape(B, MP)
+    return dict(k_full=k_full, v_full=v_full, qb=qb, scale=scale, codes=codes, rope=rope, page_of=page_of, T=T,
+                pools=(_scatter_pages(codes, page_of, NP, P), _scatter_pages(rope, page_of, NP, P),
+                       _scatter_pages(v_full, page_of, NP, P)))
+
+
+def test_paged_step_equals_the_contiguous_step_on_scattered_pages():
+    # the pools are built by a scatter written here, page by page and row by row; the paged
+    # step must give the contiguous step's output, and its appended rows must land where the
+    # scatter of the contiguous step's updated cache puts them
+    rng = np.random.default_rng(51)
+    B, H, P, MP, Dn, Dr, Dv = 3, 2, 16, 4, 32, 16, 16
+    c = _paged_case(rng, B, H, P, MP, Dn, Dr, Dv)
+    NP = c["pools"][0].shape[0]
+    sm = np.float32(1 / math.sqrt(Dn + Dr))
+    for kv_len, append in (([0, 17, 63], True), ([15, 16, 40], True), ([1, 33, 64], False)):
+        kv_len = np.array(kv_len, np.int32)
+        kn = c["k_full"][:, :, 5] if append else None
+        vn = c["v_full"][:, :, 9] if append else None
+        want, c2, r2, v2 = oracle.decode_append_attn(c["qb"], kn, vn, c["scale"], c["codes"], c["rope"],
+                                                     c["v_full"], kv_len, sm, Dn)
+        got, pc, pr, pv = oracle.decode_paged_attn(c["qb"], kn, vn, c["scale"], *c["pools"], c["page_of"], kv_len,
+                                                   sm, Dn)
+        np.testing.assert_allclose(got, want, rtol=1e-13, atol=1e-15)  # float64, summation order aside
+        np.testing.assert_array_equal(pc, _scatter_pages(c2, c["page_of"], NP, P))
+        np.testing.assert_array_equal(pr, _scatter_pages(r2, c["page_of"], NP, P))
+        np.testing.assert_array_equal(pv, _scatter_pages(v2, c["page_of"], NP, P))
+
+
+def test_paged_step_reads_only_the_pages_it_needs():
+    rng = np.random.default_rng(52)
+    B, H, P, MP, Dn, Dr, Dv = 2, 2, 16, 4, 16, 8, 16
+    c = _paged_case(rng, B, H, P, MP, Dn, Dr, Dv)
+    kv_len = np.array([20, 3], np.int32)  # pages 0-1 and page 0
+    out, _, _, _ = oracle.decode_paged_attn(c["qb"], None, None, c["scale"], *c["pools"], c["page_of"], kv_len, 0.3, Dn)
+    # table entries of pages past the length may be anything, even outside the pool
+    bt = c["page_of"].copy()
+    bt[0, 2:] = -7
+    bt[1, 1:] = 10 ** 6
+    out2, _, _, _ = oracle.decode_paged_attn(c["qb"], None, None, c["scale"], *c["pools"], bt, kv_len, 0.3, Dn)
+    np.testing.assert_array_equal(out, out2)
+    with pytest.raises(ValueError):
+        oracle.decode_paged_attn(c["qb"], None, None, c["scale"], *c["pools"], bt, np.array([40, 3], np.int32), 0.3, Dn)
+
+
+def test_paged_sequences_sharing_pages_agree():
+    # two sequences whose block tables name the same pages read the same cache
+    rng = np.random.default_rng(53)
+    B, H, P, MP, Dn, Dr, Dv = 2, 3, 16, 3, 16, 8, 16
+    c = _paged_case(rng, B, H, P, MP, Dn, Dr, Dv)
+    bt = np.stack([c["page_of"][0], c["page_of"][0]])
+    q = c["qb"].copy()
+    q[1] = q[0]
+    out, _, _, _ = oracle.decode_paged_attn(q, None, None, c["scale"], *c["pools"], bt, np.array([37, 37], np.int32),
+                                            0.2, Dn)
+    np.testing.assert_array_equal(out[0], out[1])
+
+
 # ----------------------------------------------------------------------------- Q, K, V all INT8
 
 

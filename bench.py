@@ -443,6 +443,25 @@ def main() -> int:
                                 "note": "B=8 H=128 T=32768 Dv=128, split over the tokens (outside the step)"}
     del ld_ws
 
+    # Paged cache: the step's cache bytes read as pools of 64-token pages (4096 pages of
+    # (H, 64, .)), each sequence's 64 pages scattered by a seeded permutation; attention over
+    # all 4096 tokens of every sequence through the block table; outside the step.
+    PG = 64
+    n_pages = QB * QS // PG
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(700)
+    table = torch.randperm(n_pages, generator=gen).to(torch.int32).view(QB, QS // PG).to(dev)
+    full_len = torch.full((QB,), QS, dtype=torch.int32, device=dev)
+    kq_p, kr_p, v_p = kq.view(n_pages, H, PG, DN), kr.view(n_pages, H, PG, DR), v.view(n_pages, H, PG, DV)
+    pg_ms = timed(lambda: fa.fa3q_decode_paged_attn(q, None, None, scale, kq_p, kr_p, v_p, table, full_len, sm, out,
+                                                    ws_dec, stream=stream))
+    pg_bytes = DEC_BYTES + table.numel() * 4
+    breakdown["decode_paged"] = {"ms": pg_ms, "kv_gbs": pg_bytes / (pg_ms * 1e-3) / 1e9,
+                                 "frac_hbm": pg_bytes / (pg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                 "note": "B=64 H=128 T=4096 in 64-token pages through a permuted block table "
+                                         "(outside the step)"}
+    del table
+
     # device-to-device copy of COPY_BYTES: a reference ceiling for read+write streaming, and the
     # known-size kernel the HBM byte counters are scaled by
     src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)

@@ -22,6 +22,8 @@
  *  11. fa3q_calibrate_batches  -- 1 and 2 over several calibration batches in one call
  *  12. fa3q_fake_quant         -- quantise and dequantise (the codes of 4 turned back into bf16),
  *      in place or into a second buffer
+ *  13. fa3q_decode_paged_attn  -- 6 over a paged cache: pools of fixed-size pages and a block
+ *      table per sequence
  *
  * Sources, cited by page title and section:
  *   [MS] msModelSlim documentation, "FA3量化：Flash Attention 3激活量化算法说明"
@@ -432,6 +434,44 @@ int fa3q_decode_latent(const uint16_t* q, const int8_t* c_q, const float* scale,
  */
 int fa3q_fake_quant(const uint16_t* x, const float* scale, uint16_t* y, int64_t B, int64_t H, int64_t S,
                     int64_t Dn, int64_t Dr, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* 13. Decode step over a paged cache                                        */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * [MI] overview (the INT8 K-nope cache written and read in the decode phase), as
+ * fa3q_decode_append_attn, with the cache held in pages.  The pages leave the cache
+ * layout open; here each of the three caches is a pool of num_pages pages of
+ * page_size (P) tokens, laid out (num_pages, H, P, .) row-major, so one page of one
+ * head is P contiguous rows.  Logical token t of sequence b lives in physical page
+ * block_table[b][t / P] at row t % P.  With T = max_pages * P, the call computes what
+ * fa3q_decode_append_attn computes on the (B,H,T,.) cache that the block table
+ * describes, and the append writes the new rows into the page that holds position
+ * kv_len[b].
+ *
+ *   q, k_new, v_new, scale, sm_scale, out: as fa3q_decode_append_attn.
+ *   k_nope_pool  device int8 (num_pages,H,P,Dn), 16-byte aligned.
+ *   k_rope_pool  device bf16 (num_pages,H,P,Dr), 16-byte aligned; may be NULL iff Dr == 0.
+ *   v_pool       device bf16 (num_pages,H,P,Dv), 16-byte aligned.
+ *   block_table  device int32 [B][max_pages], 4-byte aligned; read on the device.  Only
+ *                the entries of pages that hold tokens 0..kv_len[b] (with an append) or
+ *                0..kv_len[b]-1 are read.  Entries outside [0, num_pages) are clamped
+ *                into it, so the kernels never leave a pool.  A page shared by several
+ *                sequences is read by each; appending into a shared page writes it for all.
+ *   kv_len       device int32 [B], as fa3q_decode_append_attn with capacity T.
+ *   page_size    a power of two, 16 .. 65536.  num_pages, max_pages > 0.
+ *   workspace    device, 256-byte aligned, >= fa3q_decode_attn_workspace_bytes(B,H,T,Dv)
+ *                with T = max_pages * page_size; may be NULL when that query returns 0.
+ * Ownership and errors as for every call; the only rows written are those of position
+ * kv_len[b] when appending.
+ */
+int fa3q_decode_paged_attn(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new, const float* scale,
+                           int8_t* k_nope_pool, uint16_t* k_rope_pool, uint16_t* v_pool,
+                           const int32_t* block_table, const int32_t* kv_len, int64_t B, int64_t H,
+                           int64_t num_pages, int64_t page_size, int64_t max_pages, int64_t Dn, int64_t Dr,
+                           int64_t Dv, float sm_scale, float* out, void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 #ifdef __cplusplus
 }

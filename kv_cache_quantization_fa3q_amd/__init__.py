@@ -30,6 +30,7 @@ from .ops import (  # noqa: F401
     fa3q_decode_attn_workspace_bytes,
     fa3q_decode_latent,
     fa3q_decode_latent_workspace_bytes,
+    fa3q_decode_paged_attn,
     fa3q_fake_quant,
     fa3q_init_minmax,
     fa3q_qparams,

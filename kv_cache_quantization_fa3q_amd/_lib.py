@@ -56,6 +56,8 @@ SIGNATURES = {
                                      ctypes.c_float, _vp, _vp, _sz, _vp]),
     "fa3q_quantize_asym": (_int, [_vp, _vp, _vp, _int, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp]),
     "fa3q_fake_quant": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp]),
+    "fa3q_decode_paged_attn": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
+                                      _i64, _i64, _i64, ctypes.c_float, _vp, _vp, _sz, _vp]),
     "fa3q_decode_attn_asym": (_int, [_vp, _vp, _vp, _vp, _int, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
                                      ctypes.c_float, _vp, _vp, _sz, _vp]),
     "fa3q_decode_latent_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),

@@ -63,6 +63,10 @@ struct DecodeArgs {
   const uint16_t* v;
   float* out;
   const int32_t* kv_len;   // [B] cached tokens per sequence (ragged kernels only)
+  const int32_t* block_table;  // [B][max_pages] physical page of each logical page (paged kernels)
+  int64_t num_pages;           // pages in each pool (paged kernels)
+  int32_t max_pages;           // block-table row length; T = max_pages << page_shift
+  int32_t page_shift;          // log2 of the page size
   const uint16_t* k_new;   // (B,H,Dn+Dr) token to append, or null
   const uint16_t* v_new;   // (B,H,Dv)
   const int8_t* qq;        // (B,H,Dn) query codes (INT8 kernels; q is then the (B,H,Dr) RoPE part)
@@ -149,16 +153,36 @@ constexpr int kFmtBf16 = 0;  // bf16 query and values, per-head symmetric K-nope
 constexpr int kFmtQkv8 = 1;  // INT8 query (non-RoPE part) and values; LV is then Dv/16
 constexpr int kFmtAsym = 2;  // bf16 query and values, per-(head, dim) asymmetric K-nope codes
 
-// kVar: ragged lengths from kv_len[] and, when k_new is set, the appended token.
-template <int LK, int LV, bool kVar, int kFmt>
+constexpr int kVarFixed = 0;  // every sequence holds T tokens at (b, h, t)
+constexpr int kVarRagged = 1; // kv_len[] tokens, optional append, contiguous (B,H,T,.) cache
+constexpr int kVarPaged = 2;  // kVarRagged through a block table over (pages,H,P,.) pools
+
+// Pages of one split that a paged kernel stages in LDS: enough for split_len tokens starting
+// anywhere inside a page.
+__host__ __device__ constexpr int split_pages(int64_t split_len, int page_shift) {
+  return static_cast<int>(split_len >> page_shift) + 2;
+}
+
+// Float offset of the paged kernels' page rows in dynamic LDS, after the scores, the
+// reduction scratch and the per-wave partials, rounded up to 8 bytes.
+__host__ __device__ constexpr int64_t prow_offset(int64_t split_len, int64_t Dv) {
+  return (split_len + kWaves + kWaves * Dv + 1) & ~int64_t{1};
+}
+
+// kVar: kVarFixed, kVarRagged (ragged lengths from kv_len[] and, when k_new is set, the
+// appended token) or kVarPaged (the same through a block table).
+template <int LK, int LV, int kVar, int kFmt>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
   constexpr bool kQ8 = kFmt == kFmtQkv8;
   constexpr bool kAsym = kFmt == kFmtAsym;
+  constexpr bool kPaged = kVar == kVarPaged;
   static_assert(!kVar || kFmt == kFmtBf16, "the append step takes the per-head bf16-query cache");
   extern __shared__ float smem[];
   float* sc = smem;                       // [split_len] scores, then probabilities
   float* red = smem + a.split_len;        // [kWaves] block reduction scratch
   float* part = red + kWaves;             // [kWaves][Dv] per-wave output partials
+  // paged kernels: row index (page * H + h) * P of each page the split touches
+  int64_t* prow = reinterpret_cast<int64_t*>(smem + prow_offset(a.split_len, a.Dv));
 
   const int bh = static_cast<int>(blockIdx.x) / a.nsplit;
   const int sp = static_cast<int>(blockIdx.x) - bh * a.nsplit;
@@ -194,6 +218,28 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     }
   }
   const int n_all = n + (own_new ? 1 : 0);  // scores in LDS: the cached tokens, then the new one
+  // Row of logical token t0 + tt in the (B,H,T,.) cache, or in the pools through the page rows
+  // staged below.  Page indices out of [0, num_pages) are clamped, so no access leaves a pool.
+  const int64_t pg0 = kPaged ? (t0 >> a.page_shift) : 0;
+  const int64_t pmask = (int64_t{1} << a.page_shift) - 1;
+  if constexpr (kPaged) {
+    const int b = bh / a.H;
+    const int np = static_cast<int>(((t0 + n_all - 1) >> a.page_shift) - pg0) + 1;
+    for (int i = tid; i < np; i += kThreads) {
+      const int64_t pg = min(max(static_cast<int64_t>(a.block_table[static_cast<int64_t>(b) * a.max_pages + pg0 + i]),
+                                 int64_t{0}), a.num_pages - 1);
+      prow[i] = (pg * a.H + h) << a.page_shift;
+    }
+    lds_barrier();
+  }
+  auto row_of = [&](int tt) -> int64_t {
+    if constexpr (kPaged) {
+      const int64_t t = t0 + tt;
+      return prow[(t >> a.page_shift) - pg0] + (t & pmask);
+    } else {
+      return static_cast<int64_t>(bh) * a.T + t0 + tt;
+    }
+  };
 
   // ---------------------------------------------------------------- phase 1: scores
   {
@@ -259,8 +305,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
         }
       }
     }
-    const int8_t* kq = a.kq + (static_cast<int64_t>(bh) * a.T + t0) * a.Dn + 16 * j;
-    const uint16_t* kr = a.kr + (static_cast<int64_t>(bh) * a.T + t0) * a.Dr + 8 * j;
+    const int8_t* kq = kPaged ? a.kq + 16 * j : a.kq + (static_cast<int64_t>(bh) * a.T + t0) * a.Dn + 16 * j;
+    const uint16_t* kr = kPaged ? a.kr + 8 * j : a.kr + (static_cast<int64_t>(bh) * a.T + t0) * a.Dr + 8 * j;
     const int step = kWaves * kSlots;
     for (int base = wave * kSlots + slot; base < n; base += step * kUk) {
       uint4 wn[kUk], wr[kUk];
@@ -270,8 +316,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
         wn[u] = make_uint4(0, 0, 0, 0);
         wr[u] = make_uint4(0, 0, 0, 0);
         if (tt < n) {
-          if (has_n) wn[u] = load_nt(kq + static_cast<int64_t>(tt) * a.Dn);
-          if (has_r) wr[u] = load_nt(kr + static_cast<int64_t>(tt) * a.Dr);
+          const int64_t r = kPaged ? row_of(tt) : tt;
+          if (has_n) wn[u] = load_nt(kq + r * a.Dn);
+          if (has_r) wr[u] = load_nt(kr + r * a.Dr);
         }
       }
 #pragma unroll
@@ -300,7 +347,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
       if (own_new && wave == 0) {
         // every slot of wave 0 quantises the same new row; slot 0 stores it and its score
         const uint16_t* knew = a.k_new + static_cast<int64_t>(bh) * Dk;
-        const int64_t at = static_cast<int64_t>(bh) * a.T + pos_new;
+        const int64_t at = row_of(static_cast<int>(pos_new - t0));
         uint4 cn = make_uint4(0, 0, 0, 0), rn = make_uint4(0, 0, 0, 0);
         if (has_n) {
           const uint4* p = reinterpret_cast<const uint4*>(knew + 16 * j);
@@ -357,7 +404,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
   float psum = 0.0f;  // INT8 values: sum of the weights, for the +128 offset of the byte reads
   {
     const char* vp = kQ8 ? reinterpret_cast<const char*>(a.vq + (static_cast<int64_t>(bh) * a.T + t0) * a.Dv + 16 * jv)
-                         : reinterpret_cast<const char*>(a.v + (static_cast<int64_t>(bh) * a.T + t0) * a.Dv + 8 * jv);
+                   : kPaged ? reinterpret_cast<const char*>(a.v + 8 * jv)
+                            : reinterpret_cast<const char*>(a.v + (static_cast<int64_t>(bh) * a.T + t0) * a.Dv + 8 * jv);
     const int64_t vrow = kQ8 ? a.Dv : 2 * static_cast<int64_t>(a.Dv);  // bytes per token
     const int step = kWaves * kVSlots;
     for (int base = wave * kVSlots + vslot; base < n; base += step * kUv) {
@@ -369,7 +417,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
         wv[u] = make_uint4(0, 0, 0, 0);
         p[u] = 0.0f;
         if (tt < n) {
-          wv[u] = load_nt(vp + static_cast<int64_t>(tt) * vrow);
+          wv[u] = load_nt(vp + (kPaged ? row_of(tt) : static_cast<int64_t>(tt)) * vrow);
           p[u] = sc[tt];
         }
       }
@@ -408,7 +456,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
   if constexpr (kVar) {
     if (own_new && wave == 0 && vslot == 0) {
       const uint4 wv = *reinterpret_cast<const uint4*>(a.v_new + static_cast<int64_t>(bh) * a.Dv + 8 * jv);
-      *reinterpret_cast<uint4*>(const_cast<uint16_t*>(a.v) + (static_cast<int64_t>(bh) * a.T + pos_new) * a.Dv + 8 * jv) = wv;
+      *reinterpret_cast<uint4*>(const_cast<uint16_t*>(a.v) + row_of(static_cast<int>(pos_new - t0)) * a.Dv + 8 * jv) = wv;
       const float p = sc[n];
       acc[0] = fmaf(p, bf16_lo(wv.x), acc[0]);
       acc[1] = fmaf(p, bf16_hi(wv.x), acc[1]);
@@ -487,7 +535,7 @@ int64_t next_pow2(int64_t v) {
 
 using KernelFn = void (*)(DecodeArgs);
 
-template <int LK, bool kVar, int kFmt>
+template <int LK, int kVar, int kFmt>
 KernelFn pick_lv(int lv) {
   switch (lv) {
     case 1: return decode_split_kernel<LK, 1, kVar, kFmt>;
@@ -503,7 +551,7 @@ KernelFn pick_lv(int lv) {
   }
 }
 
-template <bool kVar, int kFmt>
+template <int kVar, int kFmt>
 KernelFn pick_kernel(int lk, int lv) {
   switch (lk) {
     case 1: return pick_lv<1, kVar, kFmt>(lv);
@@ -553,16 +601,33 @@ struct Int8QV {
   int params_f16 = 0;
 };
 
-// Shared validation and launch of the decode entry points (kVar: ragged / append;
+// Block table of the paged entry point (unused by the others).
+struct PagedKV {
+  const int32_t* block_table = nullptr;
+  int64_t num_pages = 0;
+  int64_t page_size = 0;
+  int64_t max_pages = 0;
+};
+
+int log2_exact(int64_t v) {
+  int s = 0;
+  while ((int64_t{1} << s) < v) ++s;
+  return s;
+}
+
+// Shared validation and launch of the decode entry points (kVar: kVarFixed, kVarRagged or
+// kVarPaged, the last with T = max_pages * page_size and the cache pointers being pools;
 // kFmt: kFmtQkv8 takes INT8 query and values, with q the (B,H,Dr) RoPE part and v unused;
 // kFmtAsym takes the per-(head, dim) K tables instead of the per-head scale).
-template <bool kVar, int kFmt>
+template <int kVar, int kFmt>
 int decode_launch(const uint16_t* q, const int8_t* k_nope_q, const float* scale, const uint16_t* k_rope,
                   const uint16_t* v, const int32_t* kv_len, const uint16_t* k_new, const uint16_t* v_new,
                   const Int8QV& i8, int64_t B, int64_t H, int64_t T, int64_t Dn, int64_t Dr, int64_t Dv,
-                  float sm_scale, float* out, void* workspace, size_t workspace_bytes, void* stream) {
+                  float sm_scale, float* out, void* workspace, size_t workspace_bytes, void* stream,
+                  const PagedKV& pk = PagedKV{}) {
   constexpr bool kQ8 = kFmt == kFmtQkv8;
   constexpr bool kAsym = kFmt == kFmtAsym;
+  constexpr bool kPaged = kVar == kVarPaged;
   if (kQ8) {
     if (!i8.qq || !i8.vq || !i8.scale_q || !i8.scale_v || !k_nope_q || !scale || !out || (Dr > 0 && (!q || !k_rope)))
       return FA3Q_ERR_NULL;
@@ -572,6 +637,16 @@ int decode_launch(const uint16_t* q, const int8_t* k_nope_q, const float* scale,
   if (kAsym && (!i8.k_scale_hd || !i8.k_offset_hd)) return FA3Q_ERR_NULL;
   if (kAsym && i8.params_f16 != 0 && i8.params_f16 != 1) return FA3Q_ERR_DTYPE;
   if (kVar && (!kv_len || (k_new != nullptr) != (v_new != nullptr))) return FA3Q_ERR_NULL;
+  if (kPaged && !pk.block_table) return FA3Q_ERR_NULL;
+  if (kPaged) {
+    // pages: a power of two from 16 to 65536 tokens; pools of num_pages pages of H * P rows
+    if (B <= 0 || H <= 0 || H > (int64_t{1} << 20)) return FA3Q_ERR_SHAPE;
+    if (pk.page_size < 16 || pk.page_size > 65536 || !pow2(pk.page_size)) return FA3Q_ERR_SHAPE;
+    if (pk.num_pages <= 0 || pk.max_pages <= 0 || pk.max_pages > (int64_t{1} << 24)) return FA3Q_ERR_SHAPE;
+    if (pk.num_pages > (int64_t{1} << 62) / (H * pk.page_size * 1024)) return FA3Q_ERR_SHAPE;  // pool bytes
+    if (B > (int64_t{1} << 31) / pk.max_pages) return FA3Q_ERR_SHAPE;  // block-table entries
+    T = pk.max_pages * pk.page_size;
+  }
   if (B <= 0 || H <= 0 || T <= 0) return FA3Q_ERR_SHAPE;
   if (!valid_dims(Dn, Dr, Dv) || (kQ8 && Dv < 16)) return FA3Q_ERR_SHAPE;
   if (B > (int64_t{1} << 31) / H || T > (int64_t{1} << 40)) return FA3Q_ERR_SHAPE;
@@ -587,6 +662,7 @@ int decode_launch(const uint16_t* q, const int8_t* k_nope_q, const float* scale,
     return FA3Q_ERR_ALIGN;
   if (kVar && (!is_aligned(kv_len, 4) || (k_new && (!is_aligned(k_new, 16) || !is_aligned(v_new, 16)))))
     return FA3Q_ERR_ALIGN;
+  if (kPaged && !is_aligned(pk.block_table, 4)) return FA3Q_ERR_ALIGN;
   const SplitPlan p = plan_splits(B, H, T);
   if (B * H * p.nsplit > (int64_t{1} << 31) - 1) return FA3Q_ERR_SHAPE;
   const size_t need = fa3q_decode_attn_workspace_bytes(B, H, T, Dv);
@@ -607,6 +683,10 @@ int decode_launch(const uint16_t* q, const int8_t* k_nope_q, const float* scale,
   a.v = v;
   a.out = out;
   a.kv_len = kv_len;
+  a.block_table = pk.block_table;
+  a.num_pages = pk.num_pages;
+  a.max_pages = static_cast<int32_t>(pk.max_pages);
+  a.page_shift = kPaged ? log2_exact(pk.page_size) : 0;
   a.k_new = k_new;
   a.v_new = v_new;
   a.qq = i8.qq;
@@ -628,7 +708,9 @@ int decode_launch(const uint16_t* q, const int8_t* k_nope_q, const float* scale,
   a.nsplit = p.nsplit;
   a.split_len = p.split_len;
   a.sm_log2 = static_cast<float>(static_cast<double>(sm_scale) * 1.4426950408889634);
-  const size_t lds = (static_cast<size_t>(p.split_len) + kWaves + kWaves * static_cast<size_t>(Dv)) * sizeof(float);
+  const size_t lds = kPaged ? static_cast<size_t>(prow_offset(p.split_len, Dv)) * sizeof(float) +
+                                  static_cast<size_t>(split_pages(p.split_len, a.page_shift)) * sizeof(int64_t)
+                            : (static_cast<size_t>(p.split_len) + kWaves + kWaves * static_cast<size_t>(Dv)) * sizeof(float);
   hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(B * H * p.nsplit)), dim3(kThreads), lds,
                      as_stream(stream), a);
   if (p.nsplit > 1) {
@@ -646,7 +728,7 @@ extern "C" int fa3q_decode_attn(const uint16_t* q, const int8_t* k_nope_q, const
                                 int64_t T, int64_t Dn, int64_t Dr, int64_t Dv, float sm_scale,
                                 float* out, void* workspace, size_t workspace_bytes,
                                 void* stream) {
-  return decode_launch<false, kFmtBf16>(q, k_nope_q, scale, k_rope, v, nullptr, nullptr, nullptr, Int8QV{}, B, H, T,
+  return decode_launch<kVarFixed, kFmtBf16>(q, k_nope_q, scale, k_rope, v, nullptr, nullptr, nullptr, Int8QV{}, B, H, T,
                                      Dn, Dr, Dv, sm_scale, out, workspace, workspace_bytes, stream);
 }
 
@@ -656,8 +738,24 @@ extern "C" int fa3q_decode_append_attn(const uint16_t* q, const uint16_t* k_new,
                                        int64_t T, int64_t Dn, int64_t Dr, int64_t Dv, float sm_scale,
                                        float* out, void* workspace, size_t workspace_bytes,
                                        void* stream) {
-  return decode_launch<true, kFmtBf16>(q, k_nope_q, scale, k_rope, v, kv_len, k_new, v_new, Int8QV{}, B, H, T, Dn,
+  return decode_launch<kVarRagged, kFmtBf16>(q, k_nope_q, scale, k_rope, v, kv_len, k_new, v_new, Int8QV{}, B, H, T, Dn,
                                     Dr, Dv, sm_scale, out, workspace, workspace_bytes, stream);
+}
+
+extern "C" int fa3q_decode_paged_attn(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                                      const float* scale, int8_t* k_nope_pool, uint16_t* k_rope_pool,
+                                      uint16_t* v_pool, const int32_t* block_table, const int32_t* kv_len,
+                                      int64_t B, int64_t H, int64_t num_pages, int64_t page_size,
+                                      int64_t max_pages, int64_t Dn, int64_t Dr, int64_t Dv, float sm_scale,
+                                      float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  PagedKV pk;
+  pk.block_table = block_table;
+  pk.num_pages = num_pages;
+  pk.page_size = page_size;
+  pk.max_pages = max_pages;
+  return decode_launch<kVarPaged, kFmtBf16>(q, k_nope_pool, scale, k_rope_pool, v_pool, kv_len, k_new, v_new,
+                                            Int8QV{}, B, H, 0, Dn, Dr, Dv, sm_scale, out, workspace,
+                                            workspace_bytes, stream, pk);
 }
 
 extern "C" int fa3q_decode_attn_qkv8(const int8_t* q_nope_q, const uint16_t* q_rope, const float* scale_q,
@@ -670,7 +768,7 @@ extern "C" int fa3q_decode_attn_qkv8(const int8_t* q_nope_q, const uint16_t* q_r
   i8.vq = v_q;
   i8.scale_q = scale_q;
   i8.scale_v = scale_v;
-  return decode_launch<false, kFmtQkv8>(q_rope, k_nope_q, scale_k, k_rope, nullptr, nullptr, nullptr, nullptr, i8, B,
+  return decode_launch<kVarFixed, kFmtQkv8>(q_rope, k_nope_q, scale_k, k_rope, nullptr, nullptr, nullptr, nullptr, i8, B,
                                         H, T, Dn, Dr, Dv, sm_scale, out, workspace, workspace_bytes, stream);
 }
 
@@ -683,6 +781,6 @@ extern "C" int fa3q_decode_attn_asym(const uint16_t* q, const int8_t* k_nope_q, 
   i8.k_scale_hd = k_scale;
   i8.k_offset_hd = k_offset;
   i8.params_f16 = params_dtype == FA3Q_BF16 ? 0 : (params_dtype == FA3Q_F16 ? 1 : -1);
-  return decode_launch<false, kFmtAsym>(q, k_nope_q, nullptr, k_rope, v, nullptr, nullptr, nullptr, i8, B, H, T, Dn,
+  return decode_launch<kVarFixed, kFmtAsym>(q, k_nope_q, nullptr, k_rope, v, nullptr, nullptr, nullptr, i8, B, H, T, Dn,
                                         Dr, Dv, sm_scale, out, workspace, workspace_bytes, stream);
 }

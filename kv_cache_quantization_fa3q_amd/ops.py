@@ -282,6 +282,51 @@ def fa3q_decode_append_attn(q: torch.Tensor, k_new: Optional[torch.Tensor], v_ne
     return out
 
 
+def fa3q_decode_paged_attn(q: torch.Tensor, k_new: Optional[torch.Tensor], v_new: Optional[torch.Tensor],
+                           scale: torch.Tensor, k_nope_pool: torch.Tensor, k_rope_pool: Optional[torch.Tensor],
+                           v_pool: torch.Tensor, block_table: torch.Tensor, kv_len: torch.Tensor, sm_scale: float,
+                           out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                           stream=None) -> torch.Tensor:
+    """``fa3q_decode_append_attn`` over a paged cache: pools ``(num_pages, H, P, .)`` and an int32
+    ``block_table (B, max_pages)`` of physical pages per logical page.  Returns float32 ``(B,H,Dv)``."""
+    if k_nope_pool.dim() != 4 or k_nope_pool.dtype != torch.int8:
+        raise ValueError("k_nope_pool must be int8 (num_pages, H, P, Dn)")
+    NP, H, P, Dn = (int(s) for s in k_nope_pool.shape)
+    Dr = int(k_rope_pool.shape[-1]) if k_rope_pool is not None else 0
+    Dv = int(v_pool.shape[-1])
+    if block_table.dim() != 2 or block_table.dtype != torch.int32:
+        raise ValueError("block_table must be int32 (B, max_pages)")
+    B, MP = (int(s) for s in block_table.shape)
+    if q.shape != (B, H, Dn + Dr) or q.dtype != torch.bfloat16:
+        raise ValueError("q must be bfloat16 (B, H, Dn + Dr)")
+    if v_pool.shape != (NP, H, P, Dv) or v_pool.dtype != torch.bfloat16:
+        raise ValueError("v_pool must be bfloat16 (num_pages, H, P, Dv)")
+    if k_rope_pool is not None and (k_rope_pool.shape != (NP, H, P, Dr) or k_rope_pool.dtype != torch.bfloat16):
+        raise ValueError("k_rope_pool must be bfloat16 (num_pages, H, P, Dr)")
+    if (k_new is None) != (v_new is None):
+        raise ValueError("k_new and v_new are given together or not at all")
+    if k_new is not None:
+        if k_new.shape != (B, H, Dn + Dr) or k_new.dtype != torch.bfloat16:
+            raise ValueError("k_new must be bfloat16 (B, H, Dn + Dr)")
+        if v_new.shape != (B, H, Dv) or v_new.dtype != torch.bfloat16:
+            raise ValueError("v_new must be bfloat16 (B, H, Dv)")
+    if kv_len.shape != (B,) or kv_len.dtype != torch.int32:
+        raise ValueError("kv_len must be int32 (B,)")
+    if out is None:
+        out = torch.empty((B, H, Dv), dtype=torch.float32, device=q.device)
+    _need_gpu("fa3q_decode_paged_attn", q, k_new, v_new, scale, k_nope_pool, k_rope_pool, v_pool, block_table,
+              kv_len, out)
+    nbytes = int(lib().fa3q_decode_attn_workspace_bytes(B, H, MP * P, Dv))
+    workspace = _workspace(nbytes, q.device, workspace)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().fa3q_decode_paged_attn(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(scale), _ptr(k_nope_pool),
+                                      _ptr(k_rope_pool) if Dr > 0 else None, _ptr(v_pool), _ptr(block_table),
+                                      _ptr(kv_len), B, H, NP, P, MP, Dn, Dr, Dv, ctypes.c_float(float(sm_scale)),
+                                      _ptr(out), _ptr(workspace), wbytes, _stream(stream))
+    _check(st, "fa3q_decode_paged_attn")
+    return out
+
+
 def fa3q_decode_attn_qkv8(q_nope_q: torch.Tensor, q_rope: Optional[torch.Tensor], scale_q: torch.Tensor,
                           k_nope_q: torch.Tensor, scale_k: torch.Tensor, k_rope: Optional[torch.Tensor],
                           v_q: torch.Tensor, scale_v: torch.Tensor, sm_scale: float,

@@ -203,6 +203,37 @@ def test_decode_append_rejections():
 
 
 @no_gpu_only
+def test_decode_paged_rejections():
+    f = fa.lib().fa3q_decode_paged_attn
+    ok = dict(q=_p(), kn=_p(), vn=_p(), s=_p(), kq=_p(), kr=_p(), v=_p(), bt=_p(), kl=_p(), B=8, H=128, NP=4096,
+              P=64, MP=512, Dn=128, Dr=64, Dv=128, sm=0.07, o=_p(), ws=_p(), wsb=1 << 30)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["q"], a["kn"], a["vn"], a["s"], a["kq"], a["kr"], a["v"], a["bt"], a["kl"], a["B"], a["H"],
+                 a["NP"], a["P"], a["MP"], a["Dn"], a["Dr"], a["Dv"], ctypes.c_float(a["sm"]), a["o"], a["ws"],
+                 a["wsb"], None)
+
+    for name in ("q", "s", "kq", "kr", "v", "bt", "kl", "o"):
+        assert call(**{name: None}) == L.FA3Q_ERR_NULL, name
+    assert call(vn=None) == L.FA3Q_ERR_NULL
+    for bad in (0, 8, 48, 1 << 17):                      # pages: a power of two, 16 .. 65536
+        assert call(P=bad) == L.FA3Q_ERR_SHAPE, bad
+    assert call(NP=0) == L.FA3Q_ERR_SHAPE
+    assert call(MP=0) == L.FA3Q_ERR_SHAPE
+    assert call(B=0) == L.FA3Q_ERR_SHAPE
+    assert call(Dn=120) == L.FA3Q_ERR_SHAPE
+    assert call(bt=_p(2)) == L.FA3Q_ERR_ALIGN
+    assert call(kq=_p(8)) == L.FA3Q_ERR_ALIGN
+    assert call(kl=_p(2)) == L.FA3Q_ERR_ALIGN
+    # the workspace is sized for T = max_pages * page_size
+    need = fa.lib().fa3q_decode_attn_workspace_bytes(8, 128, 512 * 64, 128)
+    assert need > 0
+    assert call(wsb=need - 1) == L.FA3Q_ERR_WORKSPACE
+    assert call(ws=None) == L.FA3Q_ERR_WORKSPACE
+
+
+@no_gpu_only
 def test_decode_qkv8_rejections():
     f = fa.lib().fa3q_decode_attn_qkv8
     ok = dict(qq=_p(), qr=_p(), sq=_p(), kq=_p(), sk=_p(), kr=_p(), vq=_p(), sv=_p(), B=8, H=128, T=32768, Dn=128,

@@ -22,12 +22,14 @@
 //                        threshold; when a buffer passes 2K entries an exact LDS radix
 //                        select cuts it back to the K extreme values and tightens the
 //                        threshold.  At most K values per side go to the workspace.
-//   calib_merge_kernel   one workgroup per head: the same select over the chunks' lists
-//                        gives the head's exact K smallest and K largest values, a
-//                        bitonic sort orders them, and a block reduction finds the
-//                        shortest float32 window U[i]-L[i], smallest i on ties.  Heads
-//                        whose lists fit in registers take calib_merge_wave_kernel
-//                        instead: one wave per side, no LDS select.
+//   calib_merge_side_kernel  one workgroup per (head, side): the same select over the
+//                        keys the chunks' lists hold gives the side's exact K extreme
+//                        values, and a counting sort (or a bitonic one) orders them into
+//                        the workspace;
+//   calib_window_kernel  one workgroup per head, after both passes: the shortest float32
+//                        window U[i]-L[i] over the two sorted sides, smallest i on ties.
+//                        Heads whose lists fit in registers take calib_merge_wave_kernel
+//                        instead: one wave per side and the window in the same workgroup.
 //
 // Estimated bounds.  A group-minimum bound is certain but loose: with a sampled fraction f
 // of the head it lets about K/f values per side through.  When K is large against the
@@ -36,9 +38,10 @@
 // number of sampled keys among the head's K smallest: about r/f values pass, a few times K.
 // Such a bound is checked, exactly, by the merge: it holds at least K head values iff the
 // chunk lists together hold at least K keys (a chunk that cut its buffer held K by
-// itself; otherwise every value within the bound was kept).  A head that fails is flagged
-// and redone by a second chunk pass and merge that use no bound (their workgroups exit at
-// once for every head that passed).
+// itself; otherwise every value within the bound was kept).  Each chunk records how many
+// keys its lists hold, so the check is a sum.  A side that fails sets its flag, and a head
+// with either flag set is redone by a second chunk pass and merge that use no bound (their
+// workgroups exit at once for every head that passed).
 //
 // Why the union of the chunk lists holds the head's K smallest values: a value v at or
 // below the head's K-th smallest value is never dropped.  The head bound has at least K
@@ -114,6 +117,7 @@ enum Ctl : int {
 };
 constexpr size_t kCtlBytes = 2048;
 static_assert(kCtlWords * 4 <= kCtlBytes, "control block too small");
+static_assert(kWaveScratch + 16 <= kCtlWords, "wave scratch holds a total per wave of 1024 threads");
 static_assert(kWaveTot + 3 * kChunkWaves <= kHist, "wave totals overlap the histogram");
 constexpr size_t kStageBytes = static_cast<size_t>(kChunkWaves) * kStageVecs * 16;
 
@@ -429,8 +433,10 @@ struct ChunkArgs {
   int32_t H;
   int32_t cps;        // chunks per slab
   int32_t nch;        // chunks per head = B*cps
+  uint32_t* counts;        // [2][H][nch] keys each list holds (the rest are unused slots)
   const uint32_t* bounds;  // [2][H] sampled bound keys per head (lo side, then hi side)
-  const uint32_t* fail;    // fix-up pass: [H] heads to redo with no bound (nullptr: the first pass)
+  const uint32_t* fail;    // fix-up pass: [2][H] check flags per side, a head is redone when
+                           // either is set (nullptr: the first pass)
   uint32_t K;
   uint32_t cap;
 };
@@ -624,6 +630,7 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
   const int bid = static_cast<int>(blockIdx.x) - batch * bt.per;
   a.x = bt.x[batch];
   a.lists = in_region(a.lists, batch * bt.region);
+  a.counts = in_region(a.counts, batch * bt.region);
   a.bounds = in_region(a.bounds, batch * bt.region);
   a.fail = in_region(a.fail, batch * bt.region);
   const int slab_i = bid / a.cps;
@@ -653,7 +660,7 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
   // fewer than K such keys), then its own K-th extreme key once it holds K.
   Lim lo_lim = static_cast<Lim>(a.bounds[h]) + 1, hi_lim = static_cast<Lim>(a.bounds[a.H + h]) - 1;
   if (a.fail != nullptr) {  // fix-up pass: only flagged heads, and every key is a candidate
-    if (a.fail[h] == 0) return;  // uniform over the workgroup
+    if ((a.fail[h] | a.fail[a.H + h]) == 0) return;  // uniform over the workgroup
     lo_lim = kKeyMax + 1;
     hi_lim = -1;
   }
@@ -743,13 +750,19 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
     out_lo[i] = i < st.base_lo ? st.lo[i] : static_cast<KeyT>(KeyInfo<KeyT>::kMax);
     out_hi[i] = i < st.base_hi ? st.hi[i] : static_cast<KeyT>(0);
   }
+  if (tid == 0) {
+    a.counts[list] = st.base_lo;
+    a.counts[heads_lists + list] = st.base_hi;
+  }
 }
 
 struct MergeArgs {
   const void* lists;
+  const uint32_t* counts;  // [2][H][nch] keys each list holds
+  void* sorted;            // [2][H][K] each side's K extreme keys, ascending (hi side complemented)
   float* win_min;
   float* win_max;
-  uint32_t* fail;  // [H] with an estimated bound: written by the check pass, read by the fix-up
+  uint32_t* fail;  // [2][H] with an estimated bound: written by the check pass, read by the fix-up
   int32_t fixup;   // 0: check pass (verifies the bound when fail != nullptr), 1: fix-up pass
   int32_t H;
   int32_t nch;
@@ -758,50 +771,40 @@ struct MergeArgs {
   uint32_t P;  // next power of two >= K
 };
 
-// Ascending bitonic sort of lo[0..P) and hi[0..P) together, P = kMergeThreads * E.
-// Thread t holds elements t*E .. t*E+E-1 of each array in registers: compare-exchange
-// distances below E stay in registers, distances below 64*E go through lane shuffles, and
-// only the wider ones through LDS (one barrier each) -- 10 barriers instead of 91 for
-// P = 8192.
+constexpr int kMaxPrefixLists = 2048;  // list counts the side merge keeps as an LDS prefix
+
+// Ascending bitonic sort of buf[0..P), P = kMergeThreads * E.  Thread t holds elements
+// t*E .. t*E+E-1 in registers: compare-exchange distances below E stay in registers,
+// distances below 64*E go through lane shuffles, and only the wider ones through LDS (one
+// barrier each) -- 10 barriers instead of 91 for P = 8192.
 template <typename KeyT, int E>
-__device__ void bitonic_sort2(KeyT* lo, KeyT* hi, int tid) {
+__device__ void bitonic_sort_regs(KeyT* buf, int tid) {
   constexpr int NT = kMergeThreads;
   constexpr uint32_t P = static_cast<uint32_t>(NT) * E;
   constexpr uint32_t kWide = static_cast<uint32_t>(kWave) * E;  // distances from here on cross waves
-  uint32_t a[E], b[E];
+  uint32_t a[E];
   const uint32_t base = static_cast<uint32_t>(tid) * E;
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    a[e] = lo[base + e];
-    b[e] = hi[base + e];
-  }
+  for (int e = 0; e < E; ++e) a[e] = buf[base + e];
 #pragma unroll
   for (uint32_t k = 2; k <= P; k <<= 1) {
     uint32_t j = k >> 1;
     if (j >= kWide) {
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        lo[base + e] = static_cast<KeyT>(a[e]);
-        hi[base + e] = static_cast<KeyT>(b[e]);
-      }
+      for (int e = 0; e < E; ++e) buf[base + e] = static_cast<KeyT>(a[e]);
       lds_barrier();
       for (; j >= kWide; j >>= 1) {
         for (uint32_t i = static_cast<uint32_t>(tid); i < P / 2; i += NT) {
           const uint32_t l = ((i & ~(j - 1)) << 1) | (i & (j - 1));
           const uint32_t r = l + j;
           const bool up = (l & k) == 0;
-          const KeyT a0 = lo[l], a1 = lo[r];
-          if ((a0 > a1) == up) { lo[l] = a1; lo[r] = a0; }
-          const KeyT b0 = hi[l], b1 = hi[r];
-          if ((b0 > b1) == up) { hi[l] = b1; hi[r] = b0; }
+          const KeyT a0 = buf[l], a1 = buf[r];
+          if ((a0 > a1) == up) { buf[l] = a1; buf[r] = a0; }
         }
         lds_barrier();
       }
 #pragma unroll
-      for (int e = 0; e < E; ++e) {  // each thread reads back only its own elements
-        a[e] = lo[base + e];
-        b[e] = hi[base + e];
-      }
+      for (int e = 0; e < E; ++e) a[e] = buf[base + e];  // each thread reads back only its own elements
     }
 #pragma unroll
     for (; j >= static_cast<uint32_t>(E); j >>= 1) {
@@ -809,11 +812,9 @@ __device__ void bitonic_sort2(KeyT* lo, KeyT* hi, int tid) {
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const uint32_t oa = static_cast<uint32_t>(__shfl_xor(static_cast<int>(a[e]), lm));
-        const uint32_t ob = static_cast<uint32_t>(__shfl_xor(static_cast<int>(b[e]), lm));
         const uint32_t i = base + e;
         const bool keep_min = ((i & k) == 0) == ((i & j) == 0);
         a[e] = keep_min ? min(a[e], oa) : max(a[e], oa);
-        b[e] = keep_min ? min(b[e], ob) : max(b[e], ob);
       }
     }
 #pragma unroll
@@ -826,104 +827,25 @@ __device__ void bitonic_sort2(KeyT* lo, KeyT* hi, int tid) {
           const bool sa = (x0 > x1) == up;
           a[e] = sa ? x1 : x0;
           a[e ^ j] = sa ? x0 : x1;
-          const uint32_t y0 = b[e], y1 = b[e ^ j];
-          const bool sb = (y0 > y1) == up;
-          b[e] = sb ? y1 : y0;
-          b[e ^ j] = sb ? y0 : y1;
         }
       }
     }
   }
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    lo[base + e] = static_cast<KeyT>(a[e]);
-    hi[base + e] = static_cast<KeyT>(b[e]);
-  }
+  for (int e = 0; e < E; ++e) buf[base + e] = static_cast<KeyT>(a[e]);
   lds_barrier();
 }
 
+// Ascending sort of buf[0..P), P a power of two.
 template <typename KeyT>
-__global__ __launch_bounds__(kMergeThreads) void calib_merge_kernel(MergeArgs a, Batches bt) {
+__device__ void bitonic_sort(KeyT* buf, uint32_t P, int tid) {
   constexpr int NT = kMergeThreads;
-  extern __shared__ __align__(16) unsigned char smem[];
-  uint32_t* ctl = reinterpret_cast<uint32_t*>(smem);
-  KeyT* lo = reinterpret_cast<KeyT*>(smem + kCtlBytes);
-
-  TailState<KeyT, NT> st;
-  st.lo = lo;
-  st.hi = lo + a.cap;
-  st.tmp = lo + 2 * a.cap;
-  st.ctl = ctl;
-  st.K = a.K;
-  st.cap = a.cap;
-  st.room = kMergeTile;
-  st.init();
-
-  const int batch = static_cast<int>(blockIdx.x) / bt.per;
-  const int h = static_cast<int>(blockIdx.x) - batch * bt.per;
-  a.lists = in_region(a.lists, batch * bt.region);
-  a.fail = in_region(a.fail, batch * bt.region);
-  a.win_min += static_cast<int64_t>(batch) * a.H;
-  a.win_max += static_cast<int64_t>(batch) * a.H;
-  const int tid = static_cast<int>(threadIdx.x);
-  if (a.fixup && a.fail[h] == 0) return;  // uniform over the workgroup
-  const bool check = !a.fixup && a.fail != nullptr;
-  const int64_t per_head = static_cast<int64_t>(a.nch) * a.K;
-  const KeyT* src_lo = static_cast<const KeyT*>(a.lists) + h * per_head;
-  const KeyT* src_hi = static_cast<const KeyT*>(a.lists) + (static_cast<int64_t>(a.H) + h) * per_head;
-
-  // Stream the head's chunk tails (one flat array per side) through the same filter,
-  // counting the keys the lists hold (their unused slots hold keys no filter passes).
-  uint32_t held_lo = 0, held_hi = 0;
-  for (int64_t t0 = 0; t0 < per_head; t0 += kMergeTile) {
-    uint32_t klo[kMergePerThread], khi[kMergePerThread];
-    bool ev[kMergePerThread];
-#pragma unroll
-    for (int e = 0; e < kMergePerThread; ++e) {
-      const int64_t i = t0 + e * NT + tid;
-      ev[e] = i < per_head;
-      klo[e] = ev[e] ? static_cast<uint32_t>(src_lo[i]) : KeyInfo<KeyT>::kMax;
-      khi[e] = ev[e] ? static_cast<uint32_t>(src_hi[i]) : 0u;
-      held_lo += klo[e] != KeyInfo<KeyT>::kMax ? 1u : 0u;
-      held_hi += khi[e] != 0u ? 1u : 0u;
-    }
-#pragma unroll
-    for (int e = 0; e < kMergePerThread; ++e) st.append_lo(klo[e] < st.thr_lo, klo[e]);
-#pragma unroll
-    for (int e = 0; e < kMergePerThread; ++e) st.append_hi(khi[e] > st.thr_hi, khi[e]);
-    st.end_round();
-  }
-  if (check) {
-    // the estimated bound holds iff the lists hold at least K keys per side
-    uint32_t* cnt = ctl + kWaveScratch;
-    if (tid < 2) cnt[tid] = 0;
-    lds_barrier();
-    held_lo = wave_sum(held_lo);
-    held_hi = wave_sum(held_hi);
-    if (lane_id() == 0) {
-      atomicAdd(&cnt[0], held_lo);
-      atomicAdd(&cnt[1], held_hi);
-    }
-    lds_barrier();
-    const bool ok = cnt[0] >= a.K && cnt[1] >= a.K;
-    if (tid == 0) a.fail[h] = ok ? 0u : 1u;
-    if (!ok) return;  // uniform: the fix-up pass redoes this head
-  }
-  st.finish();  // now exactly K per side (every head holds at least K values)
-
-  // Ascending bitonic sort of both tails, padded to P with the largest key.
-  const uint32_t K = a.K, P = a.P;
-  for (uint32_t i = K + tid; i < P; i += NT) {
-    st.lo[i] = static_cast<KeyT>(KeyInfo<KeyT>::kMax);
-    st.hi[i] = static_cast<KeyT>(KeyInfo<KeyT>::kMax);
-  }
-  lds_barrier();
   switch (P / NT) {  // P >= NT: registers, shuffles and LDS; smaller: all in LDS
-    case 1: bitonic_sort2<KeyT, 1>(st.lo, st.hi, tid); break;
-    case 2: bitonic_sort2<KeyT, 2>(st.lo, st.hi, tid); break;
-    case 4: bitonic_sort2<KeyT, 4>(st.lo, st.hi, tid); break;
-    case 8: bitonic_sort2<KeyT, 8>(st.lo, st.hi, tid); break;
-    case 16: bitonic_sort2<KeyT, 16>(st.lo, st.hi, tid); break;
+    case 1: bitonic_sort_regs<KeyT, 1>(buf, tid); break;
+    case 2: bitonic_sort_regs<KeyT, 2>(buf, tid); break;
+    case 4: bitonic_sort_regs<KeyT, 4>(buf, tid); break;
+    case 8: bitonic_sort_regs<KeyT, 8>(buf, tid); break;
+    case 16: bitonic_sort_regs<KeyT, 16>(buf, tid); break;
     default:
       for (uint32_t k = 2; k <= P; k <<= 1) {
         for (uint32_t j = k >> 1; j > 0; j >>= 1) {
@@ -931,54 +853,284 @@ __global__ __launch_bounds__(kMergeThreads) void calib_merge_kernel(MergeArgs a,
             const uint32_t l = ((i & ~(j - 1)) << 1) | (i & (j - 1));
             const uint32_t r = l + j;
             const bool up = (l & k) == 0;
-            const KeyT a0 = st.lo[l], a1 = st.lo[r];
-            if ((a0 > a1) == up) { st.lo[l] = a1; st.lo[r] = a0; }
-            const KeyT b0 = st.hi[l], b1 = st.hi[r];
-            if ((b0 > b1) == up) { st.hi[l] = b1; st.hi[r] = b0; }
+            const KeyT a0 = buf[l], a1 = buf[r];
+            if ((a0 > a1) == up) { buf[l] = a1; buf[r] = a0; }
           }
           lds_barrier();
         }
       }
   }
+}
 
-  // Shortest window U[i] - L[i] (float32), smallest i on ties.
-  float best_len = __uint_as_float(0x7f800000u);
-  uint32_t best_i = 0xffffffffu;
+constexpr int kSortBuckets = 16;  // top-byte buckets the counting sort of 16-bit keys takes
+constexpr int kSortBins = kSortBuckets * 256;
+constexpr size_t kSortLdsBytes = (kSortBins + 256 + kSortBuckets) * 4;  // bins, bucket of each top byte, top byte of each bucket
+static_assert(kSortBins == 4 * kMergeThreads, "the prefix takes four bins per thread");
+
+// Ascending sort of the K 16-bit keys buf[0..K) into dst (device memory) by counting: equal
+// keys are indistinguishable, so the sorted sequence follows from the counts of each key
+// value.  Keys are counted per (top byte, low byte) over the top bytes present; output
+// slot i holds the key of the bin whose prefix range contains i.  Returns false (nothing
+// written) when the keys span more than kSortBuckets top bytes.
+__device__ bool value_sort16(const uint16_t* buf, uint32_t K, uint32_t* sort_lds, uint32_t* ctl, uint16_t* dst,
+                             int tid) {
+  constexpr int NT = kMergeThreads;
+  uint32_t* bins = sort_lds;                 // [kSortBins]
+  uint32_t* bidx = sort_lds + kSortBins;     // [256] bucket of each present top byte
+  uint32_t* btop = bidx + 256;               // [kSortBuckets] top byte of each bucket
+  uint32_t* hist = ctl + kHist;              // [256] keys per top byte
+  for (int i = tid; i < 256; i += NT) hist[i] = 0;
+  for (int i = tid; i < kSortBins; i += NT) bins[i] = 0;
+  lds_barrier();
+  // tail keys share few top bytes: one atomic per distinct top byte of a wave
+  const uint32_t k_round = (K + NT - 1) / NT * NT;
+  for (uint32_t i = tid; i < k_round; i += NT) {
+    const bool act = i < K;
+    const uint32_t d = act ? static_cast<uint32_t>(buf[i]) >> 8 : 0u;
+    uint64_t pending = __ballot(act);
+    while (pending != 0) {
+      const int leader = __ffsll(static_cast<unsigned long long>(pending)) - 1;
+      const uint32_t dl = __builtin_amdgcn_readlane(d, leader);
+      const uint64_t same = __ballot(act && d == dl);
+      if (lane_id() == leader) atomicAdd(&hist[dl], static_cast<uint32_t>(__popcll(same)));
+      pending &= ~same;
+    }
+  }
+  lds_barrier();
+  if (tid < kWave) {
+    uint32_t f[4], n = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f[q] = hist[4 * tid + q] != 0 ? 1u : 0u;
+      n += f[q];
+    }
+    const uint32_t incl = wave_inclusive_scan(n);
+    uint32_t idx = incl - n;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (f[q]) {
+        bidx[4 * tid + q] = idx;
+        if (idx < kSortBuckets) btop[idx] = 4 * tid + q;
+        ++idx;
+      }
+    }
+    if (tid == kWave - 1) ctl[kSelCount] = incl;
+  }
+  lds_barrier();
+  const uint32_t nbk = ctl[kSelCount];
+  if (nbk > kSortBuckets) return false;  // uniform
   for (uint32_t i = tid; i < K; i += NT) {
-    const float len = value_of_key(st.hi[i], KeyT{}) - value_of_key(st.lo[i], KeyT{});
-    if (len < best_len || best_i == 0xffffffffu) {
-      best_len = len;
-      best_i = i;
+    const uint32_t k = buf[i];
+    atomicAdd(&bins[bidx[k >> 8] * 256 + (k & 255u)], 1u);
+  }
+  lds_barrier();
+  // exclusive prefix over the nbk * 256 bins, four consecutive bins per thread
+  const uint32_t nbins = nbk * 256;
+  uint32_t c[4], sum = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t j = 4 * static_cast<uint32_t>(tid) + q;
+    c[q] = j < nbins ? bins[j] : 0u;
+    sum += c[q];
+  }
+  const uint32_t incl = wave_inclusive_scan(sum);
+  uint32_t* wsum = ctl + kWaveScratch;  // [NT / kWave] wave totals
+  const int wave = tid / kWave;
+  if (lane_id() == kWave - 1) wsum[wave] = incl;
+  lds_barrier();
+  uint32_t run = incl - sum;
+  for (int w = 0; w < wave; ++w) run += wsum[w];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t j = 4 * static_cast<uint32_t>(tid) + q;
+    if (j < nbins) bins[j] = run;
+    run += c[q];
+  }
+  lds_barrier();
+  // slot i: the largest bin j with prefix[j] <= i (empty bins share the next bin's prefix)
+  for (uint32_t i = tid; i < K; i += NT) {
+    uint32_t lo = 0, hi = nbins;
+    while (hi - lo > 1) {
+      const uint32_t mid = (lo + hi) >> 1;
+      if (bins[mid] <= i) lo = mid; else hi = mid;
+    }
+    dst[i] = static_cast<uint16_t>((btop[lo >> 8] << 8) | (lo & 255u));
+  }
+  return true;
+}
+
+// One side of one head (workgroup = batch, side, head; the hi side works on complemented
+// keys kMax - key, so both sides look for their K smallest keys): the keys the chunk lists
+// hold go through the chunk kernel's filter and cuts, and the K smallest are sorted into
+// the workspace.  Only the lists' real keys are read: an LDS prefix of the list counts maps
+// a flat index to (list, slot); past kMaxPrefixLists lists every slot is read and the
+// unused ones fail the filter.
+template <typename KeyT>
+__global__ __launch_bounds__(kMergeThreads) void calib_merge_side_kernel(MergeArgs a, Batches bt) {
+  constexpr int NT = kMergeThreads;
+  constexpr uint32_t kMax = KeyInfo<KeyT>::kMax;
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint32_t* ctl = reinterpret_cast<uint32_t*>(smem);
+  uint32_t* pre = reinterpret_cast<uint32_t*>(smem + kCtlBytes);  // [nch + 1] when nch <= kMaxPrefixLists
+  const bool use_pre = a.nch <= kMaxPrefixLists;
+  const size_t pre_bytes = use_pre ? (static_cast<size_t>(a.nch + 1) * 4 + 15) / 16 * 16 : 0;  // as the plan sizes it
+  KeyT* buf = reinterpret_cast<KeyT*>(smem + kCtlBytes + pre_bytes);
+  // counting-sort scratch (16-bit keys) after the buffer and cut scratch
+  uint32_t* sort_lds = reinterpret_cast<uint32_t*>(
+      smem + kCtlBytes + pre_bytes + (static_cast<size_t>(a.cap + a.K) * sizeof(KeyT) + 15) / 16 * 16);
+
+  const int batch = static_cast<int>(blockIdx.x) / bt.per;
+  const int r = static_cast<int>(blockIdx.x) - batch * bt.per;
+  const int side = r / a.H;
+  const int h = r - side * a.H;
+  a.lists = in_region(a.lists, batch * bt.region);
+  a.counts = in_region(a.counts, batch * bt.region);
+  a.sorted = in_region(a.sorted, batch * bt.region);
+  a.fail = in_region(a.fail, batch * bt.region);
+  const int tid = static_cast<int>(threadIdx.x);
+  if (a.fixup && (a.fail[h] | a.fail[a.H + h]) == 0) return;  // uniform over the workgroup
+
+  TailState<KeyT, NT> st;
+  st.lo = buf;
+  st.hi = buf;  // one side only: nothing is appended to the hi buffer
+  st.tmp = buf + a.cap;
+  st.ctl = ctl;
+  st.K = a.K;
+  st.cap = a.cap;
+  st.room = kMergeTile;
+  st.init();
+
+  const int64_t lists0 = (static_cast<int64_t>(side) * a.H + h) * a.nch;
+  const KeyT* src = static_cast<const KeyT*>(a.lists) + lists0 * a.K;
+  const uint32_t* cnt = a.counts + lists0;
+  const uint32_t flip = side == 0 ? 0u : kMax;
+  uint32_t total = static_cast<uint32_t>(a.nch) * a.K;
+  if (use_pre) {
+    if (tid < kWave) {
+      uint32_t carry = 0;
+      for (int c0 = 0; c0 < a.nch; c0 += kWave) {
+        const int c = c0 + tid;
+        const uint32_t v = c < a.nch ? cnt[c] : 0u;
+        const uint32_t incl = wave_inclusive_scan(v);
+        if (c < a.nch) pre[c] = carry + incl - v;
+        carry += __shfl(incl, kWave - 1);
+      }
+      if (tid == 0) pre[a.nch] = carry;
+    }
+    lds_barrier();
+    total = pre[a.nch];
+  }
+  if (!a.fixup && a.fail != nullptr) {
+    // the estimated bound holds iff the lists hold at least K keys (a list that was cut
+    // holds K by itself); the hi-side workgroup writes the hi flag
+    uint32_t held = total;
+    if (!use_pre) {
+      held = 0;
+      for (int c = tid; c < a.nch; c += NT) held += cnt[c];
+      held = wave_sum(held);
+      uint32_t* acc = ctl + kWaveScratch;
+      if (tid == 0) acc[0] = 0;
+      lds_barrier();
+      if (lane_id() == 0) atomicAdd(&acc[0], held);
+      lds_barrier();
+      held = acc[0];
+    }
+    const bool ok = held >= a.K;
+    if (tid == 0) a.fail[side * a.H + h] = ok ? 0u : 1u;
+    if (!ok) return;  // uniform: the fix-up pass redoes this head
+  }
+
+  for (uint32_t t0 = 0; t0 < total; t0 += kMergeTile) {
+    uint32_t k[kMergePerThread];
+#pragma unroll
+    for (int e = 0; e < kMergePerThread; ++e) {
+      const uint32_t i = t0 + static_cast<uint32_t>(e * NT + tid);
+      k[e] = kMax;
+      if (i < total) {
+        int64_t at = i;
+        if (use_pre) {
+          int c = 0, hi = a.nch;  // largest c with pre[c] <= i
+          while (hi - c > 1) {
+            const int mid = (c + hi) >> 1;
+            if (pre[mid] <= i) c = mid; else hi = mid;
+          }
+          at = static_cast<int64_t>(c) * a.K + (i - pre[c]);
+        }
+        k[e] = static_cast<uint32_t>(src[at]) ^ flip;  // an unused slot (kMax lo, 0 hi) reads as kMax
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < kMergePerThread; ++e) st.append_lo(k[e] < st.thr_lo, k[e]);
+    st.end_round();
+  }
+  st.finish();  // now exactly K (every head holds at least K values)
+
+  // Ascending sort of the side's K keys into the workspace: by counting for 16-bit keys
+  // spanning few top bytes, else a bitonic sort padded to P with the largest key.
+  const uint32_t K = a.K, P = a.P;
+  KeyT* dst = static_cast<KeyT*>(a.sorted) + (static_cast<int64_t>(side) * a.H + h) * K;
+  bool sorted = false;
+  if constexpr (sizeof(KeyT) == 2) sorted = value_sort16(buf, K, sort_lds, ctl, dst, tid);
+  if (!sorted) {
+    for (uint32_t i = K + tid; i < P; i += NT) buf[i] = static_cast<KeyT>(kMax);
+    lds_barrier();
+    bitonic_sort<KeyT>(buf, P, tid);
+    for (uint32_t i = tid; i < K; i += NT) dst[i] = buf[i];
+  }
+
+}
+
+// Shortest window U[i] - L[i] (float32), smallest i on ties, over the two sorted sides of
+// a head: L[i] = lo[i], U[i] = kMax - hi_c[K-1-i] (hi_c: the complemented hi keys in
+// ascending order).  One launch after the fix-up pass, so it reads each head's final lists.
+template <typename KeyT>
+__global__ __launch_bounds__(256) void calib_window_kernel(MergeArgs a, Batches bt) {
+  constexpr uint32_t kMax = KeyInfo<KeyT>::kMax;
+  constexpr int NT = 256;
+  __shared__ float wl[NT / kWave];
+  __shared__ uint32_t wi[NT / kWave];
+  const int batch = static_cast<int>(blockIdx.x) / bt.per;
+  const int h = static_cast<int>(blockIdx.x) - batch * bt.per;
+  a.sorted = in_region(a.sorted, batch * bt.region);
+  a.win_min += static_cast<int64_t>(batch) * a.H;
+  a.win_max += static_cast<int64_t>(batch) * a.H;
+  const uint32_t K = a.K;
+  const KeyT* lo = static_cast<const KeyT*>(a.sorted) + static_cast<int64_t>(h) * K;
+  const KeyT* hic = static_cast<const KeyT*>(a.sorted) + (static_cast<int64_t>(a.H) + h) * K;
+  const int tid = static_cast<int>(threadIdx.x);
+  float bl = __uint_as_float(0x7f800000u);
+  uint32_t bi = 0xffffffffu;
+  for (uint32_t i = static_cast<uint32_t>(tid); i < K; i += NT) {
+    const float len = value_of_key(kMax - hic[K - 1 - i], KeyT{}) - value_of_key(lo[i], KeyT{});
+    if (len < bl || bi == 0xffffffffu) {
+      bl = len;
+      bi = i;
     }
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
-    const float ol = __shfl_xor(best_len, o);
-    const uint32_t oi = __shfl_xor(best_i, o);
-    if (ol < best_len || (ol == best_len && oi < best_i)) {
-      best_len = ol;
-      best_i = oi;
+    const float ol = __shfl_xor(bl, o);
+    const uint32_t oi = static_cast<uint32_t>(__shfl_xor(static_cast<int>(bi), o));
+    if (ol < bl || (ol == bl && oi < bi)) {
+      bl = ol;
+      bi = oi;
     }
   }
-  float* wl = reinterpret_cast<float*>(ctl + kWaveScratch);
-  uint32_t* wi = ctl + kWaveScratch + 16;
   const int wave = tid / kWave;
   if (lane_id() == 0) {
-    wl[wave] = best_len;
-    wi[wave] = best_i;
+    wl[wave] = bl;
+    wi[wave] = bi;
   }
-  lds_barrier();
+  __syncthreads();
   if (tid == 0) {
-    float bl = wl[0];
-    uint32_t bi = wi[0];
     for (int w = 1; w < NT / kWave; ++w) {
       if (wl[w] < bl || (wl[w] == bl && wi[w] < bi)) {
         bl = wl[w];
         bi = wi[w];
       }
     }
-    a.win_min[h] = value_of_key(st.lo[bi], KeyT{});
-    a.win_max[h] = value_of_key(st.hi[bi], KeyT{});
+    a.win_min[h] = value_of_key(lo[bi], KeyT{});
+    a.win_max[h] = value_of_key(kMax - hic[K - 1 - bi], KeyT{});
   }
 }
 
@@ -1013,7 +1165,7 @@ __global__ __launch_bounds__(kWaveMergeThreads) void calib_merge_wave_kernel(Mer
   const KeyT* src = static_cast<const KeyT*>(a.lists) +
                     (static_cast<int64_t>(side) * a.H + h) * static_cast<int64_t>(n);
   const uint32_t flip = side == 0 ? 0u : kMax;  // hi side: complemented keys
-  if (a.fixup && a.fail[h] == 0) return;  // uniform over the workgroup
+  if (a.fixup && (a.fail[h] | a.fail[a.H + h]) == 0) return;  // uniform over the workgroup
 
   uint32_t k[R];
 #pragma unroll
@@ -1032,7 +1184,7 @@ __global__ __launch_bounds__(kWaveMergeThreads) void calib_merge_wave_kernel(Mer
     __syncthreads();
     const bool ok = best_at[0] >= K && best_at[1] >= K;
     __syncthreads();  // both waves have read best_at before it is reused
-    if (tid == 0) a.fail[h] = ok ? 0u : 1u;
+    if (tid < 2) a.fail[tid * a.H + h] = ok ? 0u : 1u;  // the head's result in both side flags
     if (!ok) return;  // uniform: the fix-up pass redoes this head
   }
   // least t with #{k <= t} >= K (entries past n hold kMax and never change that answer,
@@ -1148,7 +1300,8 @@ struct CalibPlan {
   int wave_merge_r = 0;  // and this many union keys per lane
   uint32_t rank = 0;     // rank of the sampled group minimum used as the bound
   bool estimate = false; // rank < K: the bound is checked by the merge, failures redone
-  size_t lists_bytes = 0, bounds_bytes = 0, fail_bytes = 0, total_bytes = 0;
+  // workspace per batch: lists | counts | sorted | bounds | fail
+  size_t lists_bytes = 0, counts_bytes = 0, sorted_bytes = 0, bounds_bytes = 0, fail_bytes = 0, total_bytes = 0;
 };
 
 int64_t next_pow2(int64_t v) {
@@ -1225,8 +1378,7 @@ int make_plan(int dtype, int64_t B, int64_t H, int64_t S, int64_t D, double rati
   p.cap_merge = static_cast<uint32_t>(2 * p.K + kMergeTile);
   p.P = static_cast<uint32_t>(next_pow2(p.K));
   p.lds_chunk = kCtlBytes + kStageBytes + (2 * static_cast<size_t>(p.cap_chunk) + tmp_keys) * p.key_bytes;
-  p.lds_merge = kCtlBytes + (2 * static_cast<size_t>(p.cap_merge) + p.K) * p.key_bytes;
-  if (p.lds_chunk > kLdsLimit || p.lds_merge > kLdsLimit) return FA3Q_ERR_UNSUPPORTED;
+  if (p.lds_chunk > kLdsLimit) return FA3Q_ERR_UNSUPPORTED;
 
   // Workgroups resident per CU (bound by LDS and by registers) times 256 CUs: one round of
   // chunks, each as long as possible, never shorter than kMinTilesPerChunk tiles.
@@ -1250,11 +1402,28 @@ int make_plan(int dtype, int64_t B, int64_t H, int64_t S, int64_t D, double rati
     }
   }
 
+  // the side merge: control block, the list-count prefix, one side's buffer and cut
+  // scratch, and the counting-sort bins (16-bit keys)
+  const size_t pre_bytes = p.nch <= kMaxPrefixLists ? round_up(static_cast<size_t>(p.nch + 1) * 4, 16) : 0;
+  const size_t sort_bytes = p.key_bytes == 2 ? kSortLdsBytes : 0;
+  {
+    // a buffer of up to 4K + one tile where the LDS allows: the estimated bounds let a few
+    // times K keys through per head, which then need no cut before the last
+    const int64_t fit = (static_cast<int64_t>(kLdsLimit) - static_cast<int64_t>(kCtlBytes + pre_bytes + sort_bytes) - 16) /
+                            static_cast<int64_t>(p.key_bytes) - p.K;
+    const int64_t want = std::min<int64_t>(4 * p.K + kMergeTile, fit);
+    if (want > static_cast<int64_t>(p.cap_merge)) p.cap_merge = static_cast<uint32_t>(want);
+  }
+  p.lds_merge = kCtlBytes + pre_bytes + round_up((static_cast<size_t>(p.cap_merge) + p.K) * p.key_bytes, 16) + sort_bytes;
+  if (p.wave_merge_e == 0 && p.lds_merge > kLdsLimit) return FA3Q_ERR_UNSUPPORTED;
+
   const size_t lists = static_cast<size_t>(H) * p.nch;
   p.lists_bytes = round_up(2 * lists * static_cast<size_t>(p.K) * p.key_bytes, 256);
+  p.counts_bytes = round_up(2 * lists * sizeof(uint32_t), 256);
+  p.sorted_bytes = p.wave_merge_e > 0 ? 0 : round_up(2 * static_cast<size_t>(H) * p.K * p.key_bytes, 256);
   p.bounds_bytes = round_up(2 * static_cast<size_t>(H) * sizeof(uint32_t), 256);
-  p.fail_bytes = round_up(static_cast<size_t>(H) * sizeof(uint32_t), 256);
-  p.total_bytes = p.lists_bytes + p.bounds_bytes + p.fail_bytes;
+  p.fail_bytes = round_up(2 * static_cast<size_t>(H) * sizeof(uint32_t), 256);
+  p.total_bytes = p.lists_bytes + p.counts_bytes + p.sorted_bytes + p.bounds_bytes + p.fail_bytes;
 
   return FA3Q_OK;
 }
@@ -1279,14 +1448,19 @@ int launch(const void* const* x, int64_t nb, int64_t H, const CalibPlan& p, floa
   using KeyT = InT;
   int st = allow_dynamic_lds(reinterpret_cast<const void*>(calib_chunk_kernel<InT>), p.lds_chunk);
   if (st != FA3Q_OK) return st;
-  st = allow_dynamic_lds(reinterpret_cast<const void*>(calib_merge_kernel<KeyT>), p.lds_merge);
-  if (st != FA3Q_OK) return st;
+  if (p.wave_merge_e == 0) {
+    st = allow_dynamic_lds(reinterpret_cast<const void*>(calib_merge_side_kernel<KeyT>), p.lds_merge);
+    if (st != FA3Q_OK) return st;
+  }
 
   Batches bt;
   for (int b = 0; b < kMaxBatches; ++b) bt.x[b] = b < nb ? x[b] : nullptr;
   bt.region = static_cast<int64_t>(p.total_bytes);
-  uint32_t* bounds = reinterpret_cast<uint32_t*>(static_cast<unsigned char*>(workspace) + p.lists_bytes);
-  uint32_t* fail = reinterpret_cast<uint32_t*>(static_cast<unsigned char*>(workspace) + p.lists_bytes + p.bounds_bytes);
+  unsigned char* w0 = static_cast<unsigned char*>(workspace);
+  uint32_t* counts = reinterpret_cast<uint32_t*>(w0 + p.lists_bytes);
+  void* sorted = w0 + p.lists_bytes + p.counts_bytes;
+  uint32_t* bounds = reinterpret_cast<uint32_t*>(w0 + p.lists_bytes + p.counts_bytes + p.sorted_bytes);
+  uint32_t* fail = reinterpret_cast<uint32_t*>(w0 + p.total_bytes - p.fail_bytes);
   SampleArgs sa;
   sa.x = nullptr;
   sa.bounds = bounds;
@@ -1309,6 +1483,7 @@ int launch(const void* const* x, int64_t nb, int64_t H, const CalibPlan& p, floa
   ChunkArgs ca;
   ca.x = nullptr;
   ca.lists = workspace;
+  ca.counts = counts;
   ca.bounds = bounds;
   ca.fail = nullptr;
   ca.L = p.L;
@@ -1324,6 +1499,8 @@ int launch(const void* const* x, int64_t nb, int64_t H, const CalibPlan& p, floa
   hipLaunchKernelGGL(calib_chunk_kernel<InT>, g_chunks, dim3(kChunkThreads), p.lds_chunk, stream, ca, bc);
   MergeArgs ma;
   ma.lists = workspace;
+  ma.counts = counts;
+  ma.sorted = sorted;
   ma.win_min = win_min;
   ma.win_max = win_max;
   ma.fail = p.estimate ? fail : nullptr;
@@ -1338,8 +1515,12 @@ int launch(const void* const* x, int64_t nb, int64_t H, const CalibPlan& p, floa
       launch_wave_merge<KeyT, 32>(p.wave_merge_e, nb * H, m, bt, stream);
     else if (p.wave_merge_e > 0)
       launch_wave_merge<KeyT, 64>(p.wave_merge_e, nb * H, m, bt, stream);
-    else
-      hipLaunchKernelGGL(calib_merge_kernel<KeyT>, g_heads, dim3(kMergeThreads), p.lds_merge, stream, m, bt);
+    else {
+      Batches bs = bt;
+      bs.per = static_cast<int32_t>(2 * H);
+      hipLaunchKernelGGL(calib_merge_side_kernel<KeyT>, dim3(static_cast<unsigned>(2 * nb * H)),
+                         dim3(kMergeThreads), p.lds_merge, stream, m, bs);
+    }
   };
   merge(ma);
   if (p.estimate) {
@@ -1351,6 +1532,8 @@ int launch(const void* const* x, int64_t nb, int64_t H, const CalibPlan& p, floa
     mf.fixup = 1;
     merge(mf);
   }
+  if (p.wave_merge_e == 0)  // the windows of every head from its final sorted sides
+    hipLaunchKernelGGL(calib_window_kernel<KeyT>, g_heads, dim3(256), 0, stream, ma, bt);
   return launch_status();
 }
 
@@ -1386,15 +1569,18 @@ using namespace fa3q;
 
 extern "C" int64_t fa3q_calibrate_max_windows(int dtype) {
   // The chunk kernel keeps 2*cap + K keys (cap = 2K + one round of appends) after its
-  // control block and stage; the merge kernel 2*cap + K keys (cap = 2K + one merge tile)
-  // after its control block.  Largest K for which both fit the 160 KiB a gfx950
+  // control block and stage; the side merge cap + K keys (cap = 2K + one merge tile) after
+  // its control block and a list-count prefix of up to kMaxPrefixLists + 1 words, then the
+  // counting-sort bins for 16-bit keys.  Largest K for which both fit the 160 KiB a gfx950
   // workgroup may use.
   if (dtype != FA3Q_F32 && dtype != FA3Q_BF16) return 0;
   const int64_t kb = dtype == FA3Q_BF16 ? 2 : 4;
   const int64_t round = dtype == FA3Q_BF16 ? chunk_room<uint16_t>() : chunk_room<uint32_t>();
   const int64_t lds = static_cast<int64_t>(kLdsLimit);
   const int64_t chunk = (lds - static_cast<int64_t>(kCtlBytes + kStageBytes) - 2 * round * kb) / (5 * kb);
-  const int64_t merge = (lds - static_cast<int64_t>(kCtlBytes) - 2 * kMergeTile * kb) / (5 * kb);
+  const int64_t pre = static_cast<int64_t>(round_up(static_cast<size_t>(kMaxPrefixLists + 1) * 4, 16));
+  const int64_t sort = kb == 2 ? static_cast<int64_t>(kSortLdsBytes) : 0;
+  const int64_t merge = (lds - static_cast<int64_t>(kCtlBytes) - pre - sort - 16 - kMergeTile * kb) / (3 * kb);
   return std::min(chunk, merge);
 }
 

@@ -156,6 +156,18 @@ def test_large_k_uses_more_than_64k_lds(fa):
     _check(fa, x[:, :, :64], (0.5,), "large_k_f32")               # N = 8192, K = 4097
 
 
+def test_tails_across_many_binades(fa):
+    # log-uniform magnitudes over 2^-60 .. 2^60: the K tail keys span more top bytes than
+    # the counting sort takes, so the side merge sorts them bitonically; narrow tails (the
+    # other cases) take the counting sort
+    rng = np.random.default_rng(37)
+    B, H, S, D = 1, 2, 8192, 128
+    mag = np.exp2(rng.uniform(-60.0, 60.0, size=(B, H, S, D)))
+    x = (np.where(rng.random((B, H, S, D)) < 0.5, -1.0, 1.0) * mag).astype(np.float32)
+    xt = torch.from_numpy(x).to(torch.bfloat16)
+    _check(fa, xt, (0.99, 0.999), "wide_tails")
+
+
 def test_estimated_bound_that_fails_is_redone_exactly(fa):
     # K = 10487 against 2048 sampled groups: the head bound is an estimate, checked by the
     # merge.  Values placed where the evenly spaced sample reads (runs of 256 vectors every
@@ -178,15 +190,15 @@ def test_estimated_bound_that_fails_is_redone_exactly(fa):
     xt = torch.from_numpy(x.reshape(B, H, S, D)).to(torch.bfloat16)
     _check(fa, xt, (0.99,), "estimate_fails")
     _check(fa, xt, (0.999, 0.9999), "estimate_fails_other_ratios")
-    # the per-head check flags (the workspace's last 256-byte block) show that both heads
-    # failed the check and took the second pass
+    # the check flags (the workspace's last 256-byte block, low side of each head, then high
+    # side) show which sides failed: both of head 0, the low side of head 1
     dev = torch.device("cuda:0")
     nbytes = fa.fa3q_calibrate_workspace_bytes(torch.bfloat16, B, H, S, D, 0.99)
     ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
     fa.fa3q_calibrate_perhead(xt.to(dev), 0.99, workspace=ws)
     torch.cuda.synchronize()
-    flags = ws[nbytes - 256:nbytes - 256 + 4 * H].cpu().view(torch.int32).numpy()
-    assert flags.tolist() == [1, 1], flags
+    flags = ws[nbytes - 256:nbytes - 256 + 8 * H].cpu().view(torch.int32).numpy()
+    assert flags.tolist() == [1, 1, 1, 0], flags
 
 
 def test_batches_in_one_call_match_the_oracle(fa):

@@ -867,25 +867,27 @@ constexpr int kSortBins = kSortBuckets * 256;
 constexpr size_t kSortLdsBytes = (kSortBins + 256 + kSortBuckets) * 4;  // bins, bucket of each top byte, top byte of each bucket
 static_assert(kSortBins == 4 * kMergeThreads, "the prefix takes four bins per thread");
 
-// Ascending sort of the K 16-bit keys buf[0..K) into dst (device memory) by counting: equal
-// keys are indistinguishable, so the sorted sequence follows from the counts of each key
-// value.  Keys are counted per (top byte, low byte) over the top bytes present; output
-// slot i holds the key of the bin whose prefix range contains i.  Returns false (nothing
-// written) when the keys span more than kSortBuckets top bytes.
-__device__ bool value_sort16(const uint16_t* buf, uint32_t K, uint32_t* sort_lds, uint32_t* ctl, uint16_t* dst,
-                             int tid) {
+// The K smallest of the n >= K 16-bit keys buf[0..n), in ascending order, into dst (device
+// memory), by counting: equal keys are indistinguishable, so the sorted sequence follows
+// from how many times each key value occurs.  A top-byte histogram locates the top byte of
+// the K-th smallest key; the keys at or below it are counted per (top byte, low byte)
+// over the top bytes present, and output slot i < K holds the key of the bin whose prefix
+// range contains i.  Returns false (nothing written) when those keys span more than
+// kSortBuckets top bytes.
+__device__ bool value_select_sort16(const uint16_t* buf, uint32_t n, uint32_t K, uint32_t* sort_lds, uint32_t* ctl,
+                                    uint16_t* dst, int tid) {
   constexpr int NT = kMergeThreads;
   uint32_t* bins = sort_lds;                 // [kSortBins]
-  uint32_t* bidx = sort_lds + kSortBins;     // [256] bucket of each present top byte
+  uint32_t* bidx = sort_lds + kSortBins;     // [256] bucket of each counted top byte
   uint32_t* btop = bidx + 256;               // [kSortBuckets] top byte of each bucket
   uint32_t* hist = ctl + kHist;              // [256] keys per top byte
   for (int i = tid; i < 256; i += NT) hist[i] = 0;
   for (int i = tid; i < kSortBins; i += NT) bins[i] = 0;
   lds_barrier();
   // tail keys share few top bytes: one atomic per distinct top byte of a wave
-  const uint32_t k_round = (K + NT - 1) / NT * NT;
-  for (uint32_t i = tid; i < k_round; i += NT) {
-    const bool act = i < K;
+  const uint32_t n_round = (n + NT - 1) / NT * NT;
+  for (uint32_t i = tid; i < n_round; i += NT) {
+    const bool act = i < n;
     const uint32_t d = act ? static_cast<uint32_t>(buf[i]) >> 8 : 0u;
     uint64_t pending = __ballot(act);
     while (pending != 0) {
@@ -898,14 +900,35 @@ __device__ bool value_sort16(const uint16_t* buf, uint32_t K, uint32_t* sort_lds
   }
   lds_barrier();
   if (tid < kWave) {
-    uint32_t f[4], n = 0;
+    // the top byte t* holding the K-th smallest key, then the buckets: top bytes <= t* present
+    uint32_t c[4], sum = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      f[q] = hist[4 * tid + q] != 0 ? 1u : 0u;
-      n += f[q];
+      c[q] = hist[4 * tid + q];
+      sum += c[q];
     }
-    const uint32_t incl = wave_inclusive_scan(n);
-    uint32_t idx = incl - n;
+    const uint32_t incl = wave_inclusive_scan(sum);
+    uint32_t cum = incl - sum;
+    uint32_t tk = 0;
+    bool mine = false;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (!mine && cum < K && K <= cum + c[q]) {
+        tk = 4 * tid + q;
+        mine = true;
+      }
+      cum += c[q];
+    }
+    const uint64_t who = __ballot(mine);  // one lane (n >= K); none would count every key
+    const uint32_t t_star = who ? __builtin_amdgcn_readlane(tk, __ffsll(static_cast<unsigned long long>(who)) - 1) : 255u;
+    uint32_t f[4], m = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f[q] = (c[q] != 0 && static_cast<uint32_t>(4 * tid + q) <= t_star) ? 1u : 0u;
+      m += f[q];
+    }
+    const uint32_t mincl = wave_inclusive_scan(m);
+    uint32_t idx = mincl - m;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       if (f[q]) {
@@ -914,14 +937,18 @@ __device__ bool value_sort16(const uint16_t* buf, uint32_t K, uint32_t* sort_lds
         ++idx;
       }
     }
-    if (tid == kWave - 1) ctl[kSelCount] = incl;
+    if (tid == kWave - 1) {
+      ctl[kSelCount] = mincl;
+      ctl[kSelDigit] = t_star;
+    }
   }
   lds_barrier();
   const uint32_t nbk = ctl[kSelCount];
+  const uint32_t t_star = ctl[kSelDigit];
   if (nbk > kSortBuckets) return false;  // uniform
-  for (uint32_t i = tid; i < K; i += NT) {
+  for (uint32_t i = tid; i < n; i += NT) {
     const uint32_t k = buf[i];
-    atomicAdd(&bins[bidx[k >> 8] * 256 + (k & 255u)], 1u);
+    if ((k >> 8) <= t_star) atomicAdd(&bins[bidx[k >> 8] * 256 + (k & 255u)], 1u);
   }
   lds_barrier();
   // exclusive prefix over the nbk * 256 bins, four consecutive bins per thread
@@ -947,7 +974,8 @@ __device__ bool value_sort16(const uint16_t* buf, uint32_t K, uint32_t* sort_lds
     run += c[q];
   }
   lds_barrier();
-  // slot i: the largest bin j with prefix[j] <= i (empty bins share the next bin's prefix)
+  // slot i: the largest bin j with prefix[j] <= i (empty bins share the next bin's prefix);
+  // the counted keys number at least K, so every slot i < K lies in a bin
   for (uint32_t i = tid; i < K; i += NT) {
     uint32_t lo = 0, hi = nbins;
     while (hi - lo > 1) {
@@ -1040,7 +1068,23 @@ __global__ __launch_bounds__(kMergeThreads) void calib_merge_side_kernel(MergeAr
     if (!ok) return;  // uniform: the fix-up pass redoes this head
   }
 
-  for (uint32_t t0 = 0; t0 < total; t0 += kMergeTile) {
+  // Every list key fits the buffer (the usual case under a sampled bound): copy them as they
+  // are and let the counting sort select the K smallest; else filter and cut as the chunk
+  // kernel does.
+  const bool direct = sizeof(KeyT) == 2 && use_pre && total <= a.cap;
+  if (direct) {
+    for (uint32_t i = tid; i < total; i += NT) {
+      int c = 0, hi = a.nch;  // largest c with pre[c] <= i
+      while (hi - c > 1) {
+        const int mid = (c + hi) >> 1;
+        if (pre[mid] <= i) c = mid; else hi = mid;
+      }
+      buf[i] = static_cast<KeyT>(static_cast<uint32_t>(src[static_cast<int64_t>(c) * a.K + (i - pre[c])]) ^ flip);
+    }
+    lds_barrier();
+    st.base_lo = total;
+  }
+  for (uint32_t t0 = 0; !direct && t0 < total; t0 += kMergeTile) {
     uint32_t k[kMergePerThread];
 #pragma unroll
     for (int e = 0; e < kMergePerThread; ++e) {
@@ -1063,15 +1107,15 @@ __global__ __launch_bounds__(kMergeThreads) void calib_merge_side_kernel(MergeAr
     for (int e = 0; e < kMergePerThread; ++e) st.append_lo(k[e] < st.thr_lo, k[e]);
     st.end_round();
   }
-  st.finish();  // now exactly K (every head holds at least K values)
-
-  // Ascending sort of the side's K keys into the workspace: by counting for 16-bit keys
-  // spanning few top bytes, else a bitonic sort padded to P with the largest key.
+  // The side's K smallest keys, ascending, into the workspace: by counting for 16-bit keys
+  // spanning few top bytes (straight from the held keys), else a cut to exactly K and a
+  // bitonic sort padded to P with the largest key.
   const uint32_t K = a.K, P = a.P;
   KeyT* dst = static_cast<KeyT*>(a.sorted) + (static_cast<int64_t>(side) * a.H + h) * K;
   bool sorted = false;
-  if constexpr (sizeof(KeyT) == 2) sorted = value_sort16(buf, K, sort_lds, ctl, dst, tid);
+  if constexpr (sizeof(KeyT) == 2) sorted = value_select_sort16(buf, st.base_lo, K, sort_lds, ctl, dst, tid);
   if (!sorted) {
+    st.finish();  // now exactly K (every head holds at least K values)
     for (uint32_t i = K + tid; i < P; i += NT) buf[i] = static_cast<KeyT>(kMax);
     lds_barrier();
     bitonic_sort<KeyT>(buf, P, tid);

@@ -168,6 +168,15 @@ def test_tails_across_many_binades(fa):
     _check(fa, xt, (0.99, 0.999), "wide_tails")
 
 
+def test_more_chunk_lists_than_the_merge_prefix_holds(fa):
+    # 2560 slabs of 128 values: one chunk per slab, so 2560 lists per head, past the
+    # 2048-list prefix of the side merge, which then reads every list slot (unused ones
+    # fail its filter); K = 328 on 327,680 values per head
+    x = synth.activations((2560, 2, 16, 8), synth.head_sigmas(2, seed=51), law="t3", outlier_frac=0.001,
+                          outlier_mult=40.0, dtype=torch.bfloat16, seed=52)
+    _check(fa, x, (0.999,), "many_lists")
+
+
 def test_estimated_bound_that_fails_is_redone_exactly(fa):
     # K = 10487 against 2048 sampled groups: the head bound is an estimate, checked by the
     # merge.  Values placed where the evenly spaced sample reads (runs of 256 vectors every

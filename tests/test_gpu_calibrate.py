@@ -171,7 +171,7 @@ def test_tails_across_many_binades(fa):
 def test_more_chunk_lists_than_the_merge_prefix_holds(fa):
     # 2560 slabs of 128 values: one chunk per slab, so 2560 lists per head, past the
     # 2048-list prefix of the side merge, which then reads every list slot (unused ones
-    # fail its filter); K = 328 on 327,680 values per head
+    # fail its filter); K = 329 on 327,680 values per head
     x = synth.activations((2560, 2, 16, 8), synth.head_sigmas(2, seed=51), law="t3", outlier_frac=0.001,
                           outlier_mult=40.0, dtype=torch.bfloat16, seed=52)
     _check(fa, x, (0.999,), "many_lists")

@@ -9,9 +9,10 @@
 // starting at i is [L[i], U[i]] with L the K smallest values and U the K largest, both
 // ascending.  So instead of sorting N values the library selects the two tails:
 //
-//   calib_sample_kernel  one workgroup per head reads a small evenly spaced sample of the
-//                        head (32 runs of 256 16-byte vectors, about 3% of a 2M-value
-//                        head) and sets per-head bounds: the K-th smallest minimum of a
+//   calib_sample_kernel  one workgroup per head reads a small sample spread over the
+//                        head (32 runs of 256 16-byte vectors, one per 1/32 of the head at
+//                        a fixed phase inside it, about 3% of a 2M-value head) and sets
+//                        per-head bounds: the K-th smallest minimum of a
 //                        group of sampled vectors (K-th largest maximum), which has at
 //                        least K of the head's values at or beyond it.
 //   calib_chunk_kernel   one HBM pass.  Each workgroup streams a contiguous chunk of one
@@ -495,7 +496,7 @@ struct SampleArgs {
   uint32_t K;
 };
 
-// Head bounds from a sample: kSampleRuns evenly spaced runs of kSampleThreads consecutive
+// Head bounds from a sample: kSampleRuns spread-out runs of kSampleThreads consecutive
 // 16-byte vectors of the head (all of it when it is small).  A thread's vectors of
 // kSampleGroupRuns runs form a group of keys; the K-th smallest of the M sampled group
 // minima has at least K of the head's keys at or below it (one per group), so the head's
@@ -1372,13 +1373,18 @@ int make_plan(int dtype, int64_t B, int64_t H, int64_t S, int64_t D, double rati
   p.K = p.N - p.t + 1;
   if (p.K > fa3q_calibrate_max_windows(dtype)) return FA3Q_ERR_UNSUPPORTED;
 
-  // Sample runs: evenly spaced over the head's B*L/vec vectors, or back to back (covering
+  // Sample runs: one per 1/32 of the head's B*L/vec vectors, or back to back (covering
   // the whole head) when it has fewer than kSampleRuns runs' worth.
   const int64_t Lv = p.L / vec, Q = B * Lv;
+  // Run j starts at a fixed pseudo-random phase inside its stride (an odd multiple of a
+  // 16-bit golden-ratio step, as a fraction of the free range), so that runs do not line up
+  // with slab starts or any other period of the data: an over-sampled structure (large
+  // first tokens of every sequence, say) would make an estimated bound fail for every head.
   const int64_t stride = std::max<int64_t>(kSampleThreads, Q / kSampleRuns);
   int64_t m = 0;
   for (int j = 0; j < kSampleRuns; ++j) {
-    const int64_t q0 = j * stride;
+    const int64_t phase = ((((2 * j + 1) * 40503) & 0xffff) * (stride - kSampleThreads) >> 16) & ~int64_t{7};  // whole lines
+    const int64_t q0 = j * stride + phase;
     p.sample_n[j] = static_cast<uint32_t>(std::min<int64_t>(kSampleThreads, std::max<int64_t>(0, Q - q0)));
     const int64_t b = p.sample_n[j] ? q0 / Lv : 0, w = p.sample_n[j] ? q0 - b * Lv : 0;
     p.sample_off[j] = (b * H * Lv + w) * vec;

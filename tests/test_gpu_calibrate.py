@@ -177,6 +177,39 @@ def test_more_chunk_lists_than_the_merge_prefix_holds(fa):
     _check(fa, x, (0.999,), "many_lists")
 
 
+def _run_start(j: int, q_vecs: int) -> int:
+    """First vector of sample run j: the library spreads 32 runs of 256 vectors over the
+    head, run j inside [j * stride, (j + 1) * stride) at a fixed phase."""
+    stride = max(256, q_vecs // 32)
+    return j * stride + ((((((2 * j + 1) * 40503) & 0xFFFF) * (stride - 256)) >> 16) & ~7)
+
+
+def _workspace_flags(fa, x: torch.Tensor, ratio: float) -> list:
+    """The check flags (the workspace's last 256-byte block: low side of each head, then
+    high side) after one call."""
+    dev = torch.device("cuda:0")
+    B, H, S, D = x.shape
+    nbytes = fa.fa3q_calibrate_workspace_bytes(x.dtype, B, H, S, D, ratio)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+    fa.fa3q_calibrate_perhead(x.to(dev), ratio, workspace=ws)
+    torch.cuda.synchronize()
+    return ws[nbytes - 256:nbytes - 256 + 8 * H].cpu().view(torch.int32).numpy().tolist()
+
+
+def test_large_first_tokens_do_not_defeat_the_estimated_bound(fa):
+    # every sequence starts with four tokens of large values (as attention-sink tokens
+    # have): 4 slabs, so runs at multiples of 1/32 of the head would all start on a slab
+    # start and sample every one of them; the run phases keep the sample representative,
+    # the estimated bound holds and no head takes the fix-up pass
+    B, H, S, D = 4, 2, 8192, 128
+    rng = np.random.default_rng(41)
+    x = rng.standard_t(3, size=(B, H, S, D)).astype(np.float32)
+    x[:, :, :4, :] = np.where(rng.random((B, H, 4, D)) < 0.5, -30.0, 30.0)
+    xt = torch.from_numpy(x).to(torch.bfloat16)
+    _check(fa, xt, (0.999,), "first_tokens")
+    assert _workspace_flags(fa, xt, 0.999) == [0] * (2 * H)
+
+
 def test_estimated_bound_that_fails_is_redone_exactly(fa):
     # K = 10487 against 2048 sampled groups: the head bound is an estimate, checked by the
     # merge.  Values placed where the evenly spaced sample reads (runs of 256 vectors every
@@ -186,28 +219,20 @@ def test_estimated_bound_that_fails_is_redone_exactly(fa):
     B, H, S, D = 1, 2, 8192, 128
     vec = 8                                   # bf16 values per 16-byte vector
     q_vecs = B * S * D // vec                 # vectors per head
-    stride = max(256, q_vecs // 32)
     rng = np.random.default_rng(23)
     x = np.ones((B, H, S * D), np.float32)
     x[0, 1] = rng.standard_normal(S * D).astype(np.float32)
     for g in range(8):
-        lo_run, hi_run = 4 * g, 4 * g + 1
+        lo_run, hi_run = _run_start(4 * g, q_vecs), _run_start(4 * g + 1, q_vecs)
         for t in range(256):
-            x[0, 0, (lo_run * stride + t) * vec] = -7.0        # head 0: both sides fail
-            x[0, 0, (hi_run * stride + t) * vec] = 9.0
-            x[0, 1, (lo_run * stride + t) * vec + 3] = -50.0   # head 1: the low side fails
+            x[0, 0, (lo_run + t) * vec] = -7.0        # head 0: both sides fail
+            x[0, 0, (hi_run + t) * vec] = 9.0
+            x[0, 1, (lo_run + t) * vec + 3] = -50.0   # head 1: the low side fails
     xt = torch.from_numpy(x.reshape(B, H, S, D)).to(torch.bfloat16)
     _check(fa, xt, (0.99,), "estimate_fails")
     _check(fa, xt, (0.999, 0.9999), "estimate_fails_other_ratios")
-    # the check flags (the workspace's last 256-byte block, low side of each head, then high
-    # side) show which sides failed: both of head 0, the low side of head 1
-    dev = torch.device("cuda:0")
-    nbytes = fa.fa3q_calibrate_workspace_bytes(torch.bfloat16, B, H, S, D, 0.99)
-    ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
-    fa.fa3q_calibrate_perhead(xt.to(dev), 0.99, workspace=ws)
-    torch.cuda.synchronize()
-    flags = ws[nbytes - 256:nbytes - 256 + 8 * H].cpu().view(torch.int32).numpy()
-    assert flags.tolist() == [1, 1, 1, 0], flags
+    # the check flags show which sides failed: both of head 0, the low side of head 1
+    assert _workspace_flags(fa, xt, 0.99) == [1, 1, 1, 0]
 
 
 def test_batches_in_one_call_match_the_oracle(fa):
@@ -270,7 +295,7 @@ def test_batches_with_an_estimated_bound_that_fails_in_one_batch(fa):
     # its check fail; batches 0 and 2 are ordinary.  Each batch has its own flags and lists.
     dev = torch.device("cuda:0")
     B, H, S, D = 1, 2, 8192, 128
-    vec, stride = 8, max(256, (B * S * D // 8) // 32)
+    vec, q_vecs = 8, B * S * D // 8
     rng = np.random.default_rng(29)
     xs = []
     for i in range(3):
@@ -278,8 +303,8 @@ def test_batches_with_an_estimated_bound_that_fails_in_one_batch(fa):
         if i == 1:
             for g in range(8):
                 for t in range(256):
-                    x[0, :, (4 * g * stride + t) * vec] = -70.0
-                    x[0, :, ((4 * g + 1) * stride + t) * vec] = 90.0
+                    x[0, :, (_run_start(4 * g, q_vecs) + t) * vec] = -70.0
+                    x[0, :, (_run_start(4 * g + 1, q_vecs) + t) * vec] = 90.0
         xs.append(torch.from_numpy(x.reshape(B, H, S, D)).to(torch.bfloat16))
     rmin = torch.empty(H, dtype=torch.float32, device=dev)
     rmax = torch.empty(H, dtype=torch.float32, device=dev)

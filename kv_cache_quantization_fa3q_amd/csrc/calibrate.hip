@@ -1186,7 +1186,9 @@ __global__ __launch_bounds__(256) void calib_window_kernel(MergeArgs a, Batches 
 // registers, summed with DPP), the K keys below it (ballot appends, then copies of the
 // K-th key up to K), and a bitonic sort of them, E keys per lane (element lane*E + e),
 // exchanging registers across lanes for the wide steps.  One barrier, then the window.
-constexpr int kWaveMergeRegs = 64;  // most union keys per lane
+// Up to 32 union keys per lane.  Larger unions (64 per lane at K = 421 on the long-context
+// shape) took 32 us against 13 us (plus the window kernel) for the side merge.
+constexpr int kWaveMergeRegs = 32;  // most union keys per lane
 constexpr int kWaveMergeThreads = 2 * kWave;
 
 template <typename KeyT, int R, int E>
@@ -1342,7 +1344,6 @@ struct CalibPlan {
   size_t lds_chunk = 0, lds_merge = 0;
   size_t key_bytes = 0;
   int wave_merge_e = 0;  // > 0: the two-wave merge with this many sorted keys per lane
-  int wave_merge_r = 0;  // and this many union keys per lane
   uint32_t rank = 0;     // rank of the sampled group minimum used as the bound
   bool estimate = false; // rank < K: the bound is checked by the merge, failures redone
   // workspace per batch: lists | counts | sorted | bounds | fail
@@ -1443,7 +1444,6 @@ int make_plan(int dtype, int64_t B, int64_t H, int64_t S, int64_t D, double rati
   if (B * p.cps > (int64_t{1} << 30) || H * B * p.cps > (int64_t{1} << 31) - 1) return FA3Q_ERR_SHAPE;
   p.nch = static_cast<int32_t>(B * p.cps);
   if (static_cast<int64_t>(p.nch) * p.K <= static_cast<int64_t>(kWave) * kWaveMergeRegs) {
-    p.wave_merge_r = static_cast<int64_t>(p.nch) * p.K <= static_cast<int64_t>(kWave) * 32 ? 32 : 64;
     for (int e = 1; e <= 16; e <<= 1) {
       if (p.K <= static_cast<int64_t>(kWave) * e) {
         p.wave_merge_e = e;
@@ -1561,10 +1561,8 @@ int launch(const void* const* x, int64_t nb, int64_t H, const CalibPlan& p, floa
   ma.cap = p.cap_merge;
   ma.P = p.P;
   auto merge = [&](const MergeArgs& m) {
-    if (p.wave_merge_e > 0 && p.wave_merge_r == 32)
-      launch_wave_merge<KeyT, 32>(p.wave_merge_e, nb * H, m, bt, stream);
-    else if (p.wave_merge_e > 0)
-      launch_wave_merge<KeyT, 64>(p.wave_merge_e, nb * H, m, bt, stream);
+    if (p.wave_merge_e > 0)
+      launch_wave_merge<KeyT, kWaveMergeRegs>(p.wave_merge_e, nb * H, m, bt, stream);
     else {
       Batches bs = bt;
       bs.per = static_cast<int32_t>(2 * H);

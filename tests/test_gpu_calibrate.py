@@ -235,18 +235,27 @@ def test_estimated_bound_that_fails_is_redone_exactly(fa):
     assert _workspace_flags(fa, xt, 0.99) == [1, 1, 1, 0]
 
 
-def test_batches_in_one_call_match_the_oracle(fa):
+BATCH_CASES = [
+    # dtype, shape, ratio, batches: register merge; 16 batches; side merge (8 lists of K = 526); float32 keys
+    (torch.bfloat16, (2, 4, 2048, 64), 0.999, 3),
+    (torch.bfloat16, (2, 4, 2048, 64), 0.999, 16),
+    (torch.bfloat16, (4, 3, 4096, 32), 0.999, 2),
+    (torch.float32, (2, 4, 1024, 64), 0.999, 3),
+]
+
+
+@pytest.mark.parametrize("dtype,shape,ratio,nb", BATCH_CASES, ids=["bf16", "bf16_16", "bf16_side", "f32"])
+def test_batches_in_one_call_match_the_oracle(fa, dtype, shape, ratio, nb):
     dev = torch.device("cuda:0")
-    shape, ratio = (2, 4, 2048, 64), 0.999
     sigma = synth.head_sigmas(shape[1], seed=321)
-    xs = [synth.activations(shape, sigma, law="t3", outlier_frac=0.0005, outlier_mult=40.0, dtype=torch.bfloat16,
-                            seed=330 + i) for i in range(3)]
-    log(f"calibrate_batches: 3 x {shape} ratio={ratio}")
+    xs = [synth.activations(shape, sigma, law="t3", outlier_frac=0.0005, outlier_mult=40.0, dtype=dtype,
+                            seed=330 + i) for i in range(nb)]
+    log(f"calibrate_batches: {nb} x {shape} {dtype} ratio={ratio}")
     H = shape[1]
     rmin = torch.empty(H, dtype=torch.float32, device=dev)
     rmax = torch.empty(H, dtype=torch.float32, device=dev)
-    wmin = torch.empty((3, H), dtype=torch.float32, device=dev)
-    wmax = torch.empty((3, H), dtype=torch.float32, device=dev)
+    wmin = torch.empty((nb, H), dtype=torch.float32, device=dev)
+    wmax = torch.empty((nb, H), dtype=torch.float32, device=dev)
     fa.fa3q_calibrate_batches([x.to(dev) for x in xs], ratio, rmin, rmax, True, wmin, wmax)
     torch.cuda.synchronize()
     run_lo, run_hi = oracle.init_running(H)

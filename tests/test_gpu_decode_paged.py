@@ -113,6 +113,14 @@ def test_mla_dims(fa):
     _step(fa, "mla", c, [5, 64, 300, 511], True)
 
 
+def test_widest_values_and_one_page_sequences(fa):
+    # Dv = 512 (64 lanes per token), pages of 16 tokens, one page per sequence
+    B, H, P, MP, Dn, Dr, Dv = 3, 2, 16, 1, 32, 16, 512
+    c = _case(B, H, P, MP, Dn, Dr, Dv, seed=635)
+    _step(fa, "wide_v_append", c, [0, 7, 15], True)
+    _step(fa, "wide_v_read", c, [1, 9, 16], False)
+
+
 def test_no_rope_part(fa):
     B, H, P, MP, Dn, Dr, Dv = 3, 4, 16, 5, 64, 0, 64
     c = _case(B, H, P, MP, Dn, Dr, Dv, seed=630)

@@ -440,6 +440,7 @@ struct ChunkArgs {
                            // either is set (nullptr: the first pass)
   uint32_t K;
   uint32_t cap;
+  int32_t pad;             // fill the unused list slots (the merges that read every slot need it)
 };
 
 template <typename InT>
@@ -742,14 +743,16 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
   }
   st.finish();
 
-  // Fixed-size list per chunk; slots past the held count get keys that fail both filters.
+  // Fixed-size list per chunk and its count; with `pad`, slots past the held count get keys
+  // that fail both filters (the side merge with a count prefix reads only the held keys).
   const int64_t list = static_cast<int64_t>(h) * a.nch + c;
   const int64_t heads_lists = static_cast<int64_t>(a.H) * a.nch;
   KeyT* out_lo = static_cast<KeyT*>(a.lists) + list * a.K;
   KeyT* out_hi = static_cast<KeyT*>(a.lists) + (heads_lists + list) * a.K;
-  for (uint32_t i = tid; i < a.K; i += NT) {
-    out_lo[i] = i < st.base_lo ? st.lo[i] : static_cast<KeyT>(KeyInfo<KeyT>::kMax);
-    out_hi[i] = i < st.base_hi ? st.hi[i] : static_cast<KeyT>(0);
+  const uint32_t n_out = a.pad ? a.K : max(st.base_lo, st.base_hi);
+  for (uint32_t i = tid; i < n_out; i += NT) {
+    if (a.pad || i < st.base_lo) out_lo[i] = i < st.base_lo ? st.lo[i] : static_cast<KeyT>(KeyInfo<KeyT>::kMax);
+    if (a.pad || i < st.base_hi) out_hi[i] = i < st.base_hi ? st.hi[i] : static_cast<KeyT>(0);
   }
   if (tid == 0) {
     a.counts[list] = st.base_lo;
@@ -1543,6 +1546,7 @@ int launch(const void* const* x, int64_t nb, int64_t H, const CalibPlan& p, floa
   ca.nch = p.nch;
   ca.K = static_cast<uint32_t>(p.K);
   ca.cap = p.cap_chunk;
+  ca.pad = (p.wave_merge_e > 0 || p.nch > kMaxPrefixLists) ? 1 : 0;
   Batches bc = bt;
   bc.per = static_cast<int32_t>(H * p.nch);
   const dim3 g_chunks(static_cast<unsigned>(nb * H * p.nch));

@@ -6,7 +6,7 @@ the q, k and v activations carry a scale and an offset of shape
 The pages print the tables' shapes and dtypes but no formula and no way to
 compute them; here they are inputs.
 
-Readings (also in DESIGN.md):
+Readings:
 
 * S1 the plain asymmetric INT8 code: ``code = clamp(rne(fl32(fl32(x / s) + o)),
   -128, 127)`` with ``s = scale[h, d]`` and ``o = offset[h, d]`` widened exactly

@@ -6,7 +6,7 @@ attention operator of the decode phase); MindIE page "Attention Quantization",
 overview (same purpose for q/k/v).  The pages show no attention operator, so
 this is the textbook single-query softmax attention over the dequantised cache.
 
-Readings (also in DESIGN.md):
+Readings:
 
 * A1 the dequantised K-nope value is ``scale[h] * code`` (per head); the score
   is ``sm_scale * (q_nope . k_nope + q_rope . k_rope)``.
@@ -53,7 +53,7 @@ def decode_append_attn(q_bits, k_new_bits, v_new_bits, scale, codes, rope_bits, 
                        sm_scale: float, Dn: int):
     """One decode step on a cache of capacity ``T`` with ragged lengths.
 
-    Readings (also in the design doc): A5 sequence ``b`` holds ``kv_len[b]`` cached
+    Readings: A5 sequence ``b`` holds ``kv_len[b]`` cached
     tokens at positions ``0 .. kv_len[b]-1``; the rest of its capacity is not
     part of the attention.  A6 a new token (``k_new (B,H,Dn+Dr)``,
     ``v_new (B,H,Dv)`` bf16 patterns) goes to the next free position
@@ -95,7 +95,7 @@ def decode_paged_attn(q_bits, k_new_bits, v_new_bits, scale, code_pool, rope_poo
                       sm_scale: float, Dn: int):
     """:func:`decode_append_attn` over a paged cache.
 
-    Reading P1 (also in the design doc): each cache is a pool of pages of ``P`` tokens laid
+    Reading P1: each cache is a pool of pages of ``P`` tokens laid
     out ``(num_pages, H, P, .)``; logical token ``t`` of sequence ``b`` is row ``t % P`` of
     physical page ``block_table[b, t // P]``.  The step reads the rows of tokens
     ``0 .. n-1`` (``n = kv_len[b] + 1`` with a new token, else ``kv_len[b]``), and the new
@@ -149,7 +149,7 @@ def decode_attn_qkv8(q_codes, q_rope_bits, scale_q, k_codes, scale_k, k_rope_bit
                      sm_scale: float) -> np.ndarray:
     """Attention with Q, K and V all per-head INT8 (the RoPE parts of Q and K in bf16).
 
-    Readings (also in the design doc): A8 Q's non-RoPE part and all of V are quantised
+    Readings: A8 Q's non-RoPE part and all of V are quantised
     per head with the same symmetric formula as K (``quantize_k``); their
     dequantised values are ``scale_q[h] * code`` and ``scale_v[h] * code``; the
     RoPE parts of Q and K stay bf16.  The attention is the textbook one over the
@@ -185,7 +185,7 @@ def decode_attn_latent(q_bits, codes, scale, rope_bits, sm_scale: float, Dl: int
 
     MindIE LLM page "FA3 quantization", overview (MLA attention; only the non-RoPE part of
     K goes to INT8, the RoPE part stays floating point).  The pages give no layout for the
-    shared latent; the readings (also in the design doc) are:
+    shared latent; the readings are:
 
     * L1 the latent rows ``[c | k_rope]`` of a sequence form one head shared by all query
       heads, so the per-head method runs with one head: ``c`` holds INT8 codes with one

@@ -5,7 +5,7 @@ non-RoPE slice of K is quantised to 8 bits, per head; the RoPE slice of K is
 left unquantised); msModelSlim page "FA3量化", section 适用要求 (only symmetric
 INT8) and section 算法流程 (``scale = abs_max / 127``).
 
-The pages print no quantisation formula.  Readings (also in the design doc):
+The pages print no quantisation formula.  Readings:
 
 * Q1 symmetric INT8 means no offset: ``code = clamp(round(x / scale), -127, 127)``;
   -128 is never produced and values beyond the calibrated range saturate.

@@ -16,7 +16,7 @@ page "FA3量化：Flash Attention 3激活量化算法说明", section 原理 -> 
 4. symmetric parameters: ``abs_max[h] = max(|min_values[h]|, |max_values[h]|)``
    and ``scale[h] = abs_max[h] / 127``.
 
-Readings where the page is silent or ambiguous (each one also in the design doc):
+Readings where the page is silent or ambiguous:
 
 * R1 "reshape x to (H, N)": grouped per head (``x[:, h]`` flattened), since the
   page says each head collects its own N points; a raw row-major reshape of a

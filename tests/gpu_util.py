@@ -5,8 +5,8 @@ import sys
 import numpy as np
 import torch
 
-DECODE_TOL = 2e-2        # contract: max row-normalised relative error vs the float64 oracle
-DECODE_DESIGN_TOL = 1e-4  # what float32 accumulation should reach (derived in the design notes)
+DECODE_TOL = 2e-2        # required bound: max row-normalised relative error vs the float64 oracle
+DECODE_DESIGN_TOL = 1e-4  # tighter bound the float32-accumulating kernels are held to
 
 
 def log(msg: str) -> None:

@@ -58,6 +58,20 @@ def test_max_windows_cover_the_workloads():
     assert lib.fa3q_calibrate_max_windows(7) == 0
 
 
+def _ratio_for_k(N: int, K: int) -> float:
+    # int(ratio * N) = N - K + 1 exactly: the ratio sits half a value inside the step
+    return (N - K + 1 + 0.5) / N
+
+
+@pytest.mark.parametrize("dtype,S", [(L.FA3Q_BF16, 4096), (L.FA3Q_F32, 2048)])
+def test_window_count_limit_is_where_the_plan_stops(dtype, S):
+    lib = fa.lib()
+    kmax = lib.fa3q_calibrate_max_windows(dtype)
+    N = S * 16
+    assert lib.fa3q_calibrate_workspace_bytes(dtype, 1, 2, S, 16, _ratio_for_k(N, kmax)) > 0
+    assert lib.fa3q_calibrate_workspace_bytes(dtype, 1, 2, S, 16, _ratio_for_k(N, kmax + 1)) == 0
+
+
 def test_workspace_queries():
     lib = fa.lib()
     # bf16 (8,128,2048,128), ratio 0.9999: K=211

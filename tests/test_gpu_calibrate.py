@@ -156,6 +156,19 @@ def test_large_k_uses_more_than_64k_lds(fa):
     _check(fa, x[:, :, :64], (0.5,), "large_k_f32")               # N = 8192, K = 4097
 
 
+@pytest.mark.parametrize("dtype,S", [(torch.bfloat16, 4096), (torch.float32, 2048)], ids=["bf16", "f32"])
+def test_largest_supported_window_count(fa, dtype, S):
+    # K = fa3q_calibrate_max_windows(dtype) exactly: the chunk and merge buffers at their
+    # largest (14950 bf16 windows, 7475 float32 ones, on 2 heads of S * 16 values)
+    kmax = fa.fa3q_calibrate_max_windows(dtype)
+    N = S * 16
+    ratio = (N - kmax + 1 + 0.5) / N
+    assert N - int(ratio * N) + 1 == kmax
+    rng = np.random.default_rng(23)
+    x = torch.from_numpy((rng.standard_t(3, size=(1, 2, S, 16)) * 0.9).astype(np.float32)).to(dtype)
+    _check(fa, x, (ratio,), f"k_max_{kmax}")
+
+
 def test_tails_across_many_binades(fa):
     # log-uniform magnitudes over 2^-60 .. 2^60: the K tail keys span more top bytes than
     # the counting sort takes, so the side merge sorts them bitonically; narrow tails (the

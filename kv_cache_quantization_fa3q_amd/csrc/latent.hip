@@ -238,9 +238,7 @@ __global__ __launch_bounds__(kLatThreads) void latent_split_kernel(LatentArgs a)
       p[i] = exp2f(p[i] - mu);
       rsum += p[i];
     }
-    rsum += __shfl_xor(rsum, 16);
-    rsum += __shfl_xor(rsum, 32);
-    l += rsum;
+    l += rsum;  // this lane's part: the four lanes of a head are summed once, at the end
     bf16x8 phi, plo;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -290,6 +288,19 @@ __global__ __launch_bounds__(kLatThreads) void latent_split_kernel(LatentArgs a)
           sr[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w), qr[kk], sr[tt], 0, 0, 0);
         }
       }
+      {
+        // keep kSDepth operand reads in flight ahead of the score MFMAs (left alone, the
+        // scheduler issues each read one MFMA before its use)
+        constexpr int NS = 2 * (KL + KR);
+        constexpr int kSDepth = NS < 6 ? NS : 6;
+        __builtin_amdgcn_sched_group_barrier(0x100, kSDepth, 0);  // DS reads
+#pragma unroll
+        for (int i = 0; i < NS - kSDepth; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kSDepth, 0);
+      }
       // the other buffer was last read before the previous barrier
       if (t0 + kTT < t_end) stage(st, buf ^ 1);
       if (t0 + 2 * kTT < t_end) fetch(t0 + 2 * kTT, st);
@@ -326,6 +337,9 @@ __global__ __launch_bounds__(kLatThreads) void latent_split_kernel(LatentArgs a)
     buf ^= 1;
   }
 
+  // a head's reference mu is the same in its four lanes, so their partial sums share scale
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
   // ---- lane holds O^T[dims 16mt + 4lg + j][head]
   if (!hv) return;
   const int64_t row = static_cast<int64_t>(b) * a.H + head;

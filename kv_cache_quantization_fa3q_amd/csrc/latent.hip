@@ -145,7 +145,7 @@ __global__ __launch_bounds__(kLatThreads) void latent_split_kernel(LatentArgs a)
 #pragma unroll
     for (int k = 0; k < UPT; ++k) {
       const int u = tid + k * kLatThreads;
-      if (u < UNITS) {
+      if (UNITS % kLatThreads == 0 || u < UNITS) {  // folds when every thread has a unit
         const int tg = u % (kTT / 4), dc = u / (kTT / 4);  // token group fastest: spreads LDS banks
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -155,7 +155,7 @@ __global__ __launch_bounds__(kLatThreads) void latent_split_kernel(LatentArgs a)
       }
     }
     if constexpr (DR > 0) {
-      if (tid < RCH) {
+      if (RCH == kLatThreads || tid < RCH) {
         const int r = tid / (DR / 8), k8 = tid - r * (DR / 8);
         const int64_t tok = min(t0 + r, t_end - 1);
         st[0].r = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(rbase + tok * DR + 8 * k8));
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(kLatThreads) void latent_split_kernel(LatentArgs a)
 #pragma unroll
     for (int k = 0; k < UPT; ++k) {
       const int u = tid + k * kLatThreads;
-      if (u < UNITS) {
+      if (UNITS % kLatThreads == 0 || u < UNITS) {  // folds when every thread has a unit
         const int tg = u % (kTT / 4), dc = u / (kTT / 4);  // token group fastest: spreads LDS banks
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -196,7 +196,7 @@ __global__ __launch_bounds__(kLatThreads) void latent_split_kernel(LatentArgs a)
       }
     }
     if constexpr (DR > 0) {
-      if (tid < RCH) {
+      if (RCH == kLatThreads || tid < RCH) {
         const int r = tid / (DR / 8), k8 = tid - r * (DR / 8);
         *reinterpret_cast<u32x4v*>(krope + r * RROW + 8 * k8) = st[0].r;
       }
@@ -301,9 +301,12 @@ __global__ __launch_bounds__(kLatThreads) void latent_split_kernel(LatentArgs a)
         }
         __builtin_amdgcn_sched_group_barrier(0x008, kSDepth, 0);
       }
-      // the other buffer was last read before the previous barrier
-      if (t0 + kTT < t_end) stage(st, buf ^ 1);
-      if (t0 + 2 * kTT < t_end) fetch(t0 + 2 * kTT, st);
+      // the other buffer was last read before the previous barrier.  Staged and fetched
+      // unconditionally, so that the score MFMAs and the staging share one basic block and
+      // the scheduler interleaves them: past the end the fetch re-reads the last row (in
+      // bounds) and the staged buffer is never read.
+      stage(st, buf ^ 1);
+      fetch(t0 + 2 * kTT, st);
       // ---- scores (log2 domain) of the lane's head over its 8 tokens (16tt + 4lg + j)
       rmax = -INFINITY;
 #pragma unroll

@@ -89,6 +89,17 @@ struct LatentStage {
 };
 
 // Two bf16 (packed) from two float32 (exact here: small integers).
+// Max over lanes i, i^16, i^32 and i^48 (the four lane groups that hold one head), in
+// VALU lane swaps instead of LDS permutes.  permlane16_swap(x, x) returns (a, b) with row
+// pairs (0,1) and (2,3) of 16 lanes holding x's even rows in a and odd rows in b, so
+// max(a, b) is the max over i and i^16; permlane32_swap does the same for halves (i^32).
+__device__ __forceinline__ float max_over_lane_groups(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
   return __builtin_bit_cast(uint32_t, v);
@@ -318,8 +329,7 @@ __global__ __launch_bounds__(kLatThreads) void latent_split_kernel(LatentArgs a)
           p[4 * tt + j] = tok < t_end ? sc : -INFINITY;
           rmax = fmaxf(rmax, p[4 * tt + j]);
         }
-      rmax = fmaxf(rmax, __shfl_xor(rmax, 16));
-      rmax = fmaxf(rmax, __shfl_xor(rmax, 32));  // finite: every tile holds a valid token
+      rmax = max_over_lane_groups(rmax);  // finite: every tile holds a valid token
       if (__builtin_amdgcn_ballot_w64(rmax > mu + kLazy) != 0) break;
       accumulate(p, vt_buf[buf]);
       __syncthreads();

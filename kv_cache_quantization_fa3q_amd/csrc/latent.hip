@@ -246,7 +246,9 @@ __global__ __launch_bounds__(kLatThreads) void latent_split_kernel(LatentArgs a)
     float rsum = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      p[i] = exp2f(p[i] - mu);
+      // the hardware exp2 alone: exponents are <= kLazy, and only weights below 2^-126
+      // (against a head total >= 1) lose their denormal tail
+      p[i] = __builtin_amdgcn_exp2f(p[i] - mu);
       rsum += p[i];
     }
     l += rsum;  // this lane's part: the four lanes of a head are summed once, at the end

@@ -70,25 +70,12 @@ struct LatentArgs {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
-// 4x4 byte transpose: y[e] byte r = x[r] byte e.
-__device__ __forceinline__ void transpose4x4(const uint32_t (&x)[4], uint32_t (&y)[4]) {
-  const uint32_t a = __builtin_amdgcn_perm(x[1], x[0], 0x05010400u);  // x0.b0 x1.b0 x0.b1 x1.b1
-  const uint32_t b = __builtin_amdgcn_perm(x[1], x[0], 0x07030602u);  // x0.b2 x1.b2 x0.b3 x1.b3
-  const uint32_t c = __builtin_amdgcn_perm(x[3], x[2], 0x05010400u);
-  const uint32_t d = __builtin_amdgcn_perm(x[3], x[2], 0x07030602u);
-  y[0] = __builtin_amdgcn_perm(c, a, 0x05040100u);  // a.lo16 c.lo16
-  y[1] = __builtin_amdgcn_perm(c, a, 0x07060302u);  // a.hi16 c.hi16
-  y[2] = __builtin_amdgcn_perm(d, b, 0x05040100u);
-  y[3] = __builtin_amdgcn_perm(d, b, 0x07060302u);
-}
-
 // Staged operands of one tile: 4 tokens x 16 latent dims and one 16-byte RoPE chunk.
 struct LatentStage {
   u32x4v x[4];
   u32x4v r;
 };
 
-// Two bf16 (packed) from two float32 (exact here: small integers).
 // Max over lanes i, i^16, i^32 and i^48 (the four lane groups that hold one head), in
 // VALU lane swaps instead of LDS permutes.  permlane16_swap(x, x) returns (a, b) with row
 // pairs (0,1) and (2,3) of 16 lanes holding x's even rows in a and odd rows in b, so
@@ -100,18 +87,15 @@ __device__ __forceinline__ float max_over_lane_groups(float v) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// Two bf16 (packed) from two float32 (exact here: small integers).
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// 4 INT8 codes of one dword -> 4 bf16 in two dwords, element order kept.
-__device__ __forceinline__ uint2 widen4(uint32_t w) {
-  const float f0 = static_cast<float>(static_cast<int8_t>(w));
-  const float f1 = static_cast<float>(static_cast<int8_t>(w >> 8));
-  const float f2 = static_cast<float>(static_cast<int8_t>(w >> 16));
-  const float f3 = static_cast<float>(static_cast<int8_t>(w >> 24));
-  return make_uint2(pack_bf16(f0, f1), pack_bf16(f2, f3));
+// Code `e` (0..3) of a dword of INT8 codes as float32 (one byte-select conversion).
+__device__ __forceinline__ float code_f32(uint32_t w, int e) {
+  return static_cast<float>(static_cast<int8_t>(w >> (8 * e)));
 }
 
 template <int DL, int DR>
@@ -183,27 +167,28 @@ __global__ __launch_bounds__(kLatThreads) void latent_split_kernel(LatentArgs a)
       const int u = tid + k * kLatThreads;
       if (UNITS % kLatThreads == 0 || u < UNITS) {  // folds when every thread has a unit
         const int tg = u % (kTT / 4), dc = u / (kTT / 4);  // token group fastest: spreads LDS banks
+        // each code is converted once; the row-major copy pairs neighbouring dims of a
+        // token, the transposed copy neighbouring tokens of a dim
+        float f[4][16];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) f[r][j] = code_f32(st[k].x[r][j / 4], j % 4);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const uint32_t w[4] = {st[k].x[r][0], st[k].x[r][1], st[k].x[r][2], st[k].x[r][3]};
-          uint2 h[4];
+          uint32_t h[8];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) h[e] = widen4(w[e]);
+          for (int i = 0; i < 8; ++i) h[i] = pack_bf16(f[r][2 * i], f[r][2 * i + 1]);
           uint16_t* row = klat + (4 * tg + r) * KROW + 16 * dc;
-          *reinterpret_cast<uint4*>(row) = make_uint4(h[0].x, h[0].y, h[1].x, h[1].y);
-          *reinterpret_cast<uint4*>(row + 8) = make_uint4(h[2].x, h[2].y, h[3].x, h[3].y);
+          *reinterpret_cast<uint4*>(row) = make_uint4(h[0], h[1], h[2], h[3]);
+          *reinterpret_cast<uint4*>(row + 8) = make_uint4(h[4], h[5], h[6], h[7]);
         }
         // token offset t = 4tg + r (tg = 4*b4 + (b3 b2))  ->  position 8*(b3 b2) + 4*b4 + r
         const int pos = 8 * (tg & 3) + 4 * (tg >> 2);
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t xs[4] = {st[k].x[0][w], st[k].x[1][w], st[k].x[2][w], st[k].x[3][w]};
-          uint32_t y[4];
-          transpose4x4(xs, y);
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            *reinterpret_cast<uint2*>(vt + (16 * dc + 4 * w + e) * VROW + pos) = widen4(y[e]);
-        }
+        for (int j = 0; j < 16; ++j)
+          *reinterpret_cast<uint2*>(vt + (16 * dc + j) * VROW + pos) =
+              make_uint2(pack_bf16(f[0][j], f[1][j]), pack_bf16(f[2][j], f[3][j]));
       }
     }
     if constexpr (DR > 0) {

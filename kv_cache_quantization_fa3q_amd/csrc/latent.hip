@@ -49,7 +49,10 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 constexpr int kLatThreads = 256;  // four waves, 16 heads each
 constexpr int kLatHeads = 64;     // heads per workgroup
 constexpr int kTT = 32;           // tokens per tile
-constexpr int64_t kLatTargetGroups = 512;
+// A workgroup's two LDS buffers (157 KB at the MLA shape) leave room for one per CU, so
+// 256 workgroups fill the chip in a single wave; more splits would only add a second,
+// partial wave and more partial rows for the combine to read.
+constexpr int64_t kLatTargetGroups = 256;
 constexpr int64_t kLatMinSplit = 64;
 
 struct LatentArgs {

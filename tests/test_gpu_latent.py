@@ -108,3 +108,31 @@ def test_latent_decode_is_deterministic(fa):
     b = fa.fa3q_decode_latent(q, cq, scale, kr, 0.07)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_latent_decode_with_scores_that_keep_growing(fa):
+    # One split per (b, head group) over 16 tiles whose scores climb by about 7 (log2) per
+    # tile for even heads, so those heads move their softmax reference again and again while
+    # the odd heads of the same waves (falling scores) keep theirs from the first tile
+    dev = torch.device("cuda:0")
+    B, H, T, Dl, Dr = 256, 64, 512, 128, 32
+    rng = np.random.default_rng(97)
+    codes = rng.integers(-20, 21, size=(B, T, Dl)).astype(np.int8)
+    rope = np.zeros((B, T, Dr), np.float32)
+    rope[:, :, 0] = 0.5 * np.arange(T, dtype=np.float32)
+    rope[:, :, 1:] = rng.standard_normal((B, T, Dr - 1)).astype(np.float32)
+    rope_t = torch.from_numpy(rope).to(torch.bfloat16)
+    q = synth.normal_tensor((B, H, Dl + Dr), dtype=torch.bfloat16, seed=98)
+    q[:, :, Dl] = torch.where(torch.arange(H) % 2 == 0, 4.0, -4.0).to(torch.bfloat16)
+    scale = torch.tensor([0.01], dtype=torch.float32)
+    sm = 1.0 / math.sqrt(Dl + Dr)
+    log(f"latent growing scores: B={B} H={H} T={T} Dl={Dl} Dr={Dr}")
+    out = fa.fa3q_decode_latent(q.to(dev), torch.from_numpy(codes).to(dev), scale.to(dev), rope_t.to(dev), sm)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.all(np.isfinite(got))
+    ref = oracle.decode_attn_latent(bits16(q), codes, np.float32(0.01), bits16(rope_t), sm, Dl)
+    err = row_rel_err(got, ref)
+    log(f"  row-normalised error {err:.3e}")
+    assert err <= DECODE_TOL, err
+    assert err <= DECODE_DESIGN_TOL, err

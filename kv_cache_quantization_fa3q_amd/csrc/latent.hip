@@ -367,10 +367,18 @@ __global__ __launch_bounds__(128) void latent_combine_kernel(LatentArgs a, int d
   for (int s = 0; s < a.nsplit; ++s) mmax = fmaxf(mmax, ml[2 * s]);
   float den = 0.0f;
   for (int s = 0; s < a.nsplit; ++s) den += exp2f(ml[2 * s] - mmax) * ml[2 * s + 1];
-  for (int d = threadIdx.x; d < dl; d += blockDim.x) {
-    float num = 0.0f;
-    for (int s = 0; s < a.nsplit; ++s) num += exp2f(ml[2 * s] - mmax) * a.ws_o[(row * a.nsplit + s) * dl + d];
-    a.out[row * dl + d] = num / den;
+  // four dims per thread (dl is a multiple of 16; rows and partials are 16-byte aligned)
+  for (int d = 4 * static_cast<int>(threadIdx.x); d < dl; d += 4 * static_cast<int>(blockDim.x)) {
+    float4 num = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int s = 0; s < a.nsplit; ++s) {
+      const float w = exp2f(ml[2 * s] - mmax);
+      const float4 o = *reinterpret_cast<const float4*>(a.ws_o + (row * a.nsplit + s) * dl + d);
+      num.x += w * o.x;
+      num.y += w * o.y;
+      num.z += w * o.z;
+      num.w += w * o.w;
+    }
+    *reinterpret_cast<float4*>(a.out + row * dl + d) = make_float4(num.x / den, num.y / den, num.z / den, num.w / den);
   }
 }
 

@@ -17,13 +17,15 @@
  *   8. fa3q_quantize_asym      -- non-RoPE part of K -> asymmetric INT8 codes with a scale and
  *      an offset per (head, dim); RoPE part kept in bf16
  *   9. fa3q_decode_attn_asym   -- attention as in 5 over the asymmetric K-nope cache of 8
- *  10. fa3q_decode_latent      -- attention of every head of a sequence over one shared-latent
+ *  10. fa3q_calibrate_batches  -- 1 and 2 over several calibration batches in one call
+ *  11. fa3q_decode_latent      -- attention of every head of a sequence over one shared-latent
  *      (absorbed MLA) cache: INT8 latent (one scale) + bf16 RoPE part, on the matrix cores
- *  11. fa3q_calibrate_batches  -- 1 and 2 over several calibration batches in one call
  *  12. fa3q_fake_quant         -- quantise and dequantise (the codes of 4 turned back into bf16),
  *      in place or into a second buffer
  *  13. fa3q_decode_paged_attn  -- 6 over a paged cache: pools of fixed-size pages and a block
  *      table per sequence
+ *  14. fa3q_decode_attn_noalloc -- 5 with the library's own static scratch instead of a
+ *      caller workspace (for callers that cannot allocate device memory)
  *
  * Sources, cited by page title and section:
  *   [MS] msModelSlim documentation, "FA3量化：Flash Attention 3激活量化算法说明"
@@ -35,7 +37,8 @@
  *
  * Conventions shared by every entry point:
  *   - Every pointer is a DEVICE pointer owned by the caller; the library never
- *     allocates, frees or retains memory and keeps no state between calls.
+ *     allocates, frees or retains memory and keeps no state between calls (the one
+ *     exception is the static scratch array of fa3q_decode_attn_noalloc).
  *   - `stream` is a hipStream_t passed as void*; NULL means the default stream.
  *     Calls only enqueue work on `stream`; they never synchronise.
  *   - Arguments are validated on the host BEFORE anything is enqueued: a
@@ -71,7 +74,8 @@ typedef enum fa3q_status {
   FA3Q_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than the *_workspace_bytes query */
   FA3Q_ERR_HIP = 7,         /* the HIP runtime rejected a launch */
   FA3Q_ERR_UNSUPPORTED = 8, /* valid arguments outside what this build handles (see each call) */
-  FA3Q_ERR_ALIAS = 9        /* an output partly overlaps an input (where exact aliasing is allowed) */
+  FA3Q_ERR_ALIAS = 9,       /* an output partly overlaps an input (where exact aliasing is allowed) */
+  FA3Q_ERR_SCRATCH = 10     /* the call needs more scratch than the library's static array holds */
 } fa3q_status;
 
 typedef enum fa3q_dtype {
@@ -79,6 +83,12 @@ typedef enum fa3q_dtype {
   FA3Q_BF16 = 1, /* bfloat16, raw 16-bit patterns */
   FA3Q_F16 = 2   /* IEEE binary16, raw 16-bit patterns (asymmetric parameter tables only) */
 } fa3q_dtype;
+
+/*
+ * Signatures take and return plain `int` for statuses and dtype codes: the values are
+ * those of fa3q_status and fa3q_dtype, but C leaves the integer type behind an enum to
+ * the compiler, while `int` has one fixed width for every caller (ctypes, other FFIs).
+ */
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* fa3q_status_string(int status);
@@ -341,7 +351,7 @@ int fa3q_decode_attn_asym(const uint16_t* q, const int8_t* k_nope_q, const uint1
                           size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
-/* 11. Several calibration batches: windows and running min/max in one call  */
+/* 10. Several calibration batches: windows and running min/max in one call  */
 /* ------------------------------------------------------------------------ */
 
 /*
@@ -375,7 +385,7 @@ int fa3q_calibrate_batches(const void* const* xs, int64_t nb, int dtype, int64_t
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
-/* 10. Decode attention over a shared-latent (absorbed MLA) cache            */
+/* 11. Decode attention over a shared-latent (absorbed MLA) cache            */
 /* ------------------------------------------------------------------------ */
 
 /*
@@ -472,6 +482,35 @@ int fa3q_decode_paged_attn(const uint16_t* q, const uint16_t* k_new, const uint1
                            int64_t num_pages, int64_t page_size, int64_t max_pages, int64_t Dn, int64_t Dr,
                            int64_t Dv, float sm_scale, float* out, void* workspace, size_t workspace_bytes,
                            void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* 14. Decode attention with no workspace argument                           */
+/* ------------------------------------------------------------------------ */
+
+/* Bytes of the static device array fa3q_decode_attn_noalloc uses as its scratch. */
+#define FA3Q_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): fa3q_decode_attn with the same
+ * arguments minus the workspace, and the same result bit for bit (same kernels, same
+ * split plan).  The split softmax states go to a file-scope device array of
+ * FA3Q_NOALLOC_SCRATCH_BYTES bytes that the library holds on every GPU it runs on until
+ * the process ends; the call allocates and frees nothing.
+ *
+ *   Arguments as fa3q_decode_attn.  Calls whose fa3q_decode_attn_workspace_bytes(B,H,T,Dv)
+ *   exceeds FA3Q_NOALLOC_SCRATCH_BYTES return FA3Q_ERR_SCRATCH before anything is
+ *   enqueued (e.g. B*H = 1024, Dv = 128 is accepted up to T = 65536).  The first call on
+ *   a device that needs scratch looks up that device's copy of the array (a HIP call);
+ *   FA3Q_ERR_HIP if that fails.
+ *   All calls on one GPU share its array: calls that overlap in time on one GPU (on
+ *   different streams, or from different threads without ordering) race and give
+ *   undefined results.  Calls ordered on one stream are safe.
+ */
+int fa3q_decode_attn_noalloc(const uint16_t* q, const int8_t* k_nope_q, const float* scale,
+                             const uint16_t* k_rope, const uint16_t* v, int64_t B, int64_t H,
+                             int64_t T, int64_t Dn, int64_t Dr, int64_t Dv, float sm_scale,
+                             float* out, void* stream);
 
 #ifdef __cplusplus
 }

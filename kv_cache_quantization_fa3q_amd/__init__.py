@@ -25,6 +25,7 @@ from .ops import (  # noqa: F401
     fa3q_calibrate_workspace_bytes,
     fa3q_decode_append_attn,
     fa3q_decode_attn,
+    fa3q_decode_attn_noalloc,
     fa3q_decode_attn_asym,
     fa3q_decode_attn_qkv8,
     fa3q_decode_attn_workspace_bytes,

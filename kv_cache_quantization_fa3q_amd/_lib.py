@@ -26,6 +26,9 @@ FA3Q_ERR_WORKSPACE = 6
 FA3Q_ERR_HIP = 7
 FA3Q_ERR_UNSUPPORTED = 8
 FA3Q_ERR_ALIAS = 9
+FA3Q_ERR_SCRATCH = 10
+
+FA3Q_NOALLOC_SCRATCH_BYTES = 16 << 20  # include/fa3q.h
 
 FA3Q_F32 = 0
 FA3Q_BF16 = 1
@@ -66,6 +69,8 @@ SIGNATURES = {
                                       _vp, _int, _vp, _vp, _vp, _sz, _vp]),
     "fa3q_decode_latent": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, ctypes.c_float, _vp, _vp, _sz,
                                   _vp]),
+    "fa3q_decode_attn_noalloc": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_float,
+                                        _vp, _vp]),
 }
 
 _lock = threading.Lock()

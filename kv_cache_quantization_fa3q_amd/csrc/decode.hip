@@ -41,8 +41,18 @@
 // The per-dim scale folds into the query (q'_d = q_d * s[h,d]) and the offsets into one
 // constant per (b, h) (sum_d q'_d * o[h,d]), so the score is the same code dot product.
 #include <cmath>
+#include <mutex>
+#include <unordered_map>
 
 #include "fa3q_internal.hpp"
+
+// Scratch of fa3q_decode_attn_noalloc: the split softmax states (max, sum, unnormalised
+// output per split) live in this file-scope device array instead of a caller workspace.
+// Each GPU holds its own copy, at its own address, until the process ends; host code must
+// use the address hipGetSymbolAddress gives on that device, never the array's name (on the
+// host the name is a stand-in, not a device address).  Every split writes its whole state
+// before the combine kernel reads it, so nothing needs clearing between calls.
+static __device__ __align__(256) unsigned char scratch[FA3Q_NOALLOC_SCRATCH_BYTES];
 
 namespace fa3q {
 namespace {
@@ -589,6 +599,25 @@ extern "C" size_t fa3q_decode_attn_workspace_bytes(int64_t B, int64_t H, int64_t
 namespace fa3q {
 namespace {
 
+constexpr size_t kScratchBytes = FA3Q_NOALLOC_SCRATCH_BYTES;
+
+// Device address of the current device's scratch array, looked up once per device.
+int scratch_address(void** out) {
+  static std::mutex mu;
+  static std::unordered_map<int, void*> addr;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FA3Q_ERR_HIP;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = addr.find(dev);
+  if (it == addr.end()) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return FA3Q_ERR_HIP;
+    it = addr.emplace(dev, p).first;
+  }
+  *out = it->second;
+  return FA3Q_OK;
+}
+
 // INT8 query and values of fa3q_decode_attn_qkv8, and the asymmetric K tables of
 // fa3q_decode_attn_asym (unused by the other entry points).
 struct Int8QV {
@@ -624,7 +653,7 @@ int decode_launch(const uint16_t* q, const int8_t* k_nope_q, const float* scale,
                   const uint16_t* v, const int32_t* kv_len, const uint16_t* k_new, const uint16_t* v_new,
                   const Int8QV& i8, int64_t B, int64_t H, int64_t T, int64_t Dn, int64_t Dr, int64_t Dv,
                   float sm_scale, float* out, void* workspace, size_t workspace_bytes, void* stream,
-                  const PagedKV& pk = PagedKV{}) {
+                  const PagedKV& pk = PagedKV{}, bool use_scratch = false) {
   constexpr bool kQ8 = kFmt == kFmtQkv8;
   constexpr bool kAsym = kFmt == kFmtAsym;
   constexpr bool kPaged = kVar == kVarPaged;
@@ -666,7 +695,9 @@ int decode_launch(const uint16_t* q, const int8_t* k_nope_q, const float* scale,
   const SplitPlan p = plan_splits(B, H, T);
   if (B * H * p.nsplit > (int64_t{1} << 31) - 1) return FA3Q_ERR_SHAPE;
   const size_t need = fa3q_decode_attn_workspace_bytes(B, H, T, Dv);
-  if (need > 0) {
+  if (use_scratch) {
+    if (need > kScratchBytes) return FA3Q_ERR_SCRATCH;
+  } else if (need > 0) {
     if (!workspace || workspace_bytes < need) return FA3Q_ERR_WORKSPACE;
     if (!is_aligned(workspace, 256)) return FA3Q_ERR_ALIGN;
   }
@@ -674,6 +705,11 @@ int decode_launch(const uint16_t* q, const int8_t* k_nope_q, const float* scale,
   const int lv = static_cast<int>(Dv / (kQ8 ? 16 : 8));
   KernelFn fn = pick_kernel<kVar, kFmt>(lk, lv);
   if (!fn) return FA3Q_ERR_UNSUPPORTED;
+  if (use_scratch && need > 0) {
+    // every argument is valid: only now touch the runtime for this device's copy of the array
+    const int st = scratch_address(&workspace);
+    if (st != FA3Q_OK) return st;
+  }
 
   DecodeArgs a;
   a.q = q;
@@ -783,4 +819,12 @@ extern "C" int fa3q_decode_attn_asym(const uint16_t* q, const int8_t* k_nope_q, 
   i8.params_f16 = params_dtype == FA3Q_BF16 ? 0 : (params_dtype == FA3Q_F16 ? 1 : -1);
   return decode_launch<kVarFixed, kFmtAsym>(q, k_nope_q, nullptr, k_rope, v, nullptr, nullptr, nullptr, i8, B, H, T, Dn,
                                         Dr, Dv, sm_scale, out, workspace, workspace_bytes, stream);
+}
+
+extern "C" int fa3q_decode_attn_noalloc(const uint16_t* q, const int8_t* k_nope_q, const float* scale,
+                                        const uint16_t* k_rope, const uint16_t* v, int64_t B, int64_t H, int64_t T,
+                                        int64_t Dn, int64_t Dr, int64_t Dv, float sm_scale, float* out,
+                                        void* stream) {
+  return decode_launch<kVarFixed, kFmtBf16>(q, k_nope_q, scale, k_rope, v, nullptr, nullptr, nullptr, Int8QV{}, B, H, T,
+                                            Dn, Dr, Dv, sm_scale, out, nullptr, 0, stream, PagedKV{}, true);
 }

@@ -26,6 +26,7 @@ __all__ = [
     "fa3q_quantize_k",
     "fa3q_decode_attn_workspace_bytes",
     "fa3q_decode_attn",
+    "fa3q_decode_attn_noalloc",
     "fa3q_decode_append_attn",
     "fa3q_decode_attn_qkv8",
     "fa3q_quantize_asym",
@@ -238,6 +239,33 @@ def fa3q_decode_attn(q: torch.Tensor, k_nope_q: torch.Tensor, scale: torch.Tenso
                                 B, H, T, Dn, Dr, Dv, ctypes.c_float(float(sm_scale)), _ptr(out), _ptr(workspace),
                                 wbytes, _stream(stream))
     _check(st, "fa3q_decode_attn")
+    return out
+
+
+def fa3q_decode_attn_noalloc(q: torch.Tensor, k_nope_q: torch.Tensor, scale: torch.Tensor, k_rope: torch.Tensor,
+                             v: torch.Tensor, sm_scale: float, out: Optional[torch.Tensor] = None,
+                             stream=None) -> torch.Tensor:
+    """``fa3q_decode_attn`` with no workspace: the library keeps the split states in its own static
+    device array (``FA3Q_ERR_SCRATCH`` when they need more than it holds).  Calls that overlap in
+    time on one GPU share that array and race; calls on one stream are ordered."""
+    if k_nope_q.dim() != 4 or k_nope_q.dtype != torch.int8:
+        raise ValueError("k_nope_q must be int8 (B, H, T, Dn)")
+    B, H, T, Dn = (int(s) for s in k_nope_q.shape)
+    Dr = int(k_rope.shape[-1]) if k_rope is not None else 0
+    Dv = int(v.shape[-1])
+    if q.shape != (B, H, Dn + Dr) or q.dtype != torch.bfloat16:
+        raise ValueError("q must be bfloat16 (B, H, Dn + Dr)")
+    if v.shape != (B, H, T, Dv) or v.dtype != torch.bfloat16:
+        raise ValueError("v must be bfloat16 (B, H, T, Dv)")
+    if k_rope is not None and (k_rope.shape != (B, H, T, Dr) or k_rope.dtype != torch.bfloat16):
+        raise ValueError("k_rope must be bfloat16 (B, H, T, Dr)")
+    if out is None:
+        out = torch.empty((B, H, Dv), dtype=torch.float32, device=q.device)
+    _need_gpu("fa3q_decode_attn_noalloc", q, k_nope_q, scale, k_rope, v, out)
+    st = lib().fa3q_decode_attn_noalloc(_ptr(q), _ptr(k_nope_q), _ptr(scale), _ptr(k_rope) if Dr > 0 else None,
+                                        _ptr(v), B, H, T, Dn, Dr, Dv, ctypes.c_float(float(sm_scale)), _ptr(out),
+                                        _stream(stream))
+    _check(st, "fa3q_decode_attn_noalloc")
     return out
 
 

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_function():
 def test_version_and_status_strings():
     lib = fa.lib()
     assert lib.fa3q_version() >> 16 == 1
-    for code in range(10):
+    for code in range(11):
         s = fa.status_string(code)
         assert s.startswith("FA3Q_")
     assert fa.status_string(0) == "FA3Q_OK"
@@ -187,6 +187,38 @@ def test_decode_rejections():
     assert call(wsb=64) == L.FA3Q_ERR_WORKSPACE
     assert call(ws=_p(128)) == L.FA3Q_ERR_ALIGN
 
+
+
+@no_gpu_only
+def test_decode_noalloc_rejections():
+    f = fa.lib().fa3q_decode_attn_noalloc
+    ok = dict(q=_p(), kq=_p(), s=_p(), kr=_p(), v=_p(), B=8, H=128, T=32768, Dn=128, Dr=64, Dv=128,
+              sm=0.07, o=_p())
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["q"], a["kq"], a["s"], a["kr"], a["v"], a["B"], a["H"], a["T"], a["Dn"], a["Dr"], a["Dv"],
+                 ctypes.c_float(a["sm"]), a["o"], None)
+
+    for name in ("q", "kq", "s", "kr", "v", "o"):
+        assert call(**{name: None}) == L.FA3Q_ERR_NULL, name
+    assert call(T=0) == L.FA3Q_ERR_SHAPE
+    assert call(Dn=120) == L.FA3Q_ERR_SHAPE
+    assert call(Dv=96) == L.FA3Q_ERR_SHAPE
+    assert call(v=_p(8)) == L.FA3Q_ERR_ALIGN
+    # split states beyond the static array: rejected before any HIP call
+    lib = fa.lib()
+    for B, H, T, Dv in ((64, 128, 32768, 128), (8, 128, 1 << 20, 512)):
+        assert lib.fa3q_decode_attn_workspace_bytes(B, H, T, Dv) > L.FA3Q_NOALLOC_SCRATCH_BYTES
+        assert call(B=B, H=H, T=T, Dv=Dv) == L.FA3Q_ERR_SCRATCH
+    assert fa.status_string(L.FA3Q_ERR_SCRATCH).startswith("FA3Q_ERR_SCRATCH")
+
+
+def test_noalloc_scratch_covers_the_long_context_decode():
+    lib = fa.lib()
+    # the long-context decode (B=8, H=128, T=32768, Dv=128) and B*H=1024 up to T=65536 fit
+    assert 0 < lib.fa3q_decode_attn_workspace_bytes(8, 128, 32768, 128) <= L.FA3Q_NOALLOC_SCRATCH_BYTES
+    assert lib.fa3q_decode_attn_workspace_bytes(8, 128, 65536, 128) <= L.FA3Q_NOALLOC_SCRATCH_BYTES
 
 
 @no_gpu_only

@@ -1,0 +1,416 @@
+// Recall Window of 16-bit inputs (bf16, float16) for any window count, through one
+// histogram per head.
+//
+// msModelSlim page "FA3量化：Flash Attention 3激活量化算法说明", section 原理 -> 算法流程:
+// head h's N values are sorted (s[0] <= ... <= s[N-1]), t = int(ratio*N), and among the
+// windows [s[i], s[i+t-1]], i = 0 .. N-t, the one with the smallest length wins (here:
+// float32 length, smallest i on ties).
+//
+// A 16-bit input has at most 65536 distinct values, so the sorted head is fully described
+// by the count of each value: with the keys k (order-preserving images of the values) and
+// inc[k] the number of values whose key is <= k, s[r] is the value of the smallest key k
+// with inc[k] > r.  The windows need no sort either.  The first shortest window starts at
+// the first index of its lower value: if s[i-1] == s[i], the window at i-1 has the same
+// lower end and an upper end s[i+t-2] <= s[i+t-1], so it is at most as long (float32
+// subtraction is monotone), and the first minimum cannot be at i.  So only one window per
+// distinct value a matters, the one at its first index f(a) = inc[a] - count[a], and
+// only while f(a) <= N - t; its upper end is s[f(a) + t - 1].  Among these candidates the
+// smallest (length, a) is exactly the first shortest window of the sorted head.
+//
+//   calib_hist_kernel         one streaming pass.  Each workgroup counts the values of one
+//                             part of one head into a 65536-bin LDS histogram of packed
+//                             16-bit counters (two bins per dword) and writes the part's
+//                             counts to the workspace.  A counter that reaches 0x8000 is
+//                             taken back by 0x8000 and the event logged; the logged events
+//                             add 32768 each when the part is written out, so any part size
+//                             is counted exactly.
+//   calib_hist_window_kernel  one workgroup per head: sums the parts, scans the counts,
+//                             lists the distinct values with their inc[] (in LDS while they
+//                             fit, else as inc[] over all bins in the workspace), and finds
+//                             each candidate's upper end by binary search over inc[].
+#include <cmath>
+
+#include "calib_hist.hpp"
+
+namespace fa3q {
+namespace {
+
+constexpr int kHistThreads = 1024;
+constexpr int kBins = 65536;
+constexpr int kHistUnroll = 4;  // 16-byte vectors per thread in flight
+constexpr uint32_t kMaxEvents = 2048;  // overflow events one workgroup can log
+constexpr int64_t kMaxPartValues = static_cast<int64_t>(kMaxEvents) * 32768;  // so no log overflows
+constexpr int kBinsPerThread = kBins / kHistThreads;  // 64
+constexpr size_t kHistLds = kBins / 2 * 4 + kMaxEvents * 4 + 16;
+// one part's record in the workspace: the packed counters as they stand in LDS, then the
+// event count and the logged event keys (each event stands for 32768 more values)
+constexpr int64_t kPartPacked = kBins / 2;
+constexpr int64_t kPartWords = kPartPacked + 64 + kMaxEvents;
+constexpr int64_t kMinPartValues = int64_t{1} << 19;  // parts smaller than this do not pay for their record
+// distinct values the window kernel keeps in LDS: a 16-bit key and a 32-bit inc[] each
+constexpr int kWinCap = 24576;
+constexpr size_t kWinCtlWords = 64;
+constexpr size_t kWinLds = kWinCtlWords * 4 + static_cast<size_t>(kWinCap) * 4 + static_cast<size_t>(kWinCap) * 2;
+
+static_assert(kBinsPerThread * kHistThreads == kBins, "bins per thread");
+static_assert(kHistLds <= kLdsLimit && kWinLds <= kLdsLimit, "LDS budget");
+
+struct HistArgs {
+  const void* x[kHistMaxBatches];
+  uint32_t* hist;        // [nb][H][P][kPartWords] part records
+  int64_t Lv;            // 16-byte vectors per (b, h) slab
+  int64_t Qv;            // vectors per head: B * Lv
+  int64_t part_vecs;     // vectors per part (the last part may be shorter)
+  int64_t head_words;    // workspace words per head: P part records, at least 65536
+  int32_t H;
+  int32_t P;
+};
+
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+
+// Order-preserving keys of two 16-bit sign-magnitude values in one dword:
+// key = bits ^ (negative ? 0xffff : 0x8000).
+__device__ __forceinline__ uint32_t keys16(uint32_t w) {
+  const s16x2 sg = __builtin_bit_cast(s16x2, w) >> (s16x2){15, 15};
+  return w ^ ((__builtin_bit_cast(uint32_t, sg) & 0x7fff7fffu) | 0x80008000u);
+}
+
+__device__ __forceinline__ uint4 load_nt16(const uint4* p) {
+  const u32x4v v = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// One value into the packed LDS histogram; a counter reaching 0x8000 is taken back and logged.
+__device__ __forceinline__ void count_key(uint32_t* hist, uint32_t* ev, uint32_t* nev, uint32_t key) {
+  const uint32_t sh = (key & 1u) << 4;
+  const uint32_t old = atomicAdd(&hist[key >> 1], 1u << sh);
+  if (((old >> sh) & 0xffffu) == 0x7fffu) {
+    const uint32_t e = atomicAdd(nev, 1u);
+    ev[e] = key;
+    atomicSub(&hist[key >> 1], 0x8000u << sh);
+  }
+}
+
+__device__ __forceinline__ void count_vec(uint32_t* hist, uint32_t* ev, uint32_t* nev, const uint4& v) {
+  const uint32_t w[4] = {keys16(v.x), keys16(v.y), keys16(v.z), keys16(v.w)};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    count_key(hist, ev, nev, w[i] & 0xffffu);
+    count_key(hist, ev, nev, w[i] >> 16);
+  }
+}
+
+__global__ __launch_bounds__(kHistThreads) void calib_hist_kernel(HistArgs a) {
+  extern __shared__ uint32_t lds[];
+  uint32_t* hist = lds;                 // [32768] two 16-bit counters per dword
+  uint32_t* ev = lds + kBins / 2;       // [kMaxEvents] keys of logged overflow events
+  uint32_t* nev = ev + kMaxEvents;      // event count
+  const int tid = static_cast<int>(threadIdx.x);
+  for (int i = tid; i < kBins / 8; i += kHistThreads) reinterpret_cast<uint4*>(hist)[i] = make_uint4(0, 0, 0, 0);
+  if (tid == 0) *nev = 0;
+  __syncthreads();
+
+  const int part = static_cast<int>(blockIdx.x) % a.P;
+  const int bh = static_cast<int>(blockIdx.x) / a.P;  // batch * H + head
+  const int h = bh % a.H;
+  const int bi = bh / a.H;
+  const uint4* xb = static_cast<const uint4*>(a.x[bi]);
+  int64_t q = static_cast<int64_t>(part) * a.part_vecs;
+  const int64_t q_end = min(q + a.part_vecs, a.Qv);
+  while (q < q_end) {  // one (b, h) slab segment at a time
+    const int64_t b = q / a.Lv;
+    const int64_t w = q - b * a.Lv;
+    const int64_t n = min(q_end - q, a.Lv - w);
+    const uint4* src = xb + (b * a.H + h) * a.Lv + w;
+    for (int64_t i0 = 0; i0 < n; i0 += static_cast<int64_t>(kHistThreads) * kHistUnroll) {
+      uint4 v[kHistUnroll];
+#pragma unroll
+      for (int u = 0; u < kHistUnroll; ++u) {
+        const int64_t i = i0 + u * kHistThreads + tid;
+        v[u] = load_nt16(src + min(i, n - 1));  // in bounds; a re-read vector is not counted
+      }
+#pragma unroll
+      for (int u = 0; u < kHistUnroll; ++u) {
+        if (i0 + u * kHistThreads + tid < n) count_vec(hist, ev, nev, v[u]);
+      }
+    }
+    q += n;
+  }
+  __syncthreads();
+
+  // the part's record: the packed counters, the event count and the event keys
+  uint32_t* out = a.hist + static_cast<int64_t>(bh) * a.head_words + static_cast<int64_t>(part) * kPartWords;
+  for (int i = tid; i < kBins / 8; i += kHistThreads)
+    reinterpret_cast<uint4*>(out)[i] = reinterpret_cast<const uint4*>(hist)[i];
+  const uint32_t ne = *nev;
+  if (tid == 0) out[kPartPacked] = ne;
+  for (uint32_t e = tid; e < ne; e += kHistThreads) out[kPartPacked + 64 + e] = ev[e];
+}
+
+struct WinArgs {
+  uint32_t* hist;   // [nb*H][P][kPartWords] part records; part 0's first 65536 words become inc[]
+                    // when the distinct values do not fit in LDS
+  float* win_min;   // [nb*H]
+  float* win_max;
+  int64_t head_words;  // workspace words per head
+  uint32_t t;       // target_num
+  uint32_t K;       // windows: N - t + 1
+  int32_t P;
+  int32_t f16;      // 1: float16 input, 0: bf16
+};
+
+__device__ __forceinline__ float value16(uint32_t key, bool f16) {
+  const uint32_t bits = (key & 0x8000u) ? (key ^ 0x8000u) : (key ^ 0xffffu);
+  return f16 ? static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)))
+             : __uint_as_float(bits << 16);
+}
+
+// Exclusive scan of one value per thread over the 1024 threads; *total gets the sum.
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* scratch, uint32_t* total) {
+  const int tid = static_cast<int>(threadIdx.x);
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  uint32_t inc = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const uint32_t u = __shfl_up(inc, o);
+    if (lane >= o) inc += u;
+  }
+  if (lane == kWave - 1) scratch[wave] = inc;
+  __syncthreads();
+  if (wave == 0) {
+    constexpr int kWaves = kHistThreads / kWave;
+    uint32_t s = lane < kWaves ? scratch[lane] : 0u;
+    uint32_t si = s;
+#pragma unroll
+    for (int o = 1; o < kWaves; o <<= 1) {
+      const uint32_t u = __shfl_up(si, o);
+      if (lane >= o) si += u;
+    }
+    if (lane < kWaves) scratch[lane] = si - s;  // exclusive wave offsets
+    if (lane == kWaves - 1) scratch[kWaves] = si;
+  }
+  __syncthreads();
+  const uint32_t r = scratch[wave] + inc - v;
+  *total = scratch[kHistThreads / kWave];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(kHistThreads) void calib_hist_window_kernel(WinArgs a) {
+  extern __shared__ uint32_t lds[];
+  uint32_t* ctl = lds;                                  // [kWinCtlWords] scan and reduction scratch
+  uint32_t* inc_l = lds + kWinCtlWords;                 // [kWinCap] inc of each distinct value
+  uint16_t* key_l = reinterpret_cast<uint16_t*>(inc_l + kWinCap);  // [kWinCap] its key
+  const int tid = static_cast<int>(threadIdx.x);
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  const int64_t bh = blockIdx.x;
+  uint32_t* hs = a.hist + bh * a.head_words;
+  const int bin0 = tid * kBinsPerThread;
+  const bool f16 = a.f16 != 0;
+
+  // this thread's 64 bins, summed over the parts (two 16-bit counters per packed word)
+  uint32_t c[kBinsPerThread];
+#pragma unroll
+  for (int i = 0; i < kBinsPerThread; ++i) c[i] = 0;
+  uint32_t n_events = 0;
+  for (int p = 0; p < a.P; ++p) {
+    const uint32_t* rec = hs + static_cast<int64_t>(p) * kPartWords;
+#pragma unroll
+    for (int i = 0; i < kBinsPerThread / 8; ++i) {
+      const uint4 v = reinterpret_cast<const uint4*>(rec + bin0 / 2)[i];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        c[8 * i + 2 * k] += w[k] & 0xffffu;
+        c[8 * i + 2 * k + 1] += w[k] >> 16;
+      }
+    }
+    n_events += rec[kPartPacked];
+  }
+  if (n_events) {
+    // logged overflow events (rare: a bin past 32767 values in one part), 32768 values each:
+    // counted per bin in LDS as packed 16-bit counters, then added to the owners' bins
+    for (int i = tid; i < kBins / 8; i += kHistThreads) reinterpret_cast<uint4*>(lds)[i] = make_uint4(0, 0, 0, 0);
+    __syncthreads();
+    for (int p = 0; p < a.P; ++p) {
+      const uint32_t* rec = hs + static_cast<int64_t>(p) * kPartWords;
+      const uint32_t ne = rec[kPartPacked];
+      for (uint32_t e = tid; e < ne; e += kHistThreads) {
+        const uint32_t key = rec[kPartPacked + 64 + e];
+        atomicAdd(&lds[key >> 1], 1u << ((key & 1u) << 4));
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kBinsPerThread / 2; ++i) {
+      const uint32_t w = lds[bin0 / 2 + i];
+      c[2 * i] += (w & 0xffffu) << 15;
+      c[2 * i + 1] += (w >> 16) << 15;
+    }
+    __syncthreads();
+  }
+  uint32_t sum = 0, nz = 0;
+#pragma unroll
+  for (int i = 0; i < kBinsPerThread; ++i) {
+    sum += c[i];
+    nz += c[i] ? 1u : 0u;
+  }
+  uint32_t n_total = 0, distinct = 0;
+  const uint32_t pre0 = block_exclusive_scan(sum, ctl, &n_total);
+  const uint32_t j0 = block_exclusive_scan(nz, ctl, &distinct);
+  const bool in_lds = distinct <= static_cast<uint32_t>(kWinCap);
+
+  uint32_t run = pre0;
+  if (in_lds) {
+    uint32_t j = j0;
+#pragma unroll
+    for (int i = 0; i < kBinsPerThread; ++i) {
+      if (c[i]) {
+        run += c[i];
+        inc_l[j] = run;
+        key_l[j] = static_cast<uint16_t>(bin0 + i);
+        ++j;
+      }
+    }
+    __syncthreads();
+  } else {
+    // inc[] over all bins, in place over the head's records (every thread has read its bins
+    // of every part above; the head's region holds at least 65536 words)
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kBinsPerThread; ++i) {
+      run += c[i];
+      hs[bin0 + i] = run;
+    }
+    __threadfence();
+    __syncthreads();
+  }
+
+  // candidates: each distinct value a whose first index f(a) is below K; the window's
+  // upper end is the smallest key m with inc[m] > f(a) + t - 1.
+  uint64_t best = ~uint64_t{0};
+  uint32_t best_hi = 0;
+  if (in_lds) {
+    for (uint32_t j = static_cast<uint32_t>(tid); j < distinct; j += kHistThreads) {
+      const uint32_t f = j ? inc_l[j - 1] : 0u;
+      if (f >= a.K) break;  // f grows with j
+      const uint32_t r = f + a.t - 1;
+      uint32_t lo = j, hi = distinct - 1;  // inc_l[distinct-1] = N > r
+      while (lo < hi) {
+        const uint32_t mid = (lo + hi) >> 1;
+        if (inc_l[mid] > r) hi = mid; else lo = mid + 1;
+      }
+      const uint32_t kl = key_l[j], ku = key_l[lo];
+      const float len = value16(ku, f16) - value16(kl, f16);
+      const uint64_t cand = (static_cast<uint64_t>(__float_as_uint(len)) << 32) | j;
+      if (cand < best) {
+        best = cand;
+        best_hi = (kl << 16) | ku;
+      }
+    }
+  } else {
+    uint32_t f = pre0;
+#pragma unroll
+    for (int i = 0; i < kBinsPerThread; ++i) {
+      if (c[i] && f < a.K) {
+        const uint32_t r = f + a.t - 1;
+        uint32_t lo = static_cast<uint32_t>(bin0 + i), hi = kBins - 1;
+        while (lo < hi) {
+          const uint32_t mid = (lo + hi) >> 1;
+          const uint32_t im = __hip_atomic_load(hs + mid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (im > r) hi = mid; else lo = mid + 1;
+        }
+        const uint32_t kl = static_cast<uint32_t>(bin0 + i);
+        const float len = value16(lo, f16) - value16(kl, f16);
+        const uint64_t cand = (static_cast<uint64_t>(__float_as_uint(len)) << 32) | kl;
+        if (cand < best) {
+          best = cand;
+          best_hi = (kl << 16) | lo;
+        }
+      }
+      f += c[i];
+    }
+  }
+  // lengths are >= +0, so their bits order as unsigned: the smallest (length, index) wins
+  uint64_t m = best;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint64_t u = __shfl_xor(m, o);
+    m = u < m ? u : m;
+  }
+  uint64_t* wbest = reinterpret_cast<uint64_t*>(ctl);
+  if (lane == 0) wbest[wave] = m;
+  __syncthreads();
+  if (tid == 0) {
+    uint64_t g = wbest[0];
+    for (int w = 1; w < kHistThreads / kWave; ++w) g = wbest[w] < g ? wbest[w] : g;
+    ctl[40] = static_cast<uint32_t>(g);
+    ctl[41] = static_cast<uint32_t>(g >> 32);
+  }
+  __syncthreads();
+  const uint64_t g = (static_cast<uint64_t>(ctl[41]) << 32) | ctl[40];
+  if (best == g && g != ~uint64_t{0}) {  // exactly one thread holds the winning candidate
+    a.win_min[bh] = value16(best_hi >> 16, f16);
+    a.win_max[bh] = value16(best_hi & 0xffffu, f16);
+  }
+}
+
+}  // namespace
+
+int hist_plan(int64_t B, int64_t H, int64_t S, int64_t D, HistPlan& hp) {
+  if (B <= 0 || H <= 0 || S <= 0 || D <= 0) return FA3Q_ERR_SHAPE;
+  const int64_t L = S * D;
+  if (L % 8 != 0) return FA3Q_ERR_SHAPE;
+  const int64_t N = B * L;
+  if (N >= (int64_t{1} << 32)) return FA3Q_ERR_SHAPE;
+  hp.Lv = L / 8;
+  hp.Qv = B * hp.Lv;
+  // parts per head: one workgroup per CU for a single batch of H heads (the plan does not
+  // depend on the batch count, so every batch has a region of the same size), each part
+  // small enough for the event log
+  int64_t P = std::max<int64_t>(1, (256 + H - 1) / H);
+  P = std::min<int64_t>(P, std::max<int64_t>(1, N / kMinPartValues));
+  P = std::max<int64_t>(P, (N + kMaxPartValues - 1) / kMaxPartValues);
+  P = std::min<int64_t>(P, hp.Qv);
+  hp.part_vecs = (hp.Qv + P - 1) / P;
+  hp.P = (hp.Qv + hp.part_vecs - 1) / hp.part_vecs;
+  if (hp.part_vecs * 8 > kMaxPartValues) return FA3Q_ERR_SHAPE;
+  if (kHistMaxBatches * H * hp.P > (int64_t{1} << 31) - 1) return FA3Q_ERR_SHAPE;
+  hp.head_words = std::max<int64_t>(hp.P * kPartWords, kBins);
+  hp.bytes = static_cast<size_t>(H * hp.head_words) * sizeof(uint32_t);
+  return FA3Q_OK;
+}
+
+int hist_launch(const void* const* xs, int64_t nb, int64_t H, bool f16, int64_t t, int64_t K, const HistPlan& hp,
+                float* win_min, float* win_max, void* workspace, hipStream_t stream) {
+  int st = allow_dynamic_lds(reinterpret_cast<const void*>(calib_hist_kernel), kHistLds);
+  if (st != FA3Q_OK) return st;
+  st = allow_dynamic_lds(reinterpret_cast<const void*>(calib_hist_window_kernel), kWinLds);
+  if (st != FA3Q_OK) return st;
+  HistArgs ha;
+  for (int b = 0; b < kHistMaxBatches; ++b) ha.x[b] = b < nb ? xs[b] : nullptr;
+  ha.hist = static_cast<uint32_t*>(workspace);
+  ha.Lv = hp.Lv;
+  ha.Qv = hp.Qv;
+  ha.part_vecs = hp.part_vecs;
+  ha.head_words = hp.head_words;
+  ha.H = static_cast<int32_t>(H);
+  ha.P = static_cast<int32_t>(hp.P);
+  hipLaunchKernelGGL(calib_hist_kernel, dim3(static_cast<unsigned>(nb * H * hp.P)), dim3(kHistThreads), kHistLds,
+                     stream, ha);
+  WinArgs wa;
+  wa.hist = static_cast<uint32_t*>(workspace);
+  wa.win_min = win_min;
+  wa.win_max = win_max;
+  wa.head_words = hp.head_words;
+  wa.t = static_cast<uint32_t>(t);
+  wa.K = static_cast<uint32_t>(K);
+  wa.P = static_cast<int32_t>(hp.P);
+  wa.f16 = f16 ? 1 : 0;
+  hipLaunchKernelGGL(calib_hist_window_kernel, dim3(static_cast<unsigned>(nb * H)), dim3(kHistThreads), kWinLds,
+                     stream, wa);
+  return launch_status();
+}
+
+}  // namespace fa3q

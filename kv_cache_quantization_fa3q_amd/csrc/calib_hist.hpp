@@ -1,0 +1,30 @@
+// Recall Window of 16-bit inputs through one histogram per head (calib_hist.hip):
+// the path the calibration entry points take when the window count is past what the
+// streaming tail selection keeps on chip.
+#pragma once
+
+#include "fa3q_internal.hpp"
+
+namespace fa3q {
+
+constexpr int kHistMaxBatches = 16;
+
+struct HistPlan {
+  int64_t Lv = 0;         // 16-byte vectors per (b, h) slab
+  int64_t Qv = 0;         // vectors per head
+  int64_t part_vecs = 0;  // vectors per part
+  int64_t P = 0;          // parts per head
+  int64_t head_words = 0; // workspace words per head: P part records, at least 65536
+  size_t bytes = 0;       // workspace per batch: H regions of head_words uint32
+};
+
+// Plan for batches of (B, H, S, D) 16-bit values; S*D must be a multiple of 8 and
+// N = B*S*D below 2^32.  Batch b uses the workspace bytes [b*bytes, (b+1)*bytes).
+int hist_plan(int64_t B, int64_t H, int64_t S, int64_t D, HistPlan& hp);
+
+// Windows of nb (<= kHistMaxBatches) batches into win_min/win_max [nb][H]; f16: float16
+// input, else bf16; t = int(ratio*N), K = N - t + 1.
+int hist_launch(const void* const* xs, int64_t nb, int64_t H, bool f16, int64_t t, int64_t K, const HistPlan& hp,
+                float* win_min, float* win_max, void* workspace, hipStream_t stream);
+
+}  // namespace fa3q

@@ -66,6 +66,7 @@
 #include <cmath>
 #include <type_traits>
 
+#include "calib_hist.hpp"
 #include "fa3q_internal.hpp"
 
 namespace fa3q {
@@ -85,7 +86,7 @@ constexpr int kMergeTile = kMergeThreads * kMergePerThread;
 constexpr int64_t kTargetCUs = 256;    // MI355X compute units (sizes the chunk grid)
 constexpr int64_t kChunkGroupsPerCU = 4;  // chunk workgroups resident per CU (VGPR-bound)
 constexpr int kMinTilesPerChunk = 4;
-constexpr int kMaxBatches = 16;        // calibration batches one call can take
+constexpr int kMaxBatches = kHistMaxBatches;  // calibration batches one call can take (16)
 
 // Several batches of the same shape in one launch: workgroup i serves batch i / per, with
 // that batch's input and its own region of the workspace (lists, bounds, flags).
@@ -1351,6 +1352,8 @@ struct CalibPlan {
   bool estimate = false; // rank < K: the bound is checked by the merge, failures redone
   // workspace per batch: lists | counts | sorted | bounds | fail
   size_t lists_bytes = 0, counts_bytes = 0, sorted_bytes = 0, bounds_bytes = 0, fail_bytes = 0, total_bytes = 0;
+  bool hist = false;     // K past the on-chip tail lists: the histogram path (16-bit keys)
+  HistPlan hp;
 };
 
 int64_t next_pow2(int64_t v) {
@@ -1371,11 +1374,21 @@ int make_plan(int dtype, int64_t B, int64_t H, int64_t S, int64_t D, double rati
   if (B > (int64_t{1} << 40) / p.L || B * H > (int64_t{1} << 31)) return FA3Q_ERR_SHAPE;
   if (B * H > (int64_t{1} << 50) / p.L) return FA3Q_ERR_SHAPE;
   p.N = B * p.L;
+  if (p.N >= (int64_t{1} << 32)) return FA3Q_ERR_SHAPE;  // values per head
   if (!(ratio > 0.0 && ratio <= 1.0)) return FA3Q_ERR_RATIO;  // also rejects NaN
   p.t = static_cast<int64_t>(ratio * static_cast<double>(p.N));  // truncation toward zero
   if (p.t < 1) return FA3Q_ERR_RATIO;
   p.K = p.N - p.t + 1;
-  if (p.K > fa3q_calibrate_max_windows(dtype)) return FA3Q_ERR_UNSUPPORTED;
+  if (p.K > fa3q_calibrate_max_windows(dtype)) {
+    if (dtype == FA3Q_F32) return FA3Q_ERR_UNSUPPORTED;
+    // 16-bit keys: the whole head as one histogram, any K
+    p.hist = true;
+    p.key_bytes = 2;
+    const int st = hist_plan(B, H, S, D, p.hp);
+    if (st != FA3Q_OK) return st;
+    p.total_bytes = p.hp.bytes;
+    return FA3Q_OK;
+  }
 
   // Sample runs: one per 1/32 of the head's B*L/vec vectors, or back to back (covering
   // the whole head) when it has fewer than kSampleRuns runs' worth.
@@ -1655,6 +1668,8 @@ extern "C" int fa3q_calibrate_perhead(const void* x, int dtype, int64_t B, int64
   if (!workspace || workspace_bytes < p.total_bytes) return FA3Q_ERR_WORKSPACE;
   if (!is_aligned(workspace, 256)) return FA3Q_ERR_ALIGN;
   const void* xs[1] = {x};
+  if (p.hist)
+    return hist_launch(xs, 1, H, false, p.t, p.K, p.hp, win_min, win_max, workspace, as_stream(stream));
   if (dtype == FA3Q_BF16)
     return launch<uint16_t>(xs, 1, H, p, win_min, win_max, workspace, as_stream(stream));
   return launch<uint32_t>(xs, 1, H, p, win_min, win_max, workspace, as_stream(stream));
@@ -1664,7 +1679,7 @@ extern "C" size_t fa3q_calibrate_batches_workspace_bytes(int dtype, int64_t nb, 
                                                          int64_t D, double ratio) {
   CalibPlan p;
   if (nb <= 0 || nb > kMaxBatches || make_plan(dtype, B, H, S, D, ratio, p) != FA3Q_OK) return 0;
-  if (nb * B * H * p.nch > (int64_t{1} << 31) - 1) return 0;
+  if (!p.hist && nb * B * H * p.nch > (int64_t{1} << 31) - 1) return 0;
   return static_cast<size_t>(nb) * p.total_bytes + round_up(2 * static_cast<size_t>(nb * H) * sizeof(float), 256);
 }
 
@@ -1679,7 +1694,7 @@ extern "C" int fa3q_calibrate_batches(const void* const* xs, int64_t nb, int dty
   CalibPlan p;
   const int st = make_plan(dtype, B, H, S, D, ratio, p);
   if (st != FA3Q_OK) return st;
-  if (nb * H * p.nch > (int64_t{1} << 31) - 1) return FA3Q_ERR_SHAPE;
+  if (!p.hist && nb * H * p.nch > (int64_t{1} << 31) - 1) return FA3Q_ERR_SHAPE;
   for (int64_t b = 0; b < nb; ++b)
     if (!is_aligned(xs[b], 16)) return FA3Q_ERR_ALIGN;
   if (!is_aligned(run_min, 4) || !is_aligned(run_max, 4) || (win_min && (!is_aligned(win_min, 4) || !is_aligned(win_max, 4))))
@@ -1691,8 +1706,9 @@ extern "C" int fa3q_calibrate_batches(const void* const* xs, int64_t nb, int dty
   float* wmin = win_min ? win_min : wins;
   float* wmax = win_max ? win_max : wins + nb * H;
   hipStream_t s = as_stream(stream);
-  const int lst = dtype == FA3Q_BF16 ? launch<uint16_t>(xs, nb, H, p, wmin, wmax, workspace, s)
-                                     : launch<uint32_t>(xs, nb, H, p, wmin, wmax, workspace, s);
+  const int lst = p.hist ? hist_launch(xs, nb, H, false, p.t, p.K, p.hp, wmin, wmax, workspace, s)
+                  : dtype == FA3Q_BF16 ? launch<uint16_t>(xs, nb, H, p, wmin, wmax, workspace, s)
+                                       : launch<uint32_t>(xs, nb, H, p, wmin, wmax, workspace, s);
   if (lst != FA3Q_OK) return lst;
   hipLaunchKernelGGL(accumulate_batches_kernel, dim3(static_cast<unsigned>((H + 255) / 256)), dim3(256), 0, s, run_min,
                      run_max, wmin, wmax, nb, H, init ? 1 : 0);

@@ -44,3 +44,32 @@ def row_rel_err(out: np.ndarray, ref: np.ndarray) -> float:
     ref = np.asarray(ref, dtype=np.float64).reshape(-1, ref.shape[-1])
     denom = np.maximum(np.abs(ref).max(axis=1), 1e-300)
     return float((np.abs(out - ref).max(axis=1) / denom).max())
+
+
+def host_threads() -> int:
+    """Worker threads for oracle checks: the host cores this process may use (at most 16)."""
+    import os
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def oracle_windows(x: torch.Tensor, ratio: float, heads=None):
+    """The oracle's Recall Window of every head (or of `heads`) of a (B,H,S,D) device tensor,
+    computed head by head on a thread pool (numpy's sort runs outside the GIL).
+    Returns float32 (lo[len], hi[len])."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+
+    H = x.shape[1]
+    heads = list(range(H)) if heads is None else list(heads)
+    lo = np.empty(len(heads), np.float32)
+    hi = np.empty(len(heads), np.float32)
+    xh = x.detach().cpu()  # one copy to the host; heads are gathered there (exact widening to float32)
+
+    def one(i):
+        h = heads[i]
+        lo[i], hi[i] = oracle.recall_window(xh[:, h].to(torch.float32).numpy().reshape(-1), ratio)
+
+    with ThreadPoolExecutor(max_workers=host_threads()) as ex:
+        list(ex.map(one, range(len(heads))))
+    return lo, hi

@@ -64,12 +64,31 @@ def _ratio_for_k(N: int, K: int) -> float:
 
 
 @pytest.mark.parametrize("dtype,S", [(L.FA3Q_BF16, 4096), (L.FA3Q_F32, 2048)])
-def test_window_count_limit_is_where_the_plan_stops(dtype, S):
+def test_window_count_limit_is_where_the_tail_lists_stop(dtype, S):
     lib = fa.lib()
     kmax = lib.fa3q_calibrate_max_windows(dtype)
     N = S * 16
-    assert lib.fa3q_calibrate_workspace_bytes(dtype, 1, 2, S, 16, _ratio_for_k(N, kmax)) > 0
-    assert lib.fa3q_calibrate_workspace_bytes(dtype, 1, 2, S, 16, _ratio_for_k(N, kmax + 1)) == 0
+    at_cap = lib.fa3q_calibrate_workspace_bytes(dtype, 1, 2, S, 16, _ratio_for_k(N, kmax))
+    past = lib.fa3q_calibrate_workspace_bytes(dtype, 1, 2, S, 16, _ratio_for_k(N, kmax + 1))
+    assert at_cap > 0
+    if dtype == L.FA3Q_BF16:
+        # past the on-chip tail lists the histogram path takes over: a region of 65536 words per head
+        assert past >= 2 * 65536 * 4
+    else:
+        assert past == 0
+
+
+def test_bf16_calibration_takes_every_valid_ratio():
+    lib = fa.lib()
+    for B, H, S, D in ((1, 2, 64, 32), (8, 128, 2048, 128), (2, 128, 16384, 128)):
+        N = B * S * D
+        for ratio in (1.0, 0.99999, 0.9999, 0.999, 0.99, 0.9, 0.5, 0.1, 1.0 / N):
+            if int(ratio * N) < 1:
+                continue
+            assert lib.fa3q_calibrate_workspace_bytes(L.FA3Q_BF16, B, H, S, D, ratio) > 0, (B, H, S, D, ratio)
+            assert lib.fa3q_calibrate_batches_workspace_bytes(L.FA3Q_BF16, 4, B, H, S, D, ratio) > 0
+    # values per head must stay below 2^32
+    assert lib.fa3q_calibrate_workspace_bytes(L.FA3Q_BF16, 1 << 14, 1, 1 << 10, 1 << 8, 0.5) == 0
 
 
 def test_workspace_queries():

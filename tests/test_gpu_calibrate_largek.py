@@ -1,0 +1,127 @@
+"""Recall Window past the on-chip tail lists: the histogram path of 16-bit inputs.
+
+msModelSlim page "FA3量化", section 原理 -> 算法流程: the window is defined for every ratio
+in (0, 1] through target_num = int(ratio*N); K = N - target_num + 1 windows.  Once K is
+above fa3q_calibrate_max_windows the library counts each head into a 65536-bin histogram
+and finds the window from it.  Every head is compared bit for bit with the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import assert_bits_equal, f32, log, oracle_windows
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import kv_cache_quantization_fa3q_amd as m
+    return m
+
+
+def _k_of(ratio, N):
+    return N - int(ratio * N) + 1
+
+
+def _check(fa, x, ratio, what):
+    B, H, S, D = x.shape
+    N = B * S * D
+    K = _k_of(ratio, N)
+    assert K > fa.fa3q_calibrate_max_windows(x.dtype), (what, K)
+    log(f"{what}: shape {tuple(x.shape)} ratio={ratio!r} K={K} ws={fa.fa3q_calibrate_workspace_bytes(x.dtype, B, H, S, D, ratio)}")
+    wmin, wmax = fa.fa3q_calibrate_perhead(x, ratio)
+    torch.cuda.synchronize()
+    lo, hi = oracle_windows(x, ratio)
+    assert_bits_equal(f32(wmin), lo, f"{what} win_min")
+    assert_bits_equal(f32(wmax), hi, f"{what} win_max")
+    return wmin, wmax
+
+
+def test_first_k_past_the_tail_lists(fa):
+    cap = fa.fa3q_calibrate_max_windows(torch.bfloat16)
+    shape = (2, 8, 4096, 128)
+    N = 2 * 4096 * 128
+    sigma = synth.head_sigmas(8, seed=31)
+    x = synth.activations(shape, sigma, law="t3", outlier_frac=1e-4, outlier_mult=60.0, dtype=torch.bfloat16,
+                          seed=32, device=DEV)
+    ratio = (N - cap) / N  # exact in double: t = N - cap, K = cap + 1
+    assert _k_of(ratio, N) == cap + 1
+    _check(fa, x, ratio, "K = cap + 1")
+    for r in (0.98, 0.9, 0.5, 0.01):
+        _check(fa, x, r, f"ratio {r}")
+
+
+def test_config2_heads_at_0_99_and_0_9(fa):
+    # a full calibration batch of the DeepSeek-like K-nope shape: 128 heads of 2,097,152 values
+    shape = (8, 128, 2048, 128)
+    sigma = synth.head_sigmas(128, seed=2024)
+    x = synth.activations(shape, sigma, law="t3", dtype=torch.bfloat16, seed=100, device=DEV)
+    for ratio, K in ((0.99, 20973), (0.9, 209717)):
+        assert _k_of(ratio, 8 * 2048 * 128) == K
+        _check(fa, x, ratio, f"config-2 batch ratio {ratio}")
+
+
+def test_several_batches_in_one_call(fa):
+    shape, ratio, nb = (4, 16, 1024, 128), 0.95, 4
+    H = shape[1]
+    sigma = synth.head_sigmas(H, seed=41)
+    xs = [synth.activations(shape, sigma, law="t3", outlier_frac=1e-4, outlier_mult=60.0, dtype=torch.bfloat16,
+                            seed=42 + b, device=DEV) for b in range(nb)]
+    run_min = torch.empty(H, dtype=torch.float32, device=DEV)
+    run_max = torch.empty(H, dtype=torch.float32, device=DEV)
+    win_min = torch.empty((nb, H), dtype=torch.float32, device=DEV)
+    win_max = torch.empty((nb, H), dtype=torch.float32, device=DEV)
+    log(f"batches nb={nb} {shape} ratio={ratio} K={_k_of(ratio, 4 * 1024 * 128)}")
+    fa.fa3q_calibrate_batches(xs, ratio, run_min, run_max, True, win_min, win_max)
+    torch.cuda.synchronize()
+    omin, omax = oracle.init_running(H)
+    for b in range(nb):
+        lo, hi = oracle_windows(xs[b], ratio)
+        assert_bits_equal(f32(win_min[b]), lo, f"batch {b} win_min")
+        assert_bits_equal(f32(win_max[b]), hi, f"batch {b} win_max")
+        omin, omax = oracle.accumulate(omin, omax, lo, hi)
+    assert_bits_equal(f32(run_min), omin, "run_min")
+    assert_bits_equal(f32(run_max), omax, "run_max")
+
+
+def test_degenerate_heads(fa):
+    # head 0 all equal (every value in one bin: counter overflow events), head 1 two values,
+    # head 2 signed zeros and a few values, head 3 every finite bf16 pattern (more distinct
+    # values than the window kernel keeps on chip), head 4 arithmetic progression, head 5 normal
+    B, H, S, D = 1, 6, 2048, 512
+    N = S * D
+    g = torch.Generator(device="cpu")
+    g.manual_seed(7)
+    x = torch.empty((B, H, S, D), dtype=torch.bfloat16)
+    x[0, 0] = 1.5
+    x[0, 1] = torch.where(torch.rand((S, D), generator=g) < 0.3, torch.tensor(-2.0), torch.tensor(3.0)).to(torch.bfloat16)
+    z = torch.where(torch.rand((S, D), generator=g) < 0.5, torch.tensor(-0.0), torch.tensor(0.0))
+    z.view(-1)[:1000] = torch.randn(1000, generator=g)
+    x[0, 2] = z.to(torch.bfloat16)
+    bits = torch.arange(N, dtype=torch.int64) % 65536
+    finite = ((bits >> 7) & 0xff) != 0xff
+    pats = bits[finite]
+    pats = pats[torch.randperm(pats.numel(), generator=g)]
+    reps = (N + pats.numel() - 1) // pats.numel()
+    x[0, 3] = pats.repeat(reps)[:N].to(torch.int16).view(torch.bfloat16).view(S, D)
+    x[0, 4] = (torch.arange(N, dtype=torch.float32) % 251).to(torch.bfloat16).view(S, D)
+    x[0, 5] = torch.randn((S, D), generator=g).to(torch.bfloat16)
+    x = x.to(DEV)
+    for ratio in (0.97, 0.5, 1.0 / N):
+        _check(fa, x, ratio, f"degenerate heads ratio {ratio!r}")
+
+
+def test_float32_past_the_cap_is_refused(fa):
+    cap = fa.fa3q_calibrate_max_windows(torch.float32)
+    B, H, S, D = 1, 2, 256, 128
+    N = S * D
+    ratio = (N - cap) / N
+    assert _k_of(ratio, N) == cap + 1
+    x = torch.zeros((B, H, S, D), dtype=torch.float32, device=DEV)
+    with pytest.raises(fa.Fa3qError):
+        fa.fa3q_calibrate_perhead(x, ratio)

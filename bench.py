@@ -15,7 +15,11 @@ Prints one JSON line.  ``value`` is the step's algorithmic HBM bytes divided by 
 wall time (GB/s); per-stage figures (calib Gelem/s, quantize GB/s, decode KV GB/s, each
 as a fraction of the 8 TB/s HBM peak) are under ``breakdown``; ``roofline`` is for the
 kernel that takes the most time, timed with HIP events on the stream it runs on;
-``cpu_baseline`` is the CPU oracle timed on a bounded sample of the same workload.
+``cpu_baseline`` is the CPU oracle timed on a bounded sample of the same workload, on a
+pool of worker processes (one per host core the process may use, at most 16).
+
+Measurements outside the step (``breakdown`` entries after the four stages) can be
+narrowed with ``--only name,name`` for profiling runs.
 """
 from __future__ import annotations
 
@@ -70,6 +74,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of CPU oracle work for the baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default=None,
+                    help="comma-separated measurements outside the step to run (default: all): " + ", ".join(EXTRAS))
     return ap.parse_args()
 
 
@@ -107,75 +113,162 @@ def traffic_from_summary(kernel: str):
     return float(e["hbm_bytes_per_launch"]), f"{os.path.relpath(TRAFFIC_SUMMARY, ROOT)} (sources {e['source_sha256_16']})"
 
 
-def cpu_baseline(inputs, budget_s: float):
-    """Time the oracle (as is, single process, one BLAS thread) on bounded slices of the same workload."""
-    from threadpoolctl import threadpool_limits
+# ----------------------------------------------------------------------------- CPU oracle baseline
+#
+# The oracle as it stands, timed on the host's cores: a pool of spawned worker processes
+# (one BLAS/OpenMP thread each) reads the same synthetic inputs from shared memory and runs
+# the oracle's own functions on whole heads (calibration), (sequence, 8 heads) slices
+# (quantisation) and (sequence, 4 heads) slices (decode).  Each stage runs rounds of one
+# task per worker until its share of the budget is spent; its rate is the work done over
+# the stage's wall time.
 
-    with threadpool_limits(limits=1):
-        return _cpu_baseline(inputs, budget_s)
+_SHM = {}
 
 
-def _cpu_baseline(inputs, budget_s: float):
+def _cpu_worker_init():
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "BLIS_NUM_THREADS"):
+        os.environ[var] = "1"
+
+
+def _shm_array(name, shape, dtype):
     import numpy as np
-    import torch
+    from multiprocessing import shared_memory
+
+    if name not in _SHM:
+        _SHM[name] = shared_memory.SharedMemory(name=name)
+    return np.ndarray(shape, dtype=dtype, buffer=_SHM[name].buf)
+
+
+def _cpu_task(task):
+    """One oracle call in a worker on inputs in shared memory; returns the units it covered."""
+    import numpy as np
 
     import oracle
 
-    def bits16(t):
-        return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
-
-    per_stage = budget_s / 3.0
-    # calibrate: whole heads of batch 0 (one Recall Window per head)
-    x0 = inputs["calib"][0]
-    n_head = CAL_SHAPE[0] * CAL_SHAPE[2] * CAL_SHAPE[3]
-    done, t_cal, h = 0, 0.0, 0
-    while t_cal < per_stage and h < H:
-        head = x0[:, h].to(torch.float32).cpu().numpy().reshape(-1)
-        t0 = time.perf_counter()
+    kind, spec, arg = task
+    if kind == "calib":
+        x = _shm_array(*spec["x"])
+        head = oracle.bf16_bits_to_f32(x[:, arg].reshape(-1))
         oracle.recall_window(head, RATIO)
-        t_cal += time.perf_counter() - t0
-        done += n_head
-        h += 1
-    cal_rate = done / t_cal  # elements / s
-    heads_cal = h
-    # quantize: 8 heads x 4096 tokens of one sequence per round
-    k = inputs["k"]
-    scale = inputs["scale"].cpu().numpy()
-    done_b, t_q, rounds = 0, 0.0, 0
-    while t_q < per_stage and rounds < QB:
-        kb = bits16(k[rounds:rounds + 1, :8])
-        t0 = time.perf_counter()
-        oracle.quantize_k(kb, scale[:8], DN)
-        t_q += time.perf_counter() - t0
-        done_b += kb.size // (DN + DR) * (2 * (DN + DR) + DN + 2 * DR)
-        rounds += 1
-    q_rate = done_b / t_q
-    # decode: 4 (b,h) pairs per round
-    kq, kr, v, q = inputs["kq"], inputs["kr"], inputs["v"], inputs["q"]
-    done_d, t_d, r = 0, 0.0, 0
-    while t_d < per_stage and r < QB:
-        args = (bits16(q[r:r + 1, :4]), kq[r:r + 1, :4].cpu().numpy(), scale[:4], bits16(kr[r:r + 1, :4]),
-                bits16(v[r:r + 1, :4]), 1.0 / math.sqrt(DN + DR))
-        t0 = time.perf_counter()
-        oracle.decode_attn(*args)
-        t_d += time.perf_counter() - t0
-        done_d += 4 * QS * (DN + 2 * DR + 2 * DV)
-        r += 1
-    d_rate = done_d / t_d
+        return head.size
+    if kind == "quant":
+        b, h0 = arg
+        k = _shm_array(*spec["k"])
+        scale = _shm_array(*spec["scale"])
+        kb = np.ascontiguousarray(k[b:b + 1, h0:h0 + 8])
+        oracle.quantize_k(kb, scale[h0:h0 + 8], DN)
+        return kb.size // (DN + DR) * (2 * (DN + DR) + DN + 2 * DR)
+    if kind == "decode":
+        b, h0 = arg
+        kq, kr, v, q = (_shm_array(*spec[n]) for n in ("kq", "kr", "v", "q"))
+        scale = _shm_array(*spec["scale"])
+        sl = (slice(b, b + 1), slice(h0, h0 + 4))
+        oracle.decode_attn(q[sl], kq[sl], scale[h0:h0 + 4], kr[sl], v[sl], 1.0 / math.sqrt(DN + DR))
+        return 4 * kq.shape[2] * (DN + 2 * DR + 2 * DV)
+    raise ValueError(kind)
+
+
+def _host_info():
+    model, mem = None, None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        with open("/proc/meminfo") as f:
+            for line in f:
+                if line.startswith("MemTotal:"):
+                    mem = int(line.split()[1]) * 1024
+                    break
+    except OSError:
+        pass
+    return model or platform.processor() or platform.machine(), mem
+
+
+def cpu_pool(workers: int):
+    """The worker pool, started before the GPU is touched (spawned interpreters that only run the oracle)."""
+    import multiprocessing as mp
+
+    return mp.get_context("spawn").Pool(workers, initializer=_cpu_worker_init)
+
+
+def cpu_baseline(pool, workers: int, inputs, budget_s: float):
+    """Oracle throughput on `workers` host processes over the same workload (bounded sample)."""
+    import numpy as np
+    import torch
+    from multiprocessing import shared_memory
+
+    owned = []
+
+    def share(name, t):
+        a = t.detach().contiguous().cpu()
+        if a.dtype in (torch.bfloat16, torch.float16):
+            a = a.view(torch.int16)
+        arr = a.numpy()
+        if arr.dtype == np.int16:
+            arr = arr.view(np.uint16)
+        shm = shared_memory.SharedMemory(create=True, size=max(1, arr.nbytes))
+        owned.append(shm)
+        np.ndarray(arr.shape, dtype=arr.dtype, buffer=shm.buf)[...] = arr
+        return (shm.name, arr.shape, arr.dtype.str)
+
+    NS = 4  # sequences of the quantisation / decode workload shared with the workers
+    try:
+        spec = {
+            "x": share("x", inputs["calib"][0]),
+            "k": share("k", inputs["k"][:NS]),
+            "scale": share("scale", inputs["scale"]),
+            "kq": share("kq", inputs["kq"][:NS]),
+            "kr": share("kr", inputs["kr"][:NS]),
+            "v": share("v", inputs["v"][:NS]),
+            "q": share("q", inputs["q"][:NS]),
+        }
+        per_stage = budget_s / 3.0
+
+        def stage(kind, args):
+            # one task per worker first (it also attaches the shared inputs), then as many more as
+            # the stage's budget allows at that pace, in one map so no worker waits on a round
+            t0 = time.perf_counter()
+            done = sum(pool.map(_cpu_task, [(kind, spec, a) for a in args[:workers]], chunksize=1))
+            first = time.perf_counter() - t0
+            rounds = int(max(0.0, per_stage - first) / max(first, 1e-3))
+            rest = args[workers:workers + workers * rounds]
+            if rest:
+                done += sum(pool.map(_cpu_task, [(kind, spec, a) for a in rest], chunksize=1))
+            return done / (time.perf_counter() - t0), min(len(args), workers) + len(rest)
+
+        cal_rate, n_heads = stage("calib", list(range(H)))
+        q_rate, n_q = stage("quant", [(b, h0) for b in range(NS) for h0 in range(0, H, 8)])
+        d_rate, n_d = stage("decode", [(b, h0) for b in range(NS) for h0 in range(0, H, 4)])
+    finally:
+        for shm in owned:
+            shm.close()
+            shm.unlink()
     step_s = CAL_BATCHES * CAL_BYTES / (2 * cal_rate) + QUANT_BYTES / q_rate + DEC_BYTES / d_rate
     total = CAL_BATCHES * CAL_BYTES + QUANT_BYTES + DEC_BYTES
+    model, mem = _host_info()
     return {
         "value": total / step_s / 1e9,
         "unit": "GB/s",
-        "cores": 1,
+        "cores": workers,
         "kind": "oracle",
-        "sample": (f"{heads_cal} whole heads of one calibration batch (2,097,152 values each), {rounds} x "
-                   f"(8 heads x 4096 tokens) of K quantisation, {r} x 4 (b,h) decode pairs over 4096 tokens; "
-                   "rates scaled to one full step by the step's bytes per stage"),
+        "sample": (f"{n_heads} whole heads of one calibration batch (2,097,152 values each), {n_q} x "
+                   f"(sequence, 8 heads x 4096 tokens) of K quantisation, {n_d} x (sequence, 4 heads) decode slices "
+                   f"over 4096 tokens, on {workers} worker processes with one BLAS thread each; rates scaled to one "
+                   "full step by the step's bytes per stage"),
         "stages": {"calib_gelem_s": cal_rate / 1e9, "quantize_gbs": q_rate / 1e9, "decode_kv_gbs": d_rate / 1e9},
-        "cpu": platform.processor() or platform.machine(),
+        "cpu": model,
+        "host_mem_bytes": mem,
         "host_threads_available": len(os.sched_getaffinity(0)),
     }
+
+
+EXTRAS = ("decode_append", "decode_qkv8", "asym", "fake_quant", "decode_latent", "calibrate_long",
+          "calibrate_largek", "decode_long", "decode_noalloc", "decode_paged")
 
 
 def main() -> int:
@@ -184,6 +277,22 @@ def main() -> int:
         log("bench.py measures one GPU: this build has no multi-GPU path (each GPU would run its own "
             "heads or sequences with no exchange); run with --gpus 1")
         return 2
+    only = set(EXTRAS) if args.only is None else {e for e in args.only.split(",") if e}
+    unknown = only - set(EXTRAS)
+    if unknown:
+        log(f"unknown --only entries {sorted(unknown)}; choose from {', '.join(EXTRAS)}")
+        return 2
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    pool = None if args.no_cpu_baseline else cpu_pool(workers)  # before the GPU is touched
+    try:
+        return run(args, only, pool, workers)
+    finally:
+        if pool is not None:
+            pool.terminate()
+            pool.join()
+
+
+def run(args, only, pool, workers) -> int:
     import torch
 
     import kv_cache_quantization_fa3q_amd as fa
@@ -257,9 +366,12 @@ def main() -> int:
     total_bytes = CAL_BATCHES * CAL_BYTES + QUANT_BYTES + DEC_BYTES
     value = total_bytes / (ms_per_step * 1e-3) / 1e9
 
-    cal_gbs = CAL_BATCHES * CAL_BYTES / (cal_ms * 1e-3) / 1e9
-    quant_gbs = QUANT_BYTES / (quant_ms * 1e-3) / 1e9
-    dec_gbs = DEC_BYTES / (dec_ms * 1e-3) / 1e9
+    def gbs(nbytes, ms):
+        return nbytes / (ms * 1e-3) / 1e9
+
+    cal_gbs = gbs(CAL_BATCHES * CAL_BYTES, cal_ms)
+    quant_gbs = gbs(QUANT_BYTES, quant_ms)
+    dec_gbs = gbs(DEC_BYTES, dec_ms)
     breakdown = {
         "calibrate": {"ms": cal_ms, "gelem_s": CAL_BATCHES * CAL_BYTES / 2 / (cal_ms * 1e-3) / 1e9,
                       "gbs": cal_gbs, "frac_hbm": cal_gbs / HBM_PEAK_GBS,
@@ -273,82 +385,13 @@ def main() -> int:
               "calib_chunk_kernel": (cal_ms, CAL_BATCHES * CAL_BYTES, 1)}
     dom = max(stages, key=lambda s: stages[s][0] * stages[s][2])
     d_ms, d_bytes, _ = stages[dom]
-    achieved = d_bytes / (d_ms * 1e-3) / 1e9
+    achieved = gbs(d_bytes, d_ms)
     traffic, traffic_src = traffic_from_summary(dom)
     roofline = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "traffic_source": traffic_src,
                 "algorithmic_bytes_per_launch": d_bytes, "avg_launch_ms": d_ms}
     if dom == "calib_chunk_kernel":
         roofline["note"] = "calibration: sample, chunk, merge and accumulate kernels, events around all four"
-
-    # Decode step with append (one new token per (b,h) written into the cache at position
-    # T-1, then attention over all T tokens): the same cache reads as decode plus one row
-    # written per (b,h); measured after the timed steps, outside the step.
-    k_new = synth.normal_tensor((QB, H, DN + DR), dtype=torch.bfloat16, seed=410, device=dev)
-    v_new = synth.normal_tensor((QB, H, DV), dtype=torch.bfloat16, seed=420, device=dev)
-    kv_len = torch.full((QB,), QS - 1, dtype=torch.int32, device=dev)
-    for _ in range(2):
-        fa.fa3q_decode_append_attn(q, k_new, v_new, scale, kq, kr, v, kv_len, sm, out, ws_dec, stream=stream)
-    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a0.record(stream)
-    for _ in range(5):
-        fa.fa3q_decode_append_attn(q, k_new, v_new, scale, kq, kr, v, kv_len, sm, out, ws_dec, stream=stream)
-    a1.record(stream)
-    torch.cuda.synchronize()
-    app_ms = a0.elapsed_time(a1) / 5
-    breakdown["decode_append"] = {"ms": app_ms, "kv_gbs": DEC_BYTES / (app_ms * 1e-3) / 1e9,
-                                  "frac_hbm": DEC_BYTES / (app_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                                  "note": "append one token per (b,h) at position T-1, then attention over T "
-                                          "(outside the step)"}
-
-    # Decode with Q (non-RoPE part), K-nope and V all INT8: V and Q get per-head scales from
-    # the library's own calibration (V: sequence 0 of the cache; Q: its non-RoPE part), are
-    # quantised by fa3q_quantize_k, then fa3q_decode_attn_qkv8 runs over the same K cache;
-    # measured outside the step.  384 B per cached token instead of 512.
-    def per_head_scale(x4):
-        nh = int(x4.shape[1])
-        mn = torch.empty(nh, dtype=torch.float32, device=dev)
-        mx = torch.empty(nh, dtype=torch.float32, device=dev)
-        rmin = torch.empty(nh, dtype=torch.float32, device=dev)
-        rmax = torch.empty(nh, dtype=torch.float32, device=dev)
-        fa.fa3q_init_minmax(rmin, rmax, stream=stream)
-        fa.fa3q_calibrate_perhead(x4, RATIO, mn, mx, stream=stream)
-        fa.fa3q_accumulate_minmax(rmin, rmax, mn, mx, stream=stream)
-        return fa.fa3q_qparams(rmin, rmax, stream=stream)
-
-    scale_v = per_head_scale(v[:1].contiguous())
-    scale_q = per_head_scale(q[:, :, :DN].contiguous().view(QB, H, 1, DN))
-    vq, _ = fa.fa3q_quantize_k(v, scale_v, DV, stream=stream)
-    qc, qrope = fa.fa3q_quantize_k(q.view(QB, H, 1, DN + DR), scale_q, DN, stream=stream)
-    qc, qrope = qc.view(QB, H, DN), qrope.view(QB, H, DR)
-    for _ in range(2):
-        fa.fa3q_decode_attn_qkv8(qc, qrope, scale_q, kq, scale, kr, vq, scale_v, sm, out, ws_dec, stream=stream)
-    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    b0.record(stream)
-    for _ in range(5):
-        fa.fa3q_decode_attn_qkv8(qc, qrope, scale_q, kq, scale, kr, vq, scale_v, sm, out, ws_dec, stream=stream)
-    b1.record(stream)
-    torch.cuda.synchronize()
-    q8_ms = b0.elapsed_time(b1) / 5
-    q8_bytes = QB * H * (QS * (DN + 2 * DR + DV) + DN + 2 * DR + 4 * DV)
-    breakdown["decode_qkv8"] = {"ms": q8_ms, "bytes": q8_bytes, "kv_gbs": q8_bytes / (q8_ms * 1e-3) / 1e9,
-                                "frac_hbm": q8_bytes / (q8_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                                "note": "Q (non-RoPE), K-nope and V INT8 with per-head scales; 384 B per cached "
-                                        "token (outside the step)"}
-    del vq
-
-    # Asymmetric K cache with a scale and an offset per (head, dim) (float16 tables): the tables
-    # are inputs (per-channel min/max of sequence 0 of K mapped onto [-128, 127], set up with
-    # torch), then fa3q_quantize_asym over the whole K and fa3q_decode_attn_asym over the
-    # resulting cache; measured outside the step.
-    kn0 = k[0, :, :, :DN].float()
-    lo, hi = kn0.amin(dim=1), kn0.amax(dim=1)
-    a_scale = ((hi - lo) / 255.0).clamp_min(1e-6)
-    a_offset = -128.0 - lo / a_scale
-    a_scale, a_offset = a_scale.to(torch.float16).contiguous(), a_offset.to(torch.float16).contiguous()
-    del kn0, lo, hi
-    akq = torch.empty_like(kq)
-    akr = torch.empty_like(kr)
 
     def timed(fn, reps=5):
         for _ in range(2):
@@ -361,130 +404,189 @@ def main() -> int:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
-    aq_ms = timed(lambda: fa.fa3q_quantize_asym(k, a_scale, a_offset, DN, akq, akr, stream=stream))
-    ad_ms = timed(lambda: fa.fa3q_decode_attn_asym(q, akq, a_scale, a_offset, akr, v, sm, out, ws_dec,
-                                                   stream=stream))
-    breakdown["quantize_asym"] = {"ms": aq_ms, "gbs": QUANT_BYTES / (aq_ms * 1e-3) / 1e9,
-                                  "frac_hbm": QUANT_BYTES / (aq_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                                  "note": "scale and offset per (head, dim), float16 tables (outside the step)"}
-    breakdown["decode_asym"] = {"ms": ad_ms, "kv_gbs": DEC_BYTES / (ad_ms * 1e-3) / 1e9,
-                                "frac_hbm": DEC_BYTES / (ad_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                                "note": "attention over the asymmetric K-nope cache (outside the step)"}
-    del akq, akr
+    def hbm_row(ms, nbytes, note, key="gbs", **extra):
+        r = {"ms": ms, key: gbs(nbytes, ms), "frac_hbm": gbs(nbytes, ms) / HBM_PEAK_GBS, "note": note}
+        r.update(extra)
+        return r
 
-    # Fake quantisation of the same K (quantise, dequantise back to bf16; the RoPE part copied):
-    # out of place (768 B per (token, head)), then in place on the result (512 B: the RoPE part
-    # is neither read nor written; the operation is idempotent, so every call does the same
-    # work); outside the step.
-    fq_y = torch.empty_like(k)
-    fq_ms = timed(lambda: fa.fa3q_fake_quant(k, scale, DN, fq_y, stream=stream))
-    fqi_ms = timed(lambda: fa.fa3q_fake_quant(fq_y, scale, DN, fq_y, stream=stream))
-    fq_bytes = QB * H * QS * 4 * (DN + DR)
-    fqi_bytes = QB * H * QS * 4 * DN
-    breakdown["fake_quant"] = {"ms": fq_ms, "gbs": fq_bytes / (fq_ms * 1e-3) / 1e9,
-                               "frac_hbm": fq_bytes / (fq_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                               "note": "K (64,128,4096,128+64) bf16 -> bf16, out of place (outside the step)"}
-    breakdown["fake_quant_in_place"] = {"ms": fqi_ms, "gbs": fqi_bytes / (fqi_ms * 1e-3) / 1e9,
-                                        "frac_hbm": fqi_bytes / (fqi_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                                        "note": "the same in place: only the non-RoPE part is touched"}
-    del fq_y
+    def per_head_scale(x4):
+        nh = int(x4.shape[1])
+        mn = torch.empty(nh, dtype=torch.float32, device=dev)
+        mx = torch.empty(nh, dtype=torch.float32, device=dev)
+        rmin = torch.empty(nh, dtype=torch.float32, device=dev)
+        rmax = torch.empty(nh, dtype=torch.float32, device=dev)
+        fa.fa3q_init_minmax(rmin, rmax, stream=stream)
+        fa.fa3q_calibrate_perhead(x4, RATIO, mn, mx, stream=stream)
+        fa.fa3q_accumulate_minmax(rmin, rmax, mn, mx, stream=stream)
+        return fa.fa3q_qparams(rmin, rmax, stream=stream)
 
-    # Shared-latent (absorbed MLA) cache, the same sequences: per token one latent row of
-    # 512 features (+ 64 RoPE) shared by all 128 heads, built by the library's own path with
-    # one head (calibration, scale, quantisation), then fa3q_decode_latent; outside the step.
-    # Both products run on MFMA: 2 * H * (Dl + Dr + Dl) flop per (b, t).
-    LAT_DL = 512
-    lat_rows = synth.activations((QB, 1, QS, LAT_DL + DR), sigma[:1], law="normal", outlier_frac=0.0005,
-                                 outlier_mult=40.0, dtype=torch.bfloat16, seed=500, device=dev)
-    lat_scale = per_head_scale(lat_rows[:, :, :, :LAT_DL].contiguous())
-    lat_c, lat_r = fa.fa3q_quantize_k(lat_rows, lat_scale, LAT_DL, stream=stream)
-    del lat_rows
-    lat_q = synth.normal_tensor((QB, H, LAT_DL + DR), dtype=torch.bfloat16, seed=510, device=dev)
-    lat_out = torch.empty((QB, H, LAT_DL), dtype=torch.float32, device=dev)
-    lat_ws_bytes = fa.fa3q_decode_latent_workspace_bytes(QB, H, QS, LAT_DL)
-    lat_ws = torch.empty(max(1, lat_ws_bytes), dtype=torch.uint8, device=dev)
-    lt_ms = timed(lambda: fa.fa3q_decode_latent(lat_q, lat_c, lat_scale, lat_r, sm, lat_out, lat_ws, stream=stream))
-    lat_flop = QB * H * QS * 2 * (2 * LAT_DL + DR)
-    lat_bytes = QB * QS * (LAT_DL + 2 * DR) + QB * H * (2 * (LAT_DL + DR) + 4 * LAT_DL)
-    breakdown["decode_latent"] = {
-        "ms": lt_ms, "tflops": lat_flop / (lt_ms * 1e-3) / 1e12,
-        "frac_mfma_bf16": lat_flop / (lt_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-        "cache_gbs": lat_bytes / (lt_ms * 1e-3) / 1e9,
-        "note": "shared-latent MLA cache, B=64 H=128 T=4096 Dl=512 Dr=64, MFMA bf16 (outside the step)"}
-    del lat_c, lat_r, lat_q, lat_out, lat_ws
+    # ------------------------------------------------------------------ measurements outside the step
+    if "decode_append" in only:
+        # one new token per (b,h) written into the cache at position T-1, then attention over all
+        # T tokens: the cache reads of decode plus one row written per (b,h)
+        k_new = synth.normal_tensor((QB, H, DN + DR), dtype=torch.bfloat16, seed=410, device=dev)
+        v_new = synth.normal_tensor((QB, H, DV), dtype=torch.bfloat16, seed=420, device=dev)
+        kv_len = torch.full((QB,), QS - 1, dtype=torch.int32, device=dev)
+        app_ms = timed(lambda: fa.fa3q_decode_append_attn(q, k_new, v_new, scale, kq, kr, v, kv_len, sm, out, ws_dec,
+                                                          stream=stream))
+        breakdown["decode_append"] = hbm_row(app_ms, DEC_BYTES, "append one token per (b,h) at position T-1, then "
+                                             "attention over T (outside the step)", key="kv_gbs")
+        del k_new, v_new, kv_len
 
-    # Long context, outside the step.  Calibration of one (2,128,16384,128) bf16 tensor
-    # (Student-t(3) tails, 1e-4 outliers at +-60 sigma) at each of the three ratios, one
-    # fa3q_calibrate_perhead call each; then decode with B=8, T=32768 over the step's cache
-    # bytes read as 8 sequences of 32768 tokens (the same 17.2 GB; the split path).
-    long_x = synth.activations(LONG_SHAPE, synth.head_sigmas(H, seed=77), law="t3", outlier_frac=1e-4,
-                               outlier_mult=60.0, dtype=torch.bfloat16, seed=501, device=dev)
-    long_ws = torch.empty(max(fa.fa3q_calibrate_workspace_bytes(torch.bfloat16, *LONG_SHAPE, r) for r in LONG_RATIOS),
-                          dtype=torch.uint8, device=dev)
-    long_min = torch.empty(H, dtype=torch.float32, device=dev)
-    long_max = torch.empty(H, dtype=torch.float32, device=dev)
+    if "decode_qkv8" in only:
+        # Q (non-RoPE part), K-nope and V all INT8: V and Q get per-head scales from the library's
+        # own calibration (V: sequence 0 of the cache; Q: its non-RoPE part); 384 B per cached token
+        scale_v = per_head_scale(v[:1].contiguous())
+        scale_q = per_head_scale(q[:, :, :DN].contiguous().view(QB, H, 1, DN))
+        vq, _ = fa.fa3q_quantize_k(v, scale_v, DV, stream=stream)
+        qc, qrope = fa.fa3q_quantize_k(q.view(QB, H, 1, DN + DR), scale_q, DN, stream=stream)
+        qc, qrope = qc.view(QB, H, DN), qrope.view(QB, H, DR)
+        q8_ms = timed(lambda: fa.fa3q_decode_attn_qkv8(qc, qrope, scale_q, kq, scale, kr, vq, scale_v, sm, out,
+                                                       ws_dec, stream=stream))
+        q8_bytes = QB * H * (QS * (DN + 2 * DR + DV) + DN + 2 * DR + 4 * DV)
+        breakdown["decode_qkv8"] = hbm_row(q8_ms, q8_bytes, "Q (non-RoPE), K-nope and V INT8 with per-head scales; "
+                                           "384 B per cached token (outside the step)", key="kv_gbs", bytes=q8_bytes)
+        del vq
+
+    if "asym" in only:
+        # asymmetric K cache with a scale and an offset per (head, dim) (float16 tables derived with
+        # torch from per-channel min/max of sequence 0), quantised then decoded
+        kn0 = k[0, :, :, :DN].float()
+        lo, hi = kn0.amin(dim=1), kn0.amax(dim=1)
+        a_scale = ((hi - lo) / 255.0).clamp_min(1e-6)
+        a_offset = -128.0 - lo / a_scale
+        a_scale, a_offset = a_scale.to(torch.float16).contiguous(), a_offset.to(torch.float16).contiguous()
+        del kn0, lo, hi
+        akq = torch.empty_like(kq)
+        akr = torch.empty_like(kr)
+        aq_ms = timed(lambda: fa.fa3q_quantize_asym(k, a_scale, a_offset, DN, akq, akr, stream=stream))
+        ad_ms = timed(lambda: fa.fa3q_decode_attn_asym(q, akq, a_scale, a_offset, akr, v, sm, out, ws_dec,
+                                                       stream=stream))
+        breakdown["quantize_asym"] = hbm_row(aq_ms, QUANT_BYTES, "scale and offset per (head, dim), float16 tables "
+                                             "(outside the step)")
+        breakdown["decode_asym"] = hbm_row(ad_ms, DEC_BYTES, "attention over the asymmetric K-nope cache (outside "
+                                           "the step)", key="kv_gbs")
+        del akq, akr
+
+    if "fake_quant" in only:
+        # out of place (768 B per (token, head)), then in place on the result (512 B: the RoPE part is
+        # neither read nor written; the operation is idempotent, so every call does the same work)
+        fq_y = torch.empty_like(k)
+        fq_ms = timed(lambda: fa.fa3q_fake_quant(k, scale, DN, fq_y, stream=stream))
+        fqi_ms = timed(lambda: fa.fa3q_fake_quant(fq_y, scale, DN, fq_y, stream=stream))
+        breakdown["fake_quant"] = hbm_row(fq_ms, QB * H * QS * 4 * (DN + DR), "K (64,128,4096,128+64) bf16 -> bf16, "
+                                          "out of place (outside the step)")
+        breakdown["fake_quant_in_place"] = hbm_row(fqi_ms, QB * H * QS * 4 * DN, "the same in place: only the "
+                                                   "non-RoPE part is touched")
+        del fq_y
+
+    if "decode_latent" in only:
+        # shared-latent (absorbed MLA) cache: per token one latent row of 512 features (+ 64 RoPE)
+        # shared by all 128 heads, built by the library's own path with one head; both products on
+        # MFMA: 2 * H * (Dl + Dr + Dl) flop per (b, t)
+        LAT_DL = 512
+        lat_rows = synth.activations((QB, 1, QS, LAT_DL + DR), sigma[:1], law="normal", outlier_frac=0.0005,
+                                     outlier_mult=40.0, dtype=torch.bfloat16, seed=500, device=dev)
+        lat_scale = per_head_scale(lat_rows[:, :, :, :LAT_DL].contiguous())
+        lat_c, lat_r = fa.fa3q_quantize_k(lat_rows, lat_scale, LAT_DL, stream=stream)
+        del lat_rows
+        lat_q = synth.normal_tensor((QB, H, LAT_DL + DR), dtype=torch.bfloat16, seed=510, device=dev)
+        lat_out = torch.empty((QB, H, LAT_DL), dtype=torch.float32, device=dev)
+        lat_ws = torch.empty(max(1, fa.fa3q_decode_latent_workspace_bytes(QB, H, QS, LAT_DL)), dtype=torch.uint8,
+                             device=dev)
+        lt_ms = timed(lambda: fa.fa3q_decode_latent(lat_q, lat_c, lat_scale, lat_r, sm, lat_out, lat_ws,
+                                                    stream=stream))
+        lat_flop = QB * H * QS * 2 * (2 * LAT_DL + DR)
+        lat_bytes = QB * QS * (LAT_DL + 2 * DR) + QB * H * (2 * (LAT_DL + DR) + 4 * LAT_DL)
+        breakdown["decode_latent"] = {
+            "ms": lt_ms, "tflops": lat_flop / (lt_ms * 1e-3) / 1e12,
+            "frac_mfma_bf16": lat_flop / (lt_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "cache_gbs": gbs(lat_bytes, lt_ms),
+            "note": "shared-latent MLA cache, B=64 H=128 T=4096 Dl=512 Dr=64, MFMA bf16 (outside the step)"}
+        del lat_c, lat_r, lat_q, lat_out, lat_ws
+
     long_bytes = 2 * math.prod(LONG_SHAPE)
-    for r in LONG_RATIOS:
-        n = LONG_SHAPE[0] * LONG_SHAPE[2] * LONG_SHAPE[3]
-        c_ms = timed(lambda: fa.fa3q_calibrate_perhead(long_x, r, long_min, long_max, long_ws, stream=stream))
-        breakdown[f"calibrate_long_{r}"] = {
-            "ms": c_ms, "gbs": long_bytes / (c_ms * 1e-3) / 1e9,
-            "frac_hbm": long_bytes / (c_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "K": n - int(r * n) + 1,
-            "note": f"one (2,128,16384,128) bf16 tensor at ratio {r} (outside the step)"}
-    del long_x, long_ws
+    n_long = LONG_SHAPE[0] * LONG_SHAPE[2] * LONG_SHAPE[3]
+    if "calibrate_long" in only or "calibrate_largek" in only:
+        # one (2,128,16384,128) bf16 tensor (Student-t(3) tails, 1e-4 outliers at +-60 sigma)
+        long_x = synth.activations(LONG_SHAPE, synth.head_sigmas(H, seed=77), law="t3", outlier_frac=1e-4,
+                                   outlier_mult=60.0, dtype=torch.bfloat16, seed=501, device=dev)
+        long_min = torch.empty(H, dtype=torch.float32, device=dev)
+        long_max = torch.empty(H, dtype=torch.float32, device=dev)
+
+        def calib_row(x, r, key, note):
+            B_, H_, S_, D_ = x.shape
+            ws = torch.empty(max(1, fa.fa3q_calibrate_workspace_bytes(torch.bfloat16, B_, H_, S_, D_, r)),
+                             dtype=torch.uint8, device=dev)
+            n = B_ * S_ * D_
+            c_ms = timed(lambda: fa.fa3q_calibrate_perhead(x, r, long_min, long_max, ws, stream=stream))
+            breakdown[key] = hbm_row(c_ms, 2 * x.numel(), note, K=n - int(r * n) + 1,
+                                     path="histogram" if n - int(r * n) + 1 > fa.fa3q_calibrate_max_windows(
+                                         torch.bfloat16) else "tail lists")
+            del ws
+
+        if "calibrate_long" in only:
+            for r in LONG_RATIOS:
+                calib_row(long_x, r, f"calibrate_long_{r}", f"one (2,128,16384,128) bf16 tensor at ratio {r} "
+                          "(outside the step)")
+        if "calibrate_largek" in only:
+            calib_row(long_x, 0.99, "calibrate_largek_long_0.99", "one (2,128,16384,128) bf16 tensor at ratio 0.99 "
+                      "(K past the on-chip tail lists: histogram path; outside the step)")
+            for r in (0.99, 0.9):
+                calib_row(calib[0], r, f"calibrate_largek_{r}", f"one (8,128,2048,128) bf16 batch at ratio {r} "
+                          "(histogram path; outside the step)")
+        del long_x
+
     LB, LT = 8, QB * QS // 8
     long_dec_bytes = LB * H * LT * (DN + 2 * DR + 2 * DV) + LB * H * (2 * (DN + DR) + 4 * DV)
-    ld_ws = torch.empty(max(1, fa.fa3q_decode_attn_workspace_bytes(LB, H, LT, DV)), dtype=torch.uint8, device=dev)
     kq_l, kr_l, v_l = kq.view(LB, H, LT, DN), kr.view(LB, H, LT, DR), v.view(LB, H, LT, DV)
     q_l, out_l = q[:LB], out[:LB]
-    ld_ms = timed(lambda: fa.fa3q_decode_attn(q_l, kq_l, scale, kr_l, v_l, sm, out_l, ld_ws, stream=stream))
-    breakdown["decode_long"] = {"ms": ld_ms, "kv_gbs": long_dec_bytes / (ld_ms * 1e-3) / 1e9,
-                                "frac_hbm": long_dec_bytes / (ld_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                                "note": "B=8 H=128 T=32768 Dv=128, split over the tokens (outside the step)"}
-    del ld_ws
+    if "decode_long" in only:
+        # decode with B=8, T=32768 over the step's cache bytes read as 8 sequences of 32768 tokens
+        ld_ws = torch.empty(max(1, fa.fa3q_decode_attn_workspace_bytes(LB, H, LT, DV)), dtype=torch.uint8,
+                            device=dev)
+        ld_ms = timed(lambda: fa.fa3q_decode_attn(q_l, kq_l, scale, kr_l, v_l, sm, out_l, ld_ws, stream=stream))
+        breakdown["decode_long"] = hbm_row(ld_ms, long_dec_bytes, "B=8 H=128 T=32768 Dv=128, split over the tokens "
+                                           "(outside the step)", key="kv_gbs")
+        del ld_ws
+    if "decode_noalloc" in only:
+        # the same long-context decode through the entry point that keeps its split states in the
+        # library's static scratch array
+        nd_ms = timed(lambda: fa.fa3q_decode_attn_noalloc(q_l, kq_l, scale, kr_l, v_l, sm, out_l, stream=stream))
+        breakdown["decode_noalloc"] = hbm_row(nd_ms, long_dec_bytes, "B=8 H=128 T=32768 through "
+                                              "fa3q_decode_attn_noalloc (outside the step)", key="kv_gbs")
 
-    # Paged cache: the step's cache bytes read as pools of 64-token pages (4096 pages of
-    # (H, 64, .)), each sequence's 64 pages scattered by a seeded permutation; attention over
-    # all 4096 tokens of every sequence through the block table; outside the step.
-    PG = 64
-    n_pages = QB * QS // PG
-    gen = torch.Generator(device="cpu")
-    gen.manual_seed(700)
-    table = torch.randperm(n_pages, generator=gen).to(torch.int32).view(QB, QS // PG).to(dev)
-    full_len = torch.full((QB,), QS, dtype=torch.int32, device=dev)
-    kq_p, kr_p, v_p = kq.view(n_pages, H, PG, DN), kr.view(n_pages, H, PG, DR), v.view(n_pages, H, PG, DV)
-    pg_ms = timed(lambda: fa.fa3q_decode_paged_attn(q, None, None, scale, kq_p, kr_p, v_p, table, full_len, sm, out,
-                                                    ws_dec, stream=stream))
-    pg_bytes = DEC_BYTES + table.numel() * 4
-    breakdown["decode_paged"] = {"ms": pg_ms, "kv_gbs": pg_bytes / (pg_ms * 1e-3) / 1e9,
-                                 "frac_hbm": pg_bytes / (pg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                                 "note": "B=64 H=128 T=4096 in 64-token pages through a permuted block table "
-                                         "(outside the step)"}
-    del table
+    if "decode_paged" in only:
+        # the step's cache bytes read as pools of 64-token pages, each sequence's 64 pages scattered by
+        # a seeded permutation; attention over all 4096 tokens of every sequence through the table
+        PG = 64
+        n_pages = QB * QS // PG
+        gen = torch.Generator(device="cpu")
+        gen.manual_seed(700)
+        table = torch.randperm(n_pages, generator=gen).to(torch.int32).view(QB, QS // PG).to(dev)
+        full_len = torch.full((QB,), QS, dtype=torch.int32, device=dev)
+        kq_p, kr_p, v_p = kq.view(n_pages, H, PG, DN), kr.view(n_pages, H, PG, DR), v.view(n_pages, H, PG, DV)
+        pg_ms = timed(lambda: fa.fa3q_decode_paged_attn(q, None, None, scale, kq_p, kr_p, v_p, table, full_len, sm,
+                                                        out, ws_dec, stream=stream))
+        breakdown["decode_paged"] = hbm_row(pg_ms, DEC_BYTES + table.numel() * 4, "B=64 H=128 T=4096 in 64-token "
+                                            "pages through a permuted block table (outside the step)", key="kv_gbs")
+        del table
 
     # device-to-device copy of COPY_BYTES: a reference ceiling for read+write streaming, and the
     # known-size kernel the HBM byte counters are scaled by
     src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
     dst = torch.empty_like(src)
     src.fill_(1.0)
-    for _ in range(2):
-        dst.copy_(src)
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record(stream)
-    for _ in range(5):
-        dst.copy_(src)
-    c1.record(stream)
-    torch.cuda.synchronize()
-    copy_ms = c0.elapsed_time(c1) / 5
+    copy_ms = timed(lambda: dst.copy_(src))
     copy_ref = {"bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES, "ms": copy_ms,
                 "gbs_read_plus_write": 2 * COPY_BYTES / (copy_ms * 1e-3) / 1e9}
     del src, dst
 
     cpu = None
-    if not args.no_cpu_baseline:
-        log("timing the CPU oracle on a bounded sample ...")
-        cpu = cpu_baseline({"calib": calib, "k": k, "scale": scale, "kq": kq, "kr": kr, "v": v, "q": q},
-                           args.cpu_budget)
+    if pool is not None:
+        log(f"timing the CPU oracle on a bounded sample with {workers} worker processes ...")
+        cpu = cpu_baseline(pool, workers, {"calib": calib, "k": k, "scale": scale, "kq": kq, "kr": kr, "v": v,
+                                           "q": q}, args.cpu_budget)
 
     rec = {
         "metric": METRIC,
@@ -497,12 +599,13 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
         "data": "synthetic",
         "config": {
             "workload": ("fa3q hot path: calibrate 4 x bf16 (8,128,2048,128) ratio 0.9999 -> accumulate -> qparams "
                          "-> quantize K (64,128,4096,128+64) -> decode attention B=64 H=128 T=4096 Dv=128"),
             "storage": "bf16 activations/K-rope/V, int8 K-nope cache, float32 stats and scales",
+            "arithmetic": "integer keys and float32 (window lengths, scales, quotients, attention)",
             "algorithmic_bytes_per_step": total_bytes,
         },
         "breakdown": breakdown,

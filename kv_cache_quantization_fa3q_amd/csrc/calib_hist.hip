@@ -19,15 +19,24 @@
 //
 //   calib_hist_kernel         one streaming pass.  Each workgroup counts the values of one
 //                             part of one head into a 65536-bin LDS histogram of packed
-//                             16-bit counters (two bins per dword) and writes the part's
-//                             counts to the workspace.  A counter that reaches 0x8000 is
-//                             taken back by 0x8000 and the event logged; the logged events
-//                             add 32768 each when the part is written out, so any part size
-//                             is counted exactly.
-//   calib_hist_window_kernel  one workgroup per head: sums the parts, scans the counts,
+//                             16-bit counters (two bins per dword), one bin per raw 16-bit
+//                             pattern, and writes the part's counters to the workspace.
+//                             Counters wrap, exactly accounted:
+//                             atomics on one dword are serialised, so each wrap of a 16-bit
+//                             field is seen by exactly one increment (the one that returned
+//                             0xffff in that field, or, for the upper field, a lower-field
+//                             increment that returned 0xffffffff and so carried it over).
+//                             That increment logs the wrap.  With W_lo lower and W_hi upper
+//                             wraps of dword d, bins 2d and 2d+1 hold
+//                             lower + 65536 W_lo and upper + 65536 W_hi - W_lo values (each
+//                             lower wrap also carried one into the upper field).
+//   calib_hist_window_kernel  one workgroup per head: sums the parts (reading the bins in
+//                             key order: patterns of non-negative values ascend with their
+//                             keys, those of negative values descend), scans the counts,
 //                             lists the distinct values with their inc[] (in LDS while they
 //                             fit, else as inc[] over all bins in the workspace), and finds
 //                             each candidate's upper end by binary search over inc[].
+
 #include <cmath>
 
 #include "calib_hist.hpp"
@@ -38,132 +47,145 @@ namespace {
 constexpr int kHistThreads = 1024;
 constexpr int kBins = 65536;
 constexpr int kHistUnroll = 4;  // 16-byte vectors per thread in flight
-constexpr uint32_t kMaxEvents = 2048;  // overflow events one workgroup can log
-constexpr int64_t kMaxPartValues = static_cast<int64_t>(kMaxEvents) * 32768;  // so no log overflows
+constexpr uint32_t kMaxEvents = 2048;  // counter wraps one workgroup can log
+// at most two wraps per 65536 values of a part (a lower wrap and the upper wrap its carry
+// completes), so parts of this size never overflow the log
+constexpr int64_t kMaxPartValues = static_cast<int64_t>(kMaxEvents) * 32768;
 constexpr int kBinsPerThread = kBins / kHistThreads;  // 64
+constexpr int kCtlWords = 64;  // scan and reduction scratch at the start of LDS
+// LDS of the counting kernel (static): packed counters, wrap log, wrap count
 constexpr size_t kHistLds = kBins / 2 * 4 + kMaxEvents * 4 + 16;
-// one part's record in the workspace: the packed counters as they stand in LDS, then the
-// event count and the logged event keys (each event stands for 32768 more values)
+// one part's record in the workspace: the packed counters as they stand in LDS, a header,
+// then the logged wraps (the pattern whose 16-bit field wrapped)
 constexpr int64_t kPartPacked = kBins / 2;
 constexpr int64_t kPartWords = kPartPacked + 64 + kMaxEvents;
+enum Hdr : int { kHdrEvents = 0 };
 constexpr int64_t kMinPartValues = int64_t{1} << 19;  // parts smaller than this do not pay for their record
 // distinct values the window kernel keeps in LDS: a 16-bit key and a 32-bit inc[] each
 constexpr int kWinCap = 24576;
-constexpr size_t kWinCtlWords = 64;
-constexpr size_t kWinLds = kWinCtlWords * 4 + static_cast<size_t>(kWinCap) * 4 + static_cast<size_t>(kWinCap) * 2;
+constexpr size_t kWinLds = kCtlWords * 4 + std::max<size_t>(static_cast<size_t>(kWinCap) * 6, kBins * 2);
 
 static_assert(kBinsPerThread * kHistThreads == kBins, "bins per thread");
 static_assert(kHistLds <= kLdsLimit && kWinLds <= kLdsLimit, "LDS budget");
+static_assert(kWinLds >= kCtlWords * 4 + kBins * 2, "the window kernel counts wraps in its LDS");
 
 struct HistArgs {
   const void* x[kHistMaxBatches];
-  uint32_t* hist;        // [nb][H][P][kPartWords] part records
+  uint32_t* hist;        // [nb][H] regions of head_words: P part records each
   int64_t Lv;            // 16-byte vectors per (b, h) slab
   int64_t Qv;            // vectors per head: B * Lv
   int64_t part_vecs;     // vectors per part (the last part may be shorter)
   int64_t head_words;    // workspace words per head: P part records, at least 65536
   int32_t H;
   int32_t P;
+  uint32_t t;            // target_num (window kernel)
+  uint32_t K;            // windows: N - t + 1 (window kernel)
+  float* win_min;        // [nb*H] (window kernel)
+  float* win_max;
+  int32_t f16;           // 1: float16 input, 0: bf16 (window kernel)
 };
 
-typedef short s16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
-
-// Order-preserving keys of two 16-bit sign-magnitude values in one dword:
-// key = bits ^ (negative ? 0xffff : 0x8000).
-__device__ __forceinline__ uint32_t keys16(uint32_t w) {
-  const s16x2 sg = __builtin_bit_cast(s16x2, w) >> (s16x2){15, 15};
-  return w ^ ((__builtin_bit_cast(uint32_t, sg) & 0x7fff7fffu) | 0x80008000u);
-}
 
 __device__ __forceinline__ uint4 load_nt16(const uint4* p) {
   const u32x4v v = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// One value into the packed LDS histogram; a counter reaching 0x8000 is taken back and logged.
-__device__ __forceinline__ void count_key(uint32_t* hist, uint32_t* ev, uint32_t* nev, uint32_t key) {
-  const uint32_t sh = (key & 1u) << 4;
-  const uint32_t old = atomicAdd(&hist[key >> 1], 1u << sh);
-  if (((old >> sh) & 0xffffu) == 0x7fffu) {
-    const uint32_t e = atomicAdd(nev, 1u);
-    ev[e] = key;
-    atomicSub(&hist[key >> 1], 0x8000u << sh);
-  }
+__device__ __forceinline__ float value16(uint32_t key, bool f16) {
+  const uint32_t bits = (key & 0x8000u) ? (key ^ 0x8000u) : (key ^ 0xffffu);
+  return f16 ? static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)))
+             : __uint_as_float(bits << 16);
 }
 
-__device__ __forceinline__ void count_vec(uint32_t* hist, uint32_t* ev, uint32_t* nev, const uint4& v) {
-  const uint32_t w[4] = {keys16(v.x), keys16(v.y), keys16(v.z), keys16(v.w)};
+// Counts the values of U vectors into the packed LDS histogram (with kAll false, lanes whose
+// valid[u] is false skip vector u).  Pattern p lives in dword p >> 1 (byte offset (p << 1) &
+// 0x1fffc), field p & 1, and is counted by adding 1 << (16 (p & 1)); both come straight
+// from the dword x holding two patterns (a shift amount's low five bits: (x << 4) & 31 is
+// 16 (x & 1)).  A field can only wrap once it holds 0xffff, so while no returned dword has
+// bit 15 of either field set (one OR per increment) no wrap happened; otherwise each
+// increment is looked at and its wraps logged (see the file header).
+template <int U, bool kAll>
+__device__ __forceinline__ void count_vecs(uint32_t* hist, uint32_t* ev, uint32_t* nev, const uint4 (&v)[U],
+                                           const bool (&valid)[U]) {
+  uint32_t o[U][8];  // returned dwords
+  unsigned char* base = reinterpret_cast<unsigned char*>(hist);
+  uint32_t seen = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    count_key(hist, ev, nev, w[i] & 0xffffu);
-    count_key(hist, ev, nev, w[i] >> 16);
+  for (int u = 0; u < U; ++u) {
+    const uint32_t xs[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t x = xs[d];
+      const uint32_t a0 = (x << 1) & 0x1fffcu, i0 = 1u << ((x << 4) & 31u);
+      const uint32_t a1 = (x >> 15) & 0x1fffcu, i1 = 1u << ((x >> 12) & 16u);
+      o[u][2 * d] = 0;
+      o[u][2 * d + 1] = 0;
+      if (kAll || valid[u]) {
+        o[u][2 * d] = atomicAdd(reinterpret_cast<uint32_t*>(base + a0), i0);
+        o[u][2 * d + 1] = atomicAdd(reinterpret_cast<uint32_t*>(base + a1), i1);
+      }
+      seen |= o[u][2 * d] | o[u][2 * d + 1];
+    }
+  }
+  if (seen & 0x80008000u) {  // rare: some field of a touched dword held 0x8000 or more
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t xs[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t p = (i & 1) ? (xs[i >> 1] >> 16) : (xs[i >> 1] & 0xffffu);
+        const uint32_t oo = o[u][i];
+        const bool counted = kAll || valid[u];
+        // upper field: this increment wrapped it (odd pattern), or its carry did (even, 0xffffffff)
+        const bool wrap_lo = counted && !(p & 1u) && (oo & 0xffffu) == 0xffffu;
+        const bool wrap_hi = counted && ((p & 1u) ? (oo >> 16) == 0xffffu : oo == 0xffffffffu);
+        if (wrap_lo || wrap_hi) {
+          const uint32_t e = atomicAdd(nev, (wrap_lo && wrap_hi) ? 2u : 1u);
+          if (wrap_lo) ev[e] = p;
+          if (wrap_hi) ev[e + (wrap_lo ? 1u : 0u)] = p | 1u;
+        }
+      }
+    }
   }
 }
 
-__global__ __launch_bounds__(kHistThreads) void calib_hist_kernel(HistArgs a) {
-  extern __shared__ uint32_t lds[];
-  uint32_t* hist = lds;                 // [32768] two 16-bit counters per dword
-  uint32_t* ev = lds + kBins / 2;       // [kMaxEvents] keys of logged overflow events
-  uint32_t* nev = ev + kMaxEvents;      // event count
+// Streams head vectors [q0, q1) of head h in batch xb into the LDS histogram, U vectors per
+// thread in flight.
+template <int U>
+__device__ __forceinline__ void count_range(const HistArgs& a, const uint4* xb, int h, int64_t q, int64_t q_end,
+                                            uint32_t* hist, uint32_t* ev, uint32_t* nev) {
   const int tid = static_cast<int>(threadIdx.x);
-  for (int i = tid; i < kBins / 8; i += kHistThreads) reinterpret_cast<uint4*>(hist)[i] = make_uint4(0, 0, 0, 0);
-  if (tid == 0) *nev = 0;
-  __syncthreads();
-
-  const int part = static_cast<int>(blockIdx.x) % a.P;
-  const int bh = static_cast<int>(blockIdx.x) / a.P;  // batch * H + head
-  const int h = bh % a.H;
-  const int bi = bh / a.H;
-  const uint4* xb = static_cast<const uint4*>(a.x[bi]);
-  int64_t q = static_cast<int64_t>(part) * a.part_vecs;
-  const int64_t q_end = min(q + a.part_vecs, a.Qv);
+  constexpr int64_t kRound = static_cast<int64_t>(kHistThreads) * U;
   while (q < q_end) {  // one (b, h) slab segment at a time
     const int64_t b = q / a.Lv;
     const int64_t w = q - b * a.Lv;
     const int64_t n = min(q_end - q, a.Lv - w);
     const uint4* src = xb + (b * a.H + h) * a.Lv + w;
-    for (int64_t i0 = 0; i0 < n; i0 += static_cast<int64_t>(kHistThreads) * kHistUnroll) {
-      uint4 v[kHistUnroll];
+    int64_t i0 = 0;
+    for (; i0 + kRound <= n; i0 += kRound) {  // full rounds: every lane counts all U vectors
+      uint4 v[U];
+      bool valid[U];
 #pragma unroll
-      for (int u = 0; u < kHistUnroll; ++u) {
+      for (int u = 0; u < U; ++u) {
+        valid[u] = true;
+        v[u] = load_nt16(src + i0 + u * kHistThreads + tid);
+      }
+      count_vecs<U, true>(hist, ev, nev, v, valid);
+    }
+    if (i0 < n) {  // the segment's last, partial round
+      uint4 v[U];
+      bool valid[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
         const int64_t i = i0 + u * kHistThreads + tid;
+        valid[u] = i < n;
         v[u] = load_nt16(src + min(i, n - 1));  // in bounds; a re-read vector is not counted
       }
-#pragma unroll
-      for (int u = 0; u < kHistUnroll; ++u) {
-        if (i0 + u * kHistThreads + tid < n) count_vec(hist, ev, nev, v[u]);
-      }
+      count_vecs<U, false>(hist, ev, nev, v, valid);
     }
     q += n;
   }
-  __syncthreads();
-
-  // the part's record: the packed counters, the event count and the event keys
-  uint32_t* out = a.hist + static_cast<int64_t>(bh) * a.head_words + static_cast<int64_t>(part) * kPartWords;
-  for (int i = tid; i < kBins / 8; i += kHistThreads)
-    reinterpret_cast<uint4*>(out)[i] = reinterpret_cast<const uint4*>(hist)[i];
-  const uint32_t ne = *nev;
-  if (tid == 0) out[kPartPacked] = ne;
-  for (uint32_t e = tid; e < ne; e += kHistThreads) out[kPartPacked + 64 + e] = ev[e];
-}
-
-struct WinArgs {
-  uint32_t* hist;   // [nb*H][P][kPartWords] part records; part 0's first 65536 words become inc[]
-                    // when the distinct values do not fit in LDS
-  float* win_min;   // [nb*H]
-  float* win_max;
-  int64_t head_words;  // workspace words per head
-  uint32_t t;       // target_num
-  uint32_t K;       // windows: N - t + 1
-  int32_t P;
-  int32_t f16;      // 1: float16 input, 0: bf16
-};
-
-__device__ __forceinline__ float value16(uint32_t key, bool f16) {
-  const uint32_t bits = (key & 0x8000u) ? (key ^ 0x8000u) : (key ^ 0xffffu);
-  return f16 ? static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)))
-             : __uint_as_float(bits << 16);
 }
 
 // Exclusive scan of one value per thread over the 1024 threads; *total gets the sum.
@@ -197,11 +219,68 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
   return r;
 }
 
-__global__ __launch_bounds__(kHistThreads) void calib_hist_window_kernel(WinArgs a) {
+__device__ __forceinline__ void zero_hist(uint32_t* hist) {
+  for (int i = static_cast<int>(threadIdx.x); i < kBins / 8; i += kHistThreads)
+    reinterpret_cast<uint4*>(hist)[i] = make_uint4(0, 0, 0, 0);
+}
+
+__global__ __launch_bounds__(kHistThreads) void calib_hist_kernel(HistArgs a) {
+  // static LDS, so the histogram's address folds into each atomic's offset
+  __shared__ uint32_t hist[kBins / 2];  // two 16-bit counters per dword
+  __shared__ uint32_t ev[kMaxEvents];   // patterns whose field wrapped
+  __shared__ uint32_t nev[1];           // wrap count
+  const int tid = static_cast<int>(threadIdx.x);
+  zero_hist(hist);
+  if (tid == 0) *nev = 0;
+  __syncthreads();
+
+  const int part = static_cast<int>(blockIdx.x) % a.P;
+  const int bh = static_cast<int>(blockIdx.x) / a.P;  // batch * H + head
+  const int h = bh % a.H;
+  const int bi = bh / a.H;
+  const uint4* xb = static_cast<const uint4*>(a.x[bi]);
+
+  int64_t q = static_cast<int64_t>(part) * a.part_vecs;
+  const int64_t q_end = min(q + a.part_vecs, a.Qv);
+  count_range<kHistUnroll>(a, xb, h, q, q_end, hist, ev, nev);
+  __syncthreads();
+
+  // the part's record: the packed counters, the header and the event keys
+  uint32_t* out = a.hist + static_cast<int64_t>(bh) * a.head_words + static_cast<int64_t>(part) * kPartWords;
+  for (int i = tid; i < kBins / 8; i += kHistThreads)
+    reinterpret_cast<uint4*>(out)[i] = reinterpret_cast<const uint4*>(hist)[i];
+  const uint32_t ne = *nev;
+  if (tid == 0) out[kPartPacked + kHdrEvents] = ne;
+  for (uint32_t e = tid; e < ne; e += kHistThreads) out[kPartPacked + 64 + e] = ev[e];
+}
+
+// Applies logged wraps to the thread's 32 dwords (patterns 2*dw0 .. 2*dw0+63, counts cp in
+// pattern order): the wraps are counted per pattern in the packed LDS histogram `cnt`
+// (zeroed by the caller), then dword d gets 65536 W_lo more in its lower pattern and
+// 65536 W_hi - W_lo more in its upper one.
+__device__ __forceinline__ void add_wraps(uint32_t (&cp)[kBinsPerThread], uint32_t* cnt, int dw0,
+                                          const uint32_t* pats, uint32_t n) {
+  const int tid = static_cast<int>(threadIdx.x);
+  for (uint32_t e = tid; e < n; e += kHistThreads) {
+    const uint32_t p = pats[e];
+    atomicAdd(&cnt[p >> 1], 1u << ((p & 1u) << 4));
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kBinsPerThread / 2; ++i) {
+    const uint32_t w = cnt[dw0 + i];
+    cp[2 * i] += (w & 0xffffu) << 16;
+    cp[2 * i + 1] += ((w >> 16) << 16) - (w & 0xffffu);
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kHistThreads) void calib_hist_window_kernel(HistArgs a) {
   extern __shared__ uint32_t lds[];
-  uint32_t* ctl = lds;                                  // [kWinCtlWords] scan and reduction scratch
-  uint32_t* inc_l = lds + kWinCtlWords;                 // [kWinCap] inc of each distinct value
+  uint32_t* ctl = lds;                                  // [kCtlWords] scan and reduction scratch
+  uint32_t* inc_l = lds + kCtlWords;                    // [kWinCap] inc of each distinct value
   uint16_t* key_l = reinterpret_cast<uint16_t*>(inc_l + kWinCap);  // [kWinCap] its key
+  uint32_t* hist = lds + kCtlWords;                     // the same LDS as packed wrap counts
   const int tid = static_cast<int>(threadIdx.x);
   const int lane = tid & (kWave - 1), wave = tid / kWave;
   const int64_t bh = blockIdx.x;
@@ -209,7 +288,11 @@ __global__ __launch_bounds__(kHistThreads) void calib_hist_window_kernel(WinArgs
   const int bin0 = tid * kBinsPerThread;
   const bool f16 = a.f16 != 0;
 
-  // this thread's 64 bins, summed over the parts (two 16-bit counters per packed word)
+  // this thread's 64 keys [bin0, bin0+64): patterns 2*dw0 .. 2*dw0+63, ascending with the
+  // keys for non-negative values (key = pattern ^ 0x8000), descending for negative ones
+  // (key = 0xffff - pattern); summed over the parts in pattern order, then put in key order
+  const bool neg = bin0 < 0x8000;
+  const int dw0 = neg ? (0xffc0 - bin0) / 2 : (bin0 - 0x8000) / 2;
   uint32_t c[kBinsPerThread];
 #pragma unroll
   for (int i = 0; i < kBinsPerThread; ++i) c[i] = 0;
@@ -218,7 +301,7 @@ __global__ __launch_bounds__(kHistThreads) void calib_hist_window_kernel(WinArgs
     const uint32_t* rec = hs + static_cast<int64_t>(p) * kPartWords;
 #pragma unroll
     for (int i = 0; i < kBinsPerThread / 8; ++i) {
-      const uint4 v = reinterpret_cast<const uint4*>(rec + bin0 / 2)[i];
+      const uint4 v = reinterpret_cast<const uint4*>(rec + dw0)[i];
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -226,30 +309,26 @@ __global__ __launch_bounds__(kHistThreads) void calib_hist_window_kernel(WinArgs
         c[8 * i + 2 * k + 1] += w[k] >> 16;
       }
     }
-    n_events += rec[kPartPacked];
+    n_events += rec[kPartPacked + kHdrEvents];
   }
   if (n_events) {
-    // logged overflow events (rare: a bin past 32767 values in one part), 32768 values each:
-    // counted per bin in LDS as packed 16-bit counters, then added to the owners' bins
-    for (int i = tid; i < kBins / 8; i += kHistThreads) reinterpret_cast<uint4*>(lds)[i] = make_uint4(0, 0, 0, 0);
-    __syncthreads();
+    // logged wraps (rare: a pattern past 65535 values in one part)
     for (int p = 0; p < a.P; ++p) {
       const uint32_t* rec = hs + static_cast<int64_t>(p) * kPartWords;
-      const uint32_t ne = rec[kPartPacked];
-      for (uint32_t e = tid; e < ne; e += kHistThreads) {
-        const uint32_t key = rec[kPartPacked + 64 + e];
-        atomicAdd(&lds[key >> 1], 1u << ((key & 1u) << 4));
-      }
+      zero_hist(hist);
+      __syncthreads();
+      add_wraps(c, hist, dw0, rec + kPartPacked + 64, rec[kPartPacked + kHdrEvents]);
     }
-    __syncthreads();
+  }
+  if (neg) {  // pattern order -> key order (uniform per wave)
 #pragma unroll
     for (int i = 0; i < kBinsPerThread / 2; ++i) {
-      const uint32_t w = lds[bin0 / 2 + i];
-      c[2 * i] += (w & 0xffffu) << 15;
-      c[2 * i + 1] += (w >> 16) << 15;
+      const uint32_t t = c[i];
+      c[i] = c[kBinsPerThread - 1 - i];
+      c[kBinsPerThread - 1 - i] = t;
     }
-    __syncthreads();
   }
+
   uint32_t sum = 0, nz = 0;
 #pragma unroll
   for (int i = 0; i < kBinsPerThread; ++i) {
@@ -261,9 +340,10 @@ __global__ __launch_bounds__(kHistThreads) void calib_hist_window_kernel(WinArgs
   const uint32_t j0 = block_exclusive_scan(nz, ctl, &distinct);
   const bool in_lds = distinct <= static_cast<uint32_t>(kWinCap);
 
-  uint32_t run = pre0;
+  uint64_t best = ~uint64_t{0};
+  uint32_t best_hi = 0;
   if (in_lds) {
-    uint32_t j = j0;
+    uint32_t run = pre0, j = j0;
 #pragma unroll
     for (int i = 0; i < kBinsPerThread; ++i) {
       if (c[i]) {
@@ -274,34 +354,18 @@ __global__ __launch_bounds__(kHistThreads) void calib_hist_window_kernel(WinArgs
       }
     }
     __syncthreads();
-  } else {
-    // inc[] over all bins, in place over the head's records (every thread has read its bins
-    // of every part above; the head's region holds at least 65536 words)
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < kBinsPerThread; ++i) {
-      run += c[i];
-      hs[bin0 + i] = run;
-    }
-    __threadfence();
-    __syncthreads();
-  }
-
-  // candidates: each distinct value a whose first index f(a) is below K; the window's
-  // upper end is the smallest key m with inc[m] > f(a) + t - 1.
-  uint64_t best = ~uint64_t{0};
-  uint32_t best_hi = 0;
-  if (in_lds) {
+    // candidates: each distinct value a whose first index f(a) is below K; the window's
+    // upper end is the smallest key m with inc[m] > f(a) + t - 1
     for (uint32_t j = static_cast<uint32_t>(tid); j < distinct; j += kHistThreads) {
       const uint32_t f = j ? inc_l[j - 1] : 0u;
       if (f >= a.K) break;  // f grows with j
       const uint32_t r = f + a.t - 1;
-      uint32_t lo = j, hi = distinct - 1;  // inc_l[distinct-1] = N > r
-      while (lo < hi) {
-        const uint32_t mid = (lo + hi) >> 1;
-        if (inc_l[mid] > r) hi = mid; else lo = mid + 1;
+      uint32_t lo_i = j, hi_i = distinct - 1;  // inc_l[distinct-1] = N > r
+      while (lo_i < hi_i) {
+        const uint32_t mid = (lo_i + hi_i) >> 1;
+        if (inc_l[mid] > r) hi_i = mid; else lo_i = mid + 1;
       }
-      const uint32_t kl = key_l[j], ku = key_l[lo];
+      const uint32_t kl = key_l[j], ku = key_l[lo_i];
       const float len = value16(ku, f16) - value16(kl, f16);
       const uint64_t cand = (static_cast<uint64_t>(__float_as_uint(len)) << 32) | j;
       if (cand < best) {
@@ -310,26 +374,37 @@ __global__ __launch_bounds__(kHistThreads) void calib_hist_window_kernel(WinArgs
       }
     }
   } else {
-    uint32_t f = pre0;
+    // inc[] over all bins, in place over the head's records (every thread has read its bins
+    // of every part above; the head's region holds at least 65536 words)
+    __syncthreads();
+    uint32_t run = pre0;
 #pragma unroll
     for (int i = 0; i < kBinsPerThread; ++i) {
-      if (c[i] && f < a.K) {
+      run += c[i];
+      hs[bin0 + i] = run;
+    }
+    __threadfence();
+    __syncthreads();
+    uint32_t f = pre0;
+    for (int i = 0; i < kBinsPerThread; ++i) {
+      const uint32_t kl = static_cast<uint32_t>(bin0 + i);
+      const uint32_t inc_k = __hip_atomic_load(hs + kl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (inc_k > f && f < a.K) {
         const uint32_t r = f + a.t - 1;
-        uint32_t lo = static_cast<uint32_t>(bin0 + i), hi = kBins - 1;
-        while (lo < hi) {
-          const uint32_t mid = (lo + hi) >> 1;
+        uint32_t lo_i = kl, hi_i = kBins - 1;
+        while (lo_i < hi_i) {
+          const uint32_t mid = (lo_i + hi_i) >> 1;
           const uint32_t im = __hip_atomic_load(hs + mid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if (im > r) hi = mid; else lo = mid + 1;
+          if (im > r) hi_i = mid; else lo_i = mid + 1;
         }
-        const uint32_t kl = static_cast<uint32_t>(bin0 + i);
-        const float len = value16(lo, f16) - value16(kl, f16);
+        const float len = value16(lo_i, f16) - value16(kl, f16);
         const uint64_t cand = (static_cast<uint64_t>(__float_as_uint(len)) << 32) | kl;
         if (cand < best) {
           best = cand;
-          best_hi = (kl << 16) | lo;
+          best_hi = (kl << 16) | lo_i;
         }
       }
-      f += c[i];
+      f = inc_k;
     }
   }
   // lengths are >= +0, so their bits order as unsigned: the smallest (length, index) wins
@@ -367,8 +442,8 @@ int hist_plan(int64_t B, int64_t H, int64_t S, int64_t D, HistPlan& hp) {
   hp.Lv = L / 8;
   hp.Qv = B * hp.Lv;
   // parts per head: one workgroup per CU for a single batch of H heads (the plan does not
-  // depend on the batch count, so every batch has a region of the same size), each part
-  // small enough for the event log
+  // depend on the batch count, so every batch has a region of the same size), parts not so
+  // small that their records cost more than their data, and small enough for the event log
   int64_t P = std::max<int64_t>(1, (256 + H - 1) / H);
   P = std::min<int64_t>(P, std::max<int64_t>(1, N / kMinPartValues));
   P = std::max<int64_t>(P, (N + kMaxPartValues - 1) / kMaxPartValues);
@@ -384,9 +459,7 @@ int hist_plan(int64_t B, int64_t H, int64_t S, int64_t D, HistPlan& hp) {
 
 int hist_launch(const void* const* xs, int64_t nb, int64_t H, bool f16, int64_t t, int64_t K, const HistPlan& hp,
                 float* win_min, float* win_max, void* workspace, hipStream_t stream) {
-  int st = allow_dynamic_lds(reinterpret_cast<const void*>(calib_hist_kernel), kHistLds);
-  if (st != FA3Q_OK) return st;
-  st = allow_dynamic_lds(reinterpret_cast<const void*>(calib_hist_window_kernel), kWinLds);
+  const int st = allow_dynamic_lds(reinterpret_cast<const void*>(calib_hist_window_kernel), kWinLds);
   if (st != FA3Q_OK) return st;
   HistArgs ha;
   for (int b = 0; b < kHistMaxBatches; ++b) ha.x[b] = b < nb ? xs[b] : nullptr;
@@ -397,19 +470,15 @@ int hist_launch(const void* const* xs, int64_t nb, int64_t H, bool f16, int64_t 
   ha.head_words = hp.head_words;
   ha.H = static_cast<int32_t>(H);
   ha.P = static_cast<int32_t>(hp.P);
-  hipLaunchKernelGGL(calib_hist_kernel, dim3(static_cast<unsigned>(nb * H * hp.P)), dim3(kHistThreads), kHistLds,
+  ha.t = static_cast<uint32_t>(t);
+  ha.K = static_cast<uint32_t>(K);
+  ha.win_min = win_min;
+  ha.win_max = win_max;
+  ha.f16 = f16 ? 1 : 0;
+  hipLaunchKernelGGL(calib_hist_kernel, dim3(static_cast<unsigned>(nb * H * hp.P)), dim3(kHistThreads), 0,
                      stream, ha);
-  WinArgs wa;
-  wa.hist = static_cast<uint32_t*>(workspace);
-  wa.win_min = win_min;
-  wa.win_max = win_max;
-  wa.head_words = hp.head_words;
-  wa.t = static_cast<uint32_t>(t);
-  wa.K = static_cast<uint32_t>(K);
-  wa.P = static_cast<int32_t>(hp.P);
-  wa.f16 = f16 ? 1 : 0;
   hipLaunchKernelGGL(calib_hist_window_kernel, dim3(static_cast<unsigned>(nb * H)), dim3(kHistThreads), kWinLds,
-                     stream, wa);
+                     stream, ha);
   return launch_status();
 }
 

@@ -125,3 +125,36 @@ def test_float32_past_the_cap_is_refused(fa):
     x = torch.zeros((B, H, S, D), dtype=torch.float32, device=DEV)
     with pytest.raises(fa.Fa3qError):
         fa.fa3q_calibrate_perhead(x, ratio)
+
+
+def _sampled_vectors(Qv):
+    """Head vectors the histogram path's bound sample reads: 32 runs of 128 vectors, one per
+    1/32 of the head at a fixed phase inside it (whole 128-byte lines)."""
+    stride = Qv // 32
+    room = max(0, stride - 128)
+    out = []
+    for j in range(32):
+        phase = (((((2 * j + 1) * 40503) & 0xFFFF) * room) >> 16) & ~7
+        out.extend(range(j * stride + phase, j * stride + phase + 128))
+    return out
+
+
+def test_sample_that_misses_the_tails(fa):
+    # heads whose sampled vectors all hold an extreme value the rest of the head lacks: the
+    # bounds from the sample leave fewer than K values beyond them, the exact check fails and
+    # the window workgroup counts the head again without bounds
+    B, H, S, D = 2, 4, 4096, 256
+    N = B * S * D
+    Lv = S * D // 8
+    ratio = 0.98
+    assert _k_of(ratio, N) > 32760  # more windows than the sample holds values
+    sigma = synth.head_sigmas(H, seed=51)
+    x = synth.activations((B, H, S, D), sigma, law="t3", dtype=torch.bfloat16, seed=52, device=DEV)
+    flat = x.view(B, H, S * D)
+    for h, val in ((0, -100.0), (1, 100.0), (2, -100.0)):
+        for qv in _sampled_vectors(B * Lv):
+            b, w = divmod(qv, Lv)
+            flat[b, h, 8 * w:8 * w + 8] = val
+        if h == 2:
+            flat[:, h, : S * D // 2] = 100.0  # and half the head beyond the other bound
+    _check(fa, x, ratio, "sample misses the tails")

@@ -520,9 +520,9 @@ def run(args, only, pool, workers) -> int:
                              dtype=torch.uint8, device=dev)
             n = B_ * S_ * D_
             c_ms = timed(lambda: fa.fa3q_calibrate_perhead(x, r, long_min, long_max, ws, stream=stream))
-            breakdown[key] = hbm_row(c_ms, 2 * x.numel(), note, K=n - int(r * n) + 1,
-                                     path="histogram" if n - int(r * n) + 1 > fa.fa3q_calibrate_max_windows(
-                                         torch.bfloat16) else "tail lists")
+            k_win = n - int(r * n) + 1
+            hist = k_win > fa.fa3q_calibrate_max_windows(torch.bfloat16) or n >= 1 << 20  # the header's routing
+            breakdown[key] = hbm_row(c_ms, 2 * x.numel(), note, K=k_win, path="histogram" if hist else "tail lists")
             del ws
 
         if "calibrate_long" in only:

@@ -101,8 +101,10 @@ int fa3q_version(void);
 /* ------------------------------------------------------------------------ */
 
 /*
- * Largest number of windows K = N - int(ratio*N) + 1 that fa3q_calibrate_perhead
- * handles for `dtype`; a larger K returns FA3Q_ERR_UNSUPPORTED.  0 for an
+ * Largest number of windows K = N - int(ratio*N) + 1 that the streaming tail selection
+ * (on-chip lists of the K smallest and K largest values) takes for `dtype`.  bf16 input
+ * with a larger K, or with heads of at least 2^20 values, takes the histogram path, which
+ * handles every K; float32 input with a larger K returns FA3Q_ERR_UNSUPPORTED.  0 for an
  * unknown dtype.
  */
 int64_t fa3q_calibrate_max_windows(int dtype);
@@ -126,15 +128,18 @@ size_t fa3q_calibrate_workspace_bytes(int dtype, int64_t B, int64_t H, int64_t S
  * of the input; exact, no rounding).
  *
  *   x          device, dtype FA3Q_F32 or FA3Q_BF16, (B,H,S,D) contiguous, 16-byte aligned.
- *   B,H,S,D    > 0; S*D must be a multiple of 8 (bf16) or 4 (f32).
+ *   B,H,S,D    > 0; S*D must be a multiple of 8 (bf16) or 4 (f32); N = B*S*D < 2^32.
  *   ratio      in (0, 1]; t = int(ratio*N) must be >= 1.
  *   win_min,
  *   win_max    device float32 [H], 4-byte aligned.
  *   workspace  device, 256-byte aligned, >= fa3q_calibrate_workspace_bytes(...).
  *
- * Only the K = N-t+1 smallest and K largest values of a head can bound a
- * window, so the kernels select those two tails in one pass over x instead of
- * sorting.  K above fa3q_calibrate_max_windows(dtype) -> FA3Q_ERR_UNSUPPORTED.
+ * No sort: one pass over x.  Only the K = N-t+1 smallest and K largest values of a
+ * head can bound a window; while K <= fa3q_calibrate_max_windows(dtype) and a head holds
+ * fewer than 2^20 values, the kernels select those two tails on chip.  A bf16 head is
+ * otherwise counted into a 65536-bin histogram (its sorted order exactly) and the window
+ * found from the counts, for every K.  float32 input with K above
+ * fa3q_calibrate_max_windows(FA3Q_F32) -> FA3Q_ERR_UNSUPPORTED.
  */
 int fa3q_calibrate_perhead(const void* x, int dtype, int64_t B, int64_t H, int64_t S, int64_t D,
                            double ratio, float* win_min, float* win_max, void* workspace,

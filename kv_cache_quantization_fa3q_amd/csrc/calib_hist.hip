@@ -53,8 +53,6 @@ constexpr uint32_t kMaxEvents = 2048;  // counter wraps one workgroup can log
 constexpr int64_t kMaxPartValues = static_cast<int64_t>(kMaxEvents) * 32768;
 constexpr int kBinsPerThread = kBins / kHistThreads;  // 64
 constexpr int kCtlWords = 64;  // scan and reduction scratch at the start of LDS
-// LDS of the counting kernel (static): packed counters, wrap log, wrap count
-constexpr size_t kHistLds = kBins / 2 * 4 + kMaxEvents * 4 + 16;
 // one part's record in the workspace: the packed counters as they stand in LDS, a header,
 // then the logged wraps (the pattern whose 16-bit field wrapped)
 constexpr int64_t kPartPacked = kBins / 2;
@@ -66,7 +64,7 @@ constexpr int kWinCap = 24576;
 constexpr size_t kWinLds = kCtlWords * 4 + std::max<size_t>(static_cast<size_t>(kWinCap) * 6, kBins * 2);
 
 static_assert(kBinsPerThread * kHistThreads == kBins, "bins per thread");
-static_assert(kHistLds <= kLdsLimit && kWinLds <= kLdsLimit, "LDS budget");
+static_assert(kWinLds <= kLdsLimit, "LDS budget");
 static_assert(kWinLds >= kCtlWords * 4 + kBins * 2, "the window kernel counts wraps in its LDS");
 
 struct HistArgs {
@@ -188,35 +186,37 @@ __device__ __forceinline__ void count_range(const HistArgs& a, const uint4* xb, 
   }
 }
 
-// Exclusive scan of one value per thread over the 1024 threads; *total gets the sum.
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* scratch, uint32_t* total) {
+// Exclusive scans of two values per thread over the 1024 threads at once; tot gets the sums.
+__device__ __forceinline__ uint2 block_exclusive_scan2(uint2 v, uint32_t* scratch, uint2* tot) {
   const int tid = static_cast<int>(threadIdx.x);
   const int lane = tid & (kWave - 1), wave = tid / kWave;
-  uint32_t inc = v;
+  constexpr int kWaves = kHistThreads / kWave;
+  uint2 inc = v;
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) {
-    const uint32_t u = __shfl_up(inc, o);
-    if (lane >= o) inc += u;
-  }
-  if (lane == kWave - 1) scratch[wave] = inc;
-  __syncthreads();
-  if (wave == 0) {
-    constexpr int kWaves = kHistThreads / kWave;
-    uint32_t s = lane < kWaves ? scratch[lane] : 0u;
-    uint32_t si = s;
-#pragma unroll
-    for (int o = 1; o < kWaves; o <<= 1) {
-      const uint32_t u = __shfl_up(si, o);
-      if (lane >= o) si += u;
+    const uint32_t ux = __shfl_up(inc.x, o), uy = __shfl_up(inc.y, o);
+    if (lane >= o) {
+      inc.x += ux;
+      inc.y += uy;
     }
-    if (lane < kWaves) scratch[lane] = si - s;  // exclusive wave offsets
-    if (lane == kWaves - 1) scratch[kWaves] = si;
+  }
+  if (lane == kWave - 1) {
+    scratch[wave] = inc.x;
+    scratch[kWaves + wave] = inc.y;
   }
   __syncthreads();
-  const uint32_t r = scratch[wave] + inc - v;
-  *total = scratch[kHistThreads / kWave];
-  __syncthreads();
-  return r;
+  // every wave sums the totals of the waves before it (16 values: no second barrier)
+  uint32_t bx = 0, by = 0, tx = 0, ty = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const uint32_t sx = scratch[w], sy = scratch[kWaves + w];
+    bx += w < wave ? sx : 0u;
+    by += w < wave ? sy : 0u;
+    tx += sx;
+    ty += sy;
+  }
+  *tot = make_uint2(tx, ty);
+  return make_uint2(bx + inc.x - v.x, by + inc.y - v.y);
 }
 
 __device__ __forceinline__ void zero_hist(uint32_t* hist) {
@@ -224,34 +224,18 @@ __device__ __forceinline__ void zero_hist(uint32_t* hist) {
     reinterpret_cast<uint4*>(hist)[i] = make_uint4(0, 0, 0, 0);
 }
 
-__global__ __launch_bounds__(kHistThreads) void calib_hist_kernel(HistArgs a) {
-  // static LDS, so the histogram's address folds into each atomic's offset
-  __shared__ uint32_t hist[kBins / 2];  // two 16-bit counters per dword
-  __shared__ uint32_t ev[kMaxEvents];   // patterns whose field wrapped
-  __shared__ uint32_t nev[1];           // wrap count
-  const int tid = static_cast<int>(threadIdx.x);
-  zero_hist(hist);
-  if (tid == 0) *nev = 0;
-  __syncthreads();
-
-  const int part = static_cast<int>(blockIdx.x) % a.P;
-  const int bh = static_cast<int>(blockIdx.x) / a.P;  // batch * H + head
-  const int h = bh % a.H;
-  const int bi = bh / a.H;
-  const uint4* xb = static_cast<const uint4*>(a.x[bi]);
-
-  int64_t q = static_cast<int64_t>(part) * a.part_vecs;
-  const int64_t q_end = min(q + a.part_vecs, a.Qv);
-  count_range<kHistUnroll>(a, xb, h, q, q_end, hist, ev, nev);
-  __syncthreads();
-
-  // the part's record: the packed counters, the header and the event keys
-  uint32_t* out = a.hist + static_cast<int64_t>(bh) * a.head_words + static_cast<int64_t>(part) * kPartWords;
-  for (int i = tid; i < kBins / 8; i += kHistThreads)
-    reinterpret_cast<uint4*>(out)[i] = reinterpret_cast<const uint4*>(hist)[i];
-  const uint32_t ne = *nev;
-  if (tid == 0) out[kPartPacked + kHdrEvents] = ne;
-  for (uint32_t e = tid; e < ne; e += kHistThreads) out[kPartPacked + 64 + e] = ev[e];
+// Per-thread counts from the packed 16-bit counters of dwords dw0 .. dw0+31 (pattern order).
+__device__ __forceinline__ void add_packed(uint32_t (&c)[kBinsPerThread], const uint32_t* words, int dw0) {
+#pragma unroll
+  for (int i = 0; i < kBinsPerThread / 8; ++i) {
+    const uint4 v = reinterpret_cast<const uint4*>(words + dw0)[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      c[8 * i + 2 * k] += w[k] & 0xffffu;
+      c[8 * i + 2 * k + 1] += w[k] >> 16;
+    }
+  }
 }
 
 // Applies logged wraps to the thread's 32 dwords (patterns 2*dw0 .. 2*dw0+63, counts cp in
@@ -275,52 +259,13 @@ __device__ __forceinline__ void add_wraps(uint32_t (&cp)[kBinsPerThread], uint32
   __syncthreads();
 }
 
-__global__ __launch_bounds__(kHistThreads) void calib_hist_window_kernel(HistArgs a) {
-  extern __shared__ uint32_t lds[];
-  uint32_t* ctl = lds;                                  // [kCtlWords] scan and reduction scratch
-  uint32_t* inc_l = lds + kCtlWords;                    // [kWinCap] inc of each distinct value
-  uint16_t* key_l = reinterpret_cast<uint16_t*>(inc_l + kWinCap);  // [kWinCap] its key
-  uint32_t* hist = lds + kCtlWords;                     // the same LDS as packed wrap counts
-  const int tid = static_cast<int>(threadIdx.x);
-  const int lane = tid & (kWave - 1), wave = tid / kWave;
-  const int64_t bh = blockIdx.x;
-  uint32_t* hs = a.hist + bh * a.head_words;
-  const int bin0 = tid * kBinsPerThread;
-  const bool f16 = a.f16 != 0;
+// Thread t holds the 64 keys [64t, 64t+64): patterns 2*dw0 .. 2*dw0+63, ascending with the
+// keys for non-negative values (key = pattern ^ 0x8000), descending for negative ones
+// (key = 0xffff - pattern).
+__device__ __forceinline__ int first_dword(int bin0) { return bin0 < 0x8000 ? (0xffc0 - bin0) / 2 : (bin0 - 0x8000) / 2; }
 
-  // this thread's 64 keys [bin0, bin0+64): patterns 2*dw0 .. 2*dw0+63, ascending with the
-  // keys for non-negative values (key = pattern ^ 0x8000), descending for negative ones
-  // (key = 0xffff - pattern); summed over the parts in pattern order, then put in key order
-  const bool neg = bin0 < 0x8000;
-  const int dw0 = neg ? (0xffc0 - bin0) / 2 : (bin0 - 0x8000) / 2;
-  uint32_t c[kBinsPerThread];
-#pragma unroll
-  for (int i = 0; i < kBinsPerThread; ++i) c[i] = 0;
-  uint32_t n_events = 0;
-  for (int p = 0; p < a.P; ++p) {
-    const uint32_t* rec = hs + static_cast<int64_t>(p) * kPartWords;
-#pragma unroll
-    for (int i = 0; i < kBinsPerThread / 8; ++i) {
-      const uint4 v = reinterpret_cast<const uint4*>(rec + dw0)[i];
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        c[8 * i + 2 * k] += w[k] & 0xffffu;
-        c[8 * i + 2 * k + 1] += w[k] >> 16;
-      }
-    }
-    n_events += rec[kPartPacked + kHdrEvents];
-  }
-  if (n_events) {
-    // logged wraps (rare: a pattern past 65535 values in one part)
-    for (int p = 0; p < a.P; ++p) {
-      const uint32_t* rec = hs + static_cast<int64_t>(p) * kPartWords;
-      zero_hist(hist);
-      __syncthreads();
-      add_wraps(c, hist, dw0, rec + kPartPacked + 64, rec[kPartPacked + kHdrEvents]);
-    }
-  }
-  if (neg) {  // pattern order -> key order (uniform per wave)
+__device__ __forceinline__ void to_key_order(uint32_t (&c)[kBinsPerThread], int bin0) {
+  if (bin0 < 0x8000) {  // uniform per wave
 #pragma unroll
     for (int i = 0; i < kBinsPerThread / 2; ++i) {
       const uint32_t t = c[i];
@@ -328,6 +273,21 @@ __global__ __launch_bounds__(kHistThreads) void calib_hist_window_kernel(HistArg
       c[kBinsPerThread - 1 - i] = t;
     }
   }
+}
+
+// The Recall Window of head bh from its counts (thread t: keys [64t, 64t+64) in c, key
+// order).  lds: kCtlWords of scratch, then room for kWinCap distinct values; inc_g: 65536
+// words of global memory for inc[] when the distinct values do not fit in LDS (the caller
+// has read whatever it held).
+__device__ void window_from_counts(uint32_t (&c)[kBinsPerThread], uint32_t* lds, uint32_t* inc_g, const HistArgs& a,
+                                   int64_t bh) {
+  uint32_t* ctl = lds;                                  // [kCtlWords] scan and reduction scratch
+  uint32_t* inc_l = lds + kCtlWords;                    // [kWinCap] inc of each distinct value
+  uint16_t* key_l = reinterpret_cast<uint16_t*>(inc_l + kWinCap);  // [kWinCap] its key
+  const int tid = static_cast<int>(threadIdx.x);
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  const int bin0 = tid * kBinsPerThread;
+  const bool f16 = a.f16 != 0;
 
   uint32_t sum = 0, nz = 0;
 #pragma unroll
@@ -335,9 +295,9 @@ __global__ __launch_bounds__(kHistThreads) void calib_hist_window_kernel(HistArg
     sum += c[i];
     nz += c[i] ? 1u : 0u;
   }
-  uint32_t n_total = 0, distinct = 0;
-  const uint32_t pre0 = block_exclusive_scan(sum, ctl, &n_total);
-  const uint32_t j0 = block_exclusive_scan(nz, ctl, &distinct);
+  uint2 tot;
+  const uint2 pj = block_exclusive_scan2(make_uint2(sum, nz), ctl, &tot);
+  const uint32_t pre0 = pj.x, j0 = pj.y, distinct = tot.y;
   const bool in_lds = distinct <= static_cast<uint32_t>(kWinCap);
 
   uint64_t best = ~uint64_t{0};
@@ -374,27 +334,26 @@ __global__ __launch_bounds__(kHistThreads) void calib_hist_window_kernel(HistArg
       }
     }
   } else {
-    // inc[] over all bins, in place over the head's records (every thread has read its bins
-    // of every part above; the head's region holds at least 65536 words)
+    // inc[] over all bins in global memory (each thread writes its own 64 bins)
     __syncthreads();
     uint32_t run = pre0;
 #pragma unroll
     for (int i = 0; i < kBinsPerThread; ++i) {
       run += c[i];
-      hs[bin0 + i] = run;
+      inc_g[bin0 + i] = run;
     }
     __threadfence();
     __syncthreads();
     uint32_t f = pre0;
     for (int i = 0; i < kBinsPerThread; ++i) {
       const uint32_t kl = static_cast<uint32_t>(bin0 + i);
-      const uint32_t inc_k = __hip_atomic_load(hs + kl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t inc_k = __hip_atomic_load(inc_g + kl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (inc_k > f && f < a.K) {
         const uint32_t r = f + a.t - 1;
         uint32_t lo_i = kl, hi_i = kBins - 1;
         while (lo_i < hi_i) {
           const uint32_t mid = (lo_i + hi_i) >> 1;
-          const uint32_t im = __hip_atomic_load(hs + mid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const uint32_t im = __hip_atomic_load(inc_g + mid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           if (im > r) hi_i = mid; else lo_i = mid + 1;
         }
         const float len = value16(lo_i, f16) - value16(kl, f16);
@@ -414,37 +373,130 @@ __global__ __launch_bounds__(kHistThreads) void calib_hist_window_kernel(HistArg
     const uint64_t u = __shfl_xor(m, o);
     m = u < m ? u : m;
   }
-  uint64_t* wbest = reinterpret_cast<uint64_t*>(ctl);
+  uint64_t* wbest = reinterpret_cast<uint64_t*>(ctl + 32);  // past the scan scratch
   if (lane == 0) wbest[wave] = m;
   __syncthreads();
-  if (tid == 0) {
-    uint64_t g = wbest[0];
-    for (int w = 1; w < kHistThreads / kWave; ++w) g = wbest[w] < g ? wbest[w] : g;
-    ctl[40] = static_cast<uint32_t>(g);
-    ctl[41] = static_cast<uint32_t>(g >> 32);
+  if (wave == 0) {  // the last wave-level step: lane w takes wave w's best
+    uint64_t g = lane < kHistThreads / kWave ? wbest[lane] : ~uint64_t{0};
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) {
+      const uint64_t u = __shfl_xor(g, o);
+      g = u < g ? u : g;
+    }
+    g = __shfl(g, 0);
+    if (lane < kHistThreads / kWave) wbest[lane] = g;  // hand it back to every wave
   }
   __syncthreads();
-  const uint64_t g = (static_cast<uint64_t>(ctl[41]) << 32) | ctl[40];
+  const uint64_t g = wbest[wave];
   if (best == g && g != ~uint64_t{0}) {  // exactly one thread holds the winning candidate
     a.win_min[bh] = value16(best_hi >> 16, f16);
     a.win_max[bh] = value16(best_hi & 0xffffu, f16);
   }
 }
 
+// LDS of the counting kernel (static, so the histogram's address folds into each atomic's
+// offset): the packed counters, the wrap log and its count; with kWhole the same LDS then
+// serves the window search of the head.
+constexpr int kHistSmemWords = std::max<int>(kBins / 2 + kMaxEvents + 16,
+                                             kCtlWords + kWinCap + kWinCap / 2);
+static_assert(static_cast<size_t>(kHistSmemWords) * 4 <= kLdsLimit, "LDS budget");
+
+// kWhole: one part per head (P = 1); the workgroup holds the head's whole histogram and
+// finds the window itself.  Otherwise it writes its part's record for the window kernel.
+template <bool kWhole>
+__global__ __launch_bounds__(kHistThreads) void calib_hist_kernel(HistArgs a) {
+  __shared__ uint32_t smem[kHistSmemWords];
+  uint32_t* hist = smem;               // [32768] two 16-bit counters per dword
+  uint32_t* ev = smem + kBins / 2;     // [kMaxEvents] patterns whose field wrapped
+  uint32_t* nev = ev + kMaxEvents;     // wrap count
+  const int tid = static_cast<int>(threadIdx.x);
+  zero_hist(hist);
+  if (tid == 0) *nev = 0;
+  __syncthreads();
+
+  const int part = static_cast<int>(blockIdx.x) % a.P;
+  const int bh = static_cast<int>(blockIdx.x) / a.P;  // batch * H + head
+  const int h = bh % a.H;
+  const int bi = bh / a.H;
+  const uint4* xb = static_cast<const uint4*>(a.x[bi]);
+
+  int64_t q = static_cast<int64_t>(part) * a.part_vecs;
+  const int64_t q_end = min(q + a.part_vecs, a.Qv);
+  count_range<kHistUnroll>(a, xb, h, q, q_end, hist, ev, nev);
+  __syncthreads();
+
+  if constexpr (kWhole) {
+    const int bin0 = tid * kBinsPerThread;
+    const int dw0 = first_dword(bin0);
+    uint32_t c[kBinsPerThread];
+#pragma unroll
+    for (int i = 0; i < kBinsPerThread; ++i) c[i] = 0;
+    add_packed(c, hist, dw0);
+    const uint32_t ne = *nev;
+    __syncthreads();  // every thread has its counts: the LDS is free again
+    if (ne) {
+      zero_hist(hist);
+      __syncthreads();
+      add_wraps(c, hist, dw0, ev, ne);
+    }
+    to_key_order(c, bin0);
+    window_from_counts(c, smem, a.hist + static_cast<int64_t>(bh) * a.head_words, a, bh);
+  } else {
+    // the part's record: the packed counters, the header and the wrap log
+    uint32_t* out = a.hist + static_cast<int64_t>(bh) * a.head_words + static_cast<int64_t>(part) * kPartWords;
+    for (int i = tid; i < kBins / 8; i += kHistThreads)
+      reinterpret_cast<uint4*>(out)[i] = reinterpret_cast<const uint4*>(hist)[i];
+    const uint32_t ne = *nev;
+    if (tid == 0) out[kPartPacked + kHdrEvents] = ne;
+    for (uint32_t e = tid; e < ne; e += kHistThreads) out[kPartPacked + 64 + e] = ev[e];
+  }
+}
+
+// One workgroup per head after the parts' records are written: their counts summed, the
+// window found from them.
+__global__ __launch_bounds__(kHistThreads) void calib_hist_window_kernel(HistArgs a) {
+  extern __shared__ uint32_t lds[];
+  uint32_t* cnt = lds + kCtlWords;  // packed wrap counts (rare), before the window search
+  const int tid = static_cast<int>(threadIdx.x);
+  const int64_t bh = blockIdx.x;
+  uint32_t* hs = a.hist + bh * a.head_words;
+  const int bin0 = tid * kBinsPerThread;
+  const int dw0 = first_dword(bin0);
+  uint32_t c[kBinsPerThread];
+#pragma unroll
+  for (int i = 0; i < kBinsPerThread; ++i) c[i] = 0;
+  uint32_t n_events = 0;
+  for (int p = 0; p < a.P; ++p) {
+    const uint32_t* rec = hs + static_cast<int64_t>(p) * kPartWords;
+    add_packed(c, rec, dw0);
+    n_events += rec[kPartPacked + kHdrEvents];
+  }
+  if (n_events) {
+    // logged wraps (rare: a pattern past 65535 values in one part)
+    for (int p = 0; p < a.P; ++p) {
+      const uint32_t* rec = hs + static_cast<int64_t>(p) * kPartWords;
+      zero_hist(cnt);
+      __syncthreads();
+      add_wraps(c, cnt, dw0, rec + kPartPacked + 64, rec[kPartPacked + kHdrEvents]);
+    }
+  }
+  to_key_order(c, bin0);
+  window_from_counts(c, lds, hs, a, bh);
+}
+
 }  // namespace
 
-int hist_plan(int64_t B, int64_t H, int64_t S, int64_t D, HistPlan& hp) {
-  if (B <= 0 || H <= 0 || S <= 0 || D <= 0) return FA3Q_ERR_SHAPE;
+int hist_plan(int64_t nb, int64_t B, int64_t H, int64_t S, int64_t D, HistPlan& hp) {
+  if (nb <= 0 || nb > kHistMaxBatches || B <= 0 || H <= 0 || S <= 0 || D <= 0) return FA3Q_ERR_SHAPE;
   const int64_t L = S * D;
   if (L % 8 != 0) return FA3Q_ERR_SHAPE;
   const int64_t N = B * L;
   if (N >= (int64_t{1} << 32)) return FA3Q_ERR_SHAPE;
   hp.Lv = L / 8;
   hp.Qv = B * hp.Lv;
-  // parts per head: one workgroup per CU for a single batch of H heads (the plan does not
-  // depend on the batch count, so every batch has a region of the same size), parts not so
-  // small that their records cost more than their data, and small enough for the event log
-  int64_t P = std::max<int64_t>(1, (256 + H - 1) / H);
+  // parts per head: at least one workgroup per CU over the nb batches' heads, parts not so
+  // small that their records cost more than their data, and small enough for the wrap log
+  int64_t P = std::max<int64_t>(1, (256 + nb * H - 1) / (nb * H));
   P = std::min<int64_t>(P, std::max<int64_t>(1, N / kMinPartValues));
   P = std::max<int64_t>(P, (N + kMaxPartValues - 1) / kMaxPartValues);
   P = std::min<int64_t>(P, hp.Qv);
@@ -475,10 +527,15 @@ int hist_launch(const void* const* xs, int64_t nb, int64_t H, bool f16, int64_t 
   ha.win_min = win_min;
   ha.win_max = win_max;
   ha.f16 = f16 ? 1 : 0;
-  hipLaunchKernelGGL(calib_hist_kernel, dim3(static_cast<unsigned>(nb * H * hp.P)), dim3(kHistThreads), 0,
-                     stream, ha);
-  hipLaunchKernelGGL(calib_hist_window_kernel, dim3(static_cast<unsigned>(nb * H)), dim3(kHistThreads), kWinLds,
-                     stream, ha);
+  if (hp.P == 1) {  // each head counted by one workgroup, which also finds its window
+    hipLaunchKernelGGL(calib_hist_kernel<true>, dim3(static_cast<unsigned>(nb * H)), dim3(kHistThreads), 0, stream,
+                       ha);
+  } else {
+    hipLaunchKernelGGL(calib_hist_kernel<false>, dim3(static_cast<unsigned>(nb * H * hp.P)), dim3(kHistThreads), 0,
+                       stream, ha);
+    hipLaunchKernelGGL(calib_hist_window_kernel, dim3(static_cast<unsigned>(nb * H)), dim3(kHistThreads), kWinLds,
+                       stream, ha);
+  }
   return launch_status();
 }
 

@@ -18,9 +18,9 @@ struct HistPlan {
   size_t bytes = 0;       // workspace per batch: H regions of head_words uint32
 };
 
-// Plan for batches of (B, H, S, D) 16-bit values; S*D must be a multiple of 8 and
+// Plan for nb batches of (B, H, S, D) 16-bit values; S*D must be a multiple of 8 and
 // N = B*S*D below 2^32.  Batch b uses the workspace bytes [b*bytes, (b+1)*bytes).
-int hist_plan(int64_t B, int64_t H, int64_t S, int64_t D, HistPlan& hp);
+int hist_plan(int64_t nb, int64_t B, int64_t H, int64_t S, int64_t D, HistPlan& hp);
 
 // Windows of nb (<= kHistMaxBatches) batches into win_min/win_max [nb][H]; f16: float16
 // input, else bf16; t = int(ratio*N), K = N - t + 1.

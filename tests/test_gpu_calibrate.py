@@ -96,6 +96,19 @@ def test_k4196_long_context_shape(fa):
     _check(fa, x, (0.999, 0.99999), "k4196")
 
 
+def test_k4196_on_the_tail_lists(fa):
+    # K = 4196 on heads of 786,432 values (below 2^20: the tail lists, estimated bound and
+    # side merge), the long-context window count
+    B, H, S, D = 2, 2, 4096, 96
+    N = B * S * D
+    ratio = (N - 4196 + 1 + 0.5) / N
+    assert N - int(ratio * N) + 1 == 4196
+    sigma = synth.head_sigmas(H, seed=61)
+    x = synth.activations((B, H, S, D), sigma, law="t3", outlier_frac=1e-4, outlier_mult=60.0,
+                          dtype=torch.bfloat16, seed=62)
+    _check(fa, x, (ratio,), "k4196_tail")
+
+
 def test_batches_accumulate_and_scale(fa):
     dev = torch.device("cuda:0")
     H = 6
@@ -174,7 +187,7 @@ def test_tails_across_many_binades(fa):
     # the counting sort takes, so the side merge sorts them bitonically; narrow tails (the
     # other cases) take the counting sort
     rng = np.random.default_rng(37)
-    B, H, S, D = 1, 2, 8192, 128
+    B, H, S, D = 1, 2, 8192, 112  # below 2^20 values per head: the tail lists
     mag = np.exp2(rng.uniform(-60.0, 60.0, size=(B, H, S, D)))
     x = (np.where(rng.random((B, H, S, D)) < 0.5, -1.0, 1.0) * mag).astype(np.float32)
     xt = torch.from_numpy(x).to(torch.bfloat16)
@@ -214,7 +227,7 @@ def test_large_first_tokens_do_not_defeat_the_estimated_bound(fa):
     # have): 4 slabs, so runs at multiples of 1/32 of the head would all start on a slab
     # start and sample every one of them; the run phases keep the sample representative,
     # the estimated bound holds and no head takes the fix-up pass
-    B, H, S, D = 4, 2, 8192, 128
+    B, H, S, D = 4, 2, 2048, 112  # below 2^20 values per head: the tail lists
     rng = np.random.default_rng(41)
     x = rng.standard_t(3, size=(B, H, S, D)).astype(np.float32)
     x[:, :, :4, :] = np.where(rng.random((B, H, 4, D)) < 0.5, -30.0, 30.0)
@@ -224,12 +237,13 @@ def test_large_first_tokens_do_not_defeat_the_estimated_bound(fa):
 
 
 def test_estimated_bound_that_fails_is_redone_exactly(fa):
-    # K = 10487 against 2048 sampled groups: the head bound is an estimate, checked by the
+    # K = 9177 against 2048 sampled groups: the head bound is an estimate, checked by the
     # merge.  Values placed where the evenly spaced sample reads (runs of 256 vectors every
     # Q/32 vectors; a group is a thread's vectors of four consecutive runs) give every group
     # an extreme, so the sample bounds tightly while the head holds only 2048 values beyond
-    # the bound: the check fails and the head is redone without a bound.
-    B, H, S, D = 1, 2, 8192, 128
+    # the bound: the check fails and the head is redone without a bound.  (Heads below 2^20
+    # values: the tail lists.)
+    B, H, S, D = 1, 2, 8192, 112
     vec = 8                                   # bf16 values per 16-byte vector
     q_vecs = B * S * D // vec                 # vectors per head
     rng = np.random.default_rng(23)
@@ -313,10 +327,11 @@ def test_batches_equal_per_batch_calls_at_the_calibration_workload(fa):
 
 
 def test_batches_with_an_estimated_bound_that_fails_in_one_batch(fa):
-    # K = 10487 (estimated bounds): batch 1 plants the sampled-position extremes that make
+    # K = 9177 (estimated bounds): batch 1 plants the sampled-position extremes that make
     # its check fail; batches 0 and 2 are ordinary.  Each batch has its own flags and lists.
+    # (Heads below 2^20 values: the tail lists.)
     dev = torch.device("cuda:0")
-    B, H, S, D = 1, 2, 8192, 128
+    B, H, S, D = 1, 2, 8192, 112
     vec, q_vecs = 8, B * S * D // 8
     rng = np.random.default_rng(29)
     xs = []

@@ -73,3 +73,12 @@ def oracle_windows(x: torch.Tensor, ratio: float, heads=None):
     with ThreadPoolExecutor(max_workers=host_threads()) as ex:
         list(ex.map(one, range(len(heads))))
     return lo, hi
+
+
+def parallel(fn, items):
+    """fn over items on a thread pool of the host's cores (the oracle's numpy work runs outside
+    the GIL); results in item order."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    with ThreadPoolExecutor(max_workers=host_threads()) as ex:
+        return list(ex.map(fn, items))

@@ -24,7 +24,9 @@ Parity pins: every function here is pinned by ``tests/test_oracle_*.py``
 against brute force, closed forms, special cases, invariants or library
 routines; none is "parity unpinned".
 """
-from .floats import bf16_bits_to_f32, bf16_bits_to_f64, f32_to_bf16_bits_rne, total_order_key, key_to_f32
+from .floats import (bf16_bits_to_f32, bf16_bits_to_f64, bits16_to_f32, bits16_to_f64, f16_bits_to_f32, f16_bits_to_f64,
+                     f32_to_bf16_bits_rne, key_to_f32, total_order_key)
+from .layout import LAYOUTS, from_bhsd, to_bhsd
 from .recall_window import (
     per_head_view,
     target_num,
@@ -42,6 +44,13 @@ from .asym import params_to_f32, quantize_asym, dequantize_asym
 __all__ = [
     "bf16_bits_to_f32",
     "bf16_bits_to_f64",
+    "f16_bits_to_f32",
+    "f16_bits_to_f64",
+    "bits16_to_f32",
+    "bits16_to_f64",
+    "LAYOUTS",
+    "to_bhsd",
+    "from_bhsd",
     "f32_to_bf16_bits_rne",
     "total_order_key",
     "key_to_f32",

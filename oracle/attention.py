@@ -18,7 +18,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from .floats import bf16_bits_to_f64
+from .floats import bf16_bits_to_f64, bits16_to_f64
+from .layout import from_bhsd, to_bhsd
 from .quant import dequantize_k_nope, quantize_k
 
 
@@ -37,20 +38,24 @@ def attention_fp64(q, k, v, sm_scale: float) -> np.ndarray:
     return np.einsum("bht,bhtd->bhd", weights, v)
 
 
-def decode_attn(q_bits, codes, scale, rope_bits, v_bits, sm_scale: float) -> np.ndarray:
-    """Attention of bf16 ``q (B,H,Dn+Dr)`` over the INT8 K-nope + bf16 K-rope cache.
+def decode_attn(q_bits, codes, scale, rope_bits, v_bits, sm_scale: float, dtype: str = "bf16",
+                layout: str = "BHSD") -> np.ndarray:
+    """Attention of ``q (B,H,Dn+Dr)`` over the INT8 K-nope + 16-bit K-rope cache.
 
     ``codes (B,H,T,Dn) int8``, ``scale [H] float32``, ``rope_bits (B,H,T,Dr)`` and
-    ``v_bits (B,H,T,Dv)`` bf16 patterns.  Returns float64 ``(B,H,Dv)``.
+    ``v_bits (B,H,T,Dv)``; q, K-rope and V are raw patterns of ``dtype`` ("bf16" or
+    "f16").  With ``layout="BSHD"`` the three caches are ``(B,T,H,.)`` (reading L4 of
+    ``oracle.layout``).  Returns float64 ``(B,H,Dv)``.
     """
+    codes, rope_bits, v_bits = from_bhsd(codes, layout), from_bhsd(rope_bits, layout), from_bhsd(v_bits, layout)
     k_nope = dequantize_k_nope(codes, scale)
-    k_rope = bf16_bits_to_f64(rope_bits)
+    k_rope = bits16_to_f64(rope_bits, dtype)
     k = np.concatenate([k_nope, k_rope], axis=-1)
-    return attention_fp64(bf16_bits_to_f64(q_bits), k, bf16_bits_to_f64(v_bits), float(np.float32(sm_scale)))
+    return attention_fp64(bits16_to_f64(q_bits, dtype), k, bits16_to_f64(v_bits, dtype), float(np.float32(sm_scale)))
 
 
 def decode_append_attn(q_bits, k_new_bits, v_new_bits, scale, codes, rope_bits, v_bits, kv_len,
-                       sm_scale: float, Dn: int):
+                       sm_scale: float, Dn: int, dtype: str = "bf16", layout: str = "BHSD"):
     """One decode step on a cache of capacity ``T`` with ragged lengths.
 
     Readings: A5 sequence ``b`` holds ``kv_len[b]`` cached
@@ -62,9 +67,18 @@ def decode_append_attn(q_bits, k_new_bits, v_new_bits, scale, codes, rope_bits, 
     attends to positions ``0 .. p`` (the new token included).  Without a new
     token the query attends to ``0 .. kv_len[b]-1``.
 
+    q, the new token and the cache's K-rope and V are raw patterns of ``dtype`` ("bf16" or
+    "f16"); with ``layout="BSHD"`` the caches are ``(B,T,H,.)`` (reading L4 of
+    ``oracle.layout``) and are returned in that layout.
+
     Returns ``(out (B,H,Dv) float64, codes, rope_bits, v_bits)`` with the
     cache arrays after the step (copies; the inputs are not modified).
     """
+    if layout != "BHSD":
+        out, c, r, v = decode_append_attn(q_bits, k_new_bits, v_new_bits, scale, to_bhsd(codes, layout),
+                                          to_bhsd(rope_bits, layout), to_bhsd(v_bits, layout), kv_len, sm_scale, Dn,
+                                          dtype)
+        return out, from_bhsd(c, layout), from_bhsd(r, layout), from_bhsd(v, layout)
     codes = np.array(codes, dtype=np.int8, copy=True)
     rope_bits = np.array(rope_bits, dtype=np.uint16, copy=True)
     v_bits = np.array(v_bits, dtype=np.uint16, copy=True)
@@ -77,7 +91,8 @@ def decode_append_attn(q_bits, k_new_bits, v_new_bits, scale, codes, rope_bits, 
         if k_new_bits is not None:
             if not 0 <= p < T:
                 raise ValueError("appending needs 0 <= kv_len[b] < T")
-            new_codes, new_rope = quantize_k(np.asarray(k_new_bits, dtype=np.uint16)[b][None, :, None, :], scale, Dn)
+            new_codes, new_rope = quantize_k(np.asarray(k_new_bits, dtype=np.uint16)[b][None, :, None, :], scale, Dn,
+                                             dtype)
             codes[b, :, p, :] = new_codes[0, :, 0, :]
             rope_bits[b, :, p, :] = new_rope[0, :, 0, :]
             v_bits[b, :, p, :] = np.asarray(v_new_bits, dtype=np.uint16)[b]
@@ -87,7 +102,7 @@ def decode_append_attn(q_bits, k_new_bits, v_new_bits, scale, codes, rope_bits, 
                 raise ValueError("attention needs 1 <= kv_len[b] <= T")
             n = p
         out[b] = decode_attn(np.asarray(q_bits)[b:b + 1], codes[b:b + 1, :, :n], scale, rope_bits[b:b + 1, :, :n],
-                             v_bits[b:b + 1, :, :n], sm_scale)[0]
+                             v_bits[b:b + 1, :, :n], sm_scale, dtype)[0]
     return out, codes, rope_bits, v_bits
 
 

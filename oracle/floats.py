@@ -44,3 +44,37 @@ def key_to_f32(k) -> np.ndarray:
     from_negative = (k >> np.uint32(31)) == np.uint32(0)
     b = np.where(from_negative, ~k, k & np.uint32(0x7FFFFFFF)).astype(np.uint32)
     return b.view(np.float32)
+
+
+def f16_bits_to_f32(bits) -> np.ndarray:
+    """Exact float32 value of IEEE binary16 patterns, from the format's definition:
+    sign s, 5-bit exponent e (bias 15), 10-bit fraction f; e = 0 is the subnormal range
+    (-1)^s 2^-14 (f / 1024), e = 31 infinities and NaNs, otherwise (-1)^s 2^(e-15) (1 + f / 1024).
+    Every binary16 value is exact in float32."""
+    b = np.asarray(bits)
+    b = b.view(np.uint16) if b.dtype == np.int16 else b.astype(np.uint16)
+    s = (b >> np.uint16(15)).astype(np.int64)
+    e = ((b >> np.uint16(10)) & np.uint16(0x1F)).astype(np.int64)
+    f = (b & np.uint16(0x3FF)).astype(np.float64)
+    mag = np.where(e == 0, np.ldexp(f, -24), np.ldexp(1024.0 + f, (e - 25).astype(np.int32)))
+    mag = np.where(e == 31, np.where(f == 0, np.inf, np.nan), mag)
+    return np.where(s == 1, -mag, mag).astype(np.float32)
+
+
+def f16_bits_to_f64(bits) -> np.ndarray:
+    """Exact float64 value of IEEE binary16 patterns."""
+    return f16_bits_to_f32(bits).astype(np.float64)
+
+
+def bits16_to_f32(bits, dtype: str = "bf16") -> np.ndarray:
+    """Exact float32 value of 16-bit patterns of ``dtype`` ("bf16" or "f16")."""
+    if dtype == "bf16":
+        return bf16_bits_to_f32(bits)
+    if dtype == "f16":
+        return f16_bits_to_f32(bits)
+    raise ValueError(f"unknown 16-bit dtype {dtype!r}")
+
+
+def bits16_to_f64(bits, dtype: str = "bf16") -> np.ndarray:
+    """Exact float64 value of 16-bit patterns of ``dtype`` ("bf16" or "f16")."""
+    return bits16_to_f32(bits, dtype).astype(np.float64)

@@ -30,21 +30,27 @@ from typing import Tuple
 
 import numpy as np
 
-from .floats import bf16_bits_to_f32, f32_to_bf16_bits_rne
+from .floats import bf16_bits_to_f32, bits16_to_f32, f32_to_bf16_bits_rne
+from .layout import from_bhsd, to_bhsd
 
 
-def quantize_k(k_bits, scale, Dn: int) -> Tuple[np.ndarray, np.ndarray]:
-    """Split a bf16 K tensor ``(B, H, S, Dn + Dr)`` into INT8 K-nope codes and bf16 K-rope.
+def quantize_k(k_bits, scale, Dn: int, dtype: str = "bf16", layout: str = "BHSD") -> Tuple[np.ndarray, np.ndarray]:
+    """Split a 16-bit K tensor ``(B, H, S, Dn + Dr)`` into INT8 K-nope codes and K-rope.
 
-    ``k_bits`` holds raw bf16 patterns; ``scale`` is float32 ``[H]``.  Returns
-    ``(codes (B,H,S,Dn) int8, rope (B,H,S,Dr) uint16 patterns)``.
+    ``k_bits`` holds raw patterns of ``dtype`` ("bf16" or "f16"; Q2 takes their exact
+    float32 value); ``scale`` is float32 ``[H]``.  Returns ``(codes (B,H,S,Dn) int8,
+    rope (B,H,S,Dr) uint16 patterns)``, both in ``layout`` (for ``"BSHD"`` the input and
+    outputs are ``(B, S, H, .)``, reading L4 of ``oracle.layout``).
     """
     k_bits = np.asarray(k_bits).view(np.uint16) if np.asarray(k_bits).dtype == np.int16 else np.asarray(k_bits, dtype=np.uint16)
     if k_bits.ndim != 4:
         raise ValueError("k must be (B, H, S, Dn + Dr)")
+    if layout != "BHSD":
+        codes, rope = quantize_k(to_bhsd(k_bits, layout), scale, Dn, dtype)
+        return from_bhsd(codes, layout), from_bhsd(rope, layout)
     H = k_bits.shape[1]
     scale = np.asarray(scale, dtype=np.float32).reshape(H)
-    x = bf16_bits_to_f32(k_bits[..., :Dn])
+    x = bits16_to_f32(k_bits[..., :Dn], dtype)
     s = scale.reshape(1, H, 1, 1)
     with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
         quotient = (x / s).astype(np.float32)          # Q2: float32 division

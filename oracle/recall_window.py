@@ -42,6 +42,7 @@ from typing import Tuple
 import numpy as np
 
 from .floats import key_to_f32, total_order_key
+from .layout import to_bhsd
 
 DEFAULT_RATIO = 0.9999  # default ratio given for the Recall Window step
 
@@ -93,9 +94,12 @@ def recall_window(head_data, ratio: float = DEFAULT_RATIO) -> Tuple[np.float32, 
     return window_min[best], window_max[best]
 
 
-def calibrate(x, ratio: float = DEFAULT_RATIO) -> Tuple[np.ndarray, np.ndarray]:
-    """One calibration batch: the Recall Window of every head -> ``(min[H], max[H])``."""
-    heads = per_head_view(np.asarray(x, dtype=np.float32))
+def calibrate(x, ratio: float = DEFAULT_RATIO, layout: str = "BHSD") -> Tuple[np.ndarray, np.ndarray]:
+    """One calibration batch: the Recall Window of every head -> ``(min[H], max[H])``.
+
+    ``x`` holds float32 values in ``layout`` (``"BHSD"``, or ``"BSHD"`` read as in
+    ``oracle.layout``, reading L4)."""
+    heads = per_head_view(to_bhsd(np.asarray(x, dtype=np.float32), layout))
     H = heads.shape[0]
     lo = np.empty(H, dtype=np.float32)
     hi = np.empty(H, dtype=np.float32)

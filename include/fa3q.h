@@ -26,6 +26,9 @@
  *      table per sequence
  *  14. fa3q_decode_attn_noalloc -- 5 with the library's own static scratch instead of a
  *      caller workspace (for callers that cannot allocate device memory)
+ *  15. fa3q_calibrate_ex, fa3q_quantize_k_ex, fa3q_decode_attn_ex, fa3q_decode_append_attn_ex
+ *      -- 10, 4, 5 and 6 with a dtype (bf16 or float16 activations, K-rope and V) and a
+ *      layout ((B,H,S,D) or (B,S,H,D)) argument
  *
  * Sources, cited by page title and section:
  *   [MS] msModelSlim documentation, "FA3量化：Flash Attention 3激活量化算法说明"
@@ -75,19 +78,31 @@ typedef enum fa3q_status {
   FA3Q_ERR_HIP = 7,         /* the HIP runtime rejected a launch */
   FA3Q_ERR_UNSUPPORTED = 8, /* valid arguments outside what this build handles (see each call) */
   FA3Q_ERR_ALIAS = 9,       /* an output partly overlaps an input (where exact aliasing is allowed) */
-  FA3Q_ERR_SCRATCH = 10     /* the call needs more scratch than the library's static array holds */
+  FA3Q_ERR_SCRATCH = 10,    /* the call needs more scratch than the library's static array holds */
+  FA3Q_ERR_LAYOUT = 11      /* unknown layout code */
 } fa3q_status;
 
 typedef enum fa3q_dtype {
   FA3Q_F32 = 0,  /* IEEE binary32 */
   FA3Q_BF16 = 1, /* bfloat16, raw 16-bit patterns */
-  FA3Q_F16 = 2   /* IEEE binary16, raw 16-bit patterns (asymmetric parameter tables only) */
+  FA3Q_F16 = 2   /* IEEE binary16, raw 16-bit patterns */
 } fa3q_dtype;
 
 /*
- * Signatures take and return plain `int` for statuses and dtype codes: the values are
- * those of fa3q_status and fa3q_dtype, but C leaves the integer type behind an enum to
- * the compiler, while `int` has one fixed width for every caller (ctypes, other FFIs).
+ * Memory order of a 4-D activation or cache tensor (row-major in the order named):
+ * (batch, head, token, dim) with each head's tokens contiguous, or (batch, token, head, dim)
+ * with each token's heads contiguous.  Calls without a layout argument take FA3Q_BHSD.
+ */
+typedef enum fa3q_layout {
+  FA3Q_BHSD = 0,
+  FA3Q_BSHD = 1
+} fa3q_layout;
+
+/*
+ * Signatures take and return plain `int` for statuses, dtype and layout codes: the values
+ * are those of fa3q_status, fa3q_dtype and fa3q_layout, but C leaves the integer type
+ * behind an enum to the compiler, while `int` has one fixed width for every caller
+ * (ctypes, other FFIs).
  */
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -102,10 +117,10 @@ int fa3q_version(void);
 
 /*
  * Largest number of windows K = N - int(ratio*N) + 1 that the streaming tail selection
- * (on-chip lists of the K smallest and K largest values) takes for `dtype`.  bf16 input
- * with a larger K, or with heads of at least 2^20 values, takes the histogram path, which
- * handles every K; float32 input with a larger K returns FA3Q_ERR_UNSUPPORTED.  0 for an
- * unknown dtype.
+ * (on-chip lists of the K smallest and K largest values) takes for `dtype`.  16-bit input
+ * (bf16, float16) with a larger K, with heads of at least 2^20 values or in the FA3Q_BSHD
+ * layout takes the histogram path, which handles every K; float32 input with a larger K
+ * returns FA3Q_ERR_UNSUPPORTED.  0 for an unknown dtype.
  */
 int64_t fa3q_calibrate_max_windows(int dtype);
 
@@ -127,8 +142,9 @@ size_t fa3q_calibrate_workspace_bytes(int dtype, int64_t B, int64_t H, int64_t S
  * ties.  Writes win_min[h] = s[i*] and win_max[h] = s[i*+t-1] (float32 values
  * of the input; exact, no rounding).
  *
- *   x          device, dtype FA3Q_F32 or FA3Q_BF16, (B,H,S,D) contiguous, 16-byte aligned.
- *   B,H,S,D    > 0; S*D must be a multiple of 8 (bf16) or 4 (f32); N = B*S*D < 2^32.
+ *   x          device, dtype FA3Q_F32, FA3Q_BF16 or FA3Q_F16, (B,H,S,D) contiguous,
+ *              16-byte aligned.
+ *   B,H,S,D    > 0; S*D must be a multiple of 8 (16-bit dtypes) or 4 (f32); N = B*S*D < 2^32.
  *   ratio      in (0, 1]; t = int(ratio*N) must be >= 1.
  *   win_min,
  *   win_max    device float32 [H], 4-byte aligned.
@@ -136,7 +152,7 @@ size_t fa3q_calibrate_workspace_bytes(int dtype, int64_t B, int64_t H, int64_t S
  *
  * No sort: one pass over x.  Only the K = N-t+1 smallest and K largest values of a
  * head can bound a window; while K <= fa3q_calibrate_max_windows(dtype) and a head holds
- * fewer than 2^20 values, the kernels select those two tails on chip.  A bf16 head is
+ * fewer than 2^20 values, the kernels select those two tails on chip.  A 16-bit head is
  * otherwise counted into a 65536-bin histogram (its sorted order exactly) and the window
  * found from the counts, for every K.  float32 input with K above
  * fa3q_calibrate_max_windows(FA3Q_F32) -> FA3Q_ERR_UNSUPPORTED.
@@ -516,6 +532,77 @@ int fa3q_decode_attn_noalloc(const uint16_t* q, const int8_t* k_nope_q, const fl
                              const uint16_t* k_rope, const uint16_t* v, int64_t B, int64_t H,
                              int64_t T, int64_t Dn, int64_t Dr, int64_t Dv, float sm_scale,
                              float* out, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* 15. float16 input and (B,S,H,D) layouts                                   */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * [MT] tables 1 and 2 list float16 as well as bfloat16 variants of attention quantisation,
+ * and [MI] overview places the quantised K cache in the decode-phase KV cache, whose
+ * serving layouts keep either each head's tokens or each token's heads contiguous.  These
+ * entry points are 10, 4, 5 and 6 with the activation dtype and the tensor layout as
+ * arguments; every result is that of the (B,H,S,D) call on the tensors re-laid out, bit for
+ * bit where 4, 5, 6 and 10 are exact, and the same float32 arithmetic otherwise.
+ *
+ *   dtype   FA3Q_BF16 or FA3Q_F16 for every 16-bit tensor of the call (activations, K,
+ *           K-rope, q, V, k_new, v_new; calibration also takes FA3Q_F32); else
+ *           FA3Q_ERR_DTYPE.  Codes stay int8, scales and outputs float32.
+ *   layout  FA3Q_BHSD or FA3Q_BSHD for every 4-D tensor of the call (activations x, K, the
+ *           codes, K-rope and V of the cache); else FA3Q_ERR_LAYOUT.  Tensors of one token
+ *           per (b, h) -- q, k_new, v_new, out -- are (B,H,.) in both layouts.
+ */
+
+/* Workspace of fa3q_calibrate_ex (0 when the arguments are invalid, nb outside 1..16 included). */
+size_t fa3q_calibrate_ex_workspace_bytes(int dtype, int layout, int64_t nb, int64_t B, int64_t H,
+                                         int64_t S, int64_t D, double ratio);
+
+/*
+ * fa3q_calibrate_batches with a layout: head h of batch b gathers x[b][:, h, :, :] (BHSD)
+ * or x[b][:, :, h, :] (BSHD), N = B*S*D values, and the windows and running statistics
+ * follow.  run_min and run_max may both be NULL when win_min and win_max are given: the
+ * windows are then written and no running statistics kept (fa3q_calibrate_perhead for
+ * nb = 1).  BSHD rows of D values must be a multiple of 8 (16-bit) values; (B,S,H,D)
+ * 16-bit input always takes the histogram path (any K), float32 BSHD input returns
+ * FA3Q_ERR_UNSUPPORTED.  Other arguments, alignment and errors as fa3q_calibrate_batches.
+ */
+int fa3q_calibrate_ex(const void* const* xs, int64_t nb, int dtype, int layout, int64_t B, int64_t H,
+                      int64_t S, int64_t D, double ratio, float* run_min, float* run_max, int init,
+                      float* win_min, float* win_max, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/*
+ * fa3q_quantize_k with a dtype and a layout: k is (B,H,S,Dn+Dr) or (B,S,H,Dn+Dr) of dtype,
+ * k_nope_q and k_rope have k's layout (rows of Dn int8 codes and Dr values of dtype), and
+ * row (b, h, s) is quantised with scale[h] exactly as fa3q_quantize_k does (the quotient of
+ * the float32 value of the float16 or bf16 input).  Sizes, alignment and errors as
+ * fa3q_quantize_k.
+ */
+int fa3q_quantize_k_ex(const void* k, const float* scale, int8_t* k_nope_q, void* k_rope, int dtype,
+                       int layout, int64_t B, int64_t H, int64_t S, int64_t Dn, int64_t Dr,
+                       void* stream);
+
+/*
+ * fa3q_decode_attn with a dtype and a layout: q (B,H,Dn+Dr), k_rope and v of dtype; the
+ * cache tensors k_nope_q, k_rope and v are (B,H,T,.) or (B,T,H,.).  Workspace query,
+ * sizes, alignment and errors as fa3q_decode_attn.
+ */
+int fa3q_decode_attn_ex(const void* q, const int8_t* k_nope_q, const float* scale, const void* k_rope,
+                        const void* v, int dtype, int layout, int64_t B, int64_t H, int64_t T,
+                        int64_t Dn, int64_t Dr, int64_t Dv, float sm_scale, float* out,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa3q_decode_append_attn with a dtype and a layout: q, k_new (B,H,Dn+Dr) and v_new
+ * (B,H,Dv) of dtype; the cache (capacity T) in the layout, written in place at token
+ * kv_len[b] when appending (the new K-nope row quantised as fa3q_quantize_k_ex would).
+ * Other arguments and errors as fa3q_decode_append_attn.
+ */
+int fa3q_decode_append_attn_ex(const void* q, const void* k_new, const void* v_new, const float* scale,
+                               int8_t* k_nope_q, void* k_rope, void* v, const int32_t* kv_len,
+                               int dtype, int layout, int64_t B, int64_t H, int64_t T, int64_t Dn,
+                               int64_t Dr, int64_t Dv, float sm_scale, float* out, void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

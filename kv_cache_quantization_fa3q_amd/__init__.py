@@ -6,6 +6,8 @@ its calls.  Build the library with ``python -m kv_cache_quantization_fa3q_amd.bu
 """
 from ._lib import (  # noqa: F401
     FA3Q_BF16,
+    FA3Q_BHSD,
+    FA3Q_BSHD,
     FA3Q_F16,
     FA3Q_F32,
     FA3Q_OK,
@@ -17,14 +19,19 @@ from ._lib import (  # noqa: F401
 )
 from .ops import (  # noqa: F401
     dtype_code,
+    layout_code,
     fa3q_accumulate_minmax,
     fa3q_calibrate_batches,
     fa3q_calibrate_batches_workspace_bytes,
+    fa3q_calibrate_ex,
+    fa3q_calibrate_ex_workspace_bytes,
     fa3q_calibrate_max_windows,
     fa3q_calibrate_perhead,
     fa3q_calibrate_workspace_bytes,
     fa3q_decode_append_attn,
+    fa3q_decode_append_attn_ex,
     fa3q_decode_attn,
+    fa3q_decode_attn_ex,
     fa3q_decode_attn_noalloc,
     fa3q_decode_attn_asym,
     fa3q_decode_attn_qkv8,
@@ -37,4 +44,5 @@ from .ops import (  # noqa: F401
     fa3q_qparams,
     fa3q_quantize_asym,
     fa3q_quantize_k,
+    fa3q_quantize_k_ex,
 )

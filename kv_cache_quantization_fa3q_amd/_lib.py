@@ -27,12 +27,16 @@ FA3Q_ERR_HIP = 7
 FA3Q_ERR_UNSUPPORTED = 8
 FA3Q_ERR_ALIAS = 9
 FA3Q_ERR_SCRATCH = 10
+FA3Q_ERR_LAYOUT = 11
 
 FA3Q_NOALLOC_SCRATCH_BYTES = 16 << 20  # include/fa3q.h
 
 FA3Q_F32 = 0
 FA3Q_BF16 = 1
 FA3Q_F16 = 2
+
+FA3Q_BHSD = 0
+FA3Q_BSHD = 1
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -71,6 +75,14 @@ SIGNATURES = {
                                   _vp]),
     "fa3q_decode_attn_noalloc": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_float,
                                         _vp, _vp]),
+    "fa3q_calibrate_ex_workspace_bytes": (_sz, [_int, _int, _i64, _i64, _i64, _i64, _i64, ctypes.c_double]),
+    "fa3q_calibrate_ex": (_int, [ctypes.POINTER(_vp), _i64, _int, _int, _i64, _i64, _i64, _i64, ctypes.c_double, _vp,
+                                 _vp, _int, _vp, _vp, _vp, _sz, _vp]),
+    "fa3q_quantize_k_ex": (_int, [_vp, _vp, _vp, _vp, _int, _int, _i64, _i64, _i64, _i64, _i64, _vp]),
+    "fa3q_decode_attn_ex": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _i64, _i64, _i64, _i64, _i64, _i64,
+                                   ctypes.c_float, _vp, _vp, _sz, _vp]),
+    "fa3q_decode_append_attn_ex": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _int, _i64, _i64, _i64, _i64,
+                                          _i64, _i64, ctypes.c_float, _vp, _vp, _sz, _vp]),
 }
 
 _lock = threading.Lock()

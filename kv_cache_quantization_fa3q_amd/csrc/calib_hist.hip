@@ -70,9 +70,11 @@ static_assert(kWinLds >= kCtlWords * 4 + kBins * 2, "the window kernel counts wr
 struct HistArgs {
   const void* x[kHistMaxBatches];
   uint32_t* hist;        // [nb][H] regions of head_words: P part records each
-  int64_t Lv;            // 16-byte vectors per (b, h) slab
-  int64_t Qv;            // vectors per head: B * Lv
+  int64_t Lv;            // 16-byte vectors per row (row j of head h at vector (j*H + h)*Lv)
+  int64_t nrows;         // rows per head
+  int64_t Qv;            // vectors per head: nrows * Lv
   int64_t part_vecs;     // vectors per part (the last part may be shorter)
+  int64_t part_rows;     // rows per part (kRows kernels)
   int64_t head_words;    // workspace words per head: P part records, at least 65536
   int32_t H;
   int32_t P;
@@ -149,13 +151,13 @@ __device__ __forceinline__ void count_vecs(uint32_t* hist, uint32_t* ev, uint32_
 }
 
 // Streams head vectors [q0, q1) of head h in batch xb into the LDS histogram, U vectors per
-// thread in flight.
+// thread in flight, one row segment at a time (rows longer than a round of the workgroup).
 template <int U>
 __device__ __forceinline__ void count_range(const HistArgs& a, const uint4* xb, int h, int64_t q, int64_t q_end,
                                             uint32_t* hist, uint32_t* ev, uint32_t* nev) {
   const int tid = static_cast<int>(threadIdx.x);
   constexpr int64_t kRound = static_cast<int64_t>(kHistThreads) * U;
-  while (q < q_end) {  // one (b, h) slab segment at a time
+  while (q < q_end) {
     const int64_t b = q / a.Lv;
     const int64_t w = q - b * a.Lv;
     const int64_t n = min(q_end - q, a.Lv - w);
@@ -183,6 +185,50 @@ __device__ __forceinline__ void count_range(const HistArgs& a, const uint4* xb, 
       count_vecs<U, false>(hist, ev, nev, v, valid);
     }
     q += n;
+  }
+}
+
+// Streams rows [j0, j1) of head h in batch xb (rows of Lv <= kHistThreads vectors, as the
+// (b, s) rows of D values of a (B, S, H, D) tensor) into the LDS histogram.  The workgroup
+// takes G = kHistThreads / Lv rows per step, thread t vector t % Lv of row t / Lv (threads
+// past G * Lv idle), so a thread's vectors lie a fixed stride apart and need no division;
+// U steps in flight.
+template <int U>
+__device__ __forceinline__ void count_rows(const HistArgs& a, const uint4* xb, int h, int64_t j0, int64_t j1,
+                                           uint32_t* hist, uint32_t* ev, uint32_t* nev) {
+  const int tid = static_cast<int>(threadIdx.x);
+  const int R = static_cast<int>(a.Lv);
+  const int G = kHistThreads / R;
+  const int rt = tid / R;
+  const int wt = tid - rt * R;
+  const bool on = rt < G;
+  const int64_t nrows = j1 - j0;
+  const int64_t stride = static_cast<int64_t>(G) * a.H * R;  // vectors from one step to the next
+  const uint4* first = xb + (j0 * a.H + h) * R + wt;          // row j0: in every part
+  const uint4* mine = xb + ((j0 + rt) * a.H + h) * R + wt;    // dereferenced only for rows < j1
+  const int64_t full = nrows / G;                              // steps whose G rows all exist
+  int64_t g = 0;
+  if (G * R == kHistThreads) {
+    for (; g + U <= full; g += U) {
+      uint4 v[U];
+      bool valid[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        valid[u] = true;
+        v[u] = load_nt16(mine + (g + u) * stride);
+      }
+      count_vecs<U, true>(hist, ev, nev, v, valid);
+    }
+  }
+  for (; g * G < nrows; g += U) {
+    uint4 v[U];
+    bool valid[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      valid[u] = on && (g + u) * G + rt < nrows;
+      v[u] = load_nt16(valid[u] ? mine + (g + u) * stride : first);  // a vector not counted is re-read from row j0
+    }
+    count_vecs<U, false>(hist, ev, nev, v, valid);
   }
 }
 
@@ -403,7 +449,8 @@ static_assert(static_cast<size_t>(kHistSmemWords) * 4 <= kLdsLimit, "LDS budget"
 
 // kWhole: one part per head (P = 1); the workgroup holds the head's whole histogram and
 // finds the window itself.  Otherwise it writes its part's record for the window kernel.
-template <bool kWhole>
+// kRows: rows of at most kHistThreads vectors, parts of whole rows (count_rows).
+template <bool kWhole, bool kRows>
 __global__ __launch_bounds__(kHistThreads) void calib_hist_kernel(HistArgs a) {
   __shared__ uint32_t smem[kHistSmemWords];
   uint32_t* hist = smem;               // [32768] two 16-bit counters per dword
@@ -420,9 +467,13 @@ __global__ __launch_bounds__(kHistThreads) void calib_hist_kernel(HistArgs a) {
   const int bi = bh / a.H;
   const uint4* xb = static_cast<const uint4*>(a.x[bi]);
 
-  int64_t q = static_cast<int64_t>(part) * a.part_vecs;
-  const int64_t q_end = min(q + a.part_vecs, a.Qv);
-  count_range<kHistUnroll>(a, xb, h, q, q_end, hist, ev, nev);
+  if constexpr (kRows) {
+    const int64_t j0 = static_cast<int64_t>(part) * a.part_rows;
+    count_rows<kHistUnroll>(a, xb, h, j0, min(j0 + a.part_rows, a.nrows), hist, ev, nev);
+  } else {
+    const int64_t q = static_cast<int64_t>(part) * a.part_vecs;
+    count_range<kHistUnroll>(a, xb, h, q, min(q + a.part_vecs, a.Qv), hist, ev, nev);
+  }
   __syncthreads();
 
   if constexpr (kWhole) {
@@ -486,22 +537,39 @@ __global__ __launch_bounds__(kHistThreads) void calib_hist_window_kernel(HistArg
 
 }  // namespace
 
-int hist_plan(int64_t nb, int64_t B, int64_t H, int64_t S, int64_t D, HistPlan& hp) {
+int hist_plan(int64_t nb, bool bshd, int64_t B, int64_t H, int64_t S, int64_t D, HistPlan& hp) {
   if (nb <= 0 || nb > kHistMaxBatches || B <= 0 || H <= 0 || S <= 0 || D <= 0) return FA3Q_ERR_SHAPE;
-  const int64_t L = S * D;
-  if (L % 8 != 0) return FA3Q_ERR_SHAPE;
-  const int64_t N = B * L;
+  const int64_t row = bshd ? D : S * D;
+  if (row % 8 != 0) return FA3Q_ERR_SHAPE;
+  const int64_t N = B * S * D;
   if (N >= (int64_t{1} << 32)) return FA3Q_ERR_SHAPE;
-  hp.Lv = L / 8;
-  hp.Qv = B * hp.Lv;
+  hp.Lv = row / 8;
+  hp.nrows = bshd ? B * S : B;
+  hp.Qv = hp.nrows * hp.Lv;
+  hp.rows = hp.Lv <= kHistThreads;
   // parts per head: at least one workgroup per CU over the nb batches' heads, parts not so
   // small that their records cost more than their data, and small enough for the wrap log
   int64_t P = std::max<int64_t>(1, (256 + nb * H - 1) / (nb * H));
   P = std::min<int64_t>(P, std::max<int64_t>(1, N / kMinPartValues));
   P = std::max<int64_t>(P, (N + kMaxPartValues - 1) / kMaxPartValues);
-  P = std::min<int64_t>(P, hp.Qv);
-  hp.part_vecs = (hp.Qv + P - 1) / P;
-  hp.P = (hp.Qv + hp.part_vecs - 1) / hp.part_vecs;
+  if (hp.rows) {
+    // parts of whole rows; a row holds at most 8 * kHistThreads values, so the wrap log's
+    // bound is kept by adding parts
+    P = std::min<int64_t>(P, hp.nrows);
+    int64_t per = (hp.nrows + P - 1) / P;
+    while (per > 1 && per * hp.Lv * 8 > kMaxPartValues) {
+      ++P;
+      per = (hp.nrows + P - 1) / P;
+    }
+    hp.part_rows = per;
+    hp.part_vecs = per * hp.Lv;
+    hp.P = (hp.nrows + per - 1) / per;
+  } else {
+    P = std::min<int64_t>(P, hp.Qv);
+    hp.part_rows = 0;
+    hp.part_vecs = (hp.Qv + P - 1) / P;
+    hp.P = (hp.Qv + hp.part_vecs - 1) / hp.part_vecs;
+  }
   if (hp.part_vecs * 8 > kMaxPartValues) return FA3Q_ERR_SHAPE;
   if (kHistMaxBatches * H * hp.P > (int64_t{1} << 31) - 1) return FA3Q_ERR_SHAPE;
   hp.head_words = std::max<int64_t>(hp.P * kPartWords, kBins);
@@ -517,8 +585,10 @@ int hist_launch(const void* const* xs, int64_t nb, int64_t H, bool f16, int64_t 
   for (int b = 0; b < kHistMaxBatches; ++b) ha.x[b] = b < nb ? xs[b] : nullptr;
   ha.hist = static_cast<uint32_t*>(workspace);
   ha.Lv = hp.Lv;
+  ha.nrows = hp.nrows;
   ha.Qv = hp.Qv;
   ha.part_vecs = hp.part_vecs;
+  ha.part_rows = hp.part_rows;
   ha.head_words = hp.head_words;
   ha.H = static_cast<int32_t>(H);
   ha.P = static_cast<int32_t>(hp.P);
@@ -527,14 +597,20 @@ int hist_launch(const void* const* xs, int64_t nb, int64_t H, bool f16, int64_t 
   ha.win_min = win_min;
   ha.win_max = win_max;
   ha.f16 = f16 ? 1 : 0;
+  const dim3 blk(kHistThreads);
   if (hp.P == 1) {  // each head counted by one workgroup, which also finds its window
-    hipLaunchKernelGGL(calib_hist_kernel<true>, dim3(static_cast<unsigned>(nb * H)), dim3(kHistThreads), 0, stream,
-                       ha);
+    const dim3 g(static_cast<unsigned>(nb * H));
+    if (hp.rows)
+      hipLaunchKernelGGL((calib_hist_kernel<true, true>), g, blk, 0, stream, ha);
+    else
+      hipLaunchKernelGGL((calib_hist_kernel<true, false>), g, blk, 0, stream, ha);
   } else {
-    hipLaunchKernelGGL(calib_hist_kernel<false>, dim3(static_cast<unsigned>(nb * H * hp.P)), dim3(kHistThreads), 0,
-                       stream, ha);
-    hipLaunchKernelGGL(calib_hist_window_kernel, dim3(static_cast<unsigned>(nb * H)), dim3(kHistThreads), kWinLds,
-                       stream, ha);
+    const dim3 g(static_cast<unsigned>(nb * H * hp.P));
+    if (hp.rows)
+      hipLaunchKernelGGL((calib_hist_kernel<false, true>), g, blk, 0, stream, ha);
+    else
+      hipLaunchKernelGGL((calib_hist_kernel<false, false>), g, blk, 0, stream, ha);
+    hipLaunchKernelGGL(calib_hist_window_kernel, dim3(static_cast<unsigned>(nb * H)), blk, kWinLds, stream, ha);
   }
   return launch_status();
 }

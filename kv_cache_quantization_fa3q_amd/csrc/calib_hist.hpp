@@ -10,17 +10,21 @@ namespace fa3q {
 constexpr int kHistMaxBatches = 16;
 
 struct HistPlan {
-  int64_t Lv = 0;         // 16-byte vectors per (b, h) slab
+  int64_t Lv = 0;         // 16-byte vectors per row: a (b, h) slab of S*D values, or (BSHD) D values
+  int64_t nrows = 0;      // rows per head: B, or (BSHD) B*S; row j of head h starts at vector (j*H + h)*Lv
   int64_t Qv = 0;         // vectors per head
-  int64_t part_vecs = 0;  // vectors per part
+  bool rows = false;      // rows of at most one vector per thread: parts are whole rows
+  int64_t part_vecs = 0;  // vectors per part (whole rows when rows is set)
+  int64_t part_rows = 0;  // rows per part when rows is set
   int64_t P = 0;          // parts per head
   int64_t head_words = 0; // workspace words per head: P part records, at least 65536
   size_t bytes = 0;       // workspace per batch: H regions of head_words uint32
 };
 
-// Plan for nb batches of (B, H, S, D) 16-bit values; S*D must be a multiple of 8 and
-// N = B*S*D below 2^32.  Batch b uses the workspace bytes [b*bytes, (b+1)*bytes).
-int hist_plan(int64_t nb, int64_t B, int64_t H, int64_t S, int64_t D, HistPlan& hp);
+// Plan for nb batches of (B, H, S, D), or with bshd (B, S, H, D), 16-bit values; a row
+// (S*D, or D values) must be a multiple of 8 values and N = B*S*D below 2^32.  Batch b uses
+// the workspace bytes [b*bytes, (b+1)*bytes).
+int hist_plan(int64_t nb, bool bshd, int64_t B, int64_t H, int64_t S, int64_t D, HistPlan& hp);
 
 // Windows of nb (<= kHistMaxBatches) batches into win_min/win_max [nb][H]; f16: float16
 // input, else bf16; t = int(ratio*N), K = N - t + 1.

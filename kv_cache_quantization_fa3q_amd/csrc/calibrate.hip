@@ -153,7 +153,7 @@ template <typename InT>
 struct In;
 
 template <>
-struct In<uint16_t> {  // bf16 patterns, two per dword
+struct In<uint16_t> {  // bf16 or float16 patterns (same sign-magnitude order), two per dword
   using KeyT = uint16_t;
   using Lim = int32_t;
   static constexpr int kPerDword = 2;
@@ -202,11 +202,12 @@ struct In<uint32_t> {  // float32 patterns, one per dword
   __device__ static Lim slane_max(uint32_t p) { return static_cast<Lim>(static_cast<int32_t>(p)); }
 };
 
-__device__ __forceinline__ float value_of_key(uint32_t k, uint16_t) {
+// Value of a key: 16-bit keys hold bf16 or (f16) float16 patterns, 32-bit keys float32 ones.
+__device__ __forceinline__ float value_of_key(uint32_t k, uint16_t, bool f16) {
   const uint32_t b = (k & 0x8000u) ? (k ^ 0x8000u) : (k ^ 0xffffu);
-  return __uint_as_float(b << 16);
+  return f16 ? static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(b))) : __uint_as_float(b << 16);
 }
-__device__ __forceinline__ float value_of_key(uint32_t k, uint32_t) {
+__device__ __forceinline__ float value_of_key(uint32_t k, uint32_t, bool) {
   const uint32_t b = (k & 0x80000000u) ? (k ^ 0x80000000u) : ~k;
   return __uint_as_float(b);
 }
@@ -779,6 +780,7 @@ struct MergeArgs {
   uint32_t K;
   uint32_t cap;
   uint32_t P;  // next power of two >= K
+  int32_t f16;  // 16-bit keys: 1 float16 patterns, 0 bf16
 };
 
 constexpr int kMaxPrefixLists = 2048;  // list counts the side merge keeps as an LDS prefix
@@ -1155,7 +1157,7 @@ __global__ __launch_bounds__(256) void calib_window_kernel(MergeArgs a, Batches 
   float bl = __uint_as_float(0x7f800000u);
   uint32_t bi = 0xffffffffu;
   for (uint32_t i = static_cast<uint32_t>(tid); i < K; i += NT) {
-    const float len = value_of_key(kMax - hic[K - 1 - i], KeyT{}) - value_of_key(lo[i], KeyT{});
+    const float len = value_of_key(kMax - hic[K - 1 - i], KeyT{}, a.f16 != 0) - value_of_key(lo[i], KeyT{}, a.f16 != 0);
     if (len < bl || bi == 0xffffffffu) {
       bl = len;
       bi = i;
@@ -1183,8 +1185,8 @@ __global__ __launch_bounds__(256) void calib_window_kernel(MergeArgs a, Batches 
         bi = wi[w];
       }
     }
-    a.win_min[h] = value_of_key(lo[bi], KeyT{});
-    a.win_max[h] = value_of_key(kMax - hic[K - 1 - bi], KeyT{});
+    a.win_min[h] = value_of_key(lo[bi], KeyT{}, a.f16 != 0);
+    a.win_max[h] = value_of_key(kMax - hic[K - 1 - bi], KeyT{}, a.f16 != 0);
   }
 }
 
@@ -1308,7 +1310,8 @@ __global__ __launch_bounds__(kWaveMergeThreads) void calib_merge_wave_kernel(Mer
   float bl = __uint_as_float(0x7f800000u);
   uint32_t bi = 0xffffffffu;
   for (uint32_t i = static_cast<uint32_t>(tid); i < K; i += kWaveMergeThreads) {
-    const float len = value_of_key(sorted[1][K - 1 - i] ^ kMax, KeyT{}) - value_of_key(sorted[0][i], KeyT{});
+    const float len =
+        value_of_key(sorted[1][K - 1 - i] ^ kMax, KeyT{}, a.f16 != 0) - value_of_key(sorted[0][i], KeyT{}, a.f16 != 0);
     if (len < bl || bi == 0xffffffffu) {
       bl = len;
       bi = i;
@@ -1336,8 +1339,8 @@ __global__ __launch_bounds__(kWaveMergeThreads) void calib_merge_wave_kernel(Mer
       bl = best_l[0];
       bi = best_at[0];
     }
-    a.win_min[h] = value_of_key(sorted[0][bi], KeyT{});
-    a.win_max[h] = value_of_key(sorted[1][K - 1 - bi] ^ kMax, KeyT{});
+    a.win_min[h] = value_of_key(sorted[0][bi], KeyT{}, a.f16 != 0);
+    a.win_max[h] = value_of_key(sorted[1][K - 1 - bi] ^ kMax, KeyT{}, a.f16 != 0);
   }
 }
 
@@ -1357,7 +1360,8 @@ struct CalibPlan {
   bool estimate = false; // rank < K: the bound is checked by the merge, failures redone
   // workspace per batch: lists | counts | sorted | bounds | fail
   size_t lists_bytes = 0, counts_bytes = 0, sorted_bytes = 0, bounds_bytes = 0, fail_bytes = 0, total_bytes = 0;
-  bool hist = false;     // K past the on-chip tail lists: the histogram path (16-bit keys)
+  bool hist = false;     // the histogram path (16-bit keys)
+  bool f16 = false;      // 16-bit keys are float16 patterns (else bf16)
   HistPlan hp;
 };
 
@@ -1369,13 +1373,17 @@ int64_t next_pow2(int64_t v) {
 
 // Validates everything except pointers and computes the launch plan.  The plan depends
 // only on the arguments (not on the device), so the workspace query is reproducible.
-int make_plan(int dtype, int64_t nb, int64_t B, int64_t H, int64_t S, int64_t D, double ratio, CalibPlan& p) {
-  if (dtype != FA3Q_F32 && dtype != FA3Q_BF16) return FA3Q_ERR_DTYPE;
+int make_plan(int dtype, int layout, int64_t nb, int64_t B, int64_t H, int64_t S, int64_t D, double ratio,
+              CalibPlan& p) {
+  if (dtype != FA3Q_F32 && dtype != FA3Q_BF16 && dtype != FA3Q_F16) return FA3Q_ERR_DTYPE;
+  if (layout != FA3Q_BHSD && layout != FA3Q_BSHD) return FA3Q_ERR_LAYOUT;
   if (B <= 0 || H <= 0 || S <= 0 || D <= 0) return FA3Q_ERR_SHAPE;
-  const int vec = dtype == FA3Q_BF16 ? 8 : 4;
+  const bool k16 = dtype != FA3Q_F32;
+  const int vec = k16 ? 8 : 4;
   if (S > (int64_t{1} << 40) / D) return FA3Q_ERR_SHAPE;
   p.L = S * D;
-  if (p.L % vec != 0) return FA3Q_ERR_SHAPE;
+  // 16-byte vectors never straddle a head's rows: (b, h) slabs of S*D values, or (BSHD) rows of D
+  if ((layout == FA3Q_BHSD ? p.L : D) % vec != 0) return FA3Q_ERR_SHAPE;
   if (B > (int64_t{1} << 40) / p.L || B * H > (int64_t{1} << 31)) return FA3Q_ERR_SHAPE;
   if (B * H > (int64_t{1} << 50) / p.L) return FA3Q_ERR_SHAPE;
   p.N = B * p.L;
@@ -1384,12 +1392,13 @@ int make_plan(int dtype, int64_t nb, int64_t B, int64_t H, int64_t S, int64_t D,
   p.t = static_cast<int64_t>(ratio * static_cast<double>(p.N));  // truncation toward zero
   if (p.t < 1) return FA3Q_ERR_RATIO;
   p.K = p.N - p.t + 1;
-  if (p.K > fa3q_calibrate_max_windows(dtype) || (dtype != FA3Q_F32 && p.N >= kHistMinValues)) {
-    if (dtype == FA3Q_F32) return FA3Q_ERR_UNSUPPORTED;
-    // 16-bit keys: the whole head as one histogram, any K
+  p.f16 = dtype == FA3Q_F16;
+  if (p.K > fa3q_calibrate_max_windows(dtype) || layout == FA3Q_BSHD || (k16 && p.N >= kHistMinValues)) {
+    if (!k16) return FA3Q_ERR_UNSUPPORTED;
+    // 16-bit keys: the whole head as one histogram, any K and either layout
     p.hist = true;
     p.key_bytes = 2;
-    const int st = hist_plan(nb, B, H, S, D, p.hp);
+    const int st = hist_plan(nb, layout == FA3Q_BSHD, B, H, S, D, p.hp);
     if (st != FA3Q_OK) return st;
     p.total_bytes = p.hp.bytes;
     return FA3Q_OK;
@@ -1434,9 +1443,9 @@ int make_plan(int dtype, int64_t nb, int64_t B, int64_t H, int64_t S, int64_t D,
                (4 * r_est <= p.K || static_cast<int64_t>(p.sample_m) < p.K);  // 4: measured (K = 211 gains, K = 43 would lose)
   p.rank = static_cast<uint32_t>(p.estimate ? r_est : p.K);
 
-  p.key_bytes = dtype == FA3Q_BF16 ? 2 : 4;
-  const int64_t tile = dtype == FA3Q_BF16 ? chunk_tile<uint16_t>() : chunk_tile<uint32_t>();
-  const int64_t room = dtype == FA3Q_BF16 ? chunk_room<uint16_t>() : chunk_room<uint32_t>();
+  p.key_bytes = k16 ? 2 : 4;
+  const int64_t tile = k16 ? chunk_tile<uint16_t>() : chunk_tile<uint32_t>();
+  const int64_t room = k16 ? chunk_room<uint16_t>() : chunk_room<uint32_t>();
   const size_t tmp_keys = static_cast<size_t>(p.K);
   p.cap_chunk = static_cast<uint32_t>(2 * p.K + room);
   if (p.estimate) {
@@ -1582,6 +1591,7 @@ int launch(const void* const* x, int64_t nb, int64_t H, const CalibPlan& p, floa
   ma.K = static_cast<uint32_t>(p.K);
   ma.cap = p.cap_merge;
   ma.P = p.P;
+  ma.f16 = p.f16 ? 1 : 0;
   auto merge = [&](const MergeArgs& m) {
     if (p.wave_merge_e > 0)
       launch_wave_merge<KeyT, kWaveMergeRegs>(p.wave_merge_e, nb * H, m, bt, stream);
@@ -1643,9 +1653,9 @@ extern "C" int64_t fa3q_calibrate_max_windows(int dtype) {
   // its control block and a list-count prefix of up to kMaxPrefixLists + 1 words, then the
   // counting-sort bins for 16-bit keys.  Largest K for which both fit the 160 KiB a gfx950
   // workgroup may use.
-  if (dtype != FA3Q_F32 && dtype != FA3Q_BF16) return 0;
-  const int64_t kb = dtype == FA3Q_BF16 ? 2 : 4;
-  const int64_t round = dtype == FA3Q_BF16 ? chunk_room<uint16_t>() : chunk_room<uint32_t>();
+  if (dtype != FA3Q_F32 && dtype != FA3Q_BF16 && dtype != FA3Q_F16) return 0;
+  const int64_t kb = dtype == FA3Q_F32 ? 4 : 2;
+  const int64_t round = kb == 2 ? chunk_room<uint16_t>() : chunk_room<uint32_t>();
   const int64_t lds = static_cast<int64_t>(kLdsLimit);
   const int64_t chunk = (lds - static_cast<int64_t>(kCtlBytes + kStageBytes) - 2 * round * kb) / (5 * kb);
   const int64_t pre = static_cast<int64_t>(round_up(static_cast<size_t>(kMaxPrefixLists + 1) * 4, 16));
@@ -1654,10 +1664,64 @@ extern "C" int64_t fa3q_calibrate_max_windows(int dtype) {
   return std::min(chunk, merge);
 }
 
+namespace fa3q {
+namespace {
+
+// Windows of nb batches into win_min/win_max [nb][H] on the path the plan chose.
+int launch_windows(const void* const* xs, int64_t nb, int64_t H, const CalibPlan& p, float* win_min, float* win_max,
+                   void* workspace, hipStream_t s) {
+  if (p.hist) return hist_launch(xs, nb, H, p.f16, p.t, p.K, p.hp, win_min, win_max, workspace, s);
+  if (p.key_bytes == 2) return launch<uint16_t>(xs, nb, H, p, win_min, win_max, workspace, s);
+  return launch<uint32_t>(xs, nb, H, p, win_min, win_max, workspace, s);
+}
+
+size_t batches_workspace_bytes(int dtype, int layout, int64_t nb, int64_t B, int64_t H, int64_t S, int64_t D,
+                               double ratio) {
+  CalibPlan p;
+  if (nb <= 0 || nb > kMaxBatches || make_plan(dtype, layout, nb, B, H, S, D, ratio, p) != FA3Q_OK) return 0;
+  if (!p.hist && nb * B * H * p.nch > (int64_t{1} << 31) - 1) return 0;
+  return static_cast<size_t>(nb) * p.total_bytes + round_up(2 * static_cast<size_t>(nb * H) * sizeof(float), 256);
+}
+
+// Validation and launches of the several-batch entry points: run_min/run_max may both be
+// null when win_min/win_max are given (windows only, no running statistics).
+int calibrate_batches(const void* const* xs, int64_t nb, int dtype, int layout, int64_t B, int64_t H, int64_t S,
+                      int64_t D, double ratio, float* run_min, float* run_max, int init, float* win_min,
+                      float* win_max, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!xs || (!run_min != !run_max) || (!win_min != !win_max) || (!run_min && !win_min)) return FA3Q_ERR_NULL;
+  if (nb <= 0 || nb > kMaxBatches) return FA3Q_ERR_SHAPE;
+  for (int64_t b = 0; b < nb; ++b)
+    if (!xs[b]) return FA3Q_ERR_NULL;
+  CalibPlan p;
+  const int st = make_plan(dtype, layout, nb, B, H, S, D, ratio, p);
+  if (st != FA3Q_OK) return st;
+  if (!p.hist && nb * H * p.nch > (int64_t{1} << 31) - 1) return FA3Q_ERR_SHAPE;
+  for (int64_t b = 0; b < nb; ++b)
+    if (!is_aligned(xs[b], 16)) return FA3Q_ERR_ALIGN;
+  if ((run_min && (!is_aligned(run_min, 4) || !is_aligned(run_max, 4))) ||
+      (win_min && (!is_aligned(win_min, 4) || !is_aligned(win_max, 4))))
+    return FA3Q_ERR_ALIGN;
+  const size_t need = batches_workspace_bytes(dtype, layout, nb, B, H, S, D, ratio);
+  if (!workspace || workspace_bytes < need) return FA3Q_ERR_WORKSPACE;
+  if (!is_aligned(workspace, 256)) return FA3Q_ERR_ALIGN;
+  float* wins = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + static_cast<size_t>(nb) * p.total_bytes);
+  float* wmin = win_min ? win_min : wins;
+  float* wmax = win_max ? win_max : wins + nb * H;
+  hipStream_t s = as_stream(stream);
+  const int lst = launch_windows(xs, nb, H, p, wmin, wmax, workspace, s);
+  if (lst != FA3Q_OK || !run_min) return lst;
+  hipLaunchKernelGGL(accumulate_batches_kernel, dim3(static_cast<unsigned>((H + 255) / 256)), dim3(256), 0, s, run_min,
+                     run_max, wmin, wmax, nb, H, init ? 1 : 0);
+  return launch_status();
+}
+
+}  // namespace
+}  // namespace fa3q
+
 extern "C" size_t fa3q_calibrate_workspace_bytes(int dtype, int64_t B, int64_t H, int64_t S,
                                                  int64_t D, double ratio) {
   CalibPlan p;
-  if (make_plan(dtype, 1, B, H, S, D, ratio, p) != FA3Q_OK) return 0;
+  if (make_plan(dtype, FA3Q_BHSD, 1, B, H, S, D, ratio, p) != FA3Q_OK) return 0;
   return p.total_bytes;
 }
 
@@ -1666,56 +1730,39 @@ extern "C" int fa3q_calibrate_perhead(const void* x, int dtype, int64_t B, int64
                                       void* workspace, size_t workspace_bytes, void* stream) {
   if (!x || !win_min || !win_max) return FA3Q_ERR_NULL;
   CalibPlan p;
-  const int st = make_plan(dtype, 1, B, H, S, D, ratio, p);
+  const int st = make_plan(dtype, FA3Q_BHSD, 1, B, H, S, D, ratio, p);
   if (st != FA3Q_OK) return st;
   if (!is_aligned(x, 16) || !is_aligned(win_min, 4) || !is_aligned(win_max, 4))
     return FA3Q_ERR_ALIGN;
   if (!workspace || workspace_bytes < p.total_bytes) return FA3Q_ERR_WORKSPACE;
   if (!is_aligned(workspace, 256)) return FA3Q_ERR_ALIGN;
   const void* xs[1] = {x};
-  if (p.hist)
-    return hist_launch(xs, 1, H, false, p.t, p.K, p.hp, win_min, win_max, workspace, as_stream(stream));
-  if (dtype == FA3Q_BF16)
-    return launch<uint16_t>(xs, 1, H, p, win_min, win_max, workspace, as_stream(stream));
-  return launch<uint32_t>(xs, 1, H, p, win_min, win_max, workspace, as_stream(stream));
+  return launch_windows(xs, 1, H, p, win_min, win_max, workspace, as_stream(stream));
 }
 
 extern "C" size_t fa3q_calibrate_batches_workspace_bytes(int dtype, int64_t nb, int64_t B, int64_t H, int64_t S,
                                                          int64_t D, double ratio) {
-  CalibPlan p;
-  if (nb <= 0 || nb > kMaxBatches || make_plan(dtype, nb, B, H, S, D, ratio, p) != FA3Q_OK) return 0;
-  if (!p.hist && nb * B * H * p.nch > (int64_t{1} << 31) - 1) return 0;
-  return static_cast<size_t>(nb) * p.total_bytes + round_up(2 * static_cast<size_t>(nb * H) * sizeof(float), 256);
+  return batches_workspace_bytes(dtype, FA3Q_BHSD, nb, B, H, S, D, ratio);
 }
 
 extern "C" int fa3q_calibrate_batches(const void* const* xs, int64_t nb, int dtype, int64_t B, int64_t H, int64_t S,
                                       int64_t D, double ratio, float* run_min, float* run_max, int init,
                                       float* win_min, float* win_max, void* workspace, size_t workspace_bytes,
                                       void* stream) {
-  if (!xs || !run_min || !run_max || (!win_min != !win_max)) return FA3Q_ERR_NULL;
-  if (nb <= 0 || nb > kMaxBatches) return FA3Q_ERR_SHAPE;
-  for (int64_t b = 0; b < nb; ++b)
-    if (!xs[b]) return FA3Q_ERR_NULL;
-  CalibPlan p;
-  const int st = make_plan(dtype, nb, B, H, S, D, ratio, p);
-  if (st != FA3Q_OK) return st;
-  if (!p.hist && nb * H * p.nch > (int64_t{1} << 31) - 1) return FA3Q_ERR_SHAPE;
-  for (int64_t b = 0; b < nb; ++b)
-    if (!is_aligned(xs[b], 16)) return FA3Q_ERR_ALIGN;
-  if (!is_aligned(run_min, 4) || !is_aligned(run_max, 4) || (win_min && (!is_aligned(win_min, 4) || !is_aligned(win_max, 4))))
-    return FA3Q_ERR_ALIGN;
-  const size_t need = fa3q_calibrate_batches_workspace_bytes(dtype, nb, B, H, S, D, ratio);
-  if (!workspace || workspace_bytes < need) return FA3Q_ERR_WORKSPACE;
-  if (!is_aligned(workspace, 256)) return FA3Q_ERR_ALIGN;
-  float* wins = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + static_cast<size_t>(nb) * p.total_bytes);
-  float* wmin = win_min ? win_min : wins;
-  float* wmax = win_max ? win_max : wins + nb * H;
-  hipStream_t s = as_stream(stream);
-  const int lst = p.hist ? hist_launch(xs, nb, H, false, p.t, p.K, p.hp, wmin, wmax, workspace, s)
-                  : dtype == FA3Q_BF16 ? launch<uint16_t>(xs, nb, H, p, wmin, wmax, workspace, s)
-                                       : launch<uint32_t>(xs, nb, H, p, wmin, wmax, workspace, s);
-  if (lst != FA3Q_OK) return lst;
-  hipLaunchKernelGGL(accumulate_batches_kernel, dim3(static_cast<unsigned>((H + 255) / 256)), dim3(256), 0, s, run_min,
-                     run_max, wmin, wmax, nb, H, init ? 1 : 0);
-  return launch_status();
+  if (!run_min || !run_max) return FA3Q_ERR_NULL;
+  return calibrate_batches(xs, nb, dtype, FA3Q_BHSD, B, H, S, D, ratio, run_min, run_max, init, win_min, win_max,
+                           workspace, workspace_bytes, stream);
+}
+
+extern "C" size_t fa3q_calibrate_ex_workspace_bytes(int dtype, int layout, int64_t nb, int64_t B, int64_t H,
+                                                    int64_t S, int64_t D, double ratio) {
+  return batches_workspace_bytes(dtype, layout, nb, B, H, S, D, ratio);
+}
+
+extern "C" int fa3q_calibrate_ex(const void* const* xs, int64_t nb, int dtype, int layout, int64_t B, int64_t H,
+                                 int64_t S, int64_t D, double ratio, float* run_min, float* run_max, int init,
+                                 float* win_min, float* win_max, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  return calibrate_batches(xs, nb, dtype, layout, B, H, S, D, ratio, run_min, run_max, init, win_min, win_max,
+                           workspace, workspace_bytes, stream);
 }

@@ -88,6 +88,8 @@ struct DecodeArgs {
   int32_t params_f16;           // 1: the tables are float16, 0: bfloat16
   float* ws_ml;  // [B*H*nsplit][2] (max, sum)
   float* ws_o;   // [B*H*nsplit][Dv]
+  int64_t hs;    // cache rows from one head to the next: T (B,H,T,.) or 1 (B,T,H,.)
+  int64_t ts;    // cache rows from one token to the next: 1 (B,H,T,.) or H (B,T,H,.)
   int64_t T;
   int32_t H;
   int32_t Dn;
@@ -121,16 +123,18 @@ __device__ __forceinline__ float dot16_i8(const float (&qn)[16], float qsum, uin
   return fmaf(-128.0f, qsum, acc);
 }
 
-__device__ __forceinline__ float dot8_bf16(const float (&qr)[8], uint4 w) {
+// <q_rope, k_rope> over 8 bf16 (or, kF16, float16) values held in a uint4.
+template <bool kF16>
+__device__ __forceinline__ float dot8_16(const float (&qr)[8], uint4 w) {
   float acc = 0.0f;
-  acc = fmaf(qr[0], bf16_lo(w.x), acc);
-  acc = fmaf(qr[1], bf16_hi(w.x), acc);
-  acc = fmaf(qr[2], bf16_lo(w.y), acc);
-  acc = fmaf(qr[3], bf16_hi(w.y), acc);
-  acc = fmaf(qr[4], bf16_lo(w.z), acc);
-  acc = fmaf(qr[5], bf16_hi(w.z), acc);
-  acc = fmaf(qr[6], bf16_lo(w.w), acc);
-  acc = fmaf(qr[7], bf16_hi(w.w), acc);
+  acc = fmaf(qr[0], lo16<kF16>(w.x), acc);
+  acc = fmaf(qr[1], hi16<kF16>(w.x), acc);
+  acc = fmaf(qr[2], lo16<kF16>(w.y), acc);
+  acc = fmaf(qr[3], hi16<kF16>(w.y), acc);
+  acc = fmaf(qr[4], lo16<kF16>(w.z), acc);
+  acc = fmaf(qr[5], hi16<kF16>(w.z), acc);
+  acc = fmaf(qr[6], lo16<kF16>(w.w), acc);
+  acc = fmaf(qr[7], hi16<kF16>(w.w), acc);
   return acc;
 }
 
@@ -141,10 +145,12 @@ __device__ __forceinline__ uint4 load_nt(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// 4 bf16 values (two dwords) -> 4 INT8 codes in one dword, little-endian element order:
-// clamp(round_half_even(fl32(x / s)), -127, 127) with the IEEE quotient; 0 when s == 0.
+// 4 bf16 (kF16: float16) values (two dwords) -> 4 INT8 codes in one dword, little-endian
+// element order: clamp(round_half_even(fl32(x / s)), -127, 127) with the IEEE quotient; 0
+// when s == 0.
+template <bool kF16>
 __device__ __forceinline__ uint32_t quant4_exact(uint32_t w0, uint32_t w1, float s) {
-  const float xv[4] = {bf16_lo(w0), bf16_hi(w0), bf16_lo(w1), bf16_hi(w1)};
+  const float xv[4] = {lo16<kF16>(w0), hi16<kF16>(w0), lo16<kF16>(w1), hi16<kF16>(w1)};
   uint32_t o = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -162,9 +168,10 @@ __device__ __forceinline__ float param_f32(uint16_t bits, bool f16) {
 constexpr int kFmtBf16 = 0;  // bf16 query and values, per-head symmetric K-nope codes
 constexpr int kFmtQkv8 = 1;  // INT8 query (non-RoPE part) and values; LV is then Dv/16
 constexpr int kFmtAsym = 2;  // bf16 query and values, per-(head, dim) asymmetric K-nope codes
+constexpr int kFmtF16 = 3;   // float16 query and values, per-head symmetric K-nope codes
 
 constexpr int kVarFixed = 0;  // every sequence holds T tokens at (b, h, t)
-constexpr int kVarRagged = 1; // kv_len[] tokens, optional append, contiguous (B,H,T,.) cache
+constexpr int kVarRagged = 1; // kv_len[] tokens, optional append, contiguous (B,H,T,.) or (B,T,H,.) cache
 constexpr int kVarPaged = 2;  // kVarRagged through a block table over (pages,H,P,.) pools
 
 // Pages of one split that a paged kernel stages in LDS: enough for split_len tokens starting
@@ -186,7 +193,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
   constexpr bool kQ8 = kFmt == kFmtQkv8;
   constexpr bool kAsym = kFmt == kFmtAsym;
   constexpr bool kPaged = kVar == kVarPaged;
-  static_assert(!kVar || kFmt == kFmtBf16, "the append step takes the per-head bf16-query cache");
+  constexpr bool kH = kFmt == kFmtF16;  // float16 query, K-rope and V
+  static_assert(!kVar || kFmt == kFmtBf16 || kFmt == kFmtF16, "the append step takes the per-head symmetric cache");
   extern __shared__ float smem[];
   float* sc = smem;                       // [split_len] scores, then probabilities
   float* red = smem + a.split_len;        // [kWaves] block reduction scratch
@@ -242,12 +250,14 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     }
     lds_barrier();
   }
+  // row of the split's first token in a contiguous cache: (b, h, t0) in either layout
+  const int64_t row0 = static_cast<int64_t>(bh / a.H) * a.H * a.T + static_cast<int64_t>(h) * a.hs + t0 * a.ts;
   auto row_of = [&](int tt) -> int64_t {
     if constexpr (kPaged) {
       const int64_t t = t0 + tt;
       return prow[(t >> a.page_shift) - pg0] + (t & pmask);
     } else {
-      return static_cast<int64_t>(bh) * a.T + t0 + tt;
+      return row0 + static_cast<int64_t>(tt) * a.ts;
     }
   };
 
@@ -273,8 +283,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
       const uint32_t w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        qn[2 * i] = bf16_lo(w[i]);
-        qn[2 * i + 1] = bf16_hi(w[i]);
+        qn[2 * i] = lo16<kH>(w[i]);
+        qn[2 * i + 1] = hi16<kH>(w[i]);
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) qsum += qn[i];
@@ -287,8 +297,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
       const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        qr[2 * i] = bf16_lo(w[i]);
-        qr[2 * i + 1] = bf16_hi(w[i]);
+        qr[2 * i] = lo16<kH>(w[i]);
+        qr[2 * i + 1] = hi16<kH>(w[i]);
       }
     } else {
 #pragma unroll
@@ -315,8 +325,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
         }
       }
     }
-    const int8_t* kq = kPaged ? a.kq + 16 * j : a.kq + (static_cast<int64_t>(bh) * a.T + t0) * a.Dn + 16 * j;
-    const uint16_t* kr = kPaged ? a.kr + 8 * j : a.kr + (static_cast<int64_t>(bh) * a.T + t0) * a.Dr + 8 * j;
+    // contiguous caches: the split's first row and the rows' token stride; paged: whole rows
+    const int8_t* kq = a.kq + (kPaged ? 0 : row0 * a.Dn) + 16 * j;
+    const uint16_t* kr = a.kr + (kPaged ? 0 : row0 * a.Dr) + 8 * j;
+    const int64_t kq_tok = a.ts * a.Dn, kr_tok = a.ts * a.Dr;
     const int step = kWaves * kSlots;
     for (int base = wave * kSlots + slot; base < n; base += step * kUk) {
       uint4 wn[kUk], wr[kUk];
@@ -326,9 +338,14 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
         wn[u] = make_uint4(0, 0, 0, 0);
         wr[u] = make_uint4(0, 0, 0, 0);
         if (tt < n) {
-          const int64_t r = kPaged ? row_of(tt) : tt;
-          if (has_n) wn[u] = load_nt(kq + r * a.Dn);
-          if (has_r) wr[u] = load_nt(kr + r * a.Dr);
+          if constexpr (kPaged) {
+            const int64_t r = row_of(tt);
+            if (has_n) wn[u] = load_nt(kq + r * a.Dn);
+            if (has_r) wr[u] = load_nt(kr + r * a.Dr);
+          } else {
+            if (has_n) wn[u] = load_nt(kq + tt * kq_tok);
+            if (has_r) wr[u] = load_nt(kr + tt * kr_tok);
+          }
         }
       }
 #pragma unroll
@@ -348,7 +365,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
             s = head_scale * dot16_i8(qn, qsum, wn[u]);
           }
         }
-        if (has_r) s += dot8_bf16(qr, wr[u]);
+        if (has_r) s += dot8_16<kH>(qr, wr[u]);
         s = group_sum<LK>(s);
         if (j == 0 && tt < n) sc[tt] = s * a.sm_log2;
       }
@@ -362,8 +379,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
         if (has_n) {
           const uint4* p = reinterpret_cast<const uint4*>(knew + 16 * j);
           const uint4 u0 = p[0], u1 = p[1];
-          cn = make_uint4(quant4_exact(u0.x, u0.y, head_scale), quant4_exact(u0.z, u0.w, head_scale),
-                          quant4_exact(u1.x, u1.y, head_scale), quant4_exact(u1.z, u1.w, head_scale));
+          cn = make_uint4(quant4_exact<kH>(u0.x, u0.y, head_scale), quant4_exact<kH>(u0.z, u0.w, head_scale),
+                          quant4_exact<kH>(u1.x, u1.y, head_scale), quant4_exact<kH>(u1.z, u1.w, head_scale));
           if (slot == 0) *reinterpret_cast<uint4*>(const_cast<int8_t*>(a.kq) + at * a.Dn + 16 * j) = cn;
         }
         if (has_r) {
@@ -372,7 +389,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
         }
         float s = 0.0f;
         if (has_n) s = head_scale * dot16_i8(qn, qsum, cn);
-        if (has_r) s += dot8_bf16(qr, rn);
+        if (has_r) s += dot8_16<kH>(qr, rn);
         s = group_sum<LK>(s);
         if (j == 0 && slot == 0) sc[n] = s * a.sm_log2;
       }
@@ -413,10 +430,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
   for (int d = 0; d < kVD; ++d) acc[d] = 0.0f;
   float psum = 0.0f;  // INT8 values: sum of the weights, for the +128 offset of the byte reads
   {
-    const char* vp = kQ8 ? reinterpret_cast<const char*>(a.vq + (static_cast<int64_t>(bh) * a.T + t0) * a.Dv + 16 * jv)
-                   : kPaged ? reinterpret_cast<const char*>(a.v + 8 * jv)
-                            : reinterpret_cast<const char*>(a.v + (static_cast<int64_t>(bh) * a.T + t0) * a.Dv + 8 * jv);
-    const int64_t vrow = kQ8 ? a.Dv : 2 * static_cast<int64_t>(a.Dv);  // bytes per token
+    const int64_t vrow = kQ8 ? a.Dv : 2 * static_cast<int64_t>(a.Dv);  // bytes per cache row
+    const char* vp = (kQ8 ? reinterpret_cast<const char*>(a.vq + 16 * jv) : reinterpret_cast<const char*>(a.v + 8 * jv)) +
+                     (kPaged ? 0 : row0 * vrow);
+    const int64_t v_tok = a.ts * vrow;  // contiguous caches: bytes from one token to the next
     const int step = kWaves * kVSlots;
     for (int base = wave * kVSlots + vslot; base < n; base += step * kUv) {
       uint4 wv[kUv];
@@ -427,7 +444,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
         wv[u] = make_uint4(0, 0, 0, 0);
         p[u] = 0.0f;
         if (tt < n) {
-          wv[u] = load_nt(vp + (kPaged ? row_of(tt) : static_cast<int64_t>(tt)) * vrow);
+          wv[u] = load_nt(kPaged ? vp + row_of(tt) * vrow : vp + tt * v_tok);
           p[u] = sc[tt];
         }
       }
@@ -445,14 +462,14 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
           }
           psum += p[u];
         } else {
-          acc[0] = fmaf(p[u], bf16_lo(wv[u].x), acc[0]);
-          acc[1] = fmaf(p[u], bf16_hi(wv[u].x), acc[1]);
-          acc[2] = fmaf(p[u], bf16_lo(wv[u].y), acc[2]);
-          acc[3] = fmaf(p[u], bf16_hi(wv[u].y), acc[3]);
-          acc[4] = fmaf(p[u], bf16_lo(wv[u].z), acc[4]);
-          acc[5] = fmaf(p[u], bf16_hi(wv[u].z), acc[5]);
-          acc[6] = fmaf(p[u], bf16_lo(wv[u].w), acc[6]);
-          acc[7] = fmaf(p[u], bf16_hi(wv[u].w), acc[7]);
+          acc[0] = fmaf(p[u], lo16<kH>(wv[u].x), acc[0]);
+          acc[1] = fmaf(p[u], hi16<kH>(wv[u].x), acc[1]);
+          acc[2] = fmaf(p[u], lo16<kH>(wv[u].y), acc[2]);
+          acc[3] = fmaf(p[u], hi16<kH>(wv[u].y), acc[3]);
+          acc[4] = fmaf(p[u], lo16<kH>(wv[u].z), acc[4]);
+          acc[5] = fmaf(p[u], hi16<kH>(wv[u].z), acc[5]);
+          acc[6] = fmaf(p[u], lo16<kH>(wv[u].w), acc[6]);
+          acc[7] = fmaf(p[u], hi16<kH>(wv[u].w), acc[7]);
         }
       }
     }
@@ -468,14 +485,14 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
       const uint4 wv = *reinterpret_cast<const uint4*>(a.v_new + static_cast<int64_t>(bh) * a.Dv + 8 * jv);
       *reinterpret_cast<uint4*>(const_cast<uint16_t*>(a.v) + row_of(static_cast<int>(pos_new - t0)) * a.Dv + 8 * jv) = wv;
       const float p = sc[n];
-      acc[0] = fmaf(p, bf16_lo(wv.x), acc[0]);
-      acc[1] = fmaf(p, bf16_hi(wv.x), acc[1]);
-      acc[2] = fmaf(p, bf16_lo(wv.y), acc[2]);
-      acc[3] = fmaf(p, bf16_hi(wv.y), acc[3]);
-      acc[4] = fmaf(p, bf16_lo(wv.z), acc[4]);
-      acc[5] = fmaf(p, bf16_hi(wv.z), acc[5]);
-      acc[6] = fmaf(p, bf16_lo(wv.w), acc[6]);
-      acc[7] = fmaf(p, bf16_hi(wv.w), acc[7]);
+      acc[0] = fmaf(p, lo16<kH>(wv.x), acc[0]);
+      acc[1] = fmaf(p, hi16<kH>(wv.x), acc[1]);
+      acc[2] = fmaf(p, lo16<kH>(wv.y), acc[2]);
+      acc[3] = fmaf(p, hi16<kH>(wv.y), acc[3]);
+      acc[4] = fmaf(p, lo16<kH>(wv.z), acc[4]);
+      acc[5] = fmaf(p, hi16<kH>(wv.z), acc[5]);
+      acc[6] = fmaf(p, lo16<kH>(wv.w), acc[6]);
+      acc[7] = fmaf(p, hi16<kH>(wv.w), acc[7]);
     }
   }
 #pragma unroll
@@ -647,13 +664,14 @@ int log2_exact(int64_t v) {
 // Shared validation and launch of the decode entry points (kVar: kVarFixed, kVarRagged or
 // kVarPaged, the last with T = max_pages * page_size and the cache pointers being pools;
 // kFmt: kFmtQkv8 takes INT8 query and values, with q the (B,H,Dr) RoPE part and v unused;
-// kFmtAsym takes the per-(head, dim) K tables instead of the per-head scale).
+// kFmtAsym takes the per-(head, dim) K tables instead of the per-head scale; kFmtF16 is
+// kFmtBf16 with float16 query, K-rope and V).  bshd: contiguous caches are (B,T,H,.).
 template <int kVar, int kFmt>
 int decode_launch(const uint16_t* q, const int8_t* k_nope_q, const float* scale, const uint16_t* k_rope,
                   const uint16_t* v, const int32_t* kv_len, const uint16_t* k_new, const uint16_t* v_new,
                   const Int8QV& i8, int64_t B, int64_t H, int64_t T, int64_t Dn, int64_t Dr, int64_t Dv,
                   float sm_scale, float* out, void* workspace, size_t workspace_bytes, void* stream,
-                  const PagedKV& pk = PagedKV{}, bool use_scratch = false) {
+                  const PagedKV& pk = PagedKV{}, bool use_scratch = false, bool bshd = false) {
   constexpr bool kQ8 = kFmt == kFmtQkv8;
   constexpr bool kAsym = kFmt == kFmtAsym;
   constexpr bool kPaged = kVar == kVarPaged;
@@ -736,6 +754,8 @@ int decode_launch(const uint16_t* q, const int8_t* k_nope_q, const float* scale,
   a.ws_o = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                            round_up(static_cast<size_t>(B * H * p.nsplit) * 2 * sizeof(float), 256))
                 : nullptr;
+  a.hs = bshd ? 1 : T;
+  a.ts = bshd ? H : 1;
   a.T = T;
   a.H = static_cast<int32_t>(H);
   a.Dn = static_cast<int32_t>(Dn);
@@ -827,4 +847,60 @@ extern "C" int fa3q_decode_attn_noalloc(const uint16_t* q, const int8_t* k_nope_
                                         void* stream) {
   return decode_launch<kVarFixed, kFmtBf16>(q, k_nope_q, scale, k_rope, v, nullptr, nullptr, nullptr, Int8QV{}, B, H, T,
                                             Dn, Dr, Dv, sm_scale, out, nullptr, 0, stream, PagedKV{}, true);
+}
+
+namespace fa3q {
+namespace {
+
+// dtype and layout codes of the _ex entry points -> (float16?, (B,T,H,.)?), or a status.
+int ex_codes(int dtype, int layout, bool& f16, bool& bshd) {
+  if (dtype != FA3Q_BF16 && dtype != FA3Q_F16) return FA3Q_ERR_DTYPE;
+  if (layout != FA3Q_BHSD && layout != FA3Q_BSHD) return FA3Q_ERR_LAYOUT;
+  f16 = dtype == FA3Q_F16;
+  bshd = layout == FA3Q_BSHD;
+  return FA3Q_OK;
+}
+
+}  // namespace
+}  // namespace fa3q
+
+extern "C" int fa3q_decode_attn_ex(const void* q, const int8_t* k_nope_q, const float* scale, const void* k_rope,
+                                   const void* v, int dtype, int layout, int64_t B, int64_t H, int64_t T, int64_t Dn,
+                                   int64_t Dr, int64_t Dv, float sm_scale, float* out, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  bool f16 = false, bshd = false;
+  const int st = ex_codes(dtype, layout, f16, bshd);
+  if (st != FA3Q_OK) return st;
+  const auto* q16 = static_cast<const uint16_t*>(q);
+  const auto* r16 = static_cast<const uint16_t*>(k_rope);
+  const auto* v16 = static_cast<const uint16_t*>(v);
+  if (f16)
+    return decode_launch<kVarFixed, kFmtF16>(q16, k_nope_q, scale, r16, v16, nullptr, nullptr, nullptr, Int8QV{}, B, H,
+                                             T, Dn, Dr, Dv, sm_scale, out, workspace, workspace_bytes, stream,
+                                             PagedKV{}, false, bshd);
+  return decode_launch<kVarFixed, kFmtBf16>(q16, k_nope_q, scale, r16, v16, nullptr, nullptr, nullptr, Int8QV{}, B, H, T,
+                                            Dn, Dr, Dv, sm_scale, out, workspace, workspace_bytes, stream, PagedKV{},
+                                            false, bshd);
+}
+
+extern "C" int fa3q_decode_append_attn_ex(const void* q, const void* k_new, const void* v_new, const float* scale,
+                                          int8_t* k_nope_q, void* k_rope, void* v, const int32_t* kv_len, int dtype,
+                                          int layout, int64_t B, int64_t H, int64_t T, int64_t Dn, int64_t Dr,
+                                          int64_t Dv, float sm_scale, float* out, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  bool f16 = false, bshd = false;
+  const int st = ex_codes(dtype, layout, f16, bshd);
+  if (st != FA3Q_OK) return st;
+  const auto* q16 = static_cast<const uint16_t*>(q);
+  const auto* kn16 = static_cast<const uint16_t*>(k_new);
+  const auto* vn16 = static_cast<const uint16_t*>(v_new);
+  const auto* r16 = static_cast<const uint16_t*>(k_rope);
+  const auto* v16 = static_cast<const uint16_t*>(v);
+  if (f16)
+    return decode_launch<kVarRagged, kFmtF16>(q16, k_nope_q, scale, r16, v16, kv_len, kn16, vn16, Int8QV{}, B, H, T, Dn,
+                                              Dr, Dv, sm_scale, out, workspace, workspace_bytes, stream, PagedKV{},
+                                              false, bshd);
+  return decode_launch<kVarRagged, kFmtBf16>(q16, k_nope_q, scale, r16, v16, kv_len, kn16, vn16, Int8QV{}, B, H, T, Dn,
+                                             Dr, Dv, sm_scale, out, workspace, workspace_bytes, stream, PagedKV{},
+                                             false, bshd);
 }

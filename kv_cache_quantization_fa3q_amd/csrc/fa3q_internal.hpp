@@ -46,6 +46,26 @@ constexpr size_t kLdsLimit = 160 * 1024;  // LDS per workgroup on gfx950
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// float16 pair in one dword -> float32 of the low / high element (exact widening).
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w & 0xffffu)));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
+}
+
+// The low / high element of a pair of 16-bit floats: float16 when kF16, else bf16.
+template <bool kF16>
+__device__ __forceinline__ float lo16(uint32_t w) {
+  if constexpr (kF16) return f16_lo(w);
+  else return bf16_lo(w);
+}
+template <bool kF16>
+__device__ __forceinline__ float hi16(uint32_t w) {
+  if constexpr (kF16) return f16_hi(w);
+  else return bf16_hi(w);
+}
+
 // Workgroup barrier that orders LDS traffic only (no wait on outstanding global loads).
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");

@@ -57,7 +57,8 @@ struct QuantArgs {
   int8_t* kq;
   uint16_t* kr;
   int64_t S;
-  int64_t items;          // B*H*chunks_per_bh
+  int64_t rows;           // B*S*H (token-major items)
+  int64_t items;          // B*H*chunks_per_bh, or ceil(rows / kRowsPerItem) (token-major)
   int32_t chunks_per_bh;  // ceil(S / kRowsPerItem)
   int32_t H;
   int32_t Dn;
@@ -69,11 +70,12 @@ __device__ __forceinline__ int code_exact(float x, float s) {
   return static_cast<int>(y);
 }
 
-// 8 bf16 (one 16-byte vector) -> their 8 codes.
+// 8 bf16 (kF16: float16) values, one 16-byte vector -> their 8 codes.
+template <bool kF16 = false>
 __device__ __forceinline__ void codes8(const u32x4& w, float s, float r, bool fast, int (&c)[8]) {
   float xv[8];
-  xv[0] = bf16_lo(w.x); xv[1] = bf16_hi(w.x); xv[2] = bf16_lo(w.y); xv[3] = bf16_hi(w.y);
-  xv[4] = bf16_lo(w.z); xv[5] = bf16_hi(w.z); xv[6] = bf16_lo(w.w); xv[7] = bf16_hi(w.w);
+  xv[0] = lo16<kF16>(w.x); xv[1] = hi16<kF16>(w.x); xv[2] = lo16<kF16>(w.y); xv[3] = hi16<kF16>(w.y);
+  xv[4] = lo16<kF16>(w.z); xv[5] = hi16<kF16>(w.z); xv[6] = lo16<kF16>(w.w); xv[7] = hi16<kF16>(w.w);
   bool amb = !fast;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -90,10 +92,11 @@ __device__ __forceinline__ void codes8(const u32x4& w, float s, float r, bool fa
   }
 }
 
-// 8 bf16 -> 8 codes in two dwords (little-endian element order).
+// 8 bf16 (kF16: float16) -> 8 codes in two dwords (little-endian element order).
+template <bool kF16>
 __device__ __forceinline__ u32x2 quant8(const u32x4& w, float s, float r, bool fast) {
   int c[8];
-  codes8(w, s, r, fast, c);
+  codes8<kF16>(w, s, r, fast, c);
   u32x2 o;
   o.x = (c[0] & 0xff) | ((c[1] & 0xff) << 8) | ((c[2] & 0xff) << 16) | (static_cast<uint32_t>(c[3]) << 24);
   o.y = (c[4] & 0xff) | ((c[5] & 0xff) << 8) | ((c[6] & 0xff) << 16) | (static_cast<uint32_t>(c[7]) << 24);
@@ -110,8 +113,23 @@ __device__ __forceinline__ u32x4 fake8(const u32x4& w, float s, float r, bool fa
   return u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
 }
 
+// Quotient parameters of one head's scale: the reciprocal, whether the fast quotient
+// applies (a moderate normal scale: 1/s normal, x*(1/s) free of overflow), and a zero scale.
+struct HeadQ {
+  float s, r;
+  bool fast, zero;
+};
+
+__device__ __forceinline__ HeadQ head_q(float s) {
+  return HeadQ{s, 1.0f / s, fabsf(s) >= 0x1p-100f && fabsf(s) <= 0x1p100f, s == 0.0f};
+}
+
 // UN / UR: 8-element units per nope / rope row when known at compile time (0: runtime).
-template <int UN, int UR>
+// kF16: float16 K (the RoPE copy is float16 too), else bf16.  kTok: (B,S,H,Dn+Dr) rows; an
+// item is kRowsPerItem consecutive rows, row g belonging to head g % H, so every vector
+// carries its own head's scale.  Otherwise (B,H,S,.) rows; an item is a run of rows of one
+// (b, h) and the scale one scalar.
+template <int UN, int UR, bool kF16, bool kTok>
 __global__ __launch_bounds__(kThreads) void quantize_k_kernel(QuantArgs a) {
   const int tid = static_cast<int>(threadIdx.x);
   const int Dk = a.Dn + a.Dr;
@@ -121,12 +139,20 @@ __global__ __launch_bounds__(kThreads) void quantize_k_kernel(QuantArgs a) {
   constexpr int kRope = UR ? (kRowsPerItem * UR + kThreads - 1) / kThreads : 2;
 
   for (int64_t item = blockIdx.x; item < a.items; item += gridDim.x) {
-    const int64_t bh = item / a.chunks_per_bh;
-    const int64_t chunk = item - bh * a.chunks_per_bh;
-    const int hh = __builtin_amdgcn_readfirstlane(static_cast<int>(bh % a.H));  // uniform: scalar read
-    const int64_t r_begin = chunk * kRowsPerItem;
-    const int nr = static_cast<int>(min(static_cast<int64_t>(kRowsPerItem), a.S - r_begin));
-    const int64_t row0 = bh * a.S + r_begin;
+    int64_t row0;
+    int nr, hh;
+    if constexpr (kTok) {
+      row0 = item * kRowsPerItem;
+      nr = static_cast<int>(min(static_cast<int64_t>(kRowsPerItem), a.rows - row0));
+      hh = __builtin_amdgcn_readfirstlane(static_cast<int>(row0 % a.H));  // head of the item's first row
+    } else {
+      const int64_t bh = item / a.chunks_per_bh;
+      const int64_t chunk = item - bh * a.chunks_per_bh;
+      hh = __builtin_amdgcn_readfirstlane(static_cast<int>(bh % a.H));  // uniform: scalar read
+      const int64_t r_begin = chunk * kRowsPerItem;
+      nr = static_cast<int>(min(static_cast<int64_t>(kRowsPerItem), a.S - r_begin));
+      row0 = bh * a.S + r_begin;
+    }
     const uint16_t* __restrict__ kin = a.k + row0 * Dk;
     int8_t* __restrict__ qout = a.kq + row0 * a.Dn;
     uint16_t* __restrict__ rout = a.kr + row0 * a.Dr;
@@ -135,6 +161,7 @@ __global__ __launch_bounds__(kThreads) void quantize_k_kernel(QuantArgs a) {
     for (int pass = 0; pass * kThreads * kNope < nn || pass * kThreads * kRope < nrp; ++pass) {
       u32x4 xn[kNope], xr[kRope];
       int on[kNope], orr[kRope];
+      int hv[kNope];  // token-major: each nope vector's head
       // Loads are unconditional (a vector past the item's end re-reads its last vector and is
       // not stored), so they issue back to back instead of one exec-masked block at a time.
 #pragma unroll
@@ -143,6 +170,10 @@ __global__ __launch_bounds__(kThreads) void quantize_k_kernel(QuantArgs a) {
         const int qc = min(q, nn - 1);
         const int row = qc / Un, unit = qc - row * Un;
         on[j] = q < nn ? row * a.Dn + unit * 8 : -1;
+        if constexpr (kTok) {
+          const int hr = hh + row;  // < H + kRowsPerItem
+          hv[j] = hr < a.H ? hr : hr % a.H;
+        }
         xn[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kin + static_cast<int64_t>(row) * Dk + unit * 8));
       }
       if (Ur > 0) {
@@ -155,17 +186,24 @@ __global__ __launch_bounds__(kThreads) void quantize_k_kernel(QuantArgs a) {
           xr[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kin + static_cast<int64_t>(row) * Dk + a.Dn + unit * 8));
         }
       }
-      // the scale is read after the data loads are issued, so its latency hides behind theirs
-      const float s = a.scale[hh];
-      const bool zero = (s == 0.0f);
-      // fast quotient only for a moderate normal scale (1/s normal, x*(1/s) free of overflow)
-      const bool fast = fabsf(s) >= 0x1p-100f && fabsf(s) <= 0x1p100f;
-      const float r = 1.0f / s;
+      // the scales are read after the data loads are issued, so their latency hides behind theirs
+      if constexpr (kTok) {
 #pragma unroll
-      for (int j = 0; j < kNope; ++j) {
-        if (on[j] >= 0) {
-          const u32x2 o = zero ? u32x2{0u, 0u} : quant8(xn[j], s, r, fast);
-          __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(qout + on[j]));
+        for (int j = 0; j < kNope; ++j) {
+          if (on[j] >= 0) {
+            const HeadQ hq = head_q(a.scale[hv[j]]);
+            const u32x2 o = hq.zero ? u32x2{0u, 0u} : quant8<kF16>(xn[j], hq.s, hq.r, hq.fast);
+            __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(qout + on[j]));
+          }
+        }
+      } else {
+        const HeadQ hq = head_q(a.scale[hh]);
+#pragma unroll
+        for (int j = 0; j < kNope; ++j) {
+          if (on[j] >= 0) {
+            const u32x2 o = hq.zero ? u32x2{0u, 0u} : quant8<kF16>(xn[j], hq.s, hq.r, hq.fast);
+            __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(qout + on[j]));
+          }
         }
       }
       if (Ur > 0) {
@@ -415,9 +453,19 @@ __global__ __launch_bounds__(kThreads) void quantize_asym_kernel(AsymArgs a) {
 
 using namespace fa3q;
 
-extern "C" int fa3q_quantize_k(const uint16_t* k, const float* scale, int8_t* k_nope_q,
-                               uint16_t* k_rope, int64_t B, int64_t H, int64_t S, int64_t Dn,
-                               int64_t Dr, void* stream) {
+namespace fa3q {
+namespace {
+
+template <bool kF16, bool kTok>
+void launch_quantize_k(const QuantArgs& a, dim3 g, hipStream_t s) {
+  if (a.Dn == 128 && a.Dr == 64)
+    hipLaunchKernelGGL((quantize_k_kernel<16, 8, kF16, kTok>), g, dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((quantize_k_kernel<0, 0, kF16, kTok>), g, dim3(kThreads), 0, s, a);
+}
+
+int quantize_k(const uint16_t* k, const float* scale, int8_t* k_nope_q, uint16_t* k_rope, bool f16, bool tok,
+               int64_t B, int64_t H, int64_t S, int64_t Dn, int64_t Dr, void* stream) {
   if (!k || !scale || !k_nope_q || (Dr > 0 && !k_rope)) return FA3Q_ERR_NULL;
   if (B <= 0 || H <= 0 || S <= 0) return FA3Q_ERR_SHAPE;
   if (Dn <= 0 || Dn % 16 != 0 || Dn > 4096) return FA3Q_ERR_SHAPE;
@@ -436,18 +484,39 @@ extern "C" int fa3q_quantize_k(const uint16_t* k, const float* scale, int8_t* k_
   a.kq = k_nope_q;
   a.kr = k_rope;
   a.S = S;
+  a.rows = B * S * H;
   a.chunks_per_bh = static_cast<int32_t>(chunks);
-  a.items = B * H * chunks;
+  a.items = tok ? (a.rows + kRowsPerItem - 1) / kRowsPerItem : B * H * chunks;
   a.H = static_cast<int32_t>(H);
   a.Dn = static_cast<int32_t>(Dn);
   a.Dr = static_cast<int32_t>(Dr);
-  const int64_t grid = std::min<int64_t>(a.items, kMaxGrid);
-  const dim3 g(static_cast<unsigned>(grid)), blk(kThreads);
-  if (Dn == 128 && Dr == 64)
-    hipLaunchKernelGGL((quantize_k_kernel<16, 8>), g, blk, 0, as_stream(stream), a);
-  else
-    hipLaunchKernelGGL((quantize_k_kernel<0, 0>), g, blk, 0, as_stream(stream), a);
+  const dim3 g(static_cast<unsigned>(std::min<int64_t>(a.items, kMaxGrid)));
+  hipStream_t s = as_stream(stream);
+  if (f16) {
+    if (tok) launch_quantize_k<true, true>(a, g, s);
+    else launch_quantize_k<true, false>(a, g, s);
+  } else {
+    if (tok) launch_quantize_k<false, true>(a, g, s);
+    else launch_quantize_k<false, false>(a, g, s);
+  }
   return launch_status();
+}
+
+}  // namespace
+}  // namespace fa3q
+
+extern "C" int fa3q_quantize_k(const uint16_t* k, const float* scale, int8_t* k_nope_q,
+                               uint16_t* k_rope, int64_t B, int64_t H, int64_t S, int64_t Dn,
+                               int64_t Dr, void* stream) {
+  return quantize_k(k, scale, k_nope_q, k_rope, false, false, B, H, S, Dn, Dr, stream);
+}
+
+extern "C" int fa3q_quantize_k_ex(const void* k, const float* scale, int8_t* k_nope_q, void* k_rope, int dtype,
+                                  int layout, int64_t B, int64_t H, int64_t S, int64_t Dn, int64_t Dr, void* stream) {
+  if (dtype != FA3Q_BF16 && dtype != FA3Q_F16) return FA3Q_ERR_DTYPE;
+  if (layout != FA3Q_BHSD && layout != FA3Q_BSHD) return FA3Q_ERR_LAYOUT;
+  return quantize_k(static_cast<const uint16_t*>(k), scale, k_nope_q, static_cast<uint16_t*>(k_rope),
+                    dtype == FA3Q_F16, layout == FA3Q_BSHD, B, H, S, Dn, Dr, stream);
 }
 
 extern "C" int fa3q_fake_quant(const uint16_t* x, const float* scale, uint16_t* y, int64_t B, int64_t H,

@@ -67,6 +67,7 @@ extern "C" const char* fa3q_status_string(int status) {
     case FA3Q_ERR_UNSUPPORTED: return "FA3Q_ERR_UNSUPPORTED: arguments outside what this build handles";
     case FA3Q_ERR_ALIAS: return "FA3Q_ERR_ALIAS: an output partly overlaps an input";
     case FA3Q_ERR_SCRATCH: return "FA3Q_ERR_SCRATCH: the call needs more scratch than the static array holds";
+    case FA3Q_ERR_LAYOUT: return "FA3Q_ERR_LAYOUT: unknown layout code";
     default: return "FA3Q_ERR_UNKNOWN";
   }
 }

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_function():
 def test_version_and_status_strings():
     lib = fa.lib()
     assert lib.fa3q_version() >> 16 == 1
-    for code in range(11):
+    for code in range(12):
         s = fa.status_string(code)
         assert s.startswith("FA3Q_")
     assert fa.status_string(0) == "FA3Q_OK"
@@ -469,4 +469,142 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError):
         fa.fa3q_calibrate_perhead(x, 0.9)
     with pytest.raises(TypeError):
-        fa.fa3q_calibrate_perhead(x.to(torch.float16), 0.9)
+        fa.fa3q_calibrate_perhead(x.to(torch.float64), 0.9)
+
+
+def test_binding_checks_every_tensor_before_a_launch():
+    # host tensors throughout: each wrong dtype or size must be named before the device check
+    import torch
+    B, H, T, Dn, Dr, Dv = 2, 4, 32, 32, 16, 32
+    q = torch.zeros((B, H, Dn + Dr), dtype=torch.bfloat16)
+    kq = torch.zeros((B, H, T, Dn), dtype=torch.int8)
+    kr = torch.zeros((B, H, T, Dr), dtype=torch.bfloat16)
+    v = torch.zeros((B, H, T, Dv), dtype=torch.bfloat16)
+    scale = torch.ones(H, dtype=torch.float32)
+
+    def raises(match, fn, *args, **kw):
+        with pytest.raises(ValueError, match=match):
+            fn(*args, **kw)
+
+    raises("scale must be float32", fa.fa3q_decode_attn, q, kq, scale.to(torch.bfloat16), kr, v, 0.1)
+    raises("scale must be float32 with 4", fa.fa3q_decode_attn, q, kq, scale[:3], kr, v, 0.1)
+    raises("out must be", fa.fa3q_decode_attn, q, kq, scale, kr, v, 0.1, out=torch.empty((B, H, Dv - 1)))
+    raises("out must be", fa.fa3q_decode_attn, q, kq, scale, kr, v, 0.1,
+           out=torch.empty((B, H, Dv), dtype=torch.float16))
+    raises("v must be", fa.fa3q_decode_attn, q, kq, scale, kr, v[:, :, :-1], 0.1)
+    raises("q must be", fa.fa3q_decode_attn_ex, q.float(), kq, scale, kr, v, 0.1)
+    raises("v must be", fa.fa3q_decode_attn_ex, q.half(), kq, scale, kr.half(), v, 0.1)  # mixed dtypes
+    raises("layout", fa.fa3q_decode_attn_ex, q, kq, scale, kr, v, 0.1, layout="SBHD")
+    raises("kv_len", fa.fa3q_decode_append_attn, q, None, None, scale, kq, kr, v,
+           torch.zeros(B, dtype=torch.int64), 0.1)
+    k = torch.zeros((B, H, T, Dn + Dr), dtype=torch.bfloat16)
+    raises("k_nope_q must be", fa.fa3q_quantize_k, k, scale, Dn, k_nope_q=torch.empty((B, H, T - 1, Dn),
+                                                                                      dtype=torch.int8))
+    raises("k_rope must be", fa.fa3q_quantize_k, k, scale, Dn, k_rope=torch.empty((B, H, T, Dr)))
+    raises("scale must be float32", fa.fa3q_quantize_k, k, scale.double(), Dn)
+    raises("k must be bfloat16", fa.fa3q_quantize_k, k.half(), scale, Dn)
+    raises("k_nope_q must be", fa.fa3q_quantize_k_ex, k.transpose(1, 2).contiguous(), scale, Dn, layout="BSHD",
+           k_nope_q=torch.empty((B, H, T, Dn), dtype=torch.int8))  # codes in the other layout
+    f = torch.zeros(H, dtype=torch.float32)
+    raises("cur_min must be float32 with 4", fa.fa3q_accumulate_minmax, f, f, f[:2], f)
+    raises("run_max must be float32", fa.fa3q_qparams, f, f.half())
+    raises("scale must be float32 with 4", fa.fa3q_qparams, f, f, torch.empty(5))
+    raises("run_max must be float32 with 4", fa.fa3q_init_minmax, f, torch.empty(3))
+    x = torch.zeros((1, H, 64, 32), dtype=torch.float32)
+    raises("run_min and run_max are required", fa.fa3q_calibrate_batches, [x], 0.9, None, f)
+    raises("win_min must be float32 with 8", fa.fa3q_calibrate_batches, [x, x], 0.9, f, f,
+           win_min=torch.empty(4), win_max=torch.empty(8))
+    raises("given together", fa.fa3q_calibrate_ex, [x], 0.9, run_min=f)
+
+
+# ----------------------------------------------------------------------------- float16 and (B,S,H,D)
+
+
+def test_ex_workspace_queries():
+    lib = fa.lib()
+    q = lib.fa3q_calibrate_ex_workspace_bytes
+    r = 0.99
+    for dt in (L.FA3Q_BF16, L.FA3Q_F16):
+        # the (B,H,S,D) call equals the batches call; (B,S,H,D) 16-bit input takes the histogram
+        assert q(dt, L.FA3Q_BHSD, 2, 1, 8, 256, 64, r) == lib.fa3q_calibrate_batches_workspace_bytes(
+            dt, 2, 1, 8, 256, 64, r) > 0
+        assert q(dt, L.FA3Q_BSHD, 2, 1, 8, 256, 64, r) >= 2 * 8 * 65536 * 4
+        assert q(dt, L.FA3Q_BSHD, 1, 2, 4, 16, 12, r) == 0  # rows of 12 values: not whole vectors
+    assert q(L.FA3Q_F32, L.FA3Q_BHSD, 1, 1, 8, 256, 64, r) > 0
+    assert q(L.FA3Q_F32, L.FA3Q_BSHD, 1, 1, 8, 256, 64, r) == 0  # float32 (B,S,H,D): not handled
+    assert q(L.FA3Q_BF16, 2, 1, 1, 8, 256, 64, r) == 0
+    assert q(7, L.FA3Q_BHSD, 1, 1, 8, 256, 64, r) == 0
+    assert q(L.FA3Q_F16, L.FA3Q_BHSD, 17, 1, 8, 256, 64, r) == 0
+    # float16 heads follow bf16's routing: the same windows cap, the same workspace
+    assert lib.fa3q_calibrate_max_windows(L.FA3Q_F16) == lib.fa3q_calibrate_max_windows(L.FA3Q_BF16)
+    assert lib.fa3q_calibrate_workspace_bytes(L.FA3Q_F16, 2, 8, 4096, 128, 0.999) == \
+        lib.fa3q_calibrate_workspace_bytes(L.FA3Q_BF16, 2, 8, 4096, 128, 0.999)
+
+
+@no_gpu_only
+def test_calibrate_ex_rejections():
+    f = fa.lib().fa3q_calibrate_ex
+    xs = (ctypes.c_void_p * 2)(1 << 20, 2 << 20)
+    ok = dict(xs=xs, nb=2, dt=L.FA3Q_F16, lay=L.FA3Q_BSHD, B=1, H=8, S=256, D=64, r=0.99, rmin=_p(), rmax=_p(),
+              init=1, wmin=None, wmax=None, ws=_p(), wb=1 << 40)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["xs"], a["nb"], a["dt"], a["lay"], a["B"], a["H"], a["S"], a["D"], a["r"], a["rmin"], a["rmax"],
+                 a["init"], a["wmin"], a["wmax"], a["ws"], a["wb"], None)
+
+    assert call(lay=2) == L.FA3Q_ERR_LAYOUT
+    assert call(dt=5) == L.FA3Q_ERR_DTYPE
+    assert call(dt=L.FA3Q_F32) == L.FA3Q_ERR_UNSUPPORTED
+    assert call(D=12) == L.FA3Q_ERR_SHAPE
+    assert call(nb=0) == L.FA3Q_ERR_SHAPE
+    assert call(r=0.0) == L.FA3Q_ERR_RATIO
+    assert call(rmin=None, rmax=None) == L.FA3Q_ERR_NULL  # neither statistics nor windows
+    assert call(rmax=None) == L.FA3Q_ERR_NULL
+    assert call(rmin=None, rmax=None, wmin=_p(), wmax=None) == L.FA3Q_ERR_NULL
+    assert call(ws=None) == L.FA3Q_ERR_WORKSPACE
+    assert call(wb=16) == L.FA3Q_ERR_WORKSPACE
+    assert call(xs=(ctypes.c_void_p * 2)(1 << 20, (2 << 20) + 8)) == L.FA3Q_ERR_ALIGN
+
+
+@no_gpu_only
+def test_quantize_k_ex_rejections():
+    f = fa.lib().fa3q_quantize_k_ex
+    ok = dict(k=_p(), s=_p(), kq=_p(), kr=_p(), dt=L.FA3Q_F16, lay=L.FA3Q_BSHD, B=2, H=4, S=16, Dn=128, Dr=64)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["k"], a["s"], a["kq"], a["kr"], a["dt"], a["lay"], a["B"], a["H"], a["S"], a["Dn"], a["Dr"], None)
+
+    assert call(lay=7) == L.FA3Q_ERR_LAYOUT
+    assert call(dt=L.FA3Q_F32) == L.FA3Q_ERR_DTYPE
+    for name in ("k", "s", "kq", "kr"):
+        assert call(**{name: None}) == L.FA3Q_ERR_NULL, name
+    assert call(Dn=120) == L.FA3Q_ERR_SHAPE
+    assert call(kr=_p(8)) == L.FA3Q_ERR_ALIGN
+
+
+@no_gpu_only
+def test_decode_ex_rejections():
+    lib = fa.lib()
+    ok = dict(q=_p(), kq=_p(), s=_p(), kr=_p(), v=_p(), dt=L.FA3Q_F16, lay=L.FA3Q_BSHD, B=2, H=4, T=512, Dn=128,
+              Dr=64, Dv=128, sm=0.07, o=_p(), ws=_p(), wb=1 << 30)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return lib.fa3q_decode_attn_ex(a["q"], a["kq"], a["s"], a["kr"], a["v"], a["dt"], a["lay"], a["B"], a["H"],
+                                       a["T"], a["Dn"], a["Dr"], a["Dv"], ctypes.c_float(a["sm"]), a["o"], a["ws"],
+                                       a["wb"], None)
+
+    def append(**kw):
+        a = dict(ok, **kw)
+        return lib.fa3q_decode_append_attn_ex(a["q"], _p(), _p(), a["s"], a["kq"], a["kr"], a["v"], _p(), a["dt"],
+                                              a["lay"], a["B"], a["H"], a["T"], a["Dn"], a["Dr"], a["Dv"],
+                                              ctypes.c_float(a["sm"]), a["o"], a["ws"], a["wb"], None)
+
+    for fn in (call, append):
+        assert fn(lay=-1) == L.FA3Q_ERR_LAYOUT
+        assert fn(dt=L.FA3Q_F32) == L.FA3Q_ERR_DTYPE
+        assert fn(q=None) == L.FA3Q_ERR_NULL
+        assert fn(Dv=96) == L.FA3Q_ERR_SHAPE
+        assert fn(v=_p(8)) == L.FA3Q_ERR_ALIGN

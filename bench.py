@@ -268,7 +268,7 @@ def cpu_baseline(pool, workers: int, inputs, budget_s: float):
 
 
 EXTRAS = ("decode_append", "decode_qkv8", "asym", "fake_quant", "decode_latent", "calibrate_long",
-          "calibrate_largek", "decode_long", "decode_noalloc", "decode_paged")
+          "calibrate_largek", "decode_long", "decode_noalloc", "decode_paged", "f16_bshd")
 
 
 def main() -> int:
@@ -571,6 +571,39 @@ def run(args, only, pool, workers) -> int:
         breakdown["decode_paged"] = hbm_row(pg_ms, DEC_BYTES + table.numel() * 4, "B=64 H=128 T=4096 in 64-token "
                                             "pages through a permuted block table (outside the step)", key="kv_gbs")
         del table
+
+    if "f16_bshd" in only:
+        # the step's three streaming stages on float16 tensors in the (B,S,H,D) layout: the calibration
+        # batches, K and the decode cache transposed and converted once, outside the timing
+        def f16_bshd(t):
+            return t.transpose(1, 2).contiguous().to(torch.float16)
+
+        calib_t = [f16_bshd(x) for x in calib]
+        ws_t = torch.empty(max(1, fa.fa3q_calibrate_ex_workspace_bytes(torch.float16, "BSHD", CAL_BATCHES,
+                                                                       *CAL_SHAPE, RATIO)),
+                           dtype=torch.uint8, device=dev)
+        rmin_t = torch.empty(H, dtype=torch.float32, device=dev)
+        rmax_t = torch.empty(H, dtype=torch.float32, device=dev)
+        ct_ms = timed(lambda: fa.fa3q_calibrate_ex(calib_t, RATIO, "BSHD", rmin_t, rmax_t, True, workspace=ws_t,
+                                                   stream=stream))
+        breakdown["calibrate_f16_bshd"] = hbm_row(ct_ms, CAL_BATCHES * CAL_BYTES, "4 batches (8,2048,128,128) "
+                                                  "float16 (B,S,H,D) through fa3q_calibrate_ex (histogram path; "
+                                                  "outside the step)")
+        del calib_t, ws_t
+        k_t = f16_bshd(k)
+        kq_t = torch.empty((QB, QS, H, DN), dtype=torch.int8, device=dev)
+        kr_t = torch.empty((QB, QS, H, DR), dtype=torch.float16, device=dev)
+        qt_ms = timed(lambda: fa.fa3q_quantize_k_ex(k_t, scale, DN, "BSHD", kq_t, kr_t, stream=stream))
+        breakdown["quantize_f16_bshd"] = hbm_row(qt_ms, QUANT_BYTES, "K (64,4096,128,128+64) float16 (B,S,H,D) "
+                                                 "through fa3q_quantize_k_ex (outside the step)")
+        del k_t
+        v_t, q_t = f16_bshd(v), q.to(torch.float16)
+        dt_ms = timed(lambda: fa.fa3q_decode_attn_ex(q_t, kq_t, scale, kr_t, v_t, sm, "BSHD", out, ws_dec,
+                                                     stream=stream))
+        breakdown["decode_f16_bshd"] = hbm_row(dt_ms, DEC_BYTES, "B=64 H=128 T=4096 cache in (B,T,H,.) with float16 "
+                                               "q, K-rope and V through fa3q_decode_attn_ex (outside the step)",
+                                               key="kv_gbs")
+        del kq_t, kr_t, v_t, q_t
 
     # device-to-device copy of COPY_BYTES: a reference ceiling for read+write streaming, and the
     # known-size kernel the HBM byte counters are scaled by

@@ -52,7 +52,10 @@ constexpr uint32_t kMaxEvents = 2048;  // counter wraps one workgroup can log
 // completes), so parts of this size never overflow the log
 constexpr int64_t kMaxPartValues = static_cast<int64_t>(kMaxEvents) * 32768;
 constexpr int kBinsPerThread = kBins / kHistThreads;  // 64
-constexpr int kCtlWords = 64;  // scan and reduction scratch at the start of LDS
+// scratch at the start of LDS: scan totals [0, 32), per-wave best candidates [32, 64), the
+// keys holding ranks K - 1 and t - 1 at kCtlRanks
+constexpr int kCtlWords = 72;
+constexpr int kCtlRanks = 64;
 // one part's record in the workspace: the packed counters as they stand in LDS, a header,
 // then the logged wraps (the pattern whose 16-bit field wrapped)
 constexpr int64_t kPartPacked = kBins / 2;
@@ -61,11 +64,15 @@ enum Hdr : int { kHdrEvents = 0 };
 constexpr int64_t kMinPartValues = int64_t{1} << 19;  // parts smaller than this do not pay for their record
 // distinct values the window kernel keeps in LDS: a 16-bit key and a 32-bit inc[] each
 constexpr int kWinCap = 24576;
-constexpr size_t kWinLds = kCtlWords * 4 + std::max<size_t>(static_cast<size_t>(kWinCap) * 6, kBins * 2);
+constexpr size_t kWinLds = kCtlWords * 4 + std::max<size_t>(static_cast<size_t>(kWinCap) * 6, kBins * 2 + kBins / 4 + 4);
 
 static_assert(kBinsPerThread * kHistThreads == kBins, "bins per thread");
 static_assert(kWinLds <= kLdsLimit, "LDS budget");
 static_assert(kWinLds >= kCtlWords * 4 + kBins * 2, "the window kernel counts wraps in its LDS");
+// the merge-path search: a 16-bit prefix of every key and a prefix per 16 keys (and N) after the
+// control words
+constexpr int kMergeWords = kCtlWords + kBins / 2 + kBins / 16 + 1;
+static_assert(kWinLds >= static_cast<size_t>(kMergeWords) * 4, "merge-path search in the window kernel's LDS");
 
 struct HistArgs {
   const void* x[kHistMaxBatches];
@@ -232,6 +239,13 @@ __device__ __forceinline__ void count_rows(const HistArgs& a, const uint4* xb, i
   }
 }
 
+// v, as a value the compiler cannot see through: running sums over the counts built from it
+// cannot be shared between loops, which would keep 64 partial sums live across them
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+  __asm__ volatile("" : "+v"(v));
+  return v;
+}
+
 // Exclusive scans of two values per thread over the 1024 threads at once; tot gets the sums.
 __device__ __forceinline__ uint2 block_exclusive_scan2(uint2 v, uint32_t* scratch, uint2* tot) {
   const int tid = static_cast<int>(threadIdx.x);
@@ -270,25 +284,34 @@ __device__ __forceinline__ void zero_hist(uint32_t* hist) {
     reinterpret_cast<uint4*>(hist)[i] = make_uint4(0, 0, 0, 0);
 }
 
-// Per-thread counts from the packed 16-bit counters of dwords dw0 .. dw0+31 (pattern order).
-__device__ __forceinline__ void add_packed(uint32_t (&c)[kBinsPerThread], const uint32_t* words, int dw0) {
+// Thread t holds the 64 keys [64t, 64t+64) = bin0 .. bin0+63, in key order.  Their patterns
+// fill dwords dw0 .. dw0+31 of the packed counters, ascending with the keys for non-negative
+// values (key = pattern ^ 0x8000), descending for negative ones (key = 0xffff - pattern).
+// So key pair m (keys bin0 + 2m, bin0 + 2m + 1) is dword dw0 + m (lower field first) or,
+// with rev (bin0 < 0x8000, uniform per wave), dword dw0 + 31 - m with the upper field
+// first.  The helpers below read in key order with selects, not branches: a branch would
+// keep the counts live in both orders.
+__device__ __forceinline__ int first_dword(int bin0) { return bin0 < 0x8000 ? (0xffc0 - bin0) / 2 : (bin0 - 0x8000) / 2; }
+
+// Adds the packed 16-bit counters of the thread's keys (dwords dw0 .. dw0+31 of words).
+__device__ __forceinline__ void add_packed(uint32_t (&c)[kBinsPerThread], const uint32_t* words, int dw0, bool rev) {
 #pragma unroll
-  for (int i = 0; i < kBinsPerThread / 8; ++i) {
-    const uint4 v = reinterpret_cast<const uint4*>(words + dw0)[i];
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  for (int q = 0; q < kBinsPerThread / 8; ++q) {  // key pairs 4q .. 4q+3
+    const uint4 v = reinterpret_cast<const uint4*>(words + dw0)[rev ? 7 - q : q];
+    const uint32_t w[4] = {rev ? v.w : v.x, rev ? v.z : v.y, rev ? v.y : v.z, rev ? v.x : v.w};
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      c[8 * i + 2 * k] += w[k] & 0xffffu;
-      c[8 * i + 2 * k + 1] += w[k] >> 16;
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t lo = w[e] & 0xffffu, hi = w[e] >> 16;
+      c[8 * q + 2 * e] += rev ? hi : lo;
+      c[8 * q + 2 * e + 1] += rev ? lo : hi;
     }
   }
 }
 
-// Applies logged wraps to the thread's 32 dwords (patterns 2*dw0 .. 2*dw0+63, counts cp in
-// pattern order): the wraps are counted per pattern in the packed LDS histogram `cnt`
-// (zeroed by the caller), then dword d gets 65536 W_lo more in its lower pattern and
-// 65536 W_hi - W_lo more in its upper one.
-__device__ __forceinline__ void add_wraps(uint32_t (&cp)[kBinsPerThread], uint32_t* cnt, int dw0,
+// Applies logged wraps to the thread's keys: the wraps are counted per pattern in the packed
+// LDS histogram `cnt` (zeroed by the caller), then dword d gives its lower pattern 65536 W_lo
+// more values and its upper one 65536 W_hi - W_lo more.
+__device__ __forceinline__ void add_wraps(uint32_t (&c)[kBinsPerThread], uint32_t* cnt, int dw0, bool rev,
                                           const uint32_t* pats, uint32_t n) {
   const int tid = static_cast<int>(threadIdx.x);
   for (uint32_t e = tid; e < n; e += kHistThreads) {
@@ -297,70 +320,97 @@ __device__ __forceinline__ void add_wraps(uint32_t (&cp)[kBinsPerThread], uint32
   }
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < kBinsPerThread / 2; ++i) {
-    const uint32_t w = cnt[dw0 + i];
-    cp[2 * i] += (w & 0xffffu) << 16;
-    cp[2 * i + 1] += ((w >> 16) << 16) - (w & 0xffffu);
+  for (int m = 0; m < kBinsPerThread / 2; ++m) {
+    const uint32_t w = cnt[dw0 + (rev ? kBinsPerThread / 2 - 1 - m : m)];
+    const uint32_t lo_add = (w & 0xffffu) << 16;
+    const uint32_t hi_add = ((w >> 16) << 16) - (w & 0xffffu);
+    c[2 * m] += rev ? hi_add : lo_add;
+    c[2 * m + 1] += rev ? lo_add : hi_add;
   }
   __syncthreads();
 }
 
-// Thread t holds the 64 keys [64t, 64t+64): patterns 2*dw0 .. 2*dw0+63, ascending with the
-// keys for non-negative values (key = pattern ^ 0x8000), descending for negative ones
-// (key = 0xffff - pattern).
-__device__ __forceinline__ int first_dword(int bin0) { return bin0 < 0x8000 ? (0xffc0 - bin0) / 2 : (bin0 - 0x8000) / 2; }
-
-__device__ __forceinline__ void to_key_order(uint32_t (&c)[kBinsPerThread], int bin0) {
-  if (bin0 < 0x8000) {  // uniform per wave
-#pragma unroll
-    for (int i = 0; i < kBinsPerThread / 2; ++i) {
-      const uint32_t t = c[i];
-      c[i] = c[kBinsPerThread - 1 - i];
-      c[kBinsPerThread - 1 - i] = t;
-    }
-  }
-}
-
 // The Recall Window of head bh from its counts (thread t: keys [64t, 64t+64) in c, key
-// order).  lds: kCtlWords of scratch, then room for kWinCap distinct values; inc_g: 65536
-// words of global memory for inc[] when the distinct values do not fit in LDS (the caller
-// has read whatever it held).
+// order).  lds: kCtlWords of scratch, then room for kWinCap distinct values or for the
+// merge search's prefixes; inc_g: 65536 words of global memory for the inc[] of keys in
+// 16-key groups of more than 65535 values (the caller has read whatever it held).
+//
+// Only two key ranges take part: lower ends are keys with f(a) < K, so at most a_max, the
+// key holding rank K - 1; upper ends hold rank f(a) + t - 1 >= t - 1, so they are at least
+// m_min, the key holding rank t - 1.  (For ratios near 1 both ranges are short tails.)
+// The distinct keys of the two ranges, with their inc[], are listed in LDS while they fit
+// (every key below a candidate is below a_max, so the list holds each candidate's
+// predecessor, and the keys left out between the ranges have inc[] <= t - 1, never an
+// upper end); otherwise the merge search below runs over the two ranges.
 __device__ void window_from_counts(uint32_t (&c)[kBinsPerThread], uint32_t* lds, uint32_t* inc_g, const HistArgs& a,
                                    int64_t bh) {
   uint32_t* ctl = lds;                                  // [kCtlWords] scan and reduction scratch
-  uint32_t* inc_l = lds + kCtlWords;                    // [kWinCap] inc of each distinct value
+  uint32_t* inc_l = lds + kCtlWords;                    // [kWinCap] inc of each listed value
   uint16_t* key_l = reinterpret_cast<uint16_t*>(inc_l + kWinCap);  // [kWinCap] its key
   const int tid = static_cast<int>(threadIdx.x);
   const int lane = tid & (kWave - 1), wave = tid / kWave;
   const int bin0 = tid * kBinsPerThread;
   const bool f16 = a.f16 != 0;
 
-  uint32_t sum = 0, nz = 0;
+  uint32_t sum = 0;
 #pragma unroll
-  for (int i = 0; i < kBinsPerThread; ++i) {
-    sum += c[i];
-    nz += c[i] ? 1u : 0u;
-  }
+  for (int i = 0; i < kBinsPerThread; ++i) sum += c[i];
   uint2 tot;
-  const uint2 pj = block_exclusive_scan2(make_uint2(sum, nz), ctl, &tot);
-  const uint32_t pre0 = pj.x, j0 = pj.y, distinct = tot.y;
+  const uint32_t pre0 = block_exclusive_scan2(make_uint2(sum, 0u), ctl, &tot).x;
+  // the keys holding ranks K - 1 and t - 1: the first of the thread's keys whose inc[] passes
+  // the rank is its (number of keys with inc[] <= rank)-th; the thread whose keys hold the
+  // rank writes it
+  {
+    const uint32_t r0 = a.K - 1, r1 = a.t - 1;
+    uint32_t run = pre0, n0 = 0, n1 = 0;
+    // only the threads holding a rank count (inside a branch the unrolled loop keeps to its
+    // own registers; in straight-line code it spilled)
+    if ((pre0 <= r0 && r0 - pre0 < sum) || (pre0 <= r1 && r1 - pre0 < sum)) {
+#pragma unroll
+      for (int i = 0; i < kBinsPerThread; ++i) {
+        run = opaque(run + c[i]);
+        n0 += run <= r0 ? 1u : 0u;
+        n1 += run <= r1 ? 1u : 0u;
+      }
+    }
+    if (pre0 <= r0 && r0 < run) ctl[kCtlRanks] = static_cast<uint32_t>(bin0) + n0;
+    if (pre0 <= r1 && r1 < run) ctl[kCtlRanks + 1] = static_cast<uint32_t>(bin0) + n1;
+  }
+  __syncthreads();
+  const uint32_t a_max = ctl[kCtlRanks], m_min = ctl[kCtlRanks + 1];
+  // the thread's listed keys: bin0 + i with i < cut_lo (at most a_max) or i >= cut_hi (at
+  // least m_min); each loop below takes the cuts through opaque(), so that the compiler
+  // does not keep 64 predicates live from one loop to the next
+  const uint32_t ub0 = static_cast<uint32_t>(bin0);
+  const uint32_t cut_lo = a_max >= ub0 ? min(a_max - ub0 + 1, static_cast<uint32_t>(kBinsPerThread)) : 0u;
+  const uint32_t cut_hi = m_min > ub0 ? min(m_min - ub0, static_cast<uint32_t>(kBinsPerThread)) : 0u;
+  uint32_t nz = 0;
+  {
+    const uint32_t lo = opaque(cut_lo), hi = opaque(cut_hi);
+#pragma unroll
+    for (int i = 0; i < kBinsPerThread; ++i)
+      nz += (c[i] && (static_cast<uint32_t>(i) < lo || static_cast<uint32_t>(i) >= hi)) ? 1u : 0u;
+  }
+  const uint32_t j0 = block_exclusive_scan2(make_uint2(nz, 0u), ctl, &tot).x;
+  const uint32_t distinct = tot.x;
   const bool in_lds = distinct <= static_cast<uint32_t>(kWinCap);
 
   uint64_t best = ~uint64_t{0};
   uint32_t best_hi = 0;
   if (in_lds) {
     uint32_t run = pre0, j = j0;
+    const uint32_t lo = opaque(cut_lo), hi = opaque(cut_hi);
 #pragma unroll
     for (int i = 0; i < kBinsPerThread; ++i) {
-      if (c[i]) {
-        run += c[i];
+      run = opaque(run + c[i]);
+      if (c[i] && (static_cast<uint32_t>(i) < lo || static_cast<uint32_t>(i) >= hi)) {
         inc_l[j] = run;
         key_l[j] = static_cast<uint16_t>(bin0 + i);
         ++j;
       }
     }
     __syncthreads();
-    // candidates: each distinct value a whose first index f(a) is below K; the window's
+    // candidates: each listed value a whose first index f(a) is below K; the window's
     // upper end is the smallest key m with inc[m] > f(a) + t - 1
     for (uint32_t j = static_cast<uint32_t>(tid); j < distinct; j += kHistThreads) {
       const uint32_t f = j ? inc_l[j - 1] : 0u;
@@ -380,38 +430,122 @@ __device__ void window_from_counts(uint32_t (&c)[kBinsPerThread], uint32_t* lds,
       }
     }
   } else {
-    // inc[] over all bins in global memory (each thread writes its own 64 bins)
-    __syncthreads();
-    uint32_t run = pre0;
+    // Too many values for the list (float16 heads reach tens of thousands of distinct values
+    // at ratios far from 1).  inc[] of every key goes to LDS as a 32-bit prefix per 16-key
+    // group plus each key's 16-bit inclusive prefix inside its group; a group of more than
+    // 65535 values keeps its keys' inc[] in inc_g instead.  The upper ends come from merging
+    // two ascending sequences, A = inc[m] for keys m >= m_min and B = min(f(a), K) + t - 1
+    // for keys a <= a_max: merged with A first on ties, B[a] is preceded by exactly the
+    // A[m] <= B[a], so m_min plus their number is the smallest m with inc[m] > B[a], the
+    // upper end of a's window (for a candidate, f(a) < K and B[a] = f(a) + t - 1 < N =
+    // inc[65535]; clamping f(a) at K keeps B ascending and below 2^32; every A[m] left out
+    // below m_min is <= t - 1 <= B[a]).  Each thread emits an equal share of the merge from
+    // the split its diagonal gives (merge path).
+    //
+    // Both arrays are stored XOR-swizzled: in the search, the lanes of a wave sit a few dozen
+    // keys apart, which unswizzled would put many lanes' 16-bit reads in one LDS bank.  Key k
+    // lives at p16[k ^ (((k >> 6) & 31) << 1)] and group g's prefix at gpre[g ^ ((g >> 5) & 3)];
+    // both permute only inside a thread's own 64 keys / 4 groups.
+    uint16_t* p16 = reinterpret_cast<uint16_t*>(lds + kCtlWords);  // [65536] prefix inside the group
+    uint32_t* gpre = lds + kCtlWords + kBins / 2;                    // [4097] values below each group; N
+    {
+      uint32_t run = pre0;
+      const uint32_t m = (static_cast<uint32_t>(tid) & 31u) << 1;    // the swizzle of this thread's keys
+      uint4* dst = reinterpret_cast<uint4*>(p16 + bin0);
 #pragma unroll
-    for (int i = 0; i < kBinsPerThread; ++i) {
-      run += c[i];
-      inc_g[bin0 + i] = run;
-    }
-    __threadfence();
-    __syncthreads();
-    uint32_t f = pre0;
-    for (int i = 0; i < kBinsPerThread; ++i) {
-      const uint32_t kl = static_cast<uint32_t>(bin0 + i);
-      const uint32_t inc_k = __hip_atomic_load(inc_g + kl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (inc_k > f && f < a.K) {
-        const uint32_t r = f + a.t - 1;
-        uint32_t lo_i = kl, hi_i = kBins - 1;
-        while (lo_i < hi_i) {
-          const uint32_t mid = (lo_i + hi_i) >> 1;
-          const uint32_t im = __hip_atomic_load(inc_g + mid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if (im > r) hi_i = mid; else lo_i = mid + 1;
+      for (int q = 0; q < kBinsPerThread / 16; ++q) {  // the thread's four groups
+        const uint32_t g0 = run;
+        gpre[(tid * (kBinsPerThread / 16) + q) ^ ((tid >> 3) & 3)] = g0;
+        uint32_t tsum = 0;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) tsum += c[16 * q + e];
+        const bool heavy = tsum > 0xffffu;
+        uint32_t w[8];
+        uint32_t in = 0;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          in = opaque(in + c[16 * q + e]);
+          if (heavy) inc_g[bin0 + 16 * q + e] = g0 + in;
+          w[e >> 1] = (e & 1) ? (w[e >> 1] | ((in & 0xffffu) << 16)) : (in & 0xffffu);
         }
-        const float len = value16(lo_i, f16) - value16(kl, f16);
-        const uint64_t cand = (static_cast<uint64_t>(__float_as_uint(len)) << 32) | kl;
-        if (cand < best) {
-          best = cand;
-          best_hi = (kl << 16) | lo_i;
+        // keys 16q + 8h + e (h = 0, 1) go to the 8-key slot (2q + h) ^ (m >> 3), dword (e >> 1) ^ ((m >> 1) & 3)
+        const uint32_t pd = (m >> 1) & 3u;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          uint32_t x0 = w[4 * h], x1 = w[4 * h + 1], x2 = w[4 * h + 2], x3 = w[4 * h + 3];
+          if (pd & 1u) {  // dword p takes dword p ^ pd: swap pairs, then halves
+            const uint32_t t0 = x0, t2 = x2;
+            x0 = x1; x1 = t0; x2 = x3; x3 = t2;
+          }
+          if (pd & 2u) {
+            const uint32_t t0 = x0, t1 = x1;
+            x0 = x2; x1 = x3; x2 = t0; x3 = t1;
+          }
+          dst[(2 * q + h) ^ (m >> 3)] = make_uint4(x0, x1, x2, x3);
         }
+        run = g0 + tsum;
       }
-      f = inc_k;
+      if (tid == kHistThreads - 1) gpre[kBins / 16] = run;  // unswizzled: (4096 >> 5) & 3 == 0
+    }
+    // the barrier orders the workgroup's global stores too: no device-scope fence (on a chip
+    // of several L2 caches that would write back and invalidate this one's L2)
+    __syncthreads();
+    // inc[k] in one LDS round trip (the three reads issue together; the empty asm keeps the
+    // 16-bit read ahead of the rare branch to global memory)
+    auto inc_at = [&](uint32_t k) -> uint32_t {
+      const uint32_t g = k >> 4;
+      const uint32_t e0 = gpre[g ^ ((g >> 5) & 3u)], e1 = gpre[(g + 1) ^ (((g + 1) >> 5) & 3u)];
+      uint32_t v = e0 + static_cast<uint32_t>(p16[k ^ (((k >> 6) & 31u) << 1)]);
+      __asm__ volatile("" : "+v"(v));
+      if (e1 - e0 > 0xffffu) v = inc_g[k];
+      return v;
+    };
+    auto b_of = [&](uint32_t exc) -> uint32_t { return min(exc, a.K) + a.t - 1; };
+    const uint32_t nA = static_cast<uint32_t>(kBins) - m_min, nB = a_max + 1;
+    const uint32_t total = nA + nB;
+    const uint32_t per = (total + kHistThreads - 1) / kHistThreads;  // merge outputs per thread, <= 128
+    const uint32_t d = min(static_cast<uint32_t>(tid) * per, total);
+    const uint32_t steps = min(per, total - d);
+    uint32_t lo_i = d > nB ? d - nB : 0u;
+    uint32_t hi_i = min(d, nA);
+    while (lo_i < hi_i) {  // the most A elements among the first d outputs
+      const uint32_t mid = (lo_i + hi_i + 1) >> 1;
+      const uint32_t y = d - mid;  // < nB, since mid > d - nB
+      const uint32_t am = inc_at(m_min + mid - 1), by = inc_at(y ? y - 1 : 0u);
+      if (am <= b_of(y ? by : 0u)) lo_i = mid; else hi_i = mid - 1;
+    }
+    // The walk: one merge output per step without divergence -- the step's choice picks the
+    // key whose inc[] is read next (the next A key after an A, j + 1 after a B), so every
+    // lane issues one read per step.  Within a thread's outputs A and B are never both
+    // exhausted, so a B step always has j < nB, and a candidate's upper end is a key of A
+    // since B[j] < inc[65535].
+    uint32_t i = lo_i, j = d - lo_i;
+    uint32_t ai = inc_at(min(m_min + i, static_cast<uint32_t>(kBins) - 1));
+    uint32_t ej = j ? inc_at(j - 1) : 0u;                             // f(j): values below key j
+    uint32_t ij = inc_at(min(j, static_cast<uint32_t>(kBins) - 1));   // inc[j]
+    for (uint32_t step = 0; step < steps; ++step) {
+      const bool take_a = i < nA && (j >= nB || ai <= b_of(ej));
+      // a B step on a key that holds values with f(j) < K: a candidate window [key j, key m_min + i]
+      const uint32_t ku = (m_min + i) & 0xffffu;
+      const bool cand_ok = !take_a && ij > ej && ej < a.K;
+      const float len = value16(ku, f16) - value16(j & 0xffffu, f16);
+      const uint64_t cand = (static_cast<uint64_t>(__float_as_uint(len)) << 32) | j;
+      if (cand_ok && cand < best) {
+        best = cand;
+        best_hi = (j << 16) | ku;
+      }
+      const uint32_t v = inc_at(min(take_a ? m_min + i + 1 : j + 1, static_cast<uint32_t>(kBins) - 1));
+      if (take_a) {
+        ++i;
+        ai = v;  // past the end: never read again
+      } else {
+        ++j;
+        ej = ij;
+        ij = v;
+      }
     }
   }
+
   // lengths are >= +0, so their bits order as unsigned: the smallest (length, index) wins
   uint64_t m = best;
 #pragma unroll
@@ -443,8 +577,8 @@ __device__ void window_from_counts(uint32_t (&c)[kBinsPerThread], uint32_t* lds,
 // LDS of the counting kernel (static, so the histogram's address folds into each atomic's
 // offset): the packed counters, the wrap log and its count; with kWhole the same LDS then
 // serves the window search of the head.
-constexpr int kHistSmemWords = std::max<int>(kBins / 2 + kMaxEvents + 16,
-                                             kCtlWords + kWinCap + kWinCap / 2);
+constexpr int kHistSmemWords = std::max<int>(std::max<int>(kBins / 2 + kMaxEvents + 16, kCtlWords + kWinCap + kWinCap / 2),
+                                             kMergeWords);
 static_assert(static_cast<size_t>(kHistSmemWords) * 4 <= kLdsLimit, "LDS budget");
 
 // kWhole: one part per head (P = 1); the workgroup holds the head's whole histogram and
@@ -482,15 +616,14 @@ __global__ __launch_bounds__(kHistThreads) void calib_hist_kernel(HistArgs a) {
     uint32_t c[kBinsPerThread];
 #pragma unroll
     for (int i = 0; i < kBinsPerThread; ++i) c[i] = 0;
-    add_packed(c, hist, dw0);
+    add_packed(c, hist, dw0, bin0 < 0x8000);
     const uint32_t ne = *nev;
     __syncthreads();  // every thread has its counts: the LDS is free again
     if (ne) {
       zero_hist(hist);
       __syncthreads();
-      add_wraps(c, hist, dw0, ev, ne);
+      add_wraps(c, hist, dw0, bin0 < 0x8000, ev, ne);
     }
-    to_key_order(c, bin0);
     window_from_counts(c, smem, a.hist + static_cast<int64_t>(bh) * a.head_words, a, bh);
   } else {
     // the part's record: the packed counters, the header and the wrap log
@@ -519,7 +652,7 @@ __global__ __launch_bounds__(kHistThreads) void calib_hist_window_kernel(HistArg
   uint32_t n_events = 0;
   for (int p = 0; p < a.P; ++p) {
     const uint32_t* rec = hs + static_cast<int64_t>(p) * kPartWords;
-    add_packed(c, rec, dw0);
+    add_packed(c, rec, dw0, bin0 < 0x8000);
     n_events += rec[kPartPacked + kHdrEvents];
   }
   if (n_events) {
@@ -528,10 +661,9 @@ __global__ __launch_bounds__(kHistThreads) void calib_hist_window_kernel(HistArg
       const uint32_t* rec = hs + static_cast<int64_t>(p) * kPartWords;
       zero_hist(cnt);
       __syncthreads();
-      add_wraps(c, cnt, dw0, rec + kPartPacked + 64, rec[kPartPacked + kHdrEvents]);
+      add_wraps(c, cnt, dw0, bin0 < 0x8000, rec + kPartPacked + 64, rec[kPartPacked + kHdrEvents]);
     }
   }
-  to_key_order(c, bin0);
   window_from_counts(c, lds, hs, a, bh);
 }
 

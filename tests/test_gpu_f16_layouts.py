@@ -118,6 +118,41 @@ def test_calibrate_ex_degenerate_heads_bshd(fa):
         _check_windows(fa, [x], ratio, "BSHD", "degenerate heads")
 
 
+def _many_distinct(shape_bhsd, seed, heavy=None):
+    """float16 values spread log-uniformly over 16 binades of either sign: more distinct 16-bit
+    patterns per head than the window search keeps as a list (so it takes the merge search);
+    `heavy` = (head, count) repeats one value that many times in that head."""
+    g = np.random.default_rng(seed)
+    vals = np.exp2(g.uniform(-8.0, 8.0, size=shape_bhsd)) * np.where(g.random(shape_bhsd) < 0.5, -1.0, 1.0)
+    x = torch.from_numpy(vals.astype(np.float16))
+    if heavy is not None:
+        h, count = heavy
+        flat = x[:, h].reshape(-1)
+        flat[g.choice(flat.numel(), size=count, replace=False)] = 0.75
+        x[:, h] = flat.reshape(x[:, h].shape)
+    return x
+
+
+MANY = [
+    # (what, layout, (B,H,S,D) head-major, heavy)
+    ("one part", "BSHD", (2, 4, 2048, 128), None),
+    ("two parts", "BHSD", (2, 4, 4096, 128), None),
+    ("two parts, a value 100k times", "BHSD", (2, 4, 4096, 128), (1, 100000)),
+    ("one part, a value 70k times", "BSHD", (2, 4, 2048, 128), (2, 70000)),
+]
+
+
+@pytest.mark.parametrize("case", MANY, ids=[c[0] for c in MANY])
+def test_calibrate_ex_many_distinct_f16(fa, case):
+    what, layout, shape, heavy = case
+    x = _many_distinct(shape, seed=940 + len(what), heavy=heavy)
+    for h in range(shape[1]):
+        assert len(np.unique(x[:, h].numpy().view(np.uint16))) > 24576  # past the list the search keeps
+    x = (x if layout == "BHSD" else _bshd(x)).to(DEV)
+    for ratio in (0.9999, 0.99, 0.5, 1.0):
+        _check_windows(fa, [x], ratio, layout, f"many distinct, {what}")
+
+
 @pytest.mark.parametrize("layout", ["BHSD", "BSHD"])
 def test_calibrate_ex_running_statistics(fa, layout):
     B, H, S, D = 2, 4, 512, 64

@@ -573,12 +573,13 @@ def run(args, only, pool, workers) -> int:
         del table
 
     if "f16_bshd" in only:
-        # the step's three streaming stages on float16 tensors in the (B,S,H,D) layout: the calibration
-        # batches, K and the decode cache transposed and converted once, outside the timing
+        # the step's three streaming stages on float16 tensors in the (B,S,H,D) layout, drawn in float16
+        # with the step's recipes and laid out once, outside the timing
         def f16_bshd(t):
-            return t.transpose(1, 2).contiguous().to(torch.float16)
+            return t.transpose(1, 2).contiguous()
 
-        calib_t = [f16_bshd(x) for x in calib]
+        calib_t = [f16_bshd(synth.activations(CAL_SHAPE, sigma, law="t3", dtype=torch.float16, seed=100 + i,
+                                              device=dev)) for i in range(CAL_BATCHES)]
         ws_t = torch.empty(max(1, fa.fa3q_calibrate_ex_workspace_bytes(torch.float16, "BSHD", CAL_BATCHES,
                                                                        *CAL_SHAPE, RATIO)),
                            dtype=torch.uint8, device=dev)
@@ -590,14 +591,17 @@ def run(args, only, pool, workers) -> int:
                                                   "float16 (B,S,H,D) through fa3q_calibrate_ex (histogram path; "
                                                   "outside the step)")
         del calib_t, ws_t
-        k_t = f16_bshd(k)
+        k_t = f16_bshd(synth.activations((QB, H, QS, DN + DR), sigma, law="normal", outlier_frac=0.0005,
+                                         outlier_mult=40.0, dtype=torch.float16, seed=200, device=dev))
         kq_t = torch.empty((QB, QS, H, DN), dtype=torch.int8, device=dev)
         kr_t = torch.empty((QB, QS, H, DR), dtype=torch.float16, device=dev)
         qt_ms = timed(lambda: fa.fa3q_quantize_k_ex(k_t, scale, DN, "BSHD", kq_t, kr_t, stream=stream))
         breakdown["quantize_f16_bshd"] = hbm_row(qt_ms, QUANT_BYTES, "K (64,4096,128,128+64) float16 (B,S,H,D) "
                                                  "through fa3q_quantize_k_ex (outside the step)")
         del k_t
-        v_t, q_t = f16_bshd(v), q.to(torch.float16)
+        v_t = f16_bshd(synth.activations((QB, H, QS, DV), sigma, law="normal", dtype=torch.float16, seed=300,
+                                         device=dev))
+        q_t = synth.normal_tensor((QB, H, DN + DR), dtype=torch.float16, seed=400, device=dev)
         dt_ms = timed(lambda: fa.fa3q_decode_attn_ex(q_t, kq_t, scale, kr_t, v_t, sm, "BSHD", out, ws_dec,
                                                      stream=stream))
         breakdown["decode_f16_bshd"] = hbm_row(dt_ms, DEC_BYTES, "B=64 H=128 T=4096 cache in (B,T,H,.) with float16 "

@@ -20,12 +20,18 @@
 // which become k-slots 8g .. 8g+7; V^T is stored in LDS with its tokens in that order, so
 // one 8-byte read gives the matching A operand.
 //
-// A workgroup is four waves (64 heads, 16 per wave) of one sequence over one run of tokens
-// (a split).  Per tile of 32 tokens the workgroup widens the INT8 latent rows to bf16
-// (exact) once and stages them twice in LDS, row-major for the first product and
-// transposed for the second (a 4x4 byte transpose in registers), plus the bf16 RoPE rows;
-// the next tile's global loads are issued before the current tile is computed.  The
-// wave's query stays in registers for the whole split, with the Dl/16 output tiles.  The
+// A workgroup is eight waves of one sequence over one run of tokens (a split): four pairs
+// of waves, 16 heads per pair (64 heads).  The two waves of a pair split the work of their
+// heads in halves: each computes the first product over half of the k-steps (half the
+// latent dims and half the RoPE dims) and exchanges its partial scores with the other
+// through LDS, so both hold the same scores and weights; each then accumulates half of the
+// output dims.  Two waves run on every SIMD, so one computes while the other waits, and
+// each wave holds half the query and half the output tiles in registers.  Per tile of 32
+// tokens the workgroup widens the INT8 latent rows to bf16 (exact) once and stages them
+// twice in LDS, row-major for the first product and transposed for the second (a 4x4 byte
+// transpose in registers), plus the bf16 RoPE rows (the latent units and the RoPE chunks
+// go to different threads); the next tile's global loads are issued before the current
+// tile is computed.  The
 // output is rescaled only when a head's running max grows by more than 2^8.  Splits leave
 // (max reference, sum, s * unnormalised output) in the workspace; a combine kernel merges
 // them.
@@ -46,7 +52,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kLatThreads = 256;  // four waves, 16 heads each
+constexpr int kLatThreads = 512;  // eight waves: four pairs of 16 heads
 constexpr int kLatHeads = 64;     // heads per workgroup
 constexpr int kTT = 32;           // tokens per tile
 // A workgroup's two LDS buffers (157 KB at the MLA shape) leave room for one per CU, so
@@ -73,9 +79,9 @@ struct LatentArgs {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
-// Staged operands of one tile: 4 tokens x 16 latent dims and one 16-byte RoPE chunk.
+// Staged operands of one tile: 2 tokens x 16 latent dims and one 16-byte RoPE chunk.
 struct LatentStage {
-  u32x4v x[4];
+  u32x4v x[2];
   u32x4v r;
 };
 
@@ -106,20 +112,31 @@ __global__ __launch_bounds__(kLatThreads) void latent_split_kernel(LatentArgs a)
   constexpr int KL = DL / 32;          // k-steps of the latent part of S
   constexpr int KR = DR / 32;          // k-steps of the RoPE part
   constexpr int MT = DL / 16;          // 16-dim tiles of the output
+  // each wave of a pair: latent k-steps [half*KLH, (half+1)*KLH), RoPE k-steps
+  // [half*KRH, ...) (an odd KR leaves the last one to the second wave), output tiles
+  // [half*MTH, (half+1)*MTH)
+  constexpr int KLH = KL / 2;
+  constexpr int KRH = (KR + 1) / 2;    // RoPE k-step registers per wave
+  constexpr int MTH = MT / 2;
+  static_assert(KL % 2 == 0 && MT % 2 == 0, "the pair splits the latent k-steps and the output tiles in halves");
   constexpr int KROW = DL + 8;         // bf16 per row-major latent row in LDS
   constexpr int RROW = DR + 8;         // bf16 per RoPE row in LDS
   constexpr int VROW = kTT;            // bf16 per transposed latent row in LDS (unpadded: measured
                                        // 1.6% faster than kTT + 8; rows of Dl + 8 keep their pad)
   constexpr int DC = DL / 16;          // 16-byte chunks per latent row
-  constexpr int UNITS = (kTT / 4) * DC;  // (4 tokens x 16 dims) staging units per tile
+  constexpr int UNITS = (kTT / 2) * DC;  // (2 tokens x 16 dims) staging units per tile
   constexpr int UPT = (UNITS + kLatThreads - 1) / kLatThreads;  // units per thread
   constexpr int RCH = kTT * DR / 8;    // 16-byte RoPE chunks per tile
   static_assert(RCH <= kLatThreads, "one RoPE chunk per thread");
+  // the RoPE chunks go to the last RCH threads, past the latent units when both fit
+  constexpr int RT0 = kLatThreads - RCH;
   constexpr float kLazy = 8.0f;        // log2 headroom before the output is rescaled
   // two buffers: the next tile is staged while this one is read
   __shared__ __align__(16) uint16_t klat_buf[2][kTT * KROW];
   __shared__ __align__(16) uint16_t vt_buf[2][DL * VROW];
   __shared__ __align__(16) uint16_t krope_buf[2][DR > 0 ? kTT * RROW : 8];
+  // each wave's partial scores for its pair partner: [wave][value][lane], 16 KiB
+  __shared__ __align__(16) float xch[kLatThreads / kWave][8][kWave];
 
   const int tid = static_cast<int>(threadIdx.x);
   const int wave = tid / kWave;
@@ -130,7 +147,8 @@ __global__ __launch_bounds__(kLatThreads) void latent_split_kernel(LatentArgs a)
   const int rest = static_cast<int>(blockIdx.x / a.nsplit);
   const int grp = rest % a.groups;
   const int b = rest / a.groups;
-  const int head = grp * kLatHeads + wave * 16 + hl;
+  const int pair = wave & 3, half = wave >> 2;  // the partner is wave ^ 4
+  const int head = grp * kLatHeads + pair * 16 + hl;
   const bool hv = head < a.H;
   const int64_t t_begin = static_cast<int64_t>(split) * a.split_len;
   const int64_t t_end = min(a.T, t_begin + a.split_len);
@@ -144,17 +162,18 @@ __global__ __launch_bounds__(kLatThreads) void latent_split_kernel(LatentArgs a)
     for (int k = 0; k < UPT; ++k) {
       const int u = tid + k * kLatThreads;
       if (UNITS % kLatThreads == 0 || u < UNITS) {  // folds when every thread has a unit
-        const int tg = u % (kTT / 4), dc = u / (kTT / 4);  // token group fastest: spreads LDS banks
+        const int tg = u % (kTT / 2), dc = u / (kTT / 2);  // token pair fastest
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int64_t tok = min(t0 + 4 * tg + r, t_end - 1);
+        for (int r = 0; r < 2; ++r) {
+          const int64_t tok = min(t0 + 2 * tg + r, t_end - 1);
           st[k].x[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(cbase + tok * DL + 16 * dc));
         }
       }
     }
     if constexpr (DR > 0) {
-      if (RCH == kLatThreads || tid < RCH) {
-        const int r = tid / (DR / 8), k8 = tid - r * (DR / 8);
+      if (tid >= RT0) {
+        const int rt = tid - RT0;
+        const int r = rt / (DR / 8), k8 = rt - r * (DR / 8);
         const int64_t tok = min(t0 + r, t_end - 1);
         st[0].r = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(rbase + tok * DR + 8 * k8));
       }
@@ -169,60 +188,67 @@ __global__ __launch_bounds__(kLatThreads) void latent_split_kernel(LatentArgs a)
     for (int k = 0; k < UPT; ++k) {
       const int u = tid + k * kLatThreads;
       if (UNITS % kLatThreads == 0 || u < UNITS) {  // folds when every thread has a unit
-        const int tg = u % (kTT / 4), dc = u / (kTT / 4);  // token group fastest: spreads LDS banks
+        const int tg = u % (kTT / 2), dc = u / (kTT / 2);  // token pair fastest
         // each code is converted once; the row-major copy pairs neighbouring dims of a
-        // token, the transposed copy neighbouring tokens of a dim
-        float f[4][16];
+        // token, the transposed copy the two tokens of a dim
+        float f[2][16];
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
+        for (int r = 0; r < 2; ++r)
 #pragma unroll
           for (int j = 0; j < 16; ++j) f[r][j] = code_f32(st[k].x[r][j / 4], j % 4);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
+        for (int r = 0; r < 2; ++r) {
           uint32_t h[8];
 #pragma unroll
           for (int i = 0; i < 8; ++i) h[i] = pack_bf16(f[r][2 * i], f[r][2 * i + 1]);
-          uint16_t* row = klat + (4 * tg + r) * KROW + 16 * dc;
+          uint16_t* row = klat + (2 * tg + r) * KROW + 16 * dc;
           *reinterpret_cast<uint4*>(row) = make_uint4(h[0], h[1], h[2], h[3]);
           *reinterpret_cast<uint4*>(row + 8) = make_uint4(h[4], h[5], h[6], h[7]);
         }
-        // token offset t = 4tg + r (tg = 4*b4 + (b3 b2))  ->  position 8*(b3 b2) + 4*b4 + r
-        const int pos = 8 * (tg & 3) + 4 * (tg >> 2);
+        // token t = 2tg + r sits at k-slot position 8*((t >> 2) & 3) + 4*(t >> 4) + (t & 3) of
+        // its transposed row; the row's 16-byte chunks are XOR-swizzled by (row >> 4) & 3
+        // (= dc & 3), so the four rows a wave writes at once fall in different banks
+        const int pos = 8 * ((tg >> 1) & 3) + 4 * (tg >> 3) + 2 * (tg & 1);
+        const int spos = (((pos >> 3) ^ (dc & 3)) << 3) | (pos & 7);
 #pragma unroll
         for (int j = 0; j < 16; ++j)
-          *reinterpret_cast<uint2*>(vt + (16 * dc + j) * VROW + pos) =
-              make_uint2(pack_bf16(f[0][j], f[1][j]), pack_bf16(f[2][j], f[3][j]));
+          *reinterpret_cast<uint32_t*>(vt + (16 * dc + j) * VROW + spos) = pack_bf16(f[0][j], f[1][j]);
       }
     }
     if constexpr (DR > 0) {
-      if (RCH == kLatThreads || tid < RCH) {
-        const int r = tid / (DR / 8), k8 = tid - r * (DR / 8);
+      if (tid >= RT0) {
+        const int rt = tid - RT0;
+        const int r = rt / (DR / 8), k8 = rt - r * (DR / 8);
         *reinterpret_cast<u32x4v*>(krope + r * RROW + 8 * k8) = st[0].r;
       }
     }
   };
 
-  // the wave's query as B operands (Q^T: dims x heads): lane holds dims 32kk + 8lg .. +7
-  bf16x8 ql[KL];
-  bf16x8 qr[KR > 0 ? KR : 1];
+  // the wave's half of the query as B operands (Q^T: dims x heads): lane holds dims
+  // 32kk + 8lg .. +7 of its k-steps; a RoPE k-step past KR (odd KR, first wave) stays zero
+  const int kl0 = half * KLH, kr0 = half * (KR / 2);
+  const int nkr = half ? KR - KR / 2 : KR / 2;  // RoPE k-steps of this wave
+  bf16x8 ql[KLH];
+  bf16x8 qr[KRH > 0 ? KRH : 1];
   {
     const uint16_t* qrow = a.q + (static_cast<int64_t>(b) * a.H + (hv ? head : 0)) * (DL + DR);
 #pragma unroll
-    for (int kk = 0; kk < KL; ++kk) {
-      const uint4 u = hv ? *reinterpret_cast<const uint4*>(qrow + 32 * kk + 8 * lg) : make_uint4(0, 0, 0, 0);
+    for (int kk = 0; kk < KLH; ++kk) {
+      const uint4 u = hv ? *reinterpret_cast<const uint4*>(qrow + 32 * (kl0 + kk) + 8 * lg) : make_uint4(0, 0, 0, 0);
       ql[kk] = as_bf16x8(u);
     }
 #pragma unroll
-    for (int kk = 0; kk < KR; ++kk) {
-      const uint4 u = hv ? *reinterpret_cast<const uint4*>(qrow + DL + 32 * kk + 8 * lg) : make_uint4(0, 0, 0, 0);
+    for (int kk = 0; kk < KRH; ++kk) {
+      const uint4 u = hv && kk < nkr ? *reinterpret_cast<const uint4*>(qrow + DL + 32 * (kr0 + kk) + 8 * lg)
+                                     : make_uint4(0, 0, 0, 0);
       qr[kk] = as_bf16x8(u);
     }
   }
   const float s = a.scale[0];
 
-  f32x4 o[MT];
+  f32x4 o[MTH];  // output dims 16 (half*MTH + mt) + 4lg .. +3
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) o[mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int mt = 0; mt < MTH; ++mt) o[mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   // mu: the reference the weights are taken against (p = 2^(score - mu)); it lags the
   // running max by at most kLazy, so the output is rescaled only when the max has grown
   // by more than that (weights stay <= 2^kLazy, far inside float32 and bf16 range)
@@ -247,8 +273,10 @@ __global__ __launch_bounds__(kLatThreads) void latent_split_kernel(LatentArgs a)
       plo[i] = static_cast<__bf16>(p[i] - static_cast<float>(phi[i]));  // the difference is exact in float32
     }
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const uint4 w = *reinterpret_cast<const uint4*>(vt + (16 * mt + hl) * VROW + 8 * lg);
+    for (int mt = 0; mt < MTH; ++mt) {
+      // (the transposed rows' 16-byte chunks are swizzled by (row >> 4) & 3, uniform here)
+      const uint4 w = *reinterpret_cast<const uint4*>(vt + (16 * (half * MTH + mt) + hl) * VROW +
+                                                      8 * (lg ^ ((half * MTH + mt) & 3)));
       o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w), phi, o[mt], 0, 0, 0);
       o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w), plo, o[mt], 0, 0, 0);
     }
@@ -279,20 +307,22 @@ __global__ __launch_bounds__(kLatThreads) void latent_split_kernel(LatentArgs a)
         sl[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         sr[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int kk = 0; kk < KL; ++kk) {
-          const uint4 w = *reinterpret_cast<const uint4*>(klat + (16 * tt + hl) * KROW + 32 * kk + 8 * lg);
+        for (int kk = 0; kk < KLH; ++kk) {
+          const uint4 w = *reinterpret_cast<const uint4*>(klat + (16 * tt + hl) * KROW + 32 * (kl0 + kk) + 8 * lg);
           sl[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w), ql[kk], sl[tt], 0, 0, 0);
         }
 #pragma unroll
-        for (int kk = 0; kk < KR; ++kk) {
-          const uint4 w = *reinterpret_cast<const uint4*>(krope + (16 * tt + hl) * RROW + 32 * kk + 8 * lg);
+        for (int kk = 0; kk < KRH; ++kk) {
+          // (an odd KR: the first wave's last slot reads a valid row and multiplies zeros)
+          const int kr = min(kr0 + kk, KR - 1);
+          const uint4 w = *reinterpret_cast<const uint4*>(krope + (16 * tt + hl) * RROW + 32 * kr + 8 * lg);
           sr[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w), qr[kk], sr[tt], 0, 0, 0);
         }
       }
       {
         // keep kSDepth operand reads in flight ahead of the score MFMAs (left alone, the
         // scheduler issues each read one MFMA before its use)
-        constexpr int NS = 2 * (KL + KR);
+        constexpr int NS = 2 * (KLH + KRH);
         constexpr int kSDepth = NS < 6 ? NS : 6;
         __builtin_amdgcn_sched_group_barrier(0x100, kSDepth, 0);  // DS reads
 #pragma unroll
@@ -308,6 +338,17 @@ __global__ __launch_bounds__(kLatThreads) void latent_split_kernel(LatentArgs a)
       // bounds) and the staged buffer is never read.
       stage(st, buf ^ 1);
       fetch(t0 + 2 * kTT, st);
+      // ---- the pair's partial scores: each wave's s <q_abs, c> + <q_rope, r> over its
+      // k-steps, exchanged through LDS; both waves add the two in the same order
+      float x[8];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          x[4 * tt + j] = fmaf(s, sl[tt][j], sr[tt][j]);
+          xch[wave][4 * tt + j][lane] = x[4 * tt + j];
+        }
+      __syncthreads();
       // ---- scores (log2 domain) of the lane's head over its 8 tokens (16tt + 4lg + j)
       rmax = -INFINITY;
 #pragma unroll
@@ -315,7 +356,8 @@ __global__ __launch_bounds__(kLatThreads) void latent_split_kernel(LatentArgs a)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int64_t tok = t0 + 16 * tt + 4 * lg + j;
-          const float sc = fmaf(s, sl[tt][j], sr[tt][j]) * a.sm_log2;
+          const float other = xch[wave ^ 4][4 * tt + j][lane];
+          const float sc = (half ? other + x[4 * tt + j] : x[4 * tt + j] + other) * a.sm_log2;
           p[4 * tt + j] = tok < t_end ? sc : -INFINITY;
           rmax = fmaxf(rmax, p[4 * tt + j]);
         }
@@ -332,7 +374,7 @@ __global__ __launch_bounds__(kLatThreads) void latent_split_kernel(LatentArgs a)
     const float alpha = exp2f(mu - mu_new);
     l *= alpha;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) o[mt] *= alpha;
+    for (int mt = 0; mt < MTH; ++mt) o[mt] *= alpha;
     mu = mu_new;
     accumulate(p, vt_buf[buf]);
     __syncthreads();
@@ -349,10 +391,10 @@ __global__ __launch_bounds__(kLatThreads) void latent_split_kernel(LatentArgs a)
   const float f = a.nsplit == 1 ? s / l : s;
   float* dst = a.nsplit == 1 ? a.out + row * DL : a.ws_o + (row * a.nsplit + split) * DL;
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-    *reinterpret_cast<float4*>(dst + 16 * mt + 4 * lg) =
+  for (int mt = 0; mt < MTH; ++mt)
+    *reinterpret_cast<float4*>(dst + 16 * (half * MTH + mt) + 4 * lg) =
         make_float4(o[mt][0] * f, o[mt][1] * f, o[mt][2] * f, o[mt][3] * f);
-  if (a.nsplit > 1 && lg == 0) {
+  if (a.nsplit > 1 && lg == 0 && half == 0) {
     const int64_t slot = row * a.nsplit + split;
     a.ws_ml[2 * slot] = mu;
     a.ws_ml[2 * slot + 1] = l;

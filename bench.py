@@ -58,7 +58,7 @@ LONG_RATIOS = (0.999, 0.9999, 0.99999)
 KERNEL_SOURCES = {
     "quantize_k_kernel": ("quantize.hip", "fa3q_internal.hpp"),
     "decode_split_kernel": ("decode.hip", "fa3q_internal.hpp"),
-    "calib_chunk_kernel": ("calibrate.hip", "fa3q_internal.hpp"),
+    "calib_hist_kernel": ("calib_hist.hip", "calib_hist.hpp", "calibrate.hip", "fa3q_internal.hpp"),
 }
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fa3q_step_hbm_traffic.md")
 
@@ -375,14 +375,14 @@ def run(args, only, pool, workers) -> int:
     breakdown = {
         "calibrate": {"ms": cal_ms, "gelem_s": CAL_BATCHES * CAL_BYTES / 2 / (cal_ms * 1e-3) / 1e9,
                       "gbs": cal_gbs, "frac_hbm": cal_gbs / HBM_PEAK_GBS,
-                      "note": "4 batches in one fa3q_calibrate_batches call: sample, chunk, merge, accumulate"},
+                      "note": "4 batches in one fa3q_calibrate_batches call: per-head histograms, windows, accumulate"},
         "qparams": {"ms": qp_ms},
         "quantize": {"ms": quant_ms, "gbs": quant_gbs, "frac_hbm": quant_gbs / HBM_PEAK_GBS},
         "decode": {"ms": dec_ms, "kv_gbs": dec_gbs, "frac_hbm": dec_gbs / HBM_PEAK_GBS},
     }
     # the kernel with the largest share of the step; its events bracket exactly one launch
     stages = {"quantize_k_kernel": (quant_ms, QUANT_BYTES, 1), "decode_split_kernel": (dec_ms, DEC_BYTES, 1),
-              "calib_chunk_kernel": (cal_ms, CAL_BATCHES * CAL_BYTES, 1)}
+              "calib_hist_kernel": (cal_ms, CAL_BATCHES * CAL_BYTES, 1)}
     dom = max(stages, key=lambda s: stages[s][0] * stages[s][2])
     d_ms, d_bytes, _ = stages[dom]
     achieved = gbs(d_bytes, d_ms)
@@ -390,8 +390,8 @@ def run(args, only, pool, workers) -> int:
     roofline = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "traffic_source": traffic_src,
                 "algorithmic_bytes_per_launch": d_bytes, "avg_launch_ms": d_ms}
-    if dom == "calib_chunk_kernel":
-        roofline["note"] = "calibration: sample, chunk, merge and accumulate kernels, events around all four"
+    if dom == "calib_hist_kernel":
+        roofline["note"] = "calibration: histogram, window and accumulate kernels, events around all of them"
 
     def timed(fn, reps=5):
         for _ in range(2):

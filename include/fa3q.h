@@ -119,8 +119,8 @@ int fa3q_version(void);
  * Largest number of windows K = N - int(ratio*N) + 1 that the streaming tail selection
  * (on-chip lists of the K smallest and K largest values) takes for `dtype`.  16-bit input
  * (bf16, float16) with a larger K, with heads of at least 2^20 values or in the FA3Q_BSHD
- * layout takes the histogram path, which handles every K; float32 input with a larger K
- * returns FA3Q_ERR_UNSUPPORTED.  0 for an unknown dtype.
+ * layout takes the histogram path; float32 input with a larger K or in the FA3Q_BSHD layout
+ * takes the collect-and-sort path.  Both handle every K.  0 for an unknown dtype.
  */
 int64_t fa3q_calibrate_max_windows(int dtype);
 
@@ -154,8 +154,13 @@ size_t fa3q_calibrate_workspace_bytes(int dtype, int64_t B, int64_t H, int64_t S
  * head can bound a window; while K <= fa3q_calibrate_max_windows(dtype) and a head holds
  * fewer than 2^20 values, the kernels select those two tails on chip.  A 16-bit head is
  * otherwise counted into a 65536-bin histogram (its sorted order exactly) and the window
- * found from the counts, for every K.  float32 input with K above
- * fa3q_calibrate_max_windows(FA3Q_F32) -> FA3Q_ERR_UNSUPPORTED.
+ * found from the counts, for every K.  A float32 head with K above
+ * fa3q_calibrate_max_windows(FA3Q_F32) is counted by its values' leading 16 bits, which
+ * fixes the leading bits at ranks K-1 and t-1; a second pass collects every value at or
+ * below the first or at or above the second (both tails, M >= K values), a radix sort
+ * orders them and the K windows are scanned.  That path's workspace holds two lists of N
+ * keys per head (twice the size of a float32 batch), reused by every batch of a call.
+ * No valid ratio is refused.
  */
 int fa3q_calibrate_perhead(const void* x, int dtype, int64_t B, int64_t H, int64_t S, int64_t D,
                            double ratio, float* win_min, float* win_max, void* workspace,
@@ -389,8 +394,9 @@ size_t fa3q_calibrate_batches_workspace_bytes(int dtype, int64_t nb, int64_t B, 
  *   (win_min[b], win_max[b]) = fa3q_calibrate_perhead(xs[b], ...)   (bit for bit)
  *   run_min = min(run_min, win_min[b]), run_max = max(run_max, win_max[b])  (as fa3q_accumulate_minmax)
  * with run_min/run_max starting at (+inf, -inf) when init != 0 (fa3q_init_minmax), at
- * their current contents otherwise.  The batches share each launch: one sample, one
- * streaming pass over all of them, one merge and one accumulation.
+ * their current contents otherwise.  The batches share each launch (one sample, one
+ * streaming pass over all of them, one merge and one accumulation), except on the float32
+ * collect-and-sort path, which takes them one after the other through one workspace region.
  *
  *   xs         HOST array of nb device pointers, each as x of fa3q_calibrate_perhead
  *              (dtype, (B,H,S,D) contiguous, 16-byte aligned); read during the call only.
@@ -562,9 +568,10 @@ size_t fa3q_calibrate_ex_workspace_bytes(int dtype, int layout, int64_t nb, int6
  * or x[b][:, :, h, :] (BSHD), N = B*S*D values, and the windows and running statistics
  * follow.  run_min and run_max may both be NULL when win_min and win_max are given: the
  * windows are then written and no running statistics kept (fa3q_calibrate_perhead for
- * nb = 1).  BSHD rows of D values must be a multiple of 8 (16-bit) values; (B,S,H,D)
- * 16-bit input always takes the histogram path (any K), float32 BSHD input returns
- * FA3Q_ERR_UNSUPPORTED.  Other arguments, alignment and errors as fa3q_calibrate_batches.
+ * nb = 1).  BSHD rows of D values must be a multiple of 8 (16-bit) or 4 (float32) values;
+ * (B,S,H,D) 16-bit input always takes the histogram path and float32 input the
+ * collect-and-sort path (any K; see fa3q_calibrate_perhead).  Other arguments, alignment and
+ * errors as fa3q_calibrate_batches.
  */
 int fa3q_calibrate_ex(const void* const* xs, int64_t nb, int dtype, int layout, int64_t B, int64_t H,
                       int64_t S, int64_t D, double ratio, float* run_min, float* run_max, int init,

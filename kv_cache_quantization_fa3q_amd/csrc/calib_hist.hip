@@ -105,24 +105,43 @@ __device__ __forceinline__ float value16(uint32_t key, bool f16) {
              : __uint_as_float(bits << 16);
 }
 
-// Counts the values of U vectors into the packed LDS histogram (with kAll false, lanes whose
+// The 16-bit patterns a 16-byte vector holds, two per dword: its own eight (16-bit input),
+// or (kF32) the high halves of its four float32 values.  The high half of a float32 value's
+// order-preserving 32-bit key is the 16-bit key of its high-half pattern, so their histogram
+// orders float32 values by their leading 16 bits.
+template <bool kF32>
+__device__ __forceinline__ void pattern_dwords(const uint4& v, uint32_t (&xs)[kF32 ? 2 : 4]) {
+  if constexpr (kF32) {
+    xs[0] = (v.x >> 16) | (v.y & 0xffff0000u);
+    xs[1] = (v.z >> 16) | (v.w & 0xffff0000u);
+  } else {
+    xs[0] = v.x;
+    xs[1] = v.y;
+    xs[2] = v.z;
+    xs[3] = v.w;
+  }
+}
+
+// Counts the patterns of U vectors into the packed LDS histogram (with kAll false, lanes whose
 // valid[u] is false skip vector u).  Pattern p lives in dword p >> 1 (byte offset (p << 1) &
 // 0x1fffc), field p & 1, and is counted by adding 1 << (16 (p & 1)); both come straight
 // from the dword x holding two patterns (a shift amount's low five bits: (x << 4) & 31 is
 // 16 (x & 1)).  A field can only wrap once it holds 0xffff, so while no returned dword has
 // bit 15 of either field set (one OR per increment) no wrap happened; otherwise each
 // increment is looked at and its wraps logged (see the file header).
-template <int U, bool kAll>
+template <int U, bool kAll, bool kF32>
 __device__ __forceinline__ void count_vecs(uint32_t* hist, uint32_t* ev, uint32_t* nev, const uint4 (&v)[U],
                                            const bool (&valid)[U]) {
-  uint32_t o[U][8];  // returned dwords
+  constexpr int W = kF32 ? 2 : 4;  // dwords of patterns per vector
+  uint32_t o[U][2 * W];  // returned dwords
   unsigned char* base = reinterpret_cast<unsigned char*>(hist);
   uint32_t seen = 0;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const uint32_t xs[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+    uint32_t xs[W];
+    pattern_dwords<kF32>(v[u], xs);
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
+    for (int d = 0; d < W; ++d) {
       const uint32_t x = xs[d];
       const uint32_t a0 = (x << 1) & 0x1fffcu, i0 = 1u << ((x << 4) & 31u);
       const uint32_t a1 = (x >> 15) & 0x1fffcu, i1 = 1u << ((x >> 12) & 16u);
@@ -138,9 +157,10 @@ __device__ __forceinline__ void count_vecs(uint32_t* hist, uint32_t* ev, uint32_
   if (seen & 0x80008000u) {  // rare: some field of a touched dword held 0x8000 or more
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const uint32_t xs[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      uint32_t xs[W];
+      pattern_dwords<kF32>(v[u], xs);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < 2 * W; ++i) {
         const uint32_t p = (i & 1) ? (xs[i >> 1] >> 16) : (xs[i >> 1] & 0xffffu);
         const uint32_t oo = o[u][i];
         const bool counted = kAll || valid[u];
@@ -157,11 +177,12 @@ __device__ __forceinline__ void count_vecs(uint32_t* hist, uint32_t* ev, uint32_
   }
 }
 
-// Streams head vectors [q0, q1) of head h in batch xb into the LDS histogram, U vectors per
-// thread in flight, one row segment at a time (rows longer than a round of the workgroup).
-template <int U>
-__device__ __forceinline__ void count_range(const HistArgs& a, const uint4* xb, int h, int64_t q, int64_t q_end,
-                                            uint32_t* hist, uint32_t* ev, uint32_t* nev) {
+// Streams head vectors [q0, q1) of head h in batch xb through f (f.run<kAll>(v, valid) on U
+// vectors per thread in flight), one row segment at a time (rows longer than a round of the
+// workgroup).  Every thread makes the same calls, so f may hold workgroup barriers.
+template <int U, class F>
+__device__ __forceinline__ void stream_range(const HistArgs& a, const uint4* xb, int h, int64_t q, int64_t q_end,
+                                             F& f) {
   const int tid = static_cast<int>(threadIdx.x);
   constexpr int64_t kRound = static_cast<int64_t>(kHistThreads) * U;
   while (q < q_end) {
@@ -178,7 +199,7 @@ __device__ __forceinline__ void count_range(const HistArgs& a, const uint4* xb, 
         valid[u] = true;
         v[u] = load_nt16(src + i0 + u * kHistThreads + tid);
       }
-      count_vecs<U, true>(hist, ev, nev, v, valid);
+      f.template run<true>(v, valid);
     }
     if (i0 < n) {  // the segment's last, partial round
       uint4 v[U];
@@ -189,20 +210,19 @@ __device__ __forceinline__ void count_range(const HistArgs& a, const uint4* xb, 
         valid[u] = i < n;
         v[u] = load_nt16(src + min(i, n - 1));  // in bounds; a re-read vector is not counted
       }
-      count_vecs<U, false>(hist, ev, nev, v, valid);
+      f.template run<false>(v, valid);
     }
     q += n;
   }
 }
 
 // Streams rows [j0, j1) of head h in batch xb (rows of Lv <= kHistThreads vectors, as the
-// (b, s) rows of D values of a (B, S, H, D) tensor) into the LDS histogram.  The workgroup
+// (b, s) rows of D values of a (B, S, H, D) tensor) through f, as stream_range.  The workgroup
 // takes G = kHistThreads / Lv rows per step, thread t vector t % Lv of row t / Lv (threads
 // past G * Lv idle), so a thread's vectors lie a fixed stride apart and need no division;
 // U steps in flight.
-template <int U>
-__device__ __forceinline__ void count_rows(const HistArgs& a, const uint4* xb, int h, int64_t j0, int64_t j1,
-                                           uint32_t* hist, uint32_t* ev, uint32_t* nev) {
+template <int U, class F>
+__device__ __forceinline__ void stream_rows(const HistArgs& a, const uint4* xb, int h, int64_t j0, int64_t j1, F& f) {
   const int tid = static_cast<int>(threadIdx.x);
   const int R = static_cast<int>(a.Lv);
   const int G = kHistThreads / R;
@@ -224,7 +244,7 @@ __device__ __forceinline__ void count_rows(const HistArgs& a, const uint4* xb, i
         valid[u] = true;
         v[u] = load_nt16(mine + (g + u) * stride);
       }
-      count_vecs<U, true>(hist, ev, nev, v, valid);
+      f.template run<true>(v, valid);
     }
   }
   for (; g * G < nrows; g += U) {
@@ -235,9 +255,21 @@ __device__ __forceinline__ void count_rows(const HistArgs& a, const uint4* xb, i
       valid[u] = on && (g + u) * G + rt < nrows;
       v[u] = load_nt16(valid[u] ? mine + (g + u) * stride : first);  // a vector not counted is re-read from row j0
     }
-    count_vecs<U, false>(hist, ev, nev, v, valid);
+    f.template run<false>(v, valid);
   }
 }
+
+// The counting pass's visitor: the vectors' patterns into the packed LDS histogram.
+template <int U, bool kF32>
+struct CountVisit {
+  uint32_t* hist;
+  uint32_t* ev;
+  uint32_t* nev;
+  template <bool kAll>
+  __device__ __forceinline__ void run(const uint4 (&v)[U], const bool (&valid)[U]) {
+    count_vecs<U, kAll, kF32>(hist, ev, nev, v, valid);
+  }
+};
 
 // v, as a value the compiler cannot see through: running sums over the counts built from it
 // cannot be shared between loops, which would keep 64 partial sums live across them
@@ -583,9 +615,11 @@ static_assert(static_cast<size_t>(kHistSmemWords) * 4 <= kLdsLimit, "LDS budget"
 
 // kWhole: one part per head (P = 1); the workgroup holds the head's whole histogram and
 // finds the window itself.  Otherwise it writes its part's record for the window kernel.
-// kRows: rows of at most kHistThreads vectors, parts of whole rows (count_rows).
-template <bool kWhole, bool kRows>
+// kRows: rows of at most kHistThreads vectors, parts of whole rows (stream_rows).  kF32:
+// float32 input, counted by the high halves of its values (records only).
+template <bool kWhole, bool kRows, bool kF32>
 __global__ __launch_bounds__(kHistThreads) void calib_hist_kernel(HistArgs a) {
+  static_assert(!(kWhole && kF32), "float32 heads are counted into records");
   __shared__ uint32_t smem[kHistSmemWords];
   uint32_t* hist = smem;               // [32768] two 16-bit counters per dword
   uint32_t* ev = smem + kBins / 2;     // [kMaxEvents] patterns whose field wrapped
@@ -601,12 +635,13 @@ __global__ __launch_bounds__(kHistThreads) void calib_hist_kernel(HistArgs a) {
   const int bi = bh / a.H;
   const uint4* xb = static_cast<const uint4*>(a.x[bi]);
 
+  CountVisit<kHistUnroll, kF32> f{hist, ev, nev};
   if constexpr (kRows) {
     const int64_t j0 = static_cast<int64_t>(part) * a.part_rows;
-    count_rows<kHistUnroll>(a, xb, h, j0, min(j0 + a.part_rows, a.nrows), hist, ev, nev);
+    stream_rows<kHistUnroll>(a, xb, h, j0, min(j0 + a.part_rows, a.nrows), f);
   } else {
     const int64_t q = static_cast<int64_t>(part) * a.part_vecs;
-    count_range<kHistUnroll>(a, xb, h, q, min(q + a.part_vecs, a.Qv), hist, ev, nev);
+    stream_range<kHistUnroll>(a, xb, h, q, min(q + a.part_vecs, a.Qv), f);
   }
   __syncthreads();
 
@@ -667,15 +702,177 @@ __global__ __launch_bounds__(kHistThreads) void calib_hist_window_kernel(HistArg
   window_from_counts(c, lds, hs, a, bh);
 }
 
+// ---- float32 heads: the cut and the collected tails -------------------------------------
+//
+// A float32 head has too many distinct values for a histogram of its own, but the histogram
+// of its values' leading 16 bits (the high halves of their 32-bit keys) says which leading
+// keys hold ranks K - 1 and t - 1: a_max and m_min.  Every value of rank below K has a
+// leading key <= a_max, every value of rank >= t - 1 one >= m_min, so the values whose
+// leading key is <= a_max or >= m_min hold both tails of the sorted head; sorted, their first
+// K are s[0 .. K-1] and their last K are s[t-1 .. N-1] (any other collected value lies
+// between the two tails).  When a_max >= m_min that is every value of the head.
+
+// One workgroup per head after the parts' records are written: the leading-key counts summed,
+// a_max and m_min found, the number of collected values M, an empty list and no best window.
+__global__ __launch_bounds__(kHistThreads) void calib_cut_kernel(HistArgs a, TailCut* cut, uint64_t* best) {
+  extern __shared__ uint32_t lds[];
+  uint32_t* ctl = lds;              // [kCtlWords] scan scratch, the ranks' keys and prefixes
+  uint32_t* cnt = lds + kCtlWords;  // packed wrap counts (rare)
+  const int tid = static_cast<int>(threadIdx.x);
+  const int64_t bh = blockIdx.x;
+  const uint32_t* hs = a.hist + bh * a.head_words;
+  const int bin0 = tid * kBinsPerThread;
+  const int dw0 = first_dword(bin0);
+  uint32_t c[kBinsPerThread];
+#pragma unroll
+  for (int i = 0; i < kBinsPerThread; ++i) c[i] = 0;
+  uint32_t n_events = 0;
+  for (int p = 0; p < a.P; ++p) {
+    const uint32_t* rec = hs + static_cast<int64_t>(p) * kPartWords;
+    add_packed(c, rec, dw0, bin0 < 0x8000);
+    n_events += rec[kPartPacked + kHdrEvents];
+  }
+  if (n_events) {
+    for (int p = 0; p < a.P; ++p) {
+      const uint32_t* rec = hs + static_cast<int64_t>(p) * kPartWords;
+      zero_hist(cnt);
+      __syncthreads();
+      add_wraps(c, cnt, dw0, bin0 < 0x8000, rec + kPartPacked + 64, rec[kPartPacked + kHdrEvents]);
+    }
+  }
+  uint32_t sum = 0;
+#pragma unroll
+  for (int i = 0; i < kBinsPerThread; ++i) sum += c[i];
+  uint2 tot;
+  const uint32_t pre0 = block_exclusive_scan2(make_uint2(sum, 0u), ctl, &tot).x;
+  // a_max with inc[a_max] (the first inclusive prefix past K - 1), m_min with inc[m_min - 1]
+  // (the last prefix at most t - 1, or the values below the thread's first key)
+  const uint32_t r0 = a.K - 1, r1 = a.t - 1;
+  uint32_t run = pre0, n0 = 0, n1 = 0, inc_a = ~0u, exc_m = pre0;
+  if ((pre0 <= r0 && r0 - pre0 < sum) || (pre0 <= r1 && r1 - pre0 < sum)) {
+#pragma unroll
+    for (int i = 0; i < kBinsPerThread; ++i) {
+      run = opaque(run + c[i]);
+      n0 += run <= r0 ? 1u : 0u;
+      n1 += run <= r1 ? 1u : 0u;
+      inc_a = min(inc_a, run > r0 ? run : ~0u);
+      exc_m = max(exc_m, run <= r1 ? run : 0u);
+    }
+  }
+  if (pre0 <= r0 && r0 < run) {
+    ctl[kCtlRanks] = static_cast<uint32_t>(bin0) + n0;
+    ctl[kCtlRanks + 2] = inc_a;
+  }
+  if (pre0 <= r1 && r1 < run) {
+    ctl[kCtlRanks + 1] = static_cast<uint32_t>(bin0) + n1;
+    ctl[kCtlRanks + 3] = exc_m;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    TailCut tc;
+    tc.a_max = ctl[kCtlRanks];
+    tc.m_min = ctl[kCtlRanks + 1];
+    tc.M = tc.a_max < tc.m_min ? ctl[kCtlRanks + 2] + (tot.x - ctl[kCtlRanks + 3]) : tot.x;
+    tc.fill = 0;
+    cut[bh] = tc;
+    best[bh] = ~uint64_t{0};
+  }
+}
+constexpr size_t kCutLds = (static_cast<size_t>(kCtlWords) + kBins / 2) * 4;
+static_assert(kCutLds <= kLdsLimit, "LDS budget");
+
+// keys a collecting workgroup stages in LDS; it writes them out once a round could overflow
+constexpr uint32_t kCollectCap = 32768;
+constexpr uint32_t kCollectRound = kHistThreads * kHistUnroll * 4;  // float32 values per round
+constexpr uint32_t kCollectFlush = kCollectCap - kCollectRound;
+
+// Unsigned key whose order is the float32 total order with -0.0 below +0.0.
+__device__ __forceinline__ uint32_t key32(uint32_t b) { return (b & 0x80000000u) ? ~b : (b | 0x80000000u); }
+
+// The collecting pass's visitor: the 32-bit keys of the values whose leading key is <= a_max or
+// >= m_min are appended to the LDS stage (one LDS atomic per wave and value slot), which is
+// written to the head's list (one global atomic per write) when another round might not fit.
+template <int U>
+struct CollectVisit {
+  uint32_t* buf;    // LDS [kCollectCap]
+  uint32_t* nbuf;   // LDS: keys staged
+  uint32_t* gbase;  // LDS: list position of a write-out
+  uint32_t a_max, m_min;
+  uint32_t* fill;   // the head's append counter
+  uint32_t* list;   // the head's list
+  __device__ __forceinline__ void flush(uint32_t n) {
+    if (threadIdx.x == 0) {
+      *gbase = atomicAdd(fill, n);
+      *nbuf = 0;
+    }
+    __syncthreads();
+    const uint32_t g = *gbase;
+    for (uint32_t i = threadIdx.x; i < n; i += kHistThreads) list[g + i] = buf[i];
+    __syncthreads();
+  }
+  template <bool kAll>
+  __device__ __forceinline__ void run(const uint4 (&v)[U], const bool (&valid)[U]) {
+    const uint64_t lt = (uint64_t{1} << lane_id()) - 1;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t k = key32(w[e]);
+        const uint32_t lead = k >> 16;
+        const bool sel = (kAll || valid[u]) && (lead <= a_max || lead >= m_min);
+        const uint64_t m = __ballot(sel);
+        if (m) {
+          const int leader = __builtin_ctzll(m);
+          uint32_t base = 0;
+          if (lane_id() == leader) base = atomicAdd(nbuf, static_cast<uint32_t>(__popcll(m)));
+          base = __builtin_amdgcn_readlane(base, leader);
+          if (sel) buf[base + static_cast<uint32_t>(__popcll(m & lt))] = k;
+        }
+      }
+    }
+    __syncthreads();
+    const uint32_t n = *nbuf;
+    __syncthreads();  // every thread has read the count before the next round appends
+    if (n > kCollectFlush) flush(n);
+  }
+};
+
+// The parts of the counting pass again, one workgroup each: the head's tail values into its list.
+template <bool kRows>
+__global__ __launch_bounds__(kHistThreads) void calib_collect_kernel(HistArgs a, TailCut* cut, uint32_t* lists,
+                                                                      int64_t stride) {
+  __shared__ uint32_t buf[kCollectCap];
+  __shared__ uint32_t misc[2];
+  const int part = static_cast<int>(blockIdx.x) % a.P;
+  const int bh = static_cast<int>(blockIdx.x) / a.P;  // one batch: the head
+  const uint4* xb = static_cast<const uint4*>(a.x[0]);
+  if (threadIdx.x == 0) misc[0] = 0;
+  __syncthreads();
+  CollectVisit<kHistUnroll> f{buf, misc, misc + 1, cut[bh].a_max, cut[bh].m_min, &cut[bh].fill,
+                              lists + static_cast<int64_t>(bh) * stride};
+  if constexpr (kRows) {
+    const int64_t j0 = static_cast<int64_t>(part) * a.part_rows;
+    stream_rows<kHistUnroll>(a, xb, bh, j0, min(j0 + a.part_rows, a.nrows), f);
+  } else {
+    const int64_t q = static_cast<int64_t>(part) * a.part_vecs;
+    stream_range<kHistUnroll>(a, xb, bh, q, min(q + a.part_vecs, a.Qv), f);
+  }
+  const uint32_t n = misc[0];  // settled: the last round ended on a barrier
+  if (n) f.flush(n);
+}
+
 }  // namespace
 
-int hist_plan(int64_t nb, bool bshd, int64_t B, int64_t H, int64_t S, int64_t D, HistPlan& hp) {
+int hist_plan(int64_t nb, bool bshd, int vpv, int64_t B, int64_t H, int64_t S, int64_t D, HistPlan& hp) {
   if (nb <= 0 || nb > kHistMaxBatches || B <= 0 || H <= 0 || S <= 0 || D <= 0) return FA3Q_ERR_SHAPE;
+  if (vpv != 4 && vpv != 8) return FA3Q_ERR_SHAPE;
   const int64_t row = bshd ? D : S * D;
-  if (row % 8 != 0) return FA3Q_ERR_SHAPE;
+  if (row % vpv != 0) return FA3Q_ERR_SHAPE;
   const int64_t N = B * S * D;
   if (N >= (int64_t{1} << 32)) return FA3Q_ERR_SHAPE;
-  hp.Lv = row / 8;
+  hp.vpv = vpv;
+  hp.Lv = row / vpv;
   hp.nrows = bshd ? B * S : B;
   hp.Qv = hp.nrows * hp.Lv;
   hp.rows = hp.Lv <= kHistThreads;
@@ -685,11 +882,11 @@ int hist_plan(int64_t nb, bool bshd, int64_t B, int64_t H, int64_t S, int64_t D,
   P = std::min<int64_t>(P, std::max<int64_t>(1, N / kMinPartValues));
   P = std::max<int64_t>(P, (N + kMaxPartValues - 1) / kMaxPartValues);
   if (hp.rows) {
-    // parts of whole rows; a row holds at most 8 * kHistThreads values, so the wrap log's
+    // parts of whole rows; a row holds at most vpv * kHistThreads values, so the wrap log's
     // bound is kept by adding parts
     P = std::min<int64_t>(P, hp.nrows);
     int64_t per = (hp.nrows + P - 1) / P;
-    while (per > 1 && per * hp.Lv * 8 > kMaxPartValues) {
+    while (per > 1 && per * hp.Lv * vpv > kMaxPartValues) {
       ++P;
       per = (hp.nrows + P - 1) / P;
     }
@@ -702,7 +899,7 @@ int hist_plan(int64_t nb, bool bshd, int64_t B, int64_t H, int64_t S, int64_t D,
     hp.part_vecs = (hp.Qv + P - 1) / P;
     hp.P = (hp.Qv + hp.part_vecs - 1) / hp.part_vecs;
   }
-  if (hp.part_vecs * 8 > kMaxPartValues) return FA3Q_ERR_SHAPE;
+  if (hp.part_vecs * vpv > kMaxPartValues) return FA3Q_ERR_SHAPE;
   if (kHistMaxBatches * H * hp.P > (int64_t{1} << 31) - 1) return FA3Q_ERR_SHAPE;
   hp.head_words = std::max<int64_t>(hp.P * kPartWords, kBins);
   hp.bytes = static_cast<size_t>(H * hp.head_words) * sizeof(uint32_t);
@@ -733,17 +930,49 @@ int hist_launch(const void* const* xs, int64_t nb, int64_t H, bool f16, int64_t 
   if (hp.P == 1) {  // each head counted by one workgroup, which also finds its window
     const dim3 g(static_cast<unsigned>(nb * H));
     if (hp.rows)
-      hipLaunchKernelGGL((calib_hist_kernel<true, true>), g, blk, 0, stream, ha);
+      hipLaunchKernelGGL((calib_hist_kernel<true, true, false>), g, blk, 0, stream, ha);
     else
-      hipLaunchKernelGGL((calib_hist_kernel<true, false>), g, blk, 0, stream, ha);
+      hipLaunchKernelGGL((calib_hist_kernel<true, false, false>), g, blk, 0, stream, ha);
   } else {
     const dim3 g(static_cast<unsigned>(nb * H * hp.P));
     if (hp.rows)
-      hipLaunchKernelGGL((calib_hist_kernel<false, true>), g, blk, 0, stream, ha);
+      hipLaunchKernelGGL((calib_hist_kernel<false, true, false>), g, blk, 0, stream, ha);
     else
-      hipLaunchKernelGGL((calib_hist_kernel<false, false>), g, blk, 0, stream, ha);
+      hipLaunchKernelGGL((calib_hist_kernel<false, false, false>), g, blk, 0, stream, ha);
     hipLaunchKernelGGL(calib_hist_window_kernel, dim3(static_cast<unsigned>(nb * H)), blk, kWinLds, stream, ha);
   }
+  return launch_status();
+}
+
+
+int hist_f32_collect(const void* x, int64_t H, int64_t t, int64_t K, const HistPlan& hp, uint32_t* records,
+                     TailCut* cut, uint64_t* best, uint32_t* lists, int64_t stride, hipStream_t stream) {
+  if (hp.vpv != 4) return FA3Q_ERR_SHAPE;
+  const int st = allow_dynamic_lds(reinterpret_cast<const void*>(calib_cut_kernel), kCutLds);
+  if (st != FA3Q_OK) return st;
+  HistArgs ha{};
+  ha.x[0] = x;
+  ha.hist = records;
+  ha.Lv = hp.Lv;
+  ha.nrows = hp.nrows;
+  ha.Qv = hp.Qv;
+  ha.part_vecs = hp.part_vecs;
+  ha.part_rows = hp.part_rows;
+  ha.head_words = hp.head_words;
+  ha.H = static_cast<int32_t>(H);
+  ha.P = static_cast<int32_t>(hp.P);
+  ha.t = static_cast<uint32_t>(t);
+  ha.K = static_cast<uint32_t>(K);
+  const dim3 blk(kHistThreads), g_parts(static_cast<unsigned>(H * hp.P));
+  if (hp.rows)
+    hipLaunchKernelGGL((calib_hist_kernel<false, true, true>), g_parts, blk, 0, stream, ha);
+  else
+    hipLaunchKernelGGL((calib_hist_kernel<false, false, true>), g_parts, blk, 0, stream, ha);
+  hipLaunchKernelGGL(calib_cut_kernel, dim3(static_cast<unsigned>(H)), blk, kCutLds, stream, ha, cut, best);
+  if (hp.rows)
+    hipLaunchKernelGGL(calib_collect_kernel<true>, g_parts, blk, 0, stream, ha, cut, lists, stride);
+  else
+    hipLaunchKernelGGL(calib_collect_kernel<false>, g_parts, blk, 0, stream, ha, cut, lists, stride);
   return launch_status();
 }
 

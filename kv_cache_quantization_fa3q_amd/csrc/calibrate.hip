@@ -67,6 +67,7 @@
 #include <type_traits>
 
 #include "calib_hist.hpp"
+#include "calib_sort.hpp"
 #include "fa3q_internal.hpp"
 
 namespace fa3q {
@@ -1363,6 +1364,8 @@ struct CalibPlan {
   bool hist = false;     // the histogram path (16-bit keys)
   bool f16 = false;      // 16-bit keys are float16 patterns (else bf16)
   HistPlan hp;
+  bool sort = false;     // the collect-and-sort path (float32 keys); its workspace serves every batch in turn
+  SortPlan sp;
 };
 
 int64_t next_pow2(int64_t v) {
@@ -1394,11 +1397,19 @@ int make_plan(int dtype, int layout, int64_t nb, int64_t B, int64_t H, int64_t S
   p.K = p.N - p.t + 1;
   p.f16 = dtype == FA3Q_F16;
   if (p.K > fa3q_calibrate_max_windows(dtype) || layout == FA3Q_BSHD || (k16 && p.N >= kHistMinValues)) {
-    if (!k16) return FA3Q_ERR_UNSUPPORTED;
+    if (!k16) {
+      // float32: both tails collected through a histogram of their leading 16 bits and sorted
+      p.sort = true;
+      p.key_bytes = 4;
+      const int st = sort_plan(layout == FA3Q_BSHD, B, H, S, D, p.K, p.sp);
+      if (st != FA3Q_OK) return st;
+      p.total_bytes = p.sp.bytes;
+      return FA3Q_OK;
+    }
     // 16-bit keys: the whole head as one histogram, any K and either layout
     p.hist = true;
     p.key_bytes = 2;
-    const int st = hist_plan(nb, layout == FA3Q_BSHD, B, H, S, D, p.hp);
+    const int st = hist_plan(nb, layout == FA3Q_BSHD, 8, B, H, S, D, p.hp);
     if (st != FA3Q_OK) return st;
     p.total_bytes = p.hp.bytes;
     return FA3Q_OK;
@@ -1671,6 +1682,7 @@ namespace {
 int launch_windows(const void* const* xs, int64_t nb, int64_t H, const CalibPlan& p, float* win_min, float* win_max,
                    void* workspace, hipStream_t s) {
   if (p.hist) return hist_launch(xs, nb, H, p.f16, p.t, p.K, p.hp, win_min, win_max, workspace, s);
+  if (p.sort) return sort_launch(xs, nb, H, p.t, p.K, p.sp, win_min, win_max, workspace, s);
   if (p.key_bytes == 2) return launch<uint16_t>(xs, nb, H, p, win_min, win_max, workspace, s);
   return launch<uint32_t>(xs, nb, H, p, win_min, win_max, workspace, s);
 }
@@ -1679,8 +1691,8 @@ size_t batches_workspace_bytes(int dtype, int layout, int64_t nb, int64_t B, int
                                double ratio) {
   CalibPlan p;
   if (nb <= 0 || nb > kMaxBatches || make_plan(dtype, layout, nb, B, H, S, D, ratio, p) != FA3Q_OK) return 0;
-  if (!p.hist && nb * B * H * p.nch > (int64_t{1} << 31) - 1) return 0;
-  return static_cast<size_t>(nb) * p.total_bytes + round_up(2 * static_cast<size_t>(nb * H) * sizeof(float), 256);
+  if (!p.hist && !p.sort && nb * B * H * p.nch > (int64_t{1} << 31) - 1) return 0;
+  return static_cast<size_t>(p.sort ? 1 : nb) * p.total_bytes + round_up(2 * static_cast<size_t>(nb * H) * sizeof(float), 256);
 }
 
 // Validation and launches of the several-batch entry points: run_min/run_max may both be
@@ -1695,7 +1707,7 @@ int calibrate_batches(const void* const* xs, int64_t nb, int dtype, int layout, 
   CalibPlan p;
   const int st = make_plan(dtype, layout, nb, B, H, S, D, ratio, p);
   if (st != FA3Q_OK) return st;
-  if (!p.hist && nb * H * p.nch > (int64_t{1} << 31) - 1) return FA3Q_ERR_SHAPE;
+  if (!p.hist && !p.sort && nb * H * p.nch > (int64_t{1} << 31) - 1) return FA3Q_ERR_SHAPE;
   for (int64_t b = 0; b < nb; ++b)
     if (!is_aligned(xs[b], 16)) return FA3Q_ERR_ALIGN;
   if ((run_min && (!is_aligned(run_min, 4) || !is_aligned(run_max, 4))) ||
@@ -1704,7 +1716,8 @@ int calibrate_batches(const void* const* xs, int64_t nb, int dtype, int layout, 
   const size_t need = batches_workspace_bytes(dtype, layout, nb, B, H, S, D, ratio);
   if (!workspace || workspace_bytes < need) return FA3Q_ERR_WORKSPACE;
   if (!is_aligned(workspace, 256)) return FA3Q_ERR_ALIGN;
-  float* wins = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + static_cast<size_t>(nb) * p.total_bytes);
+  float* wins = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) +
+                                        static_cast<size_t>(p.sort ? 1 : nb) * p.total_bytes);
   float* wmin = win_min ? win_min : wins;
   float* wmax = win_max ? win_max : wins + nb * H;
   hipStream_t s = as_stream(stream);

@@ -75,7 +75,27 @@ def test_window_count_limit_is_where_the_tail_lists_stop(dtype, S):
         # past the on-chip tail lists the histogram path takes over: a region of 65536 words per head
         assert past >= 2 * 65536 * 4
     else:
-        assert past == 0
+        # float32: the collect-and-sort path, two lists of N keys per head
+        assert past >= 2 * 2 * N * 4
+
+
+@pytest.mark.parametrize("dtype", [L.FA3Q_F32, L.FA3Q_BF16, L.FA3Q_F16])
+@pytest.mark.parametrize("layout", [L.FA3Q_BHSD, L.FA3Q_BSHD])
+def test_every_valid_ratio_has_a_plan(dtype, layout):
+    # FA3量化 page, 原理 -> 算法流程: the window is defined for every ratio with int(ratio*N) >= 1;
+    # no such ratio is refused (a workspace query of 0 would mean an error status)
+    lib = fa.lib()
+    cap = lib.fa3q_calibrate_max_windows(dtype)
+    for (B, H, S, D) in [(1, 2, 64, 16), (2, 8, 2048, 128), (8, 128, 2048, 128), (3, 5, 777, 8)]:
+        N = B * S * D
+        ks = {1, 2, cap, cap + 1, N // 100, N // 10, N // 2, N - 1, N}
+        ratios = {1.0, 0.9999, 0.999, 0.99, 0.9, 0.5, 0.01, 1.0 / N}
+        ratios |= {_ratio_for_k(N, k) for k in ks if 1 <= k <= N - 1}
+        for r in sorted(ratios):
+            if r > 1.0 or int(r * N) < 1:
+                continue
+            ws = lib.fa3q_calibrate_ex_workspace_bytes(dtype, layout, 1, B, H, S, D, r)
+            assert ws > 0, (dtype, layout, (B, H, S, D), r)
 
 
 def test_bf16_calibration_takes_every_valid_ratio():
@@ -134,7 +154,6 @@ def test_calibrate_rejections():
     assert call(r=1.5) == L.FA3Q_ERR_RATIO
     assert call(r=float("nan")) == L.FA3Q_ERR_RATIO
     assert call(r=1e-9) == L.FA3Q_ERR_RATIO                 # int(ratio*N) = 0
-    assert call(r=0.01, S=4096, D=128) == L.FA3Q_ERR_UNSUPPORTED  # K far above the LDS-resident limit
     assert call(x=_p(2)) == L.FA3Q_ERR_ALIGN
     assert call(mn=_p(2)) == L.FA3Q_ERR_ALIGN
     assert call(ws=None) == L.FA3Q_ERR_WORKSPACE
@@ -531,7 +550,12 @@ def test_ex_workspace_queries():
         assert q(dt, L.FA3Q_BSHD, 2, 1, 8, 256, 64, r) >= 2 * 8 * 65536 * 4
         assert q(dt, L.FA3Q_BSHD, 1, 2, 4, 16, 12, r) == 0  # rows of 12 values: not whole vectors
     assert q(L.FA3Q_F32, L.FA3Q_BHSD, 1, 1, 8, 256, 64, r) > 0
-    assert q(L.FA3Q_F32, L.FA3Q_BSHD, 1, 1, 8, 256, 64, r) == 0  # float32 (B,S,H,D): not handled
+    # float32 (B,S,H,D): the collect-and-sort path, one region of two N-key lists per head for
+    # any number of batches (they take it in turn), plus the windows of every batch
+    one = q(L.FA3Q_F32, L.FA3Q_BSHD, 1, 1, 8, 256, 64, r)
+    assert one >= 2 * 8 * (256 * 64) * 4
+    assert 0 <= q(L.FA3Q_F32, L.FA3Q_BSHD, 4, 1, 8, 256, 64, r) - one < 4096
+    assert q(L.FA3Q_F32, L.FA3Q_BSHD, 1, 2, 4, 16, 6, r) == 0  # rows of 6 float32 values: not whole vectors
     assert q(L.FA3Q_BF16, 2, 1, 1, 8, 256, 64, r) == 0
     assert q(7, L.FA3Q_BHSD, 1, 1, 8, 256, 64, r) == 0
     assert q(L.FA3Q_F16, L.FA3Q_BHSD, 17, 1, 8, 256, 64, r) == 0
@@ -555,7 +579,7 @@ def test_calibrate_ex_rejections():
 
     assert call(lay=2) == L.FA3Q_ERR_LAYOUT
     assert call(dt=5) == L.FA3Q_ERR_DTYPE
-    assert call(dt=L.FA3Q_F32) == L.FA3Q_ERR_UNSUPPORTED
+    assert call(dt=L.FA3Q_F32, D=6) == L.FA3Q_ERR_SHAPE  # float32 rows of whole 16-byte vectors
     assert call(D=12) == L.FA3Q_ERR_SHAPE
     assert call(nb=0) == L.FA3Q_ERR_SHAPE
     assert call(r=0.0) == L.FA3Q_ERR_RATIO

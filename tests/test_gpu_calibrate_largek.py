@@ -118,17 +118,6 @@ def test_degenerate_heads(fa, S):
         _check(fa, x, ratio, f"degenerate heads ratio {ratio!r}")
 
 
-def test_float32_past_the_cap_is_refused(fa):
-    cap = fa.fa3q_calibrate_max_windows(torch.float32)
-    B, H, S, D = 1, 2, 256, 128
-    N = S * D
-    ratio = (N - cap) / N
-    assert _k_of(ratio, N) == cap + 1
-    x = torch.zeros((B, H, S, D), dtype=torch.float32, device=DEV)
-    with pytest.raises(fa.Fa3qError):
-        fa.fa3q_calibrate_perhead(x, ratio)
-
-
 def _sampled_vectors(Qv):
     """Head vectors the histogram path's bound sample reads: 32 runs of 128 vectors, one per
     1/32 of the head at a fixed phase inside it (whole 128-byte lines)."""

@@ -268,7 +268,7 @@ def cpu_baseline(pool, workers: int, inputs, budget_s: float):
 
 
 EXTRAS = ("decode_append", "decode_qkv8", "asym", "fake_quant", "decode_latent", "calibrate_long",
-          "calibrate_largek", "decode_long", "decode_noalloc", "decode_paged", "f16_bshd")
+          "calibrate_largek", "calibrate_f32", "decode_long", "decode_noalloc", "decode_paged", "f16_bshd")
 
 
 def main() -> int:
@@ -536,6 +536,33 @@ def run(args, only, pool, workers) -> int:
                 calib_row(calib[0], r, f"calibrate_largek_{r}", f"one (8,128,2048,128) bf16 batch at ratio {r} "
                           "(histogram path; outside the step)")
         del long_x
+
+    if "calibrate_f32" in only:
+        # one float32 calibration batch (8,128,2048,128): the tail lists at ratio 0.9999, the
+        # collect-and-sort path past them (0.99, 0.9) and for (B,S,H,D) input
+        x32 = synth.activations(CAL_SHAPE, synth.head_sigmas(H, seed=2024), law="t3", dtype=torch.float32, seed=100,
+                                device=dev)
+        w32_min = torch.empty((1, H), dtype=torch.float32, device=dev)
+        w32_max = torch.empty((1, H), dtype=torch.float32, device=dev)
+        n32 = CAL_SHAPE[0] * CAL_SHAPE[2] * CAL_SHAPE[3]
+        for layout, xl, ratios in (("BHSD", x32, (0.9999, 0.99, 0.9)), ("BSHD", None, (0.9999, 0.99))):
+            if layout == "BSHD":
+                xl = x32.transpose(1, 2).contiguous()
+            for r in ratios:
+                ws = torch.empty(max(1, fa.fa3q_calibrate_ex_workspace_bytes(torch.float32, layout, 1, *CAL_SHAPE, r)),
+                                 dtype=torch.uint8, device=dev)
+                c_ms = timed(lambda: fa.fa3q_calibrate_ex([xl], r, layout=layout, win_min=w32_min, win_max=w32_max,
+                                                          workspace=ws, stream=stream))
+                k_win = n32 - int(r * n32) + 1
+                sort = layout == "BSHD" or k_win > fa.fa3q_calibrate_max_windows(torch.float32)
+                tag = "" if layout == "BHSD" else "_bshd"
+                breakdown[f"calibrate_f32{tag}_{r}"] = hbm_row(
+                    c_ms, 4 * x32.numel(), f"one (8,128,2048,128) float32 batch, {layout}, at ratio {r} "
+                    "(bytes: the batch read once; outside the step)", K=k_win,
+                    path="collect and sort" if sort else "tail lists")
+                del ws
+            del xl
+        del x32
 
     LB, LT = 8, QB * QS // 8
     long_dec_bytes = LB * H * LT * (DN + 2 * DR + 2 * DV) + LB * H * (2 * (DN + DR) + 4 * DV)

@@ -790,8 +790,9 @@ constexpr uint32_t kCollectFlush = kCollectCap - kCollectRound;
 __device__ __forceinline__ uint32_t key32(uint32_t b) { return (b & 0x80000000u) ? ~b : (b | 0x80000000u); }
 
 // The collecting pass's visitor: the 32-bit keys of the values whose leading key is <= a_max or
-// >= m_min are appended to the LDS stage (one LDS atomic per wave and value slot), which is
-// written to the head's list (one global atomic per write) when another round might not fit.
+// >= m_min are appended to the LDS stage (each thread's keys at its offset from a prefix sum
+// over the wave, one LDS atomic per wave and round), which is written to the head's list (one
+// global atomic per write) when another round might not fit.
 template <int U>
 struct CollectVisit {
   uint32_t* buf;    // LDS [kCollectCap]
@@ -812,24 +813,38 @@ struct CollectVisit {
   }
   template <bool kAll>
   __device__ __forceinline__ void run(const uint4 (&v)[U], const bool (&valid)[U]) {
-    const uint64_t lt = (uint64_t{1} << lane_id()) - 1;
+    uint32_t k[U][4];
+    uint32_t sel = 0, c = 0;  // bit 4u+e: value e of vector u is collected
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t k = key32(w[e]);
-        const uint32_t lead = k >> 16;
-        const bool sel = (kAll || valid[u]) && (lead <= a_max || lead >= m_min);
-        const uint64_t m = __ballot(sel);
-        if (m) {
-          const int leader = __builtin_ctzll(m);
-          uint32_t base = 0;
-          if (lane_id() == leader) base = atomicAdd(nbuf, static_cast<uint32_t>(__popcll(m)));
-          base = __builtin_amdgcn_readlane(base, leader);
-          if (sel) buf[base + static_cast<uint32_t>(__popcll(m & lt))] = k;
-        }
+        k[u][e] = key32(w[e]);
+        const uint32_t lead = k[u][e] >> 16;
+        const bool on = (kAll || valid[u]) && (lead <= a_max || lead >= m_min);
+        sel |= on ? 1u << (4 * u + e) : 0u;
+        c += on ? 1u : 0u;
       }
+    }
+    // the wave's inclusive prefix of the counts; its last lane holds the total
+    const int lane = lane_id();
+    uint32_t inc = c;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const uint32_t t = __shfl_up(inc, o);
+      if (lane >= o) inc += t;
+    }
+    const uint32_t total = __builtin_amdgcn_readlane(inc, kWave - 1);
+    if (total) {  // uniform over the wave
+      uint32_t base = 0;
+      if (lane == 0) base = atomicAdd(nbuf, total);
+      uint32_t pos = __builtin_amdgcn_readfirstlane(base) + inc - c;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (sel & (1u << (4 * u + e))) buf[pos++] = k[u][e];
     }
     __syncthreads();
     const uint32_t n = *nbuf;

@@ -13,13 +13,13 @@
 //   lsd_count_kernel + lsd_scatter_kernel, four times: a stable least-significant-digit
 //                   radix sort of each list, 8 bits a pass, between two buffers (back in the
 //                   first after the fourth pass).  A head's list is cut into nblk blocks of
-//                   whole 4096-key tiles; the count kernel gives each block's digit counts,
+//                   whole 8192-key tiles; the count kernel gives each block's digit counts,
 //                   from which every scatter workgroup derives its block's first position for
 //                   each digit (digits in order, blocks in order).  A tile is ranked in LDS:
 //                   each wave takes 1024 consecutive keys, 64 at a time, and ranks each key
 //                   among the earlier keys of its digit from a per-wave counter and the lanes
-//                   of the same digit (eight ballots give them), so the order within a digit
-//                   is the list order (stable).  The tile is then laid out by digit in LDS and
+//                   of the same digit (a per-wave LDS table of lane masks gives them), so the
+//                   order within a digit is the list order (stable).  The tile is then laid out by digit in LDS and
 //                   written with consecutive lanes on consecutive positions of a digit's run.
 //   sort_window_kernel  the K windows [L[i], L[M-K+i]] of the sorted list L: float32 lengths,
 //                   the smallest (length, i) per workgroup, combined with a 64-bit atomic min.
@@ -31,15 +31,19 @@
 namespace fa3q {
 namespace {
 
-constexpr int kSortThreads = 256;
-constexpr int kSortWaves = kSortThreads / kWave;  // 4
+constexpr int kSortThreads = 256;                  // counting and window workgroups
+constexpr int kSortWaves = kSortThreads / kWave;   // 4
+constexpr int kScatterThreads = 512;               // scatter workgroups
+constexpr int kScatterWaves = kScatterThreads / kWave;  // 8
 constexpr int kSlots = 16;                         // keys per thread per tile
-constexpr int kTile = kSortThreads * kSlots;       // 4096
+constexpr int kTile = kScatterThreads * kSlots;    // 8192 keys: a block is whole tiles
+constexpr int kCountTile = kSortThreads * kSlots;  // 4096 keys per step of the counting workgroup
 constexpr int kWaveKeys = kWave * kSlots;          // 1024 consecutive keys per wave and tile
 constexpr int kDigits = 256;
 constexpr int kMaxBlocks = 64;
 constexpr int64_t kTargetGroups = 2048;            // sorting workgroups per launch, when the lists allow
-static_assert(kDigits == kSortThreads, "one digit per thread in the per-digit steps");
+static_assert(kDigits == kSortThreads && kDigits <= kScatterThreads, "one digit per thread in the per-digit steps");
+static_assert(kTile % kCountTile == 0, "counting steps tile a block");
 
 struct SortArgs {
   const uint32_t* src;  // [H][stride] keys, M of head h in its row
@@ -72,21 +76,10 @@ __device__ __forceinline__ void block_range(uint32_t M, int nblk, int blk, uint6
   end = min(start + per * kTile, static_cast<uint64_t>(M));
 }
 
-// Lanes of the wave (among valid) whose digit d equals this lane's.
-__device__ __forceinline__ uint64_t same_digit(uint32_t d, uint64_t valid) {
-  uint64_t m = valid;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const bool bit = (d >> j) & 1u;
-    const uint64_t b = __ballot(bit);
-    m &= bit ? b : ~b;
-  }
-  return m;
-}
-
-// Exclusive scan of one value per thread over the 256 threads (scr: 4 words, free on entry;
-// the caller separates two uses by a barrier).
-__device__ __forceinline__ uint32_t block_exclusive_scan256(uint32_t v, uint32_t* scr) {
+// Exclusive scan of one value per thread over the kWaves waves of the workgroup (scr: kWaves
+// words, free on entry; the caller separates two uses by a barrier).
+template <int kWaves>
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* scr) {
   const int lane = lane_id(), wave = static_cast<int>(threadIdx.x) / kWave;
   uint32_t inc = v;
 #pragma unroll
@@ -98,7 +91,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan256(uint32_t v, uint32_t
   __syncthreads();
   uint32_t before = 0;
 #pragma unroll
-  for (int w = 0; w < kSortWaves; ++w) before += w < wave ? scr[w] : 0u;
+  for (int w = 0; w < kWaves; ++w) before += w < wave ? scr[w] : 0u;
   return before + inc - v;
 }
 
@@ -112,108 +105,139 @@ __global__ __launch_bounds__(kSortThreads) void lsd_count_kernel(SortArgs a) {
   uint64_t start, end;
   block_range(a.cut[h].M, a.nblk, blk, start, end);
   const uint32_t* src = a.src + static_cast<int64_t>(h) * a.stride;
-  for (uint64_t t0 = start; t0 < end; t0 += kTile) {
+  uint32_t k[kSlots];
+  {
+    const uint64_t w0 = start + static_cast<uint64_t>(wave) * kWaveKeys + lane;
+#pragma unroll
+    for (int s = 0; s < kSlots; ++s) k[s] = w0 + s * kWave < end ? src[w0 + s * kWave] : 0u;
+  }
+  for (uint64_t t0 = start; t0 < end; t0 += kCountTile) {
     const uint64_t w0 = t0 + static_cast<uint64_t>(wave) * kWaveKeys + lane;
-    uint32_t k[kSlots];
+    uint32_t kn[kSlots];  // the next step's keys, loading while these are counted
+#pragma unroll
+    for (int s = 0; s < kSlots; ++s)
+      kn[s] = w0 + kCountTile + s * kWave < end ? src[w0 + kCountTile + s * kWave] : 0u;
 #pragma unroll
     for (int s = 0; s < kSlots; ++s) {
-      const uint64_t pos = w0 + s * kWave;
-      k[s] = pos < end ? src[pos] : 0u;
+      if (w0 + s * kWave < end) atomicAdd(&cnt[(k[s] >> a.shift) & 0xffu], 1u);  // counts need no order
     }
 #pragma unroll
-    for (int s = 0; s < kSlots; ++s) {
-      const bool valid = w0 + s * kWave < end;
-      const uint32_t d = (k[s] >> a.shift) & 0xffu;
-      const uint64_t peers = same_digit(d, __ballot(valid));
-      // the highest lane of each digit adds the digit's lanes
-      if (valid && lane == 63 - __builtin_clzll(peers)) atomicAdd(&cnt[d], static_cast<uint32_t>(__popcll(peers)));
-    }
+    for (int s = 0; s < kSlots; ++s) k[s] = kn[s];
   }
   __syncthreads();
   a.bcount[(static_cast<int64_t>(h) * kDigits + tid) * a.nblk + blk] = cnt[tid];
 }
 
-__global__ __launch_bounds__(kSortThreads) void lsd_scatter_kernel(SortArgs a) {
-  __shared__ uint32_t cnt[kDigits * kSortWaves];  // [digit][wave]: keys so far, then tile positions
-  __shared__ uint32_t tstart[kDigits];           // the digit's first position in the laid-out tile
-  __shared__ uint32_t gbase[kDigits];            // the digit's next list position from this block
+__global__ __launch_bounds__(kScatterThreads) void lsd_scatter_kernel(SortArgs a) {
+  __shared__ uint64_t peer[kScatterWaves * kDigits];  // [wave][digit]: the lanes of each digit (zero between uses)
+  __shared__ uint32_t cnt[kScatterWaves * kDigits];   // [wave][digit]: keys so far, then tile positions
+  __shared__ uint32_t tstart[kDigits];                // the digit's first position in the laid-out tile
+  __shared__ uint32_t gbase[kDigits];                 // the digit's next list position from this block
   __shared__ uint32_t stage[kTile];
-  __shared__ uint32_t scr[kSortWaves];
+  __shared__ uint32_t scr[kScatterWaves];
   const int tid = static_cast<int>(threadIdx.x);
   const int lane = tid & (kWave - 1), wave = tid / kWave;
+  const bool digit_thread = tid < kDigits;  // the per-digit steps: digit tid
   const int h = static_cast<int>(blockIdx.x) / a.nblk, blk = static_cast<int>(blockIdx.x) % a.nblk;
   uint64_t start, end;
   block_range(a.cut[h].M, a.nblk, blk, start, end);
   if (start >= end) return;
+#pragma unroll
+  for (int i = 0; i < kScatterWaves * kDigits / kScatterThreads; ++i) peer[i * kScatterThreads + tid] = 0;
   {
-    // digit tid: keys of smaller digits in the head, plus its keys in earlier blocks
-    const uint32_t* bc = a.bcount + (static_cast<int64_t>(h) * kDigits + tid) * a.nblk;
+    // digit tid: keys of smaller digits in the head, plus its keys in earlier blocks (the scan's
+    // barrier also orders the peer table's zeroing before its first use)
     uint32_t tot = 0, before = 0;
-    for (int b = 0; b < a.nblk; ++b) {
-      const uint32_t v = bc[b];
-      tot += v;
-      before += b < blk ? v : 0u;
+    if (digit_thread) {
+      const uint32_t* bc = a.bcount + (static_cast<int64_t>(h) * kDigits + tid) * a.nblk;
+      for (int b = 0; b < a.nblk; ++b) {
+        const uint32_t v = bc[b];
+        tot += v;
+        before += b < blk ? v : 0u;
+      }
     }
-    gbase[tid] = block_exclusive_scan256(tot, scr) + before;
+    const uint32_t ex = block_exclusive_scan<kScatterWaves>(tot, scr);
+    if (digit_thread) gbase[tid] = ex + before;
   }
   const uint32_t* src = a.src + static_cast<int64_t>(h) * a.stride;
   uint32_t* dst = a.dst + static_cast<int64_t>(h) * a.stride;
-  const uint64_t lt = (uint64_t{1} << lane) - 1;
+  const uint64_t bit = uint64_t{1} << lane;
+  uint32_t k[kSlots];
+  {
+    const uint64_t w0 = start + static_cast<uint64_t>(wave) * kWaveKeys + lane;
+#pragma unroll
+    for (int s = 0; s < kSlots; ++s) k[s] = w0 + s * kWave < end ? src[w0 + s * kWave] : 0u;
+  }
   for (uint64_t t0 = start; t0 < end; t0 += kTile) {
     const uint64_t w0 = t0 + static_cast<uint64_t>(wave) * kWaveKeys + lane;
-    uint32_t k[kSlots], rk[kSlots];
+    uint32_t rk[kSlots];
 #pragma unroll
-    for (int s = 0; s < kSlots; ++s) {
-      const uint64_t pos = w0 + s * kWave;
-      k[s] = pos < end ? src[pos] : 0u;
-    }
-#pragma unroll
-    for (int i = 0; i < kSortWaves; ++i) cnt[tid * kSortWaves + i] = 0;
+    for (int i = 0; i < kScatterWaves * kDigits / kScatterThreads; ++i) cnt[i * kScatterThreads + tid] = 0;
     __syncthreads();
-    // rank of each key among the wave's earlier keys of its digit (slots in order, lanes in order)
+    // rank of each key among the wave's earlier keys of its digit (slots in order, lanes in
+    // order): the lanes of one digit come from the wave's peer table (each lane sets its bit,
+    // reads its digit's mask, clears it), the earlier slots' count from the per-wave counter.
+    // A wave's LDS operations complete in the order it issues them.
 #pragma unroll
     for (int s = 0; s < kSlots; ++s) {
       const bool valid = w0 + s * kWave < end;
       const uint32_t d = (k[s] >> a.shift) & 0xffu;
-      const uint64_t peers = same_digit(d, __ballot(valid));
-      uint32_t* c = &cnt[d * kSortWaves + wave];
+      uint64_t* pt = &peer[wave * kDigits + d];
+      uint32_t* c = &cnt[wave * kDigits + d];
+      if (valid) atomicOr(reinterpret_cast<unsigned long long*>(pt), static_cast<unsigned long long>(bit));
+      const uint64_t peers = valid ? *pt : uint64_t{0};
       const uint32_t base = valid ? *c : 0u;
-      rk[s] = base + static_cast<uint32_t>(__popcll(peers & lt));
-      // one writer per digit; the wave's LDS operations complete in order, so every lane has
-      // read the counter first
-      if (valid && lane == 63 - __builtin_clzll(peers)) *c = base + static_cast<uint32_t>(__popcll(peers));
+      const uint32_t r = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(peers >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(peers), 0u));
+      rk[s] = base + r;
+      if (valid) {
+        *pt = 0;
+        if (r == 0) *c = base + static_cast<uint32_t>(__popcll(peers));  // the digit's first lane
+      }
     }
     __syncthreads();
     // digit tid: its tile count, its first position in the laid-out tile, each wave's first
-    uint32_t tot;
-    {
-      const uint32_t c0 = cnt[tid * kSortWaves], c1 = cnt[tid * kSortWaves + 1], c2 = cnt[tid * kSortWaves + 2],
-                     c3 = cnt[tid * kSortWaves + 3];
-      tot = c0 + c1 + c2 + c3;
-      const uint32_t ts = block_exclusive_scan256(tot, scr);
+    uint32_t tot = 0, cw[kScatterWaves];
+    if (digit_thread) {
+#pragma unroll
+      for (int w = 0; w < kScatterWaves; ++w) {
+        cw[w] = cnt[w * kDigits + tid];
+        tot += cw[w];
+      }
+    }
+    const uint32_t ts = block_exclusive_scan<kScatterWaves>(tot, scr);
+    if (digit_thread) {
       tstart[tid] = ts;
-      cnt[tid * kSortWaves] = ts;
-      cnt[tid * kSortWaves + 1] = ts + c0;
-      cnt[tid * kSortWaves + 2] = ts + c0 + c1;
-      cnt[tid * kSortWaves + 3] = ts + c0 + c1 + c2;
+      uint32_t run = ts;
+#pragma unroll
+      for (int w = 0; w < kScatterWaves; ++w) {
+        cnt[w * kDigits + tid] = run;
+        run += cw[w];
+      }
     }
     __syncthreads();
 #pragma unroll
     for (int s = 0; s < kSlots; ++s) {
       if (w0 + s * kWave < end) {
         const uint32_t d = (k[s] >> a.shift) & 0xffu;
-        stage[cnt[d * kSortWaves + wave] + rk[s]] = k[s];
+        stage[cnt[wave * kDigits + d] + rk[s]] = k[s];
       }
+    }
+    // the next tile's keys load while this one is written out
+    {
+      const uint64_t w1 = w0 + kTile;
+#pragma unroll
+      for (int s = 0; s < kSlots; ++s) k[s] = w1 + s * kWave < end ? src[w1 + s * kWave] : 0u;
     }
     __syncthreads();
     const uint32_t n = static_cast<uint32_t>(min(end - t0, static_cast<uint64_t>(kTile)));
-    for (uint32_t i = static_cast<uint32_t>(tid); i < n; i += kSortThreads) {
+    for (uint32_t i = static_cast<uint32_t>(tid); i < n; i += kScatterThreads) {
       const uint32_t key = stage[i];
       const uint32_t d = (key >> a.shift) & 0xffu;
       dst[gbase[d] + (i - tstart[d])] = key;
     }
     __syncthreads();
-    gbase[tid] += tot;  // read again only after the next tile's barriers
+    if (digit_thread) gbase[tid] += tot;  // read again only after the next tile's barriers
   }
 }
 
@@ -280,7 +304,7 @@ int sort_plan(bool bshd, int64_t B, int64_t H, int64_t S, int64_t D, int64_t K, 
   // the blocks cover it), never below four tiles each
   const int64_t m_est = std::min<int64_t>(sp.N, 2 * K);
   const int64_t by_heads = (kTargetGroups + H - 1) / H;
-  const int64_t by_tiles = (m_est + 4 * kTile - 1) / (4 * kTile);
+  const int64_t by_tiles = (m_est + 2 * kTile - 1) / (2 * kTile);
   sp.nblk = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>({by_heads, by_tiles, kMaxBlocks})));
   if (H * sp.nblk > (int64_t{1} << 31) - 1) return FA3Q_ERR_SHAPE;
   sp.rec_bytes = sp.hp.bytes;
@@ -301,7 +325,7 @@ int sort_launch(const void* const* xs, int64_t nb, int64_t H, int64_t t, int64_t
   uint32_t* bcount = reinterpret_cast<uint32_t*>(w + sp.rec_bytes + sp.cut_bytes + sp.best_bytes);
   uint32_t* list_a = reinterpret_cast<uint32_t*>(w + sp.rec_bytes + sp.cut_bytes + sp.best_bytes + sp.bcount_bytes);
   uint32_t* list_b = reinterpret_cast<uint32_t*>(reinterpret_cast<unsigned char*>(list_a) + sp.list_bytes);
-  const dim3 g_blocks(static_cast<unsigned>(H * sp.nblk)), blk(kSortThreads);
+  const dim3 g_blocks(static_cast<unsigned>(H * sp.nblk)), blk(kSortThreads), blk_sc(kScatterThreads);
   for (int64_t b = 0; b < nb; ++b) {
     const int st = hist_f32_collect(xs[b], H, t, K, sp.hp, records, cut, best, list_a, sp.N, stream);
     if (st != FA3Q_OK) return st;
@@ -315,7 +339,7 @@ int sort_launch(const void* const* xs, int64_t nb, int64_t H, int64_t t, int64_t
       sa.dst = (pass & 1) ? list_a : list_b;
       sa.shift = 8 * pass;
       hipLaunchKernelGGL(lsd_count_kernel, g_blocks, blk, 0, stream, sa);
-      hipLaunchKernelGGL(lsd_scatter_kernel, g_blocks, blk, 0, stream, sa);
+      hipLaunchKernelGGL(lsd_scatter_kernel, g_blocks, blk_sc, 0, stream, sa);
     }
     WinArgs wa;
     wa.list = list_a;  // four passes: sorted back into the first buffer

@@ -62,11 +62,20 @@ constexpr int64_t kPartPacked = kBins / 2;
 constexpr int64_t kPartWords = kPartPacked + 64 + kMaxEvents;
 enum Hdr : int { kHdrEvents = 0 };
 constexpr int64_t kMinPartValues = int64_t{1} << 19;  // parts smaller than this do not pay for their record
+// heads of at least this many parts have their records summed by calib_hist_sum_kernel (many
+// workgroups per head) into 65536 counts after the records, which the head's window or cut
+// workgroup then reads instead of the records
+constexpr int kSumMinParts = 5;
+constexpr int kSumThreads = 256;
+constexpr int kSumDwords = kSumThreads;                // packed dwords (2 bins each) per summing workgroup
+constexpr int kSumSlices = kBins / 2 / kSumDwords;     // summing workgroups per head (128)
+constexpr int kSumUnroll = 8;                          // records in flight per thread
 // distinct values the window kernel keeps in LDS: a 16-bit key and a 32-bit inc[] each
 constexpr int kWinCap = 24576;
 constexpr size_t kWinLds = kCtlWords * 4 + std::max<size_t>(static_cast<size_t>(kWinCap) * 6, kBins * 2 + kBins / 4 + 4);
 
 static_assert(kBinsPerThread * kHistThreads == kBins, "bins per thread");
+static_assert(kSumSlices * kSumDwords * 2 == kBins, "summing slices cover the bins");
 static_assert(kWinLds <= kLdsLimit, "LDS budget");
 static_assert(kWinLds >= kCtlWords * 4 + kBins * 2, "the window kernel counts wraps in its LDS");
 // the merge-path search: a 16-bit prefix of every key and a prefix per 16 keys (and N) after the
@@ -671,34 +680,115 @@ __global__ __launch_bounds__(kHistThreads) void calib_hist_kernel(HistArgs a) {
   }
 }
 
-// One workgroup per head after the parts' records are written: their counts summed, the
-// window found from them.
-__global__ __launch_bounds__(kHistThreads) void calib_hist_window_kernel(HistArgs a) {
-  extern __shared__ uint32_t lds[];
-  uint32_t* cnt = lds + kCtlWords;  // packed wrap counts (rare), before the window search
+// Sums the part records of head blockIdx.x / kSumSlices over packed dwords [d_lo, d_lo +
+// kSumDwords) of slice blockIdx.x % kSumSlices: thread t takes dword d_lo + t (two bins) of
+// every record, kSumUnroll records in flight, and the logged wraps of every part that fall in
+// the slice are added through LDS.  Writes the slice's counts, in pattern order, to the head's
+// 65536 summed counts after its records.
+__global__ __launch_bounds__(kSumThreads) void calib_hist_sum_kernel(HistArgs a) {
+  __shared__ uint32_t wraps[2 * kSumDwords];  // wrap corrections of the slice's bins (rare)
   const int tid = static_cast<int>(threadIdx.x);
-  const int64_t bh = blockIdx.x;
+  const int64_t bh = blockIdx.x / kSumSlices;
+  const int slice = static_cast<int>(blockIdx.x % kSumSlices);
   uint32_t* hs = a.hist + bh * a.head_words;
+  const int d_lo = slice * kSumDwords;
+  const uint32_t* src = hs + d_lo + tid;
+  const uint32_t* hdr = hs + kPartPacked + kHdrEvents;
+  uint32_t lo = 0, hi = 0, n_events = 0;  // n_events: the same for every thread
+  int p = 0;
+  for (; p + kSumUnroll <= a.P; p += kSumUnroll) {  // the records' dwords and headers load together
+    uint32_t w[kSumUnroll], n[kSumUnroll];
+#pragma unroll
+    for (int u = 0; u < kSumUnroll; ++u) {
+      w[u] = src[static_cast<int64_t>(p + u) * kPartWords];
+      n[u] = hdr[static_cast<int64_t>(p + u) * kPartWords];
+    }
+#pragma unroll
+    for (int u = 0; u < kSumUnroll; ++u) {
+      lo += w[u] & 0xffffu;
+      hi += w[u] >> 16;
+      n_events += n[u];
+    }
+  }
+  for (; p < a.P; ++p) {
+    const uint32_t w = src[static_cast<int64_t>(p) * kPartWords];
+    lo += w & 0xffffu;
+    hi += w >> 16;
+    n_events += hdr[static_cast<int64_t>(p) * kPartWords];
+  }
+  if (n_events) {
+    // a lower wrap of dword d gave bin 2d 65536 more and carried one into bin 2d+1's field; an
+    // upper wrap gave bin 2d+1 65536 more (modulo 2^32, as the counts are)
+    for (int i = tid; i < 2 * kSumDwords; i += kSumThreads) wraps[i] = 0;
+    __syncthreads();
+    for (int q = 0; q < a.P; ++q) {
+      const uint32_t* rec = hs + static_cast<int64_t>(q) * kPartWords;
+      const uint32_t n = rec[kPartPacked + kHdrEvents];
+      for (uint32_t e = tid; e < n; e += kSumThreads) {
+        const uint32_t pat = rec[kPartPacked + 64 + e];
+        const int d = static_cast<int>(pat >> 1);
+        if (d < d_lo || d >= d_lo + kSumDwords) continue;
+        const int i = 2 * (d - d_lo) + static_cast<int>(pat & 1u);
+        atomicAdd(&wraps[i], 65536u);
+        if (!(pat & 1u)) atomicSub(&wraps[i + 1], 1u);
+      }
+    }
+    __syncthreads();
+    lo += wraps[2 * tid];
+    hi += wraps[2 * tid + 1];
+  }
+  *reinterpret_cast<uint2*>(hs + static_cast<int64_t>(a.P) * kPartWords + 2 * (d_lo + tid)) = make_uint2(lo, hi);
+}
+
+// The counts of the thread's 64 keys [64t, 64t+64) (key order) of the head whose region is
+// hs: summed from its P part records, or read from the summed counts after them (P >=
+// kSumMinParts).  cnt: 32768 words of LDS for the rare logged wraps.
+__device__ __forceinline__ void head_counts(uint32_t (&c)[kBinsPerThread], const uint32_t* hs, int P, uint32_t* cnt) {
+  const int tid = static_cast<int>(threadIdx.x);
   const int bin0 = tid * kBinsPerThread;
+  const bool rev = bin0 < 0x8000;
+  if (P >= kSumMinParts) {
+    // patterns ascend with the keys for non-negative values (pattern = key ^ 0x8000) and
+    // descend for negative ones (pattern = 0xffff - key); selects, not branches, pick the order
+    const uint32_t* sums = hs + static_cast<int64_t>(P) * kPartWords + (rev ? 0xffc0 - bin0 : bin0 - 0x8000);
+#pragma unroll
+    for (int q = 0; q < kBinsPerThread / 4; ++q) {
+      const uint4 v = reinterpret_cast<const uint4*>(sums)[rev ? kBinsPerThread / 4 - 1 - q : q];
+      c[4 * q] = rev ? v.w : v.x;
+      c[4 * q + 1] = rev ? v.z : v.y;
+      c[4 * q + 2] = rev ? v.y : v.z;
+      c[4 * q + 3] = rev ? v.x : v.w;
+    }
+    return;
+  }
   const int dw0 = first_dword(bin0);
-  uint32_t c[kBinsPerThread];
 #pragma unroll
   for (int i = 0; i < kBinsPerThread; ++i) c[i] = 0;
   uint32_t n_events = 0;
-  for (int p = 0; p < a.P; ++p) {
+  for (int p = 0; p < P; ++p) {
     const uint32_t* rec = hs + static_cast<int64_t>(p) * kPartWords;
-    add_packed(c, rec, dw0, bin0 < 0x8000);
+    add_packed(c, rec, dw0, rev);
     n_events += rec[kPartPacked + kHdrEvents];
   }
   if (n_events) {
     // logged wraps (rare: a pattern past 65535 values in one part)
-    for (int p = 0; p < a.P; ++p) {
+    for (int p = 0; p < P; ++p) {
       const uint32_t* rec = hs + static_cast<int64_t>(p) * kPartWords;
       zero_hist(cnt);
       __syncthreads();
-      add_wraps(c, cnt, dw0, bin0 < 0x8000, rec + kPartPacked + 64, rec[kPartPacked + kHdrEvents]);
+      add_wraps(c, cnt, dw0, rev, rec + kPartPacked + 64, rec[kPartPacked + kHdrEvents]);
     }
   }
+}
+
+// One workgroup per head after the parts' records are written: their counts summed, the
+// window found from them.
+__global__ __launch_bounds__(kHistThreads) void calib_hist_window_kernel(HistArgs a) {
+  extern __shared__ uint32_t lds[];
+  const int64_t bh = blockIdx.x;
+  uint32_t* hs = a.hist + bh * a.head_words;
+  uint32_t c[kBinsPerThread];
+  head_counts(c, hs, a.P, lds + kCtlWords);
   window_from_counts(c, lds, hs, a, bh);
 }
 
@@ -720,26 +810,9 @@ __global__ __launch_bounds__(kHistThreads) void calib_cut_kernel(HistArgs a, Tai
   uint32_t* cnt = lds + kCtlWords;  // packed wrap counts (rare)
   const int tid = static_cast<int>(threadIdx.x);
   const int64_t bh = blockIdx.x;
-  const uint32_t* hs = a.hist + bh * a.head_words;
   const int bin0 = tid * kBinsPerThread;
-  const int dw0 = first_dword(bin0);
   uint32_t c[kBinsPerThread];
-#pragma unroll
-  for (int i = 0; i < kBinsPerThread; ++i) c[i] = 0;
-  uint32_t n_events = 0;
-  for (int p = 0; p < a.P; ++p) {
-    const uint32_t* rec = hs + static_cast<int64_t>(p) * kPartWords;
-    add_packed(c, rec, dw0, bin0 < 0x8000);
-    n_events += rec[kPartPacked + kHdrEvents];
-  }
-  if (n_events) {
-    for (int p = 0; p < a.P; ++p) {
-      const uint32_t* rec = hs + static_cast<int64_t>(p) * kPartWords;
-      zero_hist(cnt);
-      __syncthreads();
-      add_wraps(c, cnt, dw0, bin0 < 0x8000, rec + kPartPacked + 64, rec[kPartPacked + kHdrEvents]);
-    }
-  }
+  head_counts(c, a.hist + bh * a.head_words, a.P, cnt);
   uint32_t sum = 0;
 #pragma unroll
   for (int i = 0; i < kBinsPerThread; ++i) sum += c[i];
@@ -916,7 +989,9 @@ int hist_plan(int64_t nb, bool bshd, int vpv, int64_t B, int64_t H, int64_t S, i
   }
   if (hp.part_vecs * vpv > kMaxPartValues) return FA3Q_ERR_SHAPE;
   if (kHistMaxBatches * H * hp.P > (int64_t{1} << 31) - 1) return FA3Q_ERR_SHAPE;
-  hp.head_words = std::max<int64_t>(hp.P * kPartWords, kBins);
+  // P records, then (many parts) the summed counts; at least 65536 words (the merge search's
+  // inc[] of heavy groups reuses the start of the region)
+  hp.head_words = hp.P >= kSumMinParts ? hp.P * kPartWords + kBins : std::max<int64_t>(hp.P * kPartWords, kBins);
   hp.bytes = static_cast<size_t>(H * hp.head_words) * sizeof(uint32_t);
   return FA3Q_OK;
 }
@@ -954,6 +1029,9 @@ int hist_launch(const void* const* xs, int64_t nb, int64_t H, bool f16, int64_t 
       hipLaunchKernelGGL((calib_hist_kernel<false, true, false>), g, blk, 0, stream, ha);
     else
       hipLaunchKernelGGL((calib_hist_kernel<false, false, false>), g, blk, 0, stream, ha);
+    if (hp.P >= kSumMinParts)
+      hipLaunchKernelGGL(calib_hist_sum_kernel, dim3(static_cast<unsigned>(nb * H * kSumSlices)), dim3(kSumThreads), 0,
+                         stream, ha);
     hipLaunchKernelGGL(calib_hist_window_kernel, dim3(static_cast<unsigned>(nb * H)), blk, kWinLds, stream, ha);
   }
   return launch_status();
@@ -983,6 +1061,9 @@ int hist_f32_collect(const void* x, int64_t H, int64_t t, int64_t K, const HistP
     hipLaunchKernelGGL((calib_hist_kernel<false, true, true>), g_parts, blk, 0, stream, ha);
   else
     hipLaunchKernelGGL((calib_hist_kernel<false, false, true>), g_parts, blk, 0, stream, ha);
+  if (hp.P >= kSumMinParts)
+    hipLaunchKernelGGL(calib_hist_sum_kernel, dim3(static_cast<unsigned>(H * kSumSlices)), dim3(kSumThreads), 0, stream,
+                       ha);
   hipLaunchKernelGGL(calib_cut_kernel, dim3(static_cast<unsigned>(H)), blk, kCutLds, stream, ha, cut, best);
   if (hp.rows)
     hipLaunchKernelGGL(calib_collect_kernel<true>, g_parts, blk, 0, stream, ha, cut, lists, stride);

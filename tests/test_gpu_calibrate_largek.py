@@ -149,3 +149,29 @@ def test_sample_that_misses_the_tails(fa):
         if h == 2:
             flat[:, h, : S * D // 2] = 100.0  # and half the head beyond the other bound
     _check(fa, x, ratio, "sample misses the tails")
+
+
+@pytest.mark.parametrize("layout", ["BHSD", "BSHD"])
+def test_few_heads_many_parts(fa, layout):
+    # two heads of 8.4M values: 16 parts per head (head-major) or 8 (token-major rows), whose
+    # records the summing kernel adds up across many workgroups; head 0 holds one value only
+    # (its counters wrap in every part), head 1 Student-t(3) values and two signed zeros
+    B, H, S, D = 1, 2, 8192, 1024
+    N = B * S * D
+    g = torch.Generator(device="cpu")
+    g.manual_seed(71)
+    x = torch.empty((B, H, S, D), dtype=torch.bfloat16)
+    x[0, 0] = 1.5
+    sigma = synth.head_sigmas(1, seed=72)
+    x[0, 1] = synth.activations((1, 1, S, D), sigma, law="t3", dtype=torch.bfloat16, seed=73)[0, 0]
+    x[0, 1, 0, :2] = torch.tensor([0.0, -0.0], dtype=torch.bfloat16)
+    xl = x if layout == "BHSD" else x.transpose(1, 2).contiguous()
+    xl = xl.to(DEV)
+    for ratio in (0.999, 0.5):
+        K = _k_of(ratio, N)
+        log(f"few heads many parts: {layout} ratio={ratio} K={K}")
+        wmin, wmax = fa.fa3q_calibrate_ex([xl], ratio, layout=layout)
+        torch.cuda.synchronize()
+        lo, hi = oracle_windows(x, ratio)
+        assert_bits_equal(f32(wmin[0]), lo, f"{layout} ratio {ratio} win_min")
+        assert_bits_equal(f32(wmax[0]), hi, f"{layout} ratio {ratio} win_max")

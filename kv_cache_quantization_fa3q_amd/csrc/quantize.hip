@@ -161,7 +161,7 @@ __global__ __launch_bounds__(kThreads) void quantize_k_kernel(QuantArgs a) {
     for (int pass = 0; pass * kThreads * kNope < nn || pass * kThreads * kRope < nrp; ++pass) {
       u32x4 xn[kNope], xr[kRope];
       int on[kNope], orr[kRope];
-      int hv[kNope];  // token-major: each nope vector's head
+      int rv[kNope];  // token-major: each nope vector's row in the item
       // Loads are unconditional (a vector past the item's end re-reads its last vector and is
       // not stored), so they issue back to back instead of one exec-masked block at a time.
 #pragma unroll
@@ -170,10 +170,7 @@ __global__ __launch_bounds__(kThreads) void quantize_k_kernel(QuantArgs a) {
         const int qc = min(q, nn - 1);
         const int row = qc / Un, unit = qc - row * Un;
         on[j] = q < nn ? row * a.Dn + unit * 8 : -1;
-        if constexpr (kTok) {
-          const int hr = hh + row;  // < H + kRowsPerItem
-          hv[j] = hr < a.H ? hr : hr % a.H;
-        }
+        rv[j] = row;
         xn[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kin + static_cast<int64_t>(row) * Dk + unit * 8));
       }
       if (Ur > 0) {
@@ -188,11 +185,19 @@ __global__ __launch_bounds__(kThreads) void quantize_k_kernel(QuantArgs a) {
       }
       // the scales are read after the data loads are issued, so their latency hides behind theirs
       if constexpr (kTok) {
+        // lane l < kRowsPerItem takes row l's head (rows of one item are consecutive, row g of
+        // head g % H): one scale load and one reciprocal per lane, which each vector then
+        // fetches from its row's lane
+        const int hr = hh + (tid & (kRowsPerItem - 1));  // < H + kRowsPerItem
+        const float s_row = a.scale[hr < a.H ? hr : hr % a.H];
+        const float r_row = 1.0f / s_row;
 #pragma unroll
         for (int j = 0; j < kNope; ++j) {
           if (on[j] >= 0) {
-            const HeadQ hq = head_q(a.scale[hv[j]]);
-            const u32x2 o = hq.zero ? u32x2{0u, 0u} : quant8<kF16>(xn[j], hq.s, hq.r, hq.fast);
+            const float sj = __shfl(s_row, rv[j]);
+            const float rj = __shfl(r_row, rv[j]);
+            const bool fast = fabsf(sj) >= 0x1p-100f && fabsf(sj) <= 0x1p100f;  // as head_q
+            const u32x2 o = sj == 0.0f ? u32x2{0u, 0u} : quant8<kF16>(xn[j], sj, rj, fast);
             __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(qout + on[j]));
           }
         }

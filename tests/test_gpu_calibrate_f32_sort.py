@@ -184,3 +184,27 @@ def test_batches_with_running_statistics(fa):
     wmin2, wmax2 = fa.fa3q_calibrate_ex(xt, ratio, layout="BSHD")
     assert_bits_equal(wmin2.cpu().numpy(), win_min.cpu().numpy(), "BSHD vs BHSD win_min")
     assert_bits_equal(wmax2.cpu().numpy(), win_max.cpu().numpy(), "BSHD vs BHSD win_max")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
+def test_tiny_heads_every_ratio(fa, dtype):
+    # (B,S,H,D) heads of 4 to 24 values, every target count t = 1 .. N: lists far shorter than
+    # one sort tile (float32) or one histogram part (16-bit), K = N down to 1, heads of one
+    # repeated value, and a head with signed zeros
+    g = torch.Generator(device="cpu")
+    g.manual_seed(5)
+    D = 4 if dtype == torch.float32 else 8
+    for B, S, H in ((1, 1, 3), (2, 3, 2), (1, 3, 5)):
+        N = B * S * D
+        x = torch.randn((B, S, H, D), generator=g).to(dtype)
+        x[:, :, 0, :] = 0.75                      # head 0: one value
+        if H > 2:
+            x[:, :, 2, :] = torch.tensor([0.0, -0.0] * (D // 2)).to(dtype)
+        xd = x.to(DEV)
+        for t in range(1, N + 1):
+            ratio = (t + 0.5) / N if t < N else 1.0  # int(ratio * N) == t
+            assert int(ratio * N) == t
+            wmin, wmax = fa.fa3q_calibrate_ex([xd], ratio, layout="BSHD")
+            lo, hi = _oracle(x.float() if dtype != torch.float32 else x, ratio, "BSHD")
+            assert_bits_equal(wmin[0].cpu().numpy(), lo, f"{dtype} {(B, S, H, D)} t={t} win_min")
+            assert_bits_equal(wmax[0].cpu().numpy(), hi, f"{dtype} {(B, S, H, D)} t={t} win_max")

@@ -76,6 +76,7 @@ constexpr size_t kWinLds = kCtlWords * 4 + std::max<size_t>(static_cast<size_t>(
 
 static_assert(kBinsPerThread * kHistThreads == kBins, "bins per thread");
 static_assert(kSumSlices * kSumDwords * 2 == kBins, "summing slices cover the bins");
+static_assert(kBins / 8 % kHistThreads == 0 && kBinsPerThread == 64, "a record is 8 chunks of 16 bytes per thread");
 static_assert(kWinLds <= kLdsLimit, "LDS budget");
 static_assert(kWinLds >= kCtlWords * 4 + kBins * 2, "the window kernel counts wraps in its LDS");
 // the merge-path search: a 16-bit prefix of every key and a prefix per 16 keys (and N) after the
@@ -425,8 +426,11 @@ __device__ void window_from_counts(uint32_t (&c)[kBinsPerThread], uint32_t* lds,
   const uint32_t ub0 = static_cast<uint32_t>(bin0);
   const uint32_t cut_lo = a_max >= ub0 ? min(a_max - ub0 + 1, static_cast<uint32_t>(kBinsPerThread)) : 0u;
   const uint32_t cut_hi = m_min > ub0 ? min(m_min - ub0, static_cast<uint32_t>(kBinsPerThread)) : 0u;
+  // a thread whose keys hold no value, or all lie between the two ranges, lists nothing: it
+  // skips the loops (most threads: values occupy a small part of the 65536 keys)
+  const bool lists = sum > 0u && (cut_lo > 0u || cut_hi < static_cast<uint32_t>(kBinsPerThread));
   uint32_t nz = 0;
-  {
+  if (lists) {
     const uint32_t lo = opaque(cut_lo), hi = opaque(cut_hi);
 #pragma unroll
     for (int i = 0; i < kBinsPerThread; ++i)
@@ -439,15 +443,17 @@ __device__ void window_from_counts(uint32_t (&c)[kBinsPerThread], uint32_t* lds,
   uint64_t best = ~uint64_t{0};
   uint32_t best_hi = 0;
   if (in_lds) {
-    uint32_t run = pre0, j = j0;
-    const uint32_t lo = opaque(cut_lo), hi = opaque(cut_hi);
+    if (nz) {
+      uint32_t run = pre0, j = j0;
+      const uint32_t lo = opaque(cut_lo), hi = opaque(cut_hi);
 #pragma unroll
-    for (int i = 0; i < kBinsPerThread; ++i) {
-      run = opaque(run + c[i]);
-      if (c[i] && (static_cast<uint32_t>(i) < lo || static_cast<uint32_t>(i) >= hi)) {
-        inc_l[j] = run;
-        key_l[j] = static_cast<uint16_t>(bin0 + i);
-        ++j;
+      for (int i = 0; i < kBinsPerThread; ++i) {
+        run = opaque(run + c[i]);
+        if (c[i] && (static_cast<uint32_t>(i) < lo || static_cast<uint32_t>(i) >= hi)) {
+          inc_l[j] = run;
+          key_l[j] = static_cast<uint16_t>(bin0 + i);
+          ++j;
+        }
       }
     }
     __syncthreads();
@@ -762,13 +768,46 @@ __device__ __forceinline__ void head_counts(uint32_t (&c)[kBinsPerThread], const
     return;
   }
   const int dw0 = first_dword(bin0);
-#pragma unroll
-  for (int i = 0; i < kBinsPerThread; ++i) c[i] = 0;
   uint32_t n_events = 0;
+  // Each record goes through LDS: coalesced 16-byte loads in, then every thread takes its 32
+  // dwords (read straight from global memory, a wave's loads would touch 64 lines each).
+  // 16-byte chunk i sits at chunk i ^ ((i >> 3) & 7), so the eight chunks of a thread's block
+  // land in different banks from its neighbours'.  (Loading two records at once spills: the
+  // 64 counts hold half the registers.)
+  constexpr int kChunks = kBins / 8 / kHistThreads;
+  uint4* st = reinterpret_cast<uint4*>(cnt);
+  const int blk = dw0 / 32;  // the thread's 8 chunks: blk * 8 + q
+  auto stage = [&](const uint4 (&v)[kChunks]) {
+#pragma unroll
+    for (int k = 0; k < kChunks; ++k) {
+      const int i = tid + k * kHistThreads;
+      st[i ^ ((i >> 3) & 7)] = v[k];
+    }
+  };
+  auto take = [&](bool first) {  // first: the counts start from this record
+#pragma unroll
+    for (int q = 0; q < kBinsPerThread / 8; ++q) {
+      const int qq = rev ? 7 - q : q;
+      const uint4 w4 = st[8 * blk + (qq ^ (blk & 7))];
+      const uint32_t w[4] = {rev ? w4.w : w4.x, rev ? w4.z : w4.y, rev ? w4.y : w4.z, rev ? w4.x : w4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = w[e] & 0xffffu, hi = w[e] >> 16;
+        c[8 * q + 2 * e] = (first ? 0u : c[8 * q + 2 * e]) + (rev ? hi : lo);
+        c[8 * q + 2 * e + 1] = (first ? 0u : c[8 * q + 2 * e + 1]) + (rev ? lo : hi);
+      }
+    }
+  };
   for (int p = 0; p < P; ++p) {
     const uint32_t* rec = hs + static_cast<int64_t>(p) * kPartWords;
-    add_packed(c, rec, dw0, rev);
+    uint4 v[kChunks];
+#pragma unroll
+    for (int k = 0; k < kChunks; ++k) v[k] = reinterpret_cast<const uint4*>(rec)[tid + k * kHistThreads];
     n_events += rec[kPartPacked + kHdrEvents];
+    stage(v);
+    __syncthreads();
+    take(p == 0);
+    __syncthreads();
   }
   if (n_events) {
     // logged wraps (rare: a pattern past 65535 values in one part)

@@ -417,7 +417,10 @@ int fa3q_calibrate_batches(const void* const* xs, int64_t nb, int dtype, int64_t
 
 /*
  * Device workspace fa3q_decode_latent needs, in bytes (0 when none is needed or
- * the arguments are invalid).
+ * the arguments are invalid): the partial results of the token splits when there
+ * are several, and with H >= 128 one word per 32 heads and split (a split whose
+ * scores outgrow the reference its first tile set is marked there and recomputed
+ * by a second launch).  No state is kept between calls.
  */
 size_t fa3q_decode_latent_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t Dl);
 

@@ -51,6 +51,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kLatThreads = 512;  // eight waves: four pairs of 16 heads
 constexpr int kLatHeads = 64;     // heads per workgroup
@@ -69,6 +70,9 @@ struct LatentArgs {
   float* out;             // (B,H,Dl)
   float* ws_ml;           // [B*H*nsplit][2]
   float* ws_o;            // [B*H*nsplit][Dl]
+  // wide kernel: [B][ceil(H/128)][nsplit][4] one word per wave, 1 when the wave gave up its
+  // split; the split kernel, given them, recomputes only the 64-head groups of such waves
+  uint32_t* flags;
   int64_t T;
   int32_t H;
   int32_t groups;         // ceil(H / 64)
@@ -147,6 +151,13 @@ __global__ __launch_bounds__(kLatThreads) void latent_split_kernel(LatentArgs a)
   const int rest = static_cast<int>(blockIdx.x / a.nsplit);
   const int grp = rest % a.groups;
   const int b = rest / a.groups;
+  if (a.flags != nullptr) {
+    // recompute only what the wide kernel gave up: 64-head group grp is waves 2(grp%2) and
+    // 2(grp%2)+1 of the wide workgroup (b, grp/2, split) (uniform over the workgroup)
+    const uint32_t* f = a.flags + ((static_cast<int64_t>(b) * ((a.groups + 1) / 2) + grp / 2) * a.nsplit + split) * 4 +
+                        2 * (grp % 2);
+    if ((f[0] | f[1]) == 0u) return;
+  }
   const int pair = wave & 3, half = wave >> 2;  // the partner is wave ^ 4
   const int head = grp * kLatHeads + pair * 16 + hl;
   const bool hv = head < a.H;
@@ -401,6 +412,292 @@ __global__ __launch_bounds__(kLatThreads) void latent_split_kernel(LatentArgs a)
   }
 }
 
+// ---- 128 heads per workgroup: one wave of 32 heads per SIMD on v_mfma_f32_32x32x16_bf16.
+//   S^T (32 tokens x 32 heads) = K (tokens x 16 dims) . Q^T (16 dims x heads), per k-step
+//   O^T (32 dims x 32 heads)  += V^T (dims x 16 tokens) . P^T (16 tokens x heads)
+// A lane holds head lane % 32; its half hh = lane / 32 holds the scores of tokens
+// 8i + 4hh + j (i, j < 4) of a tile, which are k-slots 8hh .. 8hh+7 of the two PV k-steps
+// (i < 2, then i >= 2): in the transposed LDS rows token t of a tile sits at slot
+// 16(t/16) + 8((t/4)%2) + 4((t/8)%2) + t%4.  Each staged operand read (1 KB per wave) feeds a
+// 32-head MFMA, so a tile is read from LDS once per 32 heads, and no scores are exchanged
+// between waves.  The RoPE part of the query sits in LDS (the latent part and the 512 output
+// dims fill the registers).
+//
+// No rescale in the tile loop: a head's reference mu is the max of its split's first tile,
+// and weights 2^(score - mu) stay within float32 and bf16 range while no later score exceeds
+// mu + 64.  Scaling the 256 output accumulators on the rare tile that breaks this would need
+// registers the loop does not have, so a wave whose head meets such a tile marks its split
+// in `flags` and runs on (its output is then not used): the split kernel, launched after this
+// one with the flags, recomputes those splits.
+constexpr int kWideThreads = 256;  // four waves, one per SIMD
+constexpr int kWideHeads = 128;    // 32 heads per wave
+
+template <int DL, int DR>
+__global__ __launch_bounds__(kWideThreads) void latent_wide_kernel(LatentArgs a) {
+  constexpr int KS = DL / 16;          // latent k-steps of the score product
+  constexpr int RS = DR / 16;          // RoPE k-steps
+  constexpr int OT = DL / 32;          // 32-dim output tiles
+  constexpr int KROW = DL + 8;         // bf16 per row-major latent row in LDS
+  constexpr int RROW = DR + 8;         // bf16 per RoPE row in LDS
+  constexpr int VROW = kTT;            // bf16 per transposed latent row (one per dim)
+  constexpr int DC = DL / 16;          // 16-code chunks per latent row
+  constexpr int UNITS = (kTT / 4) * DC;  // staging units of 4 tokens x 16 dims
+  static_assert(UNITS <= kWideThreads, "at most one staging unit per thread");
+  constexpr int RPR = DR > 0 ? DR / 8 : 1;  // 16-byte RoPE chunks per row
+  constexpr int RCH = kTT * DR / 8;
+  static_assert(RCH <= kWideThreads, "at most one RoPE chunk per thread");
+  constexpr float kLazy = 64.0f;       // log2 headroom of the weights over the reference
+  __shared__ __align__(16) uint16_t klat_buf[2][kTT * KROW];
+  __shared__ __align__(16) uint16_t vt_buf[2][DL * VROW];
+  __shared__ __align__(16) uint16_t krope_buf[2][DR > 0 ? kTT * RROW : 8];
+  constexpr int QROW = DR + 8;         // bf16 per RoPE query row in LDS (padded: 128-byte rows conflict)
+  __shared__ __align__(16) uint16_t qrope[DR > 0 ? kWideHeads * QROW : 8];  // [head][QROW]
+
+  const int tid = static_cast<int>(threadIdx.x);
+  const int wave = tid / kWave;
+  const int lane = tid % kWave;
+  const int hc = lane & 31, hh = lane >> 5;
+
+  const int split = static_cast<int>(blockIdx.x % a.nsplit);
+  const int rest = static_cast<int>(blockIdx.x / a.nsplit);
+  const int grp = rest % a.groups;
+  const int b = rest / a.groups;
+  const int head = grp * kWideHeads + wave * 32 + hc;
+  const bool hv = head < a.H;
+  const int64_t t_begin = static_cast<int64_t>(split) * a.split_len;
+  const int64_t t_end = min(a.T, t_begin + a.split_len);
+
+  const int8_t* cbase = a.cq + static_cast<int64_t>(b) * a.T * DL;
+  const uint16_t* rbase = a.kr + static_cast<int64_t>(b) * a.T * DR;
+
+  // this thread's staging unit: tokens 4tg .. 4tg+3, latent dims 16dc .. 16dc+15
+  const int tg = tid % 8, dc = tid / 8;
+  const bool has_unit = UNITS == kWideThreads || tid < UNITS;
+  const int rr = tid / RPR, rk = tid % RPR;
+  const bool has_rope = DR > 0 && (RCH == kWideThreads || tid < RCH);
+
+  u32x4v xs[4];
+  u32x4v xr;
+  // global -> registers for tile t0 (rows past the end re-read the last row; masked later)
+  auto fetch = [&](int64_t t0) {
+    if (has_unit) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t tok = min(t0 + 4 * tg + r, t_end - 1);
+        xs[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(cbase + tok * DL + 16 * dc));
+      }
+    }
+    if (has_rope) {
+      const int64_t tok = min(t0 + rr, t_end - 1);
+      xr = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(rbase + tok * DR + 8 * rk));
+    }
+  };
+  // registers -> LDS buffer `buf`: the codes widened to bf16 (exact) once, written row-major
+  // and transposed.  Transposed row R (dim) lives at row R ^ ((R >> 4) & 3) with its 16-byte
+  // chunks XORed by 2 ((R >> 2) & 1), so the staging writes and the PV operand reads both
+  // spread over the banks.
+  auto stage = [&](int buf) {
+    if (has_unit) {
+      uint16_t* klat = klat_buf[buf];
+      uint16_t* vt = vt_buf[buf];
+      float f[4][16];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) f[r][j] = code_f32(xs[r][j / 4], j % 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        uint32_t h[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) h[i] = pack_bf16(f[r][2 * i], f[r][2 * i + 1]);
+        uint16_t* row = klat + (4 * tg + r) * KROW + 16 * dc;
+        *reinterpret_cast<uint4*>(row) = make_uint4(h[0], h[1], h[2], h[3]);
+        *reinterpret_cast<uint4*>(row + 8) = make_uint4(h[4], h[5], h[6], h[7]);
+      }
+      const int chunk = 2 * (tg / 4) + (tg % 2);  // slots 4tg' .. of tokens 4tg .. 4tg+3
+      const int half8 = (tg / 2) % 2;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int prow = (16 * dc + j) ^ (dc & 3);
+        const int pch = chunk ^ (((j >> 2) & 1) << 1);
+        *reinterpret_cast<uint2*>(vt + prow * VROW + 8 * pch + 4 * half8) =
+            make_uint2(pack_bf16(f[0][j], f[1][j]), pack_bf16(f[2][j], f[3][j]));
+      }
+    }
+    if constexpr (DR > 0) {
+      if (has_rope) *reinterpret_cast<u32x4v*>(krope_buf[buf] + rr * RROW + 8 * rk) = xr;
+    }
+  };
+
+  // the latent part of the query as B operands (Q^T: dims x heads): lane holds dims
+  // 16kk + 8hh .. +7 of its head; heads past H read as zero
+  bf16x8 ql[KS];
+  {
+    const uint16_t* qrow = a.q + (static_cast<int64_t>(b) * a.H + (hv ? head : 0)) * (DL + DR);
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const uint4 u = hv ? *reinterpret_cast<const uint4*>(qrow + 16 * kk + 8 * hh) : make_uint4(0, 0, 0, 0);
+      ql[kk] = as_bf16x8(u);
+    }
+  }
+  if constexpr (DR > 0) {
+    for (int c = tid; c < kWideHeads * DR / 8; c += kWideThreads) {
+      const int hq = c / (DR / 8), k8 = c % (DR / 8);
+      const int hg = grp * kWideHeads + hq;
+      const uint4 u = hg < a.H ? *reinterpret_cast<const uint4*>(a.q + (static_cast<int64_t>(b) * a.H + hg) * (DL + DR) +
+                                                                 DL + 8 * k8)
+                               : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(qrope + hq * QROW + 8 * k8) = u;
+    }
+  }
+  const float s = a.scale[0];
+
+  f32x16 o[OT];  // output dims 32dt + 8i + 4hh + j at o[dt][4i + j]
+#pragma unroll
+  for (int dt = 0; dt < OT; ++dt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) o[dt][v] = 0.0f;
+  float mu = -INFINITY, l = 0.0f;
+  bool gave_up = false;
+
+  fetch(t_begin);
+  stage(0);
+  if (t_begin + kTT < t_end) fetch(t_begin + kTT);
+  __syncthreads();
+  int buf = 0;
+  float p[16];
+  // Each pass computes tile t0 from buffer `buf` while tile t0 + 32 (in registers) is staged
+  // into the other buffer and tile t0 + 64 is fetched; one barrier per tile.
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += kTT, buf ^= 1) {
+    const uint16_t* klat = klat_buf[buf];
+    f32x16 sc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sc[v] = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const uint4 w = *reinterpret_cast<const uint4*>(klat + hc * KROW + 16 * kk + 8 * hh);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(w), ql[kk], sc, 0, 0, 0);
+    }
+    {
+      // keep kSDepth operand reads in flight ahead of the score MFMAs
+      constexpr int kSDepth = KS < 6 ? KS : 6;
+      __builtin_amdgcn_sched_group_barrier(0x100, kSDepth, 0);  // DS reads
+#pragma unroll
+      for (int i = 0; i < KS - kSDepth; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kSDepth, 0);
+    }
+    // the other buffer was last read before the previous barrier; staged and fetched
+    // unconditionally (past the end the fetch re-reads the last row and the buffer is never read)
+    stage(buf ^ 1);
+    fetch(t0 + 2 * kTT);
+    // s <q_abs, c> + <q_rope, r>: the latent part scaled, then the RoPE k-steps added on
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sc[v] *= s;
+    if constexpr (DR > 0) {
+      const uint16_t* krope = krope_buf[buf];
+#pragma unroll
+      for (int kk = 0; kk < RS; ++kk) {
+        const uint4 w = *reinterpret_cast<const uint4*>(krope + hc * RROW + 16 * kk + 8 * hh);
+        const uint4 qv = *reinterpret_cast<const uint4*>(qrope + (wave * 32 + hc) * QROW + 16 * kk + 8 * hh);
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(w), as_bf16x8(qv), sc, 0, 0, 0);
+      }
+    }
+    // scores (log2 domain) of the lane's head over its 16 tokens; a split's last tile may
+    // be partial (uniform branch)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) p[v] = sc[v] * a.sm_log2;
+    if (t_end - t0 < kTT) {
+      const int nv = static_cast<int>(t_end - t0);
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if (8 * (v / 4) + 4 * hh + (v % 4) >= nv) p[v] = -INFINITY;
+    }
+    float rmax = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) rmax = fmaxf(rmax, p[v]);
+    {
+      const auto m = __builtin_amdgcn_permlane32_swap(__float_as_uint(rmax), __float_as_uint(rmax), false, false);
+      rmax = fmaxf(__uint_as_float(m[0]), __uint_as_float(m[1]));  // finite: a tile holds a valid token
+    }
+    if (__builtin_amdgcn_ballot_w64(rmax > mu + kLazy) != 0) {
+      // the first tile sets every head's reference (nothing is accumulated yet); on a later
+      // tile the wave gives its split up
+      if (t0 == t_begin)
+        mu = rmax;
+      else
+        gave_up = true;
+    }
+    // ---- weights against mu, then O^T += V^T . P^T with the weights as two bf16 terms
+    float rsum = 0.0f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      p[v] = __builtin_amdgcn_exp2f(p[v] - mu);
+      rsum += p[v];
+    }
+    l += rsum;  // this lane's part; the two lanes of a head are summed once, at the end
+    bf16x8 phi[2], plo[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        phi[ks][e] = static_cast<__bf16>(p[8 * ks + e]);
+        plo[ks][e] = static_cast<__bf16>(p[8 * ks + e] - static_cast<float>(phi[ks][e]));  // exact in float32
+      }
+    {
+      // row 32dt + hc sits at 32dt + (hc ^ ((2(dt%2) + hc/16) % 4)): four lane bases, then
+      // offsets that are constants of (dt, ks)
+      const uint16_t* vt = vt_buf[buf];
+      const uint16_t* vb[2][2];
+#pragma unroll
+      for (int par = 0; par < 2; ++par)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          vb[par][ks] = vt + (hc ^ ((2 * par + (hc >> 4)) & 3)) * VROW + 8 * ((2 * ks + hh) ^ (((hc >> 2) & 1) << 1));
+      // four output tiles at a time, so that consecutive MFMAs accumulate into different tiles
+      // (one tile's four MFMAs back to back wait on each other's results)
+      constexpr int kG = OT < 4 ? OT : 4;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int d0 = 0; d0 < OT; d0 += kG) {
+          uint4 w[kG];
+#pragma unroll
+          for (int i = 0; i < kG; ++i)
+            w[i] = *reinterpret_cast<const uint4*>(vb[(d0 + i) & 1][ks] + 32 * (d0 + i) * VROW);
+#pragma unroll
+          for (int i = 0; i < kG; ++i)
+            o[d0 + i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(w[i]), phi[ks], o[d0 + i], 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < kG; ++i)
+            o[d0 + i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(w[i]), plo[ks], o[d0 + i], 0, 0, 0);
+        }
+    }
+    __syncthreads();
+  }
+
+  l += __shfl_xor(l, 32);
+  if (lane == 0)
+    a.flags[((static_cast<int64_t>(b) * a.groups + grp) * a.nsplit + split) * 4 + wave] = gave_up ? 1u : 0u;
+  if (!hv || gave_up) return;
+  const int64_t row = static_cast<int64_t>(b) * a.H + head;
+  const float f = a.nsplit == 1 ? s / l : s;
+  float* dst = a.nsplit == 1 ? a.out + row * DL : a.ws_o + (row * a.nsplit + split) * DL;
+#pragma unroll
+  for (int dt = 0; dt < OT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<float4*>(dst + 32 * dt + 8 * i + 4 * hh) =
+          make_float4(o[dt][4 * i] * f, o[dt][4 * i + 1] * f, o[dt][4 * i + 2] * f, o[dt][4 * i + 3] * f);
+  if (a.nsplit > 1 && hh == 0) {
+    const int64_t slot = row * a.nsplit + split;
+    a.ws_ml[2 * slot] = mu;
+    a.ws_ml[2 * slot + 1] = l;
+  }
+}
+
 // out = sum_s w_s o_s / sum_s w_s l_s with w_s = 2^(m_s - max m), per (b, h).
 __global__ __launch_bounds__(128) void latent_combine_kernel(LatentArgs a, int dl) {
   const int64_t row = blockIdx.x;
@@ -425,12 +722,15 @@ __global__ __launch_bounds__(128) void latent_combine_kernel(LatentArgs a, int d
 }
 
 struct LatentPlan {
+  bool wide;  // 128 heads per workgroup (latent_wide_kernel), else 64 (latent_split_kernel)
   int32_t groups, nsplit, split_len;
 };
 
 LatentPlan plan_latent(int64_t B, int64_t H, int64_t T) {
   LatentPlan p;
-  p.groups = static_cast<int32_t>((H + kLatHeads - 1) / kLatHeads);
+  p.wide = H >= kWideHeads;
+  const int64_t per = p.wide ? kWideHeads : kLatHeads;
+  p.groups = static_cast<int32_t>((H + per - 1) / per);
   const int64_t base = B * p.groups;
   int64_t ns = (kLatTargetGroups + base - 1) / base;
   ns = std::max<int64_t>(1, std::min(ns, (T + kLatMinSplit - 1) / kLatMinSplit));
@@ -455,21 +755,46 @@ bool latent_shape_ok(int64_t B, int64_t H, int64_t T, int64_t Dl) {
 
 using LatentFn = void (*)(LatentArgs);
 
+template <int DL, int DR>
+LatentFn pick_kernel(bool wide) {
+  return wide ? latent_wide_kernel<DL, DR> : latent_split_kernel<DL, DR>;
+}
+
 template <int DL>
-LatentFn pick_dr(int64_t dr) {
+LatentFn pick_dr(int64_t dr, bool wide) {
   switch (dr) {
-    case 0: return latent_split_kernel<DL, 0>;
-    case 32: return latent_split_kernel<DL, 32>;
-    default: return latent_split_kernel<DL, 64>;
+    case 0: return pick_kernel<DL, 0>(wide);
+    case 32: return pick_kernel<DL, 32>(wide);
+    default: return pick_kernel<DL, 64>(wide);
   }
 }
 
-LatentFn pick_latent(int64_t dl, int64_t dr) {
+LatentFn pick_latent(int64_t dl, int64_t dr, bool wide) {
   switch (dl) {
-    case 128: return pick_dr<128>(dr);
-    case 256: return pick_dr<256>(dr);
-    default: return pick_dr<512>(dr);
+    case 128: return pick_dr<128>(dr, wide);
+    case 256: return pick_dr<256>(dr, wide);
+    default: return pick_dr<512>(dr, wide);
   }
+}
+
+// Workspace layout: (reference, sum) per split slot and the unnormalised split outputs when
+// there are several splits; then the wide kernel's per-wave flags.
+struct LatentWs {
+  size_t ml, o, flags, bytes;
+};
+
+LatentWs latent_ws(int64_t B, int64_t H, int64_t Dl, const LatentPlan& p) {
+  LatentWs w{0, 0, 0, 0};
+  if (p.nsplit > 1) {
+    const size_t slots = static_cast<size_t>(B * H) * p.nsplit;
+    w.o = round_up(slots * 2 * sizeof(float), 256);
+    w.bytes = w.o + round_up(slots * static_cast<size_t>(Dl) * sizeof(float), 256);
+  }
+  if (p.wide) {
+    w.flags = w.bytes;
+    w.bytes += round_up(static_cast<size_t>(B) * p.groups * p.nsplit * 4 * sizeof(uint32_t), 256);
+  }
+  return w;
 }
 
 }  // namespace
@@ -479,10 +804,7 @@ using namespace fa3q;
 
 extern "C" size_t fa3q_decode_latent_workspace_bytes(int64_t B, int64_t H, int64_t T, int64_t Dl) {
   if (!latent_shape_ok(B, H, T, Dl) || !(Dl == 128 || Dl == 256 || Dl == 512)) return 0;
-  const LatentPlan p = plan_latent(B, H, T);
-  if (p.nsplit <= 1) return 0;
-  const size_t slots = static_cast<size_t>(B * H) * p.nsplit;
-  return round_up(slots * 2 * sizeof(float), 256) + slots * static_cast<size_t>(Dl) * sizeof(float);
+  return latent_ws(B, H, Dl, plan_latent(B, H, T)).bytes;
 }
 
 extern "C" int fa3q_decode_latent(const uint16_t* q, const int8_t* c_q, const float* scale, const uint16_t* k_rope,
@@ -495,33 +817,47 @@ extern "C" int fa3q_decode_latent(const uint16_t* q, const int8_t* c_q, const fl
       (Dr > 0 && !is_aligned(k_rope, 16)))
     return FA3Q_ERR_ALIGN;
   const LatentPlan p = plan_latent(B, H, T);
-  const size_t need = fa3q_decode_latent_workspace_bytes(B, H, T, Dl);
-  if (need > 0) {
-    if (!workspace || workspace_bytes < need) return FA3Q_ERR_WORKSPACE;
+  const LatentWs w = latent_ws(B, H, Dl, p);
+  if (w.bytes > 0) {
+    if (!workspace || workspace_bytes < w.bytes) return FA3Q_ERR_WORKSPACE;
     if (!is_aligned(workspace, 256)) return FA3Q_ERR_ALIGN;
   }
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
   LatentArgs a;
   a.q = q;
   a.cq = c_q;
   a.scale = scale;
   a.kr = k_rope;
   a.out = out;
-  const size_t slots = static_cast<size_t>(B * H) * p.nsplit;
-  a.ws_ml = need ? static_cast<float*>(workspace) : nullptr;
-  a.ws_o = need ? reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) +
-                                           round_up(slots * 2 * sizeof(float), 256))
-                : nullptr;
+  a.ws_ml = p.nsplit > 1 ? reinterpret_cast<float*>(ws) : nullptr;
+  a.ws_o = p.nsplit > 1 ? reinterpret_cast<float*>(ws + w.o) : nullptr;
+  a.flags = nullptr;
   a.T = T;
   a.H = static_cast<int32_t>(H);
   a.groups = p.groups;
   a.nsplit = p.nsplit;
   a.split_len = p.split_len;
   a.sm_log2 = sm_scale * 1.4426950408889634f;
-  const int64_t grid = B * p.groups * p.nsplit;
-  hipLaunchKernelGGL(pick_latent(Dl, Dr), dim3(static_cast<unsigned>(grid)), dim3(kLatThreads), 0,
-                     as_stream(stream), a);
+  hipStream_t s = as_stream(stream);
+  // Dl = 512 with a RoPE part of 0 or 32 features spills in the wide kernel's tile loop: those
+  // take the split kernel over the same splits (the workspace is the same)
+  if (p.wide && (Dl < 512 || Dr == 64)) {
+    a.flags = reinterpret_cast<uint32_t*>(ws + w.flags);
+    hipLaunchKernelGGL(pick_latent(Dl, Dr, true), dim3(static_cast<unsigned>(B * p.groups * p.nsplit)),
+                       dim3(kWideThreads), 0, s, a);
+    // the splits a wave gave up, recomputed by the split kernel over the same splits (its
+    // workgroups exit at once elsewhere)
+    LatentArgs f = a;
+    f.groups = static_cast<int32_t>((H + kLatHeads - 1) / kLatHeads);
+    hipLaunchKernelGGL(pick_latent(Dl, Dr, false), dim3(static_cast<unsigned>(B * f.groups * p.nsplit)),
+                       dim3(kLatThreads), 0, s, f);
+  } else {
+    a.groups = static_cast<int32_t>((H + kLatHeads - 1) / kLatHeads);
+    hipLaunchKernelGGL(pick_latent(Dl, Dr, false), dim3(static_cast<unsigned>(B * a.groups * p.nsplit)),
+                       dim3(kLatThreads), 0, s, a);
+  }
   if (p.nsplit > 1)
-    hipLaunchKernelGGL(latent_combine_kernel, dim3(static_cast<unsigned>(B * H)), dim3(128), 0, as_stream(stream), a,
+    hipLaunchKernelGGL(latent_combine_kernel, dim3(static_cast<unsigned>(B * H)), dim3(128), 0, s, a,
                        static_cast<int>(Dl));
   return launch_status();
 }

@@ -436,7 +436,10 @@ def test_decode_latent_rejections():
     assert call(ws=_p(128)) == L.FA3Q_ERR_ALIGN
     assert lib.fa3q_decode_latent_workspace_bytes(64, 128, 4096, 512) > 0
     assert lib.fa3q_decode_latent_workspace_bytes(64, 128, 4096, 192) == 0
-    assert lib.fa3q_decode_latent_workspace_bytes(1024, 128, 64, 512) == 0   # one split: no workspace
+    # one split: no partial outputs; 128 heads or more still take one flag word per wave of the
+    # 32-head kernel (which gives a split up on scores that outgrow its reference)
+    assert lib.fa3q_decode_latent_workspace_bytes(1024, 64, 64, 512) == 0
+    assert lib.fa3q_decode_latent_workspace_bytes(1024, 128, 64, 512) == 1024 * 4 * 4
 
 
 @no_gpu_only

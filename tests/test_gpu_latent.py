@@ -58,6 +58,10 @@ CASES = [
     ("no_rope", (3, 16, 200, 128, 0)),
     ("one_token", (2, 64, 1, 512, 64)),
     ("short_tail", (2, 128, 97, 512, 64)),
+    # 160 heads: a full group of 128 and one of 32 (two waves with no head); the 32-head kernel
+    # at Dl = 256, and Dl = 512 without a RoPE part (the paired kernel over the same splits)
+    ("heads_160", (3, 160, 700, 256, 32)),
+    ("wide_no_rope", (2, 128, 300, 512, 0)),
 ]
 
 
@@ -87,16 +91,19 @@ def test_latent_decode_against_oracle(fa, name, shape):
         np.testing.assert_array_equal(got, np.broadcast_to(want[:, None], got.shape))
 
 
-def test_latent_decode_heads_with_equal_queries_agree(fa):
+@pytest.mark.parametrize("H,copies", [(64, (17, 63)), (128, (17, 19, 100, 127))], ids=["64_heads", "128_heads"])
+def test_latent_decode_heads_with_equal_queries_agree(fa, H, copies):
+    # the same query in other waves, lanes and (128 heads) head halves gives the same output row
     dev = torch.device("cuda:0")
-    B, H, T, Dl, Dr = 2, 64, 500, 512, 64
+    B, T, Dl, Dr = 2, 500, 512, 64
     cq, kr, scale = _latent_cache(fa, B, T, Dl, Dr, seed=77)
     q = synth.normal_tensor((B, H, Dl + Dr), dtype=torch.bfloat16, seed=78, device=dev)
-    q[:, 17] = q[:, 3]   # different wave and lane, same query
-    q[:, 63] = q[:, 3]
+    for h in copies:
+        q[:, h] = q[:, 3]
     out = fa.fa3q_decode_latent(q, cq, scale, kr, 0.07)
     torch.cuda.synchronize()
-    assert torch.equal(out[:, 17], out[:, 3]) and torch.equal(out[:, 63], out[:, 3])
+    for h in copies:
+        assert torch.equal(out[:, h], out[:, 3]), h
 
 
 def test_latent_decode_is_deterministic(fa):
@@ -110,23 +117,42 @@ def test_latent_decode_is_deterministic(fa):
     assert torch.equal(a, b)
 
 
-def test_latent_decode_with_scores_that_keep_growing(fa):
-    # One split per (b, head group) over 16 tiles whose scores climb by about 7 (log2) per
-    # tile for even heads, so those heads move their softmax reference again and again while
-    # the odd heads of the same waves (falling scores) keep theirs from the first tile
+GROWING = [
+    # (B, H, T, slope, period, climbing heads): RoPE feature 0 of token t is
+    # slope * (t % period), and the climbing heads' query has 4 there (the others -4): at slope
+    # 0.5 their scores climb by about 7 (log2) per 32-token tile
+    # 64 heads (paired kernel), one split of 16 tiles: even heads move their reference again
+    # and again while the odd heads of the same waves (falling scores) keep theirs
+    ("pairs", 256, 64, 512, 0.5, 512, "even"),
+    # 128 heads (32 per wave), one split: every wave gives its split up after about 9 tiles
+    # and the paired kernel recomputes it
+    ("wide_one_split", 256, 128, 512, 0.5, 512, "even"),
+    # 128 heads, 32 splits of 4 tiles, a climb of about 100 (log2) inside each split (scores
+    # kept below about 70, so float32 sums stay far inside the tolerance): every split is
+    # given up on its last tile
+    ("wide_splits", 8, 128, 4096, 1.7, 128, "even"),
+    # the same with only the first wave's heads climbing: that wave's 64-head group is
+    # recomputed, the other group keeps the wide kernel's output
+    ("wide_one_wave", 8, 128, 4096, 1.7, 128, "first32"),
+]
+
+
+@pytest.mark.parametrize("name,B,H,T,slope,period,climb", GROWING, ids=[g[0] for g in GROWING])
+def test_latent_decode_with_scores_that_keep_growing(fa, name, B, H, T, slope, period, climb):
     dev = torch.device("cuda:0")
-    B, H, T, Dl, Dr = 256, 64, 512, 128, 32
+    Dl, Dr = 128, 32
     rng = np.random.default_rng(97)
     codes = rng.integers(-20, 21, size=(B, T, Dl)).astype(np.int8)
     rope = np.zeros((B, T, Dr), np.float32)
-    rope[:, :, 0] = 0.5 * np.arange(T, dtype=np.float32)
+    rope[:, :, 0] = slope * (np.arange(T) % period).astype(np.float32)
     rope[:, :, 1:] = rng.standard_normal((B, T, Dr - 1)).astype(np.float32)
     rope_t = torch.from_numpy(rope).to(torch.bfloat16)
     q = synth.normal_tensor((B, H, Dl + Dr), dtype=torch.bfloat16, seed=98)
-    q[:, :, Dl] = torch.where(torch.arange(H) % 2 == 0, 4.0, -4.0).to(torch.bfloat16)
+    up = torch.arange(H) % 2 == 0 if climb == "even" else torch.arange(H) < 32
+    q[:, :, Dl] = torch.where(up, 4.0, -4.0).to(torch.bfloat16)
     scale = torch.tensor([0.01], dtype=torch.float32)
     sm = 1.0 / math.sqrt(Dl + Dr)
-    log(f"latent growing scores: B={B} H={H} T={T} Dl={Dl} Dr={Dr}")
+    log(f"latent growing scores {name}: B={B} H={H} T={T} Dl={Dl} Dr={Dr} slope={slope} climbing={climb}")
     out = fa.fa3q_decode_latent(q.to(dev), torch.from_numpy(codes).to(dev), scale.to(dev), rope_t.to(dev), sm)
     torch.cuda.synchronize()
     got = out.cpu().numpy()

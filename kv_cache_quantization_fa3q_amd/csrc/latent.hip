@@ -698,27 +698,49 @@ __global__ __launch_bounds__(kWideThreads) void latent_wide_kernel(LatentArgs a)
   }
 }
 
-// out = sum_s w_s o_s / sum_s w_s l_s with w_s = 2^(m_s - max m), per (b, h).
-__global__ __launch_bounds__(128) void latent_combine_kernel(LatentArgs a, int dl) {
-  const int64_t row = blockIdx.x;
-  const float* ml = a.ws_ml + 2 * row * a.nsplit;
+// out = sum_s w_s o_s / sum_s w_s l_s with w_s = 2^(m_s - max m), per (b, h).  A workgroup
+// of 256 threads takes 256 / (dl/4) rows, four dims per thread, with the splits' partials
+// loaded four at a time.
+constexpr int kCombineThreads = 256;
+
+__global__ __launch_bounds__(kCombineThreads) void latent_combine_kernel(LatentArgs a, int dl, int64_t rows) {
+  const int per_row = dl / 4;  // threads per row (dl is 128, 256 or 512)
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * (kCombineThreads / per_row) + threadIdx.x / per_row;
+  if (row >= rows) return;
+  const int d = 4 * (static_cast<int>(threadIdx.x) % per_row);
+  const int ns = a.nsplit;
+  const float* ml = a.ws_ml + 2 * row * ns;
   float mmax = -INFINITY;
-  for (int s = 0; s < a.nsplit; ++s) mmax = fmaxf(mmax, ml[2 * s]);
+  for (int s = 0; s < ns; ++s) mmax = fmaxf(mmax, ml[2 * s]);
   float den = 0.0f;
-  for (int s = 0; s < a.nsplit; ++s) den += exp2f(ml[2 * s] - mmax) * ml[2 * s + 1];
-  // four dims per thread (dl is a multiple of 16; rows and partials are 16-byte aligned)
-  for (int d = 4 * static_cast<int>(threadIdx.x); d < dl; d += 4 * static_cast<int>(blockDim.x)) {
-    float4 num = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    for (int s = 0; s < a.nsplit; ++s) {
-      const float w = exp2f(ml[2 * s] - mmax);
-      const float4 o = *reinterpret_cast<const float4*>(a.ws_o + (row * a.nsplit + s) * dl + d);
-      num.x += w * o.x;
-      num.y += w * o.y;
-      num.z += w * o.z;
-      num.w += w * o.w;
+  float4 num = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  const float* src = a.ws_o + row * ns * dl + d;
+  int s = 0;
+  for (; s + 4 <= ns; s += 4) {
+    float4 o[4];
+    float w[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) o[u] = *reinterpret_cast<const float4*>(src + static_cast<int64_t>(s + u) * dl);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      w[u] = exp2f(ml[2 * (s + u)] - mmax);
+      den += w[u] * ml[2 * (s + u) + 1];
+      num.x += w[u] * o[u].x;
+      num.y += w[u] * o[u].y;
+      num.z += w[u] * o[u].z;
+      num.w += w[u] * o[u].w;
     }
-    *reinterpret_cast<float4*>(a.out + row * dl + d) = make_float4(num.x / den, num.y / den, num.z / den, num.w / den);
   }
+  for (; s < ns; ++s) {
+    const float4 o = *reinterpret_cast<const float4*>(src + static_cast<int64_t>(s) * dl);
+    const float w = exp2f(ml[2 * s] - mmax);
+    den += w * ml[2 * s + 1];
+    num.x += w * o.x;
+    num.y += w * o.y;
+    num.z += w * o.z;
+    num.w += w * o.w;
+  }
+  *reinterpret_cast<float4*>(a.out + row * dl + d) = make_float4(num.x / den, num.y / den, num.z / den, num.w / den);
 }
 
 struct LatentPlan {
@@ -856,8 +878,10 @@ extern "C" int fa3q_decode_latent(const uint16_t* q, const int8_t* c_q, const fl
     hipLaunchKernelGGL(pick_latent(Dl, Dr, false), dim3(static_cast<unsigned>(B * a.groups * p.nsplit)),
                        dim3(kLatThreads), 0, s, a);
   }
-  if (p.nsplit > 1)
-    hipLaunchKernelGGL(latent_combine_kernel, dim3(static_cast<unsigned>(B * H)), dim3(128), 0, s, a,
-                       static_cast<int>(Dl));
+  if (p.nsplit > 1) {
+    const int64_t rows = B * H, per_wg = kCombineThreads / (Dl / 4);
+    hipLaunchKernelGGL(latent_combine_kernel, dim3(static_cast<unsigned>((rows + per_wg - 1) / per_wg)),
+                       dim3(kCombineThreads), 0, s, a, static_cast<int>(Dl), rows);
+  }
   return launch_status();
 }

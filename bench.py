@@ -538,8 +538,9 @@ def run(args, only, pool, workers) -> int:
         del long_x
 
     if "calibrate_f32" in only:
-        # one float32 calibration batch (8,128,2048,128): the tail lists at ratio 0.9999, the
-        # collect-and-sort path past them (0.99, 0.9) and for (B,S,H,D) input
+        # one float32 calibration batch (8,128,2048,128): the tail lists at ratio 0.9999 (rows of
+        # 128 values, a power of two, take them in (B,S,H,D) too), the collect-and-sort path past
+        # them (0.99, 0.9)
         x32 = synth.activations(CAL_SHAPE, synth.head_sigmas(H, seed=2024), law="t3", dtype=torch.float32, seed=100,
                                 device=dev)
         w32_min = torch.empty((1, H), dtype=torch.float32, device=dev)
@@ -554,7 +555,7 @@ def run(args, only, pool, workers) -> int:
                 c_ms = timed(lambda: fa.fa3q_calibrate_ex([xl], r, layout=layout, win_min=w32_min, win_max=w32_max,
                                                           workspace=ws, stream=stream))
                 k_win = n32 - int(r * n32) + 1
-                sort = layout == "BSHD" or k_win > fa.fa3q_calibrate_max_windows(torch.float32)
+                sort = k_win > fa.fa3q_calibrate_max_windows(torch.float32)  # D = 128: rows take the tail lists
                 tag = "" if layout == "BHSD" else "_bshd"
                 breakdown[f"calibrate_f32{tag}_{r}"] = hbm_row(
                     c_ms, 4 * x32.numel(), f"one (8,128,2048,128) float32 batch, {layout}, at ratio {r} "

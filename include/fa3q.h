@@ -119,8 +119,9 @@ int fa3q_version(void);
  * Largest number of windows K = N - int(ratio*N) + 1 that the streaming tail selection
  * (on-chip lists of the K smallest and K largest values) takes for `dtype`.  16-bit input
  * (bf16, float16) with a larger K, with heads of at least 2^20 values or in the FA3Q_BSHD
- * layout takes the histogram path; float32 input with a larger K or in the FA3Q_BSHD layout
- * takes the collect-and-sort path.  Both handle every K.  0 for an unknown dtype.
+ * layout takes the histogram path; float32 input with a larger K, or in the FA3Q_BSHD layout
+ * with rows of D values that are not a power of two, takes the collect-and-sort path.  Both
+ * handle every K.  0 for an unknown dtype.
  */
 int64_t fa3q_calibrate_max_windows(int dtype);
 
@@ -572,9 +573,10 @@ size_t fa3q_calibrate_ex_workspace_bytes(int dtype, int layout, int64_t nb, int6
  * follow.  run_min and run_max may both be NULL when win_min and win_max are given: the
  * windows are then written and no running statistics kept (fa3q_calibrate_perhead for
  * nb = 1).  BSHD rows of D values must be a multiple of 8 (16-bit) or 4 (float32) values;
- * (B,S,H,D) 16-bit input always takes the histogram path and float32 input the
- * collect-and-sort path (any K; see fa3q_calibrate_perhead).  Other arguments, alignment and
- * errors as fa3q_calibrate_batches.
+ * (B,S,H,D) 16-bit input always takes the histogram path; float32 input takes the tail lists
+ * when D is a power of two and K is within fa3q_calibrate_max_windows(FA3Q_F32), the
+ * collect-and-sort path otherwise (any K; see fa3q_calibrate_perhead).  Other arguments,
+ * alignment and errors as fa3q_calibrate_batches.
  */
 int fa3q_calibrate_ex(const void* const* xs, int64_t nb, int dtype, int layout, int64_t B, int64_t H,
                       int64_t S, int64_t D, double ratio, float* run_min, float* run_max, int init,

@@ -449,6 +449,10 @@ struct ChunkArgs {
   uint32_t K;
   uint32_t cap;
   int32_t pad;             // fill the unused list slots (the merges that read every slot need it)
+  // (B,S,H,D) input (kRows kernels): element e of slab (b, h) is at b*H*L + h*D + (e >> log2D) *
+  // row_stride + (e & (D - 1)), with D a power of two and row_stride = H*D
+  int32_t log2D;
+  int64_t row_stride;
 };
 
 template <typename InT>
@@ -503,6 +507,11 @@ struct SampleArgs {
   int32_t H;
   uint32_t M;        // sampled groups per head
   uint32_t K;
+  // (B,S,H,D) input (kRows kernels): run j starts at head row run_row[j] (rows of D values, row R
+  // of head h at (R*H + h)*D); thread t takes vector t & (Dv - 1) of row run_row[j] + (t >> log2Dv)
+  int64_t run_row[kSampleRuns];
+  int32_t log2Dv;
+  int32_t D;
 };
 
 // Head bounds from a sample: kSampleRuns spread-out runs of kSampleThreads consecutive
@@ -515,7 +524,7 @@ struct SampleArgs {
 // barrier per bit.  M < K gives no bound (every key passes the chunk filter until the
 // chunk itself holds K).
 // kSmallSlab: slabs shorter than a run, so a run may cross several slab boundaries.
-template <typename InT, bool kSmallSlab>
+template <typename InT, bool kSmallSlab, bool kRows>
 __global__ __launch_bounds__(kSampleThreads) void calib_sample_kernel(SampleArgs a, Batches bt) {
   using T = In<InT>;
   using KeyT = typename T::KeyT;
@@ -537,12 +546,18 @@ __global__ __launch_bounds__(kSampleThreads) void calib_sample_kernel(SampleArgs
   const int64_t jump = static_cast<int64_t>(a.H - 1) * a.Lv * kPerVec;  // slab end -> next slab of the head
 #pragma unroll
   for (int j = 0; j < kSampleRuns; ++j) {
-    const uint32_t w = a.run_w[j] + static_cast<uint32_t>(tid);
-    // slab boundaries crossed inside the run: at most one unless slabs are short
-    const uint32_t d = kSmallSlab ? w / static_cast<uint32_t>(a.Lv) : static_cast<uint32_t>(w >= a.Lv);
     const bool ok = static_cast<uint32_t>(tid) < a.run_n[j];
     valid |= static_cast<uint32_t>(ok) << j;
-    const int64_t e = a.run_off[j] + head_off + static_cast<int64_t>(tid) * kPerVec + d * jump;
+    int64_t e;
+    if constexpr (kRows) {
+      const int64_t row = a.run_row[j] + (tid >> a.log2Dv);
+      e = (row * a.H + h) * a.D + static_cast<int64_t>(tid & ((1 << a.log2Dv) - 1)) * kPerVec;
+    } else {
+      const uint32_t w = a.run_w[j] + static_cast<uint32_t>(tid);
+      // slab boundaries crossed inside the run: at most one unless slabs are short
+      const uint32_t d = kSmallSlab ? w / static_cast<uint32_t>(a.Lv) : static_cast<uint32_t>(w >= a.Lv);
+      e = a.run_off[j] + head_off + static_cast<int64_t>(tid) * kPerVec + d * jump;
+    }
     xs[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + (ok ? e : 0)));
   }
   // A group is a thread's vectors of kSampleGroupRuns runs (any distinct keys make a
@@ -604,7 +619,7 @@ __global__ __launch_bounds__(kSampleThreads) void calib_sample_kernel(SampleArgs
   }
 }
 
-template <typename InT>
+template <typename InT, bool kRows>
 __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void calib_chunk_kernel(ChunkArgs a, Batches bt) {
   using T = In<InT>;
   using KeyT = typename T::KeyT;
@@ -648,7 +663,10 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
   const int b = slab_i / a.H;
   const int h = slab_i - b * a.H;
   const int c = b * a.cps + part;
-  const InT* slab = static_cast<const InT*>(a.x) + (static_cast<int64_t>(b) * a.H + h) * a.L;
+  // (b, h) slab: contiguous, or (kRows) S rows of D values a row_stride apart
+  const InT* slab = static_cast<const InT*>(a.x) +
+                    (kRows ? static_cast<int64_t>(b) * a.H * a.L + (static_cast<int64_t>(h) << a.log2D)
+                           : (static_cast<int64_t>(b) * a.H + h) * a.L);
   const int64_t begin = static_cast<int64_t>(part) * a.CL;
   const int64_t end = min(a.L, begin + a.CL);
 
@@ -660,7 +678,8 @@ __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(4
 #pragma unroll
     for (int v = 0; v < kVec; ++v) {
       const int64_t e = min(t0 + static_cast<int64_t>(v * NT + tid) * kPerVec, last);
-      x[v] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(slab + e));
+      const int64_t off = kRows ? (e >> a.log2D) * a.row_stride + (e & ((int64_t{1} << a.log2D) - 1)) : e;
+      x[v] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(slab + off));
     }
   };
 
@@ -1366,7 +1385,19 @@ struct CalibPlan {
   HistPlan hp;
   bool sort = false;     // the collect-and-sort path (float32 keys); its workspace serves every batch in turn
   SortPlan sp;
+  // tail lists over (B,S,H,D) rows (float32, D a power of two): the sample runs start at head
+  // rows sample_row[], and the chunk kernel addresses slab element e through its row
+  bool rows = false;
+  int64_t D = 0;
+  int32_t log2D = 0, log2Dv = 0;
+  int64_t sample_row[kSampleRuns] = {};
 };
+
+int32_t log2_exact(int64_t v) {  // v a power of two
+  int32_t l = 0;
+  while ((int64_t{1} << l) < v) ++l;
+  return l;
+}
 
 int64_t next_pow2(int64_t v) {
   int64_t p = 1;
@@ -1396,7 +1427,9 @@ int make_plan(int dtype, int layout, int64_t nb, int64_t B, int64_t H, int64_t S
   if (p.t < 1) return FA3Q_ERR_RATIO;
   p.K = p.N - p.t + 1;
   p.f16 = dtype == FA3Q_F16;
-  if (p.K > fa3q_calibrate_max_windows(dtype) || layout == FA3Q_BSHD || (k16 && p.N >= kHistMinValues)) {
+  // float32 (B,S,H,D) rows with D a power of two take the tail lists like (B,H,S,D) slabs
+  const bool rows_ok = layout == FA3Q_BSHD && !k16 && (D & (D - 1)) == 0 && D >= vec;
+  if (p.K > fa3q_calibrate_max_windows(dtype) || (layout == FA3Q_BSHD && !rows_ok) || (k16 && p.N >= kHistMinValues)) {
     if (!k16) {
       // float32: both tails collected through a histogram of their leading 16 bits and sorted
       p.sort = true;
@@ -1422,15 +1455,28 @@ int make_plan(int dtype, int layout, int64_t nb, int64_t B, int64_t H, int64_t S
   // 16-bit golden-ratio step, as a fraction of the free range), so that runs do not line up
   // with slab starts or any other period of the data: an over-sampled structure (large
   // first tokens of every sequence, say) would make an estimated bound fail for every head.
-  const int64_t stride = std::max<int64_t>(kSampleThreads, Q / kSampleRuns);
+  // (B,S,H,D) rows: strides and phases are whole rows of Dv vectors, so every run starts at a
+  // row and the runs stay disjoint (the group-minimum bound needs distinct values).
+  p.rows = layout == FA3Q_BSHD;
+  const int64_t Dv = p.rows ? D / vec : 1;
+  p.D = D;
+  if (p.rows) {
+    p.log2D = log2_exact(D);
+    p.log2Dv = log2_exact(Dv);
+  }
+  int64_t stride = std::max<int64_t>(kSampleThreads, Q / kSampleRuns);
+  stride = (stride + Dv - 1) / Dv * Dv;
   int64_t m = 0;
   for (int j = 0; j < kSampleRuns; ++j) {
-    const int64_t phase = ((((2 * j + 1) * 40503) & 0xffff) * (stride - kSampleThreads) >> 16) & ~int64_t{7};  // whole lines
+    int64_t phase = ((((2 * j + 1) * 40503) & 0xffff) * std::max<int64_t>(0, stride - kSampleThreads) >> 16) &
+                    ~int64_t{7};  // whole lines
+    phase = phase / Dv * Dv;
     const int64_t q0 = j * stride + phase;
     p.sample_n[j] = static_cast<uint32_t>(std::min<int64_t>(kSampleThreads, std::max<int64_t>(0, Q - q0)));
     const int64_t b = p.sample_n[j] ? q0 / Lv : 0, w = p.sample_n[j] ? q0 - b * Lv : 0;
     p.sample_off[j] = (b * H * Lv + w) * vec;
     p.sample_w[j] = static_cast<uint32_t>(w);
+    p.sample_row[j] = p.sample_n[j] ? q0 / Dv : 0;
   }
   // a thread's group holds a vector inside the head when its lane is below the largest
   // run length among the group's runs
@@ -1537,7 +1583,8 @@ template <typename InT>
 int launch(const void* const* x, int64_t nb, int64_t H, const CalibPlan& p, float* win_min, float* win_max,
            void* workspace, hipStream_t stream) {
   using KeyT = InT;
-  int st = allow_dynamic_lds(reinterpret_cast<const void*>(calib_chunk_kernel<InT>), p.lds_chunk);
+  const auto chunk_kernel = p.rows ? calib_chunk_kernel<InT, true> : calib_chunk_kernel<InT, false>;
+  int st = allow_dynamic_lds(reinterpret_cast<const void*>(chunk_kernel), p.lds_chunk);
   if (st != FA3Q_OK) return st;
   if (p.wave_merge_e == 0) {
     st = allow_dynamic_lds(reinterpret_cast<const void*>(calib_merge_side_kernel<KeyT>), p.lds_merge);
@@ -1564,12 +1611,17 @@ int launch(const void* const* x, int64_t nb, int64_t H, const CalibPlan& p, floa
   sa.H = static_cast<int32_t>(H);
   sa.M = p.sample_m;
   sa.K = p.rank;
+  for (int j = 0; j < kSampleRuns; ++j) sa.run_row[j] = p.sample_row[j];
+  sa.log2Dv = p.log2Dv;
+  sa.D = static_cast<int32_t>(p.D);
   bt.per = static_cast<int32_t>(H);
   const dim3 g_heads(static_cast<unsigned>(nb * H));
-  if (sa.Lv >= kSampleThreads)
-    hipLaunchKernelGGL((calib_sample_kernel<InT, false>), g_heads, dim3(kSampleThreads), 0, stream, sa, bt);
+  if (p.rows)
+    hipLaunchKernelGGL((calib_sample_kernel<InT, false, true>), g_heads, dim3(kSampleThreads), 0, stream, sa, bt);
+  else if (sa.Lv >= kSampleThreads)
+    hipLaunchKernelGGL((calib_sample_kernel<InT, false, false>), g_heads, dim3(kSampleThreads), 0, stream, sa, bt);
   else
-    hipLaunchKernelGGL((calib_sample_kernel<InT, true>), g_heads, dim3(kSampleThreads), 0, stream, sa, bt);
+    hipLaunchKernelGGL((calib_sample_kernel<InT, true, false>), g_heads, dim3(kSampleThreads), 0, stream, sa, bt);
 
   ChunkArgs ca;
   ca.x = nullptr;
@@ -1585,10 +1637,12 @@ int launch(const void* const* x, int64_t nb, int64_t H, const CalibPlan& p, floa
   ca.K = static_cast<uint32_t>(p.K);
   ca.cap = p.cap_chunk;
   ca.pad = (p.wave_merge_e > 0 || p.nch > kMaxPrefixLists) ? 1 : 0;
+  ca.log2D = p.log2D;
+  ca.row_stride = H * p.D;
   Batches bc = bt;
   bc.per = static_cast<int32_t>(H * p.nch);
   const dim3 g_chunks(static_cast<unsigned>(nb * H * p.nch));
-  hipLaunchKernelGGL(calib_chunk_kernel<InT>, g_chunks, dim3(kChunkThreads), p.lds_chunk, stream, ca, bc);
+  hipLaunchKernelGGL(chunk_kernel, g_chunks, dim3(kChunkThreads), p.lds_chunk, stream, ca, bc);
   MergeArgs ma;
   ma.lists = workspace;
   ma.counts = counts;
@@ -1618,7 +1672,7 @@ int launch(const void* const* x, int64_t nb, int64_t H, const CalibPlan& p, floa
     // heads whose estimated bound held fewer than K values: again with no bound
     ChunkArgs cf = ca;
     cf.fail = fail;
-    hipLaunchKernelGGL(calib_chunk_kernel<InT>, g_chunks, dim3(kChunkThreads), p.lds_chunk, stream, cf, bc);
+    hipLaunchKernelGGL(chunk_kernel, g_chunks, dim3(kChunkThreads), p.lds_chunk, stream, cf, bc);
     MergeArgs mf = ma;
     mf.fixup = 1;
     merge(mf);

@@ -553,11 +553,15 @@ def test_ex_workspace_queries():
         assert q(dt, L.FA3Q_BSHD, 2, 1, 8, 256, 64, r) >= 2 * 8 * 65536 * 4
         assert q(dt, L.FA3Q_BSHD, 1, 2, 4, 16, 12, r) == 0  # rows of 12 values: not whole vectors
     assert q(L.FA3Q_F32, L.FA3Q_BHSD, 1, 1, 8, 256, 64, r) > 0
-    # float32 (B,S,H,D): the collect-and-sort path, one region of two N-key lists per head for
-    # any number of batches (they take it in turn), plus the windows of every batch
-    one = q(L.FA3Q_F32, L.FA3Q_BSHD, 1, 1, 8, 256, 64, r)
-    assert one >= 2 * 8 * (256 * 64) * 4
-    assert 0 <= q(L.FA3Q_F32, L.FA3Q_BSHD, 4, 1, 8, 256, 64, r) - one < 4096
+    # float32 (B,S,H,D) with rows of a power-of-two width and K within the tail lists' cap: the
+    # tail lists, the same workspace as (B,H,S,D) slabs
+    assert q(L.FA3Q_F32, L.FA3Q_BSHD, 2, 1, 8, 256, 64, r) == q(L.FA3Q_F32, L.FA3Q_BHSD, 2, 1, 8, 256, 64, r) > 0
+    # other widths (96) and larger K: the collect-and-sort path, one region of two N-key lists per
+    # head for any number of batches (they take it in turn), plus the windows of every batch
+    one = q(L.FA3Q_F32, L.FA3Q_BSHD, 1, 1, 8, 256, 96, r)
+    assert one >= 2 * 8 * (256 * 96) * 4
+    assert 0 <= q(L.FA3Q_F32, L.FA3Q_BSHD, 4, 1, 8, 256, 96, r) - one < 4096
+    assert q(L.FA3Q_F32, L.FA3Q_BSHD, 1, 4, 8, 4096, 64, 0.9) >= 2 * 8 * (4 * 4096 * 64) * 4
     assert q(L.FA3Q_F32, L.FA3Q_BSHD, 1, 2, 4, 16, 6, r) == 0  # rows of 6 float32 values: not whole vectors
     assert q(L.FA3Q_BF16, 2, 1, 1, 8, 256, 64, r) == 0
     assert q(7, L.FA3Q_BHSD, 1, 1, 8, 256, 64, r) == 0

@@ -1,5 +1,9 @@
 """Recall Window of float32 heads past the on-chip tail lists, and of float32 (B,S,H,D) input.
 
+(B,S,H,D) rows whose D is a power of two take the tail lists while K is within their cap
+(the same sampled bounds and chunk lists as (B,H,S,D) slabs, the rows addressed one by one);
+other (B,S,H,D) input and larger K take the collect-and-sort path.  The cases below cover both.
+
 msModelSlim page "FA3量化：Flash Attention 3激活量化算法说明", section 原理 -> 算法流程: the
 window is defined for every ratio in (0, 1] through target_num = int(ratio*N), K = N -
 target_num + 1 windows per head.  For float32 heads with K above
@@ -46,12 +50,20 @@ def _sort_path(fa, shape_bhsd, ratio, layout="BHSD"):
     return ws1 >= 2 * H * N * 4 and ws3 - ws1 < 4096  # only the extra windows grow with nb
 
 
+def _takes_tail_lists(fa, shape_bhsd, ratio, layout):
+    """(B,S,H,D) float32 rows with D a power of two and K within the tail lists' cap take the
+    tail lists (one pass, sampled bounds) instead of the collect-and-sort path."""
+    B, H, S, D = shape_bhsd
+    K = _k_of(ratio, B * S * D)
+    return layout == "BSHD" and D & (D - 1) == 0 and K <= fa.fa3q_calibrate_max_windows(torch.float32)
+
+
 def _check(fa, x, ratio, what, layout="BHSD"):
     shape = tuple(x.shape) if layout == "BHSD" else (x.shape[0], x.shape[2], x.shape[1], x.shape[3])
     B, H, S, D = shape
     N = B * S * D
     K = _k_of(ratio, N)
-    assert _sort_path(fa, shape, ratio, layout), (what, K)
+    assert _sort_path(fa, shape, ratio, layout) != _takes_tail_lists(fa, shape, ratio, layout), (what, K)
     log(f"f32 {what}: {layout} {tuple(x.shape)} ratio={ratio!r} K={K}")
     wmin, wmax = fa.fa3q_calibrate_ex([x], ratio, layout=layout)
     torch.cuda.synchronize()
@@ -130,7 +142,8 @@ def test_degenerate_heads(fa):
 
 
 BSHD_CASES = [
-    # (what, (B,H,S,D) head-major, ratios): (B,S,H,D) float32 takes the sort path at every K
+    # (what, (B,H,S,D) head-major, ratios): the tail lists over rows (D a power of two, K within
+    # the cap), else collect and sort
     ("rows of 32 vectors", (2, 8, 2048, 128), (0.9999, 0.99)),
     ("rows of 1 vector", (3, 5, 777, 4), (0.5, 0.999)),
     ("rows of 48 vectors", (1, 4, 1000, 192), (0.9,)),
@@ -208,3 +221,58 @@ def test_tiny_heads_every_ratio(fa, dtype):
             lo, hi = _oracle(x.float() if dtype != torch.float32 else x, ratio, "BSHD")
             assert_bits_equal(wmin[0].cpu().numpy(), lo, f"{dtype} {(B, S, H, D)} t={t} win_min")
             assert_bits_equal(wmax[0].cpu().numpy(), hi, f"{dtype} {(B, S, H, D)} t={t} win_max")
+
+
+def _row_run_starts(q_vecs: int, dv: int) -> list:
+    """First vector of each of the 32 sample runs over (B,S,H,D) rows of dv vectors: runs of 256
+    vectors, run j inside [j * stride, (j + 1) * stride) at a fixed phase, strides and phases
+    whole rows."""
+    stride = max(256, q_vecs // 32)
+    stride = (stride + dv - 1) // dv * dv
+    out = []
+    for j in range(32):
+        phase = ((((2 * j + 1) * 40503) & 0xFFFF) * max(0, stride - 256)) >> 16 & ~7
+        out.append(j * stride + phase // dv * dv)
+    return out
+
+
+def test_bshd_rows_estimated_bound_that_fails_is_redone_exactly(fa):
+    # (B,S,H,D) float32 rows of 128 values on the tail lists: K = 5244 against 2048 sampled
+    # groups, so the head bound is an estimate checked by the merge.  Values planted where the
+    # row-aligned sample reads (a group is a thread's vectors of four consecutive runs) give
+    # every group an extreme: the sample bounds tightly while the head holds only 2048 values
+    # beyond the bound, the check fails and the head is redone without a bound, rows addressed
+    # one by one in both passes.
+    dev = torch.device("cuda:0")
+    B, S, H, D = 1, 8192, 2, 128
+    vec, dv = 4, 128 // 4
+    N = B * S * D
+    ratio = 0.995
+    assert _k_of(ratio, N) == 5244 <= fa.fa3q_calibrate_max_windows(torch.float32)
+    rng = np.random.default_rng(29)
+    x = np.ones((B, S, H, D), np.float32)
+    x[:, :, 1, :] = rng.standard_normal((B, S, D)).astype(np.float32)
+    starts = _row_run_starts(B * S * dv, dv)
+    for g in range(8):
+        lo_run, hi_run = starts[4 * g], starts[4 * g + 1]
+        for t in range(256):
+            for run, head, off, val in ((lo_run, 0, 0, -7.0), (hi_run, 0, 0, 9.0), (lo_run, 1, 3, -50.0)):
+                row, cv = divmod(run + t, dv)
+                b, s = divmod(row, S)
+                x[b, s, head, cv * vec + off] = val   # head 0: both sides fail; head 1: the low side
+    xt = torch.from_numpy(x).to(dev)
+    assert not _sort_path(fa, (B, H, S, D), ratio, "BSHD")
+    nbytes = fa.fa3q_calibrate_ex_workspace_bytes(torch.float32, "BSHD", 1, B, H, S, D, ratio)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+    log(f"f32 BSHD rows, failing estimate: {tuple(xt.shape)} ratio={ratio}")
+    wmin, wmax = fa.fa3q_calibrate_ex([xt], ratio, layout="BSHD", workspace=ws)
+    torch.cuda.synchronize()
+    lo, hi = _oracle(xt, ratio, "BSHD")
+    assert_bits_equal(wmin[0].cpu().numpy(), lo, "failing estimate win_min")
+    assert_bits_equal(wmax[0].cpu().numpy(), hi, "failing estimate win_max")
+    # the check flags (the 256-byte block before the windows' block: low side of each head,
+    # then high side): both sides of head 0, the low side of head 1
+    flags = ws[nbytes - 512:nbytes - 512 + 4 * 2 * H].cpu().view(torch.int32).numpy().tolist()
+    assert flags == [1, 1, 1, 0], flags
+    for r in (0.999, 0.9999):
+        _check(fa, xt, r, f"planted rows ratio {r}", layout="BSHD")

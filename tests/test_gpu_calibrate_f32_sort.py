@@ -276,3 +276,34 @@ def test_bshd_rows_estimated_bound_that_fails_is_redone_exactly(fa):
     assert flags == [1, 1, 1, 0], flags
     for r in (0.999, 0.9999):
         _check(fa, xt, r, f"planted rows ratio {r}", layout="BSHD")
+
+
+def _random_bshd_cases(n: int, seed: int):
+    """Seeded float32 (B,S,H,D) shapes: row widths from one vector to 512 values (powers of
+    two on the tail lists, 12 and 96 on collect and sort), ratios on both sides of the tail
+    lists' cap."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        D = int(rng.choice([4, 8, 12, 16, 32, 64, 96, 128, 256, 512]))
+        H = int(rng.integers(1, 7))
+        B = int(rng.integers(1, 4))
+        S = int(rng.integers(1, 1 + 200000 // (B * D)))
+        r = float(rng.choice([0.5, 0.9, 0.99, 0.999, 0.9999, 1.0]))
+        cases.append((B, H, S, D, r, 500 + i))
+    return cases
+
+
+@pytest.mark.parametrize("B,H,S,D,ratio,seed", _random_bshd_cases(16, 777))
+def test_bshd_random_shapes(fa, B, H, S, D, ratio, seed):
+    N = B * S * D
+    if int(ratio * N) < 1:
+        pytest.skip("t = int(ratio * N) < 1")
+    x = _acts((B, H, S, D), seed).transpose(1, 2).contiguous().to(DEV)
+    tail = _takes_tail_lists(fa, (B, H, S, D), ratio, "BSHD")
+    log(f"f32 BSHD random: {(B, S, H, D)} ratio={ratio} K={_k_of(ratio, N)} {'tail lists' if tail else 'collect and sort'}")
+    wmin, wmax = fa.fa3q_calibrate_ex([x], ratio, layout="BSHD")
+    torch.cuda.synchronize()
+    lo, hi = _oracle(x, ratio, "BSHD")
+    assert_bits_equal(wmin[0].cpu().numpy(), lo, f"random BSHD {(B, S, H, D)} win_min")
+    assert_bits_equal(wmax[0].cpu().numpy(), hi, f"random BSHD {(B, S, H, D)} win_max")

@@ -162,3 +162,38 @@ def test_latent_decode_with_scores_that_keep_growing(fa, name, B, H, T, slope, p
     log(f"  row-normalised error {err:.3e}")
     assert err <= DECODE_TOL, err
     assert err <= DECODE_DESIGN_TOL, err
+
+
+def _random_latent_cases(n: int, seed: int):
+    """Seeded shapes for the shared-latent decode: head counts on both kernels (below 128,
+    exactly 128, a partial 128-head group, two groups), token counts from 1 to a few
+    thousand (partial tiles, one or many splits), every (Dl, Dr)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        H = int(rng.choice([16, 64, 96, 128, 130, 160, 256]))
+        B = int(rng.integers(1, 5))
+        T = int(rng.choice([1, 31, 32, 33, 95, 511, 1000, 2049, 3001]))
+        Dl = int(rng.choice([128, 256, 512]))
+        Dr = int(rng.choice([0, 32, 64]))
+        cases.append((B, H, T, Dl, Dr, 1000 + i))
+    return cases
+
+
+@pytest.mark.parametrize("B,H,T,Dl,Dr,seed", _random_latent_cases(14, 4242))
+def test_latent_decode_random_shapes(fa, B, H, T, Dl, Dr, seed):
+    dev = torch.device("cuda:0")
+    log(f"latent random: B={B} H={H} T={T} Dl={Dl} Dr={Dr} seed={seed}")
+    cq, kr, scale = _latent_cache(fa, B, T, Dl, Dr, seed)
+    q = synth.normal_tensor((B, H, Dl + Dr), dtype=torch.bfloat16, seed=seed + 7, device=dev)
+    sm = 1.0 / math.sqrt(Dl + Dr)
+    out = fa.fa3q_decode_latent(q, cq, scale, kr if Dr else None, sm)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.all(np.isfinite(got))
+    ref = oracle.decode_attn_latent(bits16(q.cpu()), cq.cpu().numpy(), scale.cpu().numpy()[0],
+                                    bits16(kr.cpu()) if Dr else np.zeros((B, T, 0), np.uint16), sm, Dl)
+    err = row_rel_err(got, ref)
+    log(f"  row-normalised error {err:.3e}")
+    assert err <= DECODE_TOL, err
+    assert err <= DECODE_DESIGN_TOL, err

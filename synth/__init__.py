@@ -16,8 +16,9 @@ RoPE part):
 * ``t3``: ``x = sigma_h * z0 / sqrt((z1^2 + z2^2 + z3^2) / 3)``, a Student-t
   with 3 degrees of freedom (heavy tails).
 * outliers: per head, ``max(1, round(frac * N_h))`` positions drawn uniformly
-  with replacement over the head's ``N_h = B*S*D`` values (a repeated position
-  is written once), each set to ``+-mult * sigma_h`` with a fair-coin sign.
+  with replacement over the head's ``N_h = B*S*D`` values, each set to
+  ``+-mult * sigma_h`` with a fair-coin sign (a position drawn more than once
+  keeps its last draw, so the bytes do not depend on the device's store order).
 * the result is rounded once to the storage dtype (bf16 round-to-nearest-even
   via torch's cast, or kept in fp32).
 
@@ -107,7 +108,14 @@ def activations(
         rem = pos % (S * D)
         h_idx = torch.arange(H, device=dev, dtype=torch.int64).view(H, 1).expand(H, count)
         flat = (b_idx * H + h_idx) * (S * D) + rem
-        out.view(-1)[flat.reshape(-1)] = val.reshape(-1).to(dtype)
+        # a position drawn more than once takes its last draw's value: an indexed store with
+        # repeated indices leaves the winner unspecified on the GPU
+        flat = flat.reshape(-1)
+        uniq, inv = torch.unique(flat, return_inverse=True)
+        draw = torch.arange(flat.numel(), device=dev, dtype=torch.int64)
+        last = torch.full((uniq.numel(),), -1, device=dev, dtype=torch.int64)
+        last.scatter_reduce_(0, inv, draw, reduce="amax")
+        out.view(-1)[uniq] = val.reshape(-1)[last].to(dtype)
     return out
 
 

@@ -417,11 +417,23 @@ __global__ __launch_bounds__(kLatThreads) void latent_split_kernel(LatentArgs a)
 //   O^T (32 dims x 32 heads)  += V^T (dims x 16 tokens) . P^T (16 tokens x heads)
 // A lane holds head lane % 32; its half hh = lane / 32 holds the scores of tokens
 // 8i + 4hh + j (i, j < 4) of a tile, which are k-slots 8hh .. 8hh+7 of the two PV k-steps
-// (i < 2, then i >= 2): in the transposed LDS rows token t of a tile sits at slot
-// 16(t/16) + 8((t/4)%2) + 4((t/8)%2) + t%4.  Each staged operand read (1 KB per wave) feeds a
-// 32-head MFMA, so a tile is read from LDS once per 32 heads, and no scores are exchanged
-// between waves.  The RoPE part of the query sits in LDS (the latent part and the 512 output
-// dims fill the registers).
+// (i < 2, then i >= 2).  Each staged operand read feeds a 32-head MFMA, so a tile is read from
+// LDS once per 32 heads, and no scores are exchanged between waves.  The RoPE part of the
+// query sits in LDS (the latent part and the 512 output dims fill the registers).
+//
+// One staged copy: the codes are widened to bf16 once, into token rows.  The score product
+// reads them as they are; the PV product reads V^T from the same rows with the LDS transpose
+// read (ds_read_b64_tr_b16): within each group of 16 lanes, lane i receives, as its v-th
+// value, element i % 4 of the 8 bytes addressed by lane 4v + i / 4.  So lanes 4v .. 4v+3
+// address 16 consecutive dims of token row v, and lane i comes back with dim i of the four
+// tokens: two such reads give a lane its 8 k-values.  The 16-byte chunks of a row are XORed
+// with ((t & 3) << 2) | ((t >> 2) & 3) of its token t, which keeps both kinds of read free of
+// bank conflicts (16 consecutive rows at one chunk; 4 consecutive rows of 64 bytes each).
+//
+// Three buffers: while tile j's scores are computed from one, tile j+1 is staged into the
+// next, and the PV product of tile j-1 -- whose weights the previous pass left in registers --
+// reads the third, alongside tile j's softmax.  So the widening overlaps the score MFMAs and
+// the softmax overlaps the PV MFMAs.  One barrier per tile.
 //
 // No rescale in the tile loop: a head's reference mu is the max of its split's first tile,
 // and weights 2^(score - mu) stay within float32 and bf16 range while no later score exceeds
@@ -432,26 +444,41 @@ __global__ __launch_bounds__(kLatThreads) void latent_split_kernel(LatentArgs a)
 constexpr int kWideThreads = 256;  // four waves, one per SIMD
 constexpr int kWideHeads = 128;    // 32 heads per wave
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// 8 bytes at LDS byte address `p`, transposed across each group of 16 lanes (see above)
+__device__ __forceinline__ uint2 lds_read_tr16(const void* p) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(const_cast<void*>(p)));
+  return __builtin_bit_cast(uint2, v);
+}
+
+// chunk swizzle of staged token row t
+__device__ __forceinline__ int wide_swz(int t) { return ((t & 3) << 2) | ((t >> 2) & 3); }
+
 template <int DL, int DR>
 __global__ __launch_bounds__(kWideThreads) void latent_wide_kernel(LatentArgs a) {
   constexpr int KS = DL / 16;          // latent k-steps of the score product
   constexpr int RS = DR / 16;          // RoPE k-steps
   constexpr int OT = DL / 32;          // 32-dim output tiles
-  constexpr int KROW = DL + 8;         // bf16 per row-major latent row in LDS
+  constexpr int ROWB = 2 * DL;         // bytes per staged latent row (chunks swizzled, no padding)
   constexpr int RROW = DR + 8;         // bf16 per RoPE row in LDS
-  constexpr int VROW = kTT;            // bf16 per transposed latent row (one per dim)
   constexpr int DC = DL / 16;          // 16-code chunks per latent row
   constexpr int UNITS = (kTT / 4) * DC;  // staging units of 4 tokens x 16 dims
   static_assert(UNITS <= kWideThreads, "at most one staging unit per thread");
+  static_assert(DL >= 128, "the chunk swizzle spans 16 chunks");
   constexpr int RPR = DR > 0 ? DR / 8 : 1;  // 16-byte RoPE chunks per row
   constexpr int RCH = kTT * DR / 8;
   static_assert(RCH <= kWideThreads, "at most one RoPE chunk per thread");
   constexpr float kLazy = 64.0f;       // log2 headroom of the weights over the reference
-  __shared__ __align__(16) uint16_t klat_buf[2][kTT * KROW];
-  __shared__ __align__(16) uint16_t vt_buf[2][DL * VROW];
-  __shared__ __align__(16) uint16_t krope_buf[2][DR > 0 ? kTT * RROW : 8];
   constexpr int QROW = DR + 8;         // bf16 per RoPE query row in LDS (padded: 128-byte rows conflict)
+  // three buffers of each staged operand, as distinct arrays (accesses to different buffers
+  // are then known to be disjoint)
+  __shared__ __align__(16) uint16_t klb[3][kTT * DL];
+  __shared__ __align__(16) uint16_t krb[3][DR > 0 ? kTT * RROW : 8];
   __shared__ __align__(16) uint16_t qrope[DR > 0 ? kWideHeads * QROW : 8];  // [head][QROW]
+  auto klat = [&](int bc) __attribute__((always_inline)) -> uint16_t* { return klb[bc]; };
+  auto krope = [&](int bc) __attribute__((always_inline)) -> uint16_t* { return krb[bc]; };
 
   const int tid = static_cast<int>(threadIdx.x);
   const int wave = tid / kWave;
@@ -479,7 +506,7 @@ __global__ __launch_bounds__(kWideThreads) void latent_wide_kernel(LatentArgs a)
   u32x4v xs[4];
   u32x4v xr;
   // global -> registers for tile t0 (rows past the end re-read the last row; masked later)
-  auto fetch = [&](int64_t t0) {
+  auto fetch = [&](int64_t t0) __attribute__((always_inline)) {
     if (has_unit) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -492,14 +519,10 @@ __global__ __launch_bounds__(kWideThreads) void latent_wide_kernel(LatentArgs a)
       xr = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(rbase + tok * DR + 8 * rk));
     }
   };
-  // registers -> LDS buffer `buf`: the codes widened to bf16 (exact) once, written row-major
-  // and transposed.  Transposed row R (dim) lives at row R ^ ((R >> 4) & 3) with its 16-byte
-  // chunks XORed by 2 ((R >> 2) & 1), so the staging writes and the PV operand reads both
-  // spread over the banks.
-  auto stage = [&](int buf) {
+  // registers -> buffer B: the codes widened to bf16 (exact) in token rows, chunk-swizzled
+  auto stage = [&](int bc) __attribute__((always_inline)) {
     if (has_unit) {
-      uint16_t* klat = klat_buf[buf];
-      uint16_t* vt = vt_buf[buf];
+      char* kb = reinterpret_cast<char*>(klat(bc));
       float f[4][16];
 #pragma unroll
       for (int r = 0; r < 4; ++r)
@@ -510,22 +533,15 @@ __global__ __launch_bounds__(kWideThreads) void latent_wide_kernel(LatentArgs a)
         uint32_t h[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) h[i] = pack_bf16(f[r][2 * i], f[r][2 * i + 1]);
-        uint16_t* row = klat + (4 * tg + r) * KROW + 16 * dc;
-        *reinterpret_cast<uint4*>(row) = make_uint4(h[0], h[1], h[2], h[3]);
-        *reinterpret_cast<uint4*>(row + 8) = make_uint4(h[4], h[5], h[6], h[7]);
-      }
-      const int chunk = 2 * (tg / 4) + (tg % 2);  // slots 4tg' .. of tokens 4tg .. 4tg+3
-      const int half8 = (tg / 2) % 2;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int prow = (16 * dc + j) ^ (dc & 3);
-        const int pch = chunk ^ (((j >> 2) & 1) << 1);
-        *reinterpret_cast<uint2*>(vt + prow * VROW + 8 * pch + 4 * half8) =
-            make_uint2(pack_bf16(f[0][j], f[1][j]), pack_bf16(f[2][j], f[3][j]));
+        const int t = 4 * tg + r;
+        const int sw = wide_swz(t);
+        char* row = kb + t * ROWB;
+        *reinterpret_cast<uint4*>(row + 16 * ((2 * dc) ^ sw)) = make_uint4(h[0], h[1], h[2], h[3]);
+        *reinterpret_cast<uint4*>(row + 16 * ((2 * dc + 1) ^ sw)) = make_uint4(h[4], h[5], h[6], h[7]);
       }
     }
     if constexpr (DR > 0) {
-      if (has_rope) *reinterpret_cast<u32x4v*>(krope_buf[buf] + rr * RROW + 8 * rk) = xr;
+      if (has_rope) *reinterpret_cast<u32x4v*>(krope(bc) + rr * RROW + 8 * rk) = xr;
     }
   };
 
@@ -552,6 +568,23 @@ __global__ __launch_bounds__(kWideThreads) void latent_wide_kernel(LatentArgs a)
   }
   const float s = a.scale[0];
 
+  // score operand: row hc, chunk (2kk + hh) ^ swz(hc) = 2kk ^ qx
+  const int qx = wide_swz(hc) ^ hh;
+  const int qrow_b = hc * ROWB;
+  // PV operand, as the supplier lane of the transpose read: group pg, token row pv of the
+  // group's four, 4-dim piece pq; read s (0, 1) covers tokens 16ks + 8s + 4(pg/2) + pv and the
+  // dims 32dt + 16(pg%2) + 4pq .. +3, whose chunk is 4dt + 2(pg%2) + pq/2 and whose swizzle is
+  // (pv << 2) | ((2s + pg/2) & 3).  Split into a lane part for each (s, dt % 4) and
+  // compile-time offsets.
+  const int pg = lane >> 4, pv = (lane >> 2) & 3, pq = lane & 3;
+  int pbase[2][4];
+#pragma unroll
+  for (int sr = 0; sr < 2; ++sr)
+#pragma unroll
+    for (int d3 = 0; d3 < 4; ++d3)
+      pbase[sr][d3] = (4 * (pg >> 1) + pv) * ROWB + 8 * (pq & 1) +
+                      16 * ((2 * (pg & 1) + (pq >> 1)) ^ ((2 * sr + (pg >> 1)) & 3)) + 64 * (d3 ^ pv);
+
   f32x16 o[OT];  // output dims 32dt + 8i + 4hh + j at o[dt][4i + j]
 #pragma unroll
   for (int dt = 0; dt < OT; ++dt)
@@ -560,56 +593,37 @@ __global__ __launch_bounds__(kWideThreads) void latent_wide_kernel(LatentArgs a)
   float mu = -INFINITY, l = 0.0f;
   bool gave_up = false;
 
-  fetch(t_begin);
-  stage(0);
-  if (t_begin + kTT < t_end) fetch(t_begin + kTT);
-  __syncthreads();
-  int buf = 0;
-  float p[16];
-  // Each pass computes tile t0 from buffer `buf` while tile t0 + 32 (in registers) is staged
-  // into the other buffer and tile t0 + 64 is fetched; one barrier per tile.
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += kTT, buf ^= 1) {
-    const uint16_t* klat = klat_buf[buf];
+  // s <q_abs, c> + <q_rope, r> of the lane's head over its 16 tokens, from buffer B
+  auto scores = [&](int bc) __attribute__((always_inline)) {
+    const char* kb = reinterpret_cast<const char*>(klat(bc)) + qrow_b;
     f32x16 sc;
 #pragma unroll
     for (int v = 0; v < 16; ++v) sc[v] = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      const uint4 w = *reinterpret_cast<const uint4*>(klat + hc * KROW + 16 * kk + 8 * hh);
+      const uint4 w = *reinterpret_cast<const uint4*>(kb + 256 * (kk >> 3) + 16 * ((2 * (kk & 7)) ^ qx));
       sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(w), ql[kk], sc, 0, 0, 0);
     }
-    {
-      // keep kSDepth operand reads in flight ahead of the score MFMAs
-      constexpr int kSDepth = KS < 6 ? KS : 6;
-      __builtin_amdgcn_sched_group_barrier(0x100, kSDepth, 0);  // DS reads
-#pragma unroll
-      for (int i = 0; i < KS - kSDepth; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, kSDepth, 0);
-    }
-    // the other buffer was last read before the previous barrier; staged and fetched
-    // unconditionally (past the end the fetch re-reads the last row and the buffer is never read)
-    stage(buf ^ 1);
-    fetch(t0 + 2 * kTT);
-    // s <q_abs, c> + <q_rope, r>: the latent part scaled, then the RoPE k-steps added on
 #pragma unroll
     for (int v = 0; v < 16; ++v) sc[v] *= s;
     if constexpr (DR > 0) {
-      const uint16_t* krope = krope_buf[buf];
+      const uint16_t* kr = krope(bc);
 #pragma unroll
       for (int kk = 0; kk < RS; ++kk) {
-        const uint4 w = *reinterpret_cast<const uint4*>(krope + hc * RROW + 16 * kk + 8 * hh);
+        const uint4 w = *reinterpret_cast<const uint4*>(kr + hc * RROW + 16 * kk + 8 * hh);
         const uint4 qv = *reinterpret_cast<const uint4*>(qrope + (wave * 32 + hc) * QROW + 16 * kk + 8 * hh);
         sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(w), as_bf16x8(qv), sc, 0, 0, 0);
       }
     }
-    // scores (log2 domain) of the lane's head over its 16 tokens; a split's last tile may
-    // be partial (uniform branch)
+    return sc;
+  };
+  // weights of tile t0 against mu as two bf16 terms (the first tile of a split sets mu; on a
+  // later tile a wave whose head outgrows mu by more than kLazy gives its split up)
+  auto weights = [&](const f32x16& sc, int64_t t0, auto firstc, bf16x8 (&phi)[2], bf16x8 (&plo)[2]) __attribute__((always_inline)) {
+    float p[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) p[v] = sc[v] * a.sm_log2;
-    if (t_end - t0 < kTT) {
+    if (t_end - t0 < kTT) {  // a split's last tile may be partial (uniform branch)
       const int nv = static_cast<int>(t_end - t0);
 #pragma unroll
       for (int v = 0; v < 16; ++v)
@@ -622,15 +636,10 @@ __global__ __launch_bounds__(kWideThreads) void latent_wide_kernel(LatentArgs a)
       const auto m = __builtin_amdgcn_permlane32_swap(__float_as_uint(rmax), __float_as_uint(rmax), false, false);
       rmax = fmaxf(__uint_as_float(m[0]), __uint_as_float(m[1]));  // finite: a tile holds a valid token
     }
-    if (__builtin_amdgcn_ballot_w64(rmax > mu + kLazy) != 0) {
-      // the first tile sets every head's reference (nothing is accumulated yet); on a later
-      // tile the wave gives its split up
-      if (t0 == t_begin)
-        mu = rmax;
-      else
-        gave_up = true;
-    }
-    // ---- weights against mu, then O^T += V^T . P^T with the weights as two bf16 terms
+    if constexpr (decltype(firstc)::value)
+      mu = rmax;
+    else
+      gave_up = gave_up || __builtin_amdgcn_ballot_w64(rmax > mu + kLazy) != 0;
     float rsum = 0.0f;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
@@ -638,7 +647,6 @@ __global__ __launch_bounds__(kWideThreads) void latent_wide_kernel(LatentArgs a)
       rsum += p[v];
     }
     l += rsum;  // this lane's part; the two lanes of a head are summed once, at the end
-    bf16x8 phi[2], plo[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -646,37 +654,65 @@ __global__ __launch_bounds__(kWideThreads) void latent_wide_kernel(LatentArgs a)
         phi[ks][e] = static_cast<__bf16>(p[8 * ks + e]);
         plo[ks][e] = static_cast<__bf16>(p[8 * ks + e] - static_cast<float>(phi[ks][e]));  // exact in float32
       }
-    {
-      // row 32dt + hc sits at 32dt + (hc ^ ((2(dt%2) + hc/16) % 4)): four lane bases, then
-      // offsets that are constants of (dt, ks)
-      const uint16_t* vt = vt_buf[buf];
-      const uint16_t* vb[2][2];
+  };
+  // O^T += V^T . P^T for the tile in buffer B, four output tiles at a time (one tile's MFMAs
+  // back to back would wait on each other's results)
+  auto pv_product = [&](int bc, const bf16x8 (&phi)[2], const bf16x8 (&plo)[2]) __attribute__((always_inline)) {
+    const char* kb = reinterpret_cast<const char*>(klat(bc));
+    constexpr int kG = OT < 4 ? OT : 4;
 #pragma unroll
-      for (int par = 0; par < 2; ++par)
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          vb[par][ks] = vt + (hc ^ ((2 * par + (hc >> 4)) & 3)) * VROW + 8 * ((2 * ks + hh) ^ (((hc >> 2) & 1) << 1));
-      // four output tiles at a time, so that consecutive MFMAs accumulate into different tiles
-      // (one tile's four MFMAs back to back wait on each other's results)
-      constexpr int kG = OT < 4 ? OT : 4;
+      for (int d0 = 0; d0 < OT; d0 += kG) {
+        bf16x8 w[kG];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int d0 = 0; d0 < OT; d0 += kG) {
-          uint4 w[kG];
-#pragma unroll
-          for (int i = 0; i < kG; ++i)
-            w[i] = *reinterpret_cast<const uint4*>(vb[(d0 + i) & 1][ks] + 32 * (d0 + i) * VROW);
-#pragma unroll
-          for (int i = 0; i < kG; ++i)
-            o[d0 + i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(w[i]), phi[ks], o[d0 + i], 0, 0, 0);
-#pragma unroll
-          for (int i = 0; i < kG; ++i)
-            o[d0 + i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(w[i]), plo[ks], o[d0 + i], 0, 0, 0);
+        for (int i = 0; i < kG; ++i) {
+          const int dt = d0 + i;
+          const uint2 lo = lds_read_tr16(kb + pbase[0][dt & 3] + 16 * ks * ROWB + 256 * (dt >> 2));
+          const uint2 hi = lds_read_tr16(kb + pbase[1][dt & 3] + (16 * ks + 8) * ROWB + 256 * (dt >> 2));
+          w[i] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
         }
-    }
+#pragma unroll
+        for (int i = 0; i < kG; ++i)
+          o[d0 + i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w[i], phi[ks], o[d0 + i], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < kG; ++i)
+          o[d0 + i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w[i], plo[ks], o[d0 + i], 0, 0, 0);
+      }
+  };
+
+  bf16x8 phi[2], plo[2];  // weights of the previous tile, for its PV product
+  // one pass: scores of tile t0 from buffer Bq while tile t0+32 is staged into Bs and tile
+  // t0+64 fetched; then the weights of tile t0 and the PV product of the previous tile (buffer
+  // Bp); staged and fetched unconditionally (past the end the fetch re-reads the last row and
+  // the staged buffer is never read)
+  auto pass = [&](int64_t t0, int bq, int bs, int bp, auto firstc) __attribute__((always_inline)) {
+    const f32x16 sc = scores(bq);
+    stage(bs);
+    fetch(t0 + 2 * kTT);
+    bf16x8 nhi[2], nlo[2];
+    weights(sc, t0, firstc, nhi, nlo);
+    if constexpr (!decltype(firstc)::value) pv_product(bp, phi, plo);
     __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      phi[ks] = nhi[ks];
+      plo[ks] = nlo[ks];
+    }
+  };
+
+  fetch(t_begin);
+  stage(0);
+  if (t_begin + kTT < t_end) fetch(t_begin + kTT);
+  __syncthreads();
+  pass(t_begin, 0, 1, 2, std::true_type{});  // a split is never empty
+  int bq = 1;  // buffer of the next tile
+  for (int64_t t0 = t_begin + kTT; t0 < t_end; t0 += kTT) {
+    const int bs = bq == 2 ? 0 : bq + 1, bp = bq == 0 ? 2 : bq - 1;
+    pass(t0, bq, bs, bp, std::false_type{});
+    bq = bs;
   }
+  pv_product(bq == 0 ? 2 : bq - 1, phi, plo);  // the last tile's
 
   l += __shfl_xor(l, 32);
   if (lane == 0)
@@ -861,9 +897,9 @@ extern "C" int fa3q_decode_latent(const uint16_t* q, const int8_t* c_q, const fl
   a.split_len = p.split_len;
   a.sm_log2 = sm_scale * 1.4426950408889634f;
   hipStream_t s = as_stream(stream);
-  // Dl = 512 with a RoPE part of 0 or 32 features spills in the wide kernel's tile loop: those
-  // take the split kernel over the same splits (the workspace is the same)
-  if (p.wide && (Dl < 512 || Dr == 64)) {
+  // Dl = 512 with a RoPE part of 32 features spills in the wide kernel's tile loop: that one
+  // takes the split kernel over the same splits (the workspace is the same)
+  if (p.wide && (Dl < 512 || Dr != 32)) {
     a.flags = reinterpret_cast<uint32_t*>(ws + w.flags);
     hipLaunchKernelGGL(pick_latent(Dl, Dr, true), dim3(static_cast<unsigned>(B * p.groups * p.nsplit)),
                        dim3(kWideThreads), 0, s, a);

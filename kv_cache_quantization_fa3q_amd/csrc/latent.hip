@@ -36,6 +36,11 @@
 // (max reference, sum, s * unnormalised output) in the workspace; a combine kernel merges
 // them.
 //
+// With 128 heads or more, latent_wide_kernel (below) takes 128 heads per workgroup, one wave
+// of 32 heads per SIMD on the 32x32 MFMA, from one staged copy of each tile that the second
+// product reads with the LDS transpose load; this kernel then only recomputes the splits
+// that the wide kernel gave up.
+//
 // Probabilities enter the second product as two bf16 terms, p = hi + lo with hi = bf16(p)
 // and lo = bf16(p - hi), through two MFMAs that share the V operand: the weight error is
 // below 2^-17 relative instead of the 2^-9 of a single bf16 term, whose error bound

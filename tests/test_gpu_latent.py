@@ -59,7 +59,7 @@ CASES = [
     ("one_token", (2, 64, 1, 512, 64)),
     ("short_tail", (2, 128, 97, 512, 64)),
     # 160 heads: a full group of 128 and one of 32 (two waves with no head); the 32-head kernel
-    # at Dl = 256, and Dl = 512 without a RoPE part (the paired kernel over the same splits)
+    # at Dl = 256, and Dl = 512 without a RoPE part
     ("heads_160", (3, 160, 700, 256, 32)),
     ("wide_no_rope", (2, 128, 300, 512, 0)),
 ]
@@ -158,6 +158,37 @@ def test_latent_decode_with_scores_that_keep_growing(fa, name, B, H, T, slope, p
     got = out.cpu().numpy()
     assert np.all(np.isfinite(got))
     ref = oracle.decode_attn_latent(bits16(q), codes, np.float32(0.01), bits16(rope_t), sm, Dl)
+    err = row_rel_err(got, ref)
+    log(f"  row-normalised error {err:.3e}")
+    assert err <= DECODE_TOL, err
+    assert err <= DECODE_DESIGN_TOL, err
+
+
+@pytest.mark.parametrize("Dr", [0, 64])
+def test_latent_wide_512_gives_up_on_a_latent_climb(fa, Dr):
+    """The 128-head kernel at Dl = 512 (with and without a RoPE part), scores that climb
+    through latent feature 0: code 2 (t % 64) against a query of +-16 there.  The splits are
+    64 tokens (two tiles), and the climbing heads' scores rise by about 65 (log2) from the
+    first tile's max to the second's, so every wave gives every split up and the paired
+    kernel recomputes all of them."""
+    dev = torch.device("cuda:0")
+    B, H, T, Dl = 4, 128, 1024, 512
+    rng = np.random.default_rng(131 + Dr)
+    codes = rng.integers(-20, 21, size=(B, T, Dl)).astype(np.int8)
+    codes[:, :, 0] = (2 * (np.arange(T) % 64)).astype(np.int8)
+    q = synth.normal_tensor((B, H, Dl + Dr), dtype=torch.bfloat16, seed=132)
+    q[:, :, 0] = torch.where(torch.arange(H) % 2 == 0, 16.0, -16.0).to(torch.bfloat16)
+    rope_t = synth.normal_tensor((B, T, Dr), dtype=torch.bfloat16, seed=133) if Dr else None
+    scale = torch.tensor([1.0], dtype=torch.float32)
+    sm = 1.0 / math.sqrt(Dl + Dr)
+    log(f"latent climb through the latent part: B={B} H={H} T={T} Dl={Dl} Dr={Dr}")
+    out = fa.fa3q_decode_latent(q.to(dev), torch.from_numpy(codes).to(dev), scale.to(dev),
+                                rope_t.to(dev) if Dr else None, sm)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.all(np.isfinite(got))
+    ref = oracle.decode_attn_latent(bits16(q), codes, np.float32(1.0),
+                                    bits16(rope_t) if Dr else np.zeros((B, T, 0), np.uint16), sm, Dl)
     err = row_rel_err(got, ref)
     log(f"  row-normalised error {err:.3e}")
     assert err <= DECODE_TOL, err

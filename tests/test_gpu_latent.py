@@ -167,24 +167,31 @@ def test_latent_decode_with_scores_that_keep_growing(fa, name, B, H, T, slope, p
 @pytest.mark.parametrize("Dr", [0, 64])
 def test_latent_wide_512_gives_up_on_a_latent_climb(fa, Dr):
     """The 128-head kernel at Dl = 512 (with and without a RoPE part), scores that climb
-    through latent feature 0: code 2 (t % 64) against a query of +-16 there.  The splits are
-    64 tokens (two tiles), and the climbing heads' scores rise by about 65 (log2) from the
-    first tile's max to the second's, so every wave gives every split up and the paired
-    kernel recomputes all of them."""
+    through latent feature 0: code 2 (t % 64) against a query of +-24 there.  The splits are
+    64 tokens (two tiles), and the climbing heads' scores rise by more than 90 (log2) from the
+    first tile's max to the second's, so every wave gives every split up (its flag word in the
+    workspace says so) and the paired kernel recomputes all of them."""
     dev = torch.device("cuda:0")
     B, H, T, Dl = 4, 128, 1024, 512
     rng = np.random.default_rng(131 + Dr)
     codes = rng.integers(-20, 21, size=(B, T, Dl)).astype(np.int8)
     codes[:, :, 0] = (2 * (np.arange(T) % 64)).astype(np.int8)
     q = synth.normal_tensor((B, H, Dl + Dr), dtype=torch.bfloat16, seed=132)
-    q[:, :, 0] = torch.where(torch.arange(H) % 2 == 0, 16.0, -16.0).to(torch.bfloat16)
+    q[:, :, 0] = torch.where(torch.arange(H) % 2 == 0, 24.0, -24.0).to(torch.bfloat16)
     rope_t = synth.normal_tensor((B, T, Dr), dtype=torch.bfloat16, seed=133) if Dr else None
     scale = torch.tensor([1.0], dtype=torch.float32)
     sm = 1.0 / math.sqrt(Dl + Dr)
     log(f"latent climb through the latent part: B={B} H={H} T={T} Dl={Dl} Dr={Dr}")
-    out = fa.fa3q_decode_latent(q.to(dev), torch.from_numpy(codes).to(dev), scale.to(dev),
-                                rope_t.to(dev) if Dr else None, sm)
+    nb = fa.fa3q_decode_latent_workspace_bytes(B, H, T, Dl)
+    ws = torch.zeros(nb, dtype=torch.uint8, device=dev)
+    out = torch.empty((B, H, Dl), dtype=torch.float32, device=dev)
+    fa.fa3q_decode_latent(q.to(dev), torch.from_numpy(codes).to(dev), scale.to(dev),
+                          rope_t.to(dev) if Dr else None, sm, out, ws)
     torch.cuda.synchronize()
+    # 16 splits of 64 tokens, one 128-head group: the last 1 KB holds a flag word per
+    # (sequence, split, wave)
+    flags = ws[nb - 1024:].view(torch.int32).cpu()
+    assert int(flags.sum()) == B * 16 * 4, flags
     got = out.cpu().numpy()
     assert np.all(np.isfinite(got))
     ref = oracle.decode_attn_latent(bits16(q), codes, np.float32(1.0),

@@ -10,7 +10,10 @@ benchmark times (the oracle runs head by head or sequence by sequence on the hos
     the decode tolerances;
   * long context: Q, K, V (2,128,16384,128) with 1e-4 outliers at +-60 sigma, ratios 0.999 /
     0.9999 / 0.99999, every head's window; then decode B=8, T=32768 (split over the tokens),
-    every (b, h) row.
+    every (b, h) row;
+  * shared-latent decode: B=64, H=128, T=4096, Dl=512, Dr=64 over a latent cache made by the
+    library's one-head calibration and quantiser: every (b, h) row within the decode
+    tolerances.
 """
 import math
 
@@ -184,3 +187,42 @@ def test_long_context_every_head_and_pair(fa, kv_cache):
     assert bool(torch.isfinite(out).all())
     worst = _decode_every_pair(q, kq, scales["k"], kr, v, out, sm, "long decode")
     log(f"long decode: largest row error {worst:.3e} over {Bd * H} pairs")
+
+
+def test_latent_decode_every_sequence(fa):
+    B, T, Dl, Dr = 64, 4096, 512, 64
+    sigma = synth.head_sigmas(H, seed=2024)
+    rows = synth.activations((B, 1, T, Dl + Dr), sigma[:1], law="normal", outlier_frac=0.0005, outlier_mult=40.0,
+                             dtype=torch.bfloat16, seed=500, device=DEV)
+    # one scale for the shared latent: the Recall Window of its non-RoPE part at ratio 0.9999
+    mn = torch.empty(1, dtype=torch.float32, device=DEV)
+    mx = torch.empty(1, dtype=torch.float32, device=DEV)
+    rmin = torch.empty(1, dtype=torch.float32, device=DEV)
+    rmax = torch.empty(1, dtype=torch.float32, device=DEV)
+    fa.fa3q_init_minmax(rmin, rmax)
+    fa.fa3q_calibrate_perhead(rows[:, :, :, :Dl].contiguous(), 0.9999, mn, mx)
+    fa.fa3q_accumulate_minmax(rmin, rmax, mn, mx)
+    scale = fa.fa3q_qparams(rmin, rmax)
+    cq, kr = fa.fa3q_quantize_k(rows, scale, Dl)
+    del rows
+    q = synth.normal_tensor((B, H, Dl + Dr), dtype=torch.bfloat16, seed=510, device=DEV)
+    sm = 1.0 / math.sqrt(Dl + Dr)
+    log(f"full shared-latent decode B={B} H={H} T={T} Dl={Dl} Dr={Dr} "
+        f"ws={fa.fa3q_decode_latent_workspace_bytes(B, H, T, Dl)}")
+    out = fa.fa3q_decode_latent(q, cq, scale, kr, sm)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all())
+    s = np.float32(scale.cpu().numpy()[0])
+    qb, got = bits16(q.cpu()), out.cpu().numpy()
+    cb, rb = cq.cpu().numpy().reshape(B, T, Dl), bits16(kr.cpu()).reshape(B, T, Dr)
+    chunk = 8
+
+    def task(b0):
+        ref = oracle.decode_attn_latent(qb[b0:b0 + chunk], cb[b0:b0 + chunk], s, rb[b0:b0 + chunk], sm, Dl)
+        return row_rel_err(got[b0:b0 + chunk], ref)
+
+    errs = parallel(task, range(0, B, chunk))
+    worst = max(errs)
+    log(f"full shared-latent decode: largest row error {worst:.3e} over {B * H} rows")
+    assert worst <= DECODE_TOL, worst
+    assert worst <= DECODE_DESIGN_TOL, worst

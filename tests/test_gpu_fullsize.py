@@ -13,7 +13,10 @@ benchmark times (the oracle runs head by head or sequence by sequence on the hos
     every (b, h) row;
   * shared-latent decode: B=64, H=128, T=4096, Dl=512, Dr=64 over a latent cache made by the
     library's one-head calibration and quantiser: every (b, h) row within the decode
-    tolerances.
+    tolerances;
+  * the asymmetric quantiser (float16 (head, dim) tables from sequence 0's per-channel range)
+    and fake quantisation of the same K, every value of all 64 sequences bit for bit, and the
+    decode over the asymmetric cache, every (b, h) row.
 """
 import math
 
@@ -226,3 +229,60 @@ def test_latent_decode_every_sequence(fa):
     log(f"full shared-latent decode: largest row error {worst:.3e} over {B * H} rows")
     assert worst <= DECODE_TOL, worst
     assert worst <= DECODE_DESIGN_TOL, worst
+
+
+def test_asym_and_fake_quant_every_sequence(fa, kv_cache):
+    c = kv_cache
+    B, T, Dn, Dr, Dv = c["dims"]
+    k, scale = c["k"], c["scale"]
+    # float16 tables from sequence 0's per-channel min/max, as the bench makes them
+    kn0 = k[0, :, :, :Dn].float()
+    lo, hi = kn0.amin(dim=1), kn0.amax(dim=1)
+    a_scale = ((hi - lo) / 255.0).clamp_min(1e-6)
+    a_offset = -128.0 - lo / a_scale
+    a_scale, a_offset = a_scale.to(torch.float16).contiguous(), a_offset.to(torch.float16).contiguous()
+    del kn0, lo, hi
+    log("full asymmetric quantisation and fake quantisation (64,128,4096,192)")
+    akq, akr = fa.fa3q_quantize_asym(k, a_scale, a_offset, Dn)
+    fq = fa.fa3q_fake_quant(k, scale, Dn)
+    torch.cuda.synchronize()
+    sb, ob = a_scale.cpu().view(torch.int16).numpy().view(np.uint16), a_offset.cpu().view(torch.int16).numpy().view(np.uint16)
+    osc = f32(scale)
+    for b in range(B):
+        kb, qb, rb, fb = bits16(k[b:b + 1]), akq[b:b + 1].cpu().numpy(), bits16(akr[b:b + 1]), bits16(fq[b:b + 1])
+
+        def check(h0):
+            sl = slice(h0, h0 + GROUP)
+            okq, okr = oracle.quantize_asym(kb[:, sl], sb[sl], ob[sl], Dn, dtype="float16")
+            ofq = oracle.fake_quant(kb[:, sl], osc[sl], Dn)
+            return (np.array_equal(qb[:, sl], okq), np.array_equal(rb[:, sl], okr), np.array_equal(fb[:, sl], ofq))
+
+        if b % 16 == 0:
+            log(f"full asymmetric / fake quantisation oracle check, sequences {b}..{min(B, b + 16) - 1}")
+        for h0, (codes_ok, rope_ok, fake_ok) in zip(range(0, H, GROUP), parallel(check, range(0, H, GROUP))):
+            assert codes_ok, f"asymmetric codes of sequence {b} heads {h0}.. differ from the oracle"
+            assert rope_ok, f"RoPE part of sequence {b} heads {h0}.. not copied bit for bit"
+            assert fake_ok, f"fake quantisation of sequence {b} heads {h0}.. differs from the oracle"
+    del fq
+    v = synth.activations((B, H, T, Dv), c["sigma"], dtype=torch.bfloat16, seed=300, device=DEV)
+    q = synth.normal_tensor((B, H, Dn + Dr), dtype=torch.bfloat16, seed=400, device=DEV)
+    sm = 1.0 / math.sqrt(Dn + Dr)
+    out = fa.fa3q_decode_attn_asym(q, akq, a_scale, a_offset, akr, v, sm)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all())
+    worst = 0.0
+    for b in range(B):
+        qb, kqb, krb, vb, obb = (bits16(q[b:b + 1]), akq[b:b + 1].cpu().numpy(), bits16(akr[b:b + 1]),
+                                 bits16(v[b:b + 1]), out[b:b + 1].cpu().numpy())
+
+        def err(h0):
+            sl = slice(h0, h0 + GROUP)
+            ref = oracle.decode_attn_asym(qb[:, sl], kqb[:, sl], sb[sl], ob[sl], krb[:, sl], vb[:, sl], sm,
+                                          dtype="float16")
+            return row_rel_err(obb[:, sl], ref)
+
+        e = max(parallel(err, range(0, H, GROUP)))
+        assert e <= DECODE_TOL and e <= DECODE_DESIGN_TOL, ("asymmetric decode", b, e)
+        worst = max(worst, e)
+    log(f"full asymmetric decode: largest row error {worst:.3e} over {B * H} pairs")
+    del v, q, akq, akr

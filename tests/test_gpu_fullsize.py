@@ -16,7 +16,9 @@ benchmark times (the oracle runs head by head or sequence by sequence on the hos
     tolerances;
   * the asymmetric quantiser (float16 (head, dim) tables from sequence 0's per-channel range)
     and fake quantisation of the same K, every value of all 64 sequences bit for bit, and the
-    decode over the asymmetric cache, every (b, h) row.
+    decode over the asymmetric cache, every (b, h) row;
+  * the decode step that appends a token at position T-1 (the new cache row of every (b, h)
+    bit for bit, every output row) and the decode with Q, K and V in INT8 (every row).
 """
 import math
 
@@ -286,3 +288,85 @@ def test_asym_and_fake_quant_every_sequence(fa, kv_cache):
         worst = max(worst, e)
     log(f"full asymmetric decode: largest row error {worst:.3e} over {B * H} pairs")
     del v, q, akq, akr
+
+
+def _per_head_scale(fa, x4):
+    """Scales from the library's own calibration of x4 (B,H,S,D) at ratio 0.9999."""
+    nh = int(x4.shape[1])
+    rmin = torch.empty(nh, dtype=torch.float32, device=DEV)
+    rmax = torch.empty(nh, dtype=torch.float32, device=DEV)
+    fa.fa3q_init_minmax(rmin, rmax)
+    wmin, wmax = fa.fa3q_calibrate_perhead(x4, 0.9999)
+    fa.fa3q_accumulate_minmax(rmin, rmax, wmin, wmax)
+    return fa.fa3q_qparams(rmin, rmax)
+
+
+def test_append_and_qkv8_decode_every_pair(fa, kv_cache):
+    c = kv_cache
+    B, T, Dn, Dr, Dv = c["dims"]
+    kq, kr, scale = c["kq"], c["kr"], c["scale"]
+    v = synth.activations((B, H, T, Dv), c["sigma"], dtype=torch.bfloat16, seed=300, device=DEV)
+    q = synth.normal_tensor((B, H, Dn + Dr), dtype=torch.bfloat16, seed=400, device=DEV)
+    sm = 1.0 / math.sqrt(Dn + Dr)
+    osc = f32(scale)
+    # ---- append one token per (b, h) at position T-1 (into copies: the fixture's cache is shared)
+    k_new = synth.normal_tensor((B, H, Dn + Dr), dtype=torch.bfloat16, seed=410, device=DEV)
+    v_new = synth.normal_tensor((B, H, Dv), dtype=torch.bfloat16, seed=420, device=DEV)
+    kv_len = torch.full((B,), T - 1, dtype=torch.int32, device=DEV)
+    kq2, kr2, v2 = kq.clone(), kr.clone(), v.clone()
+    log(f"full decode step with append at T-1: B={B} H={H} T={T}")
+    out = fa.fa3q_decode_append_attn(q, k_new, v_new, scale, kq2, kr2, v2, kv_len, sm)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all())
+    knb, vnb = bits16(k_new), bits16(v_new)
+    worst = 0.0
+    for b in range(B):
+        qb, kqb, krb, vb = bits16(q[b:b + 1]), kq[b:b + 1].cpu().numpy(), bits16(kr[b:b + 1]), bits16(v[b:b + 1])
+        ob = out[b:b + 1].cpu().numpy()
+        row_q = kq2[b:b + 1, :, T - 1].cpu().numpy()
+        row_r, row_v = bits16(kr2[b:b + 1, :, T - 1]), bits16(v2[b:b + 1, :, T - 1])
+
+        def check(h0):
+            sl = slice(h0, h0 + GROUP)
+            ref, oc, orr, ov = oracle.decode_append_attn(qb[:, sl], knb[b:b + 1, sl], vnb[b:b + 1, sl], osc[sl],
+                                                         kqb[:, sl], krb[:, sl], vb[:, sl], np.array([T - 1]), sm, Dn)
+            rows_ok = (np.array_equal(row_q[:, sl], oc[:, :, T - 1]) and np.array_equal(row_r[:, sl], orr[:, :, T - 1])
+                       and np.array_equal(row_v[:, sl], ov[:, :, T - 1]))
+            return row_rel_err(ob[:, sl], ref), rows_ok
+
+        res = parallel(check, range(0, H, GROUP))
+        assert all(ok for _, ok in res), f"appended cache row of sequence {b} differs from the oracle"
+        e = max(err for err, _ in res)
+        assert e <= DECODE_TOL and e <= DECODE_DESIGN_TOL, ("decode with append", b, e)
+        worst = max(worst, e)
+    # the rest of the caches is untouched
+    assert torch.equal(kq2[:, :, :T - 1], kq[:, :, :T - 1]) and torch.equal(v2[:, :, :T - 1], v[:, :, :T - 1])
+    log(f"full decode with append: largest row error {worst:.3e} over {B * H} pairs")
+    del kq2, kr2, v2, k_new, v_new
+    # ---- Q, K and V in INT8, the scales of Q and V from the library's calibration
+    scale_v = _per_head_scale(fa, v[:1].contiguous())
+    scale_q = _per_head_scale(fa, q[:, :, :Dn].contiguous().view(B, H, 1, Dn))
+    vq, _ = fa.fa3q_quantize_k(v, scale_v, Dv)
+    qc, qrope = fa.fa3q_quantize_k(q.view(B, H, 1, Dn + Dr), scale_q, Dn)
+    qc, qrope = qc.view(B, H, Dn), qrope.view(B, H, Dr)
+    log(f"full decode with Q, K, V INT8: B={B} H={H} T={T}")
+    out = fa.fa3q_decode_attn_qkv8(qc, qrope, scale_q, kq, scale, kr, vq, scale_v, sm)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all())
+    sq, sv = f32(scale_q), f32(scale_v)
+    qcb, qrb = qc.cpu().numpy(), bits16(qrope)
+    worst = 0.0
+    for b in range(B):
+        kqb, krb, vqb, ob = kq[b:b + 1].cpu().numpy(), bits16(kr[b:b + 1]), vq[b:b + 1].cpu().numpy(), out[b:b + 1].cpu().numpy()
+
+        def err(h0):
+            sl = slice(h0, h0 + GROUP)
+            ref = oracle.decode_attn_qkv8(qcb[b:b + 1, sl], qrb[b:b + 1, sl], sq[sl], kqb[:, sl], osc[sl], krb[:, sl],
+                                          vqb[:, sl], sv[sl], sm)
+            return row_rel_err(ob[:, sl], ref)
+
+        e = max(parallel(err, range(0, H, GROUP)))
+        assert e <= DECODE_TOL and e <= DECODE_DESIGN_TOL, ("decode with Q, K, V INT8", b, e)
+        worst = max(worst, e)
+    log(f"full decode with Q, K, V INT8: largest row error {worst:.3e} over {B * H} pairs")
+    del v, q, vq

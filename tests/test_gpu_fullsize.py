@@ -18,7 +18,12 @@ benchmark times (the oracle runs head by head or sequence by sequence on the hos
     and fake quantisation of the same K, every value of all 64 sequences bit for bit, and the
     decode over the asymmetric cache, every (b, h) row;
   * the decode step that appends a token at position T-1 (the new cache row of every (b, h)
-    bit for bit, every output row) and the decode with Q, K and V in INT8 (every row).
+    bit for bit, every output row) and the decode with Q, K and V in INT8 (every row);
+  * the decode over the same cache bytes as pools of 64-token pages through a permuted block
+    table (every row);
+  * float16 in the (B,S,H,D) layout: 4 calibration batches (8,2048,128,128) (every head's window
+    in every batch, bit for bit), the K quantisation of (64,4096,128,192) (every code and RoPE
+    pattern) and the decode over that cache (every row).
 """
 import math
 
@@ -370,3 +375,114 @@ def test_append_and_qkv8_decode_every_pair(fa, kv_cache):
         worst = max(worst, e)
     log(f"full decode with Q, K, V INT8: largest row error {worst:.3e} over {B * H} pairs")
     del v, q, vq
+
+
+def test_paged_decode_every_pair(fa, kv_cache):
+    c = kv_cache
+    B, T, Dn, Dr, Dv = c["dims"]
+    kq, kr, scale = c["kq"], c["kr"], c["scale"]
+    v = synth.activations((B, H, T, Dv), c["sigma"], dtype=torch.bfloat16, seed=300, device=DEV)
+    q = synth.normal_tensor((B, H, Dn + Dr), dtype=torch.bfloat16, seed=400, device=DEV)
+    sm = 1.0 / math.sqrt(Dn + Dr)
+    # the cache bytes read as pools of 64-token pages, each sequence's pages a seeded permutation
+    PG = 64
+    n_pages = B * T // PG
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(700)
+    table = torch.randperm(n_pages, generator=gen).to(torch.int32).view(B, T // PG)
+    kq_p, kr_p, v_p = kq.view(n_pages, H, PG, Dn), kr.view(n_pages, H, PG, Dr), v.view(n_pages, H, PG, Dv)
+    full_len = torch.full((B,), T, dtype=torch.int32)
+    log(f"full paged decode: B={B} H={H} T={T} in {PG}-token pages")
+    out = fa.fa3q_decode_paged_attn(q, None, None, scale, kq_p, kr_p, v_p, table.to(DEV), full_len.to(DEV), sm)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all())
+    osc = f32(scale)
+    tab = table.numpy().astype(np.int64)
+    local = np.arange(T // PG, dtype=np.int64)[None, :]  # the sequence's own pages, in table order
+    worst = 0.0
+    for b in range(B):
+        pages = torch.from_numpy(tab[b]).to(DEV)
+        sq_, sr_, sv_ = (kq_p.index_select(0, pages).cpu().numpy(), bits16(kr_p.index_select(0, pages)),
+                         bits16(v_p.index_select(0, pages)))
+        qb, ob = bits16(q[b:b + 1]), out[b:b + 1].cpu().numpy()
+
+        def err(h0):
+            sl = slice(h0, h0 + GROUP)
+            ref = oracle.decode_paged_attn(qb[:, sl], None, None, osc[sl], sq_[:, sl], sr_[:, sl], sv_[:, sl], local,
+                                           np.array([T]), sm, Dn)[0]
+            return row_rel_err(ob[:, sl], ref)
+
+        e = max(parallel(err, range(0, H, GROUP)))
+        assert e <= DECODE_TOL and e <= DECODE_DESIGN_TOL, ("paged decode", b, e)
+        worst = max(worst, e)
+    log(f"full paged decode: largest row error {worst:.3e} over {B * H} pairs")
+    del v, q
+
+
+def _h16(t: torch.Tensor) -> np.ndarray:
+    """float16 tensor -> its uint16 patterns on the host."""
+    return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def test_f16_bshd_every_output(fa, kv_cache):
+    c = kv_cache
+    B, T, Dn, Dr, Dv = c["dims"]
+    sigma, scale = c["sigma"], c["scale"]
+    osc = f32(scale)
+    ratio = 0.9999
+    # ---- calibration: 4 float16 (B,S,H,D) batches, drawn head-major with the step's recipe
+    xs = [synth.activations((8, H, 2048, 128), sigma, law="t3", dtype=torch.float16, seed=100 + i, device=DEV)
+          .transpose(1, 2).contiguous() for i in range(4)]
+    log("full float16 (B,S,H,D) calibration, 4 batches (8,2048,128,128)")
+    wmin, wmax = fa.fa3q_calibrate_ex(xs, ratio, layout="BSHD")
+    torch.cuda.synchronize()
+    for i, x in enumerate(xs):
+        heads = oracle.per_head_view(oracle.to_bhsd(oracle.bits16_to_f32(_h16(x), "f16"), "BSHD"))
+        res = parallel(lambda h: oracle.recall_window(heads[h], ratio), range(H))
+        assert_bits_equal(f32(wmin[i]), np.array([r[0] for r in res], np.float32), f"f16 BSHD batch {i} win_min")
+        assert_bits_equal(f32(wmax[i]), np.array([r[1] for r in res], np.float32), f"f16 BSHD batch {i} win_max")
+        del heads
+    del xs
+    # ---- quantisation of float16 (B,S,H,D) K with the fixture's scales
+    k = synth.activations((B, H, T, Dn + Dr), sigma, law="normal", outlier_frac=0.0005, outlier_mult=40.0,
+                          dtype=torch.float16, seed=200, device=DEV).transpose(1, 2).contiguous()
+    log("full float16 (B,S,H,D) quantisation (64,4096,128,192)")
+    kq, kr = fa.fa3q_quantize_k_ex(k, scale, Dn, layout="BSHD")
+    torch.cuda.synchronize()
+    for b in range(B):
+        kb, qb, rb = _h16(k[b:b + 1]), kq[b:b + 1].cpu().numpy(), _h16(kr[b:b + 1])
+
+        def check(h0):
+            sl = slice(h0, h0 + GROUP)
+            okq, okr = oracle.quantize_k(kb[:, :, sl], osc[sl], Dn, dtype="f16", layout="BSHD")
+            return np.array_equal(qb[:, :, sl], okq), np.array_equal(rb[:, :, sl], okr)
+
+        for h0, (codes_ok, rope_ok) in zip(range(0, H, GROUP), parallel(check, range(0, H, GROUP))):
+            assert codes_ok, f"float16 (B,S,H,D) codes of sequence {b} heads {h0}.. differ from the oracle"
+            assert rope_ok, f"float16 (B,S,H,D) RoPE part of sequence {b} heads {h0}.. not copied bit for bit"
+    del k
+    # ---- decode over that cache with float16 q, K-rope and V
+    v = synth.activations((B, H, T, Dv), sigma, law="normal", dtype=torch.float16, seed=300,
+                          device=DEV).transpose(1, 2).contiguous()
+    q = synth.normal_tensor((B, H, Dn + Dr), dtype=torch.float16, seed=400, device=DEV)
+    sm = 1.0 / math.sqrt(Dn + Dr)
+    log("full float16 (B,S,H,D) decode B=64 H=128 T=4096")
+    out = fa.fa3q_decode_attn_ex(q, kq, scale, kr, v, sm, layout="BSHD")
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all())
+    worst = 0.0
+    for b in range(B):
+        qb, kqb, krb, vb, ob = (_h16(q[b:b + 1]), kq[b:b + 1].cpu().numpy(), _h16(kr[b:b + 1]), _h16(v[b:b + 1]),
+                                out[b:b + 1].cpu().numpy())
+
+        def err(h0):
+            sl = slice(h0, h0 + GROUP)
+            ref = oracle.decode_attn(qb[:, sl], kqb[:, :, sl], osc[sl], krb[:, :, sl], vb[:, :, sl], sm, dtype="f16",
+                                     layout="BSHD")
+            return row_rel_err(ob[:, sl], ref)
+
+        e = max(parallel(err, range(0, H, GROUP)))
+        assert e <= DECODE_TOL and e <= DECODE_DESIGN_TOL, ("float16 (B,S,H,D) decode", b, e)
+        worst = max(worst, e)
+    log(f"full float16 (B,S,H,D) decode: largest row error {worst:.3e} over {B * H} pairs")
+    del v, q, kq, kr

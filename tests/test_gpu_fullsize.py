@@ -156,49 +156,6 @@ def test_decode_every_pair(fa, kv_cache):
     del v, q
 
 
-def test_long_context_every_head_and_pair(fa, kv_cache):
-    kv_cache.clear()  # release the 4096-token workload first
-    torch.cuda.empty_cache()
-    shape = (2, H, 16384, 128)
-    N = shape[0] * shape[2] * shape[3]
-    sigma = synth.head_sigmas(H, seed=77)
-    scales = {}
-    for name, seed in (("q", 500), ("k", 501), ("v", 502)):
-        x = synth.activations(shape, sigma, law="t3", outlier_frac=1e-4, outlier_mult=60.0, dtype=torch.bfloat16,
-                              seed=seed, device=DEV)
-        for ratio in (0.999, 0.9999, 0.99999):
-            log(f"long calib {name}: {tuple(shape)} ratio={ratio} K={N - int(ratio * N) + 1}")
-            wmin, wmax = fa.fa3q_calibrate_perhead(x, ratio)
-            torch.cuda.synchronize()
-            lo, hi = oracle_windows(x, ratio)
-            assert_bits_equal(f32(wmin), lo, f"{name} ratio={ratio} win_min")
-            assert_bits_equal(f32(wmax), hi, f"{name} ratio={ratio} win_max")
-            if name == "k" and ratio == 0.9999:
-                run_min = torch.empty(H, dtype=torch.float32, device=DEV)
-                run_max = torch.empty(H, dtype=torch.float32, device=DEV)
-                fa.fa3q_init_minmax(run_min, run_max)
-                fa.fa3q_accumulate_minmax(run_min, run_max, wmin, wmax)
-                scales["k"] = fa.fa3q_qparams(run_min, run_max)
-        del x
-    torch.cuda.empty_cache()
-
-    Bd, T, Dn, Dr, Dv = 8, 32768, 128, 64, 128
-    k = synth.activations((Bd, H, T, Dn + Dr), sigma, law="t3", outlier_frac=1e-4, outlier_mult=60.0,
-                          dtype=torch.bfloat16, seed=600, device=DEV)
-    log("long quantize (8,128,32768,192)")
-    kq, kr = fa.fa3q_quantize_k(k, scales["k"], Dn)
-    del k
-    v = synth.activations((Bd, H, T, Dv), sigma, law="t3", dtype=torch.bfloat16, seed=601, device=DEV)
-    q = synth.normal_tensor((Bd, H, Dn + Dr), dtype=torch.bfloat16, seed=602, device=DEV)
-    sm = 1.0 / math.sqrt(Dn + Dr)
-    log(f"long decode B={Bd} T={T} ws={fa.fa3q_decode_attn_workspace_bytes(Bd, H, T, Dv)}")
-    out = fa.fa3q_decode_attn(q, kq, scales["k"], kr, v, sm)
-    torch.cuda.synchronize()
-    assert bool(torch.isfinite(out).all())
-    worst = _decode_every_pair(q, kq, scales["k"], kr, v, out, sm, "long decode")
-    log(f"long decode: largest row error {worst:.3e} over {Bd * H} pairs")
-
-
 def test_latent_decode_every_sequence(fa):
     B, T, Dl, Dr = 64, 4096, 512, 64
     sigma = synth.head_sigmas(H, seed=2024)
@@ -486,3 +443,47 @@ def test_f16_bshd_every_output(fa, kv_cache):
         worst = max(worst, e)
     log(f"full float16 (B,S,H,D) decode: largest row error {worst:.3e} over {B * H} pairs")
     del v, q, kq, kr
+
+
+# last: it releases the 4096-token cache of the module fixture before its own allocations
+def test_long_context_every_head_and_pair(fa, kv_cache):
+    kv_cache.clear()  # release the 4096-token workload first
+    torch.cuda.empty_cache()
+    shape = (2, H, 16384, 128)
+    N = shape[0] * shape[2] * shape[3]
+    sigma = synth.head_sigmas(H, seed=77)
+    scales = {}
+    for name, seed in (("q", 500), ("k", 501), ("v", 502)):
+        x = synth.activations(shape, sigma, law="t3", outlier_frac=1e-4, outlier_mult=60.0, dtype=torch.bfloat16,
+                              seed=seed, device=DEV)
+        for ratio in (0.999, 0.9999, 0.99999):
+            log(f"long calib {name}: {tuple(shape)} ratio={ratio} K={N - int(ratio * N) + 1}")
+            wmin, wmax = fa.fa3q_calibrate_perhead(x, ratio)
+            torch.cuda.synchronize()
+            lo, hi = oracle_windows(x, ratio)
+            assert_bits_equal(f32(wmin), lo, f"{name} ratio={ratio} win_min")
+            assert_bits_equal(f32(wmax), hi, f"{name} ratio={ratio} win_max")
+            if name == "k" and ratio == 0.9999:
+                run_min = torch.empty(H, dtype=torch.float32, device=DEV)
+                run_max = torch.empty(H, dtype=torch.float32, device=DEV)
+                fa.fa3q_init_minmax(run_min, run_max)
+                fa.fa3q_accumulate_minmax(run_min, run_max, wmin, wmax)
+                scales["k"] = fa.fa3q_qparams(run_min, run_max)
+        del x
+    torch.cuda.empty_cache()
+
+    Bd, T, Dn, Dr, Dv = 8, 32768, 128, 64, 128
+    k = synth.activations((Bd, H, T, Dn + Dr), sigma, law="t3", outlier_frac=1e-4, outlier_mult=60.0,
+                          dtype=torch.bfloat16, seed=600, device=DEV)
+    log("long quantize (8,128,32768,192)")
+    kq, kr = fa.fa3q_quantize_k(k, scales["k"], Dn)
+    del k
+    v = synth.activations((Bd, H, T, Dv), sigma, law="t3", dtype=torch.bfloat16, seed=601, device=DEV)
+    q = synth.normal_tensor((Bd, H, Dn + Dr), dtype=torch.bfloat16, seed=602, device=DEV)
+    sm = 1.0 / math.sqrt(Dn + Dr)
+    log(f"long decode B={Bd} T={T} ws={fa.fa3q_decode_attn_workspace_bytes(Bd, H, T, Dv)}")
+    out = fa.fa3q_decode_attn(q, kq, scales["k"], kr, v, sm)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all())
+    worst = _decode_every_pair(q, kq, scales["k"], kr, v, out, sm, "long decode")
+    log(f"long decode: largest row error {worst:.3e} over {Bd * H} pairs")

@@ -95,12 +95,19 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
   return before + inc - v;
 }
 
+// Counts go to kCountCopies copies of the histogram, lane l to copy l % kCountCopies, so lanes
+// of one digit (the leading byte of a tail takes few values) meet in one counter at most
+// 64 / kCountCopies at a time; a copy's row is kDigits + 1 words, so one digit's counters in
+// the copies sit in different banks.
+constexpr int kCountCopies = 16;
+
 __global__ __launch_bounds__(kSortThreads) void lsd_count_kernel(SortArgs a) {
-  __shared__ uint32_t cnt[kDigits];
+  __shared__ uint32_t cnt[kCountCopies * (kDigits + 1)];
   const int tid = static_cast<int>(threadIdx.x);
   const int lane = tid & (kWave - 1), wave = tid / kWave;
   const int h = static_cast<int>(blockIdx.x) / a.nblk, blk = static_cast<int>(blockIdx.x) % a.nblk;
-  cnt[tid] = 0;
+  for (int i = tid; i < kCountCopies * (kDigits + 1); i += kSortThreads) cnt[i] = 0;
+  uint32_t* mine = cnt + (lane % kCountCopies) * (kDigits + 1);
   __syncthreads();
   uint64_t start, end;
   block_range(a.cut[h].M, a.nblk, blk, start, end);
@@ -119,13 +126,16 @@ __global__ __launch_bounds__(kSortThreads) void lsd_count_kernel(SortArgs a) {
       kn[s] = w0 + kCountTile + s * kWave < end ? src[w0 + kCountTile + s * kWave] : 0u;
 #pragma unroll
     for (int s = 0; s < kSlots; ++s) {
-      if (w0 + s * kWave < end) atomicAdd(&cnt[(k[s] >> a.shift) & 0xffu], 1u);  // counts need no order
+      if (w0 + s * kWave < end) atomicAdd(&mine[(k[s] >> a.shift) & 0xffu], 1u);  // counts need no order
     }
 #pragma unroll
     for (int s = 0; s < kSlots; ++s) k[s] = kn[s];
   }
   __syncthreads();
-  a.bcount[(static_cast<int64_t>(h) * kDigits + tid) * a.nblk + blk] = cnt[tid];
+  uint32_t total = 0;
+#pragma unroll
+  for (int c = 0; c < kCountCopies; ++c) total += cnt[c * (kDigits + 1) + tid];
+  a.bcount[(static_cast<int64_t>(h) * kDigits + tid) * a.nblk + blk] = total;
 }
 
 __global__ __launch_bounds__(kScatterThreads) void lsd_scatter_kernel(SortArgs a) {

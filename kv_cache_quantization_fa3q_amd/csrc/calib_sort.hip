@@ -138,8 +138,9 @@ __global__ __launch_bounds__(kSortThreads) void lsd_count_kernel(SortArgs a) {
   a.bcount[(static_cast<int64_t>(h) * kDigits + tid) * a.nblk + blk] = total;
 }
 
+template <bool kMatch>
 __global__ __launch_bounds__(kScatterThreads) void lsd_scatter_kernel(SortArgs a) {
-  __shared__ uint64_t peer[kScatterWaves * kDigits];  // [wave][digit]: the lanes of each digit (zero between uses)
+  __shared__ uint64_t peer[kMatch ? 8 : kScatterWaves * kDigits];  // [wave][digit]: the lanes of each digit (zero between uses)
   __shared__ uint32_t cnt[kScatterWaves * kDigits];   // [wave][digit]: keys so far, then tile positions
   __shared__ uint32_t tstart[kDigits];                // the digit's first position in the laid-out tile
   __shared__ uint32_t gbase[kDigits];                 // the digit's next list position from this block
@@ -152,8 +153,10 @@ __global__ __launch_bounds__(kScatterThreads) void lsd_scatter_kernel(SortArgs a
   uint64_t start, end;
   block_range(a.cut[h].M, a.nblk, blk, start, end);
   if (start >= end) return;
+  if constexpr (!kMatch) {
 #pragma unroll
-  for (int i = 0; i < kScatterWaves * kDigits / kScatterThreads; ++i) peer[i * kScatterThreads + tid] = 0;
+    for (int i = 0; i < kScatterWaves * kDigits / kScatterThreads; ++i) peer[i * kScatterThreads + tid] = 0;
+  }
   {
     // digit tid: keys of smaller digits in the head, plus its keys in earlier blocks (the scan's
     // barrier also orders the peer table's zeroing before its first use)
@@ -185,24 +188,47 @@ __global__ __launch_bounds__(kScatterThreads) void lsd_scatter_kernel(SortArgs a
     for (int i = 0; i < kScatterWaves * kDigits / kScatterThreads; ++i) cnt[i * kScatterThreads + tid] = 0;
     __syncthreads();
     // rank of each key among the wave's earlier keys of its digit (slots in order, lanes in
-    // order): the lanes of one digit come from the wave's peer table (each lane sets its bit,
-    // reads its digit's mask, clears it), the earlier slots' count from the per-wave counter.
-    // A wave's LDS operations complete in the order it issues them.
-#pragma unroll
-    for (int s = 0; s < kSlots; ++s) {
-      const bool valid = w0 + s * kWave < end;
-      const uint32_t d = (k[s] >> a.shift) & 0xffu;
-      uint64_t* pt = &peer[wave * kDigits + d];
-      uint32_t* c = &cnt[wave * kDigits + d];
-      if (valid) atomicOr(reinterpret_cast<unsigned long long*>(pt), static_cast<unsigned long long>(bit));
-      const uint64_t peers = valid ? *pt : uint64_t{0};
-      const uint32_t base = valid ? *c : 0u;
-      const uint32_t r = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(peers >> 32),
-                                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(peers), 0u));
-      rk[s] = base + r;
-      if (valid) {
-        *pt = 0;
-        if (r == 0) *c = base + static_cast<uint32_t>(__popcll(peers));  // the digit's first lane
+    // order), the earlier slots' count from the per-wave counter.  The lanes of one digit come
+    // from the wave's peer table (each lane sets its bit, reads its digit's mask, clears it), or,
+    // for the leading byte, which tails share among a handful of values (so that the table's
+    // atomics queue), from one ballot per digit bit.  A wave's LDS operations complete in the
+    // order it issues them.
+    if constexpr (kMatch) {
+  #pragma unroll
+      for (int s = 0; s < kSlots; ++s) {
+        const bool valid = w0 + s * kWave < end;
+        const uint32_t d = (k[s] >> a.shift) & 0xffu;
+        uint32_t* c = &cnt[wave * kDigits + d];
+        uint64_t peers = __builtin_amdgcn_ballot_w64(valid);
+  #pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const bool one = (d >> i) & 1u;
+          const uint64_t m = __builtin_amdgcn_ballot_w64(one);
+          peers &= one ? m : ~m;
+        }
+        const uint32_t base = valid ? *c : 0u;
+        const uint32_t r = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(peers >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(peers), 0u));
+        rk[s] = base + r;
+        if (valid && r == 0) *c = base + static_cast<uint32_t>(__popcll(peers));  // the digit's first lane
+      }
+    } else {
+  #pragma unroll
+      for (int s = 0; s < kSlots; ++s) {
+        const bool valid = w0 + s * kWave < end;
+        const uint32_t d = (k[s] >> a.shift) & 0xffu;
+        uint64_t* pt = &peer[wave * kDigits + d];
+        uint32_t* c = &cnt[wave * kDigits + d];
+        if (valid) atomicOr(reinterpret_cast<unsigned long long*>(pt), static_cast<unsigned long long>(bit));
+        const uint64_t peers = valid ? *pt : uint64_t{0};
+        const uint32_t base = valid ? *c : 0u;
+        const uint32_t r = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(peers >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(peers), 0u));
+        rk[s] = base + r;
+        if (valid) {
+          *pt = 0;
+          if (r == 0) *c = base + static_cast<uint32_t>(__popcll(peers));  // the digit's first lane
+        }
       }
     }
     __syncthreads();
@@ -349,7 +375,8 @@ int sort_launch(const void* const* xs, int64_t nb, int64_t H, int64_t t, int64_t
       sa.dst = (pass & 1) ? list_a : list_b;
       sa.shift = 8 * pass;
       hipLaunchKernelGGL(lsd_count_kernel, g_blocks, blk, 0, stream, sa);
-      hipLaunchKernelGGL(lsd_scatter_kernel, g_blocks, blk_sc, 0, stream, sa);
+      hipLaunchKernelGGL(pass == 3 ? lsd_scatter_kernel<true> : lsd_scatter_kernel<false>, g_blocks, blk_sc, 0, stream,
+                         sa);
     }
     WinArgs wa;
     wa.list = list_a;  // four passes: sorted back into the first buffer
